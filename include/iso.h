@@ -1,0 +1,127 @@
+/*
+ * iso.h -- C ABI of the MI355X (gfx950) batched weighted L2 isotonic regression library
+ * (libiso_mi355x.so).
+ *
+ * The fit.  For every row of a row-major [batch, n] array,
+ *
+ *     z* = argmin_z  sum_i w_i (z_i - y_i)^2   subject to  z_0 <= z_1 <= ... <= z_{n-1},
+ *
+ * with w_i > 0 ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 1).
+ * z* is the slope sequence of the lower convex hull of the cumulative sum diagram
+ * P_0 = (0, 0), P_{k+1} = P_k + (w_k, w_k y_k) (same page, Section 1 and Section 2.1; the
+ * page's equations for the diagram were lost in extraction, this is the classical reading).
+ * Element k starts a block exactly when P_k is a vertex of the canonical hull, in which a point
+ * lying on the segment between its neighbours is not a vertex (Section 2.1), so neighbouring
+ * blocks have strictly increasing means.
+ *
+ * Conventions common to every entry point
+ *   - Arrays are device memory owned by the caller, contiguous, row-major [batch, n]: element
+ *     (r, i) is at index r * n + i.  Indices and sizes are 64-bit.
+ *   - dtype is ISO_F32 or ISO_F64 and applies to y, w, z, g, gy and gw alike.  Whatever the
+ *     dtype, the diagram is accumulated in fp64 (an fp32 product w*y is exact in fp64) and every
+ *     output value is one fp64 slope rounded once to dtype (round to nearest even).
+ *   - stream is a hipStream_t cast to void* (NULL: the null stream).  Work is enqueued on it and
+ *     the call returns without waiting, except where a synchronous check is requested.  The
+ *     library keeps no pointer beyond the stream's completion of the call's work.
+ *   - Errors in the arguments are returned synchronously, before anything is enqueued.
+ *   - Input rows with a non-finite y or w, or a w <= 0, are flagged per row (bit 0: non-finite
+ *     value, bit 1: weight <= 0) and get an all-NaN z and no block starts; other rows are fitted
+ *     normally (the page's Section 6 keeps per-row NaN flags and checks weight positivity).
+ *   - batch == 0 or n == 0 returns ISO_OK and enqueues nothing.
+ */
+#ifndef ISO_MI355X_H
+#define ISO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+enum { ISO_F32 = 0, ISO_F64 = 1 };
+
+/* Return codes. */
+enum {
+  ISO_OK = 0,
+  ISO_EINVAL = 1,  /* bad argument: NULL pointer, negative size, overflow, bad dtype, overlap,
+                      workspace too small */
+  ISO_EWEIGHT = 2, /* synchronous weight check found a row with a weight <= 0 (or non-finite) */
+  ISO_ENOMEM = 3,  /* device allocation of the workspace failed (iso_fit only) */
+  ISO_EHIP = 4     /* a HIP runtime call or kernel launch failed */
+};
+
+/* Flags of iso_fit_ex. */
+enum {
+  /* After the fit, wait for the stream and return ISO_EWEIGHT if any row holds a weight <= 0
+     or a non-finite weight (the page's Section 6: weighted calls check positivity, which waits
+     for the GPU). */
+  ISO_FLAG_CHECK_WEIGHTS = 1u
+};
+
+/* Per-row flag bits written to row_flags. */
+enum { ISO_ROW_NONFINITE = 1u, ISO_ROW_BAD_WEIGHT = 2u };
+
+/*
+ * iso_fit -- fit every row; the simple entry point.
+ *   y      [batch, n] input values (required).
+ *   w      [batch, n] weights, or NULL for unit weights.
+ *   z      [batch, n] output fit (required; must not overlap y or w).
+ * Scratch memory is taken from the stream-ordered allocator (hipMallocAsync/hipFreeAsync).
+ * When w != NULL the call behaves as iso_fit_ex with ISO_FLAG_CHECK_WEIGHTS (it waits for the
+ * stream).  Returns ISO_OK, ISO_EINVAL, ISO_EWEIGHT, ISO_ENOMEM or ISO_EHIP.
+ */
+int iso_fit(const void* y, const void* w, void* z, int64_t batch, int64_t n, int dtype,
+            void* stream);
+
+/*
+ * iso_workspace_bytes -- size in bytes of the workspace iso_fit_ex needs for this shape
+ * (weighted != 0 when w will be passed).  0 means no workspace is needed.  Returns 0 for
+ * invalid shapes as well; iso_fit_ex reports those.
+ */
+size_t iso_workspace_bytes(int64_t batch, int64_t n, int dtype, int weighted);
+
+/*
+ * iso_fit_ex -- fit with caller-provided workspace and optional outputs.
+ *   block_start  [batch, n] bytes, or NULL: 1 where an element starts a block (its left point of
+ *                the diagram is a vertex of the canonical hull), else 0.  Element 0 of every
+ *                valid row is 1.  Needed by iso_vjp.
+ *   row_flags    [batch] uint32, or NULL: the per-row flag bits above.
+ *   ws, ws_bytes device workspace of at least iso_workspace_bytes(batch, n, dtype, w != NULL)
+ *                bytes, 256-byte aligned; may be NULL when that size is 0.  Its contents on entry
+ *                do not matter and on return are unspecified.  Calls that share a workspace must
+ *                be ordered on one stream.
+ *   flags        0 or ISO_FLAG_CHECK_WEIGHTS.
+ * Returns ISO_OK, ISO_EINVAL, ISO_EWEIGHT (only with ISO_FLAG_CHECK_WEIGHTS) or ISO_EHIP.
+ */
+int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,
+               int64_t batch, int64_t n, int dtype, void* ws, size_t ws_bytes, unsigned flags,
+               void* stream);
+
+/*
+ * iso_vjp -- backward of the fit: the vector-Jacobian product with a cotangent g.  The fit is
+ * constant on blocks, each the weighted mean of y over the block, so with G and W the sums of g
+ * and w over the block holding element i ("Merge Hulls Without Copying Vertices", Section 6,
+ * Gradient):
+ *     gy_i = w_i * G / W,       gw_i = (y_i - z_i) * G / W.
+ *   g, y, z      [batch, n] (z the fit of y)
+ *   w            weights or NULL (unit; then W is the block's length and gw must be NULL)
+ *   block_start  [batch, n] block starts written by iso_fit_ex for this y, w (required; blocks
+ *                are not re-derived from z, since distinct means can round to equal values)
+ *   gy           [batch, n] output (required)
+ *   gw           [batch, n] output or NULL
+ * Sums are taken in fp64 without atomics.  Returns ISO_OK, ISO_EINVAL or ISO_EHIP.
+ */
+int iso_vjp(const void* g, const void* y, const void* w, const void* z,
+            const uint8_t* block_start, void* gy, void* gw, int64_t batch, int64_t n, int dtype,
+            void* stream);
+
+/* iso_strerror -- static description of a return code. */
+const char* iso_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISO_MI355X_H */

@@ -1,0 +1,43 @@
+/*
+ * iso_profile.h -- per-stage GPU timing of iso_fit_ex calls (libiso_mi355x.so).
+ *
+ * "Merge Hulls Without Copying Vertices: GPU Isotonic Regression" reports the fit's time per
+ * stage (Section 7.5: chunk stage, merge levels, reconstruction, prefix sums).  These hooks give
+ * the same breakdown on the caller's stream with HIP events, so a benchmark can time the
+ * dominant kernel inside its own timed region.
+ *
+ * Stages: 0 chunk/row pass (k_wave), 1 chunk-start scan (2 launches), 2 merge levels
+ * (ceil(log2 m) launches), 3 ends, 4 fit.  Rows of at most 2048 elements run stage 0 only.
+ *
+ * While enabled, every iso_fit_ex call records one event before its first kernel and one after
+ * each stage, on its stream.  The state is process-global and not thread-safe: enable, run the
+ * calls to time, read, disable -- from one host thread.
+ */
+#ifndef ISO_MI355X_PROFILE_H
+#define ISO_MI355X_PROFILE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ISO_PROF_STAGES = 5 };
+
+/* Turn event recording on (1) or off (0).  Returns ISO_OK. */
+int iso_prof_enable(int on);
+
+/* Wait for the recorded events, add each stage's elapsed milliseconds and kernel launch count
+ * since the last reset into ms[0..4] and launches[0..4] (arrays of ISO_PROF_STAGES entries
+ * owned by the caller), store the number of timed calls in *calls, then forget the events.
+ * Returns ISO_OK or ISO_EHIP. */
+int iso_prof_read(double* ms, int64_t* launches, int64_t* calls);
+
+/* Static name of a stage ("wave", "scan", "merge", "ends", "fit"), or "?". */
+const char* iso_prof_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISO_MI355X_PROFILE_H */

@@ -1,0 +1,120 @@
+"""The C-ABI library loads and exports every entry point include/iso.h declares; argument
+errors are reported before anything touches a GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from weighted_isotonic_regression_amd import binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iso.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
+
+
+def _declared(paths=(HEADER,)):
+    names = set()
+    for p in paths:
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(iso_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def _header_enums():
+    text = open(HEADER).read()
+    return {k: int(v.rstrip("u")) for k, v in re.findall(r"\b(ISO_[A-Z0-9_]+)\s*=\s*([0-9]+u?)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB):
+        build.build()
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    assert set(_declared()) == {"iso_fit", "iso_workspace_bytes", "iso_fit_ex", "iso_vjp", "iso_strerror"}
+    names = _declared(HEADERS)
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (iso_\w+)", out))
+    for name in names:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_constants_match_binding():
+    e = _header_enums()
+    assert e["ISO_F32"] == binding.ISO_F32 and e["ISO_F64"] == binding.ISO_F64
+    assert e["ISO_OK"] == binding.ISO_OK and e["ISO_EINVAL"] == binding.ISO_EINVAL
+    assert e["ISO_EWEIGHT"] == binding.ISO_EWEIGHT and e["ISO_ENOMEM"] == binding.ISO_ENOMEM
+    assert e["ISO_EHIP"] == binding.ISO_EHIP
+    assert e["ISO_FLAG_CHECK_WEIGHTS"] == binding.ISO_FLAG_CHECK_WEIGHTS
+    assert e["ISO_ROW_NONFINITE"] == binding.ISO_ROW_NONFINITE
+    assert e["ISO_ROW_BAD_WEIGHT"] == binding.ISO_ROW_BAD_WEIGHT
+
+
+def test_strerror(lib):
+    for code in range(5):
+        assert binding.iso_strerror(code)
+    assert "unknown" in binding.iso_strerror(99)
+
+
+P = ctypes.c_void_p
+Y, Z, W = P(1 << 20), P(1 << 30), P(1 << 34)
+
+
+def test_argument_errors_before_any_launch(lib):
+    fx = binding.iso_fit_ex
+    EINVAL, OK = binding.ISO_EINVAL, binding.ISO_OK
+    assert fx(None, None, Z, None, None, 1, 10, 0, None, 0, 0, None) == EINVAL      # y NULL
+    assert fx(Y, None, None, None, None, 1, 10, 0, None, 0, 0, None) == EINVAL      # z NULL
+    assert fx(Y, None, Z, None, None, -1, 10, 0, None, 0, 0, None) == EINVAL        # negative batch
+    assert fx(Y, None, Z, None, None, 1, -5, 0, None, 0, 0, None) == EINVAL         # negative n
+    assert fx(Y, None, Z, None, None, 1, 10, 7, None, 0, 0, None) == EINVAL         # bad dtype
+    assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 8, None) == EINVAL         # unknown flag
+    assert fx(Y, None, Y, None, None, 1, 10, 0, None, 0, 0, None) == EINVAL         # z aliases y
+    assert fx(Y, W, W, None, None, 1, 10, 1, None, 0, 0, None) == EINVAL            # z aliases w
+    assert fx(Y, None, P(Y.value + 8), None, None, 1, 10, 0, None, 0, 0, None) == EINVAL  # overlap
+    assert fx(Y, None, Z, None, None, 1 << 40, 1 << 40, 0, None, 0, 0, None) == EINVAL  # overflow
+    # long rows need a workspace of iso_workspace_bytes, 256-byte aligned
+    need = binding.iso_workspace_bytes(1, 5000, 0, 0)
+    assert need > 0
+    assert fx(Y, None, Z, None, None, 1, 5000, 0, None, 0, 0, None) == EINVAL
+    assert fx(Y, None, Z, None, None, 1, 5000, 0, P(1 << 36), need - 1, 0, None) == EINVAL
+    assert fx(Y, None, Z, None, None, 1, 5000, 0, P((1 << 36) + 8), need, 0, None) == EINVAL
+    # the synchronous weight check needs the workspace too
+    assert fx(Y, W, Z, None, None, 1, 10, 0, None, 0, 1, None) == EINVAL
+    # empty problems succeed without launching anything
+    assert fx(Y, None, Z, None, None, 0, 10, 0, None, 0, 0, None) == OK
+    assert fx(Y, None, Z, None, None, 4, 0, 1, None, 0, 0, None) == OK
+    assert binding.iso_fit(Y, None, Z, 0, 5, 0, None) == OK
+    assert binding.iso_fit(None, None, Z, 1, 5, 0, None) == EINVAL
+
+
+def test_vjp_argument_errors(lib):
+    vj = binding.iso_vjp
+    EINVAL = binding.ISO_EINVAL
+    G, B, GY, GW = P(1 << 22), P(1 << 24), P(1 << 26), P(1 << 28)
+    assert vj(G, Y, None, Z, B, GY, GW, 1, 10, 0, None) == EINVAL      # gw without w
+    assert vj(G, Y, W, Z, None, GY, GW, 1, 10, 0, None) == EINVAL      # no block starts
+    assert vj(G, Y, W, Z, B, None, GW, 1, 10, 0, None) == EINVAL       # no gy
+    assert vj(G, Y, W, Z, B, G, GW, 1, 10, 0, None) == EINVAL          # gy aliases g
+    assert vj(G, Y, W, Z, B, GY, GY, 1, 10, 0, None) == EINVAL         # gy aliases gw
+    assert vj(G, Y, W, Z, B, GY, GW, 1, 10, 5, None) == EINVAL         # bad dtype
+    assert vj(G, Y, W, Z, B, GY, GW, 0, 10, 0, None) == binding.ISO_OK
+
+
+def test_workspace_sizes(lib):
+    ws = binding.iso_workspace_bytes
+    assert ws(0, 10, 0, 0) == 0 and ws(3, 0, 0, 0) == 0
+    assert ws(-1, 10, 0, 0) == 0 and ws(1, 10, 9, 0) == 0
+    short = ws(65536, 16, 0, 1)
+    assert 65536 * 4 <= short < 65536 * 4 + 4096
+    # long rows: the vertex slots dominate, about 18 bytes per element
+    big = ws(1, 10 ** 8, 0, 1)
+    assert 15 * 10 ** 8 < big < 22 * 10 ** 8

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP fit against the CPU oracle, element by element, through the C ABI.
+
+Bars: max |z - z*| / (1 + |z*|) <= 1e-10 for fp64 and <= 1e-6 for fp32 (z* the oracle's fp64
+fit of the same stored inputs); identical block starts on integer-valued inputs; every output
+also passes the KKT certificate.  Sizes span several chunks of 2048 with ragged tails, and the
+full measured shapes are run too.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import exact
+from weighted_isotonic_regression_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {np.float32: 1e-6, np.float64: 1e-10}
+
+
+def _gpu():
+    from weighted_isotonic_regression_amd import binding
+
+    binding.load()
+    return binding
+
+
+def gpu_fit(y, w, **kw):
+    b = _gpu()
+    yt = torch.from_numpy(np.ascontiguousarray(y)).cuda()
+    wt = None if w is None else torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    res = b.fit(yt, wt, block_starts=True, row_flags=True, **kw)
+    torch.cuda.synchronize()
+    z, bs, rf = res
+    return z.cpu().numpy(), bs.cpu().numpy(), rf.cpu().numpy()
+
+
+def deviation(z, zo):
+    z = z.astype(np.float64)
+    return float(np.max(np.abs(z - zo) / (1 + np.abs(zo)))) if z.size else 0.0
+
+
+def check(y, w, exact_partition=False, tol=None, kkt=True):
+    t = y.dtype.type
+    z, bs, rf = gpu_fit(y, w)
+    zo, bo, fo = oracle.pav(y.astype(np.float64), None if w is None else w.astype(np.float64),
+                            return_blocks=True)
+    zo = zo.reshape(y.shape)
+    bo = bo.reshape(y.shape)
+    assert np.array_equal(rf.astype(np.uint32), fo)
+    dev = deviation(z, zo)
+    assert dev <= (tol or TOL[t]), dev
+    if exact_partition:
+        assert np.array_equal(bs, bo)
+    if kkt and y.ndim == 2 and y.shape[1] <= 300_000:
+        for r in range(min(y.shape[0], 3)):
+            assert exact.kkt_residual(y[r], None if w is None else w[r], z[r]) < (1e-12 if t == np.float64 else 1e-6)
+    return z, bs
+
+
+SIZES = [1, 2, 3, 17, 31, 32, 33, 63, 64, 65, 100, 511, 1000, 1024, 1025, 2047, 2048, 2049, 4095, 4096,
+         4097, 6145, 10000, 65536, 200001]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("n", SIZES)
+def test_noise_sizes(n, dtype):
+    batch = 3 if n < 100000 else 1
+    for wk in ("unit", "uniform"):
+        y, w = W.family("noise", batch, n, seed=n, dtype=dtype, wkind=wk)
+        check(y, None if wk == "unit" else w)
+
+
+@pytest.mark.parametrize("fam", W.FAMILIES)
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_families(fam, dtype):
+    for n in (700, 5000, 70001):
+        for wk in ("unit", "uniform", "integer"):
+            y, w = W.family(fam, 2, n, seed=n + 1, dtype=dtype, wkind=wk)
+            w_ = None if wk == "unit" else w
+            # the cancellation family's scale is max|y| (the page's Section 7.6 measures it so)
+            tol = None
+            if fam == "cancel":
+                tol = (1e-15 if dtype == "f64" else 1e-7) * float(np.max(np.abs(y)))
+            check(y, w_, exact_partition=(fam in ("integer", "constant") and wk != "uniform"), tol=tol,
+                  kkt=fam != "cancel")
+
+
+@pytest.mark.parametrize("n", [5, 64, 2048, 2049, 40000])
+def test_integer_partitions_exact(n):
+    y, w = W.family("integer", 4, n, seed=3, dtype="f32", wkind="integer")
+    check(y, w, exact_partition=True)
+    y, w = W.calibration(seed=9, batch=2, n=n)
+    check(y, w, exact_partition=True)
+
+
+def test_config_ramp_noise_4096():
+    y, w = W.ramp_noise_4096()
+    check(y, w)
+    check(y, None)
+
+
+def test_config_short_rows_16():
+    y, w = W.short_rows_16()
+    check(y, w)
+    check(y, None)
+
+
+def test_config_calibration_full():
+    y, w = W.calibration()
+    check(y, w, exact_partition=True, kkt=False)
+
+
+def test_config_nearly_monotone_1e7():
+    y, w = W.nearly_monotone_1e7()
+    assert np.all(np.diff(y[0]) > 0)
+    for ww in (w, None):
+        z, bs = check(y, ww, kkt=False)
+        assert bs.all()  # every element its own block
+
+
+def test_config_mixed_1e8():
+    y, w = W.mixed_1e8()
+    check(y, w, kkt=False)
+
+
+def test_nearly_monotone_1e8_fp64():
+    y, w = W.nearly_monotone_1e8()
+    z, bs = check(y, None, kkt=False)
+    assert bs.all()
+
+
+def test_bad_rows_flagged_and_others_fitted():
+    b = _gpu()
+    for n in (10, 3000):
+        y, w = W.family("noise", 5, n, seed=2, dtype="f64", wkind="uniform")
+        y[1, n // 2] = np.nan
+        w[3, n - 1] = -1.0
+        w[4, 0] = np.inf
+        z, bs, rf = gpu_fit(y, w)
+        assert list(rf) == [0, b.ISO_ROW_NONFINITE, 0, b.ISO_ROW_BAD_WEIGHT, b.ISO_ROW_NONFINITE]
+        for r in (1, 3, 4):
+            assert np.all(np.isnan(z[r])) and bs[r].sum() == 0
+        for r in (0, 2):
+            assert deviation(z[r], oracle.pav(y[r], w[r])) <= 1e-10
+        yt = torch.from_numpy(y).cuda()
+        wt = torch.from_numpy(w).cuda()
+        with pytest.raises(b.IsoError) as ei:
+            b.fit(yt, wt, check_weights=True)
+        assert ei.value.code == b.ISO_EWEIGHT
+        # through the simple entry point: weighted calls check
+        zt = torch.empty_like(yt)
+        import ctypes
+
+        rc = b.iso_fit(ctypes.c_void_p(yt.data_ptr()), ctypes.c_void_p(wt.data_ptr()),
+                       ctypes.c_void_p(zt.data_ptr()), 5, n, b.ISO_F64,
+                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == b.ISO_EWEIGHT
+
+
+def test_simple_entry_point_matches():
+    import ctypes
+
+    b = _gpu()
+    for n in (16, 5000):
+        y, w = W.family("sawtooth", 3, n, seed=4, dtype="f32", wkind="uniform")
+        yt, wt = torch.from_numpy(y).cuda(), torch.from_numpy(w).cuda()
+        zt = torch.empty_like(yt)
+        rc = b.iso_fit(ctypes.c_void_p(yt.data_ptr()), ctypes.c_void_p(wt.data_ptr()),
+                       ctypes.c_void_p(zt.data_ptr()), 3, n, b.ISO_F32,
+                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0
+        torch.cuda.synchronize()
+        z2 = b.fit(yt, wt)
+        assert torch.equal(zt, z2)
+
+
+def test_deterministic_repeat():
+    b = _gpu()
+    y, w = W.family("sawtooth", 2, 300000, seed=5, dtype="f64", wkind="uniform")
+    yt, wt = torch.from_numpy(y).cuda(), torch.from_numpy(w).cuda()
+    z1, s1 = b.fit(yt, wt, block_starts=True)
+    z2, s2 = b.fit(yt, wt, block_starts=True)
+    assert torch.equal(z1, z2) and torch.equal(s1, s2)
+
+
+def test_empty_and_tiny():
+    b = _gpu()
+    y = torch.empty((0, 7), dtype=torch.float32, device="cuda")
+    assert b.fit(y).shape == (0, 7)
+    y = torch.empty((3, 0), dtype=torch.float64, device="cuda")
+    assert b.fit(y).shape == (3, 0)
+    y = torch.tensor([[2.5], [-1.0]], dtype=torch.float64, device="cuda")
+    assert torch.equal(b.fit(y), y)

@@ -1,0 +1,209 @@
+"""Thin ctypes binding of the C ABI in include/iso.h (argument marshalling only).
+
+The raw functions keep the C names and signatures (device pointers as ints, stream as an
+int handle).  ``fit`` and ``vjp`` marshal torch tensors: they check shapes, dtypes and
+devices, allocate outputs and the workspace with torch, and pass torch's current stream.
+Every step of the fit runs in the HIP library; if the library is not built, or no GPU is
+present, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import build as _build
+
+ISO_F32, ISO_F64 = 0, 1
+ISO_OK, ISO_EINVAL, ISO_EWEIGHT, ISO_ENOMEM, ISO_EHIP = 0, 1, 2, 3, 4
+ISO_FLAG_CHECK_WEIGHTS = 1
+ISO_ROW_NONFINITE, ISO_ROW_BAD_WEIGHT = 1, 2
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGS = {
+    "iso_fit": ([_P, _P, _P, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
+    "iso_workspace_bytes": ([_I64, _I64, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
+    "iso_fit_ex": ([_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, ctypes.c_size_t, ctypes.c_uint, _P],
+                   ctypes.c_int),
+    "iso_vjp": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
+    "iso_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "iso_prof_enable": ([ctypes.c_int], ctypes.c_int),
+    "iso_prof_read": ([_P, _P, _P], ctypes.c_int),
+    "iso_prof_stage_name": ([ctypes.c_int], ctypes.c_char_p),
+}
+ISO_PROF_STAGES = 5
+
+
+class IsoError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (where, iso_strerror(code), code))
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """Load libiso_mi355x.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError("the HIP library %s is not built; run __graft_entry__.build()" % path)
+            lib = ctypes.CDLL(path)
+            for name, (args, res) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------------------ raw C ABI
+
+def iso_fit(y, w, z, batch, n, dtype, stream):
+    return load().iso_fit(y, w, z, batch, n, dtype, stream)
+
+
+def iso_workspace_bytes(batch, n, dtype, weighted):
+    return load().iso_workspace_bytes(batch, n, dtype, int(bool(weighted)))
+
+
+def iso_fit_ex(y, w, z, block_start, row_flags, batch, n, dtype, ws, ws_bytes, flags, stream):
+    return load().iso_fit_ex(y, w, z, block_start, row_flags, batch, n, dtype, ws, ws_bytes, flags, stream)
+
+
+def iso_vjp(g, y, w, z, block_start, gy, gw, batch, n, dtype, stream):
+    return load().iso_vjp(g, y, w, z, block_start, gy, gw, batch, n, dtype, stream)
+
+
+def iso_strerror(code):
+    return load().iso_strerror(code).decode()
+
+
+def iso_prof_enable(on):
+    return load().iso_prof_enable(int(bool(on)))
+
+
+def iso_prof_read():
+    """Returns ({stage name: ms}, {stage name: launches}, calls) accumulated since the last read."""
+    ms = (ctypes.c_double * ISO_PROF_STAGES)()
+    la = (ctypes.c_int64 * ISO_PROF_STAGES)()
+    calls = ctypes.c_int64(0)
+    rc = load().iso_prof_read(ms, la, ctypes.byref(calls))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_prof_read")
+    names = [load().iso_prof_stage_name(k).decode() for k in range(ISO_PROF_STAGES)]
+    return dict(zip(names, list(ms))), dict(zip(names, list(la))), calls.value
+
+
+# ------------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU: the isotonic fit runs only on the HIP device")
+    return torch
+
+
+def _dtype_code(torch, t):
+    if t.dtype == torch.float32:
+        return ISO_F32
+    if t.dtype == torch.float64:
+        return ISO_F64
+    raise TypeError("y must be float32 or float64")
+
+
+def _as_rows(t):
+    if t.dim() == 1:
+        return t.reshape(1, -1)
+    if t.dim() != 2:
+        raise ValueError("expected a row [n] or a batch of rows [batch, n]")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace(batch, n, dtype_code, weighted, device):
+    """A torch uint8 buffer of iso_workspace_bytes, 256-byte aligned (None if none is needed)."""
+    torch = _torch()
+    nbytes = iso_workspace_bytes(batch, n, dtype_code, weighted)
+    if nbytes == 0:
+        return None, 0
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    shift = (-buf.data_ptr()) % 256
+    return buf[shift:shift + nbytes], nbytes
+
+
+def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, out=None, ws=None):
+    """Isotonic (non-decreasing) weighted L2 fit of every row of ``y`` on its device.
+
+    y: float32/float64 CUDA tensor [n] or [batch, n]; w: same shape and dtype, or None.
+    Returns z, or (z, block_start[uint8], row_flags[int32]) as requested.
+    """
+    torch = _torch()
+    y2 = _as_rows(y)
+    if not y2.is_cuda or not y2.is_contiguous():
+        raise ValueError("y must be a contiguous tensor on the GPU")
+    code = _dtype_code(torch, y2)
+    w2 = None
+    if w is not None:
+        w2 = _as_rows(w)
+        if w2.shape != y2.shape or w2.dtype != y2.dtype or w2.device != y2.device or not w2.is_contiguous():
+            raise ValueError("w must be a contiguous tensor of y's shape, dtype and device")
+    batch, n = y2.shape
+    z = torch.empty_like(y2) if out is None else _as_rows(out)
+    bs = torch.empty((batch, n), dtype=torch.uint8, device=y2.device) if block_starts else None
+    rf = torch.empty((batch,), dtype=torch.int32, device=y2.device) if row_flags else None
+    if ws is None:
+        ws, nbytes = workspace(batch, n, code, w2 is not None, y2.device)
+    else:
+        nbytes = ws.numel()
+    flags = ISO_FLAG_CHECK_WEIGHTS if check_weights else 0
+    rc = iso_fit_ex(_ptr(y2), _ptr(w2), _ptr(z), _ptr(bs), _ptr(rf), batch, n, code, _ptr(ws), nbytes, flags,
+                    _stream(torch, y2.device))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_fit_ex")
+    z = z.reshape(y.shape)
+    if not block_starts and not row_flags:
+        return z
+    res = [z]
+    if block_starts:
+        res.append(bs.reshape(y.shape))
+    if row_flags:
+        res.append(rf)
+    return tuple(res)
+
+
+def vjp(g, y, w, z, block_start):
+    """Backward of the fit: returns (gy, gw) (gw is None when w is None)."""
+    torch = _torch()
+    g2, y2, z2, b2 = _as_rows(g), _as_rows(y), _as_rows(z), _as_rows(block_start)
+    code = _dtype_code(torch, y2)
+    for t in (g2, z2):
+        if t.shape != y2.shape or t.dtype != y2.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("g and z must match y")
+    if b2.shape != y2.shape or b2.dtype != torch.uint8 or not b2.is_contiguous():
+        raise ValueError("block_start must be a contiguous uint8 tensor of y's shape")
+    w2 = None if w is None else _as_rows(w)
+    batch, n = y2.shape
+    gy = torch.empty_like(y2)
+    gw = None if w2 is None else torch.empty_like(y2)
+    rc = iso_vjp(_ptr(g2), _ptr(y2), _ptr(w2), _ptr(z2), _ptr(b2), _ptr(gy), _ptr(gw), batch, n, code,
+                 _stream(torch, y2.device))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_vjp")
+    return gy.reshape(y.shape), (None if gw is None else gw.reshape(y.shape))

@@ -1,0 +1,56 @@
+"""Build step of the HIP library: compiles csrc/iso_api.hip for gfx950 into
+``weighted_isotonic_regression_amd/_build/libiso_mi355x.so`` with hipcc.
+
+Flags: -O3, C++17, no floating-point contraction (products and sums round exactly where the
+source says so; explicit fma() calls stay fused), and no packed fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "iso_api.hip")
+DEPS = [os.path.join(HERE, "csrc", f) for f in ("iso_geom.h", "iso_kernels.h")] + [
+    os.path.join(ROOT, "include", "iso.h")]
+OUT_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(OUT_DIR, "libiso_mi355x.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found")
+    return path
+
+
+def command(out: str = LIB, extra=()):
+    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), *extra, "-o", out, SRC]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always) and return its path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(p) > t for p in [SRC] + DEPS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

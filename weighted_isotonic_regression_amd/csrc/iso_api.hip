@@ -1,0 +1,351 @@
+// iso_api.hip -- the C ABI of include/iso.h: argument checks, workspace layout and launches.
+//
+// Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
+//   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
+//               launch of k_wave writes z, block starts and row flags (Section 3.5).
+//   n >  2048   rows split into chunks of 2048 (one wavefront each): k_wave (chunk hulls),
+//               k_scan_reduce + k_scan_apply (chunk starts), ceil(log2 m) launches of
+//               k_merge_level, k_ends, k_fit (Section 3.3 and 3.4).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/iso.h"
+#include "../../include/iso_profile.h"
+#include "iso_kernels.h"
+
+static_assert(iso::ISO_ROW_NONFINITE_BIT == ISO_ROW_NONFINITE, "flag bits");
+static_assert(iso::ISO_ROW_BAD_WEIGHT_BIT == ISO_ROW_BAD_WEIGHT, "flag bits");
+
+namespace {
+
+using namespace iso;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t total = 0;
+  size_t o_rflags = 0, o_any = 0;
+  // long rows only
+  size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_vk = 0, o_vx = 0,
+         o_vy = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
+  int64_t m = 0, nblk = 0;
+};
+
+bool long_rows(int64_t n) { return n > kChunk; }
+
+Layout make_layout(int64_t batch, int64_t n) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.o_rflags = take((size_t)batch * sizeof(uint32_t));
+  L.o_any = take(sizeof(uint32_t));
+  if (long_rows(n)) {
+    L.m = (n + kChunk - 1) / kChunk;
+    L.nblk = (L.m + kScanBlock - 1) / kScanBlock;
+    const size_t G = (size_t)batch * (size_t)L.m;
+    L.o_tot = take(G * sizeof(double2));
+    L.o_start = take(G * sizeof(double4));
+    L.o_nv = take(G * sizeof(int));
+    L.o_cf = take(G * sizeof(uint32_t));
+    L.o_desc = take(G * sizeof(Desc));
+    L.o_nseg = take(G * sizeof(int));
+    L.o_vk = take(G * (size_t)kSlot * sizeof(uint16_t));
+    L.o_vx = take(G * (size_t)kSlot * sizeof(double));
+    L.o_vy = take(G * (size_t)kSlot * sizeof(double));
+    L.o_ends = take(G * sizeof(EndInfo));
+    L.o_bsum = take((size_t)batch * (size_t)L.nblk * sizeof(double4));
+    L.o_bflag = take((size_t)batch * (size_t)L.nblk * sizeof(uint32_t));
+  }
+  L.total = off;
+  return L;
+}
+
+bool shape_ok(int64_t batch, int64_t n, int dtype) {
+  if (batch < 0 || n < 0) return false;
+  if (dtype != ISO_F32 && dtype != ISO_F64) return false;
+  if (batch > 0 && n > INT64_MAX / 16 / batch) return false;  // element and byte counts fit
+  if (long_rows(n)) {
+    const int64_t m = (n + kChunk - 1) / kChunk;
+    if (batch > 0 && m > (int64_t)INT32_MAX / batch) return false;  // one launch block per chunk
+  } else if (batch > (int64_t)INT32_MAX) {
+    return false;
+  }
+  return true;
+}
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b || abytes == 0 || bbytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// ---- per-stage event timing (iso_profile.h)
+struct ProfCall {
+  hipEvent_t ev[ISO_PROF_STAGES + 1];
+  int launches[ISO_PROF_STAGES];
+  int marks;
+};
+bool g_prof_on = false;
+std::vector<ProfCall> g_prof_calls;
+
+// Records an event before the first kernel and after each stage of one call.
+struct Prof {
+  bool on;
+  hipStream_t s;
+  ProfCall c;
+  explicit Prof(hipStream_t st) : on(g_prof_on), s(st) {
+    c.marks = 0;
+    for (int k = 0; k < ISO_PROF_STAGES; ++k) c.launches[k] = 0;
+    if (on) mark(0);
+  }
+  void mark(int launches) {
+    if (!on) return;
+    if (c.marks > 0) c.launches[c.marks - 1] = launches;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      on = false;
+      return;
+    }
+    if (hipEventRecord(e, s) != hipSuccess) {
+      (void)hipEventDestroy(e);
+      on = false;
+      return;
+    }
+    c.ev[c.marks++] = e;
+  }
+  ~Prof() {
+    if (on && c.marks > 1) g_prof_calls.push_back(c);
+  }
+};
+
+int lanes_per_row(int64_t n) {
+  int need = (int)((n + kLanePts - 1) / kLanePts);
+  int L = 1;
+  while (L < need) L <<= 1;
+  return L;
+}
+
+template <typename T, bool W>
+int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int64_t batch,
+            int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
+  Prof prof(s);
+  if (!long_rows(n)) {
+    const int L = lanes_per_row(n);
+    const int R = kWave / L;
+    const int64_t tiles = (batch + R - 1) / R;
+    hipLaunchKernelGGL((k_wave<T, W, false>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z,
+                       bstart, rflags, batch, n, 0, L, ChunkOut{});
+    prof.mark(1);
+    return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
+  }
+  const int m = (int)Lay.m;
+  const int nblk = (int)Lay.nblk;
+  const int64_t G = batch * (int64_t)m;
+  ChunkOut co;
+  co.tot = (double2*)(ws + Lay.o_tot);
+  co.nverts = (int*)(ws + Lay.o_nv);
+  co.cflags = (uint32_t*)(ws + Lay.o_cf);
+  co.desc = (Desc*)(ws + Lay.o_desc);
+  co.nseg = (int*)(ws + Lay.o_nseg);
+  co.vk = (uint16_t*)(ws + Lay.o_vk);
+  co.vx = (double*)(ws + Lay.o_vx);
+  co.vy = (double*)(ws + Lay.o_vy);
+  double4* start = (double4*)(ws + Lay.o_start);
+  double4* bsum = (double4*)(ws + Lay.o_bsum);
+  uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
+  EndInfo* ends = (EndInfo*)(ws + Lay.o_ends);
+
+  hipLaunchKernelGGL((k_wave<T, W, true>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, bstart,
+                     rflags, batch, n, m, kWave, co);
+  prof.mark(1);
+  hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0,
+                     s, co.tot, co.cflags, bsum, bflag, m, nblk);
+  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0, s,
+                     co.tot, bsum, bflag, start, rflags, m, nblk);
+  prof.mark(2);
+  MergeArrays Ar{co.desc, co.nseg, co.vx, co.vy, co.vk, start};
+  int levels = 0;
+  for (int r = 0; (1 << r) < m; ++r) {
+    ++levels;
+    const int span = 1 << (r + 1);
+    const int per_row = (m - (1 << r) + span - 1) / span;
+    const int64_t merges = batch * (int64_t)per_row;
+    const int64_t blocks = (merges + 255) / 256;
+    hipLaunchKernelGGL(k_merge_level, dim3((unsigned)blocks), dim3(256), 0, s, Ar, batch, m, r,
+                       per_row);
+  }
+  prof.mark(levels);
+  hipLaunchKernelGGL(k_ends, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, Ar,
+                     (const int*)co.nverts, ends, batch, m);
+  prof.mark(1);
+  hipLaunchKernelGGL((k_fit<T>), dim3((unsigned)G), dim3(kWave), 0, s, (const double*)co.vx,
+                     (const double*)co.vy, (const uint16_t*)co.vk, (const EndInfo*)ends,
+                     (const uint32_t*)rflags, z, bstart, n, m);
+  prof.mark(1);
+  return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
+}
+
+template <typename T>
+int dispatch_fit(const void* y, const void* w, void* z, uint8_t* bstart, uint32_t* rflags,
+                 int64_t batch, int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
+  if (w)
+    return run_fit<T, true>((const T*)y, (const T*)w, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
+  return run_fit<T, false>((const T*)y, nullptr, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int iso_prof_enable(int on) {
+  g_prof_on = on != 0;
+  return ISO_OK;
+}
+
+int iso_prof_read(double* ms, int64_t* launches, int64_t* calls) {
+  int rc = ISO_OK;
+  for (ProfCall& c : g_prof_calls) {
+    if (hipEventSynchronize(c.ev[c.marks - 1]) != hipSuccess) rc = ISO_EHIP;
+    for (int k = 0; k + 1 < c.marks; ++k) {
+      float t = 0.0f;
+      if (hipEventElapsedTime(&t, c.ev[k], c.ev[k + 1]) != hipSuccess) rc = ISO_EHIP;
+      if (ms) ms[k] += (double)t;
+      if (launches) launches[k] += c.launches[k];
+    }
+    for (int k = 0; k < c.marks; ++k) (void)hipEventDestroy(c.ev[k]);
+  }
+  if (calls) *calls += (int64_t)g_prof_calls.size();
+  g_prof_calls.clear();
+  return rc;
+}
+
+const char* iso_prof_stage_name(int stage) {
+  static const char* names[ISO_PROF_STAGES] = {"wave", "scan", "merge", "ends", "fit"};
+  return (stage >= 0 && stage < ISO_PROF_STAGES) ? names[stage] : "?";
+}
+
+const char* iso_strerror(int code) {
+  switch (code) {
+    case ISO_OK: return "ok";
+    case ISO_EINVAL: return "invalid argument";
+    case ISO_EWEIGHT: return "a row holds a weight <= 0";
+    case ISO_ENOMEM: return "device allocation failed";
+    case ISO_EHIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+size_t iso_workspace_bytes(int64_t batch, int64_t n, int dtype, int weighted) {
+  (void)weighted;
+  if (!shape_ok(batch, n, dtype) || batch == 0 || n == 0) return 0;
+  return make_layout(batch, n).total;
+}
+
+int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,
+               int64_t batch, int64_t n, int dtype, void* ws, size_t ws_bytes, unsigned flags,
+               void* stream) {
+  if (!shape_ok(batch, n, dtype)) return ISO_EINVAL;
+  if (flags & ~(unsigned)ISO_FLAG_CHECK_WEIGHTS) return ISO_EINVAL;
+  if (batch == 0 || n == 0) return ISO_OK;
+  if (!y || !z) return ISO_EINVAL;
+  const size_t esz = dtype == ISO_F64 ? 8 : 4;
+  const size_t bytes = (size_t)batch * (size_t)n * esz;
+  if (overlaps(z, bytes, y, bytes) || overlaps(z, bytes, w, bytes)) return ISO_EINVAL;
+  if (overlaps(block_start, (size_t)batch * (size_t)n, z, bytes)) return ISO_EINVAL;
+  const Layout Lay = make_layout(batch, n);
+  const bool need_ws = long_rows(n) || (flags & ISO_FLAG_CHECK_WEIGHTS) || false;
+  if (need_ws) {
+    if (!ws || ws_bytes < Lay.total || ((uintptr_t)ws % kAlign) != 0) return ISO_EINVAL;
+  }
+  char* wsb = (char*)ws;
+  uint32_t* rflags = row_flags;
+  if (!rflags && need_ws) rflags = (uint32_t*)(wsb + Lay.o_rflags);
+  hipStream_t s = (hipStream_t)stream;
+  int rc = dtype == ISO_F64
+               ? dispatch_fit<double>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s)
+               : dispatch_fit<float>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s);
+  if (rc != ISO_OK) return rc;
+  if (flags & ISO_FLAG_CHECK_WEIGHTS) {
+    uint32_t* any = (uint32_t*)(wsb + Lay.o_any);
+    hipLaunchKernelGGL(k_flags_any, dim3(1), dim3(256), 0, s, (const uint32_t*)rflags, batch, any);
+    if (hipGetLastError() != hipSuccess) return ISO_EHIP;
+    uint32_t host = 0;
+    if (hipMemcpyAsync(&host, any, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return ISO_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return ISO_EHIP;
+    if (host & ISO_ROW_BAD_WEIGHT) return ISO_EWEIGHT;
+  }
+  return ISO_OK;
+}
+
+int iso_fit(const void* y, const void* w, void* z, int64_t batch, int64_t n, int dtype,
+            void* stream) {
+  if (!shape_ok(batch, n, dtype)) return ISO_EINVAL;
+  if (batch == 0 || n == 0) return ISO_OK;
+  if (!y || !z) return ISO_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned flags = w ? (unsigned)ISO_FLAG_CHECK_WEIGHTS : 0u;
+  const size_t need = make_layout(batch, n).total;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, need, s) != hipSuccess) return ISO_ENOMEM;
+  int rc = iso_fit_ex(y, w, z, nullptr, nullptr, batch, n, dtype, ws, need, flags, stream);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == ISO_OK) rc = ISO_EHIP;
+  return rc;
+}
+
+int iso_vjp(const void* g, const void* y, const void* w, const void* z,
+            const uint8_t* block_start, void* gy, void* gw, int64_t batch, int64_t n, int dtype,
+            void* stream) {
+  if (!shape_ok(batch, n, dtype)) return ISO_EINVAL;
+  if (batch == 0 || n == 0) return ISO_OK;
+  if (!g || !y || !z || !block_start || !gy) return ISO_EINVAL;
+  if (!w && gw) return ISO_EINVAL;
+  const size_t esz = dtype == ISO_F64 ? 8 : 4;
+  const size_t bytes = (size_t)batch * (size_t)n * esz;
+  const void* ins[5] = {g, y, w, z, block_start};
+  const size_t insz[5] = {bytes, bytes, bytes, bytes, (size_t)batch * (size_t)n};
+  for (int k = 0; k < 5; ++k) {
+    if (overlaps(gy, bytes, ins[k], insz[k]) || overlaps(gw, bytes, ins[k], insz[k])) return ISO_EINVAL;
+  }
+  if (overlaps(gy, bytes, gw, bytes)) return ISO_EINVAL;
+  const int64_t ntile = (n + kChunk - 1) / kChunk;
+  if (batch * ntile > (int64_t)INT32_MAX) return ISO_EINVAL;
+  const int64_t T = batch * ntile;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t tb = align_up((size_t)T * sizeof(VjpTile));
+  void* buf = nullptr;
+  if (hipMallocAsync(&buf, tb + (size_t)T * sizeof(double4), s) != hipSuccess) return ISO_ENOMEM;
+  VjpTile* tiles = (VjpTile*)buf;
+  double4* cc = (double4*)((char*)buf + tb);
+  if (dtype == ISO_F64) {
+    hipLaunchKernelGGL((k_vjp_tiles<double>), dim3((unsigned)T), dim3(kWave), 0, s, (const double*)g,
+                       (const double*)w, block_start, n, (int)ntile, tiles);
+    hipLaunchKernelGGL(k_vjp_rows, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s,
+                       (const VjpTile*)tiles, batch, (int)ntile, cc);
+    hipLaunchKernelGGL((k_vjp_apply<double>), dim3((unsigned)T), dim3(kWave), 0, s, (const double*)g,
+                       (const double*)y, (const double*)w, (const double*)z, block_start,
+                       (const double4*)cc, (double*)gy, (double*)gw, n, (int)ntile);
+  } else {
+    hipLaunchKernelGGL((k_vjp_tiles<float>), dim3((unsigned)T), dim3(kWave), 0, s, (const float*)g,
+                       (const float*)w, block_start, n, (int)ntile, tiles);
+    hipLaunchKernelGGL(k_vjp_rows, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s,
+                       (const VjpTile*)tiles, batch, (int)ntile, cc);
+    hipLaunchKernelGGL((k_vjp_apply<float>), dim3((unsigned)T), dim3(kWave), 0, s, (const float*)g,
+                       (const float*)y, (const float*)w, (const float*)z, block_start,
+                       (const double4*)cc, (float*)gy, (float*)gw, n, (int)ntile);
+  }
+  int rc = hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
+  if (hipFreeAsync(buf, s) != hipSuccess && rc == ISO_OK) rc = ISO_EHIP;
+  return rc;
+}
+
+}  // extern "C"

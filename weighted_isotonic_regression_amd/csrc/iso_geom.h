@@ -1,0 +1,617 @@
+// iso_geom.h -- geometry of the cumulative sum diagram (CSD) shared by the HIP kernels.
+//
+// Everything here is __host__ __device__ and free of launch or memory-space assumptions:
+// points are read through accessor functors, so the kernels bind them to LDS or global memory.
+//
+// Source: "Merge Hulls Without Copying Vertices: GPU Isotonic Regression".
+//   Section 2.1  the fit is the slope sequence of the lower hull of the CSD; a point on the
+//                segment between its neighbours is not a vertex (turn == 0 means non-convex).
+//   Section 3.1  lane hulls by the monotone chain with the stack held in a bit mask.
+//   Section 3.2 / Lemma 4.2  two neighbouring hulls sharing their boundary point s merge along
+//                a unique bridge; walking from s finds it (left end moves left while its turn
+//                is not strictly left, right end moves right symmetrically).
+//   Section 3.3 / Definition 4.3 / Theorem 4.4  segment lists: a node's hull is a sequence of
+//                (chunk, first, last) ranges of chunk hulls, at most one per chunk; a merge
+//                cuts one segment of each child and moves the right child's tail down.
+//   Section 2.2 / 5.2  Overmars-van Leeuwen simultaneous bisection for the bridge of two
+//                x-separated hulls.  The page's case analysis (its Appendix A) did not survive,
+//                so the cases below are derived here from the slopes; see bridge_search().
+//   Section 6 "Coordinates"  chunk-relative coordinates plus double-double chunk starts, so
+//                that differences of nearby points keep their precision.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define ISO_HD __host__ __device__ __forceinline__
+
+namespace iso {
+
+constexpr int kWave = 64;                    // lanes of a wavefront
+constexpr int kLanePts = 32;                 // elements per lane
+constexpr int kChunk = kWave * kLanePts;     // elements per chunk (one wavefront)
+constexpr int kSlot = kChunk + 1;            // vertex slot capacity of a chunk (C + 1 points)
+constexpr int kWalkCap = 64;                 // walk steps of a merge before it switches to search
+
+// Per-row input flags (same values as ISO_ROW_NONFINITE / ISO_ROW_BAD_WEIGHT of iso.h).
+constexpr uint32_t ISO_ROW_NONFINITE_BIT = 1u;
+constexpr uint32_t ISO_ROW_BAD_WEIGHT_BIT = 2u;
+
+// ------------------------------------------------------------------ arithmetic
+
+// (ax, ay) x (bx, by) with one rounded product.
+ISO_HD double cross2(double ax, double ay, double bx, double by) { return fma(ax, by, -(ay * bx)); }
+
+struct DD {
+  double hi, lo;
+};
+
+ISO_HD DD two_sum(double a, double b) {
+  double s = a + b;
+  double bb = s - a;
+  double e = (a - (s - bb)) + (b - bb);
+  return {s, e};
+}
+
+ISO_HD DD quick_two_sum(double a, double b) {
+  double s = a + b;
+  double e = b - (s - a);
+  return {s, e};
+}
+
+// Double-double addition (accurate to about 2^-104 relative).
+ISO_HD DD dd_add(DD a, DD b) {
+  DD s = two_sum(a.hi, b.hi);
+  DD t = two_sum(a.lo, b.lo);
+  double e = s.lo + t.hi;
+  s = quick_two_sum(s.hi, e);
+  e = s.lo + t.lo;
+  return quick_two_sum(s.hi, e);
+}
+
+// Sign-exact comparison helper: sign of (a*b - c*d) for exactly representable factors whose
+// products may exceed 2^53 (used by the separator test of the bridge search).
+ISO_HD double diff_of_products(double a, double b, double c, double d) {
+  double p1 = a * b;
+  double e1 = fma(a, b, -p1);
+  double p2 = c * d;
+  double e2 = fma(c, d, -p2);
+  return (p1 - p2) + (e1 - e2);
+}
+
+// ------------------------------------------------------------------ lane hull
+
+// Monotone chain over the points 0..c of one lane (c <= 32), read through P(k, &x, &y).
+// Returns the hull as a bit mask (bit k set iff point k is a vertex).  A point is popped when
+// the turn (under, top, next) is <= 0, so collinear middle points are dropped.  Every iteration
+// either pops or pushes, and exactly one point load is issued per iteration.
+template <class PtFn>
+ISO_HD uint64_t lane_chain(int c, PtFn P) {
+  if (c <= 0) return 0;
+  if (c == 1) return 3ull;
+  uint64_t mask = 3ull;
+  int top = 1, und = 0, k = 2;
+  double ux, uy, tx, ty, kx, ky;
+  P(0, ux, uy);
+  P(1, tx, ty);
+  P(2, kx, ky);
+  // <= 2c iterations: each point is pushed once and popped at most once.
+  for (int it = 0; it < 2 * kLanePts + 2 && k <= c; ++it) {
+    double t = cross2(tx - ux, ty - uy, kx - ux, ky - uy);
+    bool pop = (top != 0) && (t <= 0.0);
+    int load_idx;
+    if (pop) {
+      mask &= ~(1ull << top);
+      top = und;
+      tx = ux;
+      ty = uy;
+      uint64_t below = mask & ((1ull << und) - 1ull);
+      und = below ? 63 - __builtin_clzll(below) : 0;
+      load_idx = und;
+    } else {
+      mask |= 1ull << k;
+      und = top;
+      ux = tx;
+      uy = ty;
+      top = k;
+      tx = kx;
+      ty = ky;
+      ++k;
+      load_idx = k <= c ? k : c;
+    }
+    double lx, ly;
+    P(load_idx, lx, ly);
+    if (pop) {
+      ux = lx;
+      uy = ly;
+    } else {
+      kx = lx;
+      ky = ly;
+    }
+  }
+  return mask;
+}
+
+// ------------------------------------------------------------------ bit-mask neighbours
+
+// Vertex sets of a tile are bit masks: point k is word k >> 5, bit k & 31.
+// Largest set bit strictly below k (one exists: the caller's node start is a vertex).
+ISO_HD int mask_pred(const uint32_t* M, int k) {
+  int u = k >> 5;
+  uint32_t m = M[u] & ((1u << (k & 31)) - 1u);
+  while (m == 0) m = M[--u];
+  return (u << 5) + 31 - __builtin_clz(m);
+}
+
+// Smallest set bit strictly above k (one exists: the caller's node end is a vertex).
+ISO_HD int mask_succ(const uint32_t* M, int k) {
+  int u = k >> 5;
+  int b = k & 31;
+  uint32_t m = (b == 31) ? 0u : (M[u] & ~((2u << b) - 1u));
+  while (m == 0) m = M[++u];
+  return (u << 5) + __builtin_ctz(m);
+}
+
+// Clears the bits strictly between a and b (a < b).  Words holding no bit of (a, b) are not
+// written, so merges of disjoint nodes never write the same word.
+ISO_HD void mask_clear_between(uint32_t* M, int a, int b) {
+  int ua = a >> 5, ub = b >> 5;
+  for (int u = ua; u <= ub; ++u) {
+    int lo = (u == ua) ? (a & 31) + 1 : 0;    // first bit to clear
+    int hi = (u == ub) ? (b & 31) : 32;       // one past the last
+    if (lo >= hi) continue;
+    uint32_t keep_lo = lo >= 32 ? 0xffffffffu : ((1u << lo) - 1u);
+    uint32_t keep_hi = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+    M[u] &= (keep_lo | keep_hi);
+  }
+}
+
+// Merge of two neighbouring nodes of one tile by walking (Lemma 4.2): node A spans points
+// [a0, s], node B spans [s, b1]; vertices are set bits of M, coordinates come from P.
+// The bridge (alpha, beta) is found with alpha the leftmost contact in A (s included) and beta
+// the rightmost contact in B \ {s}; the bits strictly between them are cleared.
+template <class PtFn>
+ISO_HD void tile_walk_merge(uint32_t* M, int a0, int s, int b1, PtFn P) {
+  int al = s;
+  int be = mask_succ(M, s);
+  double ax, ay, bx, by;
+  P(al, ax, ay);
+  P(be, bx, by);
+  // Each move removes a vertex of A or B, so the total number of moves is below b1 - a0.
+  for (int pass = 0; pass <= b1 - a0; ++pass) {
+    bool moved = false;
+    while (al != a0) {
+      int p = mask_pred(M, al);
+      double px, py;
+      P(p, px, py);
+      if (cross2(ax - px, ay - py, bx - px, by - py) <= 0.0) {
+        al = p;
+        ax = px;
+        ay = py;
+        moved = true;
+      } else {
+        break;
+      }
+    }
+    while (be != b1) {
+      int q = mask_succ(M, be);
+      double qx, qy;
+      P(q, qx, qy);
+      if (cross2(bx - ax, by - ay, qx - ax, qy - ay) <= 0.0) {
+        be = q;
+        bx = qx;
+        by = qy;
+        moved = true;
+      } else {
+        break;
+      }
+    }
+    if (!moved) break;
+  }
+  mask_clear_between(M, al, be);
+}
+
+// ------------------------------------------------------------------ segment lists
+
+// A point in row coordinates: chunk-relative (x, y) plus the chunk's double-double start.
+struct GPt {
+  double x, y;
+  double sxh, sxl, syh, syl;
+};
+
+// q - p with the coordinate hierarchy: the start difference first (exact for nearby chunks by
+// Sterbenz's lemma), then the local difference.  For two points of one chunk the starts cancel
+// to exactly zero and the result is the local difference.
+ISO_HD void gdiff(const GPt& p, const GPt& q, double& dx, double& dy) {
+  dx = ((q.sxh - p.sxh) + (q.sxl - p.sxl)) + (q.x - p.x);
+  dy = ((q.syh - p.syh) + (q.syl - p.syl)) + (q.y - p.y);
+}
+
+ISO_HD double gturn(const GPt& a, const GPt& b, const GPt& c) {
+  double dx1, dy1, dx2, dy2;
+  gdiff(a, b, dx1, dy1);
+  gdiff(a, c, dx2, dy2);
+  return cross2(dx1, dy1, dx2, dy2);
+}
+
+ISO_HD double gslope(const GPt& a, const GPt& b) {
+  double dx, dy;
+  gdiff(a, b, dx, dy);
+  return dy / dx;
+}
+
+// Segment descriptor: x = chunk index within the row, y = first vertex position, z = last
+// vertex position (positions index the chunk's vertex slot), w unused.
+using Desc = int4;
+
+// Device arrays of the merge phase.  Chunk g (global index row * m + j) owns:
+//   desc[g], nseg[g]            the descriptor slot and, for a node starting at g, its length
+//   vx/vy[g * kSlot + p]        chunk-relative coordinates of its hull vertex p
+//   vk[g * kSlot + p]           that vertex's point index within the chunk (0..C)
+//   start[g]                    {x hi, x lo, y hi, y lo} of the chunk's first point in the row
+struct MergeArrays {
+  Desc* desc;
+  int* nseg;
+  const double* vx;
+  const double* vy;
+  const uint16_t* vk;
+  const double4* start;
+};
+
+struct VRef {
+  int u;  // segment index within the node's list
+  int p;  // vertex position within that segment's chunk slot
+};
+
+ISO_HD bool vref_eq(VRef a, VRef b) { return a.u == b.u && a.p == b.p; }
+ISO_HD bool vref_le(VRef a, VRef b) { return a.u < b.u || (a.u == b.u && a.p <= b.p); }
+
+// A node's segment list: descriptors d[0..n) in global memory.
+struct NodeList {
+  const Desc* d;
+  int n;
+  int64_t rowbase;  // global index of the row's chunk 0
+};
+
+ISO_HD GPt load_pt(const MergeArrays& A, int64_t rowbase, int j, int p) {
+  int64_t g = rowbase + j;
+  int64_t idx = g * (int64_t)kSlot + p;
+  double4 s = A.start[g];
+  GPt r;
+  r.x = A.vx[idx];
+  r.y = A.vy[idx];
+  r.sxh = s.x;
+  r.sxl = s.y;
+  r.syh = s.z;
+  r.syl = s.w;
+  return r;
+}
+
+ISO_HD GPt load_v(const MergeArrays& A, const NodeList& L, VRef v) {
+  return load_pt(A, L.rowbase, L.d[v.u].x, v.p);
+}
+
+ISO_HD VRef list_first(const NodeList& L) { return {0, L.d[0].y}; }
+ISO_HD VRef list_last(const NodeList& L) { return {L.n - 1, L.d[L.n - 1].z}; }
+
+ISO_HD VRef list_pred(const NodeList& L, VRef v) {
+  if (v.p > L.d[v.u].y) return {v.u, v.p - 1};
+  return {v.u - 1, L.d[v.u - 1].z};
+}
+
+ISO_HD VRef list_succ(const NodeList& L, VRef v) {
+  if (v.p < L.d[v.u].z) return {v.u, v.p + 1};
+  return {v.u + 1, L.d[v.u + 1].y};
+}
+
+// A vertex strictly inside [lo, hi] (or lo itself when the range has one or two vertices),
+// splitting first at segment boundaries and then within one segment.
+ISO_HD VRef list_mid(const NodeList& L, VRef lo, VRef hi) {
+  if (lo.u == hi.u) return {lo.u, (lo.p + hi.p) >> 1};
+  int um = (lo.u + hi.u + 1) >> 1;
+  return {um, L.d[um].y};
+}
+
+// Overmars-van Leeuwen simultaneous bisection for the bridge of two x-separated lower hulls.
+//
+// A is the left hull (its last vertex s at abscissa x_s), B the right hull without s (every
+// vertex right of x_s).  The bridge (alpha, beta) is the common tangent below both with alpha
+// the leftmost and beta the rightmost contact.  With e_i the slope of A's edge leaving a_i,
+// f_k the slope of B's edge leaving b_k and m the slope of a candidate pair (a_i, b_k):
+//   A-case b: e_{i-1} >= m (pred(a_i) on or below the line a_i b_k)      => alpha < i
+//   A-case a: e_i < m (succ(a_i) strictly below the line)
+//   A-case c: otherwise (a_i is the tangent point of A seen from b_k)
+//   B-case b: f_k <= m (succ(b_k) on or below the line)                   => beta > k
+//   B-case a: f_{k-1} > m (pred(b_k) strictly below the line)
+//   B-case c: otherwise
+//   (a, c) => alpha > i;  (c, a) => beta < k;  (c, c) => (a_i, b_k) is the bridge;
+//   (a, a) => the edge lines l_A through (a_i, a_{i+1}) and l_B through (b_{k-1}, b_k) cross at
+//             some x_int: if l_B is on or above l_A at x_s (x_int <= x_s) then l_A supports all
+//             of A and B with B strictly above it, so a_{i+1} stays a vertex: alpha > i;
+//             otherwise l_B supports everything with A strictly above it: beta < k.
+// Each step removes the candidate and one side of at least one range, so it ends after
+// O(log) steps per range.  lo/hi bound the ranges known to contain alpha and beta.
+// Returns false if the ranges run empty (possible only through rounding), leaving the outputs
+// unspecified; the caller then finishes by walking.
+ISO_HD bool bridge_search(const MergeArrays& Ar, const NodeList& LA, const NodeList& LB,
+                          VRef loA, VRef hiA, VRef loB, VRef hiB, const GPt& S, VRef& alpha,
+                          VRef& beta) {
+  const VRef firstA = list_first(LA), lastA = list_last(LA);
+  const VRef firstB = list_succ(LB, list_first(LB));  // first vertex of B without s
+  const VRef lastB = list_last(LB);
+  for (int it = 0; it < 4096; ++it) {
+    if (!vref_le(loA, hiA) || !vref_le(loB, hiB)) return false;
+    VRef i = list_mid(LA, loA, hiA);
+    VRef k = list_mid(LB, loB, hiB);
+    GPt a = load_v(Ar, LA, i);
+    GPt b = load_v(Ar, LB, k);
+    bool hasPA = !vref_eq(i, firstA), hasSA = !vref_eq(i, lastA);
+    bool hasPB = !vref_eq(k, firstB), hasSB = !vref_eq(k, lastB);
+    VRef pi{}, si{}, pk{}, sk{};
+    GPt pa{}, sa{}, pb{}, sb{};
+    bool Ab = false, Aa = false, Bb = false, Ba = false;
+    if (hasPA) {
+      pi = list_pred(LA, i);
+      pa = load_v(Ar, LA, pi);
+      Ab = gturn(pa, a, b) <= 0.0;
+    }
+    if (!Ab && hasSA) {
+      si = list_succ(LA, i);
+      sa = load_v(Ar, LA, si);
+      Aa = gturn(a, sa, b) > 0.0;
+    }
+    if (hasSB) {
+      sk = list_succ(LB, k);
+      sb = load_v(Ar, LB, sk);
+      Bb = gturn(a, b, sb) <= 0.0;
+    }
+    if (!Bb && hasPB) {
+      pk = list_pred(LB, k);
+      pb = load_v(Ar, LB, pk);
+      Ba = gturn(a, pb, b) > 0.0;
+    }
+    bool Ac = !Ab && !Aa, Bc = !Bb && !Ba;
+    if (Ac && Bc) {
+      alpha = i;
+      beta = k;
+      return true;
+    }
+    if (Ab) {
+      if (vref_eq(i, loA)) return false;
+      hiA = pi;
+    }
+    if (Bb) {
+      if (vref_eq(k, hiB)) return false;
+      loB = sk;
+    }
+    if (Aa && Bc) loA = si;
+    if (Ac && Ba) hiB = pk;
+    if (Aa && Ba) {
+      // Heights of s above l_A and above l_B, scaled by the edges' widths:
+      //   h_A = turn(a_i, a_{i+1}, s) / dxA,  h_B = turn(b_{k-1}, b_k, s) / dxB.
+      // l_B(x_s) >= l_A(x_s)  <=>  h_B <= h_A  <=>  turnB * dxA <= turnA * dxB.
+      double dxA, dyA, dxB, dyB;
+      gdiff(a, sa, dxA, dyA);
+      gdiff(pb, b, dxB, dyB);
+      double tA = gturn(a, sa, S);
+      double tB = gturn(pb, b, S);
+      if (diff_of_products(tA, dxB, tB, dxA) >= 0.0) {
+        loA = si;
+      } else {
+        hiB = pk;
+      }
+    }
+  }
+  return false;
+}
+
+// Merge of the nodes whose lists start at row-local chunks jA (left) and jB (right) of one row.
+// The merged list is written from jA's descriptor slot on and nseg[jA] updated.  Walks at most
+// `cap` steps, then searches; if the search fails through rounding it resumes the walk without
+// a cap.  Returns the number of walk steps taken (for statistics).
+ISO_HD int merge_nodes(const MergeArrays& Ar, int64_t rowbase, int jA, int jB, int cap) {
+  Desc* dA = Ar.desc + rowbase + jA;
+  Desc* dB = Ar.desc + rowbase + jB;
+  NodeList LA{dA, Ar.nseg[rowbase + jA], rowbase};
+  NodeList LB{dB, Ar.nseg[rowbase + jB], rowbase};
+  const VRef firstA = list_first(LA);
+  const VRef lastB = list_last(LB);
+  VRef al = list_last(LA);
+  VRef be = list_succ(LB, list_first(LB));
+  GPt Pa = load_v(Ar, LA, al);
+  const GPt S = Pa;
+  GPt Pb = load_v(Ar, LB, be);
+  int steps = 0;
+  bool done = false;
+  bool capped = cap >= 0;
+  while (!done) {
+    bool moved = false;
+    bool hit_cap = false;
+    while (!vref_eq(al, firstA)) {
+      VRef p = list_pred(LA, al);
+      GPt Pp = load_v(Ar, LA, p);
+      if (gturn(Pp, Pa, Pb) <= 0.0) {
+        al = p;
+        Pa = Pp;
+        moved = true;
+        if (capped && ++steps > cap) {
+          hit_cap = true;
+          break;
+        }
+      } else {
+        break;
+      }
+    }
+    if (!hit_cap) {
+      while (!vref_eq(be, lastB)) {
+        VRef q = list_succ(LB, be);
+        GPt Pq = load_v(Ar, LB, q);
+        if (gturn(Pa, Pb, Pq) <= 0.0) {
+          be = q;
+          Pb = Pq;
+          moved = true;
+          if (capped && ++steps > cap) {
+            hit_cap = true;
+            break;
+          }
+        } else {
+          break;
+        }
+      }
+    }
+    if (hit_cap) {
+      VRef a2, b2;
+      if (bridge_search(Ar, LA, LB, firstA, al, be, lastB, S, a2, b2)) {
+        al = a2;
+        be = b2;
+        done = true;
+      } else {
+        capped = false;  // finish by walking
+      }
+      continue;
+    }
+    if (!moved) done = true;
+  }
+  // Cut: A keeps segments 0..al.u with the last one ending at al.p; B keeps be.u.. with the first
+  // starting at be.p, moved down to follow A's kept part.
+  int nA = al.u + 1;
+  dA[al.u].z = al.p;
+  int nB = LB.n - be.u;
+  Desc first = dB[be.u];
+  first.y = be.p;
+  dA[nA] = first;  // dA + nA <= dB + be.u, so every read below is of an unwritten slot
+  for (int t = 1; t < nB; ++t) dA[nA + t] = dB[be.u + t];
+  Ar.nseg[rowbase + jA] = nA + nB;
+  return steps;
+}
+
+// ------------------------------------------------------------------ reconstruction
+
+// Per chunk, from the root list (Corollary 4.5): the chunk's surviving vertex range and the
+// slopes of the edges into and out of it; a chunk with no segment lies under one edge.
+struct EndInfo {
+  int lo, hi;     // surviving vertex positions of the chunk's hull, or -1
+  int klo, khi;   // their point indices within the chunk
+  double sin;     // slope of the edge into vertex lo (or of the single covering edge)
+  double sout;    // slope of the edge out of vertex hi
+  int p0v;        // the chunk's point 0 is a vertex of the row's hull
+  int pad[3];
+};
+
+ISO_HD EndInfo chunk_ends(const MergeArrays& Ar, const int* nverts, int64_t rb, int j) {
+  const int64_t g = rb + j;
+  const Desc* root = Ar.desc + rb;
+  const int nr = Ar.nseg[rb];
+  int lo = 0, hi = nr - 1;  // root[0].x == 0 <= j
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (root[mid].x <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  const int u = lo;
+  const Desc du = root[u];
+  EndInfo e;
+  e.pad[0] = e.pad[1] = e.pad[2] = 0;
+  if (du.x == j) {
+    e.lo = du.y;
+    e.hi = du.z;
+    e.klo = Ar.vk[g * (int64_t)kSlot + du.y];
+    e.khi = Ar.vk[g * (int64_t)kSlot + du.z];
+    const GPt plo = load_pt(Ar, rb, j, du.y);
+    const GPt phi = load_pt(Ar, rb, j, du.z);
+    e.sin = 0.0;
+    e.sout = 0.0;
+    if (u > 0) {
+      const Desc dp = root[u - 1];
+      e.sin = gslope(load_pt(Ar, rb, dp.x, dp.z), plo);
+    }
+    if (u + 1 < nr) {
+      const Desc dn = root[u + 1];
+      e.sout = gslope(phi, load_pt(Ar, rb, dn.x, dn.y));
+    }
+    int p0 = (du.y == 0) ? 1 : 0;
+    if (!p0 && u > 0 && j > 0) {
+      const Desc dp = root[u - 1];
+      if (dp.x == j - 1 && dp.z == nverts[g - 1] - 1) p0 = 1;
+    }
+    e.p0v = p0;
+  } else {
+    // root[u + 1] exists: the row's last chunk always keeps a segment.
+    e.lo = e.hi = -1;
+    e.klo = e.khi = 0;
+    const Desc dn = root[u + 1];
+    const double s = gslope(load_pt(Ar, rb, du.x, du.z), load_pt(Ar, rb, dn.x, dn.y));
+    e.sin = s;
+    e.sout = s;
+    e.p0v = (j > 0 && du.x == j - 1 && du.z == nverts[g - 1] - 1) ? 1 : 0;
+  }
+  return e;
+}
+
+// One lane's 32 elements of a chunk of `len` elements: each gets the slope of the hull edge over
+// it, rounded once to T, and its block-start byte (the element's left point is a hull vertex).
+// sb is the chunk's vertex slot base; z and bstart point at the chunk's first element.
+template <typename T>
+ISO_HD void fit_lane(const double* vx, const double* vy, const uint16_t* vk, const EndInfo& e,
+                     bool bad, int64_t sb, int len, int lane, T* z, uint8_t* bstart) {
+  const int i0 = kLanePts * lane;
+  int c = len - i0;
+  c = c < 0 ? 0 : (c > kLanePts ? kLanePts : c);
+  if (c == 0) return;
+  if (bad) {
+    for (int t = 0; t < c; ++t) {
+      z[i0 + t] = (T)NAN;
+      if (bstart) bstart[i0 + t] = 0;
+    }
+    return;
+  }
+  if (e.lo < 0) {
+    const T zv = (T)e.sin;
+    for (int t = 0; t < c; ++t) {
+      const int i = i0 + t;
+      z[i] = zv;
+      if (bstart) bstart[i] = (i == 0 && e.p0v) ? 1 : 0;
+    }
+    return;
+  }
+  // Local edges cover [klo, khi); find the vertex at or before this lane's first such element.
+  int a = e.lo;
+  const int first = i0 > e.klo ? i0 : e.klo;
+  if (first < e.khi) {
+    int lo = e.lo, hi = e.hi;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)vk[sb + mid] <= first) lo = mid;
+      else hi = mid - 1;
+    }
+    a = lo;
+  }
+  int ka = vk[sb + a];
+  int kb = (a < e.hi) ? (int)vk[sb + a + 1] : e.khi;
+  double slope = (a < e.hi) ? (vy[sb + a + 1] - vy[sb + a]) / (vx[sb + a + 1] - vx[sb + a]) : 0.0;
+  for (int t = 0; t < c; ++t) {
+    const int i = i0 + t;
+    double zv;
+    uint8_t st = 0;
+    if (i < e.klo) {
+      zv = e.sin;
+      st = (i == 0 && e.p0v) ? 1 : 0;
+    } else if (i >= e.khi) {
+      zv = e.sout;
+      st = (i == e.khi) ? 1 : 0;
+    } else {
+      if (i >= kb) {
+        ++a;
+        ka = kb;
+        kb = (int)vk[sb + a + 1];
+        slope = (vy[sb + a + 1] - vy[sb + a]) / (vx[sb + a + 1] - vx[sb + a]);
+      }
+      zv = slope;
+      st = (i == ka) ? 1 : 0;
+    }
+    z[i] = (T)zv;
+    if (bstart) bstart[i] = st;
+  }
+}
+
+}  // namespace iso

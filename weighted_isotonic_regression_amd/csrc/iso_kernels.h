@@ -1,0 +1,716 @@
+// iso_kernels.h -- HIP kernels of the isotonic fit for gfx950 (wave64).
+//
+// Pipeline ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 3):
+//   k_wave          one wavefront per tile of <= 2048 elements: coalesced loads into LDS, fp64
+//                   cumulative sums (lane-serial, then a wave scan of lane totals), lane hulls by
+//                   the bit-mask monotone chain (Section 3.1), pairwise walks merging lane hulls
+//                   (Section 3.2).  A tile is either a group of short rows (L lanes per row,
+//                   64 / L rows per wave, Section 3.5), finished here with z written, or one
+//                   chunk of a long row, whose hull is emitted to its vertex slot (Section 3.3).
+//   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
+//                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
+//   k_merge_level   one launch per level of the merge tree: segment lists merged by walk, capped
+//                   walk then Overmars-van Leeuwen search, cut and tail move (Section 3.3).
+//   k_ends          per chunk: its range of surviving vertices and the slopes into and out of it,
+//                   by bisection over the root list (Section 3.4).
+//   k_fit           per chunk: every element gets the slope of the hull edge above it, rounded
+//                   once to the output type (Section 3.4 and Corollary 4.5).
+//   k_vjp_*         block-averaging backward (Section 6 "Gradient").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "iso_geom.h"
+
+namespace iso {
+
+// ------------------------------------------------------------------ tile layout in LDS
+// A tile holds R = 64 / L row segments of up to 32 L elements.  Row segment r's points
+// 0..len occupy raw LDS indices r * (32 L + 1) + k; raw index i is stored at lds_pad(i) to
+// spread a lane's 32 consecutive points over the banks.  Element i's increment (w_i, w_i y_i)
+// is staged at the slot of its left point i and replaced by that point's coordinates.
+constexpr int kRawPts = kWave * (kLanePts + 1);           // 2112 = max R (32 L + 1)
+constexpr int kLdsPts = kRawPts + (kRawPts >> 5) + 8;     // padded
+constexpr int kMaskWords = 2 * kWave + 8;                 // R (L + 1) <= 128
+
+__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
+
+// Per-chunk outputs of a long row's wave pass.
+struct ChunkOut {
+  double2* tot;       // chunk totals (W, S) = coordinates of the chunk's end point
+  int* nverts;        // vertex count of the chunk hull
+  uint32_t* cflags;   // per-chunk input flags
+  Desc* desc;         // leaf segment list
+  int* nseg;
+  uint16_t* vk;       // vertex slots
+  double* vx;
+  double* vy;
+};
+
+template <bool W>
+struct TilePts {
+  const double* sX;
+  const double* sY;
+  int base;  // raw LDS index of point 0 of the row segment
+  __device__ __forceinline__ void operator()(int k, double& x, double& y) const {
+    int idx = lds_pad(base + k);
+    x = W ? sX[idx] : (double)k;
+    y = sY[idx];
+  }
+};
+
+template <typename T, bool W, bool CHUNK>
+__global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
+                                             T* __restrict__ z, uint8_t* __restrict__ bstart,
+                                             uint32_t* __restrict__ rflags, int64_t batch,
+                                             int64_t n, int m, int Lpack, ChunkOut out) {
+  __shared__ double sX[W ? kLdsPts : 1];
+  __shared__ double sY[kLdsPts];
+  __shared__ uint32_t sM[kMaskWords];
+  __shared__ uint32_t sF[kWave];
+
+  const int lane = threadIdx.x;
+  int L, rows, seglen, j = 0;
+  int64_t off, row0, g = 0;
+  if (CHUNK) {
+    g = blockIdx.x;
+    row0 = g / m;
+    j = (int)(g - row0 * m);
+    off = row0 * n + (int64_t)j * kChunk;
+    int64_t rem = n - (int64_t)j * kChunk;
+    seglen = rem < kChunk ? (int)rem : kChunk;
+    L = kWave;
+    rows = 1;
+  } else {
+    L = Lpack;
+    const int R = kWave / L;
+    row0 = (int64_t)blockIdx.x * R;
+    int64_t left = batch - row0;
+    rows = left < R ? (int)left : R;
+    off = row0 * n;
+    seglen = (int)n;
+  }
+  const int rowStride = kLanePts * L + 1;
+  const int maskStride = L + 1;
+
+  for (int i = lane; i < kMaskWords; i += kWave) sM[i] = 0u;
+  sF[lane] = 0u;
+  __syncthreads();
+
+  // ---- a1: coalesced load, classify, stage (w, w*y) in fp64 at each element's left point.
+  {
+    const int E = rows * seglen;
+    int r = 0, i = lane;
+    while (i >= seglen) {
+      i -= seglen;
+      ++r;
+    }
+    for (int e = lane; e < E; e += kWave) {
+      double yd = (double)y[off + e];
+      double wd = W ? (double)w[off + e] : 1.0;
+      uint32_t f = 0u;
+      if (!isfinite(yd) || !isfinite(wd)) f = ISO_ROW_NONFINITE_BIT;
+      else if (!(wd > 0.0)) f = ISO_ROW_BAD_WEIGHT_BIT;
+      if (f) {
+        atomicOr(&sF[r], f);
+        yd = 0.0;
+        wd = 1.0;
+      }
+      const int slot = lds_pad(r * rowStride + i);
+      if (W) sX[slot] = wd;
+      sY[slot] = wd * yd;
+      i += kWave;
+      while (i >= seglen) {
+        i -= seglen;
+        ++r;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- a2: cumulative sums.  Lane-serial fp64 sums of its 32 increments, a segmented wave
+  // scan of the lane totals, then each lane rewrites its slots with chunk-relative points.
+  const int lgL = __builtin_ctz(L);
+  const int r2 = lane >> lgL;
+  const int ql = lane & (L - 1);
+  const bool rowOK = r2 < rows;
+  int c = 0;
+  if (rowOK) {
+    int rem = seglen - kLanePts * ql;
+    c = rem < 0 ? 0 : (rem > kLanePts ? kLanePts : rem);
+  }
+  const int rbase = r2 * rowStride;
+  const int pbase = rbase + kLanePts * ql;
+  const int nl = (seglen + kLanePts - 1) / kLanePts;  // active lanes of a row segment
+  {
+    double tx = 0.0, ty = 0.0;
+    for (int k = 0; k < kLanePts; ++k) {
+      if (k < c) {
+        const int idx = lds_pad(pbase + k);
+        if (W) tx += sX[idx];
+        ty += sY[idx];
+      }
+    }
+    double ix = tx, iy = ty;
+    for (int d = 1; d < L; d <<= 1) {
+      double vx = __shfl_up(ix, d, L);
+      double vy = __shfl_up(iy, d, L);
+      if (ql >= d) {
+        ix += vx;
+        iy += vy;
+      }
+    }
+    double sx0 = __shfl_up(ix, 1, L);
+    double sy0 = __shfl_up(iy, 1, L);
+    if (ql == 0) {
+      sx0 = 0.0;
+      sy0 = 0.0;
+    }
+    double lx = 0.0, ly = 0.0;
+    for (int k = 0; k < kLanePts; ++k) {
+      if (k < c) {
+        const int idx = lds_pad(pbase + k);
+        double rx = W ? sX[idx] : 0.0;
+        double ry = sY[idx];
+        if (W) sX[idx] = sx0 + lx;
+        sY[idx] = sy0 + ly;
+        if (W) lx += rx;
+        ly += ry;
+      }
+    }
+    // The row segment's end point is written by its last active lane (its slot belongs to no
+    // other lane's elements).
+    if (c > 0 && kLanePts * ql + c == seglen) {
+      const int idx = lds_pad(pbase + c);
+      if (W) sX[idx] = sx0 + lx;
+      sY[idx] = sy0 + ly;
+    }
+  }
+  __syncthreads();
+
+  // ---- a3: lane hulls.
+  {
+    TilePts<W> P{sX, sY, pbase};
+    // x of an unweighted point is its row-local index.
+    auto Pl = [&](int k, double& xx, double& yy) {
+      P(k, xx, yy);
+      if (!W) xx = (double)(kLanePts * ql + k);
+    };
+    uint64_t mk = lane_chain(c, Pl);
+    if (c > 0) {
+      sM[r2 * maskStride + ql] = (uint32_t)mk;
+      if (c == kLanePts && kLanePts * ql + c == seglen) sM[r2 * maskStride + ql + 1] = 1u;
+    }
+  }
+  __syncthreads();
+
+  // ---- a4: pairwise merges of lane hulls within each row segment, by walking.
+  {
+    TilePts<W> Prow{sX, sY, rbase};
+    uint32_t* Mr = &sM[r2 * maskStride];
+    for (int d = 1; d < L; d <<= 1) {
+      if (rowOK && (ql & (2 * d - 1)) == 0 && ql + d < nl) {
+        const int a0 = kLanePts * ql;
+        const int s = kLanePts * (ql + d);
+        int b1 = kLanePts * (ql + 2 * d);
+        if (b1 > seglen) b1 = seglen;
+        tile_walk_merge(Mr, a0, s, b1, Prow);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- a5: emit.
+  TilePts<W> Prow{sX, sY, rbase};
+  if (CHUNK) {
+    uint32_t m0 = sM[lane];
+    uint32_t m1 = (lane == kWave - 1) ? sM[kWave] : 0u;
+    int cnt = __popc(m0) + __popc(m1);
+    int incl = cnt;
+    for (int d = 1; d < kWave; d <<= 1) {
+      int v = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += v;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    int pos = incl - cnt;
+    const int64_t sb = g * (int64_t)kSlot;
+    while (m0) {
+      const int b = __builtin_ctz(m0);
+      m0 &= m0 - 1u;
+      const int k = kLanePts * lane + b;
+      double xx, yy;
+      Prow(k, xx, yy);
+      out.vk[sb + pos] = (uint16_t)k;
+      out.vx[sb + pos] = xx;
+      out.vy[sb + pos] = yy;
+      ++pos;
+    }
+    while (m1) {
+      const int b = __builtin_ctz(m1);
+      m1 &= m1 - 1u;
+      const int k = kLanePts * kWave + b;
+      double xx, yy;
+      Prow(k, xx, yy);
+      out.vk[sb + pos] = (uint16_t)k;
+      out.vx[sb + pos] = xx;
+      out.vy[sb + pos] = yy;
+      ++pos;
+    }
+    if (lane == 0) {
+      out.nverts[g] = total;
+      out.desc[g] = make_int4(j, 0, total - 1, 0);
+      out.nseg[g] = 1;
+      out.cflags[g] = sF[0];
+      double xx, yy;
+      Prow(seglen, xx, yy);
+      out.tot[g] = make_double2(xx, yy);
+    }
+  } else {
+    if (rowOK && c > 0) {
+      const bool bad = sF[r2] != 0u;
+      const uint32_t* Mr = &sM[r2 * maskStride];
+      const int i0 = kLanePts * ql;
+      int a = ((Mr[ql] & 1u) != 0u) ? i0 : mask_pred(Mr, i0);
+      int b = mask_succ(Mr, i0);
+      double ax, ay, bx, by;
+      Prow(a, ax, ay);
+      Prow(b, bx, by);
+      double slope = (by - ay) / (bx - ax);
+      const int64_t ro = off + (int64_t)r2 * seglen;
+      for (int t = 0; t < kLanePts; ++t) {
+        if (t < c) {
+          const int i = i0 + t;
+          if (i >= b) {
+            a = b;
+            ax = bx;
+            ay = by;
+            b = mask_succ(Mr, b);
+            Prow(b, bx, by);
+            slope = (by - ay) / (bx - ax);
+          }
+          z[ro + i] = bad ? (T)NAN : (T)slope;
+          if (bstart) bstart[ro + i] = (!bad && i == a) ? 1 : 0;
+        }
+      }
+    }
+    if (rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
+  }
+}
+
+// ------------------------------------------------------------------ chunk-start scan
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = 4;
+constexpr int kScanBlock = kScanThreads * kScanPer;  // chunks per scan block
+
+struct DD2 {
+  DD x, y;
+};
+
+__device__ __forceinline__ DD2 dd2_add(const DD2& a, const DD2& b) {
+  return {dd_add(a.x, b.x), dd_add(a.y, b.y)};
+}
+
+// Inclusive block scan of DD2 values (Hillis-Steele in LDS).
+__device__ __forceinline__ DD2 block_scan_incl(DD2 v, double* sh) {
+  const int t = threadIdx.x;
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    sh[4 * t + 0] = v.x.hi;
+    sh[4 * t + 1] = v.x.lo;
+    sh[4 * t + 2] = v.y.hi;
+    sh[4 * t + 3] = v.y.lo;
+    __syncthreads();
+    if (t >= d) {
+      DD2 o{{sh[4 * (t - d) + 0], sh[4 * (t - d) + 1]}, {sh[4 * (t - d) + 2], sh[4 * (t - d) + 3]}};
+      v = dd2_add(o, v);
+    }
+    __syncthreads();
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const double2* __restrict__ tot,
+                                                              const uint32_t* __restrict__ cflags,
+                                                              double4* __restrict__ bsum,
+                                                              uint32_t* __restrict__ bflag, int m,
+                                                              int nblk) {
+  __shared__ double sh[4 * kScanThreads];
+  __shared__ uint32_t sf;
+  const int b = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int t = threadIdx.x;
+  if (t == 0) sf = 0u;
+  __syncthreads();
+  DD2 acc{{0.0, 0.0}, {0.0, 0.0}};
+  uint32_t f = 0u;
+  for (int k = 0; k < kScanPer; ++k) {
+    const int jj = b * kScanBlock + kScanPer * t + k;
+    if (jj < m) {
+      const double2 v = tot[row * m + jj];
+      acc = dd2_add(acc, DD2{{v.x, 0.0}, {v.y, 0.0}});
+      f |= cflags[row * m + jj];
+    }
+  }
+  if (f) atomicOr(&sf, f);
+  DD2 incl = block_scan_incl(acc, sh);
+  if (t == kScanThreads - 1) {
+    bsum[row * nblk + b] = make_double4(incl.x.hi, incl.x.lo, incl.y.hi, incl.y.lo);
+  }
+  __syncthreads();
+  if (t == 0) bflag[row * nblk + b] = sf;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __restrict__ tot,
+                                                             const double4* __restrict__ bsum,
+                                                             const uint32_t* __restrict__ bflag,
+                                                             double4* __restrict__ start,
+                                                             uint32_t* __restrict__ rflags, int m,
+                                                             int nblk) {
+  __shared__ double sh[4 * kScanThreads];
+  __shared__ double soff[4];
+  const int b = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    DD2 o{{0.0, 0.0}, {0.0, 0.0}};
+    uint32_t f = 0u;
+    for (int k = 0; k < nblk; ++k) {
+      const double4 v = bsum[row * nblk + k];
+      if (k < b) o = dd2_add(o, DD2{{v.x, v.y}, {v.z, v.w}});
+      f |= bflag[row * nblk + k];
+    }
+    soff[0] = o.x.hi;
+    soff[1] = o.x.lo;
+    soff[2] = o.y.hi;
+    soff[3] = o.y.lo;
+    if (b == 0 && rflags) rflags[row] = f;
+  }
+  DD2 loc[kScanPer + 1];
+  loc[0] = DD2{{0.0, 0.0}, {0.0, 0.0}};
+  for (int k = 0; k < kScanPer; ++k) {
+    const int jj = b * kScanBlock + kScanPer * t + k;
+    DD2 v{{0.0, 0.0}, {0.0, 0.0}};
+    if (jj < m) {
+      const double2 tv = tot[row * m + jj];
+      v = DD2{{tv.x, 0.0}, {tv.y, 0.0}};
+    }
+    loc[k + 1] = dd2_add(loc[k], v);
+  }
+  DD2 incl = block_scan_incl(loc[kScanPer], sh);
+  // exclusive prefix of this thread = inclusive of the previous thread
+  __syncthreads();
+  sh[4 * t + 0] = incl.x.hi;
+  sh[4 * t + 1] = incl.x.lo;
+  sh[4 * t + 2] = incl.y.hi;
+  sh[4 * t + 3] = incl.y.lo;
+  __syncthreads();
+  DD2 ex{{0.0, 0.0}, {0.0, 0.0}};
+  if (t > 0) ex = DD2{{sh[4 * (t - 1) + 0], sh[4 * (t - 1) + 1]}, {sh[4 * (t - 1) + 2], sh[4 * (t - 1) + 3]}};
+  const DD2 boff{{soff[0], soff[1]}, {soff[2], soff[3]}};
+  const DD2 base = dd2_add(boff, ex);
+  for (int k = 0; k < kScanPer; ++k) {
+    const int jj = b * kScanBlock + kScanPer * t + k;
+    if (jj < m) {
+      const DD2 s = dd2_add(base, loc[k]);
+      start[row * m + jj] = make_double4(s.x.hi, s.x.lo, s.y.hi, s.y.lo);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ merge levels
+__global__ __launch_bounds__(256) void k_merge_level(MergeArrays Ar, int64_t batch, int m, int r,
+                                                     int per_row) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= batch * per_row) return;
+  const int64_t row = t / per_row;
+  const int q = (int)(t - row * per_row);
+  const int jA = q << (r + 1);
+  const int jB = jA + (1 << r);
+  merge_nodes(Ar, row * m, jA, jB, kWalkCap);
+}
+
+// ------------------------------------------------------------------ ends
+__global__ __launch_bounds__(256) void k_ends(MergeArrays Ar, const int* __restrict__ nverts,
+                                              EndInfo* __restrict__ ends, int64_t batch, int m) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= batch * (int64_t)m) return;
+  const int64_t row = g / m;
+  ends[g] = chunk_ends(Ar, nverts, row * m, (int)(g - row * m));
+}
+
+// ------------------------------------------------------------------ fit
+template <typename T>
+__global__ __launch_bounds__(64) void k_fit(const double* __restrict__ vx,
+                                            const double* __restrict__ vy,
+                                            const uint16_t* __restrict__ vk,
+                                            const EndInfo* __restrict__ ends,
+                                            const uint32_t* __restrict__ rflags,
+                                            T* __restrict__ z, uint8_t* __restrict__ bstart,
+                                            int64_t n, int m) {
+  const int64_t g = blockIdx.x;
+  const int64_t row = g / m;
+  const int j = (int)(g - row * m);
+  const int64_t off = row * n + (int64_t)j * kChunk;
+  const int64_t rem = n - (int64_t)j * kChunk;
+  const int len = rem < kChunk ? (int)rem : kChunk;
+  fit_lane<T>(vx, vy, vk, ends[g], rflags[row] != 0u, g * (int64_t)kSlot, len, threadIdx.x,
+              z + off, bstart ? bstart + off : nullptr);
+}
+
+// ------------------------------------------------------------------ flags
+__global__ __launch_bounds__(256) void k_flags_any(const uint32_t* __restrict__ rflags,
+                                                   int64_t batch, uint32_t* __restrict__ any) {
+  __shared__ uint32_t s;
+  if (threadIdx.x == 0) s = 0u;
+  __syncthreads();
+  uint32_t f = 0u;
+  for (int64_t i = threadIdx.x; i < batch; i += blockDim.x) f |= rflags[i];
+  if (f) atomicOr(&s, f);
+  __syncthreads();
+  if (threadIdx.x == 0) any[0] = s;
+}
+
+// ------------------------------------------------------------------ backward (block averaging)
+// Tiles of 2048 elements (one wavefront, 32 per lane).  Per lane: whether it holds a block start,
+// the sums of (g, w) before its first start ("head"), from its last start on ("tail"), and the
+// whole lane.  Blocks crossing lanes and tiles get their sums from segmented scans.
+struct VjpTile {
+  double hg, hw;  // sums before the tile's first block start (whole tile if none)
+  double tg, tw;  // sums from the tile's last block start to its end
+  int has;        // the tile holds a block start
+  int pad;
+};
+
+template <typename T>
+__device__ __forceinline__ void vjp_lane_sums(const T* g, const T* w, const uint8_t* bs, int64_t off,
+                                              int i0, int c, int& has, double& hg, double& hw,
+                                              double& tg, double& tw) {
+  has = 0;
+  hg = hw = tg = tw = 0.0;
+  for (int t = 0; t < c; ++t) {
+    const int64_t e = off + i0 + t;
+    const double gv = (double)g[e];
+    const double wv = w ? (double)w[e] : 1.0;
+    if (bs[e]) {
+      has = 1;
+      tg = 0.0;
+      tw = 0.0;
+    }
+    if (!has) {
+      hg += gv;
+      hw += wv;
+    } else {
+      tg += gv;
+      tw += wv;
+    }
+  }
+}
+
+// Segmented combine for the running sum of the open block, left to right:
+// (has_l, s_l) then (has_r, s_r) -> (has_l | has_r, has_r ? s_r : s_l + s_r).
+template <typename T>
+__global__ __launch_bounds__(64) void k_vjp_tiles(const T* __restrict__ g, const T* __restrict__ w,
+                                                  const uint8_t* __restrict__ bs, int64_t n,
+                                                  int ntile, VjpTile* __restrict__ tiles) {
+  const int64_t tid = blockIdx.x;
+  const int64_t row = tid / ntile;
+  const int tt = (int)(tid - row * ntile);
+  const int64_t off = row * n + (int64_t)tt * kChunk;
+  const int64_t rem = n - (int64_t)tt * kChunk;
+  const int len = rem < kChunk ? (int)rem : kChunk;
+  const int lane = threadIdx.x;
+  const int i0 = kLanePts * lane;
+  int c = len - i0;
+  c = c < 0 ? 0 : (c > kLanePts ? kLanePts : c);
+  int has;
+  double hg, hw, tg, tw;
+  vjp_lane_sums(g, w, bs, off, i0, c, has, hg, hw, tg, tw);
+  // tile head: sum of heads up to and including the first lane with a start
+  // tile tail: combine tails left to right with the segmented rule
+  int h = has;
+  double sg = has ? tg : hg, sw = has ? tw : hw;  // lane's contribution to the open block at its end
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int oh = __shfl_up(h, d, kWave);
+    const double og = __shfl_up(sg, d, kWave);
+    const double ow = __shfl_up(sw, d, kWave);
+    if (lane >= d) {
+      if (!h) {
+        sg = og + sg;
+        sw = ow + sw;
+      }
+      h = h | oh;
+    }
+  }
+  // head: prefix sum of lane heads while no start has been seen
+  int seen = has;
+  double pg = hg, pw = hw;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int os = __shfl_up(seen, d, kWave);
+    const double og = __shfl_up(pg, d, kWave);
+    const double ow = __shfl_up(pw, d, kWave);
+    if (lane >= d) {
+      if (!os) {
+        pg = og + pg;
+        pw = ow + pw;
+      } else {
+        pg = og;
+        pw = ow;
+      }
+      seen = seen | os;
+    }
+  }
+  // pg at the last lane: heads summed up to the first lane holding a start (inclusive) -- the
+  // rule above freezes the value once a start was seen to the left.
+  if (lane == kWave - 1) {
+    VjpTile v;
+    v.hg = pg;
+    v.hw = pw;
+    v.tg = sg;
+    v.tw = sw;
+    v.has = h;
+    v.pad = 0;
+    tiles[tid] = v;
+  }
+}
+
+// Per row, serially over tiles: carry[t] = sums of the block open at tile t's start from
+// earlier tiles; cont[t] = sums of that block from tile t on.
+__global__ __launch_bounds__(64) void k_vjp_rows(const VjpTile* __restrict__ tiles, int64_t batch,
+                                                 int ntile, double4* __restrict__ cc) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= batch) return;
+  const VjpTile* tr = tiles + row * ntile;
+  double4* cr = cc + row * ntile;
+  double cg = 0.0, cw = 0.0;
+  for (int t = 0; t < ntile; ++t) {
+    cr[t].x = cg;
+    cr[t].y = cw;
+    const VjpTile v = tr[t];
+    if (v.has) {
+      cg = v.tg;
+      cw = v.tw;
+    } else {
+      cg += v.tg;
+      cw += v.tw;
+    }
+  }
+  double ng = 0.0, nw = 0.0;
+  for (int t = ntile - 1; t >= 0; --t) {
+    const VjpTile v = tr[t];
+    if (v.has) {
+      ng = v.hg;
+      nw = v.hw;
+    } else {
+      ng = v.hg + ng;
+      nw = v.hw + nw;
+    }
+    cr[t].z = ng;
+    cr[t].w = nw;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void k_vjp_apply(const T* __restrict__ g, const T* __restrict__ y,
+                                                  const T* __restrict__ w, const T* __restrict__ z,
+                                                  const uint8_t* __restrict__ bs,
+                                                  const double4* __restrict__ cc, T* __restrict__ gy,
+                                                  T* __restrict__ gw, int64_t n, int ntile) {
+  const int64_t tid = blockIdx.x;
+  const int64_t row = tid / ntile;
+  const int tt = (int)(tid - row * ntile);
+  const int64_t off = row * n + (int64_t)tt * kChunk;
+  const int64_t rem = n - (int64_t)tt * kChunk;
+  const int len = rem < kChunk ? (int)rem : kChunk;
+  const int lane = threadIdx.x;
+  const int i0 = kLanePts * lane;
+  int c = len - i0;
+  c = c < 0 ? 0 : (c > kLanePts ? kLanePts : c);
+  int has;
+  double hg, hw, tg, tw;
+  vjp_lane_sums(g, w, bs, off, i0, c, has, hg, hw, tg, tw);
+  const double4 me = cc[tid];
+  const bool last_tile = tt == ntile - 1;
+  const double4 nx = last_tile ? make_double4(0.0, 0.0, 0.0, 0.0) : cc[tid + 1];
+  // Forward: the open block's sums entering this lane (exclusive segmented scan of lane tails,
+  // seeded with the tile's carry).
+  int h = has;
+  double sg = has ? tg : hg, sw = has ? tw : hw;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int oh = __shfl_up(h, d, kWave);
+    const double og = __shfl_up(sg, d, kWave);
+    const double ow = __shfl_up(sw, d, kWave);
+    if (lane >= d) {
+      if (!h) {
+        sg = og + sg;
+        sw = ow + sw;
+      }
+      h = h | oh;
+    }
+  }
+  int eh = __shfl_up(h, 1, kWave);
+  double eg = __shfl_up(sg, 1, kWave), ew = __shfl_up(sw, 1, kWave);
+  if (lane == 0) {
+    eh = 0;
+    eg = 0.0;
+    ew = 0.0;
+  }
+  const double in_g = eh ? eg : me.x + eg;
+  const double in_w = eh ? ew : me.y + ew;
+  // Backward: the open block's sums after this lane (segmented scan of lane heads from the
+  // right, seeded with the next tile's continuation).
+  int bh = has;
+  double bg = hg, bw = hw;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int oh = __shfl_down(bh, d, kWave);
+    const double og = __shfl_down(bg, d, kWave);
+    const double ow = __shfl_down(bw, d, kWave);
+    if (lane + d < kWave) {
+      if (!bh) {
+        bg = bg + og;
+        bw = bw + ow;
+      }
+      bh = bh | oh;
+    }
+  }
+  int ah = __shfl_down(bh, 1, kWave);
+  double ag = __shfl_down(bg, 1, kWave), aw = __shfl_down(bw, 1, kWave);
+  if (lane == kWave - 1) {
+    ah = 0;
+    ag = 0.0;
+    aw = 0.0;
+  }
+  const double out_g = ah ? ag : ag + nx.z;
+  const double out_w = ah ? aw : aw + nx.w;
+  // Lanes with no elements (beyond the row's end) contribute zeros to the scans above.
+  if (c == 0) return;
+  // Walk the lane's elements block by block.
+  int t = 0;
+  while (t < c) {
+    int u = t + 1;
+    while (u < c && !bs[off + i0 + u]) ++u;
+    const bool starts_here = bs[off + i0 + t] != 0;
+    double G = 0.0, Wt = 0.0;
+    for (int v = t; v < u; ++v) {
+      G += (double)g[off + i0 + v];
+      Wt += w ? (double)w[off + i0 + v] : 1.0;
+    }
+    if (!starts_here) {
+      G += in_g;
+      Wt += in_w;
+    }
+    if (u == c) {
+      G += out_g;
+      Wt += out_w;
+    }
+    const double q = G / Wt;
+    for (int v = t; v < u; ++v) {
+      const int64_t e = off + i0 + v;
+      const double wv = w ? (double)w[e] : 1.0;
+      gy[e] = (T)(wv * q);
+      if (gw) gw[e] = (T)(((double)y[e] - (double)z[e]) * q);
+    }
+    t = u;
+  }
+}
+
+}  // namespace iso
