@@ -40,7 +40,9 @@ def deviation(z, zo):
     return float(np.max(np.abs(z - zo) / (1 + np.abs(zo)))) if z.size else 0.0
 
 
-def check(y, w, exact_partition=False, tol=None, kkt=True):
+def check(y, w, exact_partition=False, tol=None, kkt=True, scale_abs=False):
+    """scale_abs: measure max |z - z*| / max |y| instead (the page's Section 7.6 measure for its
+    cancellation family, whose blocks mix values of very different sizes)."""
     t = y.dtype.type
     z, bs, rf = gpu_fit(y, w)
     zo, bo, fo = oracle.pav(y.astype(np.float64), None if w is None else w.astype(np.float64),
@@ -48,7 +50,10 @@ def check(y, w, exact_partition=False, tol=None, kkt=True):
     zo = zo.reshape(y.shape)
     bo = bo.reshape(y.shape)
     assert np.array_equal(rf.astype(np.uint32), fo)
-    dev = deviation(z, zo)
+    if scale_abs:
+        dev = float(np.max(np.abs(z.astype(np.float64) - zo)) / np.max(np.abs(y.astype(np.float64))))
+    else:
+        dev = deviation(z, zo)
     assert dev <= (tol or TOL[t]), dev
     if exact_partition:
         assert np.array_equal(bs, bo)
@@ -78,12 +83,13 @@ def test_families(fam, dtype):
         for wk in ("unit", "uniform", "integer"):
             y, w = W.family(fam, 2, n, seed=n + 1, dtype=dtype, wkind=wk)
             w_ = None if wk == "unit" else w
-            # the cancellation family's scale is max|y| (the page's Section 7.6 measures it so)
-            tol = None
-            if fam == "cancel":
-                tol = (1e-15 if dtype == "f64" else 1e-7) * float(np.max(np.abs(y)))
+            # The cancellation family is measured against max|y| (the page's Section 7.6 does so).
+            # Chunk-relative coordinates there reach 32 B, so a slope carries a few ulp(32 B) of
+            # error: 1e-14 max|y| in fp64 (45 ulp of max|y|), 1e-7 max|y| in fp32.
+            cancel = fam == "cancel"
+            tol = (1e-14 if dtype == "f64" else 1e-7) if cancel else None
             check(y, w_, exact_partition=(fam in ("integer", "constant") and wk != "uniform"), tol=tol,
-                  kkt=fam != "cancel")
+                  kkt=not cancel, scale_abs=cancel)
 
 
 @pytest.mark.parametrize("n", [5, 64, 2048, 2049, 40000])

@@ -31,8 +31,8 @@ struct Layout {
   size_t total = 0;
   size_t o_rflags = 0, o_any = 0;
   // long rows only
-  size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_vk = 0, o_vx = 0,
-         o_vy = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
+  size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0, o_lx = 0,
+         o_ly = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
   int64_t m = 0, nblk = 0;
 };
 
@@ -58,9 +58,13 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.o_cf = take(G * sizeof(uint32_t));
     L.o_desc = take(G * sizeof(Desc));
     L.o_nseg = take(G * sizeof(int));
-    L.o_vk = take(G * (size_t)kSlot * sizeof(uint16_t));
-    L.o_vx = take(G * (size_t)kSlot * sizeof(double));
-    L.o_vy = take(G * (size_t)kSlot * sizeof(double));
+    L.o_lk = take(G * (size_t)kListCap * sizeof(uint16_t));
+    L.o_lx = take(G * (size_t)kListCap * sizeof(double));
+    L.o_ly = take(G * (size_t)kListCap * sizeof(double));
+    L.o_mask = take(G * (size_t)kMaskW * sizeof(uint32_t));
+    L.o_mcnt = take(G * (size_t)kMaskW * sizeof(uint16_t));
+    L.o_lsx = take(G * (size_t)kWave * sizeof(double));
+    L.o_lsy = take(G * (size_t)kWave * sizeof(double));
     L.o_ends = take(G * sizeof(EndInfo));
     L.o_bsum = take((size_t)batch * (size_t)L.nblk * sizeof(double4));
     L.o_bflag = take((size_t)batch * (size_t)L.nblk * sizeof(uint32_t));
@@ -156,9 +160,13 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   co.cflags = (uint32_t*)(ws + Lay.o_cf);
   co.desc = (Desc*)(ws + Lay.o_desc);
   co.nseg = (int*)(ws + Lay.o_nseg);
-  co.vk = (uint16_t*)(ws + Lay.o_vk);
-  co.vx = (double*)(ws + Lay.o_vx);
-  co.vy = (double*)(ws + Lay.o_vy);
+  co.lk = (uint16_t*)(ws + Lay.o_lk);
+  co.lx = (double*)(ws + Lay.o_lx);
+  co.ly = (double*)(ws + Lay.o_ly);
+  co.mask = (uint32_t*)(ws + Lay.o_mask);
+  co.mcnt = (uint16_t*)(ws + Lay.o_mcnt);
+  co.lsx = (double*)(ws + Lay.o_lsx);
+  co.lsy = (double*)(ws + Lay.o_lsy);
   double4* start = (double4*)(ws + Lay.o_start);
   double4* bsum = (double4*)(ws + Lay.o_bsum);
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
@@ -172,7 +180,23 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0, s,
                      co.tot, bsum, bflag, start, rflags, m, nblk);
   prof.mark(2);
-  MergeArrays Ar{co.desc, co.nseg, co.vx, co.vy, co.vk, start};
+  VertexStore<T, W> S;
+  S.desc = co.desc;
+  S.nseg = co.nseg;
+  S.nverts = co.nverts;
+  S.lx = co.lx;
+  S.ly = co.ly;
+  S.lk = co.lk;
+  S.mask = co.mask;
+  S.mcnt = co.mcnt;
+  S.lsx = co.lsx;
+  S.lsy = co.lsy;
+  S.tot = co.tot;
+  S.start = start;
+  S.y = y;
+  S.w = w;
+  S.n = n;
+  S.m = m;
   int levels = 0;
   for (int r = 0; (1 << r) < m; ++r) {
     ++levels;
@@ -180,16 +204,15 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int per_row = (m - (1 << r) + span - 1) / span;
     const int64_t merges = batch * (int64_t)per_row;
     const int64_t blocks = (merges + 255) / 256;
-    hipLaunchKernelGGL(k_merge_level, dim3((unsigned)blocks), dim3(256), 0, s, Ar, batch, m, r,
+    hipLaunchKernelGGL((k_merge_level<T, W>), dim3((unsigned)blocks), dim3(256), 0, s, S, batch, r,
                        per_row);
   }
   prof.mark(levels);
-  hipLaunchKernelGGL(k_ends, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, Ar,
-                     (const int*)co.nverts, ends, batch, m);
+  hipLaunchKernelGGL((k_ends<T, W>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,
+                     batch);
   prof.mark(1);
-  hipLaunchKernelGGL((k_fit<T>), dim3((unsigned)G), dim3(kWave), 0, s, (const double*)co.vx,
-                     (const double*)co.vy, (const uint16_t*)co.vk, (const EndInfo*)ends,
-                     (const uint32_t*)rflags, z, bstart, n, m);
+  hipLaunchKernelGGL((k_fit<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, S, (const EndInfo*)ends,
+                     (const uint32_t*)rflags, z, bstart);
   prof.mark(1);
   return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
 }

@@ -30,7 +30,8 @@ namespace iso {
 constexpr int kWave = 64;                    // lanes of a wavefront
 constexpr int kLanePts = 32;                 // elements per lane
 constexpr int kChunk = kWave * kLanePts;     // elements per chunk (one wavefront)
-constexpr int kSlot = kChunk + 1;            // vertex slot capacity of a chunk (C + 1 points)
+constexpr int kListCap = 256;                // chunks with at most this many hull vertices keep a list
+constexpr int kMaskW = kWave + 1;            // mask words of a chunk (points 0..C)
 constexpr int kWalkCap = 64;                 // walk steps of a merge before it switches to search
 
 // Per-row input flags (same values as ISO_ROW_NONFINITE / ISO_ROW_BAD_WEIGHT of iso.h).
@@ -241,54 +242,111 @@ ISO_HD double gslope(const GPt& a, const GPt& b) {
 }
 
 // Segment descriptor: x = chunk index within the row, y = first vertex position, z = last
-// vertex position (positions index the chunk's vertex slot), w unused.
+// vertex position (positions count the chunk hull's vertices from 0), w unused.
 using Desc = int4;
 
-// Device arrays of the merge phase.  Chunk g (global index row * m + j) owns:
-//   desc[g], nseg[g]            the descriptor slot and, for a node starting at g, its length
-//   vx/vy[g * kSlot + p]        chunk-relative coordinates of its hull vertex p
-//   vk[g * kSlot + p]           that vertex's point index within the chunk (0..C)
-//   start[g]                    {x hi, x lo, y hi, y lo} of the chunk's first point in the row
-struct MergeArrays {
-  Desc* desc;
-  int* nseg;
-  const double* vx;
-  const double* vy;
-  const uint16_t* vk;
-  const double4* start;
+// ------------------------------------------------------------------ chunk hull storage
+// A chunk's hull is stored in one of two forms, chosen by its vertex count V:
+//   list   (V <= kListCap): the vertices' chunk-relative coordinates and point indices.
+//   dense  (V >  kListCap): the vertex bit mask (65 words), the number of set bits before each
+//          word, and the coordinates of every lane's first point.  A vertex's coordinates are
+//          recomputed from its lane's start and the inputs, with the same fp64 operations in the
+//          same order as the chunk pass, so they are bitwise the values the chunk pass used.
+// Dense chunks are the ones whose points nearly all survive; storing them as lists would move
+// about 18 bytes per element, while the mask and lane starts take under one.
+template <typename T, bool W>
+struct VertexStore {
+  Desc* desc;             // [G] descriptor slots
+  int* nseg;              // [G] length of the list of the node starting at this slot
+  const int* nverts;      // [G] vertex count of each chunk hull
+  const double* lx;       // [G * kListCap] list form
+  const double* ly;
+  const uint16_t* lk;
+  const uint32_t* mask;   // [G * kMaskW] dense form
+  const uint16_t* mcnt;   // [G * kMaskW]
+  const double* lsx;      // [G * kWave]  (weighted only)
+  const double* lsy;      // [G * kWave]
+  const double2* tot;     // [G] chunk end point (W, S)
+  const double4* start;   // [G] chunk start {x hi, x lo, y hi, y lo}
+  const T* y;
+  const T* w;
+  int64_t n;              // row length
+  int m;                  // chunks per row
+
+  ISO_HD bool is_list(int64_t g) const { return nverts[g] <= kListCap; }
+
+  // Chunk-relative coordinates and point index of vertex p of chunk j of `row`.
+  ISO_HD void local(int64_t row, int j, int p, double& x, double& yy, int& k) const {
+    const int64_t g = row * m + j;
+    if (nverts[g] <= kListCap) {
+      const int64_t idx = g * kListCap + p;
+      x = lx[idx];
+      yy = ly[idx];
+      k = lk[idx];
+      return;
+    }
+    // select: the word holding the p-th set bit, then the bit within it
+    const uint16_t* mc = mcnt + g * kMaskW;
+    int lo = 0, hi = kMaskW - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)mc[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    uint32_t word = mask[g * kMaskW + lo];
+    for (int r = p - (int)mc[lo]; r > 0; --r) word &= word - 1u;
+    const int b = __builtin_ctz(word);
+    k = lo * kLanePts + b;
+    const int64_t rem = n - (int64_t)j * kChunk;
+    if (k == (rem < kChunk ? (int)rem : kChunk)) {  // the chunk's end point
+      const double2 t = tot[g];
+      x = t.x;
+      yy = t.y;
+      return;
+    }
+    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)lo * kLanePts;
+    double ax = 0.0, ay = 0.0;
+    for (int i = 0; i < b; ++i) {
+      const double wd = W ? (double)w[e0 + i] : 1.0;
+      const double yd = (double)y[e0 + i];
+      if (W) ax += wd;
+      ay += wd * yd;
+    }
+    x = W ? lsx[g * kWave + lo] + ax : (double)k;
+    yy = lsy[g * kWave + lo] + ay;
+  }
+
+  ISO_HD GPt pt(int64_t row, int j, int p) const {
+    GPt r;
+    int k;
+    local(row, j, p, r.x, r.y, k);
+    const double4 s = start[row * m + j];
+    r.sxh = s.x;
+    r.sxl = s.y;
+    r.syh = s.z;
+    r.syl = s.w;
+    return r;
+  }
 };
 
 struct VRef {
   int u;  // segment index within the node's list
-  int p;  // vertex position within that segment's chunk slot
+  int p;  // vertex position within that segment's chunk hull
 };
 
 ISO_HD bool vref_eq(VRef a, VRef b) { return a.u == b.u && a.p == b.p; }
 ISO_HD bool vref_le(VRef a, VRef b) { return a.u < b.u || (a.u == b.u && a.p <= b.p); }
 
-// A node's segment list: descriptors d[0..n) in global memory.
+// A node's segment list: descriptors d[0..n) in global memory, of row `row`.
 struct NodeList {
   const Desc* d;
   int n;
-  int64_t rowbase;  // global index of the row's chunk 0
+  int64_t row;
 };
 
-ISO_HD GPt load_pt(const MergeArrays& A, int64_t rowbase, int j, int p) {
-  int64_t g = rowbase + j;
-  int64_t idx = g * (int64_t)kSlot + p;
-  double4 s = A.start[g];
-  GPt r;
-  r.x = A.vx[idx];
-  r.y = A.vy[idx];
-  r.sxh = s.x;
-  r.sxl = s.y;
-  r.syh = s.z;
-  r.syl = s.w;
-  return r;
-}
-
-ISO_HD GPt load_v(const MergeArrays& A, const NodeList& L, VRef v) {
-  return load_pt(A, L.rowbase, L.d[v.u].x, v.p);
+template <class VS>
+ISO_HD GPt load_v(const VS& S, const NodeList& L, VRef v) {
+  return S.pt(L.row, L.d[v.u].x, v.p);
 }
 
 ISO_HD VRef list_first(const NodeList& L) { return {0, L.d[0].y}; }
@@ -333,9 +391,9 @@ ISO_HD VRef list_mid(const NodeList& L, VRef lo, VRef hi) {
 // O(log) steps per range.  lo/hi bound the ranges known to contain alpha and beta.
 // Returns false if the ranges run empty (possible only through rounding), leaving the outputs
 // unspecified; the caller then finishes by walking.
-ISO_HD bool bridge_search(const MergeArrays& Ar, const NodeList& LA, const NodeList& LB,
-                          VRef loA, VRef hiA, VRef loB, VRef hiB, const GPt& S, VRef& alpha,
-                          VRef& beta) {
+template <class VS>
+ISO_HD bool bridge_search(const VS& S, const NodeList& LA, const NodeList& LB, VRef loA, VRef hiA,
+                          VRef loB, VRef hiB, const GPt& Sp, VRef& alpha, VRef& beta) {
   const VRef firstA = list_first(LA), lastA = list_last(LA);
   const VRef firstB = list_succ(LB, list_first(LB));  // first vertex of B without s
   const VRef lastB = list_last(LB);
@@ -343,8 +401,8 @@ ISO_HD bool bridge_search(const MergeArrays& Ar, const NodeList& LA, const NodeL
     if (!vref_le(loA, hiA) || !vref_le(loB, hiB)) return false;
     VRef i = list_mid(LA, loA, hiA);
     VRef k = list_mid(LB, loB, hiB);
-    GPt a = load_v(Ar, LA, i);
-    GPt b = load_v(Ar, LB, k);
+    GPt a = load_v(S, LA, i);
+    GPt b = load_v(S, LB, k);
     bool hasPA = !vref_eq(i, firstA), hasSA = !vref_eq(i, lastA);
     bool hasPB = !vref_eq(k, firstB), hasSB = !vref_eq(k, lastB);
     VRef pi{}, si{}, pk{}, sk{};
@@ -352,22 +410,22 @@ ISO_HD bool bridge_search(const MergeArrays& Ar, const NodeList& LA, const NodeL
     bool Ab = false, Aa = false, Bb = false, Ba = false;
     if (hasPA) {
       pi = list_pred(LA, i);
-      pa = load_v(Ar, LA, pi);
+      pa = load_v(S, LA, pi);
       Ab = gturn(pa, a, b) <= 0.0;
     }
     if (!Ab && hasSA) {
       si = list_succ(LA, i);
-      sa = load_v(Ar, LA, si);
+      sa = load_v(S, LA, si);
       Aa = gturn(a, sa, b) > 0.0;
     }
     if (hasSB) {
       sk = list_succ(LB, k);
-      sb = load_v(Ar, LB, sk);
+      sb = load_v(S, LB, sk);
       Bb = gturn(a, b, sb) <= 0.0;
     }
     if (!Bb && hasPB) {
       pk = list_pred(LB, k);
-      pb = load_v(Ar, LB, pk);
+      pb = load_v(S, LB, pk);
       Ba = gturn(a, pb, b) > 0.0;
     }
     bool Ac = !Ab && !Aa, Bc = !Bb && !Ba;
@@ -393,8 +451,8 @@ ISO_HD bool bridge_search(const MergeArrays& Ar, const NodeList& LA, const NodeL
       double dxA, dyA, dxB, dyB;
       gdiff(a, sa, dxA, dyA);
       gdiff(pb, b, dxB, dyB);
-      double tA = gturn(a, sa, S);
-      double tB = gturn(pb, b, S);
+      double tA = gturn(a, sa, Sp);
+      double tB = gturn(pb, b, Sp);
       if (diff_of_products(tA, dxB, tB, dxA) >= 0.0) {
         loA = si;
       } else {
@@ -405,22 +463,24 @@ ISO_HD bool bridge_search(const MergeArrays& Ar, const NodeList& LA, const NodeL
   return false;
 }
 
-// Merge of the nodes whose lists start at row-local chunks jA (left) and jB (right) of one row.
-// The merged list is written from jA's descriptor slot on and nseg[jA] updated.  Walks at most
-// `cap` steps, then searches; if the search fails through rounding it resumes the walk without
-// a cap.  Returns the number of walk steps taken (for statistics).
-ISO_HD int merge_nodes(const MergeArrays& Ar, int64_t rowbase, int jA, int jB, int cap) {
-  Desc* dA = Ar.desc + rowbase + jA;
-  Desc* dB = Ar.desc + rowbase + jB;
-  NodeList LA{dA, Ar.nseg[rowbase + jA], rowbase};
-  NodeList LB{dB, Ar.nseg[rowbase + jB], rowbase};
+// Merge of the nodes whose lists start at chunks jA (left) and jB (right) of `row`.  The merged
+// list is written from jA's descriptor slot on and nseg updated.  Walks at most `cap` steps,
+// then searches; if the search fails through rounding it resumes the walk without a cap.
+// Returns the number of walk steps taken (for statistics).
+template <class VS>
+ISO_HD int merge_nodes(const VS& S, int64_t row, int jA, int jB, int cap) {
+  const int64_t rb = row * S.m;
+  Desc* dA = S.desc + rb + jA;
+  Desc* dB = S.desc + rb + jB;
+  NodeList LA{dA, S.nseg[rb + jA], row};
+  NodeList LB{dB, S.nseg[rb + jB], row};
   const VRef firstA = list_first(LA);
   const VRef lastB = list_last(LB);
   VRef al = list_last(LA);
   VRef be = list_succ(LB, list_first(LB));
-  GPt Pa = load_v(Ar, LA, al);
-  const GPt S = Pa;
-  GPt Pb = load_v(Ar, LB, be);
+  GPt Pa = load_v(S, LA, al);
+  const GPt Sp = Pa;
+  GPt Pb = load_v(S, LB, be);
   int steps = 0;
   bool done = false;
   bool capped = cap >= 0;
@@ -429,7 +489,7 @@ ISO_HD int merge_nodes(const MergeArrays& Ar, int64_t rowbase, int jA, int jB, i
     bool hit_cap = false;
     while (!vref_eq(al, firstA)) {
       VRef p = list_pred(LA, al);
-      GPt Pp = load_v(Ar, LA, p);
+      GPt Pp = load_v(S, LA, p);
       if (gturn(Pp, Pa, Pb) <= 0.0) {
         al = p;
         Pa = Pp;
@@ -445,7 +505,7 @@ ISO_HD int merge_nodes(const MergeArrays& Ar, int64_t rowbase, int jA, int jB, i
     if (!hit_cap) {
       while (!vref_eq(be, lastB)) {
         VRef q = list_succ(LB, be);
-        GPt Pq = load_v(Ar, LB, q);
+        GPt Pq = load_v(S, LB, q);
         if (gturn(Pa, Pb, Pq) <= 0.0) {
           be = q;
           Pb = Pq;
@@ -461,7 +521,7 @@ ISO_HD int merge_nodes(const MergeArrays& Ar, int64_t rowbase, int jA, int jB, i
     }
     if (hit_cap) {
       VRef a2, b2;
-      if (bridge_search(Ar, LA, LB, firstA, al, be, lastB, S, a2, b2)) {
+      if (bridge_search(S, LA, LB, firstA, al, be, lastB, Sp, a2, b2)) {
         al = a2;
         be = b2;
         done = true;
@@ -474,14 +534,16 @@ ISO_HD int merge_nodes(const MergeArrays& Ar, int64_t rowbase, int jA, int jB, i
   }
   // Cut: A keeps segments 0..al.u with the last one ending at al.p; B keeps be.u.. with the first
   // starting at be.p, moved down to follow A's kept part.
-  int nA = al.u + 1;
+  const int nA = al.u + 1;
   dA[al.u].z = al.p;
-  int nB = LB.n - be.u;
+  const int nB = LB.n - be.u;
   Desc first = dB[be.u];
   first.y = be.p;
   dA[nA] = first;  // dA + nA <= dB + be.u, so every read below is of an unwritten slot
-  for (int t = 1; t < nB; ++t) dA[nA + t] = dB[be.u + t];
-  Ar.nseg[rowbase + jA] = nA + nB;
+  if (dA + nA != dB + be.u) {
+    for (int t = 1; t < nB; ++t) dA[nA + t] = dB[be.u + t];
+  }
+  S.nseg[rb + jA] = nA + nB;
   return steps;
 }
 
@@ -498,10 +560,12 @@ struct EndInfo {
   int pad[3];
 };
 
-ISO_HD EndInfo chunk_ends(const MergeArrays& Ar, const int* nverts, int64_t rb, int j) {
+template <class VS>
+ISO_HD EndInfo chunk_ends(const VS& S, int64_t row, int j) {
+  const int64_t rb = row * S.m;
   const int64_t g = rb + j;
-  const Desc* root = Ar.desc + rb;
-  const int nr = Ar.nseg[rb];
+  const Desc* root = S.desc + rb;
+  const int nr = S.nseg[rb];
   int lo = 0, hi = nr - 1;  // root[0].x == 0 <= j
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -515,24 +579,25 @@ ISO_HD EndInfo chunk_ends(const MergeArrays& Ar, const int* nverts, int64_t rb, 
   if (du.x == j) {
     e.lo = du.y;
     e.hi = du.z;
-    e.klo = Ar.vk[g * (int64_t)kSlot + du.y];
-    e.khi = Ar.vk[g * (int64_t)kSlot + du.z];
-    const GPt plo = load_pt(Ar, rb, j, du.y);
-    const GPt phi = load_pt(Ar, rb, j, du.z);
+    GPt plo = S.pt(row, j, du.y);
+    GPt phi = S.pt(row, j, du.z);
+    double tx, ty;
+    S.local(row, j, du.y, tx, ty, e.klo);
+    S.local(row, j, du.z, tx, ty, e.khi);
     e.sin = 0.0;
     e.sout = 0.0;
     if (u > 0) {
       const Desc dp = root[u - 1];
-      e.sin = gslope(load_pt(Ar, rb, dp.x, dp.z), plo);
+      e.sin = gslope(S.pt(row, dp.x, dp.z), plo);
     }
     if (u + 1 < nr) {
       const Desc dn = root[u + 1];
-      e.sout = gslope(phi, load_pt(Ar, rb, dn.x, dn.y));
+      e.sout = gslope(phi, S.pt(row, dn.x, dn.y));
     }
     int p0 = (du.y == 0) ? 1 : 0;
     if (!p0 && u > 0 && j > 0) {
       const Desc dp = root[u - 1];
-      if (dp.x == j - 1 && dp.z == nverts[g - 1] - 1) p0 = 1;
+      if (dp.x == j - 1 && dp.z == S.nverts[g - 1] - 1) p0 = 1;
     }
     e.p0v = p0;
   } else {
@@ -540,78 +605,12 @@ ISO_HD EndInfo chunk_ends(const MergeArrays& Ar, const int* nverts, int64_t rb, 
     e.lo = e.hi = -1;
     e.klo = e.khi = 0;
     const Desc dn = root[u + 1];
-    const double s = gslope(load_pt(Ar, rb, du.x, du.z), load_pt(Ar, rb, dn.x, dn.y));
+    const double s = gslope(S.pt(row, du.x, du.z), S.pt(row, dn.x, dn.y));
     e.sin = s;
     e.sout = s;
-    e.p0v = (j > 0 && du.x == j - 1 && du.z == nverts[g - 1] - 1) ? 1 : 0;
+    e.p0v = (j > 0 && du.x == j - 1 && du.z == S.nverts[g - 1] - 1) ? 1 : 0;
   }
   return e;
-}
-
-// One lane's 32 elements of a chunk of `len` elements: each gets the slope of the hull edge over
-// it, rounded once to T, and its block-start byte (the element's left point is a hull vertex).
-// sb is the chunk's vertex slot base; z and bstart point at the chunk's first element.
-template <typename T>
-ISO_HD void fit_lane(const double* vx, const double* vy, const uint16_t* vk, const EndInfo& e,
-                     bool bad, int64_t sb, int len, int lane, T* z, uint8_t* bstart) {
-  const int i0 = kLanePts * lane;
-  int c = len - i0;
-  c = c < 0 ? 0 : (c > kLanePts ? kLanePts : c);
-  if (c == 0) return;
-  if (bad) {
-    for (int t = 0; t < c; ++t) {
-      z[i0 + t] = (T)NAN;
-      if (bstart) bstart[i0 + t] = 0;
-    }
-    return;
-  }
-  if (e.lo < 0) {
-    const T zv = (T)e.sin;
-    for (int t = 0; t < c; ++t) {
-      const int i = i0 + t;
-      z[i] = zv;
-      if (bstart) bstart[i] = (i == 0 && e.p0v) ? 1 : 0;
-    }
-    return;
-  }
-  // Local edges cover [klo, khi); find the vertex at or before this lane's first such element.
-  int a = e.lo;
-  const int first = i0 > e.klo ? i0 : e.klo;
-  if (first < e.khi) {
-    int lo = e.lo, hi = e.hi;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)vk[sb + mid] <= first) lo = mid;
-      else hi = mid - 1;
-    }
-    a = lo;
-  }
-  int ka = vk[sb + a];
-  int kb = (a < e.hi) ? (int)vk[sb + a + 1] : e.khi;
-  double slope = (a < e.hi) ? (vy[sb + a + 1] - vy[sb + a]) / (vx[sb + a + 1] - vx[sb + a]) : 0.0;
-  for (int t = 0; t < c; ++t) {
-    const int i = i0 + t;
-    double zv;
-    uint8_t st = 0;
-    if (i < e.klo) {
-      zv = e.sin;
-      st = (i == 0 && e.p0v) ? 1 : 0;
-    } else if (i >= e.khi) {
-      zv = e.sout;
-      st = (i == e.khi) ? 1 : 0;
-    } else {
-      if (i >= kb) {
-        ++a;
-        ka = kb;
-        kb = (int)vk[sb + a + 1];
-        slope = (vy[sb + a + 1] - vy[sb + a]) / (vx[sb + a + 1] - vx[sb + a]);
-      }
-      zv = slope;
-      st = (i == ka) ? 1 : 0;
-    }
-    z[i] = (T)zv;
-    if (bstart) bstart[i] = st;
-  }
 }
 
 }  // namespace iso

@@ -1,20 +1,21 @@
 // iso_kernels.h -- HIP kernels of the isotonic fit for gfx950 (wave64).
 //
 // Pipeline ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 3):
-//   k_wave          one wavefront per tile of <= 2048 elements: coalesced loads into LDS, fp64
-//                   cumulative sums (lane-serial, then a wave scan of lane totals), lane hulls by
-//                   the bit-mask monotone chain (Section 3.1), pairwise walks merging lane hulls
-//                   (Section 3.2).  A tile is either a group of short rows (L lanes per row,
-//                   64 / L rows per wave, Section 3.5), finished here with z written, or one
-//                   chunk of a long row, whose hull is emitted to its vertex slot (Section 3.3).
+//   k_wave          one wavefront per tile of <= 2048 elements: coalesced 16-byte loads, fp64
+//                   cumulative sums in LDS (lane-serial, then a wave scan of lane totals), lane
+//                   hulls by the bit-mask monotone chain (Section 3.1), pairwise walks merging
+//                   lane hulls (Section 3.2).  A tile is either a group of short rows (L lanes per
+//                   row, 64 / L rows per wave, Section 3.5), finished here, or one chunk of a long
+//                   row, whose hull is stored as a vertex list (sparse hulls) or as a bit mask plus
+//                   lane starts with the chunk's own fit written to z (dense hulls).
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
 //   k_merge_level   one launch per level of the merge tree: segment lists merged by walk, capped
 //                   walk then Overmars-van Leeuwen search, cut and tail move (Section 3.3).
 //   k_ends          per chunk: its range of surviving vertices and the slopes into and out of it,
 //                   by bisection over the root list (Section 3.4).
-//   k_fit           per chunk: every element gets the slope of the hull edge above it, rounded
-//                   once to the output type (Section 3.4 and Corollary 4.5).
+//   k_fit           per chunk: every element not already final gets the slope of the hull edge
+//                   above it, rounded once to the output type (Section 3.4, Corollary 4.5).
 //   k_vjp_*         block-averaging backward (Section 6 "Gradient").
 #pragma once
 
@@ -36,6 +37,43 @@ constexpr int kMaskWords = 2 * kWave + 8;                 // R (L + 1) <= 128
 
 __device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
 
+// 16-byte vectors of the element type.
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<float> {
+  using type = float4;
+  static constexpr int N = 4;
+};
+template <>
+struct Vec16<double> {
+  using type = double2;
+  static constexpr int N = 2;
+};
+
+template <typename T>
+__device__ __forceinline__ void vload(const T* p, T* out) {
+  using V = typename Vec16<T>::type;
+  const V v = *reinterpret_cast<const V*>(p);
+  if constexpr (Vec16<T>::N == 4) {
+    out[0] = v.x;
+    out[1] = v.y;
+    out[2] = v.z;
+    out[3] = v.w;
+  } else {
+    out[0] = v.x;
+    out[1] = v.y;
+  }
+}
+
+// q = e / d for 0 <= e < 4096, 1 <= d <= 2048 (float reciprocal, corrected to exact).
+__device__ __forceinline__ int small_div(int e, int d, float inv) {
+  int q = (int)((float)e * inv);
+  if (q * d > e) --q;
+  else if ((q + 1) * d <= e) ++q;
+  return q;
+}
+
 // Per-chunk outputs of a long row's wave pass.
 struct ChunkOut {
   double2* tot;       // chunk totals (W, S) = coordinates of the chunk's end point
@@ -43,9 +81,13 @@ struct ChunkOut {
   uint32_t* cflags;   // per-chunk input flags
   Desc* desc;         // leaf segment list
   int* nseg;
-  uint16_t* vk;       // vertex slots
-  double* vx;
-  double* vy;
+  double* lx;         // list form [G * kListCap]
+  double* ly;
+  uint16_t* lk;
+  uint32_t* mask;     // dense form [G * kMaskW]
+  uint16_t* mcnt;
+  double* lsx;        // [G * kWave]
+  double* lsy;
 };
 
 template <bool W>
@@ -70,6 +112,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   __shared__ uint32_t sM[kMaskWords];
   __shared__ uint32_t sF[kWave];
 
+  constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
   int L, rows, seglen, j = 0;
   int64_t off, row0, g = 0;
@@ -93,22 +136,53 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   }
   const int rowStride = kLanePts * L + 1;
   const int maskStride = L + 1;
+  const int E = rows * seglen;  // elements of the tile, contiguous from off
+  const float inv_seg = 1.0f / (float)seglen;
 
   for (int i = lane; i < kMaskWords; i += kWave) sM[i] = 0u;
   sF[lane] = 0u;
-  __syncthreads();
 
-  // ---- a1: coalesced load, classify, stage (w, w*y) in fp64 at each element's left point.
-  {
-    const int E = rows * seglen;
-    int r = 0, i = lane;
-    while (i >= seglen) {
-      i -= seglen;
-      ++r;
+  // ---- a1: load.  All of the lane's loads are issued before any is used: 16-byte vectors at
+  // element (lane + 64 k) * VN when the tile is 16-byte aligned, else scalars at lane + 64 k.
+  T yv[kLanePts], wv[kLanePts];
+  const bool vec = (((uintptr_t)(y + off)) % 16 == 0) && (!W || ((uintptr_t)(w + off)) % 16 == 0);
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kLanePts / VN; ++k) {
+      const int e = (lane + kWave * k) * VN;
+      if (e + VN <= E) {
+        vload(y + off + e, &yv[k * VN]);
+        if (W) vload(w + off + e, &wv[k * VN]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < VN; ++t) {
+          if (e + t < E) {
+            yv[k * VN + t] = y[off + e + t];
+            if (W) wv[k * VN + t] = w[off + e + t];
+          }
+        }
+      }
     }
-    for (int e = lane; e < E; e += kWave) {
-      double yd = (double)y[off + e];
-      double wd = W ? (double)w[off + e] : 1.0;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kLanePts; ++k) {
+      const int e = lane + kWave * k;
+      if (e < E) {
+        yv[k] = y[off + e];
+        if (W) wv[k] = w[off + e];
+      }
+    }
+  }
+  __syncthreads();
+  // classify and stage (w, w*y) in fp64 at each element's left point
+#pragma unroll
+  for (int k = 0; k < kLanePts; ++k) {
+    const int e = vec ? (lane + kWave * (k / VN)) * VN + (k % VN) : lane + kWave * k;
+    if (e < E) {
+      double yd = (double)yv[k];
+      double wd = W ? (double)wv[k] : 1.0;
+      const int r = CHUNK ? 0 : small_div(e, seglen, inv_seg);
+      const int i = e - r * seglen;
       uint32_t f = 0u;
       if (!isfinite(yd) || !isfinite(wd)) f = ISO_ROW_NONFINITE_BIT;
       else if (!(wd > 0.0)) f = ISO_ROW_BAD_WEIGHT_BIT;
@@ -120,11 +194,6 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       const int slot = lds_pad(r * rowStride + i);
       if (W) sX[slot] = wd;
       sY[slot] = wd * yd;
-      i += kWave;
-      while (i >= seglen) {
-        i -= seglen;
-        ++r;
-      }
     }
   }
   __syncthreads();
@@ -143,6 +212,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   const int rbase = r2 * rowStride;
   const int pbase = rbase + kLanePts * ql;
   const int nl = (seglen + kLanePts - 1) / kLanePts;  // active lanes of a row segment
+  double lane_sx = 0.0, lane_sy = 0.0;                // coordinates of the lane's point 0
   {
     double tx = 0.0, ty = 0.0;
     for (int k = 0; k < kLanePts; ++k) {
@@ -167,6 +237,8 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       sx0 = 0.0;
       sy0 = 0.0;
     }
+    lane_sx = sx0;
+    lane_sy = sy0;
     double lx = 0.0, ly = 0.0;
     for (int k = 0; k < kLanePts; ++k) {
       if (k < c) {
@@ -222,40 +294,55 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   }
 
   // ---- a5: emit.
-  TilePts<W> Prow{sX, sY, rbase};
+  bool write_z = !CHUNK;
   if (CHUNK) {
     uint32_t m0 = sM[lane];
-    uint32_t m1 = (lane == kWave - 1) ? sM[kWave] : 0u;
-    int cnt = __popc(m0) + __popc(m1);
+    const uint32_t m1 = (lane == kWave - 1) ? sM[kWave] : 0u;
+    const int cnt = __popc(m0) + __popc(m1);
     int incl = cnt;
     for (int d = 1; d < kWave; d <<= 1) {
       int v = __shfl_up(incl, d, kWave);
       if (lane >= d) incl += v;
     }
     const int total = __shfl(incl, kWave - 1, kWave);
-    int pos = incl - cnt;
-    const int64_t sb = g * (int64_t)kSlot;
-    while (m0) {
-      const int b = __builtin_ctz(m0);
-      m0 &= m0 - 1u;
-      const int k = kLanePts * lane + b;
-      double xx, yy;
-      Prow(k, xx, yy);
-      out.vk[sb + pos] = (uint16_t)k;
-      out.vx[sb + pos] = xx;
-      out.vy[sb + pos] = yy;
-      ++pos;
-    }
-    while (m1) {
-      const int b = __builtin_ctz(m1);
-      m1 &= m1 - 1u;
-      const int k = kLanePts * kWave + b;
-      double xx, yy;
-      Prow(k, xx, yy);
-      out.vk[sb + pos] = (uint16_t)k;
-      out.vx[sb + pos] = xx;
-      out.vy[sb + pos] = yy;
-      ++pos;
+    const int rank = incl - cnt;
+    TilePts<W> Prow{sX, sY, 0};
+    if (total <= kListCap) {
+      // list form
+      const int64_t lb = g * (int64_t)kListCap;
+      int pos = rank;
+      uint32_t mm = m0;
+      while (mm) {
+        const int b = __builtin_ctz(mm);
+        mm &= mm - 1u;
+        const int k = kLanePts * lane + b;
+        double xx, yy;
+        Prow(k, xx, yy);
+        out.lk[lb + pos] = (uint16_t)k;
+        out.lx[lb + pos] = xx;
+        out.ly[lb + pos] = yy;
+        ++pos;
+      }
+      if (m1) {
+        const int k = kLanePts * kWave;  // the chunk's end point (bit 0 of word 64)
+        double xx, yy;
+        Prow(k, xx, yy);
+        out.lk[lb + pos] = (uint16_t)k;
+        out.lx[lb + pos] = xx;
+        out.ly[lb + pos] = yy;
+      }
+    } else {
+      // dense form: mask, set bits before each word, lane starts; the chunk's fit goes to z
+      const int64_t mb = g * (int64_t)kMaskW;
+      out.mask[mb + lane] = m0;
+      out.mcnt[mb + lane] = (uint16_t)rank;
+      if (lane == kWave - 1) {
+        out.mask[mb + kWave] = m1;
+        out.mcnt[mb + kWave] = (uint16_t)(rank + __popc(m0));
+      }
+      if (W) out.lsx[g * kWave + lane] = lane_sx;
+      out.lsy[g * kWave + lane] = lane_sy;
+      write_z = true;
     }
     if (lane == 0) {
       out.nverts[g] = total;
@@ -266,35 +353,28 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       Prow(seglen, xx, yy);
       out.tot[g] = make_double2(xx, yy);
     }
-  } else {
-    if (rowOK && c > 0) {
-      const bool bad = sF[r2] != 0u;
-      const uint32_t* Mr = &sM[r2 * maskStride];
-      const int i0 = kLanePts * ql;
-      int a = ((Mr[ql] & 1u) != 0u) ? i0 : mask_pred(Mr, i0);
-      int b = mask_succ(Mr, i0);
+  }
+  if (write_z) {
+    // Element-parallel: element e (row r, index i) gets the slope of the tile hull's edge over
+    // it, from the vertex at or before point i to the vertex after it.  Consecutive lanes write
+    // consecutive elements.
+    for (int e = lane; e < E; e += kWave) {
+      const int r = CHUNK ? 0 : small_div(e, seglen, inv_seg);
+      const int i = e - r * seglen;
+      const uint32_t* Mr = &sM[r * maskStride];
+      TilePts<W> Pr{sX, sY, r * rowStride};
+      const bool isv = (Mr[i >> 5] >> (i & 31)) & 1u;
+      const int a = isv ? i : mask_pred(Mr, i);
+      const int b = mask_succ(Mr, i);
       double ax, ay, bx, by;
-      Prow(a, ax, ay);
-      Prow(b, bx, by);
-      double slope = (by - ay) / (bx - ax);
-      const int64_t ro = off + (int64_t)r2 * seglen;
-      for (int t = 0; t < kLanePts; ++t) {
-        if (t < c) {
-          const int i = i0 + t;
-          if (i >= b) {
-            a = b;
-            ax = bx;
-            ay = by;
-            b = mask_succ(Mr, b);
-            Prow(b, bx, by);
-            slope = (by - ay) / (bx - ax);
-          }
-          z[ro + i] = bad ? (T)NAN : (T)slope;
-          if (bstart) bstart[ro + i] = (!bad && i == a) ? 1 : 0;
-        }
-      }
+      Pr(a, ax, ay);
+      Pr(b, bx, by);
+      const bool bad = sF[r] != 0u;
+      const double slope = (by - ay) / (bx - ax);
+      z[off + e] = bad ? (T)NAN : (T)slope;
+      if (bstart) bstart[off + e] = (!bad && isv) ? 1 : 0;
     }
-    if (rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
+    if (!CHUNK && rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
   }
 }
 
@@ -418,7 +498,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __re
 }
 
 // ------------------------------------------------------------------ merge levels
-__global__ __launch_bounds__(256) void k_merge_level(MergeArrays Ar, int64_t batch, int m, int r,
+template <typename T, bool W>
+__global__ __launch_bounds__(256) void k_merge_level(VertexStore<T, W> S, int64_t batch, int r,
                                                      int per_row) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= batch * per_row) return;
@@ -426,35 +507,97 @@ __global__ __launch_bounds__(256) void k_merge_level(MergeArrays Ar, int64_t bat
   const int q = (int)(t - row * per_row);
   const int jA = q << (r + 1);
   const int jB = jA + (1 << r);
-  merge_nodes(Ar, row * m, jA, jB, kWalkCap);
+  merge_nodes(S, row, jA, jB, kWalkCap);
 }
 
 // ------------------------------------------------------------------ ends
-__global__ __launch_bounds__(256) void k_ends(MergeArrays Ar, const int* __restrict__ nverts,
-                                              EndInfo* __restrict__ ends, int64_t batch, int m) {
+template <typename T, bool W>
+__global__ __launch_bounds__(256) void k_ends(VertexStore<T, W> S, EndInfo* __restrict__ ends,
+                                              int64_t batch) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= batch * (int64_t)m) return;
-  const int64_t row = g / m;
-  ends[g] = chunk_ends(Ar, nverts, row * m, (int)(g - row * m));
+  if (g >= batch * (int64_t)S.m) return;
+  const int64_t row = g / S.m;
+  ends[g] = chunk_ends(S, row, (int)(g - row * S.m));
 }
 
 // ------------------------------------------------------------------ fit
-template <typename T>
-__global__ __launch_bounds__(64) void k_fit(const double* __restrict__ vx,
-                                            const double* __restrict__ vy,
-                                            const uint16_t* __restrict__ vk,
-                                            const EndInfo* __restrict__ ends,
-                                            const uint32_t* __restrict__ rflags,
-                                            T* __restrict__ z, uint8_t* __restrict__ bstart,
-                                            int64_t n, int m) {
+// One wavefront per chunk, element-parallel (consecutive lanes, consecutive elements).
+//   dense chunks: z already holds the chunk hull's slopes; they are final inside the chunk's
+//                 surviving range [klo, khi), so only the elements outside it are written.
+//   list chunks:  every element is written: the in/out slopes outside [klo, khi), inside it the
+//                 slope of the surviving local edge above the element.
+template <typename T, bool W>
+__global__ __launch_bounds__(64) void k_fit(VertexStore<T, W> S, const EndInfo* __restrict__ ends,
+                                            const uint32_t* __restrict__ rflags, T* __restrict__ z,
+                                            uint8_t* __restrict__ bstart) {
+  __shared__ double sSlope[kListCap];
+  __shared__ int sK[kListCap];
   const int64_t g = blockIdx.x;
-  const int64_t row = g / m;
-  const int j = (int)(g - row * m);
-  const int64_t off = row * n + (int64_t)j * kChunk;
-  const int64_t rem = n - (int64_t)j * kChunk;
+  const int64_t row = g / S.m;
+  const int j = (int)(g - row * S.m);
+  const int64_t off = row * S.n + (int64_t)j * kChunk;
+  const int64_t rem = S.n - (int64_t)j * kChunk;
   const int len = rem < kChunk ? (int)rem : kChunk;
-  fit_lane<T>(vx, vy, vk, ends[g], rflags[row] != 0u, g * (int64_t)kSlot, len, threadIdx.x,
-              z + off, bstart ? bstart + off : nullptr);
+  const int lane = threadIdx.x;
+  const EndInfo e = ends[g];
+  if (rflags[row] != 0u) {
+    for (int i = lane; i < len; i += kWave) {
+      z[off + i] = (T)NAN;
+      if (bstart) bstart[off + i] = 0;
+    }
+    return;
+  }
+  const bool dense = S.nverts[g] > kListCap;
+  if (e.lo < 0) {
+    const T zv = (T)e.sin;
+    for (int i = lane; i < len; i += kWave) {
+      z[off + i] = zv;
+      if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
+    }
+    return;
+  }
+  if (dense) {
+    const T zin = (T)e.sin, zout = (T)e.sout;
+    for (int i = lane; i < e.klo; i += kWave) {
+      z[off + i] = zin;
+      if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
+    }
+    for (int i = e.khi + lane; i < len; i += kWave) {
+      z[off + i] = zout;
+      if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
+    }
+    return;
+  }
+  // list form: stage the surviving vertices' point indices and the slopes of the edges between
+  const int nv = e.hi - e.lo + 1;
+  const int64_t lb = g * (int64_t)kListCap + e.lo;
+  for (int q = lane; q < nv; q += kWave) {
+    sK[q] = S.lk[lb + q];
+    if (q + 1 < nv) sSlope[q] = (S.ly[lb + q + 1] - S.ly[lb + q]) / (S.lx[lb + q + 1] - S.lx[lb + q]);
+  }
+  __syncthreads();
+  for (int i = lane; i < len; i += kWave) {
+    double zv;
+    uint8_t st = 0;
+    if (i < e.klo) {
+      zv = e.sin;
+      st = (i == 0 && e.p0v) ? 1 : 0;
+    } else if (i >= e.khi) {
+      zv = e.sout;
+      st = (i == e.khi) ? 1 : 0;
+    } else {
+      int lo = 0, hi = nv - 2;  // edge q covers [sK[q], sK[q + 1])
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sK[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      zv = sSlope[lo];
+      st = (sK[lo] == i) ? 1 : 0;
+    }
+    z[off + i] = (T)zv;
+    if (bstart) bstart[off + i] = st;
+  }
 }
 
 // ------------------------------------------------------------------ flags
@@ -525,8 +668,7 @@ __global__ __launch_bounds__(64) void k_vjp_tiles(const T* __restrict__ g, const
   int has;
   double hg, hw, tg, tw;
   vjp_lane_sums(g, w, bs, off, i0, c, has, hg, hw, tg, tw);
-  // tile head: sum of heads up to and including the first lane with a start
-  // tile tail: combine tails left to right with the segmented rule
+  // tile tail: combine lane tails left to right with the segmented rule
   int h = has;
   double sg = has ? tg : hg, sw = has ? tw : hw;  // lane's contribution to the open block at its end
   for (int d = 1; d < kWave; d <<= 1) {
@@ -541,7 +683,7 @@ __global__ __launch_bounds__(64) void k_vjp_tiles(const T* __restrict__ g, const
       h = h | oh;
     }
   }
-  // head: prefix sum of lane heads while no start has been seen
+  // tile head: lane heads summed up to and including the first lane holding a start
   int seen = has;
   double pg = hg, pw = hw;
   for (int d = 1; d < kWave; d <<= 1) {
@@ -559,8 +701,6 @@ __global__ __launch_bounds__(64) void k_vjp_tiles(const T* __restrict__ g, const
       seen = seen | os;
     }
   }
-  // pg at the last lane: heads summed up to the first lane holding a start (inclusive) -- the
-  // rule above freezes the value once a start was seen to the left.
   if (lane == kWave - 1) {
     VjpTile v;
     v.hg = pg;
