@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
+    ap.add_argument("--only", choices=["mixed", "short", "dense"], default=None,
+                    help="time one workload only (for profiler runs); implies --no-cpu")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (rows are independent and a "
@@ -114,6 +116,9 @@ def main():
 
     B.load()
     dev = torch.device("cuda:0")
+    if args.only:
+        run_only(args, torch, B, W, dev)
+        return
     print("bench: generating mixed_1e8", file=sys.stderr, flush=True)
     y_h, w_h = W.mixed_1e8()
     n = y_h.shape[1]
@@ -201,6 +206,27 @@ def main():
                                 "roofline": roofline_of(dms, dla, dc, nd, 8, True),
                                 "max_deviation_vs_y": dev_y}
     print(json.dumps(out), flush=True)
+
+
+def run_only(args, torch, B, W, dev):
+    """One workload, timed as in the full run; prints one JSON line of its own."""
+    if args.only == "short":
+        ys, wsh = W.short_rows_16()
+        y, w = torch.from_numpy(ys).to(dev), torch.from_numpy(wsh).to(dev)
+    elif args.only == "dense":
+        yh, wh = W.nearly_monotone_1e8()
+        y, w = torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
+    else:
+        yh, wh = W.mixed_1e8()
+        y, w = torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
+    print("bench: timing %s" % args.only, file=sys.stderr, flush=True)
+    _, ms, mse, sms, sla, sc = time_fit(torch, B, y, w, args.steps, args.warmup)
+    esz = y.element_size()
+    n_el = y.numel()
+    print(json.dumps({"workload": args.only, "ms_per_call": round(ms, 4), "ms_events": round(mse, 4),
+                      "stage_ms": {k: round(v / max(sc, 1), 4) for k, v in sms.items()},
+                      "hbm_frac": round(n_el * alg_bytes_per_elem(esz, True) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}),
+          flush=True)
 
 
 if __name__ == "__main__":

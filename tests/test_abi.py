@@ -115,7 +115,7 @@ def test_workspace_sizes(lib):
     assert ws(-1, 10, 0, 0) == 0 and ws(1, 10, 9, 0) == 0
     short = ws(65536, 16, 0, 1)
     assert 65536 * 4 <= short < 65536 * 4 + 4096
-    # long rows: per chunk of 2048 a list of up to 256 vertices (18 B each), the dense form's mask
-    # and lane starts, and descriptors: about 3 bytes per element, a quarter of an fp32 weighted input
+    # long rows: per chunk of 16384 a list of up to 256 vertices (18 B each), the dense form's mask,
+    # lane starts and checkpoints, tile marks and descriptors: about 1 byte per element
     big = ws(1, 10 ** 8, 0, 1)
-    assert 2 * 10 ** 8 < big < 4 * 10 ** 8
+    assert 0.5 * 10 ** 8 < big < 2 * 10 ** 8

@@ -3,9 +3,9 @@
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
 //   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
 //               launch of k_wave writes z, block starts and row flags (Section 3.5).
-//   n >  2048   rows split into chunks of 2048 (one wavefront each): k_wave (chunk hulls),
-//               k_scan_reduce + k_scan_apply (chunk starts), ceil(log2 m) launches of
-//               k_merge_level, k_ends, k_fit (Section 3.3 and 3.4).
+//   n >  2048   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
+//               k_chunk (chunk hulls), k_scan_reduce + k_scan_apply (chunk starts),
+//               ceil(log2 m) launches of k_merge_level, k_ends, k_fit (Section 3.3 and 3.4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -15,6 +15,7 @@
 #include "../../include/iso.h"
 #include "../../include/iso_profile.h"
 #include "iso_kernels.h"
+#include "iso_chunk.h"
 
 static_assert(iso::ISO_ROW_NONFINITE_BIT == ISO_ROW_NONFINITE, "flag bits");
 static_assert(iso::ISO_ROW_BAD_WEIGHT_BIT == ISO_ROW_BAD_WEIGHT, "flag bits");
@@ -32,11 +33,12 @@ struct Layout {
   size_t o_rflags = 0, o_any = 0;
   // long rows only
   size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0, o_lx = 0,
-         o_ly = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
+         o_ly = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0, o_ckx = 0, o_cky = 0, o_zt = 0,
+         o_df = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
   int64_t m = 0, nblk = 0;
 };
 
-bool long_rows(int64_t n) { return n > kChunk; }
+bool long_rows(int64_t n) { return n > kShortMax; }
 
 Layout make_layout(int64_t batch, int64_t n) {
   Layout L;
@@ -65,6 +67,10 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.o_mcnt = take(G * (size_t)kMaskW * sizeof(uint16_t));
     L.o_lsx = take(G * (size_t)kWave * sizeof(double));
     L.o_lsy = take(G * (size_t)kWave * sizeof(double));
+    L.o_ckx = take(G * (size_t)kWave * kLaneW * sizeof(double));
+    L.o_cky = take(G * (size_t)kWave * kLaneW * sizeof(double));
+    L.o_zt = take(G * (size_t)kZTiles);
+    L.o_df = take(G);
     L.o_ends = take(G * sizeof(EndInfo));
     L.o_bsum = take((size_t)batch * (size_t)L.nblk * sizeof(double4));
     L.o_bflag = take((size_t)batch * (size_t)L.nblk * sizeof(uint32_t));
@@ -146,8 +152,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int L = lanes_per_row(n);
     const int R = kWave / L;
     const int64_t tiles = (batch + R - 1) / R;
-    hipLaunchKernelGGL((k_wave<T, W, false>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z,
-                       bstart, rflags, batch, n, 0, L, ChunkOut{});
+    hipLaunchKernelGGL((k_wave<T, W>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
+                       rflags, batch, n, L);
     prof.mark(1);
     return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
   }
@@ -167,13 +173,16 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   co.mcnt = (uint16_t*)(ws + Lay.o_mcnt);
   co.lsx = (double*)(ws + Lay.o_lsx);
   co.lsy = (double*)(ws + Lay.o_lsy);
+  co.ckx = (double*)(ws + Lay.o_ckx);
+  co.cky = (double*)(ws + Lay.o_cky);
+  co.ztile = (uint8_t*)(ws + Lay.o_zt);
+  co.dform = (uint8_t*)(ws + Lay.o_df);
   double4* start = (double4*)(ws + Lay.o_start);
   double4* bsum = (double4*)(ws + Lay.o_bsum);
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
   EndInfo* ends = (EndInfo*)(ws + Lay.o_ends);
 
-  hipLaunchKernelGGL((k_wave<T, W, true>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, bstart,
-                     rflags, batch, n, m, kWave, co);
+  hipLaunchKernelGGL((k_chunk<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0,
                      s, co.tot, co.cflags, bsum, bflag, m, nblk);
@@ -184,6 +193,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   S.desc = co.desc;
   S.nseg = co.nseg;
   S.nverts = co.nverts;
+  S.dense = co.dform;
   S.lx = co.lx;
   S.ly = co.ly;
   S.lk = co.lk;
@@ -191,6 +201,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   S.mcnt = co.mcnt;
   S.lsx = co.lsx;
   S.lsy = co.lsy;
+  S.ckx = co.ckx;
+  S.cky = co.cky;
   S.tot = co.tot;
   S.start = start;
   S.y = y;
@@ -211,8 +223,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   hipLaunchKernelGGL((k_ends<T, W>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,
                      batch);
   prof.mark(1);
-  hipLaunchKernelGGL((k_fit<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, S, (const EndInfo*)ends,
-                     (const uint32_t*)rflags, z, bstart);
+  hipLaunchKernelGGL((k_fit<T, W>), dim3((unsigned)G), dim3(kFitThreads), 0, s, S,
+                     (const EndInfo*)ends, (const uint32_t*)rflags, (const uint8_t*)co.ztile, z, bstart);
   prof.mark(1);
   return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
 }
@@ -340,7 +352,7 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
     if (overlaps(gy, bytes, ins[k], insz[k]) || overlaps(gw, bytes, ins[k], insz[k])) return ISO_EINVAL;
   }
   if (overlaps(gy, bytes, gw, bytes)) return ISO_EINVAL;
-  const int64_t ntile = (n + kChunk - 1) / kChunk;
+  const int64_t ntile = (n + kVjpTile - 1) / kVjpTile;
   if (batch * ntile > (int64_t)INT32_MAX) return ISO_EINVAL;
   const int64_t T = batch * ntile;
   hipStream_t s = (hipStream_t)stream;

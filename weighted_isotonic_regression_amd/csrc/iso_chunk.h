@@ -1,0 +1,511 @@
+// iso_chunk.h -- the chunk pass of long rows on gfx950: one wavefront per chunk of 16384 elements,
+// each lane running the monotone chain over its own 256 consecutive points.
+//
+// "Merge Hulls Without Copying Vertices: GPU Isotonic Regression":
+//   Section 3.1  a lane builds the lower hull of its consecutive points by the monotone chain
+//                (pop while the turn is not strictly left, so collinear middle points go).  The
+//                page gives a lane 32 points; here a lane takes 256, so the 64 lanes of a wave
+//                run 64 independent chains and the chunk needs only six merge rounds.
+//   Section 3.2  the lane hulls of the chunk merge pairwise in rounds; the first lane of each
+//                right half walks to the bridge (Lemma 4.2).  A lane's surviving vertices are
+//                always one contiguous range of its stack, so a round only cuts ranges.
+//   Section 3.3  the chunk's hull is emitted for the merge levels, as a vertex list when it is
+//                small and as a bit mask with coordinate checkpoints when it is dense.
+//   Section 6    "Coordinates": a lane works in coordinates relative to its first point; the
+//                chunk-relative coordinates are its start (a wave scan of the lane totals) plus
+//                those.  All sums are fp64.
+//
+// Per lane state: the top two stack entries in registers, the last kRing entries in an LDS ring
+// indexed by depth, the stack as a bit mask in LDS, and the running sums every 32 points (the
+// checkpoints).  An entry that has left the ring is found again from the mask and recomputed
+// from its checkpoint and the inputs; on the measured workloads this is rare (the stacks of noisy
+// rows stay shallow and dense rows never pop).
+//
+// Dense rows: a tile of elements during which a lane popped nothing has had every element pushed
+// as its own block, so the lane writes z = y for it and marks the tile.  The fit pass keeps
+// those values where the final hull confirms single-element blocks (Corollary 4.5) and writes
+// the rest.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "iso_geom.h"
+#include "iso_kernels.h"
+
+namespace iso {
+
+// Per-chunk outputs of the chunk pass.
+struct ChunkOut {
+  double2* tot;       // [G] chunk end point (W, S), chunk-relative
+  int* nverts;        // [G] vertex count of the chunk hull
+  uint32_t* cflags;   // [G] input flags of the chunk
+  Desc* desc;         // [G] leaf segment list
+  int* nseg;          // [G]
+  uint16_t* lk;       // [G * kListCap] list form: chunk point index
+  double* lx;         // [G * kListCap]
+  double* ly;
+  uint32_t* mask;     // [G * kMaskW] dense form: vertex bits of chunk points 0..16384
+  uint16_t* mcnt;     // [G * kMaskW] set bits before each word
+  double* lsx;        // [G * kWave] lane starts (chunk-relative)
+  double* lsy;
+  double* ckx;        // [G * kWave * kLaneW] lane-relative running sums at points 32 j
+  double* cky;
+  uint8_t* ztile;     // [G * kZTiles] 1 where the chunk pass wrote z = y for the load tile
+  uint8_t* dform;     // [G] 1 when the hull is stored in the dense form
+};
+
+__device__ __forceinline__ double turn_pts(double2 p, double2 q, double2 r) {
+  return cross2(q.x - p.x, q.y - p.y, r.x - p.x, r.y - p.y);
+}
+
+// Lanes strictly below lane x (x in 0..64).
+__device__ __forceinline__ uint64_t lanes_below(int x) {
+  return x >= 64 ? ~0ull : ((1ull << x) - 1ull);
+}
+
+// One input element as the chain uses it: a non-finite value or a weight <= 0 is replaced by
+// (y, w) = (0, 1), and its kind is or-ed into f.
+template <bool W>
+__device__ __forceinline__ void classify(double& yd, double& wd, uint32_t& f) {
+  uint32_t fk = 0u;
+  if (!isfinite(yd) || !isfinite(wd)) fk = ISO_ROW_NONFINITE_BIT;
+  else if (!(wd > 0.0)) fk = ISO_ROW_BAD_WEIGHT_BIT;
+  if (fk) {
+    f |= fk;
+    yd = 0.0;
+    wd = 1.0;
+  }
+}
+
+// LDS of one wavefront.
+struct ChunkLds {
+  double2 ring[kRing + 2][kWave];   // stack entries by depth (ring_slot), lane-relative
+  uint16_t ringi[kRing + 2][kWave];  // their point indices (0..256)
+  uint32_t smask[kSubW][kWave];    // stack bit mask over the lane's points 0..256
+  double2 ck[kLaneW][kWave];       // lane-relative running sums at points 32 j
+  int depth[kWave];                // final stack depth
+  int lowv[kWave];                 // lowest depth still held by the ring
+  int lo[kWave], hi[kWave];        // surviving depth range of the lane's stack
+  double2 start[kWave + 1];        // lane starts, chunk-relative; [l + 1] is lane l's end point
+};
+
+// Ring slot of stack depth i: depths 0 and 1 keep slots of their own, deeper ones cycle through
+// kRing slots (an entry of depth i >= 2 is held while i >= the lane's lowest valid depth).
+__device__ __forceinline__ int ring_slot(int i) { return i < 2 ? i : 2 + ((i - 2) & (kRing - 1)); }
+
+// Lane-relative coordinates and point index of lane l's running sums at its point q, from the
+// checkpoint below q and the inputs (the same operations in the same order as the chain).
+template <typename T, bool W>
+__device__ double2 lane_point(const ChunkLds& L, int l, int q, const T* yl, const T* wl) {
+  q = min(max(q, 0), kSub);
+  const int j = min(q / kCk, kLaneW - 1);
+  double2 P = L.ck[j][l];
+  uint32_t f = 0u;
+  for (int e = kCk * j; e < q; ++e) {
+    double yd = (double)yl[e], wd = W ? (double)wl[e] : 1.0;
+    classify<W>(yd, wd, f);
+    if (W) P.x += wd;
+    P.y += wd * yd;
+  }
+  if (!W) P.x = (double)q;
+  return P;
+}
+
+// Lane-relative coordinates and point index q of the stack entry at depth i of lane l.
+template <typename T, bool W>
+__device__ double2 lane_entry(ChunkLds& L, int l, int i, const T* y, const T* w, int64_t off,
+                              int len, int& q) {
+  if (i < 2 || i >= L.lowv[l]) {
+    q = L.ringi[ring_slot(i)][l];
+    return L.ring[ring_slot(i)][l];
+  }
+  int rem = i;  // the entry at depth i is the i-th set bit (from 0) of the stack mask
+  int wd = 0;
+  for (; wd < kSubW - 1; ++wd) {
+    const int pc = __popc(L.smask[wd][l]);
+    if (rem < pc) break;
+    rem -= pc;
+  }
+  uint32_t word = L.smask[wd][l];
+  for (int r = 0; r < rem && word; ++r) word &= word - 1u;
+  // (the stack holds i + 1 entries, so the bit exists; the clamp keeps reads in the lane)
+  q = word ? kCk * wd + __builtin_ctz(word) : 0;
+  q = min(q, min(max(len - kSub * l, 0), kSub));
+  const int64_t eb = off + (int64_t)l * kSub;
+  return lane_point<T, W>(L, l, q, y + eb, W ? w + eb : nullptr);
+}
+
+// Chunk-relative coordinates of the stack entry at depth i of lane l.
+template <typename T, bool W>
+__device__ __forceinline__ double2 chunk_entry(ChunkLds& L, int l, int i, const T* y, const T* w,
+                                               int64_t off, int len) {
+  if (i == 0) return L.start[l];
+  if (i == L.depth[l] - 1) return L.start[l + 1];
+  int q;
+  const double2 P = lane_entry<T, W>(L, l, i, y, w, off, len, q);
+  const double2 S = L.start[l];
+  return double2{W ? S.x + P.x : (double)(kSub * l + q), S.y + P.y};
+}
+
+template <typename T, bool W>
+__global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* __restrict__ w,
+                                              T* __restrict__ z, int64_t n, int m, ChunkOut out) {
+  __shared__ ChunkLds L;
+  constexpr int TN = Tile<T>::N;  // elements per load tile
+  constexpr int VN = Vec16<T>::N;
+  const int lane = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t row = g / m;
+  const int j = (int)(g - row * m);
+  const int64_t off = row * n + (int64_t)j * kChunk;
+  const int64_t rem = n - (int64_t)j * kChunk;
+  const int len = rem < kChunk ? (int)rem : kChunk;
+  const int e0 = kSub * lane;
+  const int c = min(max(len - e0, 0), kSub);         // elements of this lane
+  const int nl = (len + kSub - 1) / kSub;            // lanes holding elements
+  const bool vec = (((uintptr_t)(y + off)) % 16 == 0) && (!W || ((uintptr_t)(w + off)) % 16 == 0) &&
+                   (((uintptr_t)(z + off)) % 16 == 0);
+  const T* yl = y + off + e0;
+  const T* wl = W ? w + off + e0 : nullptr;
+  T* zl = z + off + e0;
+
+  // ---- a1-a3: stream the lane's elements through the chain.  Point P_q (0 < q < c) lies between
+  // the elements q - 1 and q, whose slopes are y_{q-1} and y_q; unless y_{q-1} < y_q it is not a
+  // strict vertex of any hull containing its neighbours, so it is never pushed.
+  for (int wd = 0; wd < kSubW; ++wd) L.smask[wd][lane] = 0u;
+  uint32_t f = 0u;
+  int d = 0, ti = 0, ui = 0, lowv = 2;
+  double2 Tp{0.0, 0.0}, Up{0.0, 0.0};
+  double lx = 0.0, ly = 0.0;
+  double yprev = 0.0;
+  int wi = 0;
+  uint32_t curw = 0u;
+  if (c > 0) {
+    L.ring[0][lane] = Tp;
+    L.ringi[0][lane] = 0;
+    d = 1;
+    curw = 1u;
+  }
+  int pops = 0;
+  // pushes point q with lane-relative coordinates K, popping what it makes non-convex
+  auto push = [&](const double2 K, int q) {
+    bool more = d >= 2 && !(turn_pts(Up, Tp, K) > 0.0);
+    while (more) {
+      const uint32_t bit = 1u << (ti & 31);
+      if ((ti >> 5) == wi) curw &= ~bit;
+      else atomicAnd(&L.smask[ti >> 5][lane], ~bit);
+      ++pops;
+      Tp = Up;
+      ti = ui;
+      --d;
+      more = false;
+      if (d >= 2) {
+        const int dd = d - 2;
+        const int sl = ring_slot(dd);
+        Up = L.ring[sl][lane];
+        ui = L.ringi[sl][lane];
+        if (dd >= 2 && dd < lowv) {
+          // the new under-top has left the ring: the highest stack bit below ti, recomputed
+          int ww = ti >> 5;
+          uint32_t mw = (ww == wi ? curw : L.smask[ww][lane]) & ((1u << (ti & 31)) - 1u);
+          while (mw == 0u) {
+            --ww;
+            mw = (ww == wi) ? curw : L.smask[ww][lane];
+          }
+          ui = kCk * ww + 31 - __builtin_clz(mw);
+          Up = lane_point<T, W>(L, lane, ui, yl, wl);
+        }
+        more = !(turn_pts(Up, Tp, K) > 0.0);
+      }
+    }
+    const int sl = ring_slot(d);
+    L.ring[sl][lane] = K;
+    L.ringi[sl][lane] = (uint16_t)q;
+    lowv = max(lowv, d - kRing + 1);
+    curw |= 1u << (q & 31);
+    Up = Tp;
+    ui = ti;
+    Tp = K;
+    ti = q;
+    ++d;
+  };
+  const int ntiles = (c + TN - 1) / TN;
+  for (int t = 0; t < ntiles; ++t) {
+    const int eb = t * TN;  // lane-relative index of the tile's first element
+    if ((eb & (kCk - 1)) == 0) L.ck[eb / kCk][lane] = double2{lx, ly};
+    if ((eb >> 5) != wi) {  // the tile's points 32 w .. are in mask word w (same for every lane)
+      L.smask[wi][lane] = curw;
+      wi = eb >> 5;
+      curw = 0u;
+    }
+    T yv[TN], wv[TN];
+    if (vec && eb + TN <= c) {
+#pragma unroll
+      for (int k = 0; k < TN / VN; ++k) {
+        load16(yl + eb + k * VN, &yv[k * VN]);
+        if (W) load16(wl + eb + k * VN, &wv[k * VN]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < TN; ++k) {
+        yv[k] = (eb + k < c) ? yl[eb + k] : (T)0;
+        if (W) wv[k] = (eb + k < c) ? wl[eb + k] : (T)1;
+      }
+    }
+    const int pops0 = pops;
+    bool skipped = false;
+#pragma unroll
+    for (int k = 0; k < TN; ++k) {
+      if (eb + k < c) {
+        double yd = (double)yv[k];
+        double wd = W ? (double)wv[k] : 1.0;
+        classify<W>(yd, wd, f);
+        const int q = eb + k;  // the element's left point
+        if (q > 0) {
+          if (yprev < yd) push(double2{W ? lx : (double)q, ly}, q);
+          else skipped = true;
+        }
+        if (W) lx += wd;
+        ly += wd * yd;
+        yprev = yd;
+      }
+    }
+    // speculative fit of a tile that pushed every point and popped none: every element is its
+    // own block so far
+    uint8_t zt = 0;
+    if (pops == pops0 && !skipped && eb + TN <= c && vec) {
+#pragma unroll
+      for (int k = 0; k < TN / VN; ++k) store16(zl + eb + k * VN, &yv[k * VN]);
+      zt = 1;
+    }
+    out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
+  }
+  if (c > 0) {
+    // the lane's end point
+    if ((c >> 5) != wi) {
+      L.smask[wi][lane] = curw;
+      wi = c >> 5;
+      curw = 0u;
+    }
+    push(double2{W ? lx : (double)c, ly}, c);
+    L.smask[wi][lane] = curw;
+  }
+  for (int t = ntiles; t < kSub / TN; ++t) out.ztile[g * (int64_t)kZTiles + (e0 + t * TN) / TN] = 0;
+
+  // ---- lane starts: wave scan of the lane totals (chunk-relative coordinates).
+  double ix = lx, iy = ly;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const double vx = __shfl_up(ix, dd, kWave);
+    const double vy = __shfl_up(iy, dd, kWave);
+    if (lane >= dd) {
+      ix += vx;
+      iy += vy;
+    }
+  }
+  double sx = __shfl_up(ix, 1, kWave), sy = __shfl_up(iy, 1, kWave);
+  if (lane == 0) {
+    sx = 0.0;
+    sy = 0.0;
+  }
+  if (!W) {
+    sx = (double)e0;
+    ix = (double)(e0 + c);
+  }
+  L.start[lane] = double2{sx, sy};
+  if (lane == nl - 1) L.start[lane + 1] = double2{ix, iy};
+  L.depth[lane] = d;
+  L.lowv[lane] = lowv;
+  int lo = 1, hi = d - 1;  // depth 0 is the previous lane's end point (lane 0: the chunk start)
+  L.lo[lane] = lo;
+  L.hi[lane] = hi;
+  __syncthreads();
+
+  // ---- a4: merge rounds.  Node A = lanes [g0, sB), node B = lanes [sB, g0 + size); their
+  // shared point s is lane sB - 1's end point.  A's vertices: (g0, 0), then each lane's range;
+  // B's: each lane's range, ending at lane lb's end point.
+#pragma unroll 1
+  for (int r = 1; r <= 6; ++r) {
+    const int gsz = 1 << r, half = gsz >> 1;
+    const int g0 = lane & ~(gsz - 1);
+    const int sB = g0 + half;
+    const bool merge = sB < nl;
+    const uint64_t nzr = __ballot(lo <= hi);  // lanes with a non-empty range
+    int al = 0, ai = 0, bl = 0, bi = 0;
+    if (merge && lane == sB) {
+      const int lb = min(g0 + gsz, nl) - 1;
+      al = sB - 1;
+      ai = L.depth[al] - 1;                        // alpha = s
+      bl = min(__builtin_ctzll(nzr & ~lanes_below(sB)), lb);  // beta = B's first vertex
+      bi = L.lo[bl];
+      double2 Pa = chunk_entry<T, W>(L, al, ai, y, w, off, len);
+      double2 Pb = chunk_entry<T, W>(L, bl, bi, y, w, off, len);
+      for (int pass = 0; pass <= kChunk; ++pass) {
+        bool moved = false;
+        // alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
+        while (!(al == g0 && ai == 0)) {
+          int pl, pi;
+          if (ai > max(L.lo[al], 1)) {
+            pl = al;
+            pi = ai - 1;
+          } else {
+            const uint64_t below = nzr & lanes_below(al) & ~lanes_below(g0);
+            if (below) {
+              pl = 63 - __builtin_clzll(below);
+              pi = L.hi[pl];
+            } else {
+              pl = g0;
+              pi = 0;
+            }
+          }
+          const double2 Pp = chunk_entry<T, W>(L, pl, pi, y, w, off, len);
+          if (turn_pts(Pp, Pa, Pb) > 0.0) break;
+          al = pl;
+          ai = pi;
+          Pa = Pp;
+          moved = true;
+        }
+        // beta moves right while (alpha, beta, succ beta) is not a strict left turn
+        while (!(bl == lb && bi == L.depth[lb] - 1)) {
+          int ql, qi;
+          if (bi < L.hi[bl]) {
+            ql = bl;
+            qi = bi + 1;
+          } else {
+            ql = min(__builtin_ctzll(nzr & ~lanes_below(bl + 1)), lb);
+            qi = max(L.lo[ql], 1);
+          }
+          const double2 Pq = chunk_entry<T, W>(L, ql, qi, y, w, off, len);
+          if (turn_pts(Pa, Pb, Pq) > 0.0) break;
+          bl = ql;
+          bi = qi;
+          Pb = Pq;
+          moved = true;
+        }
+        if (!moved) break;
+      }
+    }
+    const int src = merge ? sB : lane;
+    al = __shfl(al, src, kWave);
+    ai = __shfl(ai, src, kWave);
+    bl = __shfl(bl, src, kWave);
+    bi = __shfl(bi, src, kWave);
+    if (merge) {
+      if (lane == al) hi = ai;
+      if (lane > al && lane < bl) {
+        lo = 1;
+        hi = 0;
+      }
+      if (lane == bl) lo = bi;
+    }
+    L.lo[lane] = lo;
+    L.hi[lane] = hi;
+    __syncthreads();
+  }
+
+  // ---- a5: emit.
+  const bool nonempty = lo <= hi;
+  const int cnt = (nonempty ? hi - lo + 1 : 0) + (lane == 0 ? 1 : 0);
+  int incl = cnt;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int v = __shfl_up(incl, dd, kWave);
+    if (lane >= dd) incl += v;
+  }
+  const int total = __shfl(incl, kWave - 1, kWave);
+  const int rank = incl - cnt;
+  const uint32_t fl = (__ballot((f & ISO_ROW_NONFINITE_BIT) != 0) ? ISO_ROW_NONFINITE_BIT : 0u) |
+                      (__ballot((f & ISO_ROW_BAD_WEIGHT_BIT) != 0) ? ISO_ROW_BAD_WEIGHT_BIT : 0u);
+  // coordinates of every surviving entry are at hand (no recomputation) unless the range reaches
+  // below the ring among depths 2 .. d - 2
+  const int ha = max(lo, 2), hb = min(hi, d - 2);
+  const bool held = !nonempty || ha > hb || ha >= lowv;
+  const bool listable = total <= kListCap && __all(held);
+  if (lane == 0) {
+    out.nverts[g] = total;
+    out.desc[g] = make_int4(j, 0, total - 1, 0);
+    out.nseg[g] = 1;
+    out.cflags[g] = fl;
+    out.dform[g] = listable ? 0 : 1;
+    const double2 E = L.start[nl];
+    out.tot[g] = make_double2(E.x, E.y);
+  }
+  if (listable) {
+    const int64_t lb0 = g * (int64_t)kListCap;
+    int pos = rank;
+    if (lane == 0) {
+      out.lk[lb0] = 0;
+      out.lx[lb0] = 0.0;
+      out.ly[lb0] = 0.0;
+      pos = 1;
+    }
+    for (int i = lo; i <= hi; ++i) {
+      int q = c;
+      if (i != d - 1) (void)lane_entry<T, W>(L, lane, i, y, w, off, len, q);
+      const double2 P = chunk_entry<T, W>(L, lane, i, y, w, off, len);
+      out.lk[lb0 + pos] = (uint16_t)(e0 + q);
+      out.lx[lb0 + pos] = P.x;
+      out.ly[lb0 + pos] = P.y;
+      ++pos;
+    }
+    return;
+  }
+  // dense form: vertex bits of the chunk's points, set bits before each word, lane starts and
+  // checkpoints (coordinates are recomputed from these and the inputs)
+  int qlo = kSub + 1, qhi = -1;  // the stack bits of depths lo..hi span points [qlo, qhi]
+  if (nonempty) {
+    (void)lane_entry<T, W>(L, lane, lo, y, w, off, len, qlo);
+    if (hi == d - 1) qhi = c;
+    else (void)lane_entry<T, W>(L, lane, hi, y, w, off, len, qhi);
+  }
+  // bit 0 of the lane's first word is the previous lane's end point
+  const int top_kept = (nonempty && hi == d - 1 && c == kSub) ? 1 : 0;
+  const int prev_top = __shfl(top_kept, lane > 0 ? lane - 1 : 0, kWave);
+  const int64_t mb = g * (int64_t)kMaskW;
+  uint32_t words[kLaneW];
+  int pc = 0;
+#pragma unroll
+  for (int wd = 0; wd < kLaneW; ++wd) {
+    uint32_t v = L.smask[wd][lane];
+    const int a = qlo - kCk * wd, b = qhi - kCk * wd;  // keep bits a..b
+    uint32_t keep = 0u;
+    if (b >= 0 && a <= 31) {
+      const int a2 = max(a, 0), b2 = min(b, 31);
+      keep = (b2 >= 31 ? 0xffffffffu : ((2u << b2) - 1u)) & ~((1u << a2) - 1u);
+    }
+    v &= keep;
+    if (wd == 0) v = (v & ~1u) | (lane == 0 ? 1u : (uint32_t)prev_top);
+    words[wd] = v;
+    pc += __popc(v);
+  }
+  int wincl = pc;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int v = __shfl_up(wincl, dd, kWave);
+    if (lane >= dd) wincl += v;
+  }
+  int run = wincl - pc;
+#pragma unroll
+  for (int wd = 0; wd < kLaneW; ++wd) {
+    out.mask[mb + kLaneW * lane + wd] = words[wd];
+    out.mcnt[mb + kLaneW * lane + wd] = (uint16_t)run;
+    run += __popc(words[wd]);
+  }
+  if (lane == kWave - 1) {
+    out.mask[mb + kMaskW - 1] = (len == kChunk) ? (uint32_t)top_kept : 0u;
+    out.mcnt[mb + kMaskW - 1] = (uint16_t)run;
+  }
+  const int64_t sb = g * (int64_t)kWave;
+  if (W) out.lsx[sb + lane] = L.start[lane].x;
+  out.lsy[sb + lane] = L.start[lane].y;
+  const int64_t cb = (g * kWave + lane) * (int64_t)kLaneW;
+#pragma unroll
+  for (int jj = 0; jj < kLaneW; ++jj) {
+    const double2 P = L.ck[jj][lane];
+    if (W) out.ckx[cb + jj] = P.x;
+    out.cky[cb + jj] = P.y;
+  }
+}
+
+}  // namespace iso

@@ -28,11 +28,19 @@
 namespace iso {
 
 constexpr int kWave = 64;                    // lanes of a wavefront
-constexpr int kLanePts = 32;                 // elements per lane
-constexpr int kChunk = kWave * kLanePts;     // elements per chunk (one wavefront)
+constexpr int kLanePts = 32;                 // elements per lane of a packed short-row tile
+constexpr int kShortMax = kWave * kLanePts;  // rows of at most this many elements are packed
+constexpr int kSub = 256;                    // points per lane of a long-row chunk
+constexpr int kChunk = kWave * kSub;         // elements per chunk of a long row (one wavefront)
+constexpr int kCk = 32;                      // spacing of a lane's running-sum checkpoints
+constexpr int kLaneW = kSub / kCk;           // mask words (and checkpoints) per lane
+constexpr int kSubW = kLaneW + 1;            // mask words of a lane's points 0..256
+constexpr int kRing = 16;                    // stack entries a lane keeps in LDS
 constexpr int kListCap = 256;                // chunks with at most this many hull vertices keep a list
-constexpr int kMaskW = kWave + 1;            // mask words of a chunk (points 0..C)
+constexpr int kMaskW = kChunk / 32 + 1;      // mask words of a chunk (points 0..16384)
+constexpr int kZTiles = kChunk / 16;         // load tiles of a chunk (16 or 32 elements each)
 constexpr int kWalkCap = 64;                 // walk steps of a merge before it switches to search
+constexpr int kVjpTile = kWave * 32;         // elements per backward tile (one wavefront)
 
 // Per-row input flags (same values as ISO_ROW_NONFINITE / ISO_ROW_BAD_WEIGHT of iso.h).
 constexpr uint32_t ISO_ROW_NONFINITE_BIT = 1u;
@@ -246,26 +254,30 @@ ISO_HD double gslope(const GPt& a, const GPt& b) {
 using Desc = int4;
 
 // ------------------------------------------------------------------ chunk hull storage
-// A chunk's hull is stored in one of two forms, chosen by its vertex count V:
-//   list   (V <= kListCap): the vertices' chunk-relative coordinates and point indices.
-//   dense  (V >  kListCap): the vertex bit mask (65 words), the number of set bits before each
-//          word, and the coordinates of every lane's first point.  A vertex's coordinates are
-//          recomputed from its lane's start and the inputs, with the same fp64 operations in the
-//          same order as the chunk pass, so they are bitwise the values the chunk pass used.
+// A chunk's hull is stored in one of two forms:
+//   list   the vertices' chunk-relative coordinates and chunk point indices, in order (hulls of
+//          at most kListCap vertices whose coordinates the chunk pass had at hand);
+//   dense  the vertex bit mask of the chunk's points 0..16384, the number of set bits before
+//          each word, the lane starts and every lane's running sums at each 32nd point.  A
+//          vertex's coordinates are recomputed from these and the inputs with the same fp64
+//          operations in the same order as the chunk pass, so they are bitwise its values.
 // Dense chunks are the ones whose points nearly all survive; storing them as lists would move
-// about 18 bytes per element, while the mask and lane starts take under one.
+// about 18 bytes per element, while the dense form takes under one.
 template <typename T, bool W>
 struct VertexStore {
   Desc* desc;             // [G] descriptor slots
   int* nseg;              // [G] length of the list of the node starting at this slot
   const int* nverts;      // [G] vertex count of each chunk hull
+  const uint8_t* dense;   // [G] 1 for the dense form
   const double* lx;       // [G * kListCap] list form
   const double* ly;
   const uint16_t* lk;
   const uint32_t* mask;   // [G * kMaskW] dense form
   const uint16_t* mcnt;   // [G * kMaskW]
-  const double* lsx;      // [G * kWave]  (weighted only)
+  const double* lsx;      // [G * kWave]  lane starts (weighted only)
   const double* lsy;      // [G * kWave]
+  const double* ckx;      // [G * kWave * kLaneW] lane-relative running sums (weighted only)
+  const double* cky;
   const double2* tot;     // [G] chunk end point (W, S)
   const double4* start;   // [G] chunk start {x hi, x lo, y hi, y lo}
   const T* y;
@@ -273,12 +285,49 @@ struct VertexStore {
   int64_t n;              // row length
   int m;                  // chunks per row
 
-  ISO_HD bool is_list(int64_t g) const { return nverts[g] <= kListCap; }
+  ISO_HD bool is_list(int64_t g) const { return dense[g] == 0; }
+
+  // Chunk-relative coordinates of point k (0..len) of dense chunk j of `row`.
+  ISO_HD void dense_point(int64_t row, int j, int k, double& x, double& yy) const {
+    const int64_t g = row * m + j;
+    const int64_t rem = n - (int64_t)j * kChunk;
+    const int len = rem < kChunk ? (int)rem : kChunk;
+    if (k == len) {
+      const double2 t = tot[g];
+      x = t.x;
+      yy = t.y;
+      return;
+    }
+    const int l = k / kSub, q = k % kSub;
+    const double sx = W ? lsx[g * kWave + l] : (double)(kSub * l);
+    const double sy = lsy[g * kWave + l];
+    if (q == 0) {
+      x = sx;
+      yy = sy;
+      return;
+    }
+    const int jj = q / kCk;
+    const int64_t cb = (g * kWave + l) * kLaneW + jj;
+    double ax = W ? ckx[cb] : 0.0, ay = cky[cb];
+    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
+    for (int e = kCk * jj; e < q; ++e) {
+      double wd = W ? (double)w[e0 + e] : 1.0;
+      double yd = (double)y[e0 + e];
+      if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
+        yd = 0.0;
+        wd = 1.0;
+      }
+      if (W) ax += wd;
+      ay += wd * yd;
+    }
+    x = W ? sx + ax : (double)k;
+    yy = sy + ay;
+  }
 
   // Chunk-relative coordinates and point index of vertex p of chunk j of `row`.
   ISO_HD void local(int64_t row, int j, int p, double& x, double& yy, int& k) const {
     const int64_t g = row * m + j;
-    if (nverts[g] <= kListCap) {
+    if (dense[g] == 0) {
       const int64_t idx = g * kListCap + p;
       x = lx[idx];
       yy = ly[idx];
@@ -295,25 +344,8 @@ struct VertexStore {
     }
     uint32_t word = mask[g * kMaskW + lo];
     for (int r = p - (int)mc[lo]; r > 0; --r) word &= word - 1u;
-    const int b = __builtin_ctz(word);
-    k = lo * kLanePts + b;
-    const int64_t rem = n - (int64_t)j * kChunk;
-    if (k == (rem < kChunk ? (int)rem : kChunk)) {  // the chunk's end point
-      const double2 t = tot[g];
-      x = t.x;
-      yy = t.y;
-      return;
-    }
-    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)lo * kLanePts;
-    double ax = 0.0, ay = 0.0;
-    for (int i = 0; i < b; ++i) {
-      const double wd = W ? (double)w[e0 + i] : 1.0;
-      const double yd = (double)y[e0 + i];
-      if (W) ax += wd;
-      ay += wd * yd;
-    }
-    x = W ? lsx[g * kWave + lo] + ax : (double)k;
-    yy = lsy[g * kWave + lo] + ay;
+    k = lo * 32 + __builtin_ctz(word);
+    dense_point(row, j, k, x, yy);
   }
 
   ISO_HD GPt pt(int64_t row, int j, int p) const {

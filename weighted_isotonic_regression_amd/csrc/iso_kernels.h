@@ -1,13 +1,12 @@
 // iso_kernels.h -- HIP kernels of the isotonic fit for gfx950 (wave64).
 //
 // Pipeline ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 3):
-//   k_wave          one wavefront per tile of <= 2048 elements: coalesced 16-byte loads, fp64
+//   k_wave          rows of at most 2048 elements, packed L = 1, 2, .., 64 lanes per row and
+//                   64 / L rows per wavefront (Section 3.5): coalesced 16-byte loads, fp64
 //                   cumulative sums in LDS (lane-serial, then a wave scan of lane totals), lane
 //                   hulls by the bit-mask monotone chain (Section 3.1), pairwise walks merging
-//                   lane hulls (Section 3.2).  A tile is either a group of short rows (L lanes per
-//                   row, 64 / L rows per wave, Section 3.5), finished here, or one chunk of a long
-//                   row, whose hull is stored as a vertex list (sparse hulls) or as a bit mask plus
-//                   lane starts with the chunk's own fit written to z (dense hulls).
+//                   lane hulls (Section 3.2); writes z and block starts.
+//   k_chunk         (iso_chunk.h) the chunk pass of longer rows.
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
 //   k_merge_level   one launch per level of the merge tree: segment lists merged by walk, capped
@@ -66,6 +65,29 @@ __device__ __forceinline__ void vload(const T* p, T* out) {
   }
 }
 
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, T* out) {
+  vload(p, out);
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const T* in) {
+  using V = typename Vec16<T>::type;
+  V v;
+  if constexpr (Vec16<T>::N == 4) {
+    v = V{in[0], in[1], in[2], in[3]};
+  } else {
+    v = V{in[0], in[1]};
+  }
+  *reinterpret_cast<V*>(p) = v;
+}
+
+// Elements per load tile of the chunk pass: 128 bytes of each input per lane.
+template <typename T>
+struct Tile {
+  static constexpr int N = 128 / (int)sizeof(T);
+};
+
 // q = e / d for 0 <= e < 4096, 1 <= d <= 2048 (float reciprocal, corrected to exact).
 __device__ __forceinline__ int small_div(int e, int d, float inv) {
   int q = (int)((float)e * inv);
@@ -73,22 +95,6 @@ __device__ __forceinline__ int small_div(int e, int d, float inv) {
   else if ((q + 1) * d <= e) ++q;
   return q;
 }
-
-// Per-chunk outputs of a long row's wave pass.
-struct ChunkOut {
-  double2* tot;       // chunk totals (W, S) = coordinates of the chunk's end point
-  int* nverts;        // vertex count of the chunk hull
-  uint32_t* cflags;   // per-chunk input flags
-  Desc* desc;         // leaf segment list
-  int* nseg;
-  double* lx;         // list form [G * kListCap]
-  double* ly;
-  uint16_t* lk;
-  uint32_t* mask;     // dense form [G * kMaskW]
-  uint16_t* mcnt;
-  double* lsx;        // [G * kWave]
-  double* lsy;
-};
 
 template <bool W>
 struct TilePts {
@@ -102,11 +108,11 @@ struct TilePts {
   }
 };
 
-template <typename T, bool W, bool CHUNK>
+template <typename T, bool W>
 __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
                                              T* __restrict__ z, uint8_t* __restrict__ bstart,
                                              uint32_t* __restrict__ rflags, int64_t batch,
-                                             int64_t n, int m, int Lpack, ChunkOut out) {
+                                             int64_t n, int Lpack) {
   __shared__ double sX[W ? kLdsPts : 1];
   __shared__ double sY[kLdsPts];
   __shared__ uint32_t sM[kMaskWords];
@@ -114,26 +120,13 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
 
   constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
-  int L, rows, seglen, j = 0;
-  int64_t off, row0, g = 0;
-  if (CHUNK) {
-    g = blockIdx.x;
-    row0 = g / m;
-    j = (int)(g - row0 * m);
-    off = row0 * n + (int64_t)j * kChunk;
-    int64_t rem = n - (int64_t)j * kChunk;
-    seglen = rem < kChunk ? (int)rem : kChunk;
-    L = kWave;
-    rows = 1;
-  } else {
-    L = Lpack;
-    const int R = kWave / L;
-    row0 = (int64_t)blockIdx.x * R;
-    int64_t left = batch - row0;
-    rows = left < R ? (int)left : R;
-    off = row0 * n;
-    seglen = (int)n;
-  }
+  const int L = Lpack;
+  const int R = kWave / L;
+  const int64_t row0 = (int64_t)blockIdx.x * R;
+  const int64_t left = batch - row0;
+  const int rows = left < R ? (int)left : R;
+  const int64_t off = row0 * n;
+  const int seglen = (int)n;
   const int rowStride = kLanePts * L + 1;
   const int maskStride = L + 1;
   const int E = rows * seglen;  // elements of the tile, contiguous from off
@@ -181,7 +174,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
     if (e < E) {
       double yd = (double)yv[k];
       double wd = W ? (double)wv[k] : 1.0;
-      const int r = CHUNK ? 0 : small_div(e, seglen, inv_seg);
+      const int r = small_div(e, seglen, inv_seg);
       const int i = e - r * seglen;
       uint32_t f = 0u;
       if (!isfinite(yd) || !isfinite(wd)) f = ISO_ROW_NONFINITE_BIT;
@@ -212,7 +205,6 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   const int rbase = r2 * rowStride;
   const int pbase = rbase + kLanePts * ql;
   const int nl = (seglen + kLanePts - 1) / kLanePts;  // active lanes of a row segment
-  double lane_sx = 0.0, lane_sy = 0.0;                // coordinates of the lane's point 0
   {
     double tx = 0.0, ty = 0.0;
     for (int k = 0; k < kLanePts; ++k) {
@@ -237,8 +229,6 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       sx0 = 0.0;
       sy0 = 0.0;
     }
-    lane_sx = sx0;
-    lane_sy = sy0;
     double lx = 0.0, ly = 0.0;
     for (int k = 0; k < kLanePts; ++k) {
       if (k < c) {
@@ -294,72 +284,12 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   }
 
   // ---- a5: emit.
-  bool write_z = !CHUNK;
-  if (CHUNK) {
-    uint32_t m0 = sM[lane];
-    const uint32_t m1 = (lane == kWave - 1) ? sM[kWave] : 0u;
-    const int cnt = __popc(m0) + __popc(m1);
-    int incl = cnt;
-    for (int d = 1; d < kWave; d <<= 1) {
-      int v = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += v;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    const int rank = incl - cnt;
-    TilePts<W> Prow{sX, sY, 0};
-    if (total <= kListCap) {
-      // list form
-      const int64_t lb = g * (int64_t)kListCap;
-      int pos = rank;
-      uint32_t mm = m0;
-      while (mm) {
-        const int b = __builtin_ctz(mm);
-        mm &= mm - 1u;
-        const int k = kLanePts * lane + b;
-        double xx, yy;
-        Prow(k, xx, yy);
-        out.lk[lb + pos] = (uint16_t)k;
-        out.lx[lb + pos] = xx;
-        out.ly[lb + pos] = yy;
-        ++pos;
-      }
-      if (m1) {
-        const int k = kLanePts * kWave;  // the chunk's end point (bit 0 of word 64)
-        double xx, yy;
-        Prow(k, xx, yy);
-        out.lk[lb + pos] = (uint16_t)k;
-        out.lx[lb + pos] = xx;
-        out.ly[lb + pos] = yy;
-      }
-    } else {
-      // dense form: mask, set bits before each word, lane starts; the chunk's fit goes to z
-      const int64_t mb = g * (int64_t)kMaskW;
-      out.mask[mb + lane] = m0;
-      out.mcnt[mb + lane] = (uint16_t)rank;
-      if (lane == kWave - 1) {
-        out.mask[mb + kWave] = m1;
-        out.mcnt[mb + kWave] = (uint16_t)(rank + __popc(m0));
-      }
-      if (W) out.lsx[g * kWave + lane] = lane_sx;
-      out.lsy[g * kWave + lane] = lane_sy;
-      write_z = true;
-    }
-    if (lane == 0) {
-      out.nverts[g] = total;
-      out.desc[g] = make_int4(j, 0, total - 1, 0);
-      out.nseg[g] = 1;
-      out.cflags[g] = sF[0];
-      double xx, yy;
-      Prow(seglen, xx, yy);
-      out.tot[g] = make_double2(xx, yy);
-    }
-  }
-  if (write_z) {
+  {
     // Element-parallel: element e (row r, index i) gets the slope of the tile hull's edge over
     // it, from the vertex at or before point i to the vertex after it.  Consecutive lanes write
     // consecutive elements.
     for (int e = lane; e < E; e += kWave) {
-      const int r = CHUNK ? 0 : small_div(e, seglen, inv_seg);
+      const int r = small_div(e, seglen, inv_seg);
       const int i = e - r * seglen;
       const uint32_t* Mr = &sM[r * maskStride];
       TilePts<W> Pr{sX, sY, r * rowStride};
@@ -374,7 +304,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       z[off + e] = bad ? (T)NAN : (T)slope;
       if (bstart) bstart[off + e] = (!bad && isv) ? 1 : 0;
     }
-    if (!CHUNK && rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
+    if (rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
   }
 }
 
@@ -521,62 +451,90 @@ __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W> S, EndInfo* __re
 }
 
 // ------------------------------------------------------------------ fit
-// One wavefront per chunk, element-parallel (consecutive lanes, consecutive elements).
-//   dense chunks: z already holds the chunk hull's slopes; they are final inside the chunk's
-//                 surviving range [klo, khi), so only the elements outside it are written.
-//   list chunks:  every element is written: the in/out slopes outside [klo, khi), inside it the
-//                 slope of the surviving local edge above the element.
+// One workgroup of 256 threads per chunk, element-parallel (consecutive threads, consecutive
+// elements).  Elements outside the chunk's surviving vertex range [klo, khi) lie under the edges
+// into and out of it; inside it they lie under the chunk hull's own edges (Corollary 4.5).
+//   list chunks:  the surviving vertices' point indices and the slopes between them are staged in
+//                 LDS and each element finds its edge by binary search.
+//   dense chunks: the chunk pass wrote z = y for load tiles in which nothing was popped; an
+//                 element there whose two points are both hull vertices is its own block and is
+//                 left alone.  Other elements get the slope of their edge, its end points
+//                 recomputed from the lane checkpoints (a one-element edge is the element's y).
+constexpr int kFitThreads = 256;
+
 template <typename T, bool W>
-__global__ __launch_bounds__(64) void k_fit(VertexStore<T, W> S, const EndInfo* __restrict__ ends,
-                                            const uint32_t* __restrict__ rflags, T* __restrict__ z,
-                                            uint8_t* __restrict__ bstart) {
+__global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
+                                                     const EndInfo* __restrict__ ends,
+                                                     const uint32_t* __restrict__ rflags,
+                                                     const uint8_t* __restrict__ ztile,
+                                                     T* __restrict__ z, uint8_t* __restrict__ bstart) {
   __shared__ double sSlope[kListCap];
   __shared__ int sK[kListCap];
+  __shared__ uint32_t sMask[kMaskW];
+  constexpr int TN = Tile<T>::N;
   const int64_t g = blockIdx.x;
   const int64_t row = g / S.m;
   const int j = (int)(g - row * S.m);
   const int64_t off = row * S.n + (int64_t)j * kChunk;
   const int64_t rem = S.n - (int64_t)j * kChunk;
   const int len = rem < kChunk ? (int)rem : kChunk;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const EndInfo e = ends[g];
   if (rflags[row] != 0u) {
-    for (int i = lane; i < len; i += kWave) {
+    for (int i = tid; i < len; i += kFitThreads) {
       z[off + i] = (T)NAN;
       if (bstart) bstart[off + i] = 0;
     }
     return;
   }
-  const bool dense = S.nverts[g] > kListCap;
   if (e.lo < 0) {
     const T zv = (T)e.sin;
-    for (int i = lane; i < len; i += kWave) {
+    for (int i = tid; i < len; i += kFitThreads) {
       z[off + i] = zv;
       if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
     }
     return;
   }
-  if (dense) {
-    const T zin = (T)e.sin, zout = (T)e.sout;
-    for (int i = lane; i < e.klo; i += kWave) {
-      z[off + i] = zin;
-      if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
-    }
-    for (int i = e.khi + lane; i < len; i += kWave) {
-      z[off + i] = zout;
-      if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
+  const T zin = (T)e.sin, zout = (T)e.sout;
+  if (!S.is_list(g)) {
+    for (int q = tid; q < kMaskW; q += kFitThreads) sMask[q] = S.mask[g * kMaskW + q];
+    __syncthreads();
+    for (int i = tid; i < len; i += kFitThreads) {
+      if (i < e.klo) {
+        z[off + i] = zin;
+        if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
+        continue;
+      }
+      if (i >= e.khi) {
+        z[off + i] = zout;
+        if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
+        continue;
+      }
+      const bool vl = (sMask[i >> 5] >> (i & 31)) & 1u;
+      const bool vr = (sMask[(i + 1) >> 5] >> ((i + 1) & 31)) & 1u;
+      if (bstart) bstart[off + i] = vl ? 1 : 0;
+      if (vl && vr) {
+        if (!ztile[g * kZTiles + i / TN]) z[off + i] = S.y[off + i];
+        continue;
+      }
+      const int a = vl ? i : mask_pred(sMask, i);
+      const int b = mask_succ(sMask, i);
+      double ax, ay, bx, by;
+      S.dense_point(row, j, a, ax, ay);
+      S.dense_point(row, j, b, bx, by);
+      z[off + i] = (T)((by - ay) / (bx - ax));
     }
     return;
   }
   // list form: stage the surviving vertices' point indices and the slopes of the edges between
   const int nv = e.hi - e.lo + 1;
   const int64_t lb = g * (int64_t)kListCap + e.lo;
-  for (int q = lane; q < nv; q += kWave) {
+  for (int q = tid; q < nv; q += kFitThreads) {
     sK[q] = S.lk[lb + q];
     if (q + 1 < nv) sSlope[q] = (S.ly[lb + q + 1] - S.ly[lb + q]) / (S.lx[lb + q + 1] - S.lx[lb + q]);
   }
   __syncthreads();
-  for (int i = lane; i < len; i += kWave) {
+  for (int i = tid; i < len; i += kFitThreads) {
     double zv;
     uint8_t st = 0;
     if (i < e.klo) {
@@ -658,9 +616,9 @@ __global__ __launch_bounds__(64) void k_vjp_tiles(const T* __restrict__ g, const
   const int64_t tid = blockIdx.x;
   const int64_t row = tid / ntile;
   const int tt = (int)(tid - row * ntile);
-  const int64_t off = row * n + (int64_t)tt * kChunk;
-  const int64_t rem = n - (int64_t)tt * kChunk;
-  const int len = rem < kChunk ? (int)rem : kChunk;
+  const int64_t off = row * n + (int64_t)tt * kVjpTile;
+  const int64_t rem = n - (int64_t)tt * kVjpTile;
+  const int len = rem < kVjpTile ? (int)rem : kVjpTile;
   const int lane = threadIdx.x;
   const int i0 = kLanePts * lane;
   int c = len - i0;
@@ -758,9 +716,9 @@ __global__ __launch_bounds__(64) void k_vjp_apply(const T* __restrict__ g, const
   const int64_t tid = blockIdx.x;
   const int64_t row = tid / ntile;
   const int tt = (int)(tid - row * ntile);
-  const int64_t off = row * n + (int64_t)tt * kChunk;
-  const int64_t rem = n - (int64_t)tt * kChunk;
-  const int len = rem < kChunk ? (int)rem : kChunk;
+  const int64_t off = row * n + (int64_t)tt * kVjpTile;
+  const int64_t rem = n - (int64_t)tt * kVjpTile;
+  const int len = rem < kVjpTile ? (int)rem : kVjpTile;
   const int lane = threadIdx.x;
   const int i0 = kLanePts * lane;
   int c = len - i0;
