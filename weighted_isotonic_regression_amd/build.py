@@ -13,7 +13,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "iso_api.hip")
-DEPS = [os.path.join(HERE, "csrc", f) for f in ("iso_geom.h", "iso_kernels.h", "iso_chunk.h")] + [
+DEPS = [os.path.join(HERE, "csrc", f) for f in ("iso_geom.h", "iso_kernels.h", "iso_chunk.h", "iso_merge.h")] + [
     os.path.join(ROOT, "include", "iso.h")]
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libiso_mi355x.so")

@@ -5,7 +5,7 @@
 //               launch of k_wave writes z, block starts and row flags (Section 3.5).
 //   n >  2048   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
 //               k_chunk (chunk hulls), k_scan_reduce + k_scan_apply (chunk starts),
-//               ceil(log2 m) launches of k_merge_level, k_ends, k_fit (Section 3.3 and 3.4).
+//               ceil(log2 m) launches of k_merge_wave, k_ends, k_fit (Section 3.3 and 3.4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -16,6 +16,7 @@
 #include "../../include/iso_profile.h"
 #include "iso_kernels.h"
 #include "iso_chunk.h"
+#include "iso_merge.h"
 
 static_assert(iso::ISO_ROW_NONFINITE_BIT == ISO_ROW_NONFINITE, "flag bits");
 static_assert(iso::ISO_ROW_BAD_WEIGHT_BIT == ISO_ROW_BAD_WEIGHT, "flag bits");
@@ -215,9 +216,9 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int span = 1 << (r + 1);
     const int per_row = (m - (1 << r) + span - 1) / span;
     const int64_t merges = batch * (int64_t)per_row;
-    const int64_t blocks = (merges + 255) / 256;
-    hipLaunchKernelGGL((k_merge_level<T, W>), dim3((unsigned)blocks), dim3(256), 0, s, S, batch, r,
-                       per_row);
+    const int64_t blocks = (merges + kMergeWaves - 1) / kMergeWaves;
+    hipLaunchKernelGGL((k_merge_wave<T, W>), dim3((unsigned)blocks), dim3(kMergeWaves * kWave), 0, s, S,
+                       batch, r, per_row);
   }
   prof.mark(levels);
   hipLaunchKernelGGL((k_ends<T, W>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,

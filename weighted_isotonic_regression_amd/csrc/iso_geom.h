@@ -334,14 +334,14 @@ struct VertexStore {
       k = lk[idx];
       return;
     }
-    // select: the word holding the p-th set bit, then the bit within it
+    // select: the word holding the p-th set bit (the last word whose count of earlier set bits
+    // is <= p), starting from where it would be if the bits were spread evenly, then the bit
     const uint16_t* mc = mcnt + g * kMaskW;
-    int lo = 0, hi = kMaskW - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)mc[mid] <= p) lo = mid;
-      else hi = mid - 1;
-    }
+    const int V = nverts[g] > 0 ? nverts[g] : 1;
+    int lo = (int)(((int64_t)p * (kMaskW - 1)) / V);
+    lo = lo < 0 ? 0 : (lo > kMaskW - 1 ? kMaskW - 1 : lo);
+    while (lo > 0 && (int)mc[lo] > p) --lo;
+    while (lo + 1 < kMaskW && (int)mc[lo + 1] <= p) ++lo;
     uint32_t word = mask[g * kMaskW + lo];
     for (int r = p - (int)mc[lo]; r > 0; --r) word &= word - 1u;
     k = lo * 32 + __builtin_ctz(word);

@@ -1,0 +1,259 @@
+// iso_merge.h -- one level of the segment-list merge tree with one wavefront per merge (gfx950).
+//
+// "Merge Hulls Without Copying Vertices: GPU Isotonic Regression":
+//   Section 3.3 / Definition 4.3 / Theorem 4.4  a node's hull is a list of segments (chunk,
+//                first, last) of chunk hulls, stored in the descriptor slots of its chunks; a merge
+//                cuts one segment of each child and moves the right child's tail down.
+//   Lemma 4.2    the bridge is found by walking from the shared point s: alpha moves left while
+//                (pred alpha, alpha, beta) is not a strict left turn, beta right symmetrically,
+//                until neither moves (alpha the leftmost, beta the rightmost contact).
+//   Section 5.2  a walk that runs long is replaced by a search (here the Overmars-van Leeuwen
+//                bisection of iso_geom.h).
+//
+// On the page a level runs one thread per merge when it has many merges.  Here every merge has
+// a wavefront, which walks 64 vertices at a time: the lanes gather the next 64 vertices of the
+// walk (the segments' lengths come from one coalesced read of 64 descriptors and a wave scan),
+// test the walk's predicate on all of them at once and take the first stop with a ballot.  The
+// tail of the right child's list is moved by all lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "iso_geom.h"
+
+namespace iso {
+
+constexpr int kMergeWaves = 4;   // merges per workgroup of 256
+constexpr int kWinCap = 32;      // walk windows of one side pass before switching to the search
+
+struct MergeLds {
+  int cum[kWave];
+  Desc d[kWave];
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ GPt shfl_up_pt(const GPt& p, int lane) {
+  GPt r;
+  r.x = __shfl_up(p.x, 1, kWave);
+  r.y = __shfl_up(p.y, 1, kWave);
+  r.sxh = __shfl_up(p.sxh, 1, kWave);
+  r.sxl = __shfl_up(p.sxl, 1, kWave);
+  r.syh = __shfl_up(p.syh, 1, kWave);
+  r.syl = __shfl_up(p.syl, 1, kWave);
+  (void)lane;
+  return r;
+}
+
+__device__ __forceinline__ GPt shfl_pt(const GPt& p, int src) {
+  GPt r;
+  r.x = __shfl(p.x, src, kWave);
+  r.y = __shfl(p.y, src, kWave);
+  r.sxh = __shfl(p.sxh, src, kWave);
+  r.sxl = __shfl(p.sxl, src, kWave);
+  r.syh = __shfl(p.syh, src, kWave);
+  r.syl = __shfl(p.syl, src, kWave);
+  return r;
+}
+
+// One window of a walk over the list L from v (exclusive), in direction dir (-1: towards the
+// list's first vertex, +1: towards its last).  Lane i takes v_{i+1}, the (i+1)-th vertex from v.
+// The walk stops at v_i (v_0 = v) when stop(v_i, v_{i+1}) holds.  Returns true when the walk
+// stopped inside this window; in every case v and Pv are advanced to where the walk stands.
+template <class VS, class Stop>
+__device__ bool walk_window(const VS& S, const NodeList& L, int dir, VRef& v, GPt& Pv, int lane,
+                            MergeLds& W, Stop stop) {
+  // segment lane j: v.u + dir * j, and the number of its vertices beyond v
+  const int uj = v.u + dir * lane;
+  int cnt = 0;
+  Desc dj = make_int4(0, 0, -1, 0);
+  if (uj >= 0 && uj < L.n) {
+    dj = L.d[uj];
+    if (lane == 0) cnt = dir < 0 ? v.p - dj.y : dj.z - v.p;
+    else cnt = dj.z - dj.y + 1;
+  }
+  int cum = cnt;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int o = __shfl_up(cum, dd, kWave);
+    if (lane >= dd) cum += o;
+  }
+  W.cum[lane] = cum;
+  W.d[lane] = dj;
+  wave_sync();
+  const int total = __shfl(cum, kWave - 1, kWave);
+  const int want = lane + 1;
+  const bool valid = want <= total;
+  VRef mine = v;
+  GPt P = Pv;
+  if (valid) {
+    int lo = 0, hi = kWave - 1;  // smallest j with cum[j] >= want
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (W.cum[mid] >= want) hi = mid;
+      else lo = mid + 1;
+    }
+    const int before = lo > 0 ? W.cum[lo - 1] : 0;
+    const int k = want - before - 1;  // 0-based from the segment's near end
+    const Desc d = W.d[lo];
+    int rank;
+    if (dir < 0) rank = (lo == 0) ? v.p - 1 - k : d.z - k;
+    else rank = (lo == 0) ? v.p + 1 + k : d.y + k;
+    mine = VRef{v.u + dir * lo, rank};
+    P = S.pt(L.row, d.x, rank);
+  }
+  wave_sync();
+  // lane i: v_i (from lane i - 1, lane 0: v) and v_{i+1} (its own)
+  GPt Pi = shfl_up_pt(P, lane);
+  if (lane == 0) Pi = Pv;
+  const bool st = valid && stop(Pi, P);
+  const uint64_t hit = __ballot(st || !valid);
+  const int f = hit ? __builtin_ctzll(hit) : kWave;  // first lane that stops or runs out
+  const bool stop_at_f = f < kWave && __shfl(st ? 1 : 0, f < kWave ? f : 0, kWave) != 0;
+  // the walk now stands at v_f (v_64 when no lane stopped); v_f is lane f - 1's vertex
+  const bool list_end = (dir < 0) ? (v.u - (kWave - 1) <= 0) : (v.u + (kWave - 1) >= L.n - 1);
+  if (f > 0) {
+    const int src = f - 1;
+    const int nu = __shfl(mine.u, src, kWave);
+    const int np = __shfl(mine.p, src, kWave);
+    const GPt NP = shfl_pt(P, src);
+    v = VRef{nu, np};
+    Pv = NP;
+  }
+  return stop_at_f || (f < kWave && list_end);
+}
+
+// Walk to the bridge one vertex at a time (no cap), from alpha in A and beta in B.
+template <class VS>
+__device__ void merge_finish_walk(const VS& S, const NodeList& LA, const NodeList& LB,
+                                  VRef firstA, VRef lastB, VRef& al, VRef& be) {
+  GPt Pa = load_v(S, LA, al), Pb = load_v(S, LB, be);
+  for (;;) {
+    bool moved = false;
+    while (!vref_eq(al, firstA)) {
+      const VRef p = list_pred(LA, al);
+      const GPt Pp = load_v(S, LA, p);
+      if (gturn(Pp, Pa, Pb) > 0.0) break;
+      al = p;
+      Pa = Pp;
+      moved = true;
+    }
+    while (!vref_eq(be, lastB)) {
+      const VRef q = list_succ(LB, be);
+      const GPt Pq = load_v(S, LB, q);
+      if (gturn(Pa, Pb, Pq) > 0.0) break;
+      be = q;
+      Pb = Pq;
+      moved = true;
+    }
+    if (!moved) break;
+  }
+}
+
+template <typename T, bool W>
+__global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<T, W> S,
+                                                                    int64_t batch, int r,
+                                                                    int per_row) {
+  __shared__ MergeLds sw[kMergeWaves];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int64_t t = (int64_t)blockIdx.x * kMergeWaves + wid;
+  if (t >= batch * per_row) return;  // the whole wavefront
+  MergeLds& Wl = sw[wid];
+  const int64_t row = t / per_row;
+  const int qm = (int)(t - row * per_row);
+  const int jA = qm << (r + 1);
+  const int jB = jA + (1 << r);
+  const int64_t rb = row * S.m;
+  Desc* dA = S.desc + rb + jA;
+  Desc* dB = S.desc + rb + jB;
+  const NodeList LA{dA, S.nseg[rb + jA], row};
+  const NodeList LB{dB, S.nseg[rb + jB], row};
+  const VRef firstA = list_first(LA);
+  const VRef lastB = list_last(LB);
+  VRef al = list_last(LA);
+  VRef be = list_succ(LB, list_first(LB));
+  GPt Pa = load_v(S, LA, al);
+  const GPt Sp = Pa;
+  GPt Pb = load_v(S, LB, be);
+  // the test that s is a strictly convex vertex: one step of each side
+  bool convex = true;
+  if (!vref_eq(al, firstA)) {
+    const GPt Pp = load_v(S, LA, list_pred(LA, al));
+    if (!(gturn(Pp, Pa, Pb) > 0.0)) convex = false;
+  }
+  if (convex && !vref_eq(be, lastB)) {
+    const GPt Pq = load_v(S, LB, list_succ(LB, be));
+    if (!(gturn(Pa, Pb, Pq) > 0.0)) convex = false;
+  }
+  if (!convex) {
+    bool searched = false;
+    for (int pass = 0; pass < 4 * kChunk; ++pass) {
+      bool moved = false;
+      // A side: alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
+      for (int win = 0; !vref_eq(al, firstA); ++win) {
+        if (win == kWinCap) {
+          searched = true;
+          break;
+        }
+        const VRef before = al;
+        const bool done = walk_window(S, LA, -1, al, Pa, lane, Wl,
+                                      [&](const GPt& vi, const GPt& vn) { return gturn(vn, vi, Pb) > 0.0; });
+        if (!vref_eq(before, al)) moved = true;
+        if (done) break;
+      }
+      if (searched) break;
+      // B side: beta moves right while (alpha, beta, succ beta) is not a strict left turn
+      for (int win = 0; !vref_eq(be, lastB); ++win) {
+        if (win == kWinCap) {
+          searched = true;
+          break;
+        }
+        const VRef before = be;
+        const bool done = walk_window(S, LB, +1, be, Pb, lane, Wl,
+                                      [&](const GPt& vi, const GPt& vn) { return gturn(Pa, vi, vn) > 0.0; });
+        if (!vref_eq(before, be)) moved = true;
+        if (done) break;
+      }
+      if (searched || !moved) break;
+    }
+    if (searched) {
+      // long walk: Overmars-van Leeuwen bisection over the ranges still open (every lane runs the
+      // same serial search, reading the same addresses)
+      VRef a2, b2;
+      if (bridge_search(S, LA, LB, firstA, al, be, lastB, Sp, a2, b2)) {
+        al = a2;
+        be = b2;
+      } else {
+        // rounding defeated the search: finish by plain walking
+        merge_finish_walk(S, LA, LB, firstA, lastB, al, be);
+      }
+    }
+  }
+  // Cut: A keeps segments 0..al.u with the last one ending at al.p; B keeps be.u.. with the first
+  // starting at be.p, moved down to follow A's kept part.
+  const int nA = al.u + 1;
+  const int nB = LB.n - be.u;
+  Desc first = dB[be.u];
+  first.y = be.p;
+  wave_sync();
+  if (lane == 0) {
+    dA[al.u].z = al.p;
+    dA[nA] = first;
+  }
+  // dA + nA <= dB + be.u: each round reads its descriptors before any lane writes
+  for (int b = 1; b < nB; b += kWave) {
+    const int tt = b + lane;
+    Desc dd = make_int4(0, 0, 0, 0);
+    if (tt < nB) dd = dB[be.u + tt];
+    wave_sync();
+    if (tt < nB) dA[nA + tt] = dd;
+  }
+  if (lane == 0) S.nseg[rb + jA] = nA + nB;
+}
+
+}  // namespace iso
