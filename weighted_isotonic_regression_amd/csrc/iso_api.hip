@@ -35,7 +35,7 @@ struct Layout {
   // long rows only
   size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0, o_lx = 0,
          o_ly = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0, o_ckx = 0, o_cky = 0, o_zt = 0,
-         o_df = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
+         o_df = 0, o_bnd = 0, o_bndk = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
   int64_t m = 0, nblk = 0;
 };
 
@@ -72,6 +72,8 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.o_cky = take(G * (size_t)kWave * kLaneW * sizeof(double));
     L.o_zt = take(G * (size_t)kZTiles);
     L.o_df = take(G);
+    L.o_bnd = take(G * sizeof(double4));
+    L.o_bndk = take(G * sizeof(int2));
     L.o_ends = take(G * sizeof(EndInfo));
     L.o_bsum = take((size_t)batch * (size_t)L.nblk * sizeof(double4));
     L.o_bflag = take((size_t)batch * (size_t)L.nblk * sizeof(uint32_t));
@@ -178,6 +180,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   co.cky = (double*)(ws + Lay.o_cky);
   co.ztile = (uint8_t*)(ws + Lay.o_zt);
   co.dform = (uint8_t*)(ws + Lay.o_df);
+  co.bnd = (double4*)(ws + Lay.o_bnd);
+  co.bndk = (int2*)(ws + Lay.o_bndk);
   double4* start = (double4*)(ws + Lay.o_start);
   double4* bsum = (double4*)(ws + Lay.o_bsum);
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
@@ -204,6 +208,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   S.lsy = co.lsy;
   S.ckx = co.ckx;
   S.cky = co.cky;
+  S.bnd = co.bnd;
+  S.bndk = co.bndk;
   S.tot = co.tot;
   S.start = start;
   S.y = y;

@@ -53,6 +53,8 @@ struct ChunkOut {
   double* cky;
   uint8_t* ztile;     // [G * kZTiles] 1 where the chunk pass wrote z = y for the load tile
   uint8_t* dform;     // [G] 1 when the hull is stored in the dense form
+  double4* bnd;       // [G] dense form: coordinates of hull vertices 1 and V - 2
+  int2* bndk;         // [G] their point indices
 };
 
 __device__ __forceinline__ double turn_pts(double2 p, double2 q, double2 r) {
@@ -231,6 +233,24 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
     ++d;
   };
   const int ntiles = (c + TN - 1) / TN;
+  // the next tile's inputs are loaded while the current one is processed
+  T ny[TN], nw[TN];
+  auto load_tile = [&](int eb) {
+    if (vec && eb + TN <= c) {
+#pragma unroll
+      for (int k = 0; k < TN / VN; ++k) {
+        load16(yl + eb + k * VN, &ny[k * VN]);
+        if (W) load16(wl + eb + k * VN, &nw[k * VN]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < TN; ++k) {
+        ny[k] = (eb + k < c) ? yl[eb + k] : (T)0;
+        if (W) nw[k] = (eb + k < c) ? wl[eb + k] : (T)1;
+      }
+    }
+  };
+  if (ntiles > 0) load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
     const int eb = t * TN;  // lane-relative index of the tile's first element
     if ((eb & (kCk - 1)) == 0) L.ck[eb / kCk][lane] = double2{lx, ly};
@@ -240,28 +260,22 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
       curw = 0u;
     }
     T yv[TN], wv[TN];
-    if (vec && eb + TN <= c) {
-#pragma unroll
-      for (int k = 0; k < TN / VN; ++k) {
-        load16(yl + eb + k * VN, &yv[k * VN]);
-        if (W) load16(wl + eb + k * VN, &wv[k * VN]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < TN; ++k) {
-        yv[k] = (eb + k < c) ? yl[eb + k] : (T)0;
-        if (W) wv[k] = (eb + k < c) ? wl[eb + k] : (T)1;
-      }
-    }
-    const int pops0 = pops;
-    bool skipped = false;
 #pragma unroll
     for (int k = 0; k < TN; ++k) {
+      yv[k] = ny[k];
+      wv[k] = W ? nw[k] : (T)1;
+    }
+    if (t + 1 < ntiles) load_tile(eb + TN);
+    const int pops0 = pops;
+    bool skipped = false;
+    // one element through the chain: its left point q (a candidate when y_{q-1} < y_q), then
+    // the running sums
+    auto element = [&](int k) {
       if (eb + k < c) {
         double yd = (double)yv[k];
         double wd = W ? (double)wv[k] : 1.0;
         classify<W>(yd, wd, f);
-        const int q = eb + k;  // the element's left point
+        const int q = eb + k;
         if (q > 0) {
           if (yprev < yd) push(double2{W ? lx : (double)q, ly}, q);
           else skipped = true;
@@ -270,6 +284,51 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
         ly += wd * yd;
         yprev = yd;
       }
+    };
+    // A tile whose elements are clean and strictly increasing in y after the previous element
+    // has every turn among its points strictly convex in exact arithmetic (the slopes of the
+    // one-element edges are the y values), so once its first point sits on the stack above the
+    // previous one, the rest are pushed without tests.
+    bool clean = eb + TN <= c;
+    {
+      double yp = yprev;
+#pragma unroll
+      for (int k = 0; k < TN; ++k) {
+        const double yd = (double)yv[k];
+        const double wd = W ? (double)wv[k] : 1.0;
+        clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0 && (yp < yd || (eb == 0 && k == 0));
+        yp = yd;
+      }
+    }
+    element(0);
+    const bool bulk = clean && (eb == 0 ? d == 1 : (ti == eb && ui == eb - 1));
+    if (__all(bulk)) {
+      const int d0 = d;
+#pragma unroll
+      for (int k = 1; k < TN; ++k) {
+        const double2 K{W ? lx : (double)(eb + k), ly};
+        const int depth = d0 + k - 1;
+        if (k >= TN - kRing || depth < 2) {
+          const int sl = ring_slot(depth);
+          L.ring[sl][lane] = K;
+          L.ringi[sl][lane] = (uint16_t)(eb + k);
+        }
+        if (k == TN - 2) Up = K;
+        if (k == TN - 1) Tp = K;
+        const double wd = W ? (double)wv[k] : 1.0;
+        if (W) lx += wd;
+        ly += wd * (double)yv[k];
+      }
+      yprev = (double)yv[TN - 1];
+      ui = eb + TN - 2;
+      ti = eb + TN - 1;
+      d = d0 + TN - 1;
+      lowv = max(lowv, d - kRing);
+      const int b0 = (eb & 31) + 1, b1 = (eb & 31) + TN - 1;  // bits of points eb+1 .. eb+TN-1
+      curw |= (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u);
+    } else {
+#pragma unroll
+      for (int k = 1; k < TN; ++k) element(k);
     }
     // speculative fit of a tile that pushed every point and popped none: every element is its
     // own block so far
@@ -452,7 +511,41 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
     return;
   }
   // dense form: vertex bits of the chunk's points, set bits before each word, lane starts and
-  // checkpoints (coordinates are recomputed from these and the inputs)
+  // checkpoints (coordinates are recomputed from these and the inputs); vertices 1 and V - 2,
+  // which the merge levels test at every chunk boundary, are also stored directly.
+  {
+    const uint64_t nz = __ballot(nonempty);
+    const int l1 = __builtin_ctzll(nz);       // vertex 1: the first entry of the first range
+    const int lz = 63 - __builtin_clzll(nz);  // vertex V - 1 ends the last range
+    if (lane == l1) {
+      int q = c;
+      if (lo != d - 1) (void)lane_entry<T, W>(L, lane, lo, y, w, off, len, q);
+      const double2 P = chunk_entry<T, W>(L, lane, lo, y, w, off, len);
+      out.bnd[g].x = P.x;
+      out.bnd[g].y = P.y;
+      out.bndk[g].x = e0 + q;
+    }
+    // vertex V - 2: the entry before lz's last, or the last of the range before it, or point 0
+    const uint64_t before = nz & lanes_below(lz);
+    const int lp = before ? 63 - __builtin_clzll(before) : 0;
+    const int lzc = __shfl(hi - lo, lz, kWave);   // (entries in lz's range) - 1
+    const int src = lzc >= 1 ? lz : lp;
+    if (lane == src) {
+      const bool in_lz = lzc >= 1;
+      int i = in_lz ? hi - 1 : hi;
+      double2 P{0.0, 0.0};
+      int kq = 0;
+      if (in_lz || before) {
+        int q = c;
+        if (i != d - 1) (void)lane_entry<T, W>(L, lane, i, y, w, off, len, q);
+        P = chunk_entry<T, W>(L, lane, i, y, w, off, len);
+        kq = e0 + q;
+      }
+      out.bnd[g].z = P.x;
+      out.bnd[g].w = P.y;
+      out.bndk[g].y = kq;
+    }
+  }
   int qlo = kSub + 1, qhi = -1;  // the stack bits of depths lo..hi span points [qlo, qhi]
   if (nonempty) {
     (void)lane_entry<T, W>(L, lane, lo, y, w, off, len, qlo);

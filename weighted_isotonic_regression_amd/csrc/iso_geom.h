@@ -280,6 +280,8 @@ struct VertexStore {
   const double* cky;
   const double2* tot;     // [G] chunk end point (W, S)
   const double4* start;   // [G] chunk start {x hi, x lo, y hi, y lo}
+  const double4* bnd;     // [G] dense form: coordinates of vertices 1 and V - 2
+  const int2* bndk;       // [G] their point indices
   const T* y;
   const T* w;
   int64_t n;              // row length
@@ -334,11 +336,40 @@ struct VertexStore {
       k = lk[idx];
       return;
     }
+    // the vertices the merges and ends touch most: the chunk's two ends and their neighbours
+    const int V = nverts[g];
+    if (p == 0) {
+      x = 0.0;
+      yy = 0.0;
+      k = 0;
+      return;
+    }
+    if (p == V - 1) {
+      const int64_t rem = n - (int64_t)j * kChunk;
+      k = rem < kChunk ? (int)rem : kChunk;
+      const double2 t = tot[g];
+      x = t.x;
+      yy = t.y;
+      return;
+    }
+    if (p == 1 || p == V - 2) {
+      const double4 b = bnd[g];
+      const int2 bk = bndk[g];
+      if (p == 1) {
+        x = b.x;
+        yy = b.y;
+        k = bk.x;
+      } else {
+        x = b.z;
+        yy = b.w;
+        k = bk.y;
+      }
+      return;
+    }
     // select: the word holding the p-th set bit (the last word whose count of earlier set bits
     // is <= p), starting from where it would be if the bits were spread evenly, then the bit
     const uint16_t* mc = mcnt + g * kMaskW;
-    const int V = nverts[g] > 0 ? nverts[g] : 1;
-    int lo = (int)(((int64_t)p * (kMaskW - 1)) / V);
+    int lo = (int)(((int64_t)p * (kMaskW - 1)) / (V > 0 ? V : 1));
     lo = lo < 0 ? 0 : (lo > kMaskW - 1 ? kMaskW - 1 : lo);
     while (lo > 0 && (int)mc[lo] > p) --lo;
     while (lo + 1 < kMaskW && (int)mc[lo + 1] <= p) ++lo;
@@ -598,7 +629,32 @@ ISO_HD EndInfo chunk_ends(const VS& S, int64_t row, int j) {
   const int64_t g = rb + j;
   const Desc* root = S.desc + rb;
   const int nr = S.nseg[rb];
+  // the root segment of the last chunk <= j: bracket it from a guess (exact when every chunk
+  // keeps a segment), then bisect
   int lo = 0, hi = nr - 1;  // root[0].x == 0 <= j
+  {
+    int u0 = (int)(((int64_t)j * nr) / S.m);
+    u0 = u0 < 0 ? 0 : (u0 > nr - 1 ? nr - 1 : u0);
+    if (root[u0].x <= j) {
+      lo = u0;
+      int step = 1;
+      while (lo + step <= hi && root[lo + step].x <= j) {
+        lo += step;
+        step <<= 1;
+      }
+      if (lo + step <= hi) hi = lo + step - 1;
+    } else {
+      hi = u0 - 1;  // the answer is below u0; probe downwards with doubling steps
+      int probe = u0 - 1, step = 1;
+      while (probe > 0 && root[probe].x > j) {
+        hi = probe - 1;
+        probe -= step;
+        step <<= 1;
+        if (probe < 0) probe = 0;
+      }
+      if (root[probe].x <= j) lo = probe;
+    }
+  }
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (root[mid].x <= j) lo = mid;

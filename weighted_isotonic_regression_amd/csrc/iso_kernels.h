@@ -499,30 +499,47 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
   if (!S.is_list(g)) {
     for (int q = tid; q < kMaskW; q += kFitThreads) sMask[q] = S.mask[g * kMaskW + q];
     __syncthreads();
-    for (int i = tid; i < len; i += kFitThreads) {
-      if (i < e.klo) {
-        z[off + i] = zin;
-        if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
-        continue;
+    // one word (32 elements) per thread at a time: a word inside [klo, khi) whose points and the
+    // next one are all vertices, in tiles whose z the chunk pass wrote, needs nothing
+    const int nw = (len + 31) >> 5;
+    for (int wd = tid; wd < nw; wd += kFitThreads) {
+      const int i0 = wd << 5;
+      const int i1 = min(i0 + 32, len);
+      if (i0 >= e.klo && i1 <= e.khi && sMask[wd] == 0xffffffffu && (sMask[wd + 1] & 1u)) {
+        bool written = true;
+        for (int tt = i0 / TN; tt < (i1 + TN - 1) / TN; ++tt) written = written && ztile[g * kZTiles + tt];
+        if (written) {
+          if (bstart) {
+            for (int i = i0; i < i1; ++i) bstart[off + i] = 1;
+          }
+          continue;
+        }
       }
-      if (i >= e.khi) {
-        z[off + i] = zout;
-        if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
-        continue;
+      for (int i = i0; i < i1; ++i) {
+        if (i < e.klo) {
+          z[off + i] = zin;
+          if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
+          continue;
+        }
+        if (i >= e.khi) {
+          z[off + i] = zout;
+          if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
+          continue;
+        }
+        const bool vl = (sMask[i >> 5] >> (i & 31)) & 1u;
+        const bool vr = (sMask[(i + 1) >> 5] >> ((i + 1) & 31)) & 1u;
+        if (bstart) bstart[off + i] = vl ? 1 : 0;
+        if (vl && vr) {
+          if (!ztile[g * kZTiles + i / TN]) z[off + i] = S.y[off + i];
+          continue;
+        }
+        const int a = vl ? i : mask_pred(sMask, i);
+        const int b = mask_succ(sMask, i);
+        double ax, ay, bx, by;
+        S.dense_point(row, j, a, ax, ay);
+        S.dense_point(row, j, b, bx, by);
+        z[off + i] = (T)((by - ay) / (bx - ax));
       }
-      const bool vl = (sMask[i >> 5] >> (i & 31)) & 1u;
-      const bool vr = (sMask[(i + 1) >> 5] >> ((i + 1) & 31)) & 1u;
-      if (bstart) bstart[off + i] = vl ? 1 : 0;
-      if (vl && vr) {
-        if (!ztile[g * kZTiles + i / TN]) z[off + i] = S.y[off + i];
-        continue;
-      }
-      const int a = vl ? i : mask_pred(sMask, i);
-      const int b = mask_succ(sMask, i);
-      double ax, ay, bx, by;
-      S.dense_point(row, j, a, ax, ay);
-      S.dense_point(row, j, b, bx, by);
-      z[off + i] = (T)((by - ay) / (bx - ax));
     }
     return;
   }

@@ -245,13 +245,21 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
     dA[al.u].z = al.p;
     dA[nA] = first;
   }
-  // dA + nA <= dB + be.u: each round reads its descriptors before any lane writes
-  for (int b = 1; b < nB; b += kWave) {
-    const int tt = b + lane;
-    Desc dd = make_int4(0, 0, 0, 0);
-    if (tt < nB) dd = dB[be.u + tt];
-    wave_sync();
-    if (tt < nB) dA[nA + tt] = dd;
+  // dA + nA <= dB + be.u, so a write never lands on a descriptor a later read needs; each lane
+  // keeps four reads in flight
+  constexpr int kCopy = 4;
+  for (int b = 1; b < nB; b += kCopy * kWave) {
+    Desc dd[kCopy];
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+      const int tt = b + k * kWave + lane;
+      if (tt < nB) dd[k] = dB[be.u + tt];
+    }
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+      const int tt = b + k * kWave + lane;
+      if (tt < nB) dA[nA + tt] = dd[k];
+    }
   }
   if (lane == 0) S.nseg[rb + jA] = nA + nB;
 }
