@@ -1,17 +1,28 @@
 """Throughput of the batched weighted L2 isotonic fit on one MI355X.
 
-One step = one iso_fit_ex call (all stages of the fit) over the 1 x 10^8 fp32 mixed row
-(y_i = sin(8 pi i/n) + 2 i/n + N(0, 0.05^2), w ~ LogUniform[0.1, 10]), inputs resident in HBM.
-Prints one JSON line: elements/s of the whole fit, the roofline of the dominant kernel (its
-algorithmic bytes over its average launch time, timed with HIP events inside the timed region),
-the fit's whole-call fraction of the HBM roofline, rows/s on 65536 rows of 16 elements, the dense
-1 x 10^8 fp64 nearly monotone row, and the CPU oracle timed on this host.
+One step = one iso_fit_ex call (every stage of the fit) over the 1 x 10^8 fp32 mixed row
+(y_i = sin(8 pi i/n) + 2 i/n + N(0, 0.05^2), w ~ LogUniform[0.1, 10], seed 5), inputs resident
+in HBM.  Prints one JSON line: elements/s of the whole fit; the roofline of the dominant kernel
+(its algorithmic bytes per launch over its average launch time, timed with HIP events recorded
+on the launch stream inside the timed region) with the HBM traffic measured by rocprofv3
+counters when they were taken on the current kernel sources; the fit's whole-call fraction of
+the HBM roofline; rows/s on 65536 rows of 16 elements; the dense 1 x 10^8 fp64 nearly monotone
+row; and the CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+    python bench.py --only mixed|dense|short [--copy-calib]      (one workload, for profilers)
+    python bench.py --summarize-pmc WORKLOAD FETCH_DIR WRITE_DIR  (updates profiles/traffic.txt)
+
+Algorithmic bytes per element are read y + read w + write z (sizeof(T) each).  Of these the
+chunk pass (k_chunk) reads y and w; the fit (k_fit) writes z, except where the chunk pass already
+wrote z = y (dense tiles).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -21,10 +32,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+COPY_BYTES = 1 << 30   # the calibration copy: 1 GiB read and 1 GiB written per launch
+METRIC = "elements/s and % HBM roofline: 1x10^8 row; rows/s at 65536x16"
 
 
-def _sync(torch):
-    torch.cuda.synchronize()
+def source_hash():
+    """sha256 of the HIP sources and headers the kernels are built from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "weighted_isotonic_regression_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for p in files:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def alg_bytes_per_elem(esz, weighted):
@@ -33,8 +55,8 @@ def alg_bytes_per_elem(esz, weighted):
 
 
 def stage_alg_bytes(stage, n_elems, esz, weighted):
-    """Algorithmic bytes one launch of a stage's kernel moves: the row pass reads y (and w), the
-    fit writes z; the scan, merge and ends kernels touch only workspace (no algorithmic bytes)."""
+    """Algorithmic bytes one launch of a stage's kernel moves: the chunk pass reads y (and w), the
+    fit writes z; the scan, merge and ends kernels touch only workspace."""
     if stage == "wave":
         return n_elems * esz * (2 if weighted else 1)
     if stage == "fit":
@@ -42,9 +64,13 @@ def stage_alg_bytes(stage, n_elems, esz, weighted):
     return 0
 
 
-def time_fit(torch, B, y, w, steps, warmup, rotate=None):
-    """Times `steps` fits after `warmup`; `rotate` is a list of (y, w) input sets used in turn."""
-    sets = rotate or [(y, w)]
+STAGE_KERNEL = {"wave": "k_chunk", "scan": "k_scan", "merge": "k_merge_wave", "ends": "k_ends",
+                "fit": "k_fit"}
+
+
+def time_fit(torch, B, sets, steps, warmup):
+    """Times `steps` fits after `warmup`; `sets` is a list of (y, w) input sets used in turn.
+    Per-stage HIP events are recorded on the launch stream inside the timed loop."""
     batch, n = sets[0][0].shape
     code = B.ISO_F64 if sets[0][0].dtype == torch.float64 else B.ISO_F32
     z = torch.empty_like(sets[0][0])
@@ -60,37 +86,112 @@ def time_fit(torch, B, y, w, steps, warmup, rotate=None):
 
     for k in range(warmup):
         call(k)
-    _sync(torch)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for k in range(steps):
-        call(k)
-    ev1.record()
-    _sync(torch)
-    t1 = time.perf_counter()
-    ms_events = ev0.elapsed_time(ev1) / steps
-    ms_host = (t1 - t0) * 1e3 / steps
-    # second pass of the same calls with per-stage events
+    torch.cuda.synchronize()
+    B.iso_prof_read()  # forget anything recorded before
     B.iso_prof_enable(1)
+    t0 = time.perf_counter()
     for k in range(steps):
         call(k)
-    _sync(torch)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     B.iso_prof_enable(0)
     st_ms, st_launch, calls = B.iso_prof_read()
-    return z, ms_host, ms_events, st_ms, st_launch, calls
+    ms_host = (t1 - t0) * 1e3 / steps
+    return z, ms_host, st_ms, st_launch, calls
 
 
-def roofline_of(stages_ms, stages_launch, calls, n_elems, esz, weighted):
+def read_traffic():
+    """{workload: {kernel: (fetch_bytes, write_bytes)}} from profiles/traffic.txt when it was
+    measured on the current sources, else {}."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    out, sha = {}, None
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line.startswith("source_sha256"):
+            sha = line.split("=")[1].strip()
+        elif line and not line.startswith("#") and "=" not in line:
+            parts = line.split()
+            if len(parts) == 4:
+                out.setdefault(parts[0], {})[parts[1]] = (float(parts[2]), float(parts[3]))
+    return out if sha == source_hash() else {}
+
+
+def roofline_of(workload, stages_ms, stages_launch, calls, n_elems, esz, weighted, traffic):
     dom = max(stages_ms, key=lambda k: stages_ms[k])
     launches = max(stages_launch[dom], 1)
     avg_ms = stages_ms[dom] / launches
     per_launch_bytes = stage_alg_bytes(dom, n_elems, esz, weighted) * calls / launches
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
+    kern = STAGE_KERNEL[dom]
+    t = traffic.get(workload, {}).get(kern)
     return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_" + dom,
-            "alg_bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4)}
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if t is None else int(t[0] + t[1]),
+            "kernel": kern, "alg_bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4)}
+
+
+def stage_line(st_ms, calls):
+    return {k: round(v / max(calls, 1), 4) for k, v in st_ms.items()}
+
+
+def load_workload(torch, W, name, dev):
+    if name == "short":
+        yh, wh = W.short_rows_16()
+    elif name == "dense":
+        yh, wh = W.nearly_monotone_1e8()
+    else:
+        yh, wh = W.mixed_1e8()
+    return yh, wh, torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
+
+
+def run_only(args, torch, B, W, dev):
+    """One workload, timed as in the full run; prints one JSON line of its own."""
+    if args.copy_calib:
+        # a plain device copy of known size, for scaling the memory counters
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
+    _, _, y, w = load_workload(torch, W, args.only, dev)
+    print("bench: timing %s" % args.only, file=sys.stderr, flush=True)
+    _, ms, sms, sla, sc = time_fit(torch, B, [(y, w)], args.steps, args.warmup)
+    esz = y.element_size()
+    print(json.dumps({"workload": args.only, "ms_per_call": round(ms, 4), "stage_ms": stage_line(sms, sc),
+                      "hbm_frac": round(y.numel() * alg_bytes_per_elem(esz, True) / (ms * 1e-3) / 1e9 /
+                                        HBM_PEAK_GBS, 4)}), flush=True)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel, scaled by the calibration copy's
+    counters against its known 1 GiB read and 1 GiB write; writes profiles/traffic.txt."""
+    def per_kernel(d, counter):
+        acc = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                acc.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
+        return acc
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_f = [v for k, vs in fetch.items() if "elementwise" in k or "copy" in k.lower() for v in vs]
+    copy_w = [v for k, vs in write.items() if "elementwise" in k or "copy" in k.lower() for v in vs]
+    if not copy_f or not copy_w:
+        raise SystemExit("no calibration copy kernel in the counter runs")
+    sf = COPY_BYTES / (sorted(copy_f)[len(copy_f) // 2])
+    sw = COPY_BYTES / (sorted(copy_w)[len(copy_w) // 2])
+    lines = []
+    for key in ("k_chunk", "k_fit", "k_merge_wave"):
+        fs = [v for k, vs in fetch.items() if key in k for v in vs]
+        wsz = [v for k, vs in write.items() if key in k for v in vs]
+        if fs and wsz:
+            lines.append((key, sum(fs) / len(fs) * sf, sum(wsz) / len(wsz) * sw))
+    return sf, sw, lines
 
 
 def main():
@@ -101,8 +202,39 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
     ap.add_argument("--only", choices=["mixed", "short", "dense"], default=None,
-                    help="time one workload only (for profiler runs); implies --no-cpu")
+                    help="time one workload only (for profiler runs)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="with --only: first run a 1 GiB device copy (memory-counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="append the scaled counter traffic of a workload to profiles/traffic.txt")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        wl, fd, wd = args.summarize_pmc
+        sf, sw, lines = summarize_pmc(fd, wd)
+        sha = source_hash()
+        keep = []
+        if os.path.exists(TRAFFIC_FILE):
+            old = open(TRAFFIC_FILE).read().splitlines()
+            if any(l.strip() == "source_sha256 = %s" % sha for l in old):
+                keep = [l for l in old if l and not l.startswith("#") and "=" not in l and not l.startswith(wl + " ")]
+        with open(TRAFFIC_FILE, "w") as f:
+            f.write("# HBM bytes per launch of the fit's kernels: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE\n")
+            f.write("# (KiB per dispatch) scaled by the same counters for a 1 GiB device copy in the same run\n")
+            f.write("# (latest scale factors: fetch %.4f, write %.4f).  Columns: workload kernel fetch_bytes\n"
+                    % (sf, sw))
+            f.write("# write_bytes.  Valid only for the kernel sources of this hash (bench.py checks it).\n")
+            f.write("# Made by, for each workload W in mixed, dense (R = the repository root, run from /tmp):\n")
+            f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/meas/pf_W -o run -- \\\n")
+            f.write("#     python3 $R/bench.py --only W --steps 2 --warmup 1 --copy-calib\n")
+            f.write("#   (the same with WRITE_SIZE into pw_W), then\n")
+            f.write("#   python bench.py --summarize-pmc W_1e8_<dtype> gpurun_out/meas/pf_W gpurun_out/meas/pw_W\n")
+            f.write("source_sha256 = %s\n" % sha)
+            for l in keep:
+                f.write(l + "\n")
+            for k, fb, wb in lines:
+                f.write("%s %s %.0f %.0f\n" % (wl, k, fb, wb))
+        print(open(TRAFFIC_FILE).read())
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (rows are independent and a "
               "long row is fitted on one device); run with --gpus 1", file=sys.stderr)
@@ -119,28 +251,24 @@ def main():
     if args.only:
         run_only(args, torch, B, W, dev)
         return
+    traffic = read_traffic()
     print("bench: generating mixed_1e8", file=sys.stderr, flush=True)
-    y_h, w_h = W.mixed_1e8()
+    y_h, w_h, y, w = load_workload(torch, W, "mixed", dev)
     n = y_h.shape[1]
-    y = torch.from_numpy(y_h).to(dev)
-    w = torch.from_numpy(w_h).to(dev)
     print("bench: timing mixed_1e8", file=sys.stderr, flush=True)
-    z, ms_host, ms_ev, st_ms, st_la, calls = time_fit(torch, B, y, w, args.steps, args.warmup)
+    z, ms_host, st_ms, st_la, calls = time_fit(torch, B, [(y, w)], args.steps, args.warmup)
     esz = 4
     elems_per_s = n / (ms_host * 1e-3)
     fit_gbs = n * alg_bytes_per_elem(esz, True) / (ms_host * 1e-3) / 1e9
-    roof = roofline_of(st_ms, st_la, calls, n, esz, True)
-    stages = {k: round(v / max(calls, 1), 4) for k, v in st_ms.items()}
 
     out = {
-        "metric": "elements/s and % HBM roofline: 1x10^8 row; rows/s at 65536x16",
+        "metric": METRIC,
         "value": round(elems_per_s, 1),
         "unit": "elements/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_host, 4),
-        "ms_per_step_events": round(ms_ev, 4),
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
@@ -151,25 +279,26 @@ def main():
                    "batch": 1, "n": n, "io_dtype": "f32", "weighted": True},
         "fit_hbm_roofline": {"alg_bytes": n * alg_bytes_per_elem(esz, True), "achieved": round(fit_gbs, 2),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fit_gbs / HBM_PEAK_GBS, 4)},
-        "stage_ms": stages,
-        "roofline": roof,
+        "stage_ms": stage_line(st_ms, calls),
+        "roofline": roofline_of("mixed_1e8_f32", st_ms, st_la, calls, n, esz, True, traffic),
     }
 
-    zo = None
     if not args.no_cpu:
         import oracle
 
+        # The oracle (one thread, fp64 pool adjacent violators) on the whole row, 15 runs.
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         yd, wd = y_h.astype(np.float64), w_h.astype(np.float64)
-        times = []
-        for _ in range(3):
+        times, zo = [], None
+        for _ in range(15):
             t0 = time.perf_counter()
             zo = oracle.pav(yd, wd)
             times.append(time.perf_counter() - t0)
-        t = sorted(times)[1]
+        t = sorted(times)[len(times) // 2]
         out["cpu_baseline"] = {"value": round(n / t, 1), "unit": "elements/s", "cores": 1, "kind": "oracle",
-                               "sample": "the whole 1 x 10^8 row (fp64 pool adjacent violators, one thread), "
-                                         "median of 3 runs of %.3f s" % t}
+                               "sample": "the whole 1 x 10^8 mixed row, 15 runs of the fp64 pool-adjacent-"
+                                         "violators oracle on one thread, median %.3f s (total %.1f s)"
+                                         % (t, sum(times))}
         zg = z.cpu().numpy().astype(np.float64)
         out["max_deviation_vs_oracle"] = float(np.max(np.abs(zg - zo) / (1 + np.abs(zo))))
         del yd, wd, zo
@@ -183,50 +312,25 @@ def main():
         base_y = torch.from_numpy(ys).to(dev)
         base_w = torch.from_numpy(wsh).to(dev)
         sets = [(base_y.roll(k, dims=0).contiguous(), base_w.clone()) for k in range(64)]
-        _, msh, mse, sms, sla, sc = time_fit(torch, B, None, None, 200, 20, rotate=sets)
+        _, msh, _, _, _ = time_fit(torch, B, sets, 200, 20)
         out["short_rows_65536x16"] = {"rows_per_s": round(65536 / (msh * 1e-3), 1), "ms_per_call": round(msh, 5),
-                                      "ms_per_call_events": round(mse, 5),
                                       "hbm_frac": round(65536 * 16 * 12 / (msh * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del sets, base_y, base_w
         torch.cuda.empty_cache()
         # dense row: 1 x 10^8 fp64 nearly monotone, unit weights passed explicitly
         print("bench: timing nearly_monotone_1e8 (fp64)", file=sys.stderr, flush=True)
-        yd_h, wd_h = W.nearly_monotone_1e8()
-        yd = torch.from_numpy(yd_h).to(dev)
-        wd = torch.from_numpy(wd_h).to(dev)
-        del yd_h, wd_h
-        zd, msd, msde, dms, dla, dc = time_fit(torch, B, yd, wd, max(3, args.steps // 2), 2)
+        _, _, yd, wd = load_workload(torch, W, "dense", dev)
+        zd, msd, dms, dla, dc = time_fit(torch, B, [(yd, wd)], max(3, args.steps // 2), 2)
         nd = yd.shape[1]
         gbs = nd * alg_bytes_per_elem(8, True) / (msd * 1e-3) / 1e9
         # the exact fit of this row is y itself (every element its own block)
         dev_y = float(((zd - yd).abs() / (1 + yd.abs())).max().item())
         out["dense_1e8_f64"] = {"elements_per_s": round(nd / (msd * 1e-3), 1), "ms_per_call": round(msd, 4),
                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "achieved_gbs": round(gbs, 2),
-                                "stage_ms": {k: round(v / max(dc, 1), 4) for k, v in dms.items()},
-                                "roofline": roofline_of(dms, dla, dc, nd, 8, True),
+                                "stage_ms": stage_line(dms, dc),
+                                "roofline": roofline_of("dense_1e8_f64", dms, dla, dc, nd, 8, True, traffic),
                                 "max_deviation_vs_y": dev_y}
     print(json.dumps(out), flush=True)
-
-
-def run_only(args, torch, B, W, dev):
-    """One workload, timed as in the full run; prints one JSON line of its own."""
-    if args.only == "short":
-        ys, wsh = W.short_rows_16()
-        y, w = torch.from_numpy(ys).to(dev), torch.from_numpy(wsh).to(dev)
-    elif args.only == "dense":
-        yh, wh = W.nearly_monotone_1e8()
-        y, w = torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
-    else:
-        yh, wh = W.mixed_1e8()
-        y, w = torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
-    print("bench: timing %s" % args.only, file=sys.stderr, flush=True)
-    _, ms, mse, sms, sla, sc = time_fit(torch, B, y, w, args.steps, args.warmup)
-    esz = y.element_size()
-    n_el = y.numel()
-    print(json.dumps({"workload": args.only, "ms_per_call": round(ms, 4), "ms_events": round(mse, 4),
-                      "stage_ms": {k: round(v / max(sc, 1), 4) for k, v in sms.items()},
-                      "hbm_frac": round(n_el * alg_bytes_per_elem(esz, True) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}),
-          flush=True)
 
 
 if __name__ == "__main__":
