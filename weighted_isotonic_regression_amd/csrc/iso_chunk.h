@@ -80,29 +80,76 @@ __device__ __forceinline__ void classify(double& yd, double& wd, uint32_t& f) {
   }
 }
 
-// LDS of one wavefront.
-struct ChunkLds {
-  double2 ring[kRing + 2][kWave];   // stack entries by depth (ring_slot), lane-relative
-  uint16_t ringi[kRing + 2][kWave];  // their point indices (0..256)
-  uint32_t smask[kSubW][kWave];    // stack bit mask over the lane's points 0..256
-  double2 ck[kLaneW][kWave];       // lane-relative running sums at points 32 j
-  int depth[kWave];                // final stack depth
-  int lowv[kWave];                 // lowest depth still held by the ring
-  int lo[kWave], hi[kWave];        // surviving depth range of the lane's stack
-  double2 start[kWave + 1];        // lane starts, chunk-relative; [l + 1] is lane l's end point
+// Stack entries a lane keeps in LDS: depths 0 and 1 have slots of their own, deeper entries cycle
+// through kRingS - 2 slots.  Every slot carries a tag (point index | depth << 16), so a read knows
+// whether the slot still holds the entry of the depth it asks for; an entry that has been
+// overwritten is found again from the stack mask and recomputed from its checkpoint and the
+// inputs.
+constexpr int kRingS = 12;
+
+template <bool W>
+struct RingCoord {
+  using type = double2;  // lane-relative (x, y)
+};
+template <>
+struct RingCoord<false> {
+  using type = double;  // y only: x is the point index
 };
 
-// Ring slot of stack depth i: depths 0 and 1 keep slots of their own, deeper ones cycle through
-// kRing slots (an entry of depth i >= 2 is held while i >= the lane's lowest valid depth).
-__device__ __forceinline__ int ring_slot(int i) { return i < 2 ? i : 2 + ((i - 2) & (kRing - 1)); }
+// LDS of one wavefront.
+template <bool W>
+struct ChunkLds {
+  typename RingCoord<W>::type ring[kRingS][kWave];
+  uint32_t rtag[kRingS][kWave];
+  uint32_t smask[kSubW][kWave];  // stack bit mask over the lane's points 0..256
+  int depth[kWave];              // final stack depth
+  int lo[kWave], hi[kWave];      // surviving depth range of the lane's stack
+  double2 start[kWave + 1];      // lane starts, chunk-relative; [l + 1] is lane l's end point
+};
 
-// Lane-relative coordinates and point index of lane l's running sums at its point q, from the
-// checkpoint below q and the inputs (the same operations in the same order as the chain).
+// Ring slot of stack depth i.
+__device__ __forceinline__ int ring_slot(int i) { return i < 2 ? i : 2 + (i - 2) % (kRingS - 2); }
+
+// Slot of depth i + 1 from the slot s of depth i, and of depth i - 1 from the slot s of depth i.
+__device__ __forceinline__ int ring_next(int s) { return s == kRingS - 1 ? 2 : s + 1; }
+__device__ __forceinline__ int ring_prev(int s, int i) { return (s == 2 && i > 2) ? kRingS - 1 : s - 1; }
+
+__device__ __forceinline__ uint32_t ring_tag(int q, int i) { return (uint32_t)q | ((uint32_t)i << 16); }
+
+template <bool W>
+__device__ __forceinline__ void ring_put(ChunkLds<W>& L, int s, int lane, double x, double y,
+                                         uint32_t tag) {
+  if constexpr (W) L.ring[s][lane] = double2{x, y};
+  else L.ring[s][lane] = y;
+  L.rtag[s][lane] = tag;
+}
+
+// Reads slot s of lane l: point index q, lane-relative coordinates, and whether the slot holds
+// the entry of depth i (tag and coordinates are read together, whatever the answer).
+template <bool W>
+__device__ __forceinline__ bool ring_get(const ChunkLds<W>& L, int s, int l, int i, int& q,
+                                         double& x, double& y) {
+  const uint32_t tg = L.rtag[s][l];
+  const typename RingCoord<W>::type P = L.ring[s][l];
+  q = (int)(tg & 0xffffu);
+  if constexpr (W) {
+    x = P.x;
+    y = P.y;
+  } else {
+    x = (double)q;
+    y = P;
+  }
+  return (tg >> 16) == (uint32_t)i;
+}
+
+// Lane-relative coordinates of lane l's point q, from the checkpoint below q and the inputs (the
+// same operations in the same order as the chain).  ck = the chunk's checkpoints.
 template <typename T, bool W>
-__device__ double2 lane_point(const ChunkLds& L, int l, int q, const T* yl, const T* wl) {
-  q = min(max(q, 0), kSub);
+__device__ double2 lane_point(const double* ckx, const double* cky, int l, int q, int c,
+                              const T* yl, const T* wl) {
+  q = min(max(q, 0), c);
   const int j = min(q / kCk, kLaneW - 1);
-  double2 P = L.ck[j][l];
+  double2 P{W ? ckx[l * kLaneW + j] : 0.0, cky[l * kLaneW + j]};
   uint32_t f = 0u;
   for (int e = kCk * j; e < q; ++e) {
     double yd = (double)yl[e], wd = W ? (double)wl[e] : 1.0;
@@ -114,15 +161,27 @@ __device__ double2 lane_point(const ChunkLds& L, int l, int q, const T* yl, cons
   return P;
 }
 
-// Lane-relative coordinates and point index q of the stack entry at depth i of lane l.
-template <typename T, bool W>
-__device__ double2 lane_entry(ChunkLds& L, int l, int i, const T* y, const T* w, int64_t off,
-                              int len, int& q) {
-  if (i < 2 || i >= L.lowv[l]) {
-    q = L.ringi[ring_slot(i)][l];
-    return L.ring[ring_slot(i)][l];
+// Stack mask word ww of lane l; the word the chain is filling (cw) is still in a register.
+template <bool W>
+__device__ __forceinline__ uint32_t mask_word(const ChunkLds<W>& L, int l, int ww, int wi,
+                                              uint32_t curw) {
+  return ww == wi ? curw : L.smask[ww][l];
+}
+
+// Point index of the stack entry at depth i of lane l (after the chain: the whole mask is in
+// LDS): the ring's tag, else the i-th set bit (from 0) of the stack mask.  The stack holds more
+// than i entries, so the bit exists; the clamp keeps later reads inside the lane.
+template <bool W>
+__device__ int lane_index(const ChunkLds<W>& L, int l, int i, int c, bool& in_ring) {
+  in_ring = false;
+  if (i == 0) return 0;
+  const int s = ring_slot(i);
+  const uint32_t tg = L.rtag[s][l];
+  if ((tg >> 16) == (uint32_t)i) {
+    in_ring = true;
+    return (int)(tg & 0xffffu);
   }
-  int rem = i;  // the entry at depth i is the i-th set bit (from 0) of the stack mask
+  int rem = i;
   int wd = 0;
   for (; wd < kSubW - 1; ++wd) {
     const int pc = __popc(L.smask[wd][l]);
@@ -131,30 +190,61 @@ __device__ double2 lane_entry(ChunkLds& L, int l, int i, const T* y, const T* w,
   }
   uint32_t word = L.smask[wd][l];
   for (int r = 0; r < rem && word; ++r) word &= word - 1u;
-  // (the stack holds i + 1 entries, so the bit exists; the clamp keeps reads in the lane)
-  q = word ? kCk * wd + __builtin_ctz(word) : 0;
-  q = min(q, min(max(len - kSub * l, 0), kSub));
-  const int64_t eb = off + (int64_t)l * kSub;
-  return lane_point<T, W>(L, l, q, y + eb, W ? w + eb : nullptr);
+  const int q = word ? kCk * wd + __builtin_ctz(word) : 0;
+  return min(q, c);
 }
 
-// Chunk-relative coordinates of the stack entry at depth i of lane l.
+// Point index q and lane-relative coordinates of the stack entry at depth i of lane l.
 template <typename T, bool W>
-__device__ __forceinline__ double2 chunk_entry(ChunkLds& L, int l, int i, const T* y, const T* w,
-                                               int64_t off, int len) {
-  if (i == 0) return L.start[l];
-  if (i == L.depth[l] - 1) return L.start[l + 1];
-  int q;
-  const double2 P = lane_entry<T, W>(L, l, i, y, w, off, len, q);
+__device__ double2 lane_entry(const ChunkLds<W>& L, const double* ckx, const double* cky, int l,
+                              int i, int c, const T* yl, const T* wl, int& q) {
+  bool in_ring;
+  q = lane_index<W>(L, l, i, c, in_ring);
+  if (i == 0) return double2{0.0, 0.0};
+  if (in_ring) {
+    double x, yy;
+    (void)ring_get<W>(L, ring_slot(i), l, i, q, x, yy);
+    return double2{x, yy};
+  }
+  return lane_point<T, W>(ckx, cky, l, q, c, yl, wl);
+}
+
+// Chunk-relative coordinates and point index q (0..256, within the lane) of the stack entry at
+// depth i of lane l.
+template <typename T, bool W>
+__device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const double* ckx,
+                                               const double* cky, int l, int i, int len,
+                                               const T* yc, const T* wc, int& q) {
+  const int c = min(max(len - kSub * l, 0), kSub);
+  if (i == 0) {
+    q = 0;
+    return L.start[l];
+  }
+  if (i == L.depth[l] - 1) {
+    q = c;
+    return L.start[l + 1];
+  }
+  const double2 P = lane_entry<T, W>(L, ckx, cky, l, i, c, yc + kSub * l,
+                                     W ? wc + kSub * l : nullptr, q);
   const double2 S = L.start[l];
   return double2{W ? S.x + P.x : (double)(kSub * l + q), S.y + P.y};
 }
 
 template <typename T, bool W>
-__global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* __restrict__ w,
-                                              T* __restrict__ z, int64_t n, int m, ChunkOut out) {
-  __shared__ ChunkLds L;
-  constexpr int TN = Tile<T>::N;  // elements per load tile
+__device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const double* ckx,
+                                               const double* cky, int l, int i, int len,
+                                               const T* yc, const T* wc) {
+  int q;
+  return chunk_entry<T, W>(L, ckx, cky, l, i, len, yc, wc, q);
+}
+
+template <typename T, bool W>
+__global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y,
+                                                        const T* __restrict__ w,
+                                                        T* __restrict__ z, int64_t n, int m,
+                                                        ChunkOut out) {
+  __shared__ ChunkLds<W> L;
+  constexpr int TN = Tile<T, W>::N;  // elements per load tile
   constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
   const int64_t g = blockIdx.x;
@@ -168,68 +258,92 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
   const int nl = (len + kSub - 1) / kSub;            // lanes holding elements
   const bool vec = (((uintptr_t)(y + off)) % 16 == 0) && (!W || ((uintptr_t)(w + off)) % 16 == 0) &&
                    (((uintptr_t)(z + off)) % 16 == 0);
-  const T* yl = y + off + e0;
-  const T* wl = W ? w + off + e0 : nullptr;
+  const T* yc = y + off;  // the chunk's inputs
+  const T* wc = W ? w + off : nullptr;
+  const T* yl = yc + e0;  // the lane's
+  const T* wl = W ? wc + e0 : nullptr;
   T* zl = z + off + e0;
+  double* ckx = out.ckx + g * (int64_t)(kWave * kLaneW);  // the chunk's checkpoints
+  double* cky = out.cky + g * (int64_t)(kWave * kLaneW);
 
   // ---- a1-a3: stream the lane's elements through the chain.  Point P_q (0 < q < c) lies between
   // the elements q - 1 and q, whose slopes are y_{q-1} and y_q; unless y_{q-1} < y_q it is not a
   // strict vertex of any hull containing its neighbours, so it is never pushed.
   for (int wd = 0; wd < kSubW; ++wd) L.smask[wd][lane] = 0u;
+  for (int sl = 0; sl < kRingS; ++sl) L.rtag[sl][lane] = 0xffffffffu;
   uint32_t f = 0u;
-  int d = 0, ti = 0, ui = 0, lowv = 2;
-  double2 Tp{0.0, 0.0}, Up{0.0, 0.0};
+  // The top three stack entries T (depth d - 1), U (d - 2) and V (d - 3) are held in registers
+  // with their point indices ti, ui, vi and ring slots ts, us, vs.
+  int d = 0, ti = 0, ui = 0, vi = 0, ts = 0, us = 0, vs = 0;
+  double tx = 0.0, ty = 0.0, ux = 0.0, uy = 0.0, vx = 0.0, vy = 0.0;
   double lx = 0.0, ly = 0.0;
   double yprev = 0.0;
   int wi = 0;
   uint32_t curw = 0u;
-  if (c > 0) {
-    L.ring[0][lane] = Tp;
-    L.ringi[0][lane] = 0;
+  if (c > 0) {  // point 0 at depth 0
+    ring_put<W>(L, 0, lane, 0.0, 0.0, ring_tag(0, 0));
     d = 1;
     curw = 1u;
   }
   int pops = 0;
-  // pushes point q with lane-relative coordinates K, popping what it makes non-convex
-  auto push = [&](const double2 K, int q) {
-    bool more = d >= 2 && !(turn_pts(Up, Tp, K) > 0.0);
-    while (more) {
-      const uint32_t bit = 1u << (ti & 31);
-      if ((ti >> 5) == wi) curw &= ~bit;
-      else atomicAnd(&L.smask[ti >> 5][lane], ~bit);
-      ++pops;
-      Tp = Up;
-      ti = ui;
-      --d;
-      more = false;
-      if (d >= 2) {
-        const int dd = d - 2;
-        const int sl = ring_slot(dd);
-        Up = L.ring[sl][lane];
-        ui = L.ringi[sl][lane];
-        if (dd >= 2 && dd < lowv) {
-          // the new under-top has left the ring: the highest stack bit below ti, recomputed
-          int ww = ti >> 5;
-          uint32_t mw = (ww == wi ? curw : L.smask[ww][lane]) & ((1u << (ti & 31)) - 1u);
-          while (mw == 0u) {
-            --ww;
-            mw = (ww == wi) ? curw : L.smask[ww][lane];
-          }
-          ui = kCk * ww + 31 - __builtin_clz(mw);
-          Up = lane_point<T, W>(L, lane, ui, yl, wl);
-        }
-        more = !(turn_pts(Up, Tp, K) > 0.0);
+  // V after a pop: depth d - 3 from its ring slot, else (overwritten) the highest stack bit below
+  // ui, recomputed.  The recomputation waits for its own loads before it leaves, so that no load
+  // of it is still pending where the loop continues.
+  auto refill_v = [&]() {
+    vs = max(ring_prev(us, d - 2), 0);
+    const bool ok = ring_get<W>(L, vs, lane, d - 3, vi, vx, vy);  // (unused while d < 3)
+    if (d >= 3 && !ok) {
+      int ww = ui >> 5;
+      uint32_t mw = mask_word<W>(L, lane, ww, wi, curw) & ((1u << (ui & 31)) - 1u);
+      while (mw == 0u) {
+        --ww;
+        mw = mask_word<W>(L, lane, ww, wi, curw);
       }
+      vi = kCk * ww + 31 - __builtin_clz(mw);
+      const double2 P = lane_point<T, W>(ckx, cky, lane, vi, c, yl, wl);
+      vx = P.x;
+      vy = P.y;
+      __builtin_amdgcn_s_waitcnt(0);
     }
-    const int sl = ring_slot(d);
-    L.ring[sl][lane] = K;
-    L.ringi[sl][lane] = (uint16_t)q;
-    lowv = max(lowv, d - kRing + 1);
+  };
+  // pushes point q with lane-relative coordinates (kx, ky), first popping what it makes
+  // non-convex (pop while the turn (U, T, K) is not strictly left)
+  auto push = [&](const double kx, const double ky, const int q) {
+    bool more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
+    while (more) {
+      // T leaves the stack: its bit is cleared in LDS (the word being filled is rewritten from
+      // curw later) and in curw
+      const uint32_t nbit = ~(1u << (ti & 31));
+      atomicAnd(&L.smask[ti >> 5][lane], nbit);
+      if ((ti >> 5) == wi) curw &= nbit;
+      ++pops;
+      tx = ux;
+      ty = uy;
+      ti = ui;
+      ts = us;
+      ux = vx;
+      uy = vy;
+      ui = vi;
+      us = vs;
+      --d;
+      refill_v();
+      more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
+    }
+    const int ks = ring_next(ts);
+    ring_put<W>(L, ks, lane, kx, ky, ring_tag(q, d));
     curw |= 1u << (q & 31);
-    Up = Tp;
+    vx = ux;
+    vy = uy;
+    vi = ui;
+    vs = us;
+    ux = tx;
+    uy = ty;
     ui = ti;
-    Tp = K;
+    us = ts;
+    tx = kx;
+    ty = ky;
     ti = q;
+    ts = ks;
     ++d;
   };
   const int ntiles = (c + TN - 1) / TN;
@@ -253,7 +367,10 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
   if (ntiles > 0) load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
     const int eb = t * TN;  // lane-relative index of the tile's first element
-    if ((eb & (kCk - 1)) == 0) L.ck[eb / kCk][lane] = double2{lx, ly};
+    if ((eb & (kCk - 1)) == 0) {
+      if (W) ckx[lane * kLaneW + eb / kCk] = lx;
+      cky[lane * kLaneW + eb / kCk] = ly;
+    }
     if ((eb >> 5) != wi) {  // the tile's points 32 w .. are in mask word w (same for every lane)
       L.smask[wi][lane] = curw;
       wi = eb >> 5;
@@ -266,74 +383,107 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
       wv[k] = W ? nw[k] : (T)1;
     }
     if (t + 1 < ntiles) load_tile(eb + TN);
-    const int pops0 = pops;
-    bool skipped = false;
-    // one element through the chain: its left point q (a candidate when y_{q-1} < y_q), then
-    // the running sums
-    auto element = [&](int k) {
-      if (eb + k < c) {
-        double yd = (double)yv[k];
-        double wd = W ? (double)wv[k] : 1.0;
-        classify<W>(yd, wd, f);
-        const int q = eb + k;
-        if (q > 0) {
-          if (yprev < yd) push(double2{W ? lx : (double)q, ly}, q);
-          else skipped = true;
-        }
-        if (W) lx += wd;
-        ly += wd * yd;
-        yprev = yd;
-      }
-    };
-    // A tile whose elements are clean and strictly increasing in y after the previous element
-    // has every turn among its points strictly convex in exact arithmetic (the slopes of the
-    // one-element edges are the y values), so once its first point sits on the stack above the
-    // previous one, the rest are pushed without tests.
-    bool clean = eb + TN <= c;
+    const int kn = min(TN, c - eb);
+    // Tile checks.  A non-finite value or a weight <= 0 is replaced by (y, w) = (0, 1) and its
+    // kind recorded.  When the tile's elements are clean and strictly increasing in y after the
+    // previous element, every turn among its points and the two before them is strictly convex
+    // in exact arithmetic (the slopes of the one-element edges are the y values), so once the
+    // stack's top two entries are the points just before the tile's (the first of them was
+    // pushed on top of its own predecessor, so its turn is convex too), all of the tile's points
+    // are pushed without tests.
+    bool clean = kn == TN, incr = true;
     {
       double yp = yprev;
 #pragma unroll
       for (int k = 0; k < TN; ++k) {
         const double yd = (double)yv[k];
         const double wd = W ? (double)wv[k] : 1.0;
-        clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0 && (yp < yd || (eb == 0 && k == 0));
+        clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0;
+        incr = incr && (yp < yd || (eb == 0 && k == 0));
         yp = yd;
       }
     }
-    element(0);
-    const bool bulk = clean && (eb == 0 ? d == 1 : (ti == eb && ui == eb - 1));
-    if (__all(bulk)) {
-      const int d0 = d;
+    if (!__all(clean)) {
 #pragma unroll
-      for (int k = 1; k < TN; ++k) {
-        const double2 K{W ? lx : (double)(eb + k), ly};
-        const int depth = d0 + k - 1;
-        if (k >= TN - kRing || depth < 2) {
-          const int sl = ring_slot(depth);
-          L.ring[sl][lane] = K;
-          L.ringi[sl][lane] = (uint16_t)(eb + k);
+      for (int k = 0; k < TN; ++k) {
+        if (k < kn) {
+          double yd = (double)yv[k], wd = W ? (double)wv[k] : 1.0;
+          classify<W>(yd, wd, f);
+          yv[k] = (T)yd;
+          if (W) wv[k] = (T)wd;
         }
-        if (k == TN - 2) Up = K;
-        if (k == TN - 1) Tp = K;
-        const double wd = W ? (double)wv[k] : 1.0;
-        if (W) lx += wd;
-        ly += wd * (double)yv[k];
+      }
+    }
+    const int pops0 = pops;
+    bool skipped = false;
+    // one element through the chain: its left point q (a candidate when y_{q-1} < y_q), then
+    // the running sums
+    auto element = [&](int k) {
+      const double yd = (double)yv[k];
+      const double wd = W ? (double)wv[k] : 1.0;
+      const int q = eb + k;
+      if (q > 0) {
+        if (yprev < yd) push(W ? lx : (double)q, ly, q);
+        else skipped = true;
+      }
+      if (W) lx += wd;
+      ly += wd * yd;
+      yprev = yd;
+    };
+    // pushes the tile's points eb + k, k >= kp, without tests, and consumes its elements k >= kc
+    // (point eb + k is pushed before element k is added to the running sums)
+    auto bulk_push = [&](const int kp, const int kc) {
+      int s = ts;
+#pragma unroll
+      for (int k = 0; k < TN; ++k) {
+        if (k >= kp) {
+          const double kx = W ? lx : (double)(eb + k), ky = ly;
+          s = ring_next(s);
+          if (k >= TN - (kRingS - 2) || d < 2) ring_put<W>(L, s, lane, kx, ky, ring_tag(eb + k, d));
+          vx = ux;
+          vy = uy;
+          vi = ui;
+          vs = us;
+          ux = tx;
+          uy = ty;
+          ui = ti;
+          us = ts;
+          tx = kx;
+          ty = ky;
+          ti = eb + k;
+          ts = s;
+          ++d;
+        }
+        if (k >= kc) {
+          const double wd = W ? (double)wv[k] : 1.0;
+          if (W) lx += wd;
+          ly += wd * (double)yv[k];
+        }
       }
       yprev = (double)yv[TN - 1];
-      ui = eb + TN - 2;
-      ti = eb + TN - 1;
-      d = d0 + TN - 1;
-      lowv = max(lowv, d - kRing);
-      const int b0 = (eb & 31) + 1, b1 = (eb & 31) + TN - 1;  // bits of points eb+1 .. eb+TN-1
+      const int b0 = (eb & 31) + kp, b1 = (eb & 31) + TN - 1;  // bits of points eb+kp .. eb+TN-1
       curw |= (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u);
+    };
+    // bulk from the tile's first point, or else after element 0 went through the chain (at
+    // eb == 0, d == 1 means point 0 alone on the stack)
+    bool bulk = __all(clean && incr && (eb == 0 ? d == 1 : (ti == eb - 1 && ui == eb - 2)));
+    int kp = eb == 0 ? 1 : 0, kc = 0;
+    if (!bulk) {
+      if (kn > 0) element(0);
+      bulk = __all(clean && incr && ti == eb && (eb == 0 ? d == 1 : ui == eb - 1));
+      kp = 1;
+      kc = 1;
+    }
+    if (bulk) {
+      bulk_push(kp, kc);
     } else {
-#pragma unroll
-      for (int k = 1; k < TN; ++k) element(k);
+#pragma unroll 1
+      for (int k = 1; k < kn; ++k) element(k);
     }
     // speculative fit of a tile that pushed every point and popped none: every element is its
     // own block so far
     uint8_t zt = 0;
-    if (pops == pops0 && !skipped && eb + TN <= c && vec) {
+    if (pops == pops0 && !skipped && kn == TN && vec) {
 #pragma unroll
       for (int k = 0; k < TN / VN; ++k) store16(zl + eb + k * VN, &yv[k * VN]);
       zt = 1;
@@ -341,13 +491,18 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
     out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
   }
   if (c > 0) {
-    // the lane's end point
+    // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
+    // point of the lane has one)
+    if ((c & (kCk - 1)) == 0 && c < kSub) {
+      if (W) ckx[lane * kLaneW + c / kCk] = lx;
+      cky[lane * kLaneW + c / kCk] = ly;
+    }
     if ((c >> 5) != wi) {
       L.smask[wi][lane] = curw;
       wi = c >> 5;
       curw = 0u;
     }
-    push(double2{W ? lx : (double)c, ly}, c);
+    push(W ? lx : (double)c, ly, c);
     L.smask[wi][lane] = curw;
   }
   for (int t = ntiles; t < kSub / TN; ++t) out.ztile[g * (int64_t)kZTiles + (e0 + t * TN) / TN] = 0;
@@ -375,7 +530,6 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
   L.start[lane] = double2{sx, sy};
   if (lane == nl - 1) L.start[lane + 1] = double2{ix, iy};
   L.depth[lane] = d;
-  L.lowv[lane] = lowv;
   int lo = 1, hi = d - 1;  // depth 0 is the previous lane's end point (lane 0: the chunk start)
   L.lo[lane] = lo;
   L.hi[lane] = hi;
@@ -398,8 +552,8 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
       ai = L.depth[al] - 1;                        // alpha = s
       bl = min(__builtin_ctzll(nzr & ~lanes_below(sB)), lb);  // beta = B's first vertex
       bi = L.lo[bl];
-      double2 Pa = chunk_entry<T, W>(L, al, ai, y, w, off, len);
-      double2 Pb = chunk_entry<T, W>(L, bl, bi, y, w, off, len);
+      double2 Pa = chunk_entry<T, W>(L, ckx, cky, al, ai, len, yc, wc);
+      double2 Pb = chunk_entry<T, W>(L, ckx, cky, bl, bi, len, yc, wc);
       for (int pass = 0; pass <= kChunk; ++pass) {
         bool moved = false;
         // alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
@@ -418,7 +572,7 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
               pi = 0;
             }
           }
-          const double2 Pp = chunk_entry<T, W>(L, pl, pi, y, w, off, len);
+          const double2 Pp = chunk_entry<T, W>(L, ckx, cky, pl, pi, len, yc, wc);
           if (turn_pts(Pp, Pa, Pb) > 0.0) break;
           al = pl;
           ai = pi;
@@ -435,7 +589,7 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
             ql = min(__builtin_ctzll(nzr & ~lanes_below(bl + 1)), lb);
             qi = max(L.lo[ql], 1);
           }
-          const double2 Pq = chunk_entry<T, W>(L, ql, qi, y, w, off, len);
+          const double2 Pq = chunk_entry<T, W>(L, ckx, cky, ql, qi, len, yc, wc);
           if (turn_pts(Pa, Pb, Pq) > 0.0) break;
           bl = ql;
           bi = qi;
@@ -476,11 +630,7 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
   const int rank = incl - cnt;
   const uint32_t fl = (__ballot((f & ISO_ROW_NONFINITE_BIT) != 0) ? ISO_ROW_NONFINITE_BIT : 0u) |
                       (__ballot((f & ISO_ROW_BAD_WEIGHT_BIT) != 0) ? ISO_ROW_BAD_WEIGHT_BIT : 0u);
-  // coordinates of every surviving entry are at hand (no recomputation) unless the range reaches
-  // below the ring among depths 2 .. d - 2
-  const int ha = max(lo, 2), hb = min(hi, d - 2);
-  const bool held = !nonempty || ha > hb || ha >= lowv;
-  const bool listable = total <= kListCap && __all(held);
+  const bool listable = total <= kListCap;
   if (lane == 0) {
     out.nverts[g] = total;
     out.desc[g] = make_int4(j, 0, total - 1, 0);
@@ -500,9 +650,8 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
       pos = 1;
     }
     for (int i = lo; i <= hi; ++i) {
-      int q = c;
-      if (i != d - 1) (void)lane_entry<T, W>(L, lane, i, y, w, off, len, q);
-      const double2 P = chunk_entry<T, W>(L, lane, i, y, w, off, len);
+      int q;
+      const double2 P = chunk_entry<T, W>(L, ckx, cky, lane, i, len, yc, wc, q);
       out.lk[lb0 + pos] = (uint16_t)(e0 + q);
       out.lx[lb0 + pos] = P.x;
       out.ly[lb0 + pos] = P.y;
@@ -518,9 +667,8 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
     const int l1 = __builtin_ctzll(nz);       // vertex 1: the first entry of the first range
     const int lz = 63 - __builtin_clzll(nz);  // vertex V - 1 ends the last range
     if (lane == l1) {
-      int q = c;
-      if (lo != d - 1) (void)lane_entry<T, W>(L, lane, lo, y, w, off, len, q);
-      const double2 P = chunk_entry<T, W>(L, lane, lo, y, w, off, len);
+      int q;
+      const double2 P = chunk_entry<T, W>(L, ckx, cky, lane, lo, len, yc, wc, q);
       out.bnd[g].x = P.x;
       out.bnd[g].y = P.y;
       out.bndk[g].x = e0 + q;
@@ -536,9 +684,8 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
       double2 P{0.0, 0.0};
       int kq = 0;
       if (in_lz || before) {
-        int q = c;
-        if (i != d - 1) (void)lane_entry<T, W>(L, lane, i, y, w, off, len, q);
-        P = chunk_entry<T, W>(L, lane, i, y, w, off, len);
+        int q;
+        P = chunk_entry<T, W>(L, ckx, cky, lane, i, len, yc, wc, q);
         kq = e0 + q;
       }
       out.bnd[g].z = P.x;
@@ -548,9 +695,9 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
   }
   int qlo = kSub + 1, qhi = -1;  // the stack bits of depths lo..hi span points [qlo, qhi]
   if (nonempty) {
-    (void)lane_entry<T, W>(L, lane, lo, y, w, off, len, qlo);
-    if (hi == d - 1) qhi = c;
-    else (void)lane_entry<T, W>(L, lane, hi, y, w, off, len, qhi);
+    bool in_ring;
+    qlo = lane_index<W>(L, lane, lo, c, in_ring);
+    qhi = hi == d - 1 ? c : lane_index<W>(L, lane, hi, c, in_ring);
   }
   // bit 0 of the lane's first word is the previous lane's end point
   const int top_kept = (nonempty && hi == d - 1 && c == kSub) ? 1 : 0;
@@ -592,13 +739,6 @@ __global__ __launch_bounds__(64) void k_chunk(const T* __restrict__ y, const T* 
   const int64_t sb = g * (int64_t)kWave;
   if (W) out.lsx[sb + lane] = L.start[lane].x;
   out.lsy[sb + lane] = L.start[lane].y;
-  const int64_t cb = (g * kWave + lane) * (int64_t)kLaneW;
-#pragma unroll
-  for (int jj = 0; jj < kLaneW; ++jj) {
-    const double2 P = L.ck[jj][lane];
-    if (W) out.ckx[cb + jj] = P.x;
-    out.cky[cb + jj] = P.y;
-  }
 }
 
 }  // namespace iso

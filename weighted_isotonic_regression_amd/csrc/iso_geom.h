@@ -35,11 +35,9 @@ constexpr int kChunk = kWave * kSub;         // elements per chunk of a long row
 constexpr int kCk = 32;                      // spacing of a lane's running-sum checkpoints
 constexpr int kLaneW = kSub / kCk;           // mask words (and checkpoints) per lane
 constexpr int kSubW = kLaneW + 1;            // mask words of a lane's points 0..256
-constexpr int kRing = 16;                    // stack entries a lane keeps in LDS
 constexpr int kListCap = 256;                // chunks with at most this many hull vertices keep a list
 constexpr int kMaskW = kChunk / 32 + 1;      // mask words of a chunk (points 0..16384)
-constexpr int kZTiles = kChunk / 16;         // load tiles of a chunk (16 or 32 elements each)
-constexpr int kWalkCap = 64;                 // walk steps of a merge before it switches to search
+constexpr int kZTiles = kChunk / 8;          // load tiles of a chunk (at least 8 elements each)
 constexpr int kVjpTile = kWave * 32;         // elements per backward tile (one wavefront)
 
 // Per-row input flags (same values as ISO_ROW_NONFINITE / ISO_ROW_BAD_WEIGHT of iso.h).
@@ -524,90 +522,6 @@ ISO_HD bool bridge_search(const VS& S, const NodeList& LA, const NodeList& LB, V
     }
   }
   return false;
-}
-
-// Merge of the nodes whose lists start at chunks jA (left) and jB (right) of `row`.  The merged
-// list is written from jA's descriptor slot on and nseg updated.  Walks at most `cap` steps,
-// then searches; if the search fails through rounding it resumes the walk without a cap.
-// Returns the number of walk steps taken (for statistics).
-template <class VS>
-ISO_HD int merge_nodes(const VS& S, int64_t row, int jA, int jB, int cap) {
-  const int64_t rb = row * S.m;
-  Desc* dA = S.desc + rb + jA;
-  Desc* dB = S.desc + rb + jB;
-  NodeList LA{dA, S.nseg[rb + jA], row};
-  NodeList LB{dB, S.nseg[rb + jB], row};
-  const VRef firstA = list_first(LA);
-  const VRef lastB = list_last(LB);
-  VRef al = list_last(LA);
-  VRef be = list_succ(LB, list_first(LB));
-  GPt Pa = load_v(S, LA, al);
-  const GPt Sp = Pa;
-  GPt Pb = load_v(S, LB, be);
-  int steps = 0;
-  bool done = false;
-  bool capped = cap >= 0;
-  while (!done) {
-    bool moved = false;
-    bool hit_cap = false;
-    while (!vref_eq(al, firstA)) {
-      VRef p = list_pred(LA, al);
-      GPt Pp = load_v(S, LA, p);
-      if (gturn(Pp, Pa, Pb) <= 0.0) {
-        al = p;
-        Pa = Pp;
-        moved = true;
-        if (capped && ++steps > cap) {
-          hit_cap = true;
-          break;
-        }
-      } else {
-        break;
-      }
-    }
-    if (!hit_cap) {
-      while (!vref_eq(be, lastB)) {
-        VRef q = list_succ(LB, be);
-        GPt Pq = load_v(S, LB, q);
-        if (gturn(Pa, Pb, Pq) <= 0.0) {
-          be = q;
-          Pb = Pq;
-          moved = true;
-          if (capped && ++steps > cap) {
-            hit_cap = true;
-            break;
-          }
-        } else {
-          break;
-        }
-      }
-    }
-    if (hit_cap) {
-      VRef a2, b2;
-      if (bridge_search(S, LA, LB, firstA, al, be, lastB, Sp, a2, b2)) {
-        al = a2;
-        be = b2;
-        done = true;
-      } else {
-        capped = false;  // finish by walking
-      }
-      continue;
-    }
-    if (!moved) done = true;
-  }
-  // Cut: A keeps segments 0..al.u with the last one ending at al.p; B keeps be.u.. with the first
-  // starting at be.p, moved down to follow A's kept part.
-  const int nA = al.u + 1;
-  dA[al.u].z = al.p;
-  const int nB = LB.n - be.u;
-  Desc first = dB[be.u];
-  first.y = be.p;
-  dA[nA] = first;  // dA + nA <= dB + be.u, so every read below is of an unwritten slot
-  if (dA + nA != dB + be.u) {
-    for (int t = 1; t < nB; ++t) dA[nA + t] = dB[be.u + t];
-  }
-  S.nseg[rb + jA] = nA + nB;
-  return steps;
 }
 
 // ------------------------------------------------------------------ reconstruction

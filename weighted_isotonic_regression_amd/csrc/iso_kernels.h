@@ -9,8 +9,7 @@
 //   k_chunk         (iso_chunk.h) the chunk pass of longer rows.
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
-//   k_merge_level   one launch per level of the merge tree: segment lists merged by walk, capped
-//                   walk then Overmars-van Leeuwen search, cut and tail move (Section 3.3).
+//   k_merge_wave    (iso_merge.h) one launch per level of the merge tree, one wavefront per merge.
 //   k_ends          per chunk: its range of surviving vertices and the slopes into and out of it,
 //                   by bisection over the root list (Section 3.4).
 //   k_fit           per chunk: every element not already final gets the slope of the hull edge
@@ -82,10 +81,11 @@ __device__ __forceinline__ void store16(T* p, const T* in) {
   *reinterpret_cast<V*>(p) = v;
 }
 
-// Elements per load tile of the chunk pass: 128 bytes of each input per lane.
-template <typename T>
+// Elements per load tile of the chunk pass: 64 bytes of each input per lane when weights are
+// passed, 128 bytes otherwise (the tile and its prefetched successor stay in registers).
+template <typename T, bool W>
 struct Tile {
-  static constexpr int N = 128 / (int)sizeof(T);
+  static constexpr int N = (W ? 64 : 128) / (int)sizeof(T);
 };
 
 // q = e / d for 0 <= e < 4096, 1 <= d <= 2048 (float reciprocal, corrected to exact).
@@ -427,19 +427,6 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __re
   }
 }
 
-// ------------------------------------------------------------------ merge levels
-template <typename T, bool W>
-__global__ __launch_bounds__(256) void k_merge_level(VertexStore<T, W> S, int64_t batch, int r,
-                                                     int per_row) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= batch * per_row) return;
-  const int64_t row = t / per_row;
-  const int q = (int)(t - row * per_row);
-  const int jA = q << (r + 1);
-  const int jB = jA + (1 << r);
-  merge_nodes(S, row, jA, jB, kWalkCap);
-}
-
 // ------------------------------------------------------------------ ends
 template <typename T, bool W>
 __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W> S, EndInfo* __restrict__ ends,
@@ -471,7 +458,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
   __shared__ double sSlope[kListCap];
   __shared__ int sK[kListCap];
   __shared__ uint32_t sMask[kMaskW];
-  constexpr int TN = Tile<T>::N;
+  constexpr int TN = Tile<T, W>::N;
   const int64_t g = blockIdx.x;
   const int64_t row = g / S.m;
   const int j = (int)(g - row * S.m);
