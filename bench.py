@@ -57,14 +57,14 @@ def alg_bytes_per_elem(esz, weighted):
 def stage_alg_bytes(stage, n_elems, esz, weighted):
     """Algorithmic bytes one launch of a stage's kernel moves: the chunk pass reads y (and w), the
     fit writes z; the scan, merge and ends kernels touch only workspace."""
-    if stage == "wave":
+    if stage == "chunk":
         return n_elems * esz * (2 if weighted else 1)
     if stage == "fit":
         return n_elems * esz
     return 0
 
 
-STAGE_KERNEL = {"wave": "k_chunk", "scan": "k_scan", "merge": "k_merge_wave", "ends": "k_ends",
+STAGE_KERNEL = {"chunk": "k_chunk", "scan": "k_scan", "merge": "k_merge_wave", "ends": "k_ends",
                 "fit": "k_fit"}
 
 

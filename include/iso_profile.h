@@ -6,8 +6,9 @@
  * the same breakdown on the caller's stream with HIP events, so a benchmark can time the
  * dominant kernel inside its own timed region.
  *
- * Stages: 0 chunk/row pass (k_wave), 1 chunk-start scan (2 launches), 2 merge levels
- * (ceil(log2 m) launches), 3 ends, 4 fit.  Rows of at most 2048 elements run stage 0 only.
+ * Stages: 0 chunk pass (k_chunk; k_wave for rows of at most 2048 elements), 1 chunk-start scan
+ * (2 launches), 2 merge levels (ceil(log2 m) launches), 3 ends, 4 fit.  Rows of at most 2048
+ * elements run stage 0 only.
  *
  * While enabled, every iso_fit_ex call records one event before its first kernel and one after
  * each stage, on its stream.  The state is process-global and not thread-safe: enable, run the

@@ -271,7 +271,7 @@ int iso_prof_read(double* ms, int64_t* launches, int64_t* calls) {
 }
 
 const char* iso_prof_stage_name(int stage) {
-  static const char* names[ISO_PROF_STAGES] = {"wave", "scan", "merge", "ends", "fit"};
+  static const char* names[ISO_PROF_STAGES] = {"chunk", "scan", "merge", "ends", "fit"};
   return (stage >= 0 && stage < ISO_PROF_STAGES) ? names[stage] : "?";
 }
 
