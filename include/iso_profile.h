@@ -6,9 +6,9 @@
  * the same breakdown on the caller's stream with HIP events, so a benchmark can time the
  * dominant kernel inside its own timed region.
  *
- * Stages: 0 chunk pass (k_chunk; k_wave for rows of at most 2048 elements), 1 chunk-start scan
- * (2 launches), 2 merge levels (ceil(log2 m) launches), 3 ends, 4 fit.  Rows of at most 2048
- * elements run stage 0 only.
+ * Stages: 0 whole-diagram chunks (k_increasing), 1 chunk pass (k_chunk; k_wave for rows of at
+ * most 2048 elements), 2 chunk-start scan (2 launches), 3 merge levels (ceil(log2 m) launches),
+ * 4 ends, 5 fit.  Rows of at most 2048 elements run stage 1 only.
  *
  * While enabled, every iso_fit_ex call records one event before its first kernel and one after
  * each stage, on its stream.  The state is process-global and not thread-safe: enable, run the
@@ -23,18 +23,18 @@
 extern "C" {
 #endif
 
-enum { ISO_PROF_STAGES = 5 };
+enum { ISO_PROF_STAGES = 6 };
 
 /* Turn event recording on (1) or off (0).  Returns ISO_OK. */
 int iso_prof_enable(int on);
 
 /* Wait for the recorded events, add each stage's elapsed milliseconds and kernel launch count
- * since the last reset into ms[0..4] and launches[0..4] (arrays of ISO_PROF_STAGES entries
+ * since the last reset into ms[0..5] and launches[0..5] (arrays of ISO_PROF_STAGES entries
  * owned by the caller), store the number of timed calls in *calls, then forget the events.
  * Returns ISO_OK or ISO_EHIP. */
 int iso_prof_read(double* ms, int64_t* launches, int64_t* calls);
 
-/* Static name of a stage ("wave", "scan", "merge", "ends", "fit"), or "?". */
+/* Static name of a stage ("increasing", "chunk", "scan", "merge", "ends", "fit"), or "?". */
 const char* iso_prof_stage_name(int stage);
 
 #ifdef __cplusplus

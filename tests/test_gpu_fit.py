@@ -136,6 +136,46 @@ def test_nearly_monotone_1e8_fp64():
     assert bs.all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_increasing_chunks_with_one_break(dtype):
+    """Rows that are strictly increasing except at one element: a tie or a drop at the first,
+    middle or last element of a full 16384-element chunk (a chunk that is increasing throughout
+    is a whole-diagram hull; one that breaks late is processed again by the lane chains), and a
+    drop deep enough to pool across several increasing chunks."""
+    C = 16384
+    n = 3 * C + 100
+    t = np.float32 if dtype == "f32" else np.float64
+    base = np.arange(n, dtype=np.float64) / n
+    cases = [(C, "tie"), (C + C // 2 - 1, "drop"), (2 * C - 1, "tie"), (3 * C - 1, "drop"), (C - 1, "drop"),
+             (2 * C + 5, "cliff")]
+    rows = []
+    for pos, kind in cases:
+        y = base.copy()
+        if kind == "tie":
+            y[pos] = y[pos - 1]
+        elif kind == "drop":
+            y[pos] = y[pos - 1] - 1e-3
+        else:
+            y[pos] = -5.0
+        rows.append(y)
+    y = np.stack(rows).astype(t)
+    rng = np.random.default_rng(11)
+    w = rng.uniform(0.5, 2.0, size=y.shape).astype(t)
+    check(y, w)
+    check(y, None)
+
+
+def test_increasing_row_with_nan_is_flagged():
+    n = 2 * 16384
+    y = np.tile(np.arange(n, dtype=np.float64) / n, (2, 1))
+    y[1, 20000] = np.nan
+    z, bs, flags = gpu_fit(y, None)
+    assert flags[0] == 0 and flags[1] == 1
+    assert np.isnan(z[1]).all()
+    np.testing.assert_array_equal(z[0], y[0])
+    assert bs[0].all()
+
+
 def test_bad_rows_flagged_and_others_fitted():
     b = _gpu()
     for n in (10, 3000):

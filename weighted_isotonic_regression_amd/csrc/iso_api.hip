@@ -4,7 +4,8 @@
 //   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
 //               launch of k_wave writes z, block starts and row flags (Section 3.5).
 //   n >  2048   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
-//               k_chunk (chunk hulls), k_scan_reduce + k_scan_apply (chunk starts),
+//               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls),
+//               k_scan_reduce + k_scan_apply (chunk starts),
 //               ceil(log2 m) launches of k_merge_wave, k_ends, k_fit (Section 3.3 and 3.4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -104,6 +105,7 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 // ---- per-stage event timing (iso_profile.h)
 struct ProfCall {
   hipEvent_t ev[ISO_PROF_STAGES + 1];
+  bool own[ISO_PROF_STAGES + 1];  // false: the previous boundary's event, reused
   int launches[ISO_PROF_STAGES];
   int marks;
 };
@@ -133,7 +135,16 @@ struct Prof {
       on = false;
       return;
     }
+    c.own[c.marks] = true;
     c.ev[c.marks++] = e;
+  }
+  // a stage that launches nothing: its end is its start
+  void skip() {
+    if (!on || c.marks == 0) return;
+    c.launches[c.marks - 1] = 0;
+    c.own[c.marks] = false;
+    c.ev[c.marks] = c.ev[c.marks - 1];
+    ++c.marks;
   }
   ~Prof() {
     if (on && c.marks > 1) g_prof_calls.push_back(c);
@@ -155,6 +166,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int L = lanes_per_row(n);
     const int R = kWave / L;
     const int64_t tiles = (batch + R - 1) / R;
+    prof.skip();
     hipLaunchKernelGGL((k_wave<T, W>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
                        rflags, batch, n, L);
     prof.mark(1);
@@ -187,6 +199,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
   EndInfo* ends = (EndInfo*)(ws + Lay.o_ends);
 
+  hipLaunchKernelGGL((k_increasing<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
+  prof.mark(1);
   hipLaunchKernelGGL((k_chunk<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0,
@@ -263,7 +277,8 @@ int iso_prof_read(double* ms, int64_t* launches, int64_t* calls) {
       if (ms) ms[k] += (double)t;
       if (launches) launches[k] += c.launches[k];
     }
-    for (int k = 0; k < c.marks; ++k) (void)hipEventDestroy(c.ev[k]);
+    for (int k = 0; k < c.marks; ++k)
+      if (c.own[k]) (void)hipEventDestroy(c.ev[k]);
   }
   if (calls) *calls += (int64_t)g_prof_calls.size();
   g_prof_calls.clear();
@@ -271,7 +286,7 @@ int iso_prof_read(double* ms, int64_t* launches, int64_t* calls) {
 }
 
 const char* iso_prof_stage_name(int stage) {
-  static const char* names[ISO_PROF_STAGES] = {"chunk", "scan", "merge", "ends", "fit"};
+  static const char* names[ISO_PROF_STAGES] = {"increasing", "chunk", "scan", "merge", "ends", "fit"};
   return (stage >= 0 && stage < ISO_PROF_STAGES) ? names[stage] : "?";
 }
 

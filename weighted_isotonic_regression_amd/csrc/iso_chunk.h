@@ -52,7 +52,8 @@ struct ChunkOut {
   double* ckx;        // [G * kWave * kLaneW] lane-relative running sums at points 32 j
   double* cky;
   uint8_t* ztile;     // [G * kZTiles] 1 where the chunk pass wrote z = y for the load tile
-  uint8_t* dform;     // [G] 1 when the hull is stored in the dense form
+  uint8_t* dform;     // [G] 0 list form, 1 dense form, 2 dense form with every point a vertex
+                      //     and z = y written for the whole chunk
   double4* bnd;       // [G] dense form: coordinates of hull vertices 1 and V - 2
   int2* bndk;         // [G] their point indices
 };
@@ -238,6 +239,203 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
   return chunk_entry<T, W>(L, ckx, cky, l, i, len, yc, wc, q);
 }
 
+// Chunks whose elements are all clean and strictly increasing.  Every turn of such a chunk's
+// diagram compares two consecutive y values, so every point P_0 .. P_len is a strict vertex of the
+// chunk hull: the hull is the whole diagram and every element is its own block.  The wavefront
+// streams the chunk's len elements with coalesced 16-byte loads, checks the pattern, writes z = y
+// and stores the dense form directly: vertex bits of points 0..len set, lane starts, checkpoints
+// (here block sums accumulated in a fixed order; every later coordinate of the chunk is computed
+// from these stored values), and the cache of vertices 1 and V - 2 computed exactly as the
+// stored-form readers recompute points.  It returns false, having written only z, as soon as an
+// element breaks the pattern; the lane chains then process the chunk and rewrite everything.
+// Requires len >= 2 * kCk and 16-byte aligned y, w, z.  bsx, bsy: 512 doubles each of LDS.
+template <typename T, bool W>
+__device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__ wc,
+                                 T* __restrict__ zc, int len, int64_t g, int j,
+                                 const ChunkOut& out, double* bsx, double* bsy) {
+  constexpr int VN = Vec16<T>::N;
+  constexpr int U = 4;                 // vectors per lane per step
+  constexpr int SE = kWave * VN * U;   // elements per step
+  constexpr int BL = kCk / VN;         // lanes per 32-element block
+  const int lane = threadIdx.x;
+  {
+    // probe: the first 16 bytes of every lane's 256-element segment (noisy rows fail here, and
+    // the lines read are the ones the lane chains read first)
+    bool ok = true;
+    if (kSub * lane + VN <= len) {
+      T pv[VN];
+      load16(yc + kSub * lane, pv);
+#pragma unroll
+      for (int k = 0; k < VN; ++k) ok = ok && isfinite((double)pv[k]) && (k == 0 || pv[k - 1] < pv[k]);
+    }
+    if (!__all(ok)) return false;
+  }
+  double carry = -INFINITY;  // y of the element before the current vector (every lane)
+  for (int s0 = 0; s0 < len; s0 += SE) {
+    T yv[U * VN], wv[U * VN];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = s0 + (u * kWave + lane) * VN;
+      if (e + VN <= len) {
+        load16(yc + e, &yv[u * VN]);
+        if (W) load16(wc + e, &wv[u * VN]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+          yv[u * VN + k] = e + k < len ? yc[e + k] : (T)0;
+          if (W) wv[u * VN + k] = e + k < len ? wc[e + k] : (T)0;
+        }
+      }
+    }
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = s0 + (u * kWave + lane) * VN;
+      const double last = (double)yv[u * VN + VN - 1];
+      double prev = __shfl_up(last, 1, kWave);
+      if (lane == 0) prev = carry;
+      double sw = 0.0, sy = 0.0;
+#pragma unroll
+      for (int k = 0; k < VN; ++k) {
+        if (e + k < len) {
+          const double yd = (double)yv[u * VN + k];
+          const double wd = W ? (double)wv[u * VN + k] : 1.0;
+          ok = ok && isfinite(yd) && isfinite(wd) && wd > 0.0 && prev < yd;
+          prev = yd;
+          if (W) sw += wd;
+          sy += wd * yd;
+        }
+      }
+      carry = __shfl(last, kWave - 1, kWave);
+#pragma unroll
+      for (int o = 1; o < BL; o <<= 1) {
+        if (W) sw += __shfl_xor(sw, o, kWave);
+        sy += __shfl_xor(sy, o, kWave);
+      }
+      if ((lane & (BL - 1)) == 0 && e < kChunk) {
+        if (W) bsx[e / kCk] = sw;
+        bsy[e / kCk] = sy;
+      }
+      if (e + VN <= len) {
+        store16(zc + e, &yv[u * VN]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < VN; ++k)
+          if (e + k < len) zc[e + k] = yv[u * VN + k];
+      }
+    }
+    if (!__all(ok)) return false;
+  }
+  __syncthreads();
+  // lane l: checkpoints of its points (exclusive sums of its eight blocks; a block past len sums
+  // to zero) and its total; jv = the block of point len - 1 in the lane that holds it
+  const int kv = len - 1, lv = kv / kSub, jv = (kv % kSub) / kCk;
+  double cx = 0.0, cy = 0.0, cvx = 0.0, cvy = 0.0;
+  const int64_t cb = (g * kWave + lane) * (int64_t)kLaneW;
+#pragma unroll
+  for (int jj = 0; jj < kLaneW; ++jj) {
+    if (W) out.ckx[cb + jj] = cx;
+    out.cky[cb + jj] = cy;
+    if (jj == jv) {
+      cvx = cx;
+      cvy = cy;
+    }
+    const int bi = kLaneW * lane + jj;
+    if (kCk * bi < len) {
+      if (W) cx += bsx[bi];
+      cy += bsy[bi];
+    }
+  }
+  // lane starts: wave scan of the lane totals
+  double ix = cx, iy = cy;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const double vx = __shfl_up(ix, dd, kWave);
+    const double vy = __shfl_up(iy, dd, kWave);
+    if (lane >= dd) {
+      ix += vx;
+      iy += vy;
+    }
+  }
+  double sx = __shfl_up(ix, 1, kWave), sy = __shfl_up(iy, 1, kWave);
+  if (lane == 0) {
+    sx = 0.0;
+    sy = 0.0;
+  }
+  if (!W) sx = (double)(kSub * lane);
+  if (W) out.lsx[g * kWave + lane] = sx;
+  out.lsy[g * kWave + lane] = sy;
+  // vertex bits of points 0..len, set bits before each word
+  const int64_t mb = g * (int64_t)kMaskW;
+#pragma unroll
+  for (int wd = 0; wd < kLaneW; ++wd) {
+    const int w0 = kCk * (kLaneW * lane + wd);  // the word's first point
+    uint32_t bits = 0u;
+    if (w0 + 31 <= len) bits = 0xffffffffu;
+    else if (w0 <= len) bits = (2u << (len - w0)) - 1u;
+    out.mask[mb + kLaneW * lane + wd] = bits;
+    out.mcnt[mb + kLaneW * lane + wd] = (uint16_t)min(w0, len + 1);
+  }
+  constexpr int TN = Tile<T, W>::N;
+  for (int t = lane; t < kChunk / TN; t += kWave) out.ztile[g * (int64_t)kZTiles + t] = (t + 1) * TN <= len ? 1 : 0;
+  if (lane == 0) {
+    // vertex 1 = point 1: lane 0's checkpoint 0 (zero) plus element 0
+    const double w0 = W ? (double)wc[0] : 1.0;
+    double ax = 0.0, ay = 0.0;
+    if (W) ax += w0;
+    ay += w0 * (double)yc[0];
+    out.bnd[g].x = W ? 0.0 + ax : 1.0;
+    out.bnd[g].y = 0.0 + ay;
+    out.bndk[g].x = 1;
+    out.nverts[g] = len + 1;
+    out.desc[g] = make_int4(j, 0, len, 0);
+    out.nseg[g] = 1;
+    out.cflags[g] = 0u;
+    out.dform[g] = 2;
+  }
+  if (lane == kWave - 1) {
+    out.mask[mb + kMaskW - 1] = len == kChunk ? 1u : 0u;  // point 16384
+    out.mcnt[mb + kMaskW - 1] = (uint16_t)min(kChunk, len + 1);
+    out.tot[g] = make_double2(W ? ix : (double)len, iy);
+  }
+  if (lane == lv) {
+    // vertex V - 2 = point len - 1: this lane's checkpoint below it plus its elements from the
+    // checkpoint on, in order
+    double ax = cvx, ay = cvy;
+    for (int e = kSub * lv + kCk * jv; e < kv; ++e) {
+      const double wd = W ? (double)wc[e] : 1.0;
+      if (W) ax += wd;
+      ay += wd * (double)yc[e];
+    }
+    out.bnd[g].z = W ? sx + ax : (double)kv;
+    out.bnd[g].w = sy + ay;
+    out.bndk[g].y = kv;
+  }
+  return true;
+}
+
+// Runs before k_chunk: one wavefront per chunk tries increasing_chunk on chunks of at least 64
+// elements whose inputs are 16-byte aligned, and marks the chunk's form byte 2 when it succeeds,
+// 3 otherwise (k_chunk then processes the chunk and writes its form).
+template <typename T, bool W>
+__global__ __launch_bounds__(64) void k_increasing(const T* __restrict__ y, const T* __restrict__ w,
+                                                   T* __restrict__ z, int64_t n, int m, ChunkOut out) {
+  __shared__ double bsx[kChunk / kCk];
+  __shared__ double bsy[kChunk / kCk];
+  const int64_t g = blockIdx.x;
+  const int64_t row = g / m;
+  const int j = (int)(g - row * m);
+  const int64_t off = row * n + (int64_t)j * kChunk;
+  const int64_t rem = n - (int64_t)j * kChunk;
+  const int len = rem < kChunk ? (int)rem : kChunk;
+  const bool vec = (((uintptr_t)(y + off)) % 16 == 0) && (!W || ((uintptr_t)(w + off)) % 16 == 0) &&
+                   (((uintptr_t)(z + off)) % 16 == 0);
+  bool done = false;
+  if (len >= 2 * kCk && vec)
+    done = increasing_chunk<T, W>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bsx, bsy);
+  if (!done && threadIdx.x == 0) out.dform[g] = 3;
+}
+
 template <typename T, bool W>
 __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y,
                                                         const T* __restrict__ w,
@@ -265,6 +463,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   T* zl = z + off + e0;
   double* ckx = out.ckx + g * (int64_t)(kWave * kLaneW);  // the chunk's checkpoints
   double* cky = out.cky + g * (int64_t)(kWave * kLaneW);
+  if (out.dform[g] == 2) return;  // done by k_increasing
 
   // ---- a1-a3: stream the lane's elements through the chain.  Point P_q (0 < q < c) lies between
   // the elements q - 1 and q, whose slopes are y_{q-1} and y_q; unless y_{q-1} < y_q it is not a

@@ -266,7 +266,7 @@ struct VertexStore {
   Desc* desc;             // [G] descriptor slots
   int* nseg;              // [G] length of the list of the node starting at this slot
   const int* nverts;      // [G] vertex count of each chunk hull
-  const uint8_t* dense;   // [G] 1 for the dense form
+  const uint8_t* dense;   // [G] 0 list form, 1 dense form, 2 dense form of an all-vertex chunk
   const double* lx;       // [G * kListCap] list form
   const double* ly;
   const uint16_t* lk;

@@ -483,6 +483,15 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
     return;
   }
   const T zin = (T)e.sin, zout = (T)e.sout;
+  if (S.dense[g] == 2 && e.khi == len && (e.klo == 0 || (e.klo == 1 && e.p0v))) {
+    // every point of the chunk is a vertex of the chunk hull, and all of them are vertices of the
+    // row's hull (point 0 possibly as the previous chunk's last vertex): every element is its own
+    // block, and z = y was written for the whole chunk
+    if (bstart) {
+      for (int i = tid; i < len; i += kFitThreads) bstart[off + i] = 1;
+    }
+    return;
+  }
   if (!S.is_list(g)) {
     for (int q = tid; q < kMaskW; q += kFitThreads) sMask[q] = S.mask[g * kMaskW + q];
     __syncthreads();
