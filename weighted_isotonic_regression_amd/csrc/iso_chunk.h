@@ -485,13 +485,18 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     curw = 1u;
   }
   int pops = 0;
-  // V after a pop: depth d - 3 from its ring slot, else (overwritten) the highest stack bit below
-  // ui, recomputed.  The recomputation waits for its own loads before it leaves, so that no load
-  // of it is still pending where the loop continues.
-  auto refill_v = [&]() {
-    vs = max(ring_prev(us, d - 2), 0);
-    const bool ok = ring_get<W>(L, vs, lane, d - 3, vi, vx, vy);  // (unused while d < 3)
-    if (d >= 3 && !ok) {
+  // V is refilled from the ring after each pop (depth d - 3); its tag is checked only when the
+  // next pop is about to make it U, so the LDS read overlaps the next turn.  An overwritten entry
+  // is recomputed: the highest stack bit below ui, from its checkpoint and the inputs; that
+  // recomputation waits for its own loads before it leaves, so no load of it is still pending
+  // where the loop continues.
+  uint32_t vtag = 0u;
+  bool vchk = false;
+  auto check_v = [&]() {
+    if (!vchk) return;
+    vi = (int)(vtag & 0xffffu);
+    if (!W) vx = (double)vi;
+    if (d >= 3 && (vtag >> 16) != (uint32_t)(d - 3)) {
       int ww = ui >> 5;
       uint32_t mw = mask_word<W>(L, lane, ww, wi, curw) & ((1u << (ui & 31)) - 1u);
       while (mw == 0u) {
@@ -504,29 +509,44 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       vy = P.y;
       __builtin_amdgcn_s_waitcnt(0);
     }
+    vchk = false;
   };
   // pushes point q with lane-relative coordinates (kx, ky), first popping what it makes
-  // non-convex (pop while the turn (U, T, K) is not strictly left)
+  // non-convex (pop while the turn (U, T, K) is not strictly left).  A popped entry's stack bit
+  // is cleared in LDS (the word being filled is rewritten from curw later) and in curw.
   auto push = [&](const double kx, const double ky, const int q) {
     bool more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
-    while (more) {
-      // T leaves the stack: its bit is cleared in LDS (the word being filled is rewritten from
-      // curw later) and in curw
-      const uint32_t nbit = ~(1u << (ti & 31));
-      atomicAnd(&L.smask[ti >> 5][lane], nbit);
-      if ((ti >> 5) == wi) curw &= nbit;
-      ++pops;
-      tx = ux;
-      ty = uy;
-      ti = ui;
-      ts = us;
-      ux = vx;
-      uy = vy;
-      ui = vi;
-      us = vs;
-      --d;
-      refill_v();
-      more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
+    if (more) {
+      while (more) {
+        check_v();
+        {
+          const uint32_t nbit = ~(1u << (ti & 31));
+          atomicAnd(&L.smask[ti >> 5][lane], nbit);
+          if ((ti >> 5) == wi) curw &= nbit;
+        }
+        ++pops;
+        tx = ux;
+        ty = uy;
+        ti = ui;
+        ts = us;
+        ux = vx;
+        uy = vy;
+        ui = vi;
+        us = vs;
+        --d;
+        vs = max(ring_prev(us, d - 2), 0);
+        const uint32_t tg = L.rtag[vs][lane];
+        if constexpr (W) {
+          const double2 P = L.ring[vs][lane];
+          vx = P.x;
+          vy = P.y;
+        } else {
+          vy = L.ring[vs][lane];
+        }
+        vtag = tg;  // (the point index and the check wait until V is used)
+        vchk = true;
+        more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
+      }
     }
     const int ks = ring_next(ts);
     ring_put<W>(L, ks, lane, kx, ky, ring_tag(q, d));
@@ -543,6 +563,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     ty = ky;
     ti = q;
     ts = ks;
+    vchk = false;
     ++d;
   };
   const int ntiles = (c + TN - 1) / TN;
