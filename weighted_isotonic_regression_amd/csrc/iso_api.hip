@@ -199,7 +199,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
   EndInfo* ends = (EndInfo*)(ws + Lay.o_ends);
 
-  hipLaunchKernelGGL((k_increasing<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
+  hipLaunchKernelGGL((k_increasing<T, W>), dim3((unsigned)G), dim3(kIncWaves * kWave), 0, s, y, w, z, n,
+                     m, co);
   prof.mark(1);
   hipLaunchKernelGGL((k_chunk<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);

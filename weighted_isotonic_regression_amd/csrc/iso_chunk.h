@@ -241,49 +241,62 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
 
 // Chunks whose elements are all clean and strictly increasing.  Every turn of such a chunk's
 // diagram compares two consecutive y values, so every point P_0 .. P_len is a strict vertex of the
-// chunk hull: the hull is the whole diagram and every element is its own block.  The wavefront
-// streams the chunk's len elements with coalesced 16-byte loads, checks the pattern, writes z = y
-// and stores the dense form directly: vertex bits of points 0..len set, lane starts, checkpoints
-// (here block sums accumulated in a fixed order; every later coordinate of the chunk is computed
-// from these stored values), and the cache of vertices 1 and V - 2 computed exactly as the
-// stored-form readers recompute points.  It returns false, having written only z, as soon as an
-// element breaks the pattern; the lane chains then process the chunk and rewrite everything.
-// Requires len >= 2 * kCk and 16-byte aligned y, w, z.  bsx, bsy: 512 doubles each of LDS.
+// chunk hull: the hull is the whole diagram and every element is its own block.  A workgroup of
+// kIncWaves wavefronts streams the chunk's len elements with coalesced 16-byte loads (wavefront
+// q takes the q-th quarter), checks the pattern, writes z = y and stores the dense form directly:
+// vertex bits of points 0..len set, lane starts, checkpoints (here block sums accumulated in a
+// fixed order; every later coordinate of the chunk is computed from these stored values), and the
+// cache of vertices 1 and V - 2 computed exactly as the stored-form readers recompute points.
+// It returns false, having written only z, when an element breaks the pattern; the lane chains
+// then process the chunk and rewrite everything.  Requires len >= 2 * kCk and 16-byte aligned y,
+// w, z.  bsx, bsy: 512 doubles each of LDS (block sums); bad: an int of LDS.
+constexpr int kIncWaves = 4;
+
 template <typename T, bool W>
 __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__ wc,
                                  T* __restrict__ zc, int len, int64_t g, int j,
-                                 const ChunkOut& out, double* bsx, double* bsy) {
+                                 const ChunkOut& out, double* bsx, double* bsy, int* bad) {
   constexpr int VN = Vec16<T>::N;
-  constexpr int U = 4;                 // vectors per lane per step
-  constexpr int SE = kWave * VN * U;   // elements per step
-  constexpr int BL = kCk / VN;         // lanes per 32-element block
-  const int lane = threadIdx.x;
+  constexpr int U = 4;                   // vectors per lane per step
+  constexpr int SE = kWave * VN * U;     // elements per step of one wavefront
+  constexpr int BL = kCk / VN;           // lanes per 32-element block
+  constexpr int QE = kChunk / kIncWaves; // elements per wavefront
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  if (threadIdx.x == 0) *bad = 0;
   {
-    // probe: the first 16 bytes of every lane's 256-element segment (noisy rows fail here, and
-    // the lines read are the ones the lane chains read first)
+    // probe: the first 64 bytes of each of the wavefront's 16 lane segments (noisy rows fail
+    // here, and the lines read are the ones the lane chains read first)
     bool ok = true;
-    if (kSub * lane + VN <= len) {
+    const int e = kSub * (16 * wv + (lane & 15)) + VN * (lane >> 4);
+    if (e + VN <= len) {
       T pv[VN];
-      load16(yc + kSub * lane, pv);
+      load16(yc + e, pv);
+      const double before = (lane >> 4) ? (double)yc[e - 1] : -INFINITY;
+      double prev = before;
 #pragma unroll
-      for (int k = 0; k < VN; ++k) ok = ok && isfinite((double)pv[k]) && (k == 0 || pv[k - 1] < pv[k]);
+      for (int k = 0; k < VN; ++k) {
+        const double yd = (double)pv[k];
+        ok = ok && isfinite(yd) && prev < yd;
+        prev = yd;
+      }
     }
-    if (!__all(ok)) return false;
+    if (__syncthreads_or(!ok)) return false;
   }
-  double carry = -INFINITY;  // y of the element before the current vector (every lane)
-  for (int s0 = 0; s0 < len; s0 += SE) {
-    T yv[U * VN], wv[U * VN];
+  const int q0 = QE * wv, q1 = min(QE * (wv + 1), len);
+  double carry = q0 > 0 && q0 < len ? (double)yc[q0 - 1] : -INFINITY;
+  for (int s0 = q0; s0 < q1; s0 += SE) {
+    T yv[U * VN], wv_[U * VN];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = s0 + (u * kWave + lane) * VN;
-      if (e + VN <= len) {
+      if (e + VN <= q1) {
         load16(yc + e, &yv[u * VN]);
-        if (W) load16(wc + e, &wv[u * VN]);
+        if (W) load16(wc + e, &wv_[u * VN]);
       } else {
 #pragma unroll
         for (int k = 0; k < VN; ++k) {
-          yv[u * VN + k] = e + k < len ? yc[e + k] : (T)0;
-          if (W) wv[u * VN + k] = e + k < len ? wc[e + k] : (T)0;
+          yv[u * VN + k] = e + k < q1 ? yc[e + k] : (T)0;
+          if (W) wv_[u * VN + k] = e + k < q1 ? wc[e + k] : (T)0;
         }
       }
     }
@@ -297,9 +310,9 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
       double sw = 0.0, sy = 0.0;
 #pragma unroll
       for (int k = 0; k < VN; ++k) {
-        if (e + k < len) {
+        if (e + k < q1) {
           const double yd = (double)yv[u * VN + k];
-          const double wd = W ? (double)wv[u * VN + k] : 1.0;
+          const double wd = W ? (double)wv_[u * VN + k] : 1.0;
           ok = ok && isfinite(yd) && isfinite(wd) && wd > 0.0 && prev < yd;
           prev = yd;
           if (W) sw += wd;
@@ -312,23 +325,29 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
         if (W) sw += __shfl_xor(sw, o, kWave);
         sy += __shfl_xor(sy, o, kWave);
       }
-      if ((lane & (BL - 1)) == 0 && e < kChunk) {
+      if ((lane & (BL - 1)) == 0 && e < q1) {
         if (W) bsx[e / kCk] = sw;
         bsy[e / kCk] = sy;
       }
-      if (e + VN <= len) {
+      if (e + VN <= q1) {
         store16(zc + e, &yv[u * VN]);
       } else {
 #pragma unroll
         for (int k = 0; k < VN; ++k)
-          if (e + k < len) zc[e + k] = yv[u * VN + k];
+          if (e + k < q1) zc[e + k] = yv[u * VN + k];
       }
     }
-    if (!__all(ok)) return false;
+    if (!__all(ok)) {
+      if (lane == 0) *bad = 1;
+      break;
+    }
+    if (*(volatile int*)bad) break;  // another wavefront failed (seen late at worst)
   }
-  __syncthreads();
-  // lane l: checkpoints of its points (exclusive sums of its eight blocks; a block past len sums
-  // to zero) and its total; jv = the block of point len - 1 in the lane that holds it
+  if (__syncthreads_or(*bad)) return false;
+  if (wv != 0) return true;
+  // wavefront 0 stores the form.  Lane l: checkpoints of its points (exclusive sums of its eight
+  // blocks; a block past len sums to zero) and its total; jv = the block of point len - 1 in the
+  // lane that holds it
   const int kv = len - 1, lv = kv / kSub, jv = (kv % kSub) / kCk;
   double cx = 0.0, cy = 0.0, cvx = 0.0, cvy = 0.0;
   const int64_t cb = (g * kWave + lane) * (int64_t)kLaneW;
@@ -388,7 +407,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     out.bnd[g].y = 0.0 + ay;
     out.bndk[g].x = 1;
     out.nverts[g] = len + 1;
-    out.desc[g] = make_int4(j, 0, len, 0);
+    out.desc[g] = make_int4(j, 0, len, 2);
     out.nseg[g] = 1;
     out.cflags[g] = 0u;
     out.dform[g] = 2;
@@ -414,14 +433,17 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   return true;
 }
 
-// Runs before k_chunk: one wavefront per chunk tries increasing_chunk on chunks of at least 64
+// Runs before k_chunk: one workgroup per chunk tries increasing_chunk on chunks of at least 64
 // elements whose inputs are 16-byte aligned, and marks the chunk's form byte 2 when it succeeds,
 // 3 otherwise (k_chunk then processes the chunk and writes its form).
 template <typename T, bool W>
-__global__ __launch_bounds__(64) void k_increasing(const T* __restrict__ y, const T* __restrict__ w,
-                                                   T* __restrict__ z, int64_t n, int m, ChunkOut out) {
+__global__ __launch_bounds__(kIncWaves * kWave) void k_increasing(const T* __restrict__ y,
+                                                                  const T* __restrict__ w,
+                                                                  T* __restrict__ z, int64_t n,
+                                                                  int m, ChunkOut out) {
   __shared__ double bsx[kChunk / kCk];
   __shared__ double bsy[kChunk / kCk];
+  __shared__ int bad;
   const int64_t g = blockIdx.x;
   const int64_t row = g / m;
   const int j = (int)(g - row * m);
@@ -432,7 +454,8 @@ __global__ __launch_bounds__(64) void k_increasing(const T* __restrict__ y, cons
                    (((uintptr_t)(z + off)) % 16 == 0);
   bool done = false;
   if (len >= 2 * kCk && vec)
-    done = increasing_chunk<T, W>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bsx, bsy);
+    done = increasing_chunk<T, W>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bsx, bsy,
+                                  &bad);
   if (!done && threadIdx.x == 0) out.dform[g] = 3;
 }
 
@@ -853,7 +876,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   const bool listable = total <= kListCap;
   if (lane == 0) {
     out.nverts[g] = total;
-    out.desc[g] = make_int4(j, 0, total - 1, 0);
+    out.desc[g] = make_int4(j, 0, total - 1, listable ? 0 : 1);
     out.nseg[g] = 1;
     out.cflags[g] = fl;
     out.dform[g] = listable ? 0 : 1;

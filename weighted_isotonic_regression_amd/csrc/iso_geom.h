@@ -248,7 +248,8 @@ ISO_HD double gslope(const GPt& a, const GPt& b) {
 }
 
 // Segment descriptor: x = chunk index within the row, y = first vertex position, z = last
-// vertex position (positions count the chunk hull's vertices from 0), w unused.
+// vertex position (positions count the chunk hull's vertices from 0), w = the chunk hull's
+// storage form (0 list, 1 dense, 2 dense form of an all-vertex chunk).
 using Desc = int4;
 
 // ------------------------------------------------------------------ chunk hull storage
@@ -375,6 +376,21 @@ struct VertexStore {
     for (int r = p - (int)mc[lo]; r > 0; --r) word &= word - 1u;
     k = lo * 32 + __builtin_ctz(word);
     dense_point(row, j, k, x, yy);
+  }
+
+  // pt() for a chunk known to be in list form (one round of independent loads).
+  ISO_HD GPt pt_list(int64_t row, int j, int p) const {
+    const int64_t g = row * m + j;
+    const int64_t idx = g * kListCap + p;
+    GPt r;
+    r.x = lx[idx];
+    r.y = ly[idx];
+    const double4 s = start[g];
+    r.sxh = s.x;
+    r.sxl = s.y;
+    r.syh = s.z;
+    r.syl = s.w;
+    return r;
   }
 
   ISO_HD GPt pt(int64_t row, int j, int p) const {

@@ -155,15 +155,151 @@ __device__ void merge_finish_walk(const VS& S, const NodeList& LA, const NodeLis
   }
 }
 
+// The vertices beyond s on one side (dir -1: towards the list's first vertex, +1: towards its
+// last), up to kWave of them, stopping before the first dense-form segment: lane i gets v_{i+1},
+// the (i+1)-th vertex from s (mine, P) when i < nw.  exhausted: the window reaches the end of the
+// list.  One read of descriptors and one read of points.
+template <class VS>
+__device__ void side_window(const VS& S, const NodeList& L, int dir, VRef s, int lane,
+                            MergeLds& W, int& nw, bool& exhausted, VRef& mine, GPt& P) {
+  const int u = s.u + dir * lane;
+  const bool inr = dir < 0 ? u >= 0 : u < L.n;
+  Desc dj = make_int4(0, 0, -1, 0);
+  if (inr) dj = L.d[u];
+  const uint64_t dm = __ballot(inr && dj.w != 0);
+  const int fd = dm ? __builtin_ctzll(dm) : kWave;  // first dense segment
+  int cnt = 0;
+  if (inr && lane < fd) cnt = lane == 0 ? (dir < 0 ? s.p - dj.y : dj.z - s.p) : dj.z - dj.y + 1;
+  int cum = cnt;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const int o = __shfl_up(cum, dd, kWave);
+    if (lane >= dd) cum += o;
+  }
+  W.cum[lane] = cum;
+  W.d[lane] = dj;
+  wave_sync();
+  const int total = __shfl(cum, kWave - 1, kWave);
+  nw = min(total, kWave - 1);
+  const bool all_segs = dir < 0 ? (s.u - (kWave - 1) <= 0) : (s.u + (kWave - 1) >= L.n - 1);
+  exhausted = fd == kWave && all_segs && total <= kWave - 1;
+  mine = s;
+  P = GPt{0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  const int want = lane + 1;
+  if (want <= nw) {
+    int lo = 0, hi = kWave - 1;  // smallest j with cum[j] >= want
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (W.cum[mid] >= want) hi = mid;
+      else lo = mid + 1;
+    }
+    const int before = lo > 0 ? W.cum[lo - 1] : 0;
+    const int k = want - before - 1;  // 0-based from the segment's near end
+    const Desc d = W.d[lo];
+    int rank;
+    if (dir < 0) rank = (lo == 0) ? s.p - 1 - k : d.z - k;
+    else rank = (lo == 0) ? s.p + 1 + k : d.y + k;
+    mine = VRef{s.u + dir * lo, rank};
+    P = S.pt_list(L.row, d.x, rank);
+  }
+}
+
+// First phase of a merge: the walk of Lemma 4.2 on the vertices next to s.  Both side windows are
+// read at once (a_i = the i-th vertex of A left of s, b_i of B right of s, a_0 = b_0 = s), then
+// the walks alternate on registers: alpha stops at a_k when (a_{k+1}, a_k, beta) is a strict
+// left turn, beta at b_k when (alpha, b_k, b_{k+1}) is; each walk's first stop is found with a
+// ballot.  Returns true with the bridge (al, be) when both walks end inside their windows, else
+// false with the furthest positions reached (al, be, Pa, Pb), from which the walk continues in
+// memory.
+template <class VS>
+__device__ bool window_bridge(const VS& S, const NodeList& LA, const NodeList& LB, int lane,
+                              MergeLds& WA, MergeLds& WB, const GPt& Sp, VRef& al, VRef& be,
+                              GPt& Pa, GPt& Pb) {
+  int na, nb;
+  bool exA, exB;
+  VRef ra, rb;
+  GPt PA, PB;
+  side_window(S, LA, -1, list_last(LA), lane, WA, na, exA, ra, PA);
+  side_window(S, LB, +1, list_first(LB), lane, WB, nb, exB, rb, PB);
+  al = list_last(LA);
+  Pa = Sp;
+  if (nb < 1) {  // (no list-form vertex after s in B's window)
+    be = list_succ(LB, list_first(LB));
+    Pb = load_v(S, LB, be);
+    return false;
+  }
+  be = VRef{__shfl(rb.u, 0, kWave), __shfl(rb.p, 0, kWave)};
+  Pb = shfl_pt(PB, 0);
+  int ka = 0, kb = 1;
+  const GPt Aprev = [&]() {  // lane i: a_i
+    GPt r = shfl_up_pt(PA, lane);
+    if (lane == 0) r = Sp;
+    return r;
+  }();
+  const GPt Bnext = [&]() {  // lane i: b_{i+2}
+    GPt r;
+    r.x = __shfl_down(PB.x, 1, kWave);
+    r.y = __shfl_down(PB.y, 1, kWave);
+    r.sxh = __shfl_down(PB.sxh, 1, kWave);
+    r.sxl = __shfl_down(PB.sxl, 1, kWave);
+    r.syh = __shfl_down(PB.syh, 1, kWave);
+    r.syl = __shfl_down(PB.syl, 1, kWave);
+    return r;
+  }();
+  for (int it = 0; it < 4 * kWave; ++it) {
+    bool moved = false;
+    // alpha: lane i decides k = i (a_{i+1} = its own PA); k = na has no a_{na+1} in the window
+    {
+      const bool st = lane >= ka && ((lane < na && gturn(PA, Aprev, Pb) > 0.0) || (lane == na && exA));
+      const uint64_t hit = __ballot(st);
+      if (!hit) {  // alpha walks past the window
+        ka = na;
+        al = ka == 0 ? list_last(LA) : VRef{__shfl(ra.u, ka - 1, kWave), __shfl(ra.p, ka - 1, kWave)};
+        if (ka > 0) Pa = shfl_pt(PA, ka - 1);
+        return false;
+      }
+      const int k = __builtin_ctzll(hit);
+      if (k != ka) {
+        moved = true;
+        ka = k;
+        al = VRef{__shfl(ra.u, ka - 1, kWave), __shfl(ra.p, ka - 1, kWave)};
+        Pa = shfl_pt(PA, ka - 1);
+      }
+    }
+    // beta: lane i decides k = i + 1 (b_{i+1} = its own PB, b_{i+2} from lane i + 1); k = nb
+    // has no b_{nb+1} in the window
+    {
+      const int k1 = lane + 1;
+      const bool st = k1 >= kb && ((k1 < nb && gturn(Pa, PB, Bnext) > 0.0) || (k1 == nb && exB));
+      const uint64_t hit = __ballot(st);
+      if (!hit) {  // beta walks past the window
+        kb = nb;
+        be = VRef{__shfl(rb.u, kb - 1, kWave), __shfl(rb.p, kb - 1, kWave)};
+        Pb = shfl_pt(PB, kb - 1);
+        return false;
+      }
+      const int k = __builtin_ctzll(hit) + 1;
+      if (k != kb) {
+        moved = true;
+        kb = k;
+        be = VRef{__shfl(rb.u, kb - 1, kWave), __shfl(rb.p, kb - 1, kWave)};
+        Pb = shfl_pt(PB, kb - 1);
+      }
+    }
+    if (!moved) return true;
+  }
+  return false;
+}
+
 template <typename T, bool W>
 __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<T, W> S,
                                                                     int64_t batch, int r,
                                                                     int per_row) {
-  __shared__ MergeLds sw[kMergeWaves];
+  __shared__ MergeLds sw[kMergeWaves][2];
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * kMergeWaves + wid;
   if (t >= batch * per_row) return;  // the whole wavefront
-  MergeLds& Wl = sw[wid];
+  MergeLds& Wl = sw[wid][0];
   const int64_t row = t / per_row;
   const int qm = (int)(t - row * per_row);
   const int jA = qm << (r + 1);
@@ -175,22 +311,25 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
   const NodeList LB{dB, S.nseg[rb + jB], row};
   const VRef firstA = list_first(LA);
   const VRef lastB = list_last(LB);
-  VRef al = list_last(LA);
-  VRef be = list_succ(LB, list_first(LB));
-  GPt Pa = load_v(S, LA, al);
-  const GPt Sp = Pa;
-  GPt Pb = load_v(S, LB, be);
-  // the test that s is a strictly convex vertex: one step of each side
-  bool convex = true;
-  if (!vref_eq(al, firstA)) {
-    const GPt Pp = load_v(S, LA, list_pred(LA, al));
-    if (!(gturn(Pp, Pa, Pb) > 0.0)) convex = false;
+  VRef al, be;
+  GPt Pa, Pb;
+  const GPt Sp = load_v(S, LA, list_last(LA));
+  bool settled = window_bridge(S, LA, LB, lane, sw[wid][0], sw[wid][1], Sp, al, be, Pa, Pb);
+  if (!settled) {
+    // both walks may already stop where the windows ended (always the case at a strictly convex
+    // s, which dense-form chunks, outside the windows, reach this way): one step of each side
+    settled = true;
+    if (!vref_eq(al, firstA)) {
+      const GPt Pp = load_v(S, LA, list_pred(LA, al));
+      if (!(gturn(Pp, Pa, Pb) > 0.0)) settled = false;
+    }
+    if (settled && !vref_eq(be, lastB)) {
+      const GPt Pq = load_v(S, LB, list_succ(LB, be));
+      if (!(gturn(Pa, Pb, Pq) > 0.0)) settled = false;
+    }
   }
-  if (convex && !vref_eq(be, lastB)) {
-    const GPt Pq = load_v(S, LB, list_succ(LB, be));
-    if (!(gturn(Pa, Pb, Pq) > 0.0)) convex = false;
-  }
-  if (!convex) {
+  if (!settled) {
+    // the walk continues in memory, 64 vertices at a time, from where the windows ended
     bool searched = false;
     for (int pass = 0; pass < 4 * kChunk; ++pass) {
       bool moved = false;
@@ -246,9 +385,10 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
     dA[nA] = first;
   }
   // dA + nA <= dB + be.u, so a write never lands on a descriptor a later read needs; each lane
-  // keeps four reads in flight
+  // keeps four reads in flight.  When they are equal the tail is already in place.
   constexpr int kCopy = 4;
-  for (int b = 1; b < nB; b += kCopy * kWave) {
+  const int bstart = (dA + nA == dB + be.u) ? nB : 1;
+  for (int b = bstart; b < nB; b += kCopy * kWave) {
     Desc dd[kCopy];
 #pragma unroll
     for (int k = 0; k < kCopy; ++k) {
