@@ -423,7 +423,8 @@ struct NodeList {
 
 template <class VS>
 ISO_HD GPt load_v(const VS& S, const NodeList& L, VRef v) {
-  return S.pt(L.row, L.d[v.u].x, v.p);
+  const Desc d = L.d[v.u];
+  return d.w == 0 ? S.pt_list(L.row, d.x, v.p) : S.pt(L.row, d.x, v.p);
 }
 
 ISO_HD VRef list_first(const NodeList& L) { return {0, L.d[0].y}; }

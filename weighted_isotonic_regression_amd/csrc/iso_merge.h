@@ -11,10 +11,12 @@
 //                bisection of iso_geom.h).
 //
 // On the page a level runs one thread per merge when it has many merges.  Here every merge has
-// a wavefront, which walks 64 vertices at a time: the lanes gather the next 64 vertices of the
-// walk (the segments' lengths come from one coalesced read of 64 descriptors and a wave scan),
-// test the walk's predicate on all of them at once and take the first stop with a ballot.  The
-// tail of the right child's list is moved by all lanes.
+// a wavefront.  It first reads up to 64 list-form vertices on each side of s into registers and
+// runs both walks there, one ballot per walk (window_bridge); that settles nearly every merge
+// of the lower levels.  A longer walk continues in memory 256 vertices at a time: the lanes
+// gather the next vertices of the walk (the segments' lengths come from one coalesced read of
+// descriptors and a scan), test the walk's predicate on all of them at once and take the first
+// stop with a ballot.  The tail of the right child's list is moved by all lanes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,7 +27,6 @@
 namespace iso {
 
 constexpr int kMergeWaves = 4;   // merges per workgroup of 256
-constexpr int kWinCap = 32;      // walk windows of one side pass before switching to the search
 
 struct MergeLds {
   int cum[kWave];
@@ -62,70 +63,130 @@ __device__ __forceinline__ GPt shfl_pt(const GPt& p, int src) {
 }
 
 // One window of a walk over the list L from v (exclusive), in direction dir (-1: towards the
-// list's first vertex, +1: towards its last).  Lane i takes v_{i+1}, the (i+1)-th vertex from v.
-// The walk stops at v_i (v_0 = v) when stop(v_i, v_{i+1}) holds.  Returns true when the walk
-// stopped inside this window; in every case v and Pv are advanced to where the walk stands.
+// list's first vertex, +1: towards its last): the kWalkK * kWave vertices after v, lane i taking
+// v_{kWalkK i + 1} .. v_{kWalkK i + kWalkK}.  The segments' lengths come from one read of up to
+// kWalkK * kWave descriptors and a scan in LDS.  The walk stops at v_i when stop(v_i, v_{i+1})
+// holds; returns true when it stopped inside this window, and in every case advances v and Pv to
+// where the walk stands.
+constexpr int kWalkK = 4;
+constexpr int kWideCap = 32;  // wide windows of one side pass before switching to the search
+
+struct WideLds {
+  int cum[kWalkK * kWave];
+  Desc d[kWalkK * kWave];
+};
+
 template <class VS, class Stop>
-__device__ bool walk_window(const VS& S, const NodeList& L, int dir, VRef& v, GPt& Pv, int lane,
-                            MergeLds& W, Stop stop) {
-  // segment lane j: v.u + dir * j, and the number of its vertices beyond v
-  const int uj = v.u + dir * lane;
-  int cnt = 0;
-  Desc dj = make_int4(0, 0, -1, 0);
-  if (uj >= 0 && uj < L.n) {
-    dj = L.d[uj];
-    if (lane == 0) cnt = dir < 0 ? v.p - dj.y : dj.z - v.p;
-    else cnt = dj.z - dj.y + 1;
+__device__ bool walk_window_wide(const VS& S, const NodeList& L, int dir, VRef& v, GPt& Pv,
+                                 int lane, WideLds& W, Stop stop) {
+  constexpr int NW = kWalkK * kWave;
+  // segments j = lane * kWalkK + t: v.u + dir * j, and the number of their vertices beyond v
+  int cnt[kWalkK];
+  int lsum = 0;
+#pragma unroll
+  for (int t = 0; t < kWalkK; ++t) {
+    const int jj = lane * kWalkK + t;
+    const int uj = v.u + dir * jj;
+    Desc dj = make_int4(0, 0, -1, 0);
+    int c = 0;
+    if (uj >= 0 && uj < L.n) {
+      dj = L.d[uj];
+      if (jj == 0) c = dir < 0 ? v.p - dj.y : dj.z - v.p;
+      else c = dj.z - dj.y + 1;
+    }
+    W.d[jj] = dj;
+    cnt[t] = c;
+    lsum += c;
   }
-  int cum = cnt;
+  int incl = lsum;
 #pragma unroll
   for (int dd = 1; dd < kWave; dd <<= 1) {
-    const int o = __shfl_up(cum, dd, kWave);
-    if (lane >= dd) cum += o;
+    const int o = __shfl_up(incl, dd, kWave);
+    if (lane >= dd) incl += o;
   }
-  W.cum[lane] = cum;
-  W.d[lane] = dj;
+  int run = incl - lsum;
+#pragma unroll
+  for (int t = 0; t < kWalkK; ++t) {
+    run += cnt[t];
+    W.cum[lane * kWalkK + t] = run;
+  }
   wave_sync();
-  const int total = __shfl(cum, kWave - 1, kWave);
-  const int want = lane + 1;
-  const bool valid = want <= total;
-  VRef mine = v;
-  GPt P = Pv;
-  if (valid) {
-    int lo = 0, hi = kWave - 1;  // smallest j with cum[j] >= want
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (W.cum[mid] >= want) hi = mid;
-      else lo = mid + 1;
+  const int total = __shfl(incl, kWave - 1, kWave);
+  VRef mine[kWalkK];
+  GPt P[kWalkK];
+  bool valid[kWalkK];
+  // the segment of each of this lane's vertices: the number of segments whose cumulative count is
+  // below the vertex's ordinal, by strides over the power-of-two table (the kWalkK searches run
+  // side by side)
+  static_assert((NW & (NW - 1)) == 0, "stride search");
+  int seg[kWalkK];
+#pragma unroll
+  for (int t = 0; t < kWalkK; ++t) seg[t] = 0;
+#pragma unroll
+  for (int st = NW / 2; st > 0; st >>= 1) {
+#pragma unroll
+    for (int t = 0; t < kWalkK; ++t) {
+      const int want = lane * kWalkK + t + 1;
+      if (W.cum[seg[t] + st - 1] < want) seg[t] += st;
     }
-    const int before = lo > 0 ? W.cum[lo - 1] : 0;
-    const int k = want - before - 1;  // 0-based from the segment's near end
-    const Desc d = W.d[lo];
-    int rank;
-    if (dir < 0) rank = (lo == 0) ? v.p - 1 - k : d.z - k;
-    else rank = (lo == 0) ? v.p + 1 + k : d.y + k;
-    mine = VRef{v.u + dir * lo, rank};
-    P = S.pt(L.row, d.x, rank);
+  }
+#pragma unroll
+  for (int t = 0; t < kWalkK; ++t) {
+    const int want = lane * kWalkK + t + 1;
+    valid[t] = want <= total;
+    mine[t] = v;
+    P[t] = Pv;
+    if (valid[t]) {
+      const int lo = seg[t];
+      const int before = lo > 0 ? W.cum[lo - 1] : 0;
+      const int k = want - before - 1;
+      const Desc d = W.d[lo];
+      int rank;
+      if (dir < 0) rank = (lo == 0) ? v.p - 1 - k : d.z - k;
+      else rank = (lo == 0) ? v.p + 1 + k : d.y + k;
+      mine[t] = VRef{v.u + dir * lo, rank};
+      P[t] = d.w == 0 ? S.pt_list(L.row, d.x, rank) : S.pt(L.row, d.x, rank);
+    }
   }
   wave_sync();
-  // lane i: v_i (from lane i - 1, lane 0: v) and v_{i+1} (its own)
-  GPt Pi = shfl_up_pt(P, lane);
+  // v_{K i} (the vertex before this lane's first): the previous lane's last, lane 0: v
+  GPt Pi = shfl_up_pt(P[kWalkK - 1], lane);
   if (lane == 0) Pi = Pv;
-  const bool st = valid && stop(Pi, P);
-  const uint64_t hit = __ballot(st || !valid);
-  const int f = hit ? __builtin_ctzll(hit) : kWave;  // first lane that stops or runs out
-  const bool stop_at_f = f < kWave && __shfl(st ? 1 : 0, f < kWave ? f : 0, kWave) != 0;
-  // the walk now stands at v_f (v_64 when no lane stopped); v_f is lane f - 1's vertex
-  const bool list_end = (dir < 0) ? (v.u - (kWave - 1) <= 0) : (v.u + (kWave - 1) >= L.n - 1);
-  if (f > 0) {
-    const int src = f - 1;
-    const int nu = __shfl(mine.u, src, kWave);
-    const int np = __shfl(mine.p, src, kWave);
-    const GPt NP = shfl_pt(P, src);
-    v = VRef{nu, np};
-    Pv = NP;
+  int first = kWalkK;  // this lane's first stop or run-out (t: stop between v_{K i + t} and v_{K i + t + 1})
+  bool first_stop = false;
+#pragma unroll
+  for (int t = kWalkK - 1; t >= 0; --t) {
+    const GPt& a = t == 0 ? Pi : P[t - 1];
+    const bool st = valid[t] && stop(a, P[t]);
+    if (st || !valid[t]) {
+      first = t;
+      first_stop = st;
+    }
   }
-  return stop_at_f || (f < kWave && list_end);
+  const uint64_t hit = __ballot(first < kWalkK);
+  const int fl = hit ? __builtin_ctzll(hit) : kWave;
+  int f = NW;  // walk position reached: v_f
+  bool stop_at_f = false;
+  if (fl < kWave) {
+    f = fl * kWalkK + __shfl(first, fl, kWave);
+    stop_at_f = __shfl(first_stop ? 1 : 0, fl, kWave) != 0;
+  }
+  const bool list_end = (dir < 0) ? (v.u - (NW - 1) <= 0) : (v.u + (NW - 1) >= L.n - 1);
+  if (f > 0) {
+    // v_f is vertex f - 1 of the window: lane (f - 1) / K, slot (f - 1) % K
+    const int src = (f - 1) / kWalkK, slot = (f - 1) % kWalkK;
+    VRef mr = mine[0];
+    GPt mp = P[0];
+#pragma unroll
+    for (int t = 1; t < kWalkK; ++t)
+      if (slot == t) {
+        mr = mine[t];
+        mp = P[t];
+      }
+    v = VRef{__shfl(mr.u, src, kWave), __shfl(mr.p, src, kWave)};
+    Pv = shfl_pt(mp, src);
+  }
+  return stop_at_f || (f < NW && list_end);
 }
 
 // Walk to the bridge one vertex at a time (no cap), from alpha in A and beta in B.
@@ -296,10 +357,10 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
                                                                     int64_t batch, int r,
                                                                     int per_row) {
   __shared__ MergeLds sw[kMergeWaves][2];
+  __shared__ WideLds sww[kMergeWaves];
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * kMergeWaves + wid;
   if (t >= batch * per_row) return;  // the whole wavefront
-  MergeLds& Wl = sw[wid][0];
   const int64_t row = t / per_row;
   const int qm = (int)(t - row * per_row);
   const int jA = qm << (r + 1);
@@ -329,32 +390,38 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
     }
   }
   if (!settled) {
-    // the walk continues in memory, 64 vertices at a time, from where the windows ended
+    // the walk continues in memory, kWalkK * 64 vertices at a time, from where the windows ended
+    WideLds& Ww = sww[wid];
     bool searched = false;
     for (int pass = 0; pass < 4 * kChunk; ++pass) {
       bool moved = false;
+      // (from the second pass on, a side whose first step already stops gathers no window)
+      bool walk_a = !vref_eq(al, firstA);
+      if (pass > 0 && walk_a) walk_a = !(gturn(load_v(S, LA, list_pred(LA, al)), Pa, Pb) > 0.0);
       // A side: alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
-      for (int win = 0; !vref_eq(al, firstA); ++win) {
-        if (win == kWinCap) {
+      for (int win = 0; walk_a && !vref_eq(al, firstA); ++win) {
+        if (win == kWideCap) {
           searched = true;
           break;
         }
         const VRef before = al;
-        const bool done = walk_window(S, LA, -1, al, Pa, lane, Wl,
-                                      [&](const GPt& vi, const GPt& vn) { return gturn(vn, vi, Pb) > 0.0; });
+        const bool done = walk_window_wide(S, LA, -1, al, Pa, lane, Ww,
+                                           [&](const GPt& vi, const GPt& vn) { return gturn(vn, vi, Pb) > 0.0; });
         if (!vref_eq(before, al)) moved = true;
         if (done) break;
       }
       if (searched) break;
+      bool walk_b = !vref_eq(be, lastB);
+      if (pass > 0 && walk_b) walk_b = !(gturn(Pa, Pb, load_v(S, LB, list_succ(LB, be))) > 0.0);
       // B side: beta moves right while (alpha, beta, succ beta) is not a strict left turn
-      for (int win = 0; !vref_eq(be, lastB); ++win) {
-        if (win == kWinCap) {
+      for (int win = 0; walk_b && !vref_eq(be, lastB); ++win) {
+        if (win == kWideCap) {
           searched = true;
           break;
         }
         const VRef before = be;
-        const bool done = walk_window(S, LB, +1, be, Pb, lane, Wl,
-                                      [&](const GPt& vi, const GPt& vn) { return gturn(Pa, vi, vn) > 0.0; });
+        const bool done = walk_window_wide(S, LB, +1, be, Pb, lane, Ww,
+                                           [&](const GPt& vi, const GPt& vn) { return gturn(Pa, vi, vn) > 0.0; });
         if (!vref_eq(before, be)) moved = true;
         if (done) break;
       }
