@@ -299,17 +299,18 @@ def main():
     if not args.no_cpu:
         import oracle
 
-        # The oracle (one thread, fp64 pool adjacent violators) on the whole row, 15 runs.
+        # The oracle (one thread, fp64 pool adjacent violators) on the whole row, 20 runs (about
+        # 12 s of CPU work).
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         yd, wd = y_h.astype(np.float64), w_h.astype(np.float64)
         times, zo = [], None
-        for _ in range(15):
+        for _ in range(20):
             t0 = time.perf_counter()
             zo = oracle.pav(yd, wd)
             times.append(time.perf_counter() - t0)
         t = sorted(times)[len(times) // 2]
         out["cpu_baseline"] = {"value": round(n / t, 1), "unit": "elements/s", "cores": 1, "kind": "oracle",
-                               "sample": "the whole 1 x 10^8 mixed row, 15 runs of the fp64 pool-adjacent-"
+                               "sample": "the whole 1 x 10^8 mixed row, 20 runs of the fp64 pool-adjacent-"
                                          "violators oracle on one thread, median %.3f s (total %.1f s)"
                                          % (t, sum(times))}
         zg = z.cpu().numpy().astype(np.float64)
