@@ -419,12 +419,22 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   }
   if (lane == lv) {
     // vertex V - 2 = point len - 1: this lane's checkpoint below it plus its elements from the
-    // checkpoint on, in order
+    // checkpoint on, in order (all loads issued before the first add)
     double ax = cvx, ay = cvy;
-    for (int e = kSub * lv + kCk * jv; e < kv; ++e) {
-      const double wd = W ? (double)wc[e] : 1.0;
-      if (W) ax += wd;
-      ay += wd * (double)yc[e];
+    const int e0v = kSub * lv + kCk * jv;
+    T ye[kCk - 1], we[kCk - 1];
+#pragma unroll
+    for (int k = 0; k < kCk - 1; ++k) {
+      ye[k] = e0v + k < kv ? yc[e0v + k] : (T)0;
+      we[k] = (W && e0v + k < kv) ? wc[e0v + k] : (T)1;
+    }
+#pragma unroll
+    for (int k = 0; k < kCk - 1; ++k) {
+      if (e0v + k < kv) {
+        const double wd = W ? (double)we[k] : 1.0;
+        if (W) ax += wd;
+        ay += wd * (double)ye[k];
+      }
     }
     out.bnd[g].z = W ? sx + ax : (double)kv;
     out.bnd[g].w = sy + ay;

@@ -385,8 +385,16 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
       if (!(gturn(Pp, Pa, Pb) > 0.0)) settled = false;
     }
     if (settled && !vref_eq(be, lastB)) {
-      const GPt Pq = load_v(S, LB, list_succ(LB, be));
-      if (!(gturn(Pa, Pb, Pq) > 0.0)) settled = false;
+      // (alpha, beta, succ beta) three consecutive points of a chunk whose y is strictly
+      // increasing (form 2: vertices are points) turn strictly left in exact arithmetic, the
+      // slopes of the two one-element edges being consecutive y values
+      const Desc d0 = LB.d[0];
+      const bool consecutive = d0.w == 2 && be.u == 0 && vref_eq(al, list_last(LA)) &&
+                               be.p == d0.y + 1 && be.p < d0.z;
+      if (!consecutive) {
+        const GPt Pq = load_v(S, LB, list_succ(LB, be));
+        if (!(gturn(Pa, Pb, Pq) > 0.0)) settled = false;
+      }
     }
   }
   if (!settled) {
