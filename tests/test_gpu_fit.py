@@ -176,6 +176,13 @@ def test_increasing_row_with_nan_is_flagged():
     assert bs[0].all()
 
 
+def test_row_of_8194_chunks():
+    """A row of more than 8192 chunks of 16384 (over 1.34e8 elements, eight scan blocks)."""
+    n = 8193 * 16384 + 77
+    y, w = W.family("noise", 1, n, seed=21, dtype="f32", wkind="uniform")
+    check(y, w, kkt=False)
+
+
 def test_bad_rows_flagged_and_others_fitted():
     b = _gpu()
     for n in (10, 3000):

@@ -407,7 +407,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     out.bnd[g].y = 0.0 + ay;
     out.bndk[g].x = 1;
     out.nverts[g] = len + 1;
-    out.desc[g] = make_int4(j, 0, len, 2);
+    out.desc[g] = make_int4(j, 0, len, desc_w(2, len + 1));
     out.nseg[g] = 1;
     out.cflags[g] = 0u;
     out.dform[g] = 2;
@@ -886,7 +886,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   const bool listable = total <= kListCap;
   if (lane == 0) {
     out.nverts[g] = total;
-    out.desc[g] = make_int4(j, 0, total - 1, listable ? 0 : 1);
+    out.desc[g] = make_int4(j, 0, total - 1, desc_w(listable ? 0 : 1, total));
     out.nseg[g] = 1;
     out.cflags[g] = fl;
     out.dform[g] = listable ? 0 : 1;

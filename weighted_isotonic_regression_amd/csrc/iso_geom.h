@@ -249,8 +249,13 @@ ISO_HD double gslope(const GPt& a, const GPt& b) {
 
 // Segment descriptor: x = chunk index within the row, y = first vertex position, z = last
 // vertex position (positions count the chunk hull's vertices from 0), w = the chunk hull's
-// storage form (0 list, 1 dense, 2 dense form of an all-vertex chunk).
+// storage form (bits 0-1: 0 list, 1 dense, 2 dense form of an all-vertex chunk) and vertex count
+// (bits 2 and up).
 using Desc = int4;
+
+ISO_HD int desc_w(int form, int nverts) { return form | (nverts << 2); }
+ISO_HD int desc_form(const Desc& d) { return d.w & 3; }
+ISO_HD int desc_nverts(const Desc& d) { return d.w >> 2; }
 
 // ------------------------------------------------------------------ chunk hull storage
 // A chunk's hull is stored in one of two forms:
@@ -393,6 +398,36 @@ struct VertexStore {
     return r;
   }
 
+  // pt() of vertex p of the chunk of descriptor d, whose form and vertex count the descriptor
+  // carries: list vertices and the dense form's cached ones need one round of loads.
+  ISO_HD GPt pt_desc(int64_t row, const Desc& d, int p) const {
+    const int form = desc_form(d), V = desc_nverts(d);
+    if (form == 0) return pt_list(row, d.x, p);
+    const int64_t g = row * m + d.x;
+    if (p == 0 || p == V - 1 || p == 1 || p == V - 2) {
+      GPt r;
+      const double4 s = start[g];
+      r.sxh = s.x;
+      r.sxl = s.y;
+      r.syh = s.z;
+      r.syl = s.w;
+      if (p == 0) {
+        r.x = 0.0;
+        r.y = 0.0;
+      } else if (p == V - 1) {
+        const double2 t = tot[g];
+        r.x = t.x;
+        r.y = t.y;
+      } else {
+        const double4 b = bnd[g];
+        r.x = p == 1 ? b.x : b.z;
+        r.y = p == 1 ? b.y : b.w;
+      }
+      return r;
+    }
+    return pt(row, d.x, p);
+  }
+
   ISO_HD GPt pt(int64_t row, int j, int p) const {
     GPt r;
     int k;
@@ -424,7 +459,7 @@ struct NodeList {
 template <class VS>
 ISO_HD GPt load_v(const VS& S, const NodeList& L, VRef v) {
   const Desc d = L.d[v.u];
-  return d.w == 0 ? S.pt_list(L.row, d.x, v.p) : S.pt(L.row, d.x, v.p);
+  return S.pt_desc(L.row, d, v.p);
 }
 
 ISO_HD VRef list_first(const NodeList& L) { return {0, L.d[0].y}; }

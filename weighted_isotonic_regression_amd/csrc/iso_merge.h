@@ -145,7 +145,7 @@ __device__ bool walk_window_wide(const VS& S, const NodeList& L, int dir, VRef& 
       if (dir < 0) rank = (lo == 0) ? v.p - 1 - k : d.z - k;
       else rank = (lo == 0) ? v.p + 1 + k : d.y + k;
       mine[t] = VRef{v.u + dir * lo, rank};
-      P[t] = d.w == 0 ? S.pt_list(L.row, d.x, rank) : S.pt(L.row, d.x, rank);
+      P[t] = S.pt_desc(L.row, d, rank);
     }
   }
   wave_sync();
@@ -227,7 +227,7 @@ __device__ void side_window(const VS& S, const NodeList& L, int dir, VRef s, int
   const bool inr = dir < 0 ? u >= 0 : u < L.n;
   Desc dj = make_int4(0, 0, -1, 0);
   if (inr) dj = L.d[u];
-  const uint64_t dm = __ballot(inr && dj.w != 0);
+  const uint64_t dm = __ballot(inr && desc_form(dj) != 0);
   const int fd = dm ? __builtin_ctzll(dm) : kWave;  // first dense segment
   int cnt = 0;
   if (inr && lane < fd) cnt = lane == 0 ? (dir < 0 ? s.p - dj.y : dj.z - s.p) : dj.z - dj.y + 1;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
       // increasing (form 2: vertices are points) turn strictly left in exact arithmetic, the
       // slopes of the two one-element edges being consecutive y values
       const Desc d0 = LB.d[0];
-      const bool consecutive = d0.w == 2 && be.u == 0 && vref_eq(al, list_last(LA)) &&
+      const bool consecutive = desc_form(d0) == 2 && be.u == 0 && vref_eq(al, list_last(LA)) &&
                                be.p == d0.y + 1 && be.p < d0.z;
       if (!consecutive) {
         const GPt Pq = load_v(S, LB, list_succ(LB, be));
