@@ -243,11 +243,11 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
 // diagram compares two consecutive y values, so every point P_0 .. P_len is a strict vertex of the
 // chunk hull: the hull is the whole diagram and every element is its own block.  A workgroup of
 // kIncWaves wavefronts streams the chunk's len elements with coalesced 16-byte loads (wavefront
-// q takes the q-th quarter), checks the pattern, writes z = y and stores the dense form directly:
-// vertex bits of points 0..len set, lane starts, checkpoints (here block sums accumulated in a
-// fixed order; every later coordinate of the chunk is computed from these stored values), and the
-// cache of vertices 1 and V - 2 computed exactly as the stored-form readers recompute points.
-// It returns false, having written only z, when an element breaks the pattern; the lane chains
+// q takes the q-th of kIncWaves equal parts), checks the pattern, writes z = y and stores the
+// dense form directly: vertex bits of points 0..len set, lane starts, checkpoints (here block
+// sums accumulated in a fixed order; every later coordinate of the chunk is computed from these
+// stored values), and the cache of vertices 1 and V - 2 computed exactly as the stored-form
+// readers recompute points.  It returns false, having written only z, when an element breaks the pattern; the lane chains
 // then process the chunk and rewrite everything.  Requires len >= 2 * kCk and 16-byte aligned y,
 // w, z.  bsx, bsy: 512 doubles each of LDS (block sums); bad: an int of LDS.
 constexpr int kIncWaves = 4;
@@ -264,14 +264,15 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
   if (threadIdx.x == 0) *bad = 0;
   {
-    // probe: the first 64 bytes of each of the wavefront's 16 lane segments (noisy rows fail
-    // here, and the lines read are the ones the lane chains read first)
+    // probe: the first kIncWaves 16-byte vectors of each of the wavefront's lane segments (noisy
+    // rows fail here, and the lines read are the ones the lane chains read first)
+    constexpr int SPW = kWave / kIncWaves;  // lane segments per wavefront
     bool ok = true;
-    const int e = kSub * (16 * wv + (lane & 15)) + VN * (lane >> 4);
+    const int e = kSub * (SPW * wv + (lane % SPW)) + VN * (lane / SPW);
     if (e + VN <= len) {
       T pv[VN];
       load16(yc + e, pv);
-      const double before = (lane >> 4) ? (double)yc[e - 1] : -INFINITY;
+      const double before = (lane / SPW) ? (double)yc[e - 1] : -INFINITY;
       double prev = before;
 #pragma unroll
       for (int k = 0; k < VN; ++k) {
