@@ -113,6 +113,46 @@ def time_fit(torch, B, sets, steps, warmup):
     return z, ms_host, st_ms, st_launch, calls
 
 
+def time_vjp(torch, B, y, w, dev, steps):
+    """iso_vjp on a row whose block starts come from one fit: reads g, y, w, z and the block starts
+    and writes gy and gw (algorithmic bytes 6 sizeof(T) + 1 per element)."""
+    print("bench: timing the backward", file=sys.stderr, flush=True)
+    batch, n = y.shape
+    code = B.ISO_F64 if y.dtype == torch.float64 else B.ISO_F32
+    stream = B._stream(torch, dev)
+    z = torch.empty_like(y)
+    bs = torch.empty((batch, n), dtype=torch.uint8, device=dev)
+    ws, nbytes = B.workspace(batch, n, code, True, dev)
+    rc = B.iso_fit_ex(B._ptr(y), B._ptr(w), B._ptr(z), B._ptr(bs), None, batch, n, code, B._ptr(ws), nbytes,
+                      0, stream)
+    if rc != 0:
+        raise B.IsoError(rc, "iso_fit_ex")
+    del ws
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    g = torch.randn(y.shape, dtype=y.dtype, device=dev, generator=gen)
+    gy, gw = torch.empty_like(y), torch.empty_like(y)
+
+    def call():
+        rc = B.iso_vjp(B._ptr(g), B._ptr(y), B._ptr(w), B._ptr(z), B._ptr(bs), B._ptr(gy), B._ptr(gw),
+                       batch, n, code, stream)
+        if rc != 0:
+            raise B.IsoError(rc, "iso_vjp")
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    esz = y.element_size()
+    nbytes_alg = batch * n * (6 * esz + 1)
+    return {"elements_per_s": round(batch * n / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+            "alg_bytes": nbytes_alg, "hbm_frac": round(nbytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def read_traffic():
     """{workload: {kernel: (fetch_bytes, write_bytes)}} from profiles/traffic.txt when it was
     measured on the current sources, else {}."""
@@ -168,6 +208,10 @@ def run_only(args, torch, B, W, dev):
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
+    if args.only == "vjp":
+        _, _, y, w = load_workload(torch, W, "mixed", dev)
+        print(json.dumps({"workload": "vjp", **time_vjp(torch, B, y, w, dev, args.steps)}), flush=True)
+        return
     _, _, y, w = load_workload(torch, W, args.only, dev)
     print("bench: timing %s" % args.only, file=sys.stderr, flush=True)
     _, ms, sms, sla, sc = time_fit(torch, B, [(y, w)], args.steps, args.warmup)
@@ -214,7 +258,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
-    ap.add_argument("--only", choices=["mixed", "short", "dense"], default=None,
+    ap.add_argument("--only", choices=["mixed", "short", "dense", "vjp"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="with --only: first run a 1 GiB device copy (memory-counter calibration)")
@@ -295,6 +339,9 @@ def main():
         "stage_ms": stage_line(st_ms, calls),
         "roofline": roofline_of("mixed_1e8_f32", st_ms, st_la, calls, n, esz, True, False, traffic),
     }
+
+    if not args.no_extra:
+        out["backward_1e8_f32"] = time_vjp(torch, B, y, w, dev, max(3, args.steps // 2))
 
     if not args.no_cpu:
         import oracle

@@ -183,6 +183,13 @@ def test_row_of_8194_chunks():
     check(y, w, kkt=False)
 
 
+def test_65537_long_rows():
+    """A batch of 65537 rows of 2049 (long rows, one chunk each): more rows than a grid's second
+    dimension holds."""
+    y, w = W.family("noise", 65537, 2049, seed=22, dtype="f32", wkind="uniform")
+    check(y, w, kkt=False)
+
+
 def test_bad_rows_flagged_and_others_fitted():
     b = _gpu()
     for n in (10, 3000):

@@ -46,3 +46,36 @@ def test_vjp_matches_block_averaging(fam, n, dtype):
         else:
             gw_h = gw.cpu().numpy().astype(np.float64)
             assert np.max(np.abs(gw_h - rw) / (1 + np.abs(rw))) <= tol
+
+
+def _check_vjp(b, y, w_, g, tol):
+    yt = torch.from_numpy(y).cuda()
+    wt = None if w_ is None else torch.from_numpy(w_).cuda()
+    gt = torch.from_numpy(g).cuda()
+    z, bs = b.fit(yt, wt, block_starts=True)
+    gy, gw = b.vjp(gt, yt, wt, z, bs)
+    torch.cuda.synchronize()
+    ry, rw = oracle.vjp(g.astype(np.float64), y.astype(np.float64),
+                        None if w_ is None else w_.astype(np.float64), z.cpu().numpy().astype(np.float64),
+                        bs.cpu().numpy())
+    assert np.max(np.abs(gy.cpu().numpy().astype(np.float64) - ry) / (1 + np.abs(ry))) <= tol
+    if w_ is not None:
+        assert np.max(np.abs(gw.cpu().numpy().astype(np.float64) - rw) / (1 + np.abs(rw))) <= tol
+
+
+@pytest.mark.parametrize("fam", ["noise", "decreasing", "sawtooth"])
+def test_vjp_rows_of_many_tiles(fam):
+    """Rows of 3073 tiles of 2048: the carries of blocks cross the scan's blocks of 1024 tiles (the
+    decreasing row is one block end to end)."""
+    b = _b()
+    n = 3 * 2**21 + 5
+    y, w = W.family(fam, 2, n, seed=5, dtype="f64", wkind="uniform")
+    g = np.random.default_rng(6).standard_normal((2, n))
+    _check_vjp(b, y, w, g, 1e-12)
+
+
+def test_vjp_65537_rows():
+    b = _b()
+    y, w = W.family("noise", 65537, 16, seed=7, dtype="f32", wkind="uniform")
+    g = np.random.default_rng(8).standard_normal((65537, 16)).astype(np.float32)
+    _check_vjp(b, y, w, g, 2e-6)

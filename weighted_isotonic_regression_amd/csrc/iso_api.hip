@@ -204,9 +204,9 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   prof.mark(1);
   hipLaunchKernelGGL((k_chunk<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);
-  hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0,
+  hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
                      s, co.tot, co.cflags, bsum, bflag, m, nblk);
-  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nblk, (unsigned)batch), dim3(kScanThreads), 0, s,
+  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
                      co.tot, bsum, bflag, start, rflags, m, nblk);
   prof.mark(2);
   VertexStore<T, W> S;
@@ -379,25 +379,35 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
   if (batch * ntile > (int64_t)INT32_MAX) return ISO_EINVAL;
   const int64_t T = batch * ntile;
   hipStream_t s = (hipStream_t)stream;
+  const int64_t nblk = (ntile + kVjpBlock - 1) / kVjpBlock;
   const size_t tb = align_up((size_t)T * sizeof(VjpTile));
+  const size_t cb = align_up((size_t)T * sizeof(double4));
+  const size_t bb = align_up((size_t)(batch * nblk) * sizeof(double4));
   void* buf = nullptr;
-  if (hipMallocAsync(&buf, tb + (size_t)T * sizeof(double4), s) != hipSuccess) return ISO_ENOMEM;
+  if (hipMallocAsync(&buf, tb + cb + 2 * bb, s) != hipSuccess) return ISO_ENOMEM;
   VjpTile* tiles = (VjpTile*)buf;
   double4* cc = (double4*)((char*)buf + tb);
+  double4* bfw = (double4*)((char*)buf + tb + cb);
+  double4* bbw = (double4*)((char*)buf + tb + cb + bb);
+  auto carries = [&]() {
+    hipLaunchKernelGGL(k_vjp_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kVjpScanThreads),
+                       0, s, (const VjpTile*)tiles, (int)ntile, (int)nblk, bfw, bbw);
+    hipLaunchKernelGGL(k_vjp_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kVjpScanThreads),
+                       0, s, (const VjpTile*)tiles, (int)ntile, (int)nblk, (const double4*)bfw,
+                       (const double4*)bbw, cc);
+  };
   if (dtype == ISO_F64) {
-    hipLaunchKernelGGL((k_vjp_tiles<double>), dim3((unsigned)T), dim3(kWave), 0, s, (const double*)g,
+    hipLaunchKernelGGL((k_vjp_tiles<double>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const double*)g,
                        (const double*)w, block_start, n, (int)ntile, tiles);
-    hipLaunchKernelGGL(k_vjp_rows, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s,
-                       (const VjpTile*)tiles, batch, (int)ntile, cc);
-    hipLaunchKernelGGL((k_vjp_apply<double>), dim3((unsigned)T), dim3(kWave), 0, s, (const double*)g,
+    carries();
+    hipLaunchKernelGGL((k_vjp_apply<double>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const double*)g,
                        (const double*)y, (const double*)w, (const double*)z, block_start,
                        (const double4*)cc, (double*)gy, (double*)gw, n, (int)ntile);
   } else {
-    hipLaunchKernelGGL((k_vjp_tiles<float>), dim3((unsigned)T), dim3(kWave), 0, s, (const float*)g,
+    hipLaunchKernelGGL((k_vjp_tiles<float>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const float*)g,
                        (const float*)w, block_start, n, (int)ntile, tiles);
-    hipLaunchKernelGGL(k_vjp_rows, dim3((unsigned)((batch + 63) / 64)), dim3(64), 0, s,
-                       (const VjpTile*)tiles, batch, (int)ntile, cc);
-    hipLaunchKernelGGL((k_vjp_apply<float>), dim3((unsigned)T), dim3(kWave), 0, s, (const float*)g,
+    carries();
+    hipLaunchKernelGGL((k_vjp_apply<float>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const float*)g,
                        (const float*)y, (const float*)w, (const float*)z, block_start,
                        (const double4*)cc, (float*)gy, (float*)gw, n, (int)ntile);
   }

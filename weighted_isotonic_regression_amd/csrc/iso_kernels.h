@@ -346,8 +346,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const double2* __r
                                                               int nblk) {
   __shared__ double sh[4 * kScanThreads];
   __shared__ uint32_t sf;
-  const int b = blockIdx.x;
-  const int64_t row = blockIdx.y;
+  const int64_t row = blockIdx.x / nblk;  // one-dimensional grid: batch * nblk blocks
+  const int b = (int)(blockIdx.x - row * nblk);
   const int t = threadIdx.x;
   if (t == 0) sf = 0u;
   __syncthreads();
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __re
                                                              int nblk) {
   __shared__ double sh[4 * kScanThreads];
   __shared__ double soff[4];
-  const int b = blockIdx.x;
-  const int64_t row = blockIdx.y;
+  const int64_t row = blockIdx.x / nblk;  // one-dimensional grid: batch * nblk blocks
+  const int b = (int)(blockIdx.x - row * nblk);
   const int t = threadIdx.x;
   if (t == 0) {
     DD2 o{{0.0, 0.0}, {0.0, 0.0}};
@@ -585,242 +585,360 @@ __global__ __launch_bounds__(256) void k_flags_any(const uint32_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------ backward (block averaging)
-// Tiles of 2048 elements (one wavefront, 32 per lane).  Per lane: whether it holds a block start,
-// the sums of (g, w) before its first start ("head"), from its last start on ("tail"), and the
-// whole lane.  Blocks crossing lanes and tiles get their sums from segmented scans.
+// With G and W the sums of g and w over the block holding element i, gy_i = w_i G / W and
+// gw_i = (y_i - z_i) G / W.  For element i, G = F_i + R_i - g_i, where F_i sums g from its block's
+// start to i (a left-to-right scan that restarts at every block start) and R_i from i to its
+// block's end (a right-to-left scan that restarts after every block end); W likewise.  Tiles of
+// kVjpTile elements, one workgroup of kVjpThreads threads each, kVjpPer2 consecutive elements
+// per thread (coalesced loads); blocks crossing tiles get their sums from segmented scans of the
+// tiles' head and tail sums.
+constexpr int kVjpThreads = 256;
+constexpr int kVjpPer2 = kVjpTile / kVjpThreads;
+
 struct VjpTile {
   double hg, hw;  // sums before the tile's first block start (whole tile if none)
-  double tg, tw;  // sums from the tile's last block start to its end
+  double tg, tw;  // sums from the tile's last block start to its end (whole tile if none)
   int has;        // the tile holds a block start
   int pad;
 };
 
+struct Seg {
+  int h;
+  double g, w;
+};
+
+// left-to-right: a then b (a block start in b drops what a carried)
+__device__ __forceinline__ Seg seg_lr(const Seg& a, const Seg& b) {
+  return Seg{a.h | b.h, b.h ? b.g : a.g + b.g, b.h ? b.w : a.w + b.w};
+}
+// right-to-left: a (left) holds the fold of b (right) unless a holds a block start
+__device__ __forceinline__ Seg seg_rl(const Seg& a, const Seg& b) {
+  return Seg{a.h | b.h, a.h ? a.g : a.g + b.g, a.h ? a.w : a.w + b.w};
+}
+
+__device__ __forceinline__ Seg shfl_up_seg(const Seg& v, int d) {
+  return Seg{__shfl_up(v.h, d, kWave), __shfl_up(v.g, d, kWave), __shfl_up(v.w, d, kWave)};
+}
+__device__ __forceinline__ Seg shfl_down_seg(const Seg& v, int d) {
+  return Seg{__shfl_down(v.h, d, kWave), __shfl_down(v.g, d, kWave), __shfl_down(v.w, d, kWave)};
+}
+
+// Exclusive workgroup scans of one Seg per thread, in thread order: fw = fold of the threads
+// before (left to right, seeded with fseed), bw = fold of the threads after (right to left,
+// seeded with bseed).  sh: LDS of 2 * kVjpThreads / kWave Segs.
+__device__ void vjp_wg_scans(Seg f, Seg r, const Seg& fseed, const Seg& bseed, Seg* sh, Seg& fw,
+                             Seg& bw) {
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
+  constexpr int NW = kVjpThreads / kWave;
+  Seg fi = f, ri = r;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const Seg o = shfl_up_seg(fi, d);
+    if (lane >= d) fi = seg_lr(o, fi);
+    const Seg p = shfl_down_seg(ri, d);
+    if (lane + d < kWave) ri = seg_rl(ri, p);
+  }
+  if (lane == kWave - 1) sh[wv] = fi;
+  if (lane == 0) sh[NW + wv] = ri;
+  __syncthreads();
+  Seg fp = fseed;
+  for (int k = 0; k < wv; ++k) fp = seg_lr(fp, sh[k]);
+  Seg bp = bseed;
+  for (int k = NW - 1; k > wv; --k) bp = seg_rl(sh[NW + k], bp);
+  Seg fx = shfl_up_seg(fi, 1), rx = shfl_down_seg(ri, 1);
+  fw = lane == 0 ? fp : seg_lr(fp, fx);
+  bw = lane == kWave - 1 ? bp : seg_rl(rx, bp);
+  __syncthreads();
+}
+
 template <typename T>
-__device__ __forceinline__ void vjp_lane_sums(const T* g, const T* w, const uint8_t* bs, int64_t off,
-                                              int i0, int c, int& has, double& hg, double& hw,
-                                              double& tg, double& tw) {
-  has = 0;
-  hg = hw = tg = tw = 0.0;
-  for (int t = 0; t < c; ++t) {
-    const int64_t e = off + i0 + t;
-    const double gv = (double)g[e];
-    const double wv = w ? (double)w[e] : 1.0;
-    if (bs[e]) {
-      has = 1;
-      tg = 0.0;
-      tw = 0.0;
-    }
-    if (!has) {
-      hg += gv;
-      hw += wv;
-    } else {
-      tg += gv;
-      tw += wv;
-    }
+__device__ __forceinline__ void vjp_load(const T* __restrict__ p, int64_t e0, int c, T (&v)[kVjpPer2],
+                                         T fill) {
+  constexpr int VN = Vec16<T>::N;
+  if (c == kVjpPer2 && ((uintptr_t)(p + e0)) % 16 == 0) {
+#pragma unroll
+    for (int k = 0; k < kVjpPer2 / VN; ++k) load16(p + e0 + k * VN, &v[k * VN]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kVjpPer2; ++k) v[k] = k < c ? p[e0 + k] : fill;
   }
 }
 
-// Segmented combine for the running sum of the open block, left to right:
-// (has_l, s_l) then (has_r, s_r) -> (has_l | has_r, has_r ? s_r : s_l + s_r).
+// Pass 1: each tile's head and tail sums.
 template <typename T>
-__global__ __launch_bounds__(64) void k_vjp_tiles(const T* __restrict__ g, const T* __restrict__ w,
-                                                  const uint8_t* __restrict__ bs, int64_t n,
-                                                  int ntile, VjpTile* __restrict__ tiles) {
+__global__ __launch_bounds__(kVjpThreads) void k_vjp_tiles(const T* __restrict__ g, const T* __restrict__ w,
+                                                           const uint8_t* __restrict__ bs, int64_t n,
+                                                           int ntile, VjpTile* __restrict__ tiles) {
+  __shared__ Seg sh[2 * kVjpThreads / kWave];
   const int64_t tid = blockIdx.x;
   const int64_t row = tid / ntile;
   const int tt = (int)(tid - row * ntile);
   const int64_t off = row * n + (int64_t)tt * kVjpTile;
   const int64_t rem = n - (int64_t)tt * kVjpTile;
   const int len = rem < kVjpTile ? (int)rem : kVjpTile;
-  const int lane = threadIdx.x;
-  const int i0 = kLanePts * lane;
-  int c = len - i0;
-  c = c < 0 ? 0 : (c > kLanePts ? kLanePts : c);
-  int has;
-  double hg, hw, tg, tw;
-  vjp_lane_sums(g, w, bs, off, i0, c, has, hg, hw, tg, tw);
-  // tile tail: combine lane tails left to right with the segmented rule
-  int h = has;
-  double sg = has ? tg : hg, sw = has ? tw : hw;  // lane's contribution to the open block at its end
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int oh = __shfl_up(h, d, kWave);
-    const double og = __shfl_up(sg, d, kWave);
-    const double ow = __shfl_up(sw, d, kWave);
-    if (lane >= d) {
-      if (!h) {
-        sg = og + sg;
-        sw = ow + sw;
+  const int i0 = kVjpPer2 * threadIdx.x;
+  const int c = min(max(len - i0, 0), kVjpPer2);
+  T gv[kVjpPer2], wv[kVjpPer2];
+  vjp_load(g, off + i0, c, gv, (T)0);
+  if (w) vjp_load(w, off + i0, c, wv, (T)0);
+  // tail: left-to-right fold restarting at starts; head: sums before the first start
+  Seg tl{0, 0.0, 0.0}, hd{0, 0.0, 0.0};
+#pragma unroll
+  for (int k = 0; k < kVjpPer2; ++k) {
+    if (k < c) {
+      const int b = bs[off + i0 + k] ? 1 : 0;
+      const double gd = (double)gv[k], wd = w ? (double)wv[k] : 1.0;
+      tl = seg_lr(tl, Seg{b, gd, wd});
+      if (!hd.h && b) hd.h = 1;
+      if (!hd.h) {
+        hd.g += gd;
+        hd.w += wd;
       }
-      h = h | oh;
     }
   }
-  // tile head: lane heads summed up to and including the first lane holding a start
-  int seen = has;
-  double pg = hg, pw = hw;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int os = __shfl_up(seen, d, kWave);
-    const double og = __shfl_up(pg, d, kWave);
-    const double ow = __shfl_up(pw, d, kWave);
-    if (lane >= d) {
-      if (!os) {
-        pg = og + pg;
-        pw = ow + pw;
-      } else {
-        pg = og;
-        pw = ow;
-      }
-      seen = seen | os;
-    }
+  // The head fold is the right-to-left rule on (starts, sums before the first start): a thread
+  // holding a start keeps only what precedes it.
+  Seg fw, bw;
+  vjp_wg_scans(tl, hd, Seg{0, 0.0, 0.0}, Seg{0, 0.0, 0.0}, sh, fw, bw);
+  if (threadIdx.x == kVjpThreads - 1) {
+    const Seg tot = seg_lr(fw, tl);
+    tiles[tid].tg = tot.g;
+    tiles[tid].tw = tot.w;
+    tiles[tid].has = tot.h;
+    tiles[tid].pad = 0;
   }
-  if (lane == kWave - 1) {
-    VjpTile v;
-    v.hg = pg;
-    v.hw = pw;
-    v.tg = sg;
-    v.tw = sw;
-    v.has = h;
-    v.pad = 0;
-    tiles[tid] = v;
+  if (threadIdx.x == 0) {
+    const Seg tot = seg_rl(hd, bw);
+    tiles[tid].hg = tot.g;
+    tiles[tid].hw = tot.w;
   }
 }
 
-// Per row, serially over tiles: carry[t] = sums of the block open at tile t's start from
-// earlier tiles; cont[t] = sums of that block from tile t on.
-__global__ __launch_bounds__(64) void k_vjp_rows(const VjpTile* __restrict__ tiles, int64_t batch,
-                                                 int ntile, double4* __restrict__ cc) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= batch) return;
+// Carries across tiles, per row: carry[t] = sums of the block open at tile t's start from earlier
+// tiles (an exclusive left-to-right segmented scan of the tiles' tail sums) and cont[t] = sums of
+// that block from tile t on (an inclusive right-to-left segmented scan of the tiles' head sums).
+// The segmented rule, for a fold in either direction: (has, s) then (has', s') ->
+// (has | has', has' ? s' : s + s') reading left to right, (has | has', has ? s : s + s') reading
+// right to left.  Two passes over blocks of kVjpBlock tiles: each block's two folds, then each
+// block combines the folds of the blocks before and after it and scans its own tiles.
+constexpr int kVjpScanThreads = 256;
+constexpr int kVjpPer = 4;
+constexpr int kVjpBlock = kVjpScanThreads * kVjpPer;
+
+// Inclusive block scan of Seg values: left to right (dir 1) or right to left (dir -1).
+__device__ Seg vjp_block_scan(Seg v, int dir, int* sh_h, double* sh_g, double* sh_w) {
+  const int t = threadIdx.x;
+  for (int d = 1; d < kVjpScanThreads; d <<= 1) {
+    sh_h[t] = v.h;
+    sh_g[t] = v.g;
+    sh_w[t] = v.w;
+    __syncthreads();
+    const int o = dir > 0 ? t - d : t + d;
+    if (o >= 0 && o < kVjpScanThreads) {
+      const Seg u{sh_h[o], sh_g[o], sh_w[o]};
+      v = dir > 0 ? seg_lr(u, v) : seg_rl(v, u);
+    }
+    __syncthreads();
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kVjpScanThreads) void k_vjp_scan_reduce(const VjpTile* __restrict__ tiles,
+                                                                    int ntile, int nblk,
+                                                                    double4* __restrict__ bfw,
+                                                                    double4* __restrict__ bbw) {
+  __shared__ int sh_h[kVjpScanThreads];
+  __shared__ double sh_g[kVjpScanThreads], sh_w[kVjpScanThreads];
+  const int64_t row = blockIdx.x / nblk;  // one-dimensional grid: batch * nblk blocks
+  const int b = (int)(blockIdx.x - row * nblk);
+  const int t = threadIdx.x;
   const VjpTile* tr = tiles + row * ntile;
-  double4* cr = cc + row * ntile;
-  double cg = 0.0, cw = 0.0;
-  for (int t = 0; t < ntile; ++t) {
-    cr[t].x = cg;
-    cr[t].y = cw;
-    const VjpTile v = tr[t];
-    if (v.has) {
-      cg = v.tg;
-      cw = v.tw;
-    } else {
-      cg += v.tg;
-      cw += v.tw;
+  Seg f{0, 0.0, 0.0}, r{0, 0.0, 0.0};
+  for (int k = 0; k < kVjpPer; ++k) {
+    const int tt = b * kVjpBlock + kVjpPer * t + k;
+    if (tt < ntile) {
+      const VjpTile v = tr[tt];
+      f = seg_lr(f, Seg{v.has, v.tg, v.tw});
     }
   }
-  double ng = 0.0, nw = 0.0;
-  for (int t = ntile - 1; t >= 0; --t) {
-    const VjpTile v = tr[t];
-    if (v.has) {
-      ng = v.hg;
-      nw = v.hw;
-    } else {
-      ng = v.hg + ng;
-      nw = v.hw + nw;
+  for (int k = kVjpPer - 1; k >= 0; --k) {
+    const int tt = b * kVjpBlock + kVjpPer * t + k;
+    if (tt < ntile) {
+      const VjpTile v = tr[tt];
+      r = seg_rl(Seg{v.has, v.hg, v.hw}, r);
     }
-    cr[t].z = ng;
-    cr[t].w = nw;
+  }
+  f = vjp_block_scan(f, 1, sh_h, sh_g, sh_w);
+  r = vjp_block_scan(r, -1, sh_h, sh_g, sh_w);
+  if (t == kVjpScanThreads - 1) bfw[row * nblk + b] = make_double4(f.g, f.w, (double)f.h, 0.0);
+  if (t == 0) bbw[row * nblk + b] = make_double4(r.g, r.w, (double)r.h, 0.0);
+}
+
+__global__ __launch_bounds__(kVjpScanThreads) void k_vjp_scan_apply(const VjpTile* __restrict__ tiles,
+                                                                   int ntile, int nblk,
+                                                                   const double4* __restrict__ bfw,
+                                                                   const double4* __restrict__ bbw,
+                                                                   double4* __restrict__ cc) {
+  __shared__ int sh_h[kVjpScanThreads];
+  __shared__ double sh_g[kVjpScanThreads], sh_w[kVjpScanThreads];
+  __shared__ double soff[4];
+  __shared__ int shas[2];
+  const int64_t row = blockIdx.x / nblk;  // one-dimensional grid: batch * nblk blocks
+  const int b = (int)(blockIdx.x - row * nblk);
+  const int t = threadIdx.x;
+  const VjpTile* tr = tiles + row * ntile;
+  if (t == 0) {
+    Seg pf{0, 0.0, 0.0};
+    for (int k = 0; k < b; ++k) {
+      const double4 v = bfw[row * nblk + k];
+      pf = seg_lr(pf, Seg{(int)v.z, v.x, v.y});
+    }
+    Seg pb{0, 0.0, 0.0};
+    for (int k = nblk - 1; k > b; --k) {
+      const double4 v = bbw[row * nblk + k];
+      pb = seg_rl(Seg{(int)v.z, v.x, v.y}, pb);
+    }
+    soff[0] = pf.g;
+    soff[1] = pf.w;
+    soff[2] = pb.g;
+    soff[3] = pb.w;
+    shas[0] = pf.h;
+    shas[1] = pb.h;
+  }
+  // this thread's tiles, its left-to-right fold and its right-to-left fold
+  Seg tv[kVjpPer], hv[kVjpPer];
+  Seg f{0, 0.0, 0.0}, r{0, 0.0, 0.0};
+  for (int k = 0; k < kVjpPer; ++k) {
+    const int tt = b * kVjpBlock + kVjpPer * t + k;
+    tv[k] = Seg{0, 0.0, 0.0};
+    hv[k] = Seg{0, 0.0, 0.0};
+    if (tt < ntile) {
+      const VjpTile v = tr[tt];
+      tv[k] = Seg{v.has, v.tg, v.tw};
+      hv[k] = Seg{v.has, v.hg, v.hw};
+    }
+    f = seg_lr(f, tv[k]);
+  }
+  for (int k = kVjpPer - 1; k >= 0; --k) r = seg_rl(hv[k], r);
+  const Seg fi = vjp_block_scan(f, 1, sh_h, sh_g, sh_w);
+  const Seg ri = vjp_block_scan(r, -1, sh_h, sh_g, sh_w);
+  // exclusive: the neighbouring thread's inclusive value
+  sh_h[t] = fi.h;
+  sh_g[t] = fi.g;
+  sh_w[t] = fi.w;
+  __syncthreads();
+  Seg fe = Seg{shas[0], soff[0], soff[1]};
+  if (t > 0) fe = seg_lr(fe, Seg{sh_h[t - 1], sh_g[t - 1], sh_w[t - 1]});
+  __syncthreads();
+  sh_h[t] = ri.h;
+  sh_g[t] = ri.g;
+  sh_w[t] = ri.w;
+  __syncthreads();
+  Seg re = Seg{shas[1], soff[2], soff[3]};
+  if (t + 1 < kVjpScanThreads) re = seg_rl(Seg{sh_h[t + 1], sh_g[t + 1], sh_w[t + 1]}, re);
+  // per tile: carry (exclusive, from the left) and cont (inclusive, from the right)
+  Seg run = fe;
+  double4 out[kVjpPer];
+  for (int k = 0; k < kVjpPer; ++k) {
+    out[k].x = run.g;
+    out[k].y = run.w;
+    run = seg_lr(run, tv[k]);
+  }
+  Seg back = re;
+  for (int k = kVjpPer - 1; k >= 0; --k) {
+    back = seg_rl(hv[k], back);
+    out[k].z = back.g;
+    out[k].w = back.w;
+  }
+  for (int k = 0; k < kVjpPer; ++k) {
+    const int tt = b * kVjpBlock + kVjpPer * t + k;
+    if (tt < ntile) cc[row * ntile + tt] = out[k];
   }
 }
 
+// Pass 3: each element's block sums from the two scans, seeded with its tile's carries.
 template <typename T>
-__global__ __launch_bounds__(64) void k_vjp_apply(const T* __restrict__ g, const T* __restrict__ y,
-                                                  const T* __restrict__ w, const T* __restrict__ z,
-                                                  const uint8_t* __restrict__ bs,
-                                                  const double4* __restrict__ cc, T* __restrict__ gy,
-                                                  T* __restrict__ gw, int64_t n, int ntile) {
+__global__ __launch_bounds__(kVjpThreads) void k_vjp_apply(const T* __restrict__ g, const T* __restrict__ y,
+                                                           const T* __restrict__ w, const T* __restrict__ z,
+                                                           const uint8_t* __restrict__ bs,
+                                                           const double4* __restrict__ cc, T* __restrict__ gy,
+                                                           T* __restrict__ gw, int64_t n, int ntile) {
+  __shared__ Seg sh[2 * kVjpThreads / kWave];
   const int64_t tid = blockIdx.x;
   const int64_t row = tid / ntile;
   const int tt = (int)(tid - row * ntile);
   const int64_t off = row * n + (int64_t)tt * kVjpTile;
   const int64_t rem = n - (int64_t)tt * kVjpTile;
   const int len = rem < kVjpTile ? (int)rem : kVjpTile;
-  const int lane = threadIdx.x;
-  const int i0 = kLanePts * lane;
-  int c = len - i0;
-  c = c < 0 ? 0 : (c > kLanePts ? kLanePts : c);
-  int has;
-  double hg, hw, tg, tw;
-  vjp_lane_sums(g, w, bs, off, i0, c, has, hg, hw, tg, tw);
+  const int i0 = kVjpPer2 * threadIdx.x;
+  const int c = min(max(len - i0, 0), kVjpPer2);
+  T gv[kVjpPer2], wv[kVjpPer2], yv[kVjpPer2], zv[kVjpPer2];
+  vjp_load(g, off + i0, c, gv, (T)0);
+  if (w) vjp_load(w, off + i0, c, wv, (T)0);
+  vjp_load(y, off + i0, c, yv, (T)0);
+  vjp_load(z, off + i0, c, zv, (T)0);
+  int st[kVjpPer2 + 1];  // starts of this thread's elements and of the one after them
+#pragma unroll
+  for (int k = 0; k <= kVjpPer2; ++k) st[k] = (k < c || (k == c && i0 + k < len)) ? (bs[off + i0 + k] ? 1 : 0) : 0;
+  // forward fold (restart at starts) and backward fold (restart after block ends: the flag of
+  // element k is the start of element k + 1)
+  Seg f{0, 0.0, 0.0}, r{0, 0.0, 0.0};
+#pragma unroll
+  for (int k = 0; k < kVjpPer2; ++k) {
+    if (k < c) f = seg_lr(f, Seg{st[k], (double)gv[k], w ? (double)wv[k] : 1.0});
+  }
+#pragma unroll
+  for (int k = kVjpPer2 - 1; k >= 0; --k) {
+    if (k < c) r = seg_rl(Seg{st[k + 1], (double)gv[k], w ? (double)wv[k] : 1.0}, r);
+  }
   const double4 me = cc[tid];
-  const bool last_tile = tt == ntile - 1;
-  const double4 nx = last_tile ? make_double4(0.0, 0.0, 0.0, 0.0) : cc[tid + 1];
-  // Forward: the open block's sums entering this lane (exclusive segmented scan of lane tails,
-  // seeded with the tile's carry).
-  int h = has;
-  double sg = has ? tg : hg, sw = has ? tw : hw;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int oh = __shfl_up(h, d, kWave);
-    const double og = __shfl_up(sg, d, kWave);
-    const double ow = __shfl_up(sw, d, kWave);
-    if (lane >= d) {
-      if (!h) {
-        sg = og + sg;
-        sw = ow + sw;
-      }
-      h = h | oh;
-    }
-  }
-  int eh = __shfl_up(h, 1, kWave);
-  double eg = __shfl_up(sg, 1, kWave), ew = __shfl_up(sw, 1, kWave);
-  if (lane == 0) {
-    eh = 0;
-    eg = 0.0;
-    ew = 0.0;
-  }
-  const double in_g = eh ? eg : me.x + eg;
-  const double in_w = eh ? ew : me.y + ew;
-  // Backward: the open block's sums after this lane (segmented scan of lane heads from the
-  // right, seeded with the next tile's continuation).
-  int bh = has;
-  double bg = hg, bw = hw;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int oh = __shfl_down(bh, d, kWave);
-    const double og = __shfl_down(bg, d, kWave);
-    const double ow = __shfl_down(bw, d, kWave);
-    if (lane + d < kWave) {
-      if (!bh) {
-        bg = bg + og;
-        bw = bw + ow;
-      }
-      bh = bh | oh;
-    }
-  }
-  int ah = __shfl_down(bh, 1, kWave);
-  double ag = __shfl_down(bg, 1, kWave), aw = __shfl_down(bw, 1, kWave);
-  if (lane == kWave - 1) {
-    ah = 0;
-    ag = 0.0;
-    aw = 0.0;
-  }
-  const double out_g = ah ? ag : ag + nx.z;
-  const double out_w = ah ? aw : aw + nx.w;
-  // Lanes with no elements (beyond the row's end) contribute zeros to the scans above.
+  const double4 nx = tt == ntile - 1 ? make_double4(0.0, 0.0, 0.0, 0.0) : cc[tid + 1];
+  Seg fw, bw;
+  vjp_wg_scans(f, r, Seg{0, me.x, me.y}, Seg{0, nx.z, nx.w}, sh, fw, bw);
   if (c == 0) return;
-  // Walk the lane's elements block by block.
-  int t = 0;
-  while (t < c) {
-    int u = t + 1;
-    while (u < c && !bs[off + i0 + u]) ++u;
-    const bool starts_here = bs[off + i0 + t] != 0;
-    double G = 0.0, Wt = 0.0;
-    for (int v = t; v < u; ++v) {
-      G += (double)g[off + i0 + v];
-      Wt += w ? (double)w[off + i0 + v] : 1.0;
+  double Fg[kVjpPer2], Fw[kVjpPer2];
+  Seg run = fw;
+#pragma unroll
+  for (int k = 0; k < kVjpPer2; ++k) {
+    if (k < c) {
+      run = seg_lr(run, Seg{st[k], (double)gv[k], w ? (double)wv[k] : 1.0});
+      Fg[k] = run.g;
+      Fw[k] = run.w;
     }
-    if (!starts_here) {
-      G += in_g;
-      Wt += in_w;
+  }
+  T oy[kVjpPer2], ow[kVjpPer2];
+  Seg back = bw;
+#pragma unroll
+  for (int k = kVjpPer2 - 1; k >= 0; --k) {
+    oy[k] = (T)0;
+    ow[k] = (T)0;
+    if (k < c) {
+      const double gd = (double)gv[k], wd = w ? (double)wv[k] : 1.0;
+      back = seg_rl(Seg{st[k + 1], gd, wd}, back);
+      const double G = Fg[k] + back.g - gd;
+      const double Wt = Fw[k] + back.w - wd;
+      const double q = G / Wt;
+      oy[k] = (T)(wd * q);
+      ow[k] = (T)(((double)yv[k] - (double)zv[k]) * q);
     }
-    if (u == c) {
-      G += out_g;
-      Wt += out_w;
+  }
+  constexpr int VN = Vec16<T>::N;
+  const bool vec = c == kVjpPer2 && ((uintptr_t)(gy + off + i0)) % 16 == 0 &&
+                   (!gw || ((uintptr_t)(gw + off + i0)) % 16 == 0);
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kVjpPer2 / VN; ++k) {
+      store16(gy + off + i0 + k * VN, &oy[k * VN]);
+      if (gw) store16(gw + off + i0 + k * VN, &ow[k * VN]);
     }
-    const double q = G / Wt;
-    for (int v = t; v < u; ++v) {
-      const int64_t e = off + i0 + v;
-      const double wv = w ? (double)w[e] : 1.0;
-      gy[e] = (T)(wv * q);
-      if (gw) gw[e] = (T)(((double)y[e] - (double)z[e]) * q);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kVjpPer2; ++k) {
+      if (k < c) {
+        gy[off + i0 + k] = oy[k];
+        if (gw) gw[off + i0 + k] = ow[k];
+      }
     }
-    t = u;
   }
 }
 
