@@ -51,7 +51,7 @@ struct ChunkOut {
   double* lsy;
   double* ckx;        // [G * kWave * kLaneW] lane-relative running sums at points 32 j
   double* cky;
-  uint8_t* ztile;     // [G * kZTiles] 1 where the chunk pass wrote z = y for the load tile
+  uint8_t* ztile;     // [G * kZTiles] 1 where the lane chains wrote z = y for the load tile
   uint8_t* dform;     // [G] 0 list form, 1 dense form, 2 dense form with every point a vertex
                       //     and z = y written for the whole chunk
   double4* bnd;       // [G] dense form: coordinates of hull vertices 1 and V - 2
@@ -242,14 +242,16 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
 // Chunks whose elements are all clean and strictly increasing.  Every turn of such a chunk's
 // diagram compares two consecutive y values, so every point P_0 .. P_len is a strict vertex of the
 // chunk hull: the hull is the whole diagram and every element is its own block.  A workgroup of
-// kIncWaves wavefronts streams the chunk's len elements with coalesced 16-byte loads (wavefront
-// q takes the q-th of kIncWaves equal parts), checks the pattern, writes z = y and stores the
-// dense form directly: vertex bits of points 0..len set, lane starts, checkpoints (here block
-// sums accumulated in a fixed order; every later coordinate of the chunk is computed from these
-// stored values), and the cache of vertices 1 and V - 2 computed exactly as the stored-form
-// readers recompute points.  It returns false, having written only z, when an element breaks the pattern; the lane chains
-// then process the chunk and rewrite everything.  Requires len >= 2 * kCk and 16-byte aligned y,
-// w, z.  bsx, bsy: 512 doubles each of LDS (block sums); bad: an int of LDS.
+// kIncWaves wavefronts streams the chunk's len elements with coalesced nontemporal 16-byte loads
+// and stores (wavefront q takes the q-th of kIncWaves equal parts), checks the pattern, writes
+// z = y and stores the dense form directly: vertex bits of points 0..len set, lane starts,
+// checkpoints (here block sums accumulated in a fixed order; every later coordinate of the chunk
+// is computed from these stored values), and the cache of vertices 1 and V - 2 computed exactly
+// as the stored-form readers recompute points.  It keeps no z tile marks: form 2 itself tells the
+// fit that z = y holds for every element.  It returns false, having written only z, when an
+// element breaks the pattern; the lane chains then process the chunk and rewrite everything.
+// Requires len >= 2 * kCk and 16-byte aligned y, w, z.  bsx, bsy: 512 doubles each of LDS
+// (block sums); bad: an int of LDS.
 constexpr int kIncWaves = 4;
 
 template <typename T, bool W>
@@ -291,8 +293,8 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     for (int u = 0; u < U; ++u) {
       const int e = s0 + (u * kWave + lane) * VN;
       if (e + VN <= q1) {
-        load16(yc + e, &yv[u * VN]);
-        if (W) load16(wc + e, &wv_[u * VN]);
+        load16_nt(yc + e, &yv[u * VN]);
+        if (W) load16_nt(wc + e, &wv_[u * VN]);
       } else {
 #pragma unroll
         for (int k = 0; k < VN; ++k) {
@@ -331,7 +333,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
         bsy[e / kCk] = sy;
       }
       if (e + VN <= q1) {
-        store16(zc + e, &yv[u * VN]);
+        store16_nt(zc + e, &yv[u * VN]);
       } else {
 #pragma unroll
         for (int k = 0; k < VN; ++k)
@@ -396,8 +398,6 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     out.mask[mb + kLaneW * lane + wd] = bits;
     out.mcnt[mb + kLaneW * lane + wd] = (uint16_t)min(w0, len + 1);
   }
-  constexpr int TN = Tile<T, W>::N;
-  for (int t = lane; t < kChunk / TN; t += kWave) out.ztile[g * (int64_t)kZTiles + t] = (t + 1) * TN <= len ? 1 : 0;
   if (lane == 0) {
     // vertex 1 = point 1: lane 0's checkpoint 0 (zero) plus element 0
     const double w0 = W ? (double)wc[0] : 1.0;
