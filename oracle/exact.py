@@ -13,6 +13,10 @@ at most a few hundred elements.
   P_0 = (0, 0), P_{k+1} = P_k + (w_k, w_k y_k); the fit of element k is the slope of the hull
   edge over [X_k, X_{k+1}]; collinear middle points are not vertices, and element k starts a
   block exactly when P_k is a vertex.
+* ``minmax`` and ``upper_hull``: the same two characterisations for the decreasing fit
+  (z_0 >= ... >= z_{n-1}, the direction of the page's benchmarks, Section 7.2): the min-max
+  formula z_i = min_{j<=i} max_{k>=i} Av(j..k) (the theorem above with the order reversed),
+  and the least concave majorant of the same diagram.
 * ``kkt_residual``: the optimality certificate of the page's Section 7.6 (fourth accuracy
   measure), computed from an output alone.
 * ``measures``: the page's other Section 7.6 measures (step down, deviation from a reference,
@@ -74,6 +78,28 @@ def maxmin(y, w=None):
     return z
 
 
+def minmax(y, w=None):
+    """Exact decreasing fit by the min-max block-average formula.  Returns a list of Fractions."""
+    y, w = _fr_row(y, w)
+    n = len(y)
+    W = [Fraction(0)]
+    S = [Fraction(0)]
+    for yi, wi in zip(y, w):
+        W.append(W[-1] + wi)
+        S.append(S[-1] + wi * yi)
+    # sufmax[j][k] = max over k' >= k of Av(j..k')
+    sufmax = []
+    for j in range(n):
+        row = [None] * n
+        best = None
+        for k in range(n - 1, j - 1, -1):
+            av = (S[k + 1] - S[j]) / (W[k + 1] - W[j])
+            best = av if best is None or av > best else best
+            row[k] = best
+        sufmax.append(row)
+    return [min(sufmax[j][i] for j in range(i + 1)) for i in range(n)]
+
+
 def _cross(o, a, b):
     return (a[0] - o[0]) * (b[1] - o[1]) - (a[1] - o[1]) * (b[0] - o[0])
 
@@ -102,17 +128,42 @@ def lower_hull(y, w=None):
     return hull, z, starts
 
 
+def upper_hull(y, w=None):
+    """Canonical upper hull (least concave majorant) of the CSD, popping on cross >= 0.
+
+    Returns (vertices, z, block_start) as ``lower_hull`` does, for the decreasing fit.
+    """
+    pts = csd(y, w)
+    hull = []
+    for k, p in enumerate(pts):
+        while len(hull) >= 2 and _cross(pts[hull[-2]], pts[hull[-1]], p) >= 0:
+            hull.pop()
+        hull.append(k)
+    n = len(pts) - 1
+    z = [None] * n
+    starts = [0] * n
+    for a, b in zip(hull[:-1], hull[1:]):
+        slope = (pts[b][1] - pts[a][1]) / (pts[b][0] - pts[a][0])
+        for i in range(a, b):
+            z[i] = slope
+        if a < n:
+            starts[a] = 1
+    return hull, z, starts
+
+
 def blocks_from_exact(z):
     """Block starts of an exact fit: maximal runs of equal values."""
     return [1 if i == 0 or z[i] != z[i - 1] else 0 for i in range(len(z))]
 
 
-def kkt_residual(y, w, z):
+def kkt_residual(y, w, z, decreasing=False):
     """Largest KKT violation of an output z, relative to 2 * sum w |y| (0 for an empty row).
 
     lambda_i = -2 sum_{j<=i} w_j (z_j - y_j) must be >= 0, zero at the last element and zero
     wherever z steps up (z_{i+1} > z_i).  Feasibility (z non-decreasing) plus these
-    conditions prove optimality of the convex problem.  Sums use 80-bit extended precision.
+    conditions prove optimality of the convex problem.  For the decreasing fit the sign of
+    lambda flips and the steps that free it are steps down.  Sums use 80-bit extended
+    precision.
     """
     y = np.asarray(y, dtype=np.float64).ravel()
     z = np.asarray(z, dtype=np.float64).ravel()
@@ -123,12 +174,14 @@ def kkt_residual(y, w, z):
     ld = np.longdouble
     terms = w.astype(ld) * (z.astype(ld) - y.astype(ld))
     lam = -2 * np.cumsum(terms)
+    if decreasing:
+        lam = -lam
     scale = 2 * np.sum(w.astype(ld) * np.abs(y.astype(ld)))
     if scale == 0:
         scale = ld(1)
     viol = np.maximum(-lam, 0)
     res = max(float(viol.max()), float(abs(lam[-1])))
-    up = z[1:] > z[:-1]
+    up = (z[1:] < z[:-1]) if decreasing else (z[1:] > z[:-1])
     if np.any(up):
         res = max(res, float(np.abs(lam[:-1][up]).max()))
     return float(res / scale)

@@ -14,9 +14,15 @@
  * once, keep a stack of blocks, and merge the top two blocks while their means
  * violate the order.
  *
+ * Direction.  The page's benchmarks fit the decreasing direction (Section 7.2,
+ * Table 1; the soft rank of Section 7.9 too): z_0 >= ... >= z_{n-1}.  Pool
+ * adjacent violators fits it directly with the order reversed: two neighbouring
+ * blocks violate it when the lower one's mean is <= the top one's.
+ *
  * Canonical partition (Section 2.1 of the page: a point on the segment between
  * its neighbours is not a vertex): two neighbouring blocks with EQUAL means are
- * pooled, so adjacent blocks of the result have strictly increasing means.  An
+ * pooled, so adjacent blocks of the result have strictly increasing (decreasing
+ * fit: strictly decreasing) means.  An
  * element starts a block exactly when its left point of the cumulative sum
  * diagram is a vertex of the canonical lower hull; element 0 always does.
  *
@@ -38,10 +44,11 @@
 #define ORACLE_FLAG_NONFINITE 1u
 #define ORACLE_FLAG_WEIGHT 2u
 
-/* One row.  Scratch arrays hold up to n blocks. */
+/* One row.  Scratch arrays hold up to n blocks.  decreasing != 0 fits the
+ * decreasing direction. */
 static uint32_t pav_row(const double *y, const double *w, int64_t n, double *z,
                         uint8_t *block_start, int64_t *bstart, double *bw,
-                        double *bs) {
+                        double *bs, int decreasing) {
   uint32_t flag = 0;
   for (int64_t i = 0; i < n; ++i) {
     double wi = w ? w[i] : 1.0;
@@ -62,8 +69,10 @@ static uint32_t pav_row(const double *y, const double *w, int64_t n, double *z,
     bstart[top] = k;
     bw[top] = wk;
     bs[top] = wk * y[k];
-    /* Pool while the block below has a mean >= the top block's mean. */
-    while (top >= 1 && bs[top - 1] * bw[top] >= bs[top] * bw[top - 1]) {
+    /* Pool while the block below has a mean >= the top block's mean (decreasing
+     * fit: <=). */
+    while (top >= 1 && (decreasing ? bs[top - 1] * bw[top] <= bs[top] * bw[top - 1]
+                                   : bs[top - 1] * bw[top] >= bs[top] * bw[top - 1])) {
       bw[top - 1] += bw[top];
       bs[top - 1] += bs[top];
       --top;
@@ -81,17 +90,18 @@ static uint32_t pav_row(const double *y, const double *w, int64_t n, double *z,
 }
 
 /*
- * iso_oracle_fit: rows of common length n, row-major [batch, n], fp64.
+ * iso_oracle_fit_dir: rows of common length n, row-major [batch, n], fp64.
  *   y          input values (required)
  *   w          weights, or NULL for unit weights
  *   z          output fit (required, may not alias y or w)
  *   block_start  output, 1 byte per element, or NULL
  *   row_flags  output, one uint32 per row, or NULL
+ *   decreasing 0: non-decreasing fit; otherwise non-increasing
  * Returns 0 on success, -1 if scratch could not be allocated, -2 on bad sizes.
  */
-int iso_oracle_fit(const double *y, const double *w, double *z,
-                   uint8_t *block_start, uint32_t *row_flags, int64_t batch,
-                   int64_t n) {
+int iso_oracle_fit_dir(const double *y, const double *w, double *z,
+                       uint8_t *block_start, uint32_t *row_flags, int64_t batch,
+                       int64_t n, int decreasing) {
   if (batch < 0 || n < 0) return -2;
   if (batch == 0 || n == 0) return 0;
   int64_t *bstart = (int64_t *)malloc((size_t)n * sizeof(int64_t));
@@ -108,13 +118,20 @@ int iso_oracle_fit(const double *y, const double *w, double *z,
     const double *wr = w ? w + r * n : NULL;
     uint32_t f = pav_row(yr, wr, n, z + r * n,
                          block_start ? block_start + r * n : NULL, bstart, bw,
-                         bs);
+                         bs, decreasing);
     if (row_flags) row_flags[r] = f;
   }
   free(bstart);
   free(bw);
   free(bs);
   return 0;
+}
+
+/* iso_oracle_fit: the non-decreasing fit (iso_oracle_fit_dir with decreasing = 0). */
+int iso_oracle_fit(const double *y, const double *w, double *z,
+                   uint8_t *block_start, uint32_t *row_flags, int64_t batch,
+                   int64_t n) {
+  return iso_oracle_fit_dir(y, w, z, block_start, row_flags, batch, n, 0);
 }
 
 /*

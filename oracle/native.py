@@ -46,6 +46,8 @@ def _load():
             P = ctypes.c_void_p
             lib.iso_oracle_fit.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64]
             lib.iso_oracle_fit.restype = ctypes.c_int
+            lib.iso_oracle_fit_dir.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+            lib.iso_oracle_fit_dir.restype = ctypes.c_int
             lib.iso_oracle_vjp.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64]
             lib.iso_oracle_vjp.restype = ctypes.c_int
             _lib = lib
@@ -65,8 +67,9 @@ def _as2d(a):
     return a
 
 
-def pav(y, w=None, *, return_blocks: bool = False):
-    """Fit every row of ``y`` (1-D or [batch, n]) with weights ``w`` (same shape or None).
+def pav(y, w=None, *, return_blocks: bool = False, decreasing: bool = False):
+    """Fit every row of ``y`` (1-D or [batch, n]) with weights ``w`` (same shape or None);
+    ``decreasing=True`` fits z_0 >= ... >= z_{n-1} instead.
 
     Returns ``z`` (fp64, same shape as ``y``), and with ``return_blocks=True`` also the
     block-start mask (uint8, same shape) and the per-row flags (uint32, [batch]).
@@ -80,7 +83,8 @@ def pav(y, w=None, *, return_blocks: bool = False):
     z = np.empty_like(y2)
     bs = np.empty(y2.shape, dtype=np.uint8)
     flags = np.empty(batch, dtype=np.uint32)
-    rc = _load().iso_oracle_fit(_ptr(y2), _ptr(w2), _ptr(z), _ptr(bs), _ptr(flags), batch, n)
+    rc = _load().iso_oracle_fit_dir(_ptr(y2), _ptr(w2), _ptr(z), _ptr(bs), _ptr(flags), batch, n,
+                                    1 if decreasing else 0)
     if rc != 0:
         raise RuntimeError("iso_oracle_fit failed with code %d" % rc)
     if y_in.ndim == 1:

@@ -8,6 +8,9 @@ The oracle (oracle/iso_oracle.c, a pool-adjacent-violators scan) is checked agai
   * metamorphic relations (affine maps of y, scaled weights, row order, concatenation);
   * the KKT certificate and the block-mean / weighted-sum invariants;
   * scipy.optimize.isotonic_regression as an independent library routine.
+The decreasing direction is pinned the same way: the exact min-max formula and the exact upper
+hull on tiny rows, reversal of the row (exact on integer rows), closed forms, KKT with the
+flipped sign, and scipy with increasing=False.
 """
 import os
 from fractions import Fraction
@@ -244,3 +247,86 @@ def test_vjp_oracle_against_dense_jacobian_and_finite_differences():
             fd_w[j] = g @ (oracle.pav(y, w + e) - oracle.pav(y, w - e)) / (2 * h)
         assert np.allclose(gy, fd_y, atol=1e-6)
         assert np.allclose(gw, fd_w, atol=1e-6)
+
+
+# ------------------------------------------------------------------ decreasing direction
+
+def test_decreasing_matches_minmax_and_upper_hull_on_tiny_rows():
+    for y, w in _tiny_rows():
+        z, starts, _ = oracle.pav(y, w, return_blocks=True, decreasing=True)
+        zm = exact.minmax(y, w)
+        _, zh, sh = exact.upper_hull(y, w)
+        assert zm == zh, (y, w)
+        for a, b in zip(z, zm):
+            assert abs(a - float(b)) <= 1e-15 * (1 + abs(float(b))), (y, w)
+        assert list(starts) == exact.blocks_from_exact(zm) == sh, (y, w)
+
+
+def test_decreasing_is_the_reversed_increasing_fit():
+    """z non-increasing minimises sum w (z - y)^2 exactly when its reversal is the increasing fit
+    of the reversed row.  On integer rows both scans are exact, so the fits agree bit for bit and
+    the block partitions (read from the ends of blocks) agree."""
+    y, w = workloads.family("integer", 6, 300, seed=13, wkind="integer")
+    for r in range(6):
+        z, s, _ = oracle.pav(y[r], w[r], return_blocks=True, decreasing=True)
+        zr, sr, _ = oracle.pav(y[r][::-1].copy(), w[r][::-1].copy(), return_blocks=True)
+        assert np.array_equal(z, zr[::-1])
+        # a block of the reversed fit starting at reversed index i ends at n - 1 - i here
+        ends = np.zeros(300, dtype=np.uint8)
+        ends[np.nonzero(sr[::-1])[0]] = 1
+        starts_from_ends = np.zeros(300, dtype=np.uint8)
+        starts_from_ends[0] = 1
+        starts_from_ends[1:] = ends[:-1]
+        assert np.array_equal(s, starts_from_ends)
+
+
+def test_decreasing_closed_forms():
+    rng = np.random.default_rng(5)
+    # strictly decreasing y: every element its own block, z = y (exactly with unit weights; with
+    # weights z = (w y) / w, two roundings)
+    y = np.sort(rng.standard_normal(999))[::-1].copy()
+    z, s, _ = oracle.pav(y, None, return_blocks=True, decreasing=True)
+    assert np.array_equal(z, y) and s.all()
+    z, s, _ = oracle.pav(y, rng.uniform(0.5, 2.0, 999), return_blocks=True, decreasing=True)
+    assert np.allclose(z, y, rtol=2.3e-16, atol=0) and s.all()
+    # strictly increasing y: one block at the weighted mean
+    y = np.sort(rng.standard_normal(555))
+    w = rng.uniform(0.5, 2.0, 555)
+    z, s, _ = oracle.pav(y, w, return_blocks=True, decreasing=True)
+    mean = float(sum(Fraction(a) * Fraction(b) for a, b in zip(y, w)) / sum(Fraction(b) for b in w))
+    assert s.sum() == 1 and np.allclose(z, mean, rtol=1e-14, atol=1e-14)
+    # n = 2, y0 < y1: both at the weighted mean
+    assert np.all(oracle.pav(np.array([1.0, 4.0]), np.array([3.0, 1.0]), decreasing=True) == 1.75)
+    # constant: one block
+    z, s, _ = oracle.pav(np.full(100, -1.5), None, return_blocks=True, decreasing=True)
+    assert np.all(z == -1.5) and s.sum() == 1
+
+
+@pytest.mark.parametrize("fam", workloads.FAMILIES)
+def test_decreasing_invariants_and_kkt(fam):
+    y, w = workloads.family(fam, 2, 5000, seed=22, wkind="uniform")
+    z, s, flags = oracle.pav(y, w, return_blocks=True, decreasing=True)
+    assert np.all(flags == 0)
+    for r in range(2):
+        assert np.all(np.diff(z[r]) <= 0)
+        assert exact.kkt_residual(y[r], w[r], z[r], decreasing=True) < 1e-12
+        # block means: z is the weighted mean of y over each block
+        b = np.cumsum(s[r]) - 1
+        sw = np.bincount(b, weights=w[r])
+        sy = np.bincount(b, weights=w[r] * y[r])
+        assert np.max(np.abs(z[r] - (sy / sw)[b]) / (1 + np.abs(z[r]))) < 1e-13
+
+
+def test_decreasing_scipy_cross_check():
+    from scipy.optimize import isotonic_regression
+
+    for fam in ("noise", "sawtooth", "integer"):
+        wk = "integer" if fam == "integer" else "uniform"
+        y, w = workloads.family(fam, 1, 20000, seed=4, wkind=wk)
+        z, s, _ = oracle.pav(y[0], w[0], return_blocks=True, decreasing=True)
+        res = isotonic_regression(y[0], weights=w[0], increasing=False)
+        assert np.max(np.abs(z - res.x) / (1 + np.abs(res.x))) < 1e-12
+        if fam == "integer":
+            sp = np.zeros(20000, dtype=np.uint8)
+            sp[res.blocks[:-1]] = 1
+            assert np.array_equal(sp, s)

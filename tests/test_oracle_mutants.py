@@ -29,7 +29,13 @@ MUTANTS = {
     "inverted_mean": ("double mean = bs[b] / bw[b];", "double mean = bw[b] / bs[b];"),
     "off_by_one_block_end": ("int64_t hi = (b < top) ? bstart[b + 1] : n;",
                              "int64_t hi = (b < top) ? bstart[b + 1] : n - 1;"),
-    "pool_only_once": ("while (top >= 1 && bs[top - 1]", "if (top >= 1 && bs[top - 1]"),
+    "pool_only_once": ("while (top >= 1 && (decreasing", "if (top >= 1 && (decreasing"),
+    "decreasing_strict_tie_rule": ("bs[top - 1] * bw[top] <= bs[top] * bw[top - 1]",
+                                   "bs[top - 1] * bw[top] < bs[top] * bw[top - 1]"),
+    "decreasing_transposed_comparison": ("bs[top - 1] * bw[top] <= bs[top] * bw[top - 1]",
+                                         "bs[top - 1] * bw[top - 1] <= bs[top] * bw[top]"),
+    "direction_ignored": ("(decreasing ? ", "(0 ? "),
+    "direction_not_passed": ("bs, decreasing);", "bs, 0);"),
     "wrong_sign_in_pool": ("bs[top - 1] += bs[top];", "bs[top - 1] -= bs[top];"),
 }
 
@@ -45,22 +51,28 @@ def _build(src_text, tmp, name):
     P = ctypes.c_void_p
     lib.iso_oracle_fit.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64]
     lib.iso_oracle_fit.restype = ctypes.c_int
+    lib.iso_oracle_fit_dir.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    lib.iso_oracle_fit_dir.restype = ctypes.c_int
     return lib
 
 
-def _fit(lib, y, w):
+def _fit(lib, y, w, decreasing=False):
     y = np.ascontiguousarray(y, dtype=np.float64)[None, :]
     w = None if w is None else np.ascontiguousarray(w, dtype=np.float64)[None, :]
     z = np.empty_like(y)
     s = np.empty(y.shape, dtype=np.uint8)
     fl = np.empty(1, dtype=np.uint32)
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
-    lib.iso_oracle_fit(ptr(y), ptr(w), ptr(z), ptr(s), ptr(fl), 1, y.shape[1])
+    if decreasing:
+        lib.iso_oracle_fit_dir(ptr(y), ptr(w), ptr(z), ptr(s), ptr(fl), 1, y.shape[1], 1)
+    else:
+        lib.iso_oracle_fit(ptr(y), ptr(w), ptr(z), ptr(s), ptr(fl), 1, y.shape[1])
     return z[0], s[0]
 
 
 def _pins_pass(lib):
-    """A compact run of the pins: golden rows, exact max-min / hull on random tiny rows, KKT."""
+    """A compact run of the pins: golden rows, exact max-min / hull on random tiny rows, KKT,
+    and the same for the decreasing direction against the exact min-max formula."""
     for y, w, z_exp, s_exp in GOLDEN_CASES:
         yf = np.array([float(v) for v in y])
         wf = None if w is None else np.array([float(v) for v in w])
@@ -82,6 +94,22 @@ def _pins_pass(lib):
                 return False
             if exact.kkt_residual(y, w, z) > 1e-12:
                 return False
+            zd, sd = _fit(lib, y, w, decreasing=True)
+            zx = exact.minmax(y, w)
+            if any(abs(a - float(b)) > 1e-15 * (1 + abs(float(b))) for a, b in zip(zd, zx)):
+                return False
+            if list(sd) != exact.blocks_from_exact(zx):
+                return False
+            if exact.kkt_residual(y, w, zd, decreasing=True) > 1e-12:
+                return False
+            # ties: small integers, where the canonical rule decides the partition
+            yi = rng.integers(0, 3, n).astype(float)
+            wi = rng.integers(1, 4, n).astype(float)
+            for dec, ex in ((False, exact.maxmin), (True, exact.minmax)):
+                zt, st = _fit(lib, yi, wi, decreasing=dec)
+                zx = ex(yi, wi)
+                if any(a != float(b) for a, b in zip(zt, zx)) or list(st) != exact.blocks_from_exact(zx):
+                    return False
     return True
 
 
