@@ -10,7 +10,8 @@ the HBM roofline; rows/s on 65536 rows of 16 elements; the dense 1 x 10^8 fp64 n
 row; and the CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
-    python bench.py --only mixed|dense|short [--copy-calib]      (one workload, for profilers)
+    python bench.py --only mixed|dense|short|vjp [--copy-calib] (one workload, for profilers)
+    python bench.py --configs   (every measured configuration: per-call median and IQR, oracle)
     python bench.py --summarize-pmc WORKLOAD FETCH_DIR WRITE_DIR  (updates profiles/traffic.txt)
 
 Algorithmic bytes per element are read y + read w + write z (sizeof(T) each).  Of these the
@@ -81,7 +82,7 @@ STAGE_KERNEL = {"increasing": "k_increasing", "chunk": "k_chunk", "scan": "k_sca
                 "merge": "k_merge_wave", "ends": "k_ends", "fit": "k_fit"}
 
 
-def time_fit(torch, B, sets, steps, warmup):
+def time_fit(torch, B, sets, steps, warmup, flags=0):
     """Times `steps` fits after `warmup`; `sets` is a list of (y, w) input sets used in turn.
     Per-stage HIP events are recorded on the launch stream inside the timed loop."""
     batch, n = sets[0][0].shape
@@ -93,7 +94,7 @@ def time_fit(torch, B, sets, steps, warmup):
     def call(k):
         yy, ww = sets[k % len(sets)]
         rc = B.iso_fit_ex(B._ptr(yy), B._ptr(ww), B._ptr(z), None, None, batch, n, code, B._ptr(ws), nbytes,
-                          0, stream)
+                          flags, stream)
         if rc != 0:
             raise B.IsoError(rc, "iso_fit_ex")
 
@@ -197,6 +198,117 @@ def load_workload(torch, W, name, dev):
     return yh, wh, torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
 
 
+# Every measured configuration: (name, generator, unit weights, decreasing, timed calls).  The
+# unit-weight rows are run twice, with the weights passed as an array and with w = NULL.
+CONFIGS = [
+    ("cfg1_ramp_noise_4096_f64", "ramp_noise_4096", False, False, 200),
+    ("cfg2_short_rows_65536x16_f32", "short_rows_16", True, False, 200),
+    ("cfg3_calibration_512x131072_f32", "calibration", False, False, 20),
+    ("cfg4_nearly_monotone_1e7_f64", "nearly_monotone_1e7", True, False, 20),
+    ("cfg5_mixed_1e8_f32", "mixed_1e8", False, False, 10),
+    ("gate_nearly_monotone_1e8_f64", "nearly_monotone_1e8", True, False, 10),
+    ("table1_noise_1e7_f32_decreasing", "noise_1e7_decreasing", True, True, 20),
+]
+ROTATE_BYTES = 512 << 20  # written between timed calls of inputs smaller than this (the MALL is 256 MB)
+
+
+def oracle_times(oracle, y, w, decreasing, threads):
+    """The oracle on the same rows: one thread (median of 3, or 1 run when a run takes over 2 s),
+    and, for batches, rows split across `threads` threads (the C oracle releases the GIL)."""
+    import concurrent.futures
+
+    import numpy as np
+
+    yd = y.astype(np.float64)
+    wd = None if w is None else w.astype(np.float64)
+    times, z = [], None
+    for _ in range(3):
+        t0 = time.perf_counter()
+        z = oracle.pav(yd, wd, decreasing=decreasing)
+        times.append(time.perf_counter() - t0)
+        if times[-1] > 2.0:
+            break
+    one = sorted(times)[len(times) // 2]
+    multi = None
+    if y.shape[0] > 1:
+        parts = np.array_split(np.arange(y.shape[0]), threads)
+        t0 = time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda p: oracle.pav(yd[p], None if wd is None else wd[p], decreasing=decreasing), parts))
+        multi = time.perf_counter() - t0
+    return z, one, multi
+
+
+def run_configs(args, torch, B, W, dev):
+    """One JSON line per configuration: per-call GPU time (HIP events on the launch stream around
+    each call; median and interquartile range), elements/s, rows/s, fraction of the HBM roofline,
+    deviation from the oracle, and the oracle's own time on this host."""
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    host = {"cpu_count": os.cpu_count(), "oracle_threads": threads}
+    try:
+        with open("/proc/cpuinfo") as f:
+            host["cpu_model"] = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    print(json.dumps({"host": host}), flush=True)
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(ROTATE_BYTES, dtype=torch.uint8, device=dev)
+    for name, gen, unit, dec, steps in CONFIGS:
+        print("bench: config %s" % name, file=sys.stderr, flush=True)
+        yh, wh = W.WORKLOADS[gen]()
+        batch, n = yh.shape
+        zo, t1, tm = oracle_times(oracle, yh, wh, dec, threads)
+        y = torch.from_numpy(yh).to(dev)
+        runs = [("passed", torch.from_numpy(wh).to(dev))] if wh is not None else []
+        if unit:
+            runs.append(("NULL", None))
+        esz = y.element_size()
+        code = B.ISO_F64 if esz == 8 else B.ISO_F32
+        flags = B.ISO_FLAG_DECREASING if dec else 0
+        rotate = y.numel() * esz * 3 < ROTATE_BYTES
+        for wname, w in runs:
+            z = torch.empty_like(y)
+            ws, nbytes = B.workspace(batch, n, code, w is not None, dev)
+
+            def call():
+                rc = B.iso_fit_ex(B._ptr(y), B._ptr(w), B._ptr(z), None, None, batch, n, code, B._ptr(ws), nbytes,
+                                  flags, B._stream(torch, dev))
+                if rc != 0:
+                    raise B.IsoError(rc, "iso_fit_ex")
+
+            for _ in range(3):
+                call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for k in range(steps):
+                if rotate:
+                    scratch.fill_(k & 255)
+                ev[k][0].record(stream)
+                call()
+                ev[k][1].record(stream)
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in ev])
+            med = float(np.median(ms))
+            q1, q3 = (float(v) for v in np.percentile(ms, [25, 75]))
+            alg = batch * n * alg_bytes_per_elem(esz, w is not None)
+            zg = z.cpu().numpy().astype(np.float64)
+            dev_o = float(np.max(np.abs(zg - zo) / (1 + np.abs(zo)))) if zg.size else 0.0
+            line = {"config": name, "shape": [batch, n], "dtype": "f64" if esz == 8 else "f32", "weights": wname,
+                    "direction": "decreasing" if dec else "increasing", "timed_calls": steps,
+                    "rotated_inputs": rotate, "median_ms": round(med, 5), "iqr_ms": [round(q1, 5), round(q3, 5)],
+                    "elements_per_s": round(batch * n / (med * 1e-3), 1), "rows_per_s": round(batch / (med * 1e-3), 1),
+                    "alg_bytes": alg, "hbm_frac": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "max_dev_vs_oracle": dev_o, "oracle_1thread_s": round(t1, 4),
+                    "oracle_threads_s": None if tm is None else round(tm, 4)}
+            print(json.dumps(line), flush=True)
+            del z, ws
+        del y, runs
+        torch.cuda.empty_cache()
+
+
 def run_only(args, torch, B, W, dev):
     """One workload, timed as in the full run; prints one JSON line of its own."""
     if args.copy_calib:
@@ -258,6 +370,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
+    ap.add_argument("--configs", action="store_true", help="measure every configuration, one JSON line each")
     ap.add_argument("--only", choices=["mixed", "short", "dense", "vjp"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -307,6 +420,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.only:
         run_only(args, torch, B, W, dev)
+        return
+    if args.configs:
+        run_configs(args, torch, B, W, dev)
         return
     traffic = read_traffic()
     print("bench: generating mixed_1e8", file=sys.stderr, flush=True)

@@ -57,7 +57,14 @@ enum {
   /* After the fit, wait for the stream and return ISO_EWEIGHT if any row holds a weight <= 0
      or a non-finite weight (the page's Section 6: weighted calls check positivity, which waits
      for the GPU). */
-  ISO_FLAG_CHECK_WEIGHTS = 1u
+  ISO_FLAG_CHECK_WEIGHTS = 1u,
+  /* Fit the decreasing direction instead: z_0 >= z_1 >= ... >= z_{n-1} (the page's benchmarks
+     fit this direction, Section 7.2 and Table 1, as does the soft rank of Section 7.9).  It is
+     computed as the negation of the increasing fit of -y; negation is exact and rounding to
+     nearest is symmetric, so the result is exactly that mirror.  Block starts mark where a block
+     of the decreasing fit starts; neighbouring blocks then have strictly decreasing means.
+     iso_vjp needs no flag: given the block starts, its formula holds in either direction. */
+  ISO_FLAG_DECREASING = 2u
 };
 
 /* Per-row flag bits written to row_flags. */
@@ -92,7 +99,7 @@ size_t iso_workspace_bytes(int64_t batch, int64_t n, int dtype, int weighted);
  *                bytes, 256-byte aligned; may be NULL when that size is 0.  Its contents on entry
  *                do not matter and on return are unspecified.  Calls that share a workspace must
  *                be ordered on one stream.
- *   flags        0 or ISO_FLAG_CHECK_WEIGHTS.
+ *   flags        0, or ISO_FLAG_CHECK_WEIGHTS and/or ISO_FLAG_DECREASING.
  * Returns ISO_OK, ISO_EINVAL, ISO_EWEIGHT (only with ISO_FLAG_CHECK_WEIGHTS) or ISO_EHIP.
  */
 int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,

@@ -54,6 +54,7 @@ def test_header_constants_match_binding():
     assert e["ISO_EWEIGHT"] == binding.ISO_EWEIGHT and e["ISO_ENOMEM"] == binding.ISO_ENOMEM
     assert e["ISO_EHIP"] == binding.ISO_EHIP
     assert e["ISO_FLAG_CHECK_WEIGHTS"] == binding.ISO_FLAG_CHECK_WEIGHTS
+    assert e["ISO_FLAG_DECREASING"] == binding.ISO_FLAG_DECREASING
     assert e["ISO_ROW_NONFINITE"] == binding.ISO_ROW_NONFINITE
     assert e["ISO_ROW_BAD_WEIGHT"] == binding.ISO_ROW_BAD_WEIGHT
 
@@ -77,6 +78,10 @@ def test_argument_errors_before_any_launch(lib):
     assert fx(Y, None, Z, None, None, 1, -5, 0, None, 0, 0, None) == EINVAL         # negative n
     assert fx(Y, None, Z, None, None, 1, 10, 7, None, 0, 0, None) == EINVAL         # bad dtype
     assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 8, None) == EINVAL         # unknown flag
+    assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 4 | 2, None) == EINVAL     # unknown with known
+    assert fx(Y, None, Y, None, None, 1, 10, 0, None, 0, 2, None) == EINVAL         # decreasing, z aliases y
+    assert fx(Y, None, Z, None, None, 1, 5000, 0, None, 0, 2, None) == EINVAL       # decreasing, no workspace
+    assert fx(Y, None, Z, None, None, 0, 10, 0, None, 0, 2, None) == OK             # decreasing, empty
     assert fx(Y, None, Y, None, None, 1, 10, 0, None, 0, 0, None) == EINVAL         # z aliases y
     assert fx(Y, W, W, None, None, 1, 10, 1, None, 0, 0, None) == EINVAL            # z aliases w
     assert fx(Y, None, P(Y.value + 8), None, None, 1, 10, 0, None, 0, 0, None) == EINVAL  # overlap

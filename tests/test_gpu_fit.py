@@ -40,13 +40,14 @@ def deviation(z, zo):
     return float(np.max(np.abs(z - zo) / (1 + np.abs(zo)))) if z.size else 0.0
 
 
-def check(y, w, exact_partition=False, tol=None, kkt=True, scale_abs=False):
+def check(y, w, exact_partition=False, tol=None, kkt=True, scale_abs=False, decreasing=False):
     """scale_abs: measure max |z - z*| / max |y| instead (the page's Section 7.6 measure for its
-    cancellation family, whose blocks mix values of very different sizes)."""
+    cancellation family, whose blocks mix values of very different sizes).  decreasing: fit and
+    compare the non-increasing direction."""
     t = y.dtype.type
-    z, bs, rf = gpu_fit(y, w)
+    z, bs, rf = gpu_fit(y, w, decreasing=decreasing)
     zo, bo, fo = oracle.pav(y.astype(np.float64), None if w is None else w.astype(np.float64),
-                            return_blocks=True)
+                            return_blocks=True, decreasing=decreasing)
     zo = zo.reshape(y.shape)
     bo = bo.reshape(y.shape)
     assert np.array_equal(rf.astype(np.uint32), fo)
@@ -59,7 +60,8 @@ def check(y, w, exact_partition=False, tol=None, kkt=True, scale_abs=False):
         assert np.array_equal(bs, bo)
     if kkt and y.ndim == 2 and y.shape[1] <= 300_000:
         for r in range(min(y.shape[0], 3)):
-            assert exact.kkt_residual(y[r], None if w is None else w[r], z[r]) < (1e-12 if t == np.float64 else 1e-6)
+            assert exact.kkt_residual(y[r], None if w is None else w[r], z[r], decreasing=decreasing) < (
+                1e-12 if t == np.float64 else 1e-6)
     return z, bs
 
 

@@ -330,3 +330,25 @@ def test_decreasing_scipy_cross_check():
             sp = np.zeros(20000, dtype=np.uint8)
             sp[res.blocks[:-1]] = 1
             assert np.array_equal(sp, s)
+
+
+def test_decreasing_vjp_against_finite_differences():
+    """The block-averaging backward holds in either direction: with the decreasing fit's blocks it
+    matches central finite differences of the decreasing fit."""
+    rng = np.random.default_rng(18)
+    for n in (6, 23, 40):
+        y = rng.standard_normal(n)
+        w = rng.uniform(0.5, 2.0, n)
+        g = rng.standard_normal(n)
+        z, s, _ = oracle.pav(y, w, return_blocks=True, decreasing=True)
+        gy, gw = oracle.vjp(g, y, w, z, s)
+        h = 1e-6
+        fd_y = np.zeros(n)
+        fd_w = np.zeros(n)
+        for j in range(n):
+            e = np.zeros(n)
+            e[j] = h
+            fd_y[j] = g @ (oracle.pav(y + e, w, decreasing=True) - oracle.pav(y - e, w, decreasing=True)) / (2 * h)
+            fd_w[j] = g @ (oracle.pav(y, w + e, decreasing=True) - oracle.pav(y, w - e, decreasing=True)) / (2 * h)
+        assert np.allclose(gy, fd_y, atol=1e-6)
+        assert np.allclose(gw, fd_w, atol=1e-6)

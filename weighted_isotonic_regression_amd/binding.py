@@ -17,6 +17,7 @@ from . import build as _build
 ISO_F32, ISO_F64 = 0, 1
 ISO_OK, ISO_EINVAL, ISO_EWEIGHT, ISO_ENOMEM, ISO_EHIP = 0, 1, 2, 3, 4
 ISO_FLAG_CHECK_WEIGHTS = 1
+ISO_FLAG_DECREASING = 2
 ISO_ROW_NONFINITE, ISO_ROW_BAD_WEIGHT = 1, 2
 
 _lock = threading.Lock()
@@ -148,8 +149,10 @@ def workspace(batch, n, dtype_code, weighted, device):
     return buf[shift:shift + nbytes], nbytes
 
 
-def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, out=None, ws=None):
-    """Isotonic (non-decreasing) weighted L2 fit of every row of ``y`` on its device.
+def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, decreasing=False, out=None,
+        ws=None):
+    """Isotonic weighted L2 fit of every row of ``y`` on its device: non-decreasing, or
+    non-increasing with ``decreasing=True``.
 
     y: float32/float64 CUDA tensor [n] or [batch, n]; w: same shape and dtype, or None.
     Returns z, or (z, block_start[uint8], row_flags[int32]) as requested.
@@ -172,7 +175,7 @@ def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, 
         ws, nbytes = workspace(batch, n, code, w2 is not None, y2.device)
     else:
         nbytes = ws.numel()
-    flags = ISO_FLAG_CHECK_WEIGHTS if check_weights else 0
+    flags = (ISO_FLAG_CHECK_WEIGHTS if check_weights else 0) | (ISO_FLAG_DECREASING if decreasing else 0)
     rc = iso_fit_ex(_ptr(y2), _ptr(w2), _ptr(z), _ptr(bs), _ptr(rf), batch, n, code, _ptr(ws), nbytes, flags,
                     _stream(torch, y2.device))
     if rc != ISO_OK:

@@ -158,7 +158,7 @@ int lanes_per_row(int64_t n) {
   return L;
 }
 
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int64_t batch,
             int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
   Prof prof(s);
@@ -167,7 +167,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int R = kWave / L;
     const int64_t tiles = (batch + R - 1) / R;
     prof.skip();
-    hipLaunchKernelGGL((k_wave<T, W>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
+    hipLaunchKernelGGL((k_wave<T, W, D>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
                        rflags, batch, n, L);
     prof.mark(1);
     return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
@@ -199,17 +199,17 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
   EndInfo* ends = (EndInfo*)(ws + Lay.o_ends);
 
-  hipLaunchKernelGGL((k_increasing<T, W>), dim3((unsigned)G), dim3(kIncWaves * kWave), 0, s, y, w, z, n,
+  hipLaunchKernelGGL((k_increasing<T, W, D>), dim3((unsigned)G), dim3(kIncWaves * kWave), 0, s, y, w, z, n,
                      m, co);
   prof.mark(1);
-  hipLaunchKernelGGL((k_chunk<T, W>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
+  hipLaunchKernelGGL((k_chunk<T, W, D>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
                      s, co.tot, co.cflags, bsum, bflag, m, nblk);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
                      co.tot, bsum, bflag, start, rflags, m, nblk);
   prof.mark(2);
-  VertexStore<T, W> S;
+  VertexStore<T, W, D> S;
   S.desc = co.desc;
   S.nseg = co.nseg;
   S.nverts = co.nverts;
@@ -238,25 +238,25 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int per_row = (m - (1 << r) + span - 1) / span;
     const int64_t merges = batch * (int64_t)per_row;
     const int64_t blocks = (merges + kMergeWaves - 1) / kMergeWaves;
-    hipLaunchKernelGGL((k_merge_wave<T, W>), dim3((unsigned)blocks), dim3(kMergeWaves * kWave), 0, s, S,
+    hipLaunchKernelGGL((k_merge_wave<T, W, D>), dim3((unsigned)blocks), dim3(kMergeWaves * kWave), 0, s, S,
                        batch, r, per_row);
   }
   prof.mark(levels);
-  hipLaunchKernelGGL((k_ends<T, W>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,
+  hipLaunchKernelGGL((k_ends<T, W, D>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,
                      batch);
   prof.mark(1);
-  hipLaunchKernelGGL((k_fit<T, W>), dim3((unsigned)G), dim3(kFitThreads), 0, s, S,
+  hipLaunchKernelGGL((k_fit<T, W, D>), dim3((unsigned)G), dim3(kFitThreads), 0, s, S,
                      (const EndInfo*)ends, (const uint32_t*)rflags, (const uint8_t*)co.ztile, z, bstart);
   prof.mark(1);
   return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
 }
 
-template <typename T>
+template <typename T, bool D>
 int dispatch_fit(const void* y, const void* w, void* z, uint8_t* bstart, uint32_t* rflags,
                  int64_t batch, int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
   if (w)
-    return run_fit<T, true>((const T*)y, (const T*)w, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
-  return run_fit<T, false>((const T*)y, nullptr, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
+    return run_fit<T, true, D>((const T*)y, (const T*)w, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
+  return run_fit<T, false, D>((const T*)y, nullptr, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
 }
 
 }  // namespace
@@ -312,7 +312,7 @@ int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint
                int64_t batch, int64_t n, int dtype, void* ws, size_t ws_bytes, unsigned flags,
                void* stream) {
   if (!shape_ok(batch, n, dtype)) return ISO_EINVAL;
-  if (flags & ~(unsigned)ISO_FLAG_CHECK_WEIGHTS) return ISO_EINVAL;
+  if (flags & ~(unsigned)(ISO_FLAG_CHECK_WEIGHTS | ISO_FLAG_DECREASING)) return ISO_EINVAL;
   if (batch == 0 || n == 0) return ISO_OK;
   if (!y || !z) return ISO_EINVAL;
   const size_t esz = dtype == ISO_F64 ? 8 : 4;
@@ -328,9 +328,13 @@ int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint
   uint32_t* rflags = row_flags;
   if (!rflags && need_ws) rflags = (uint32_t*)(wsb + Lay.o_rflags);
   hipStream_t s = (hipStream_t)stream;
-  int rc = dtype == ISO_F64
-               ? dispatch_fit<double>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s)
-               : dispatch_fit<float>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s);
+  int rc;
+  if (flags & ISO_FLAG_DECREASING)
+    rc = dtype == ISO_F64 ? dispatch_fit<double, true>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s)
+                          : dispatch_fit<float, true>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s);
+  else
+    rc = dtype == ISO_F64 ? dispatch_fit<double, false>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s)
+                          : dispatch_fit<float, false>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s);
   if (rc != ISO_OK) return rc;
   if (flags & ISO_FLAG_CHECK_WEIGHTS) {
     uint32_t* any = (uint32_t*)(wsb + Lay.o_any);

@@ -145,7 +145,7 @@ __device__ __forceinline__ bool ring_get(const ChunkLds<W>& L, int s, int l, int
 
 // Lane-relative coordinates of lane l's point q, from the checkpoint below q and the inputs (the
 // same operations in the same order as the chain).  ck = the chunk's checkpoints.
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __device__ double2 lane_point(const double* ckx, const double* cky, int l, int q, int c,
                               const T* yl, const T* wl) {
   q = min(max(q, 0), c);
@@ -153,7 +153,7 @@ __device__ double2 lane_point(const double* ckx, const double* cky, int l, int q
   double2 P{W ? ckx[l * kLaneW + j] : 0.0, cky[l * kLaneW + j]};
   uint32_t f = 0u;
   for (int e = kCk * j; e < q; ++e) {
-    double yd = (double)yl[e], wd = W ? (double)wl[e] : 1.0;
+    double yd = yval<D>(yl[e]), wd = W ? (double)wl[e] : 1.0;
     classify<W>(yd, wd, f);
     if (W) P.x += wd;
     P.y += wd * yd;
@@ -196,7 +196,7 @@ __device__ int lane_index(const ChunkLds<W>& L, int l, int i, int c, bool& in_ri
 }
 
 // Point index q and lane-relative coordinates of the stack entry at depth i of lane l.
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __device__ double2 lane_entry(const ChunkLds<W>& L, const double* ckx, const double* cky, int l,
                               int i, int c, const T* yl, const T* wl, int& q) {
   bool in_ring;
@@ -207,12 +207,12 @@ __device__ double2 lane_entry(const ChunkLds<W>& L, const double* ckx, const dou
     (void)ring_get<W>(L, ring_slot(i), l, i, q, x, yy);
     return double2{x, yy};
   }
-  return lane_point<T, W>(ckx, cky, l, q, c, yl, wl);
+  return lane_point<T, W, D>(ckx, cky, l, q, c, yl, wl);
 }
 
 // Chunk-relative coordinates and point index q (0..256, within the lane) of the stack entry at
 // depth i of lane l.
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const double* ckx,
                                                const double* cky, int l, int i, int len,
                                                const T* yc, const T* wc, int& q) {
@@ -225,18 +225,18 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
     q = c;
     return L.start[l + 1];
   }
-  const double2 P = lane_entry<T, W>(L, ckx, cky, l, i, c, yc + kSub * l,
+  const double2 P = lane_entry<T, W, D>(L, ckx, cky, l, i, c, yc + kSub * l,
                                      W ? wc + kSub * l : nullptr, q);
   const double2 S = L.start[l];
   return double2{W ? S.x + P.x : (double)(kSub * l + q), S.y + P.y};
 }
 
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const double* ckx,
                                                const double* cky, int l, int i, int len,
                                                const T* yc, const T* wc) {
   int q;
-  return chunk_entry<T, W>(L, ckx, cky, l, i, len, yc, wc, q);
+  return chunk_entry<T, W, D>(L, ckx, cky, l, i, len, yc, wc, q);
 }
 
 // Chunks whose elements are all clean and strictly increasing.  Every turn of such a chunk's
@@ -254,7 +254,7 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
 // (block sums); bad: an int of LDS.
 constexpr int kIncWaves = 4;
 
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__ wc,
                                  T* __restrict__ zc, int len, int64_t g, int j,
                                  const ChunkOut& out, double* bsx, double* bsy, int* bad) {
@@ -274,11 +274,11 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     if (e + VN <= len) {
       T pv[VN];
       load16(yc + e, pv);
-      const double before = (lane / SPW) ? (double)yc[e - 1] : -INFINITY;
+      const double before = (lane / SPW) ? yval<D>(yc[e - 1]) : -INFINITY;
       double prev = before;
 #pragma unroll
       for (int k = 0; k < VN; ++k) {
-        const double yd = (double)pv[k];
+        const double yd = yval<D>(pv[k]);
         ok = ok && isfinite(yd) && prev < yd;
         prev = yd;
       }
@@ -286,7 +286,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     if (__syncthreads_or(!ok)) return false;
   }
   const int q0 = QE * wv, q1 = min(QE * (wv + 1), len);
-  double carry = q0 > 0 && q0 < len ? (double)yc[q0 - 1] : -INFINITY;
+  double carry = q0 > 0 && q0 < len ? yval<D>(yc[q0 - 1]) : -INFINITY;
   for (int s0 = q0; s0 < q1; s0 += SE) {
     T yv[U * VN], wv_[U * VN];
 #pragma unroll
@@ -307,14 +307,14 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = s0 + (u * kWave + lane) * VN;
-      const double last = (double)yv[u * VN + VN - 1];
+      const double last = yval<D>(yv[u * VN + VN - 1]);
       double prev = __shfl_up(last, 1, kWave);
       if (lane == 0) prev = carry;
       double sw = 0.0, sy = 0.0;
 #pragma unroll
       for (int k = 0; k < VN; ++k) {
         if (e + k < q1) {
-          const double yd = (double)yv[u * VN + k];
+          const double yd = yval<D>(yv[u * VN + k]);
           const double wd = W ? (double)wv_[u * VN + k] : 1.0;
           ok = ok && isfinite(yd) && isfinite(wd) && wd > 0.0 && prev < yd;
           prev = yd;
@@ -403,7 +403,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     const double w0 = W ? (double)wc[0] : 1.0;
     double ax = 0.0, ay = 0.0;
     if (W) ax += w0;
-    ay += w0 * (double)yc[0];
+    ay += w0 * yval<D>(yc[0]);
     out.bnd[g].x = W ? 0.0 + ax : 1.0;
     out.bnd[g].y = 0.0 + ay;
     out.bndk[g].x = 1;
@@ -434,7 +434,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
       if (e0v + k < kv) {
         const double wd = W ? (double)we[k] : 1.0;
         if (W) ax += wd;
-        ay += wd * (double)ye[k];
+        ay += wd * yval<D>(ye[k]);
       }
     }
     out.bnd[g].z = W ? sx + ax : (double)kv;
@@ -447,7 +447,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
 // Runs before k_chunk: one workgroup per chunk tries increasing_chunk on chunks of at least 64
 // elements whose inputs are 16-byte aligned, and marks the chunk's form byte 2 when it succeeds,
 // 3 otherwise (k_chunk then processes the chunk and writes its form).
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __global__ __launch_bounds__(kIncWaves * kWave) void k_increasing(const T* __restrict__ y,
                                                                   const T* __restrict__ w,
                                                                   T* __restrict__ z, int64_t n,
@@ -465,12 +465,12 @@ __global__ __launch_bounds__(kIncWaves * kWave) void k_increasing(const T* __res
                    (((uintptr_t)(z + off)) % 16 == 0);
   bool done = false;
   if (len >= 2 * kCk && vec)
-    done = increasing_chunk<T, W>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bsx, bsy,
+    done = increasing_chunk<T, W, D>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bsx, bsy,
                                   &bad);
   if (!done && threadIdx.x == 0) out.dform[g] = 3;
 }
 
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y,
                                                         const T* __restrict__ w,
                                                         T* __restrict__ z, int64_t n, int m,
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         mw = mask_word<W>(L, lane, ww, wi, curw);
       }
       vi = kCk * ww + 31 - __builtin_clz(mw);
-      const double2 P = lane_point<T, W>(ckx, cky, lane, vi, c, yl, wl);
+      const double2 P = lane_point<T, W, D>(ckx, cky, lane, vi, c, yl, wl);
       vx = P.x;
       vy = P.y;
       __builtin_amdgcn_s_waitcnt(0);
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       double yp = yprev;
 #pragma unroll
       for (int k = 0; k < TN; ++k) {
-        const double yd = (double)yv[k];
+        const double yd = yval<D>(yv[k]);
         const double wd = W ? (double)wv[k] : 1.0;
         clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0;
         incr = incr && (yp < yd || (eb == 0 && k == 0));
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     // one element through the chain: its left point q (a candidate when y_{q-1} < y_q), then
     // the running sums
     auto element = [&](int k) {
-      const double yd = (double)yv[k];
+      const double yd = yval<D>(yv[k]);
       const double wd = W ? (double)wv[k] : 1.0;
       const int q = eb + k;
       if (q > 0) {
@@ -711,10 +711,10 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         if (k >= kc) {
           const double wd = W ? (double)wv[k] : 1.0;
           if (W) lx += wd;
-          ly += wd * (double)yv[k];
+          ly += wd * yval<D>(yv[k]);
         }
       }
-      yprev = (double)yv[TN - 1];
+      yprev = yval<D>(yv[TN - 1]);
       const int b0 = (eb & 31) + kp, b1 = (eb & 31) + TN - 1;  // bits of points eb+kp .. eb+TN-1
       curw |= (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u);
     };
@@ -806,8 +806,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       ai = L.depth[al] - 1;                        // alpha = s
       bl = min(__builtin_ctzll(nzr & ~lanes_below(sB)), lb);  // beta = B's first vertex
       bi = L.lo[bl];
-      double2 Pa = chunk_entry<T, W>(L, ckx, cky, al, ai, len, yc, wc);
-      double2 Pb = chunk_entry<T, W>(L, ckx, cky, bl, bi, len, yc, wc);
+      double2 Pa = chunk_entry<T, W, D>(L, ckx, cky, al, ai, len, yc, wc);
+      double2 Pb = chunk_entry<T, W, D>(L, ckx, cky, bl, bi, len, yc, wc);
       for (int pass = 0; pass <= kChunk; ++pass) {
         bool moved = false;
         // alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
               pi = 0;
             }
           }
-          const double2 Pp = chunk_entry<T, W>(L, ckx, cky, pl, pi, len, yc, wc);
+          const double2 Pp = chunk_entry<T, W, D>(L, ckx, cky, pl, pi, len, yc, wc);
           if (turn_pts(Pp, Pa, Pb) > 0.0) break;
           al = pl;
           ai = pi;
@@ -843,7 +843,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
             ql = min(__builtin_ctzll(nzr & ~lanes_below(bl + 1)), lb);
             qi = max(L.lo[ql], 1);
           }
-          const double2 Pq = chunk_entry<T, W>(L, ckx, cky, ql, qi, len, yc, wc);
+          const double2 Pq = chunk_entry<T, W, D>(L, ckx, cky, ql, qi, len, yc, wc);
           if (turn_pts(Pa, Pb, Pq) > 0.0) break;
           bl = ql;
           bi = qi;
@@ -905,7 +905,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     }
     for (int i = lo; i <= hi; ++i) {
       int q;
-      const double2 P = chunk_entry<T, W>(L, ckx, cky, lane, i, len, yc, wc, q);
+      const double2 P = chunk_entry<T, W, D>(L, ckx, cky, lane, i, len, yc, wc, q);
       out.lk[lb0 + pos] = (uint16_t)(e0 + q);
       out.lx[lb0 + pos] = P.x;
       out.ly[lb0 + pos] = P.y;
@@ -922,7 +922,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     const int lz = 63 - __builtin_clzll(nz);  // vertex V - 1 ends the last range
     if (lane == l1) {
       int q;
-      const double2 P = chunk_entry<T, W>(L, ckx, cky, lane, lo, len, yc, wc, q);
+      const double2 P = chunk_entry<T, W, D>(L, ckx, cky, lane, lo, len, yc, wc, q);
       out.bnd[g].x = P.x;
       out.bnd[g].y = P.y;
       out.bndk[g].x = e0 + q;
@@ -939,7 +939,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       int kq = 0;
       if (in_lz || before) {
         int q;
-        P = chunk_entry<T, W>(L, ckx, cky, lane, i, len, yc, wc, q);
+        P = chunk_entry<T, W, D>(L, ckx, cky, lane, i, len, yc, wc, q);
         kq = e0 + q;
       }
       out.bnd[g].z = P.x;

@@ -49,6 +49,19 @@ constexpr uint32_t ISO_ROW_BAD_WEIGHT_BIT = 2u;
 // (ax, ay) x (bx, by) with one rounded product.
 ISO_HD double cross2(double ax, double ay, double bx, double by) { return fma(ax, by, -(ay * bx)); }
 
+// An input value as the diagram uses it.  The decreasing fit (z_0 >= ... >= z_{n-1}) is the
+// negated increasing fit of -y; negation is exact and rounding to nearest is symmetric, so with D
+// every sum, turn and slope is the exact mirror of the increasing fit's of -y.
+template <bool D, typename T>
+ISO_HD double yval(T v) {
+  return D ? -(double)v : (double)v;
+}
+// A fitted slope as the caller receives it.
+template <bool D>
+ISO_HD double zval(double s) {
+  return D ? -s : s;
+}
+
 struct DD {
   double hi, lo;
 };
@@ -267,7 +280,7 @@ ISO_HD int desc_nverts(const Desc& d) { return d.w >> 2; }
 //          operations in the same order as the chunk pass, so they are bitwise its values.
 // Dense chunks are the ones whose points nearly all survive; storing them as lists would move
 // about 18 bytes per element, while the dense form takes under one.
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 struct VertexStore {
   Desc* desc;             // [G] descriptor slots
   int* nseg;              // [G] length of the list of the node starting at this slot
@@ -318,7 +331,7 @@ struct VertexStore {
     const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
     for (int e = kCk * jj; e < q; ++e) {
       double wd = W ? (double)w[e0 + e] : 1.0;
-      double yd = (double)y[e0 + e];
+      double yd = yval<D>(y[e0 + e]);
       if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
         yd = 0.0;
         wd = 1.0;

@@ -128,7 +128,7 @@ struct TilePts {
   }
 };
 
-template <typename T, bool W>
+template <typename T, bool W, bool D>
 __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
                                              T* __restrict__ z, uint8_t* __restrict__ bstart,
                                              uint32_t* __restrict__ rflags, int64_t batch,
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   for (int k = 0; k < kLanePts; ++k) {
     const int e = vec ? (lane + kWave * (k / VN)) * VN + (k % VN) : lane + kWave * k;
     if (e < E) {
-      double yd = (double)yv[k];
+      double yd = yval<D>(yv[k]);
       double wd = W ? (double)wv[k] : 1.0;
       const int r = small_div(e, seglen, inv_seg);
       const int i = e - r * seglen;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       Pr(b, bx, by);
       const bool bad = sF[r] != 0u;
       const double slope = (by - ay) / (bx - ax);
-      z[off + e] = bad ? (T)NAN : (T)slope;
+      z[off + e] = bad ? (T)NAN : (T)zval<D>(slope);
       if (bstart) bstart[off + e] = (!bad && isv) ? 1 : 0;
     }
     if (rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
@@ -448,8 +448,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __re
 }
 
 // ------------------------------------------------------------------ ends
-template <typename T, bool W>
-__global__ __launch_bounds__(256) void k_ends(VertexStore<T, W> S, EndInfo* __restrict__ ends,
+template <typename T, bool W, bool D>
+__global__ __launch_bounds__(256) void k_ends(VertexStore<T, W, D> S, EndInfo* __restrict__ ends,
                                               int64_t batch) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= batch * (int64_t)S.m) return;
@@ -469,8 +469,8 @@ __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W> S, EndInfo* __re
 //                 recomputed from the lane checkpoints (a one-element edge is the element's y).
 constexpr int kFitThreads = 256;
 
-template <typename T, bool W>
-__global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
+template <typename T, bool W, bool D>
+__global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
                                                      const EndInfo* __restrict__ ends,
                                                      const uint32_t* __restrict__ rflags,
                                                      const uint8_t* __restrict__ ztile,
@@ -495,14 +495,14 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
     return;
   }
   if (e.lo < 0) {
-    const T zv = (T)e.sin;
+    const T zv = (T)zval<D>(e.sin);
     for (int i = tid; i < len; i += kFitThreads) {
       z[off + i] = zv;
       if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
     }
     return;
   }
-  const T zin = (T)e.sin, zout = (T)e.sout;
+  const T zin = (T)zval<D>(e.sin), zout = (T)zval<D>(e.sout);
   if (S.dense[g] == 2 && e.khi == len && (e.klo == 0 || (e.klo == 1 && e.p0v))) {
     // every point of the chunk is a vertex of the chunk hull, and all of them are vertices of the
     // row's hull (point 0 possibly as the previous chunk's last vertex): every element is its own
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
         double ax, ay, bx, by;
         S.dense_point(row, j, a, ax, ay);
         S.dense_point(row, j, b, bx, by);
-        z[off + i] = (T)((by - ay) / (bx - ax));
+        z[off + i] = (T)zval<D>((by - ay) / (bx - ax));
       }
     }
     return;
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W> S,
       zv = sSlope[lo];
       st = (sK[lo] == i) ? 1 : 0;
     }
-    z[off + i] = (T)zv;
+    z[off + i] = (T)zval<D>(zv);
     if (bstart) bstart[off + i] = st;
   }
 }

@@ -352,8 +352,8 @@ __device__ bool window_bridge(const VS& S, const NodeList& LA, const NodeList& L
   return false;
 }
 
-template <typename T, bool W>
-__global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<T, W> S,
+template <typename T, bool W, bool D>
+__global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<T, W, D> S,
                                                                     int64_t batch, int r,
                                                                     int per_row) {
   __shared__ MergeLds sw[kMergeWaves][2];

@@ -110,6 +110,14 @@ def mixed_1e8(seed=5, n=100_000_000, batch=1, dtype="f32"):
     return y, w
 
 
+def noise_1e7_decreasing(seed=7, n=10_000_000, dtype="f32"):
+    """y ~ N(0, 1) i.i.d., one row, fp32, no weights (returned as None), to be fitted in the
+    decreasing direction: the setting of the page's Table 1 comparison (Section 7.2), whose own
+    inputs the page does not give."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((1, n)).astype(_dt(dtype)), None
+
+
 WORKLOADS = {
     "ramp_noise_4096": ramp_noise_4096,
     "short_rows_16": short_rows_16,
@@ -117,6 +125,7 @@ WORKLOADS = {
     "nearly_monotone_1e7": nearly_monotone_1e7,
     "mixed_1e8": mixed_1e8,
     "nearly_monotone_1e8": nearly_monotone_1e8,
+    "noise_1e7_decreasing": noise_1e7_decreasing,
 }
 
 
