@@ -166,7 +166,7 @@ def read_traffic():
             sha = line.split("=")[1].strip()
         elif line and not line.startswith("#") and "=" not in line:
             parts = line.split()
-            if len(parts) == 4:
+            if len(parts) >= 4:
                 out.setdefault(parts[0], {})[parts[1]] = (float(parts[2]), float(parts[3]))
     return out if sha == source_hash() else {}
 
@@ -188,14 +188,13 @@ def stage_line(st_ms, calls):
     return {k: round(v / max(calls, 1), 4) for k, v in st_ms.items()}
 
 
+ONLY = {"mixed": "mixed_1e8", "dense": "nearly_monotone_1e8", "short": "short_rows_16", "calib": "calibration",
+        "mono7": "nearly_monotone_1e7", "ramp": "ramp_noise_4096", "table1": "noise_1e7_decreasing"}
+
+
 def load_workload(torch, W, name, dev):
-    if name == "short":
-        yh, wh = W.short_rows_16()
-    elif name == "dense":
-        yh, wh = W.nearly_monotone_1e8()
-    else:
-        yh, wh = W.mixed_1e8()
-    return yh, wh, torch.from_numpy(yh).to(dev), torch.from_numpy(wh).to(dev)
+    yh, wh = W.WORKLOADS[ONLY[name]]()
+    return yh, wh, torch.from_numpy(yh).to(dev), None if wh is None else torch.from_numpy(wh).to(dev)
 
 
 # Every measured configuration: (name, generator, unit weights, decreasing, timed calls).  The
@@ -326,10 +325,11 @@ def run_only(args, torch, B, W, dev):
         return
     _, _, y, w = load_workload(torch, W, args.only, dev)
     print("bench: timing %s" % args.only, file=sys.stderr, flush=True)
-    _, ms, sms, sla, sc = time_fit(torch, B, [(y, w)], args.steps, args.warmup)
+    flags = B.ISO_FLAG_DECREASING if args.only == "table1" else 0
+    _, ms, sms, sla, sc = time_fit(torch, B, [(y, w)], args.steps, args.warmup, flags=flags)
     esz = y.element_size()
     print(json.dumps({"workload": args.only, "ms_per_call": round(ms, 4), "stage_ms": stage_line(sms, sc),
-                      "hbm_frac": round(y.numel() * alg_bytes_per_elem(esz, True) / (ms * 1e-3) / 1e9 /
+                      "hbm_frac": round(y.numel() * alg_bytes_per_elem(esz, w is not None) / (ms * 1e-3) / 1e9 /
                                         HBM_PEAK_GBS, 4)}), flush=True)
 
 
@@ -354,12 +354,18 @@ def summarize_pmc(fetch_dir, write_dir):
         raise SystemExit("no calibration copy kernel in the counter runs")
     sf = COPY_BYTES / (sorted(copy_f)[len(copy_f) // 2])
     sw = COPY_BYTES / (sorted(copy_w)[len(copy_w) // 2])
+    def mine(k, key):
+        return ("iso::%s<" % key) in k or ("iso::%s(" % key) in k
+
+    # fit calls in the run: one k_chunk (long rows) or k_wave (short rows) dispatch each
+    calls = max(sum(len(vs) for k, vs in fetch.items() if mine(k, "k_chunk") or mine(k, "k_wave")), 1)
     lines = []
-    for key in ("k_increasing", "k_chunk", "k_fit", "k_merge_wave"):
-        fs = [v for k, vs in fetch.items() if key in k for v in vs]
-        wsz = [v for k, vs in write.items() if key in k for v in vs]
+    for key in ("k_wave", "k_increasing", "k_chunk", "k_scan_reduce", "k_scan_apply", "k_merge_wave", "k_ends",
+                "k_fit"):
+        fs = [v for k, vs in fetch.items() if mine(k, key) for v in vs]
+        wsz = [v for k, vs in write.items() if mine(k, key) for v in vs]
         if fs and wsz:
-            lines.append((key, sum(fs) / len(fs) * sf, sum(wsz) / len(wsz) * sw))
+            lines.append((key, sum(fs) / len(fs) * sf, sum(wsz) / len(wsz) * sw, len(fs) / calls))
     return sf, sw, lines
 
 
@@ -371,7 +377,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
     ap.add_argument("--configs", action="store_true", help="measure every configuration, one JSON line each")
-    ap.add_argument("--only", choices=["mixed", "short", "dense", "vjp"], default=None,
+    ap.add_argument("--only", choices=sorted(ONLY) + ["vjp"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="with --only: first run a 1 GiB device copy (memory-counter calibration)")
@@ -392,17 +398,21 @@ def main():
             f.write("# (KiB per dispatch) scaled by the same counters for a 1 GiB device copy in the same run\n")
             f.write("# (latest scale factors: fetch %.4f, write %.4f).  Columns: workload kernel fetch_bytes\n"
                     % (sf, sw))
-            f.write("# write_bytes.  Valid only for the kernel sources of this hash (bench.py checks it).\n")
-            f.write("# Made by, for each workload W in mixed, dense (R = the repository root, run from /tmp):\n")
+            f.write("# write_bytes launches_per_call.  Valid only for the kernel sources of this hash (bench.py\n")
+            f.write("# checks it).\n")
+            f.write("# Made by, for each workload W in mixed, dense, short, calib, mono7 (R = the repository root,\n")
+            f.write("# run from /tmp):\n")
             f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/meas/pf_W -o run -- \\\n")
             f.write("#     python3 $R/bench.py --only W --steps 2 --warmup 1 --copy-calib\n")
             f.write("#   (the same with WRITE_SIZE into pw_W), then\n")
-            f.write("#   python bench.py --summarize-pmc W_1e8_<dtype> gpurun_out/meas/pf_W gpurun_out/meas/pw_W\n")
+            f.write("#   python bench.py --summarize-pmc NAME gpurun_out/meas/pf_W gpurun_out/meas/pw_W\n")
+            f.write("# with NAME mixed_1e8_f32, dense_1e8_f64, short_65536x16_f32, calib_512x131072_f32,\n")
+            f.write("# mono_1e7_f64 for those W.\n")
             f.write("source_sha256 = %s\n" % sha)
             for l in keep:
                 f.write(l + "\n")
-            for k, fb, wb in lines:
-                f.write("%s %s %.0f %.0f\n" % (wl, k, fb, wb))
+            for k, fb, wb, lpc in lines:
+                f.write("%s %s %.0f %.0f %g\n" % (wl, k, fb, wb, lpc))
         print(open(TRAFFIC_FILE).read())
         return
     if args.gpus != 1:
