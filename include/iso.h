@@ -124,6 +124,42 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
             const uint8_t* block_start, void* gy, void* gw, int64_t batch, int64_t n, int dtype,
             void* stream);
 
+/*
+ * iso_fit_ragged -- fit rows of unequal lengths laid end to end ("Merge Hulls Without Copying
+ * Vertices", Section 9, Limitations: the operator takes a rectangular batch, and rows of unequal
+ * length are padded).  Row r is the elements offsets[r] .. offsets[r+1]-1 of the packed arrays.
+ *   values       packed input values, at least offsets[batch] elements (device)
+ *   weights      packed weights of the same layout, or NULL for unit weights (device)
+ *   offsets      batch + 1 non-decreasing int64 offsets, offsets[0] >= 0, in HOST memory; read
+ *                during the call only
+ *   z            packed output fit, same layout (device; must not overlap values or weights)
+ *   block_start  packed block starts, or NULL (device); as in iso_fit_ex, within each row
+ *   row_flags    [batch] uint32 per-row flags, or NULL (device); an empty row gets 0
+ *   ws, ws_bytes device workspace of at least iso_ragged_workspace_bytes(offsets, batch, dtype,
+ *                weights != NULL) bytes, 256-byte aligned
+ *   flags        0, or ISO_FLAG_CHECK_WEIGHTS and/or ISO_FLAG_DECREASING
+ * Each row's fit equals its fit as a row of its own, to rounding.  Method: rows are grouped in
+ * buckets of lengths within a factor of two; each bucket is copied into a rectangular buffer
+ * whose rows are padded after their last element, at unit weight, with a value beyond the row's
+ * range (its maximum M plus |M|/1024 + 1; for the decreasing fit its minimum minus that).  Those
+ * pads never pool with the row's elements.  The bucket is fitted as by iso_fit_ex and each row's
+ * part copied back.  A row whose extreme is so large that the pad overflows the element type is
+ * flagged ISO_ROW_NONFINITE.  The call uploads the bucket plan and waits for the stream once
+ * before enqueueing its kernels; it returns without waiting for them unless
+ * ISO_FLAG_CHECK_WEIGHTS is given.  Returns ISO_OK, ISO_EINVAL (bad offsets, sizes, flags,
+ * pointers or workspace), ISO_EWEIGHT or ISO_EHIP.
+ */
+int iso_fit_ragged(const void* values, const void* weights, const int64_t* offsets, int64_t batch,
+                   int dtype, void* z, uint8_t* block_start, uint32_t* row_flags, void* ws,
+                   size_t ws_bytes, unsigned flags, void* stream);
+
+/*
+ * iso_ragged_workspace_bytes -- size in bytes of the workspace iso_fit_ragged needs for these
+ * host offsets (weighted != 0 when weights will be passed); 0 for invalid offsets or sizes, or
+ * when batch == 0.
+ */
+size_t iso_ragged_workspace_bytes(const int64_t* offsets, int64_t batch, int dtype, int weighted);
+
 /* iso_strerror -- static description of a return code. */
 const char* iso_strerror(int code);
 

@@ -254,3 +254,26 @@ def test_empty_and_tiny():
     assert b.fit(y).shape == (3, 0)
     y = torch.tensor([[2.5], [-1.0]], dtype=torch.float64, device="cuda")
     assert torch.equal(b.fit(y), y)
+
+
+@pytest.mark.parametrize("n", [1000, 2048, 20001, 70000])
+def test_one_element_blocks_output_their_y(n):
+    """A block of one element gets its y, its exact mean: on a ramp through zero from -1e20 to 1e20,
+    where the diagram's coordinates are twenty orders of magnitude above the elements near zero,
+    and on a noisy trend, whose long rows are chunks of both storage forms with one-element blocks
+    inside them and at their ends; short rows, both directions, both dtypes."""
+    for dtype in (np.float32, np.float64):
+        y = np.linspace(-1e20, 1e20, n).astype(dtype)[None, :]
+        z, bs, rf = gpu_fit(y, None)
+        assert bs.all()
+        np.testing.assert_array_equal(z, y)
+        rng = np.random.default_rng(n)
+        base = (np.arange(n) * 1e-3 + 1e-3 * rng.standard_normal((4, n))).astype(dtype)
+        w2 = rng.uniform(0.5, 2.0, (4, n)).astype(dtype)
+        for dec in (False, True):
+            y2 = -base if dec else base  # a noisy trend in the fitted direction: blocks of all sizes
+            z2, bs2, _ = gpu_fit(y2, w2, decreasing=dec)
+            ends = np.concatenate([bs2[:, 1:], np.ones((4, 1), dtype=bs2.dtype)], axis=1)
+            one = (bs2 == 1) & (ends == 1)
+            assert one.sum() > 0
+            np.testing.assert_array_equal(z2[one], y2[one])

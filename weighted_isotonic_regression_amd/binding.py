@@ -31,6 +31,9 @@ _SIGS = {
     "iso_fit_ex": ([_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, ctypes.c_size_t, ctypes.c_uint, _P],
                    ctypes.c_int),
     "iso_vjp": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
+    "iso_fit_ragged": ([_P, _P, _P, _I64, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_uint, _P],
+                       ctypes.c_int),
+    "iso_ragged_workspace_bytes": ([_P, _I64, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
     "iso_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "iso_prof_enable": ([ctypes.c_int], ctypes.c_int),
     "iso_prof_read": ([_P, _P, _P], ctypes.c_int),
@@ -82,6 +85,15 @@ def iso_fit_ex(y, w, z, block_start, row_flags, batch, n, dtype, ws, ws_bytes, f
 
 def iso_vjp(g, y, w, z, block_start, gy, gw, batch, n, dtype, stream):
     return load().iso_vjp(g, y, w, z, block_start, gy, gw, batch, n, dtype, stream)
+
+
+def iso_fit_ragged(values, weights, offsets, batch, dtype, z, block_start, row_flags, ws, ws_bytes, flags, stream):
+    return load().iso_fit_ragged(values, weights, offsets, batch, dtype, z, block_start, row_flags, ws, ws_bytes,
+                                 flags, stream)
+
+
+def iso_ragged_workspace_bytes(offsets, batch, dtype, weighted):
+    return load().iso_ragged_workspace_bytes(offsets, batch, dtype, int(bool(weighted)))
 
 
 def iso_strerror(code):
@@ -186,6 +198,52 @@ def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, 
     res = [z]
     if block_starts:
         res.append(bs.reshape(y.shape))
+    if row_flags:
+        res.append(rf)
+    return tuple(res)
+
+
+def fit_ragged(values, offsets, weights=None, *, decreasing=False, block_starts=False, row_flags=False,
+               check_weights=False):
+    """Fit rows of unequal lengths laid end to end: row r is values[offsets[r]:offsets[r + 1]].
+
+    values, weights: 1-D float32/float64 CUDA tensors (weights may be None); offsets: batch + 1
+    non-decreasing integers on the host (a list, numpy array or CPU tensor).  Returns z (same
+    layout as values), or (z, block_start[uint8], row_flags[int32]) as requested.
+    """
+    import numpy as np
+
+    torch = _torch()
+    if values.dim() != 1 or not values.is_cuda or not values.is_contiguous():
+        raise ValueError("values must be a contiguous 1-D tensor on the GPU")
+    code = _dtype_code(torch, values)
+    if weights is not None and (weights.shape != values.shape or weights.dtype != values.dtype or
+                                weights.device != values.device or not weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous tensor of values' shape, dtype and device")
+    offs = np.ascontiguousarray(np.asarray(offsets.cpu() if hasattr(offsets, "cpu") else offsets, dtype=np.int64))
+    batch = offs.size - 1
+    if batch < 0 or (batch > 0 and offs[-1] > values.numel()):
+        raise ValueError("offsets must hold batch + 1 entries within values")
+    op = offs.ctypes.data_as(ctypes.c_void_p)
+    z = torch.empty_like(values)
+    bs = torch.empty(values.shape, dtype=torch.uint8, device=values.device) if block_starts else None
+    rf = torch.empty((max(batch, 0),), dtype=torch.int32, device=values.device) if row_flags else None
+    nbytes = iso_ragged_workspace_bytes(op, batch, code, weights is not None)
+    ws = None
+    if nbytes:
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=values.device)
+        shift = (-buf.data_ptr()) % 256
+        ws = buf[shift:shift + nbytes]
+    flags = (ISO_FLAG_CHECK_WEIGHTS if check_weights else 0) | (ISO_FLAG_DECREASING if decreasing else 0)
+    rc = iso_fit_ragged(_ptr(values), _ptr(weights), op, batch, code, _ptr(z), _ptr(bs), _ptr(rf), _ptr(ws), nbytes,
+                        flags, _stream(torch, values.device))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_fit_ragged")
+    if not block_starts and not row_flags:
+        return z
+    res = [z]
+    if block_starts:
+        res.append(bs)
     if row_flags:
         res.append(rf)
     return tuple(res)

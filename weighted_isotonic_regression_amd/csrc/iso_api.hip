@@ -7,10 +7,13 @@
 //               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls),
 //               k_scan_reduce + k_scan_apply (chunk starts),
 //               ceil(log2 m) launches of k_merge_wave, k_ends, k_fit (Section 3.3 and 3.4).
+// Rows of unequal lengths (iso_fit_ragged) are bucketed by length, padded into a rectangular
+// buffer per bucket (iso_ragged.h) and fitted by the paths above.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/iso.h"
@@ -18,6 +21,7 @@
 #include "iso_kernels.h"
 #include "iso_chunk.h"
 #include "iso_merge.h"
+#include "iso_ragged.h"
 
 static_assert(iso::ISO_ROW_NONFINITE_BIT == ISO_ROW_NONFINITE, "flag bits");
 static_assert(iso::ISO_ROW_BAD_WEIGHT_BIT == ISO_ROW_BAD_WEIGHT, "flag bits");
@@ -259,6 +263,123 @@ int dispatch_fit(const void* y, const void* w, void* z, uint8_t* bstart, uint32_
   return run_fit<T, false, D>((const T*)y, nullptr, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
 }
 
+// ---- rows of unequal lengths (iso_ragged.h)
+// Rows are bucketed by ceil(log2 length), so a bucket's padded stride L is under twice any of its
+// rows' lengths (rounded up to 16 bytes so padded rows stay aligned).  Buckets run one after the
+// other on the stream and share one region of the workspace.
+struct RagRegion {
+  size_t o_y = 0, o_w = 0, o_z = 0, o_b = 0, o_f = 0, o_keys = 0, o_ws = 0, total = 0;
+  Layout fit;
+};
+
+RagRegion rag_region(int64_t c, int64_t L, size_t esz, bool weighted) {
+  RagRegion R;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t e = (size_t)c * (size_t)L;
+  R.o_y = take(e * esz);
+  R.o_w = weighted ? take(e * esz) : 0;
+  R.o_z = take(e * esz);
+  R.o_b = take(e);
+  R.o_f = take((size_t)c * sizeof(uint32_t));
+  R.o_keys = take((size_t)c * sizeof(uint64_t));
+  R.fit = make_layout(c, L);
+  R.o_ws = take(R.fit.total);
+  R.total = off;
+  return R;
+}
+
+struct RagPlan {
+  struct Bucket {
+    int64_t first, c, L;
+  };
+  std::vector<int64_t> rows;  // the buckets' rows, bucket after bucket
+  std::vector<Bucket> buckets;
+  size_t o_plan = 0, o_rf = 0, o_any = 0, o_region = 0, total = 0;
+};
+
+// Validates the host offsets and plans the buckets.  Returns ISO_OK or ISO_EINVAL.
+int rag_plan(const int64_t* offs, int64_t batch, int dtype, bool weighted, RagPlan& P) {
+  if (batch < 0 || (dtype != ISO_F32 && dtype != ISO_F64)) return ISO_EINVAL;
+  if (batch > (int64_t)INT32_MAX) return ISO_EINVAL;
+  if (batch == 0) return ISO_OK;
+  if (!offs || offs[0] < 0) return ISO_EINVAL;
+  const size_t esz = dtype == ISO_F64 ? 8 : 4;
+  const int64_t align = (int64_t)(16 / esz);
+  std::vector<std::vector<int64_t>> by(64);
+  for (int64_t r = 0; r < batch; ++r) {
+    const int64_t len = offs[r + 1] - offs[r];
+    if (len < 0 || offs[r + 1] > INT64_MAX / 16) return ISO_EINVAL;
+    if (len == 0) continue;
+    const int k = len == 1 ? 0 : 64 - __builtin_clzll((unsigned long long)(len - 1));
+    by[k].push_back(r);
+  }
+  size_t region = 0;
+  for (int k = 0; k < 64; ++k) {
+    if (by[k].empty()) continue;
+    int64_t L = 0;
+    for (int64_t r : by[k]) L = std::max(L, offs[r + 1] - offs[r]);
+    L = (L + align - 1) / align * align;
+    const int64_t c = (int64_t)by[k].size();
+    if (!shape_ok(c, L, dtype)) return ISO_EINVAL;
+    const int64_t tiles = (L + kRagTile - 1) / kRagTile;
+    if (c > (int64_t)INT32_MAX / tiles) return ISO_EINVAL;  // one launch block per tile
+    P.buckets.push_back({(int64_t)P.rows.size(), c, L});
+    P.rows.insert(P.rows.end(), by[k].begin(), by[k].end());
+    region = std::max(region, rag_region(c, L, esz, weighted).total);
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  P.o_plan = take(((size_t)batch + 1 + P.rows.size()) * sizeof(int64_t));  // offsets, then rows
+  P.o_rf = take((size_t)batch * sizeof(uint32_t));
+  P.o_any = take(sizeof(uint32_t));
+  P.o_region = take(region);
+  P.total = off;
+  return ISO_OK;
+}
+
+template <typename T, bool D>
+int run_ragged(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rf, const RagPlan& P,
+               const int64_t* offs_dev, const int64_t* rows_dev, char* ws, hipStream_t s) {
+  const size_t esz = sizeof(T);
+  for (const RagPlan::Bucket& b : P.buckets) {
+    const RagRegion R = rag_region(b.c, b.L, esz, w != nullptr);
+    char* base = ws + P.o_region;
+    T* yp = (T*)(base + R.o_y);
+    T* wp = w ? (T*)(base + R.o_w) : nullptr;
+    T* zp = (T*)(base + R.o_z);
+    uint8_t* bp = (uint8_t*)(base + R.o_b);
+    uint32_t* fp = (uint32_t*)(base + R.o_f);
+    uint64_t* keys = (uint64_t*)(base + R.o_keys);
+    RagBucket B{offs_dev, rows_dev + b.first, b.c, b.L, (b.L + kRagTile - 1) / kRagTile};
+    const unsigned grid = (unsigned)(b.c * B.tiles);
+    hipLaunchKernelGGL(k_rag_init, dim3((unsigned)((b.c + kRagThreads - 1) / kRagThreads)), dim3(kRagThreads), 0,
+                       s, keys, b.c, D ? 1 : 0);
+    hipLaunchKernelGGL((k_rag_extreme<T, D>), dim3(grid), dim3(kRagThreads), 0, s, y, B, keys);
+    if (w)
+      hipLaunchKernelGGL((k_rag_pack<T, true, D>), dim3(grid), dim3(kRagThreads), 0, s, y, w, B,
+                         (const uint64_t*)keys, yp, wp);
+    else
+      hipLaunchKernelGGL((k_rag_pack<T, false, D>), dim3(grid), dim3(kRagThreads), 0, s, y, w, B,
+                         (const uint64_t*)keys, yp, wp);
+    if (hipGetLastError() != hipSuccess) return ISO_EHIP;
+    const int rc = dispatch_fit<T, D>(yp, wp, zp, bp, fp, b.c, b.L, base + R.o_ws, R.fit, s);
+    if (rc != ISO_OK) return rc;
+    hipLaunchKernelGGL((k_rag_unpack<T>), dim3(grid), dim3(kRagThreads), 0, s, (const T*)zp,
+                       (const uint8_t*)bp, (const uint32_t*)fp, B, z, bstart, rf);
+    if (hipGetLastError() != hipSuccess) return ISO_EHIP;
+  }
+  return ISO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,6 +539,68 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
   int rc = hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
   if (hipFreeAsync(buf, s) != hipSuccess && rc == ISO_OK) rc = ISO_EHIP;
   return rc;
+}
+
+size_t iso_ragged_workspace_bytes(const int64_t* offsets, int64_t batch, int dtype, int weighted) {
+  RagPlan P;
+  if (rag_plan(offsets, batch, dtype, weighted != 0, P) != ISO_OK) return 0;
+  return P.total;
+}
+
+int iso_fit_ragged(const void* values, const void* weights, const int64_t* offsets, int64_t batch,
+                   int dtype, void* z, uint8_t* block_start, uint32_t* row_flags, void* ws,
+                   size_t ws_bytes, unsigned flags, void* stream) {
+  if (flags & ~(unsigned)(ISO_FLAG_CHECK_WEIGHTS | ISO_FLAG_DECREASING)) return ISO_EINVAL;
+  RagPlan P;
+  const int prc = rag_plan(offsets, batch, dtype, weights != nullptr, P);
+  if (prc != ISO_OK) return prc;
+  if (batch == 0) return ISO_OK;
+  const size_t esz = dtype == ISO_F64 ? 8 : 4;
+  const size_t nel = (size_t)offsets[batch];
+  if (nel > 0 && (!values || !z)) return ISO_EINVAL;
+  if (overlaps(z, nel * esz, values, nel * esz) || overlaps(z, nel * esz, weights, nel * esz)) return ISO_EINVAL;
+  if (overlaps(block_start, nel, z, nel * esz)) return ISO_EINVAL;
+  if (!ws || ws_bytes < P.total || ((uintptr_t)ws % kAlign) != 0) return ISO_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  // the plan (offsets, then the bucket rows) goes up in one copy; the call waits for it so that
+  // no host memory is referenced after it returns
+  std::vector<int64_t> plan((size_t)batch + 1 + P.rows.size());
+  memcpy(plan.data(), offsets, ((size_t)batch + 1) * sizeof(int64_t));
+  if (!P.rows.empty()) memcpy(plan.data() + batch + 1, P.rows.data(), P.rows.size() * sizeof(int64_t));
+  if (hipMemcpyAsync(wsb + P.o_plan, plan.data(), plan.size() * sizeof(int64_t), hipMemcpyHostToDevice, s) !=
+      hipSuccess)
+    return ISO_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return ISO_EHIP;
+  const int64_t* offs_dev = (const int64_t*)(wsb + P.o_plan);
+  const int64_t* rows_dev = offs_dev + batch + 1;
+  uint32_t* rf = row_flags ? row_flags : (uint32_t*)(wsb + P.o_rf);
+  hipLaunchKernelGGL(k_rag_clear_flags, dim3((unsigned)((batch + kRagThreads - 1) / kRagThreads)), dim3(kRagThreads),
+                     0, s, rf, batch);
+  if (hipGetLastError() != hipSuccess) return ISO_EHIP;
+  const bool dec = (flags & ISO_FLAG_DECREASING) != 0;
+  int rc;
+  if (dtype == ISO_F64)
+    rc = dec ? run_ragged<double, true>((const double*)values, (const double*)weights, (double*)z, block_start, rf, P,
+                                        offs_dev, rows_dev, wsb, s)
+             : run_ragged<double, false>((const double*)values, (const double*)weights, (double*)z, block_start, rf, P,
+                                         offs_dev, rows_dev, wsb, s);
+  else
+    rc = dec ? run_ragged<float, true>((const float*)values, (const float*)weights, (float*)z, block_start, rf, P,
+                                       offs_dev, rows_dev, wsb, s)
+             : run_ragged<float, false>((const float*)values, (const float*)weights, (float*)z, block_start, rf, P,
+                                        offs_dev, rows_dev, wsb, s);
+  if (rc != ISO_OK) return rc;
+  if (flags & ISO_FLAG_CHECK_WEIGHTS) {
+    uint32_t* any = (uint32_t*)(wsb + P.o_any);
+    hipLaunchKernelGGL(k_flags_any, dim3(1), dim3(256), 0, s, (const uint32_t*)rf, batch, any);
+    if (hipGetLastError() != hipSuccess) return ISO_EHIP;
+    uint32_t host = 0;
+    if (hipMemcpyAsync(&host, any, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return ISO_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return ISO_EHIP;
+    if (host & ISO_ROW_BAD_WEIGHT) return ISO_EWEIGHT;
+  }
+  return ISO_OK;
 }
 
 }  // extern "C"

@@ -306,9 +306,11 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   // ---- a5: emit.
   {
     // Element-parallel: element e (row r, index i) gets the slope of the tile hull's edge over
-    // it, from the vertex at or before point i to the vertex after it.  Consecutive lanes write
-    // consecutive elements.
+    // it, from the vertex at or before point i to the vertex after it; an element whose two
+    // points are both vertices is a block of its own and gets its y, the block's exact mean.
+    // Consecutive lanes write consecutive elements.
     for (int e = lane; e < E; e += kWave) {
+      const T ye = y[off + e];  // issued first, so its latency overlaps the mask and LDS reads
       const int r = small_div(e, seglen, inv_seg);
       const int i = e - r * seglen;
       const uint32_t* Mr = &sM[r * maskStride];
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
       Pr(b, bx, by);
       const bool bad = sF[r] != 0u;
       const double slope = (by - ay) / (bx - ax);
-      z[off + e] = bad ? (T)NAN : (T)zval<D>(slope);
+      z[off + e] = bad ? (T)NAN : (isv && b == i + 1) ? ye : (T)zval<D>(slope);
       if (bstart) bstart[off + e] = (!bad && isv) ? 1 : 0;
     }
     if (rowOK && ql == 0 && rflags) rflags[row0 + r2] = sF[r2];
@@ -502,7 +504,13 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     }
     return;
   }
-  const T zin = (T)zval<D>(e.sin), zout = (T)zval<D>(e.sout);
+  // one-element blocks at the chunk's ends get their y: element 0 when P_0 is a vertex and P_1
+  // the chunk's first surviving vertex, element len - 1 when P_{len-1} is the last surviving
+  // vertex and P_len a vertex (the row's end, or the next chunk's point 0)
+  const bool one_in = e.klo == 1 && e.p0v;
+  const bool one_out = e.khi == len - 1 && (j + 1 == S.m || ends[g + 1].p0v);
+  const T zin = one_in ? S.y[off] : (T)zval<D>(e.sin);
+  const T zout = one_out ? S.y[off + len - 1] : (T)zval<D>(e.sout);
   if (S.dense[g] == 2 && e.khi == len && (e.klo == 0 || (e.klo == 1 && e.p0v))) {
     // every point of the chunk is a vertex of the chunk hull, and all of them are vertices of the
     // row's hull (point 0 possibly as the previous chunk's last vertex): every element is its own
@@ -563,21 +571,27 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     return;
   }
   // list form: stage the surviving vertices' point indices and the slopes of the edges between
+  // them (a one-element edge's slope is its element's y, the block's exact mean)
   const int nv = e.hi - e.lo + 1;
   const int64_t lb = g * (int64_t)kListCap + e.lo;
   for (int q = tid; q < nv; q += kFitThreads) {
-    sK[q] = S.lk[lb + q];
-    if (q + 1 < nv) sSlope[q] = (S.ly[lb + q + 1] - S.ly[lb + q]) / (S.lx[lb + q + 1] - S.lx[lb + q]);
+    const int k0 = S.lk[lb + q];
+    sK[q] = k0;
+    if (q + 1 < nv) {
+      const int k1 = S.lk[lb + q + 1];
+      sSlope[q] = k1 == k0 + 1 ? yval<D>(S.y[off + k0])
+                               : (S.ly[lb + q + 1] - S.ly[lb + q]) / (S.lx[lb + q + 1] - S.lx[lb + q]);
+    }
   }
   __syncthreads();
   for (int i = tid; i < len; i += kFitThreads) {
     double zv;
     uint8_t st = 0;
     if (i < e.klo) {
-      zv = e.sin;
+      zv = one_in ? yval<D>(S.y[off]) : e.sin;
       st = (i == 0 && e.p0v) ? 1 : 0;
     } else if (i >= e.khi) {
-      zv = e.sout;
+      zv = one_out ? yval<D>(S.y[off + i]) : e.sout;
       st = (i == e.khi) ? 1 : 0;
     } else {
       int lo = 0, hi = nv - 2;  // edge q covers [sK[q], sK[q + 1])
