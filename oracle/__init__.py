@@ -11,6 +11,9 @@ Contents
 ``exact``          exact-rational characterisations used to pin ``pav``: the max-min
                    block-average formula, the explicit lower convex hull of the cumulative
                    sum diagram, and the KKT certificate.
+``softrank``       the soft rank (projection onto the permutahedron) and its backward, built
+                   on ``pav`` and ``vjp``.
 """
 from .native import build, pav, vjp, ORACLE_FLAG_NONFINITE, ORACLE_FLAG_WEIGHT  # noqa: F401
 from . import exact  # noqa: F401
+from . import softrank  # noqa: F401
