@@ -319,6 +319,9 @@ def run_only(args, torch, B, W, dev):
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
+    if args.only == "softrank":
+        print(json.dumps({"workload": "softrank", **time_soft_rank(torch, B, dev)}), flush=True)
+        return
     if args.only == "vjp":
         _, _, y, w = load_workload(torch, W, "mixed", dev)
         print(json.dumps({"workload": "vjp", **time_vjp(torch, B, y, w, dev, args.steps)}), flush=True)
@@ -377,7 +380,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
     ap.add_argument("--configs", action="store_true", help="measure every configuration, one JSON line each")
-    ap.add_argument("--only", choices=sorted(ONLY) + ["vjp"], default=None,
+    ap.add_argument("--only", choices=sorted(ONLY) + ["vjp", "softrank"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="with --only: first run a 1 GiB device copy (memory-counter calibration)")
@@ -517,7 +520,38 @@ def main():
                                 "stage_ms": stage_line(dms, dc),
                                 "roofline": roofline_of("dense_1e8_f64", dms, dla, dc, nd, 8, True, True, traffic),
                                 "max_deviation_vs_y": dev_y}
+        out["soft_rank_f32"] = time_soft_rank(torch, B, dev)
     print(json.dumps(out), flush=True)
+
+
+def time_soft_rank(torch, B, dev, reps=20):
+    """The soft rank at the page's training-step shapes (Section 7.9, Table 6: standard normal
+    values, eps = 1/n, fp32): median ms of the forward alone and of forward plus backward, each
+    call bracketed by HIP events on the launch stream."""
+    import numpy as np
+
+    print("bench: timing the soft rank", file=sys.stderr, flush=True)
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    for batch, n in ((256, 1000), (4, 100_000)):
+        x = torch.from_numpy(np.random.default_rng(12).standard_normal((batch, n)).astype(np.float32)).to(dev)
+        g = torch.from_numpy(np.random.default_rng(13).standard_normal((batch, n)).astype(np.float32)).to(dev)
+        eps = 1.0 / n
+        fwd, both = [], []
+        for k in range(reps + 3):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            r, perm, bs = B.soft_rank(x, eps)
+            e1.record(stream)
+            B.soft_rank_vjp(g, perm, bs, eps)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            if k >= 3:
+                fwd.append(e0.elapsed_time(e1))
+                both.append(e0.elapsed_time(e2))
+        res["%dx%d" % (batch, n)] = {"eps": eps, "forward_ms": round(float(np.median(fwd)), 4),
+                                     "forward_backward_ms": round(float(np.median(both)), 4)}
+    return res
 
 
 if __name__ == "__main__":

@@ -160,6 +160,41 @@ int iso_fit_ragged(const void* values, const void* weights, const int64_t* offse
  */
 size_t iso_ragged_workspace_bytes(const int64_t* offsets, int64_t batch, int dtype, int weighted);
 
+/*
+ * iso_soft_rank -- the soft rank with L2 regularization of every row ("Merge Hulls Without Copying
+ * Vertices", Section 7.9, after Blondel et al.): the projection of theta = x / eps onto the
+ * permutahedron of w = (n, ..., 1).  Per row, theta is sorted in decreasing order into s, the
+ * decreasing isotonic regression v of z = s - w (unit weights) is fitted, and r = s - v is
+ * returned in the original order.  z is rounded to the input type, the fit runs in fp64, and each
+ * r is rounded once.  Small eps gives the hard ranks (n for the largest element); large eps pools
+ * each row into one block.
+ *   x            [batch, n] values (device)
+ *   eps          regularization strength, finite and > 0
+ *   r            [batch, n] output soft ranks (device; must not overlap x)
+ *   perm         [batch, n] uint32 output (device): perm[i * n + k] is the flat index of row i's
+ *                k-th largest element (ties keep their order).  Needed by iso_soft_rank_vjp.
+ *   block_start  [batch, n] bytes or NULL (device): the fit's block starts, in sorted order.
+ *                Needed by iso_soft_rank_vjp.
+ *   row_flags    [batch] uint32 or NULL (device): ISO_ROW_NONFINITE for a row holding a non-finite
+ *                value (its r is all NaN)
+ * batch * n must be below 2^32.  Scratch memory (about 40 bytes per element) comes from the
+ * stream-ordered allocator.  Returns ISO_OK, ISO_EINVAL, ISO_ENOMEM or ISO_EHIP.
+ */
+int iso_soft_rank(const void* x, int64_t batch, int64_t n, int dtype, double eps, void* r,
+                  uint32_t* perm, uint8_t* block_start, uint32_t* row_flags, void* stream);
+
+/*
+ * iso_soft_rank_vjp -- backward of iso_soft_rank: with g the cotangent of r, writes the cotangent
+ * of x, grad = (u - A u) / eps in the original order, where u is g in sorted order and A averages
+ * over the fit's blocks (Section 6, Gradient, with unit weights).
+ *   g, grad      [batch, n] (device; grad must not overlap g or perm)
+ *   perm, block_start  as written by the iso_soft_rank call of the same x and eps
+ * Scratch memory (16 bytes per element and the backward's own) comes from the stream-ordered
+ * allocator.  Returns ISO_OK, ISO_EINVAL, ISO_ENOMEM or ISO_EHIP.
+ */
+int iso_soft_rank_vjp(const void* g, const uint32_t* perm, const uint8_t* block_start, int64_t batch,
+                      int64_t n, int dtype, double eps, void* grad, void* stream);
+
 /* iso_strerror -- static description of a return code. */
 const char* iso_strerror(int code);
 

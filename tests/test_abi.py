@@ -39,7 +39,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     assert set(_declared()) == {"iso_fit", "iso_workspace_bytes", "iso_fit_ex", "iso_vjp", "iso_strerror",
-                                "iso_fit_ragged", "iso_ragged_workspace_bytes"}
+                                "iso_fit_ragged", "iso_ragged_workspace_bytes", "iso_soft_rank",
+                                "iso_soft_rank_vjp"}
     names = _declared(HEADERS)
     out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True,
                          check=True).stdout
@@ -172,3 +173,25 @@ def test_ragged_workspace_sizes(lib):
     big = rw(offs, 3, 1, 1)
     one = binding.iso_workspace_bytes(1, 200000, 1, 1)
     assert one + 200000 * (3 * 8 + 1) <= big < one + 200000 * (3 * 8 + 1) + 2 * 2 ** 20
+
+
+def test_soft_rank_argument_errors_before_any_launch(lib):
+    sr, sv = binding.iso_soft_rank, binding.iso_soft_rank_vjp
+    EINVAL, OK = binding.ISO_EINVAL, binding.ISO_OK
+    PERM, BS = P(1 << 40), P(1 << 41)
+    assert sr(Y, 2, 10, 0, 0.0, Z, PERM, BS, None, None) == EINVAL                 # eps = 0
+    assert sr(Y, 2, 10, 0, -1.0, Z, PERM, BS, None, None) == EINVAL                # eps < 0
+    assert sr(Y, 2, 10, 0, float("inf"), Z, PERM, BS, None, None) == EINVAL        # eps infinite
+    assert sr(Y, 2, 10, 0, float("nan"), Z, PERM, BS, None, None) == EINVAL        # eps NaN
+    assert sr(Y, 2, 10, 9, 1.0, Z, PERM, BS, None, None) == EINVAL                 # bad dtype
+    assert sr(None, 2, 10, 0, 1.0, Z, PERM, BS, None, None) == EINVAL              # x NULL
+    assert sr(Y, 2, 10, 0, 1.0, None, PERM, BS, None, None) == EINVAL              # r NULL
+    assert sr(Y, 2, 10, 0, 1.0, Z, None, BS, None, None) == EINVAL                 # perm NULL
+    assert sr(Y, 2, 10, 0, 1.0, Y, PERM, BS, None, None) == EINVAL                 # r aliases x
+    assert sr(Y, 2, 10, 0, 1.0, Z, P(Z.value + 4), BS, None, None) == EINVAL       # perm overlaps r
+    assert sr(Y, 1 << 20, 1 << 13, 0, 1.0, Z, PERM, BS, None, None) == EINVAL      # 2^33 elements
+    assert sr(Y, 0, 10, 0, 1.0, Z, PERM, BS, None, None) == OK                     # empty
+    assert sv(Y, PERM, BS, 2, 10, 0, 0.0, Z, None) == EINVAL                       # eps = 0
+    assert sv(Y, PERM, None, 2, 10, 0, 1.0, Z, None) == EINVAL                     # no block starts
+    assert sv(Y, PERM, BS, 2, 10, 0, 1.0, Y, None) == EINVAL                       # grad aliases g
+    assert sv(Y, PERM, BS, 2, 0, 0, 1.0, Z, None) == OK                            # empty

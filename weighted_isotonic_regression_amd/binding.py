@@ -34,6 +34,8 @@ _SIGS = {
     "iso_fit_ragged": ([_P, _P, _P, _I64, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_uint, _P],
                        ctypes.c_int),
     "iso_ragged_workspace_bytes": ([_P, _I64, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
+    "iso_soft_rank": ([_P, _I64, _I64, ctypes.c_int, ctypes.c_double, _P, _P, _P, _P, _P], ctypes.c_int),
+    "iso_soft_rank_vjp": ([_P, _P, _P, _I64, _I64, ctypes.c_int, ctypes.c_double, _P, _P], ctypes.c_int),
     "iso_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "iso_prof_enable": ([ctypes.c_int], ctypes.c_int),
     "iso_prof_read": ([_P, _P, _P], ctypes.c_int),
@@ -94,6 +96,14 @@ def iso_fit_ragged(values, weights, offsets, batch, dtype, z, block_start, row_f
 
 def iso_ragged_workspace_bytes(offsets, batch, dtype, weighted):
     return load().iso_ragged_workspace_bytes(offsets, batch, dtype, int(bool(weighted)))
+
+
+def iso_soft_rank(x, batch, n, dtype, eps, r, perm, block_start, row_flags, stream):
+    return load().iso_soft_rank(x, batch, n, dtype, eps, r, perm, block_start, row_flags, stream)
+
+
+def iso_soft_rank_vjp(g, perm, block_start, batch, n, dtype, eps, grad, stream):
+    return load().iso_soft_rank_vjp(g, perm, block_start, batch, n, dtype, eps, grad, stream)
 
 
 def iso_strerror(code):
@@ -247,6 +257,70 @@ def fit_ragged(values, offsets, weights=None, *, decreasing=False, block_starts=
     if row_flags:
         res.append(rf)
     return tuple(res)
+
+
+def soft_rank(x, eps, *, row_flags=False):
+    """Soft ranks of every row of x (float32/float64 CUDA tensor [n] or [batch, n]) with L2
+    regularization of strength eps.  Returns (r, perm, block_start) -- perm (int32 tensor holding
+    the uint32 sort permutation) and block_start are what soft_rank_vjp needs -- and the per-row
+    flags too when row_flags is set."""
+    torch = _torch()
+    x2 = _as_rows(x)
+    if not x2.is_cuda or not x2.is_contiguous():
+        raise ValueError("x must be a contiguous tensor on the GPU")
+    code = _dtype_code(torch, x2)
+    batch, n = x2.shape
+    r = torch.empty_like(x2)
+    perm = torch.empty((batch, n), dtype=torch.int32, device=x2.device)
+    bs = torch.empty((batch, n), dtype=torch.uint8, device=x2.device)
+    rf = torch.empty((batch,), dtype=torch.int32, device=x2.device) if row_flags else None
+    rc = iso_soft_rank(_ptr(x2), batch, n, code, float(eps), _ptr(r), _ptr(perm), _ptr(bs), _ptr(rf),
+                       _stream(torch, x2.device))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_soft_rank")
+    res = (r.reshape(x.shape), perm, bs)
+    return res + (rf,) if row_flags else res
+
+
+def soft_rank_vjp(g, perm, block_start, eps):
+    """Cotangent of x for the cotangent g of soft_rank's r."""
+    torch = _torch()
+    g2 = _as_rows(g)
+    code = _dtype_code(torch, g2)
+    batch, n = g2.shape
+    if perm.shape != (batch, n) or block_start.shape != (batch, n) or not g2.is_contiguous():
+        raise ValueError("perm and block_start must come from soft_rank of x of g's shape")
+    grad = torch.empty_like(g2)
+    rc = iso_soft_rank_vjp(_ptr(g2), _ptr(perm), _ptr(block_start), batch, n, code, float(eps), _ptr(grad),
+                           _stream(torch, g2.device))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_soft_rank_vjp")
+    return grad.reshape(g.shape)
+
+
+_SoftRankFn = None
+
+
+def soft_rank_fn(x, eps):
+    """Differentiable soft rank: a torch.autograd.Function over soft_rank and soft_rank_vjp."""
+    global _SoftRankFn
+    torch = _torch()
+    if _SoftRankFn is None:
+        class SoftRankFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, xx, e):
+                r, perm, bs = soft_rank(xx.contiguous(), e)
+                ctx.save_for_backward(perm, bs)
+                ctx.eps = e
+                return r
+
+            @staticmethod
+            def backward(ctx, g):
+                perm, bs = ctx.saved_tensors
+                return soft_rank_vjp(g.contiguous(), perm, bs, ctx.eps), None
+
+        _SoftRankFn = SoftRankFn
+    return _SoftRankFn.apply(x, eps)
 
 
 def vjp(g, y, w, z, block_start):

@@ -8,7 +8,8 @@
 //               k_scan_reduce + k_scan_apply (chunk starts),
 //               ceil(log2 m) launches of k_merge_wave, k_ends, k_fit (Section 3.3 and 3.4).
 // Rows of unequal lengths (iso_fit_ragged) are bucketed by length, padded into a rectangular
-// buffer per bucket (iso_ragged.h) and fitted by the paths above.
+// buffer per bucket (iso_ragged.h) and fitted by the paths above.  The soft rank (iso_soft_rank,
+// iso_softrank.h) sorts each row with rocPRIM's radix sort and fits the decreasing direction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -16,12 +17,16 @@
 #include <algorithm>
 #include <vector>
 
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/iterator/counting_iterator.hpp>
+
 #include "../../include/iso.h"
 #include "../../include/iso_profile.h"
 #include "iso_kernels.h"
 #include "iso_chunk.h"
 #include "iso_merge.h"
 #include "iso_ragged.h"
+#include "iso_softrank.h"
 
 static_assert(iso::ISO_ROW_NONFINITE_BIT == ISO_ROW_NONFINITE, "flag bits");
 static_assert(iso::ISO_ROW_BAD_WEIGHT_BIT == ISO_ROW_BAD_WEIGHT, "flag bits");
@@ -380,6 +385,119 @@ int run_ragged(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rf, cons
   return ISO_OK;
 }
 
+// ---- soft rank (iso_softrank.h)
+// Sorts every row's keys (decreasing value order) and leaves perm[r * n + k] = the flat index of
+// row r's k-th largest element: a stable radix sort of the value keys with the flat indices, then,
+// for more than one row, a stable radix sort of those indices by row.  With tmp == nullptr only
+// sets tmp_bytes.
+template <typename K>
+hipError_t sr_sort(K* keys, K* keys_sorted, uint32_t* idx, uint32_t* rk, uint32_t* rk_sorted, uint32_t* perm,
+                   int64_t batch, int64_t n, void* tmp, size_t& tmp_bytes, hipStream_t s) {
+  const size_t N = (size_t)(batch * n);
+  unsigned row_bits = 0;
+  while (row_bits < 32 && (1ull << row_bits) < (unsigned long long)batch) ++row_bits;
+  if (tmp == nullptr) {
+    size_t a = 0, b = 0;
+    hipError_t e = rocprim::radix_sort_pairs(nullptr, a, keys, keys_sorted, rocprim::counting_iterator<uint32_t>(0),
+                                             idx, N, 0, 8 * sizeof(K), s);
+    if (e != hipSuccess) return e;
+    if (batch > 1) {
+      e = rocprim::radix_sort_pairs(nullptr, b, rk, rk_sorted, idx, perm, N, 0, row_bits, s);
+      if (e != hipSuccess) return e;
+    }
+    tmp_bytes = std::max(a, b);
+    return hipSuccess;
+  }
+  hipError_t e = rocprim::radix_sort_pairs(tmp, tmp_bytes, keys, keys_sorted, rocprim::counting_iterator<uint32_t>(0),
+                                           batch > 1 ? idx : perm, N, 0, 8 * sizeof(K), s);
+  if (e != hipSuccess || batch == 1) return e;
+  hipLaunchKernelGGL(k_sr_rows, dim3((unsigned)((N + kSrThreads - 1) / kSrThreads)), dim3(kSrThreads), 0, s,
+                     (const uint32_t*)idx, (int64_t)N, n, rk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return rocprim::radix_sort_pairs(tmp, tmp_bytes, rk, rk_sorted, idx, perm, N, 0, row_bits, s);
+}
+
+struct SrBuffers {
+  size_t o_keys = 0, o_keys2 = 0, o_idx = 0, o_rk = 0, o_rk2 = 0, o_z = 0, o_v = 0, o_rf = 0, o_ws = 0, o_tmp = 0,
+         total = 0, tmp_bytes = 0;
+  Layout fit;
+};
+
+template <typename T, typename K>
+int run_soft_rank(const T* x, int64_t batch, int64_t n, double eps, T* r, uint32_t* perm, uint8_t* bstart,
+                  uint32_t* rflags, hipStream_t s) {
+  const int64_t N = batch * n;
+  SrBuffers B;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const bool device_sort = n > kSrRowMax;  // else one workgroup per row sorts in LDS
+  if (device_sort) {
+    B.o_keys = take(N * sizeof(K));
+    B.o_keys2 = take(N * sizeof(K));
+    B.o_idx = take(N * sizeof(uint32_t));
+    B.o_rk = take(N * sizeof(uint32_t));
+    B.o_rk2 = take(N * sizeof(uint32_t));
+  }
+  B.o_z = take(N * sizeof(double));
+  B.o_v = take(N * sizeof(double));
+  B.o_rf = take(batch * sizeof(uint32_t));
+  B.fit = make_layout(batch, n);
+  B.o_ws = take(B.fit.total);
+  if (device_sort) {
+    if (sr_sort<K>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, batch, n, nullptr, B.tmp_bytes, s) !=
+        hipSuccess)
+      return ISO_EHIP;
+    B.o_tmp = take(B.tmp_bytes);
+  }
+  B.total = off;
+  char* buf = nullptr;
+  if (hipMallocAsync((void**)&buf, B.total, s) != hipSuccess) return ISO_ENOMEM;
+  int rc = ISO_OK;
+  const unsigned grid = (unsigned)((N + kSrThreads - 1) / kSrThreads);
+  K* keys = (K*)(buf + B.o_keys);
+  double* z = (double*)(buf + B.o_z);
+  double* v = (double*)(buf + B.o_v);
+  if (!device_sort) {
+    // one workgroup sorts each row in LDS and writes perm and z
+    hipLaunchKernelGGL((k_sr_row_sort<T, K>), dim3((unsigned)batch), dim3(kSrThreads), 0, s, x, n, eps, perm, z);
+    if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+  } else {
+    hipLaunchKernelGGL((k_sr_keys<T, K>), dim3(grid), dim3(kSrThreads), 0, s, x, N, keys);
+    if (hipGetLastError() != hipSuccess ||
+        sr_sort<K>(keys, (K*)(buf + B.o_keys2), (uint32_t*)(buf + B.o_idx), (uint32_t*)(buf + B.o_rk),
+                   (uint32_t*)(buf + B.o_rk2), perm, batch, n, buf + B.o_tmp, B.tmp_bytes, s) != hipSuccess) {
+      rc = ISO_EHIP;
+    }
+    if (rc == ISO_OK) {
+      hipLaunchKernelGGL((k_sr_problem<T>), dim3(grid), dim3(kSrThreads), 0, s, x, (const uint32_t*)perm, N, n,
+                         eps, z);
+      if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+    }
+  }
+  if (rc == ISO_OK)
+    rc = dispatch_fit<double, true>(z, nullptr, v, bstart, rflags ? rflags : (uint32_t*)(buf + B.o_rf), batch, n,
+                                    buf + B.o_ws, B.fit, s);
+  if (rc == ISO_OK) {
+    hipLaunchKernelGGL((k_sr_combine<T>), dim3(grid), dim3(kSrThreads), 0, s, x, (const uint32_t*)perm,
+                       (const double*)v, N, eps, r);
+    if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+  }
+  if (hipFreeAsync(buf, s) != hipSuccess && rc == ISO_OK) rc = ISO_EHIP;
+  return rc;
+}
+
+bool sr_args_ok(int64_t batch, int64_t n, int dtype, double eps) {
+  if (!shape_ok(batch, n, dtype)) return false;
+  if (!(eps > 0.0) || !(eps < INFINITY)) return false;
+  if (batch > 0 && n > (int64_t)UINT32_MAX / batch) return false;  // flat indices are 32-bit
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -537,6 +655,60 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
                        (const double4*)cc, (float*)gy, (float*)gw, n, (int)ntile);
   }
   int rc = hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
+  if (hipFreeAsync(buf, s) != hipSuccess && rc == ISO_OK) rc = ISO_EHIP;
+  return rc;
+}
+
+int iso_soft_rank(const void* x, int64_t batch, int64_t n, int dtype, double eps, void* r, uint32_t* perm,
+                  uint8_t* block_start, uint32_t* row_flags, void* stream) {
+  if (!sr_args_ok(batch, n, dtype, eps)) return ISO_EINVAL;
+  if (batch == 0 || n == 0) return ISO_OK;
+  if (!x || !r || !perm) return ISO_EINVAL;
+  const size_t esz = dtype == ISO_F64 ? 8 : 4;
+  const size_t N = (size_t)(batch * n);
+  if (overlaps(r, N * esz, x, N * esz) || overlaps(perm, N * 4, x, N * esz) || overlaps(perm, N * 4, r, N * esz))
+    return ISO_EINVAL;
+  if (overlaps(block_start, N, r, N * esz) || overlaps(block_start, N, perm, N * 4)) return ISO_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == ISO_F64)
+    return run_soft_rank<double, uint64_t>((const double*)x, batch, n, eps, (double*)r, perm, block_start, row_flags,
+                                           s);
+  return run_soft_rank<float, uint32_t>((const float*)x, batch, n, eps, (float*)r, perm, block_start, row_flags, s);
+}
+
+int iso_soft_rank_vjp(const void* g, const uint32_t* perm, const uint8_t* block_start, int64_t batch, int64_t n,
+                      int dtype, double eps, void* grad, void* stream) {
+  if (!sr_args_ok(batch, n, dtype, eps)) return ISO_EINVAL;
+  if (batch == 0 || n == 0) return ISO_OK;
+  if (!g || !perm || !block_start || !grad) return ISO_EINVAL;
+  const size_t esz = dtype == ISO_F64 ? 8 : 4;
+  const int64_t N = batch * n;
+  if (overlaps(grad, (size_t)N * esz, g, (size_t)N * esz) || overlaps(grad, (size_t)N * esz, perm, (size_t)N * 4))
+    return ISO_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  double* buf = nullptr;
+  if (hipMallocAsync((void**)&buf, (size_t)N * 2 * sizeof(double), s) != hipSuccess) return ISO_ENOMEM;
+  double* u = buf;
+  double* au = buf + N;
+  const unsigned grid = (unsigned)((N + kSrThreads - 1) / kSrThreads);
+  int rc = ISO_OK;
+  if (dtype == ISO_F64)
+    hipLaunchKernelGGL((k_sr_gather<double>), dim3(grid), dim3(kSrThreads), 0, s, (const double*)g, perm, N, u);
+  else
+    hipLaunchKernelGGL((k_sr_gather<float>), dim3(grid), dim3(kSrThreads), 0, s, (const float*)g, perm, N, u);
+  if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+  // A u: the block averages of u over the fit's blocks (unit weights); y and z are not used
+  // without weights
+  if (rc == ISO_OK) rc = iso_vjp(u, u, nullptr, u, block_start, au, nullptr, batch, n, ISO_F64, stream);
+  if (rc == ISO_OK) {
+    if (dtype == ISO_F64)
+      hipLaunchKernelGGL((k_sr_grad<double>), dim3(grid), dim3(kSrThreads), 0, s, (const double*)u,
+                         (const double*)au, perm, N, eps, (double*)grad);
+    else
+      hipLaunchKernelGGL((k_sr_grad<float>), dim3(grid), dim3(kSrThreads), 0, s, (const double*)u,
+                         (const double*)au, perm, N, eps, (float*)grad);
+    if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+  }
   if (hipFreeAsync(buf, s) != hipSuccess && rc == ISO_OK) rc = ISO_EHIP;
   return rc;
 }
