@@ -343,6 +343,35 @@ struct VertexStore {
     yy = sy + ay;
   }
 
+  // Lane start (sx, sy) and lane-relative running sums (ax, ay) at point k (0 <= k < len) of
+  // dense chunk j: point k is (W ? sx + ax : k, sy + ay), with the operations of dense_point, so
+  // adding elements k, k + 1, ... to (ax, ay) in order gives dense_point's values of the points
+  // after k up to the next multiple of 32.
+  ISO_HD void dense_state(int64_t row, int j, int k, double& sx, double& sy, double& ax, double& ay) const {
+    const int64_t g = row * m + j;
+    const int l = k / kSub, q = k % kSub;
+    sx = W ? lsx[g * kWave + l] : (double)(kSub * l);
+    sy = lsy[g * kWave + l];
+    ax = 0.0;
+    ay = 0.0;
+    if (q == 0) return;
+    const int jj = q / kCk;
+    const int64_t cb = (g * kWave + l) * kLaneW + jj;
+    if (W) ax = ckx[cb];
+    ay = cky[cb];
+    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
+    for (int e = kCk * jj; e < q; ++e) {
+      double wd = W ? (double)w[e0 + e] : 1.0;
+      double yd = yval<D>(y[e0 + e]);
+      if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
+        yd = 0.0;
+        wd = 1.0;
+      }
+      if (W) ax += wd;
+      ay += wd * yd;
+    }
+  }
+
   // Chunk-relative coordinates and point index of vertex p of chunk j of `row`.
   ISO_HD void local(int64_t row, int j, int p, double& x, double& yy, int& k) const {
     const int64_t g = row * m + j;

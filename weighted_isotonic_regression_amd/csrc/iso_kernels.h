@@ -465,10 +465,12 @@ __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W, D> S, EndInfo* _
 // into and out of it; inside it they lie under the chunk hull's own edges (Corollary 4.5).
 //   list chunks:  the surviving vertices' point indices and the slopes between them are staged in
 //                 LDS and each element finds its edge by binary search.
-//   dense chunks: the chunk pass wrote z = y for load tiles in which nothing was popped; an
-//                 element there whose two points are both hull vertices is its own block and is
-//                 left alone.  Other elements get the slope of their edge, its end points
-//                 recomputed from the lane checkpoints (a one-element edge is the element's y).
+//   dense chunks: one thread walks each 32-element word once, carrying the lane's running sums
+//                 from the word's checkpoint, so every point it passes costs one element's loads;
+//                 at each vertex it writes the slope of the edge just closed to the elements
+//                 under it.  An edge coming from an earlier word or going on to a later one costs
+//                 one recomputation of that end point.  A one-element edge is its element's y,
+//                 which the chunk pass already wrote in tiles where nothing was popped.
 constexpr int kFitThreads = 256;
 
 template <typename T, bool W, bool D>
@@ -527,6 +529,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     __syncthreads();
     // one word (32 elements) per thread at a time: a word inside [klo, khi) whose points and the
     // next one are all vertices, in tiles whose z the chunk pass wrote, needs nothing
+    auto bit = [&](int i) { return ((sMask[i >> 5] >> (i & 31)) & 1u) != 0u; };
     const int nw = (len + 31) >> 5;
     for (int wd = tid; wd < nw; wd += kFitThreads) {
       const int i0 = wd << 5;
@@ -542,31 +545,70 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
           continue;
         }
       }
-      for (int i = i0; i < i1; ++i) {
-        if (i < e.klo) {
-          z[off + i] = zin;
-          if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
-          continue;
-        }
-        if (i >= e.khi) {
-          z[off + i] = zout;
-          if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
-          continue;
-        }
-        const bool vl = (sMask[i >> 5] >> (i & 31)) & 1u;
-        const bool vr = (sMask[(i + 1) >> 5] >> ((i + 1) & 31)) & 1u;
-        if (bstart) bstart[off + i] = vl ? 1 : 0;
-        if (vl && vr) {
-          if (!zall && !ztile[g * kZTiles + i / TN]) z[off + i] = S.y[off + i];
-          continue;
-        }
-        const int a = vl ? i : mask_pred(sMask, i);
-        const int b = mask_succ(sMask, i);
-        double ax, ay, bx, by;
-        S.dense_point(row, j, a, ax, ay);
-        S.dense_point(row, j, b, bx, by);
-        z[off + i] = (T)zval<D>((by - ay) / (bx - ax));
+      // elements before klo and from khi on lie under the edges into and out of the chunk
+      for (int i = i0; i < min(i1, e.klo); ++i) {
+        z[off + i] = zin;
+        if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
       }
+      for (int i = max(i0, e.khi); i < i1; ++i) {
+        z[off + i] = zout;
+        if (bstart) bstart[off + i] = (i == e.khi) ? 1 : 0;
+      }
+      const int a0 = max(i0, e.klo), a1 = min(i1, e.khi);
+      if (a0 >= a1) continue;
+      // the edge (pa, b) covers the elements pa .. b - 1; its slope goes to those of them from
+      // pend on (a one-element edge is its element's y, already written where its tile is marked)
+      auto close_edge = [&](int pend, int pa, double pax, double pay, int b, double bx, double by) {
+        if (b == pa + 1) {
+          if (!zall && !ztile[g * kZTiles + pa / TN]) z[off + pa] = S.y[off + pa];
+          return;
+        }
+        const T zv = (T)zval<D>((by - pay) / (bx - pax));
+        for (int i = pend; i < b; ++i) z[off + i] = zv;
+      };
+      double sx, sy, ax, ay;
+      S.dense_state(row, j, a0, sx, sy, ax, ay);
+      int pa, pend = a0;
+      double pax, pay;
+      if (bit(a0)) {
+        pa = a0;
+        pax = W ? sx + ax : (double)a0;
+        pay = sy + ay;
+      } else {
+        pa = mask_pred(sMask, a0);
+        S.dense_point(row, j, pa, pax, pay);
+      }
+      for (int i = a0; i < a1; ++i) {
+        double wd = W ? (double)S.w[off + i] : 1.0;
+        double yd = yval<D>(S.y[off + i]);
+        if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
+          yd = 0.0;
+          wd = 1.0;
+        }
+        if (bstart) bstart[off + i] = bit(i) ? 1 : 0;
+        if (W) ax += wd;
+        ay += wd * yd;
+        const int ni = i + 1;
+        if (ni < a1 && bit(ni)) {
+          const double bx = W ? sx + ax : (double)ni, by = sy + ay;
+          close_edge(pend, pa, pax, pay, ni, bx, by);
+          pa = ni;
+          pax = bx;
+          pay = by;
+          pend = ni;
+        }
+      }
+      // the elements left lie under the edge from pa to the first vertex at or after a1: point a1
+      // continues the walk unless it starts a word (a checkpoint) or ends the chunk
+      const int b = bit(a1) ? a1 : mask_succ(sMask, a1);
+      double bx, by;
+      if (b == a1 && (a1 & (kCk - 1)) != 0 && a1 != len) {
+        bx = W ? sx + ax : (double)a1;
+        by = sy + ay;
+      } else {
+        S.dense_point(row, j, b, bx, by);
+      }
+      close_edge(pend, pa, pax, pay, b, bx, by);
     }
     return;
   }
