@@ -277,3 +277,32 @@ def test_one_element_blocks_output_their_y(n):
             one = (bs2 == 1) & (ends == 1)
             assert one.sum() > 0
             np.testing.assert_array_equal(z2[one], y2[one])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_tiny_rows_every_length(dtype):
+    """Rows of 1 to 16 elements (one lane per row, pool adjacent violators): every length, with and
+    without weights, both directions, batches that do and do not fill the last wavefront, exact
+    partitions on integer rows."""
+    for n in range(1, 17):
+        for batch in (1, 63, 200):
+            y, w = W.family("noise", batch, n, seed=n * 7 + batch, dtype=dtype, wkind="uniform")
+            for dec in (False, True):
+                check(y, w, decreasing=dec)
+                check(y, None, decreasing=dec)
+        yi, wi = W.family("integer", 130, n, seed=n, dtype=dtype, wkind="integer")
+        for dec in (False, True):
+            check(yi, wi, exact_partition=True, decreasing=dec)
+
+
+def test_tiny_rows_flags_and_ties():
+    b = _gpu()
+    y = np.array([[1.0, 1.0, 1.0, 0.0], [2.0, np.nan, 1.0, 0.0], [3.0, 1.0, 2.0, 2.0], [0.0, 5.0, 5.0, 1.0]])
+    w = np.array([[1.0, 2.0, 1.0, 1.0], [1.0, 1.0, 1.0, 1.0], [1.0, 1.0, -1.0, 1.0], [1.0, 1.0, 1.0, 1.0]])
+    z, bs, rf = gpu_fit(y, w)
+    assert list(rf) == [0, b.ISO_ROW_NONFINITE, b.ISO_ROW_BAD_WEIGHT, 0]
+    assert np.isnan(z[1:3]).all() and bs[1:3].sum() == 0
+    np.testing.assert_array_equal(z[0], [0.8, 0.8, 0.8, 0.8])
+    np.testing.assert_array_equal(bs[0], [1, 0, 0, 0])
+    np.testing.assert_array_equal(z[3], [0.0, 11.0 / 3, 11.0 / 3, 11.0 / 3])
+    np.testing.assert_array_equal(bs[3], [1, 1, 0, 0])

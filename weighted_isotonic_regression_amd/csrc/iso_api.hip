@@ -1,6 +1,7 @@
 // iso_api.hip -- the C ABI of include/iso.h: argument checks, workspace layout and launches.
 //
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
+//   n <= 16     one lane per row, pool adjacent violators in registers and LDS (k_tiny)
 //   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
 //               launch of k_wave writes z, block starts and row flags (Section 3.5).
 //   n >  2048   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
@@ -171,6 +172,13 @@ template <typename T, bool W, bool D>
 int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int64_t batch,
             int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
   Prof prof(s);
+  if (n <= kTinyMax) {
+    prof.skip();
+    hipLaunchKernelGGL((k_tiny<T, W, D>), dim3((unsigned)((batch + kWave - 1) / kWave)), dim3(kWave), 0, s, y, w, z,
+                       bstart, rflags, batch, (int)n);
+    prof.mark(1);
+    return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
+  }
   if (!long_rows(n)) {
     const int L = lanes_per_row(n);
     const int R = kWave / L;

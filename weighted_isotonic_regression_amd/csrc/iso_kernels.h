@@ -330,6 +330,107 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   }
 }
 
+// ------------------------------------------------------------------ tiny rows
+// Rows of at most kTinyMax elements: one lane fits one row by pool adjacent violators, the
+// classical sequential method the page names (Section 1), which for so few elements beats
+// building the diagram's hull: the row's inputs sit in registers, each block's fp64 sums (w, w*y)
+// in LDS at its first element, and the block starts in a register bit mask.  The top block is
+// pooled with the one below while the lower mean is at least the top one, compared by
+// cross-multiplication, with the sums added in stack order: exactly the oracle's arithmetic.  The
+// fit is each block's sum quotient rounded once, or y for a block of one element (its exact mean).
+constexpr int kTinyMax = 16;
+
+template <typename T, bool W, bool D>
+__global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T* __restrict__ w,
+                                                T* __restrict__ z, uint8_t* __restrict__ bstart,
+                                                uint32_t* __restrict__ rflags, int64_t batch, int n) {
+  __shared__ double sS[kTinyMax][kWave];
+  __shared__ double sW[W ? kTinyMax : 1][kWave];
+  constexpr int VN = Vec16<T>::N;
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * kWave + lane;
+  if (row >= batch) return;
+  const int64_t off = row * n;
+  T yv[kTinyMax], wv[kTinyMax];
+  const bool vec = (n % VN) == 0 && ((uintptr_t)(y + off)) % 16 == 0 && (!W || ((uintptr_t)(w + off)) % 16 == 0);
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kTinyMax / VN; ++k) {
+      if (k * VN < n) {
+        load16(y + off + k * VN, &yv[k * VN]);
+        if (W) load16(w + off + k * VN, &wv[k * VN]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTinyMax; ++i) {
+      if (i < n) {
+        yv[i] = y[off + i];
+        if (W) wv[i] = w[off + i];
+      }
+    }
+  }
+  uint32_t flag = 0u, mask = 0u;
+#pragma unroll
+  for (int i = 0; i < kTinyMax; ++i) {
+    if (i < n) {
+      const double yd = yval<D>(yv[i]);
+      const double wd = W ? (double)wv[i] : 1.0;
+      if (!isfinite(yd) || !isfinite(wd)) flag |= ISO_ROW_NONFINITE_BIT;
+      else if (!(wd > 0.0)) flag |= ISO_ROW_BAD_WEIGHT_BIT;
+      // push element i as a block, then pool while the block below has a mean >= the top one's
+      double St = wd * yd, Wt = wd;
+      int t = i;
+      uint32_t below = mask;
+      while (below) {
+        const int p = 31 - __builtin_clz(below);
+        const double Sp = sS[p][lane], Wp = W ? sW[p][lane] : (double)(t - p);
+        if (!(Sp * Wt >= St * Wp)) break;
+        St = Sp + St;
+        Wt = Wp + Wt;
+        t = p;
+        below &= ~(1u << p);
+      }
+      mask = below | (1u << t);
+      sS[t][lane] = St;
+      if (W) sW[t][lane] = Wt;
+    }
+  }
+  // the fit: element i takes the mean of the block starting at the highest set bit <= i
+  T zv[kTinyMax];
+  uint8_t bs[kTinyMax];
+#pragma unroll
+  for (int i = 0; i < kTinyMax; ++i) {
+    if (i < n) {
+      const int b = 31 - __builtin_clz(mask & ((2u << i) - 1u));
+      const uint32_t after = mask & ~((2u << i) - 1u);  // block starts after i
+      const int e = after ? __builtin_ctz(after) : n;     // end of i's block
+      bs[i] = (b == i && !flag) ? 1 : 0;
+      if (flag) zv[i] = (T)NAN;
+      else if (e - b == 1) zv[i] = yv[i];
+      else {
+        const double Wb = W ? sW[b][lane] : (double)(e - b);
+        zv[i] = (T)zval<D>(sS[b][lane] / Wb);
+      }
+    }
+  }
+  if (vec) {
+#pragma unroll
+    for (int k = 0; k < kTinyMax / VN; ++k)
+      if (k * VN < n) store16(z + off + k * VN, &zv[k * VN]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTinyMax; ++i)
+      if (i < n) z[off + i] = zv[i];
+  }
+  if (bstart) {
+#pragma unroll
+    for (int i = 0; i < kTinyMax; ++i)
+      if (i < n) bstart[off + i] = bs[i];
+  }
+  if (rflags) rflags[row] = flag;
+}
+
 // ------------------------------------------------------------------ chunk-start scan
 constexpr int kScanThreads = 256;
 constexpr int kScanPer = 4;
