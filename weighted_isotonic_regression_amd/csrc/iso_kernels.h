@@ -371,6 +371,8 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
     }
   }
   uint32_t flag = 0u, mask = 0u;
+  double tS = 0.0, tW = 1.0;
+  int tt = 0;
 #pragma unroll
   for (int i = 0; i < kTinyMax; ++i) {
     if (i < n) {
@@ -378,24 +380,39 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
       const double wd = W ? (double)wv[i] : 1.0;
       if (!isfinite(yd) || !isfinite(wd)) flag |= ISO_ROW_NONFINITE_BIT;
       else if (!(wd > 0.0)) flag |= ISO_ROW_BAD_WEIGHT_BIT;
-      // push element i as a block, then pool while the block below has a mean >= the top one's
-      double St = wd * yd, Wt = wd;
-      int t = i;
-      uint32_t below = mask;
-      while (below) {
-        const int p = 31 - __builtin_clz(below);
-        const double Sp = sS[p][lane], Wp = W ? sW[p][lane] : (double)(t - p);
-        if (!(Sp * Wt >= St * Wp)) break;
-        St = Sp + St;
-        Wt = Wp + Wt;
-        t = p;
-        below &= ~(1u << p);
+      // push element i as a block, then pool while the block below has a mean >= the top one's;
+      // the top block lives in registers (tS, tW, tt), the blocks below it in LDS
+      double Sn = wd * yd, Wn = wd;
+      int tn = i;
+      if (i > 0) {
+        if (tS * Wn >= Sn * tW) {
+          Sn = tS + Sn;
+          Wn = tW + Wn;
+          tn = tt;
+          uint32_t below = mask & ~(1u << tt);
+          while (below) {
+            const int p = 31 - __builtin_clz(below);
+            const double Sp = sS[p][lane], Wp = W ? sW[p][lane] : (double)(tn - p);
+            if (!(Sp * Wn >= Sn * Wp)) break;
+            Sn = Sp + Sn;
+            Wn = Wp + Wn;
+            tn = p;
+            below &= ~(1u << p);
+          }
+          mask = below;
+        } else {
+          sS[tt][lane] = tS;
+          if (W) sW[tt][lane] = tW;
+        }
       }
-      mask = below | (1u << t);
-      sS[t][lane] = St;
-      if (W) sW[t][lane] = Wt;
+      mask |= 1u << tn;
+      tS = Sn;
+      tW = Wn;
+      tt = tn;
     }
   }
+  sS[tt][lane] = tS;
+  if (W) sW[tt][lane] = tW;
   // the fit: element i takes the mean of the block starting at the highest set bit <= i
   T zv[kTinyMax];
   uint8_t bs[kTinyMax];
