@@ -66,7 +66,7 @@ def stage_alg_bytes(stage, n_elems, esz, weighted, whole_diagram):
     and the chunk pass and fit handle only the partial last chunk.  Otherwise k_increasing reads
     a 16-byte probe per lane of each full chunk, the chunk pass reads y (and w) and the fit writes
     z for the whole row.  The scan, merge and ends kernels touch only workspace."""
-    full = (n_elems // CHUNK) * CHUNK if n_elems > 2048 else 0
+    full = (n_elems // CHUNK) * CHUNK if n_elems > 8192 else 0
     rest = n_elems - full if whole_diagram else n_elems
     reads = 2 if weighted else 1
     if stage == "increasing":

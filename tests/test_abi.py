@@ -83,18 +83,18 @@ def test_argument_errors_before_any_launch(lib):
     assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 8, None) == EINVAL         # unknown flag
     assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 4 | 2, None) == EINVAL     # unknown with known
     assert fx(Y, None, Y, None, None, 1, 10, 0, None, 0, 2, None) == EINVAL         # decreasing, z aliases y
-    assert fx(Y, None, Z, None, None, 1, 5000, 0, None, 0, 2, None) == EINVAL       # decreasing, no workspace
+    assert fx(Y, None, Z, None, None, 1, 20000, 0, None, 0, 2, None) == EINVAL      # decreasing, no workspace
     assert fx(Y, None, Z, None, None, 0, 10, 0, None, 0, 2, None) == OK             # decreasing, empty
     assert fx(Y, None, Y, None, None, 1, 10, 0, None, 0, 0, None) == EINVAL         # z aliases y
     assert fx(Y, W, W, None, None, 1, 10, 1, None, 0, 0, None) == EINVAL            # z aliases w
     assert fx(Y, None, P(Y.value + 8), None, None, 1, 10, 0, None, 0, 0, None) == EINVAL  # overlap
     assert fx(Y, None, Z, None, None, 1 << 40, 1 << 40, 0, None, 0, 0, None) == EINVAL  # overflow
     # long rows need a workspace of iso_workspace_bytes, 256-byte aligned
-    need = binding.iso_workspace_bytes(1, 5000, 0, 0)
+    need = binding.iso_workspace_bytes(1, 20000, 0, 0)
     assert need > 0
-    assert fx(Y, None, Z, None, None, 1, 5000, 0, None, 0, 0, None) == EINVAL
-    assert fx(Y, None, Z, None, None, 1, 5000, 0, P(1 << 36), need - 1, 0, None) == EINVAL
-    assert fx(Y, None, Z, None, None, 1, 5000, 0, P((1 << 36) + 8), need, 0, None) == EINVAL
+    assert fx(Y, None, Z, None, None, 1, 20000, 0, None, 0, 0, None) == EINVAL
+    assert fx(Y, None, Z, None, None, 1, 20000, 0, P(1 << 36), need - 1, 0, None) == EINVAL
+    assert fx(Y, None, Z, None, None, 1, 20000, 0, P((1 << 36) + 8), need, 0, None) == EINVAL
     # the synchronous weight check needs the workspace too
     assert fx(Y, W, Z, None, None, 1, 10, 0, None, 0, 1, None) == EINVAL
     # empty problems succeed without launching anything

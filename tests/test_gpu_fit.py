@@ -66,7 +66,7 @@ def check(y, w, exact_partition=False, tol=None, kkt=True, scale_abs=False, decr
 
 
 SIZES = [1, 2, 3, 17, 31, 32, 33, 63, 64, 65, 100, 511, 1000, 1024, 1025, 2047, 2048, 2049, 4095, 4096,
-         4097, 6145, 10000, 16383, 16384, 16385, 49153, 65536, 100003, 200001]
+         4097, 6145, 8191, 8192, 8193, 10000, 16383, 16384, 16385, 49153, 65536, 100003, 200001]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64"])

@@ -2,9 +2,10 @@
 //
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
 //   n <= 16     one lane per row, pool adjacent violators in registers and LDS (k_tiny)
-//   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
-//               launch of k_wave writes z, block starts and row flags (Section 3.5).
-//   n >  2048   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
+//   n <= 8192   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront (rows
+//               over 2048: one row per workgroup of 2 or 4 wavefronts); one launch of k_wave
+//               writes z, block starts and row flags (Section 3.5).
+//   n >  8192   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
 //               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls),
 //               k_scan_reduce + k_scan_apply (chunk starts),
 //               ceil(log2 m) launches of k_merge_wave, k_ends, k_fit (Section 3.3 and 3.4).
@@ -181,11 +182,19 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   }
   if (!long_rows(n)) {
     const int L = lanes_per_row(n);
-    const int R = kWave / L;
-    const int64_t tiles = (batch + R - 1) / R;
     prof.skip();
-    hipLaunchKernelGGL((k_wave<T, W, D>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
-                       rflags, batch, n, L);
+    if (L <= kWave) {
+      const int R = kWave / L;
+      const int64_t tiles = (batch + R - 1) / R;
+      hipLaunchKernelGGL((k_wave<T, W, D, 1>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
+                         rflags, batch, n, L);
+    } else if (L == 2 * kWave) {  // one row per workgroup of two wavefronts
+      hipLaunchKernelGGL((k_wave<T, W, D, 2>), dim3((unsigned)batch), dim3(2 * kWave), 0, s, y, w, z, bstart,
+                         rflags, batch, n, L);
+    } else {  // one row per workgroup of four wavefronts
+      hipLaunchKernelGGL((k_wave<T, W, D, 4>), dim3((unsigned)batch), dim3(4 * kWave), 0, s, y, w, z, bstart,
+                         rflags, batch, n, L);
+    }
     prof.mark(1);
     return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
   }

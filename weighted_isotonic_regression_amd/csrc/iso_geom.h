@@ -29,7 +29,7 @@ namespace iso {
 
 constexpr int kWave = 64;                    // lanes of a wavefront
 constexpr int kLanePts = 32;                 // elements per lane of a packed short-row tile
-constexpr int kShortMax = kWave * kLanePts;  // rows of at most this many elements are packed
+constexpr int kShortMax = 4 * kWave * kLanePts;  // rows of at most this many go to the short-row kernel
 constexpr int kSub = 256;                    // points per lane of a long-row chunk
 constexpr int kChunk = kWave * kSub;         // elements per chunk of a long row (one wavefront)
 constexpr int kCk = 32;                      // spacing of a lane's running-sum checkpoints

@@ -25,13 +25,18 @@
 namespace iso {
 
 // ------------------------------------------------------------------ tile layout in LDS
-// A tile holds R = 64 / L row segments of up to 32 L elements.  Row segment r's points
+// A tile of one wavefront holds R = 64 / L row segments of up to 32 L elements.  Row segment r's points
 // 0..len occupy raw LDS indices r * (32 L + 1) + k; raw index i is stored at lds_pad(i) to
 // spread a lane's 32 consecutive points over the banks.  Element i's increment (w_i, w_i y_i)
 // is staged at the slot of its left point i and replaced by that point's coordinates.
+// A workgroup of NW > 1 wavefronts holds one row of up to 2048 NW elements (L = 64 NW lanes).
 constexpr int kRawPts = kWave * (kLanePts + 1);           // 2112 = max R (32 L + 1)
 constexpr int kLdsPts = kRawPts + (kRawPts >> 5) + 8;     // padded
 constexpr int kMaskWords = 2 * kWave + 8;                 // R (L + 1) <= 128
+constexpr int lds_pts(int nw) {
+  return nw == 1 ? kLdsPts : (kLanePts * kWave * nw + 1) + ((kLanePts * kWave * nw + 1) >> 5) + 8;
+}
+constexpr int mask_words(int nw) { return nw == 1 ? kMaskWords : kWave * nw + 1 + 8; }
 
 __device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
 
@@ -108,7 +113,7 @@ struct Tile {
   static constexpr int N = (W ? 64 : 128) / (int)sizeof(T);
 };
 
-// q = e / d for 0 <= e < 4096, 1 <= d <= 2048 (float reciprocal, corrected to exact).
+// q = e / d for 0 <= e < 8192, 1 <= d <= 8192 (float reciprocal, corrected to exact).
 __device__ __forceinline__ int small_div(int e, int d, float inv) {
   int q = (int)((float)e * inv);
   if (q * d > e) --q;
@@ -128,20 +133,24 @@ struct TilePts {
   }
 };
 
-template <typename T, bool W, bool D>
-__global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
-                                             T* __restrict__ z, uint8_t* __restrict__ bstart,
-                                             uint32_t* __restrict__ rflags, int64_t batch,
-                                             int64_t n, int Lpack) {
-  __shared__ double sX[W ? kLdsPts : 1];
-  __shared__ double sY[kLdsPts];
-  __shared__ uint32_t sM[kMaskWords];
+template <typename T, bool W, bool D, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
+                                                     T* __restrict__ z, uint8_t* __restrict__ bstart,
+                                                     uint32_t* __restrict__ rflags, int64_t batch,
+                                                     int64_t n, int Lpack) {
+  constexpr int kThreads = NW * kWave;
+  constexpr int kPts = lds_pts(NW);
+  constexpr int kMW = mask_words(NW);
+  __shared__ double sX[W ? kPts : 1];
+  __shared__ double sY[kPts];
+  __shared__ uint32_t sM[kMW];
   __shared__ uint32_t sF[kWave];
+  __shared__ double sWave[2 * NW];  // per wavefront: lane-total sums, then their prefixes
 
   constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
   const int L = Lpack;
-  const int R = kWave / L;
+  const int R = kThreads / L;
   const int64_t row0 = (int64_t)blockIdx.x * R;
   const int64_t left = batch - row0;
   const int rows = left < R ? (int)left : R;
@@ -152,8 +161,8 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   const int E = rows * seglen;  // elements of the tile, contiguous from off
   const float inv_seg = 1.0f / (float)seglen;
 
-  for (int i = lane; i < kMaskWords; i += kWave) sM[i] = 0u;
-  sF[lane] = 0u;
+  for (int i = lane; i < kMW; i += kThreads) sM[i] = 0u;
+  if (lane < kWave) sF[lane] = 0u;
 
   // ---- a1: load.  All of the lane's loads are issued before any is used: 16-byte vectors at
   // element (lane + 64 k) * VN when the tile is 16-byte aligned, else scalars at lane + 64 k.
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   if (vec) {
 #pragma unroll
     for (int k = 0; k < kLanePts / VN; ++k) {
-      const int e = (lane + kWave * k) * VN;
+      const int e = (lane + kThreads * k) * VN;
       if (e + VN <= E) {
         vload(y + off + e, &yv[k * VN]);
         if (W) vload(w + off + e, &wv[k * VN]);
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   } else {
 #pragma unroll
     for (int k = 0; k < kLanePts; ++k) {
-      const int e = lane + kWave * k;
+      const int e = lane + kThreads * k;
       if (e < E) {
         yv[k] = y[off + e];
         if (W) wv[k] = w[off + e];
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
   // classify and stage (w, w*y) in fp64 at each element's left point
 #pragma unroll
   for (int k = 0; k < kLanePts; ++k) {
-    const int e = vec ? (lane + kWave * (k / VN)) * VN + (k % VN) : lane + kWave * k;
+    const int e = vec ? (lane + kThreads * (k / VN)) * VN + (k % VN) : lane + kThreads * k;
     if (e < E) {
       double yd = yval<D>(yv[k]);
       double wd = W ? (double)wv[k] : 1.0;
@@ -234,20 +243,61 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
         ty += sY[idx];
       }
     }
-    double ix = tx, iy = ty;
-    for (int d = 1; d < L; d <<= 1) {
-      double vx = __shfl_up(ix, d, L);
-      double vy = __shfl_up(iy, d, L);
-      if (ql >= d) {
-        ix += vx;
-        iy += vy;
+    double ix = tx, iy = ty, sx0, sy0;
+    if constexpr (NW == 1) {
+      for (int d = 1; d < L; d <<= 1) {
+        double vx = __shfl_up(ix, d, L);
+        double vy = __shfl_up(iy, d, L);
+        if (ql >= d) {
+          ix += vx;
+          iy += vy;
+        }
       }
-    }
-    double sx0 = __shfl_up(ix, 1, L);
-    double sy0 = __shfl_up(iy, 1, L);
-    if (ql == 0) {
-      sx0 = 0.0;
-      sy0 = 0.0;
+      sx0 = __shfl_up(ix, 1, L);
+      sy0 = __shfl_up(iy, 1, L);
+      if (ql == 0) {
+        sx0 = 0.0;
+        sy0 = 0.0;
+      }
+    } else {
+      // one row over NW wavefronts: a scan in each, then the wavefronts' prefixes in turn, so
+      // that a lane's start is bitwise its left neighbour's end
+      const int wl = lane & (kWave - 1), wv = lane / kWave;
+      for (int d = 1; d < kWave; d <<= 1) {
+        double vx = __shfl_up(ix, d, kWave);
+        double vy = __shfl_up(iy, d, kWave);
+        if (wl >= d) {
+          ix += vx;
+          iy += vy;
+        }
+      }
+      double ex = __shfl_up(ix, 1, kWave), ey = __shfl_up(iy, 1, kWave);
+      if (wl == kWave - 1) {
+        sWave[2 * wv] = ix;
+        sWave[2 * wv + 1] = iy;
+      }
+      __syncthreads();
+      if (lane == 0) {
+        double px = 0.0, py = 0.0;
+        for (int v = 0; v < NW; ++v) {
+          const double tvx = sWave[2 * v], tvy = sWave[2 * v + 1];
+          sWave[2 * v] = px;
+          sWave[2 * v + 1] = py;
+          px = tvx + px;
+          py = tvy + py;
+        }
+      }
+      __syncthreads();
+      const double px = sWave[2 * wv], py = sWave[2 * wv + 1];
+      if (wl == 0) {
+        sx0 = px;
+        sy0 = py;
+      } else {
+        sx0 = ex + px;
+        sy0 = ey + py;
+      }
+      ix = ix + px;
+      iy = iy + py;
     }
     double lx = 0.0, ly = 0.0;
     for (int k = 0; k < kLanePts; ++k) {
@@ -309,7 +359,7 @@ __global__ __launch_bounds__(64) void k_wave(const T* __restrict__ y, const T* _
     // it, from the vertex at or before point i to the vertex after it; an element whose two
     // points are both vertices is a block of its own and gets its y, the block's exact mean.
     // Consecutive lanes write consecutive elements.
-    for (int e = lane; e < E; e += kWave) {
+    for (int e = lane; e < E; e += kThreads) {
       const T ye = y[off + e];  // issued first, so its latency overlaps the mask and LDS reads
       const int r = small_div(e, seglen, inv_seg);
       const int i = e - r * seglen;
