@@ -38,7 +38,7 @@ constexpr int kSubW = kLaneW + 1;            // mask words of a lane's points 0.
 constexpr int kListCap = 256;                // chunks with at most this many hull vertices keep a list
 constexpr int kMaskW = kChunk / 32 + 1;      // mask words of a chunk (points 0..16384)
 constexpr int kZTiles = kChunk / 8;          // load tiles of a chunk (at least 8 elements each)
-constexpr int kVjpTile = kWave * 32;         // elements per backward tile (one wavefront)
+constexpr int kVjpTile = kWave * 32;         // elements per backward tile (256 threads, 8 each)
 
 // Per-row input flags (same values as ISO_ROW_NONFINITE / ISO_ROW_BAD_WEIGHT of iso.h).
 constexpr uint32_t ISO_ROW_NONFINITE_BIT = 1u;
