@@ -659,19 +659,30 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
   const int len = rem < kChunk ? (int)rem : kChunk;
   const int tid = threadIdx.x;
   const EndInfo e = ends[g];
-  if (rflags[row] != 0u) {
-    for (int i = tid; i < len; i += kFitThreads) {
-      z[off + i] = (T)NAN;
-      if (bstart) bstart[off + i] = 0;
+  // 16-byte groups of consecutive elements per thread (scalar stores where z is not aligned)
+  constexpr int VN = Vec16<T>::N;
+  const bool zvec = ((uintptr_t)(z + off)) % 16 == 0;
+  auto fill = [&](const T zv, const bool start0) {
+    T zo[VN];
+#pragma unroll
+    for (int u = 0; u < VN; ++u) zo[u] = zv;
+    for (int i0 = tid * VN; i0 < len; i0 += kFitThreads * VN) {
+      if (zvec && i0 + VN <= len) {
+        store16(z + off + i0, zo);
+      } else {
+        for (int i = i0; i < min(i0 + VN, len); ++i) z[off + i] = zv;
+      }
+      if (bstart) {
+        for (int i = i0; i < min(i0 + VN, len); ++i) bstart[off + i] = (i == 0 && start0) ? 1 : 0;
+      }
     }
+  };
+  if (rflags[row] != 0u) {
+    fill((T)NAN, false);
     return;
   }
   if (e.lo < 0) {
-    const T zv = (T)zval<D>(e.sin);
-    for (int i = tid; i < len; i += kFitThreads) {
-      z[off + i] = zv;
-      if (bstart) bstart[off + i] = (i == 0 && e.p0v) ? 1 : 0;
-    }
+    fill((T)zval<D>(e.sin), e.p0v != 0);
     return;
   }
   // one-element blocks at the chunk's ends get their y: element 0 when P_0 is a vertex and P_1
@@ -794,27 +805,54 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     }
   }
   __syncthreads();
-  for (int i = tid; i < len; i += kFitThreads) {
-    double zv;
-    uint8_t st = 0;
-    if (i < e.klo) {
-      zv = one_in ? yval<D>(S.y[off]) : e.sin;
-      st = (i == 0 && e.p0v) ? 1 : 0;
-    } else if (i >= e.khi) {
-      zv = one_out ? yval<D>(S.y[off + i]) : e.sout;
-      st = (i == e.khi) ? 1 : 0;
-    } else {
-      int lo = 0, hi = nv - 2;  // edge q covers [sK[q], sK[q + 1])
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sK[mid] <= i) lo = mid;
-        else hi = mid - 1;
+  // a thread takes VN consecutive elements: the first one inside [klo, khi) finds its edge by
+  // binary search (edge q covers [sK[q], sK[q + 1])), the next ones step to the following edge
+  // when they reach its first point
+  for (int i0 = tid * VN; i0 < len; i0 += kFitThreads * VN) {
+    T zo[VN];
+    uint8_t so[VN];
+    int q = -1;
+#pragma unroll
+    for (int u = 0; u < VN; ++u) {
+      const int i = i0 + u;
+      double zv = 0.0;
+      uint8_t st = 0;
+      if (i < e.klo) {
+        zv = one_in ? yval<D>(S.y[off]) : e.sin;
+        st = (i == 0 && e.p0v) ? 1 : 0;
+      } else if (i >= e.khi) {
+        if (i < len) zv = one_out ? yval<D>(S.y[off + i]) : e.sout;
+        st = (i == e.khi) ? 1 : 0;
+      } else {
+        if (q < 0) {
+          int lo = 0, hi = nv - 2;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sK[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          q = lo;
+        } else if (q + 1 <= nv - 2 && sK[q + 1] <= i) {
+          ++q;
+        }
+        zv = sSlope[q];
+        st = (sK[q] == i) ? 1 : 0;
       }
-      zv = sSlope[lo];
-      st = (sK[lo] == i) ? 1 : 0;
+      zo[u] = (T)zval<D>(zv);
+      so[u] = st;
     }
-    z[off + i] = (T)zval<D>(zv);
-    if (bstart) bstart[off + i] = st;
+    if (zvec && i0 + VN <= len) {
+      store16(z + off + i0, zo);
+    } else {
+#pragma unroll
+      for (int u = 0; u < VN; ++u)
+        if (i0 + u < len) z[off + i0 + u] = zo[u];
+    }
+    if (bstart) {
+#pragma unroll
+      for (int u = 0; u < VN; ++u)
+        if (i0 + u < len) bstart[off + i0 + u] = so[u];
+    }
   }
 }
 
