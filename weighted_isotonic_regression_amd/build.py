@@ -6,6 +6,7 @@ source says so; explicit fma() calls stay fused), and no packed fp32 instruction
 """
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
@@ -13,8 +14,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "iso_api.hip")
-DEPS = [os.path.join(HERE, "csrc", f) for f in ("iso_geom.h", "iso_kernels.h", "iso_chunk.h", "iso_merge.h")] + [
-    os.path.join(ROOT, "include", "iso.h")]
+DEPS = sorted(glob.glob(os.path.join(HERE, "csrc", "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h")))
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libiso_mi355x.so")
 ARCH = "gfx950"
