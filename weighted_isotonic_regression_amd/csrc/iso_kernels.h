@@ -966,12 +966,21 @@ __global__ __launch_bounds__(kVjpThreads) void k_vjp_tiles(const T* __restrict__
   T gv[kVjpPer2], wv[kVjpPer2];
   vjp_load(g, off + i0, c, gv, (T)0);
   if (w) vjp_load(w, off + i0, c, wv, (T)0);
+  int st[kVjpPer2];
+  if (kVjpPer2 == 8 && c == kVjpPer2 && ((uintptr_t)(bs + off + i0)) % 8 == 0) {
+    const uint64_t b8 = *reinterpret_cast<const uint64_t*>(bs + off + i0);
+#pragma unroll
+    for (int k = 0; k < kVjpPer2; ++k) st[k] = ((b8 >> (8 * k)) & 0xffu) ? 1 : 0;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kVjpPer2; ++k) st[k] = k < c ? (bs[off + i0 + k] ? 1 : 0) : 0;
+  }
   // tail: left-to-right fold restarting at starts; head: sums before the first start
   Seg tl{0, 0.0, 0.0}, hd{0, 0.0, 0.0};
 #pragma unroll
   for (int k = 0; k < kVjpPer2; ++k) {
     if (k < c) {
-      const int b = bs[off + i0 + k] ? 1 : 0;
+      const int b = st[k];
       const double gd = (double)gv[k], wd = w ? (double)wv[k] : 1.0;
       tl = seg_lr(tl, Seg{b, gd, wd});
       if (!hd.h && b) hd.h = 1;
@@ -1157,14 +1166,24 @@ __global__ __launch_bounds__(kVjpThreads) void k_vjp_apply(const T* __restrict__
   const int len = rem < kVjpTile ? (int)rem : kVjpTile;
   const int i0 = kVjpPer2 * threadIdx.x;
   const int c = min(max(len - i0, 0), kVjpPer2);
+  // every load is issued here, the tile's carries included, before any of them is waited for
+  const double4 me = cc[tid];
+  const double4 nx = tt == ntile - 1 ? make_double4(0.0, 0.0, 0.0, 0.0) : cc[tid + 1];
   T gv[kVjpPer2], wv[kVjpPer2], yv[kVjpPer2], zv[kVjpPer2];
   vjp_load(g, off + i0, c, gv, (T)0);
   if (w) vjp_load(w, off + i0, c, wv, (T)0);
   vjp_load(y, off + i0, c, yv, (T)0);
   vjp_load(z, off + i0, c, zv, (T)0);
   int st[kVjpPer2 + 1];  // starts of this thread's elements and of the one after them
+  if (kVjpPer2 == 8 && c == kVjpPer2 && ((uintptr_t)(bs + off + i0)) % 8 == 0) {
+    const uint64_t b8 = *reinterpret_cast<const uint64_t*>(bs + off + i0);
 #pragma unroll
-  for (int k = 0; k <= kVjpPer2; ++k) st[k] = (k < c || (k == c && i0 + k < len)) ? (bs[off + i0 + k] ? 1 : 0) : 0;
+    for (int k = 0; k < kVjpPer2; ++k) st[k] = ((b8 >> (8 * k)) & 0xffu) ? 1 : 0;
+    st[kVjpPer2] = (i0 + kVjpPer2 < len) ? (bs[off + i0 + kVjpPer2] ? 1 : 0) : 0;
+  } else {
+#pragma unroll
+    for (int k = 0; k <= kVjpPer2; ++k) st[k] = (k < c || (k == c && i0 + k < len)) ? (bs[off + i0 + k] ? 1 : 0) : 0;
+  }
   // forward fold (restart at starts) and backward fold (restart after block ends: the flag of
   // element k is the start of element k + 1)
   Seg f{0, 0.0, 0.0}, r{0, 0.0, 0.0};
@@ -1176,8 +1195,6 @@ __global__ __launch_bounds__(kVjpThreads) void k_vjp_apply(const T* __restrict__
   for (int k = kVjpPer2 - 1; k >= 0; --k) {
     if (k < c) r = seg_rl(Seg{st[k + 1], (double)gv[k], w ? (double)wv[k] : 1.0}, r);
   }
-  const double4 me = cc[tid];
-  const double4 nx = tt == ntile - 1 ? make_double4(0.0, 0.0, 0.0, 0.0) : cc[tid + 1];
   Seg fw, bw;
   vjp_wg_scans(f, r, Seg{0, me.x, me.y}, Seg{0, nx.z, nx.w}, sh, fw, bw);
   if (c == 0) return;
