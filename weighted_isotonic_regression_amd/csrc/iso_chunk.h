@@ -731,8 +731,9 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     if (bulk) {
       bulk_push(kp, kc);
     } else {
-#pragma unroll 1
-      for (int k = 1; k < kn; ++k) element(k);
+#pragma unroll
+      for (int k = 1; k < TN; ++k)
+        if (k < kn) element(k);
     }
     // speculative fit of a tile that pushed every point and popped none: every element is its
     // own block so far
