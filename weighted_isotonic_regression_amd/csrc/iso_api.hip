@@ -453,12 +453,20 @@ int run_soft_rank(const T* x, int64_t batch, int64_t n, double eps, T* r, uint32
     return o;
   };
   const bool device_sort = n > kSrRowMax;  // else one workgroup per row sorts in LDS
+  // fp32 values in several rows: one sort of 64-bit keys (row, value key) instead of a sort by
+  // value followed by a stable sort by row
+  const bool row_keys = device_sort && sizeof(K) == 4 && batch > 1;
+  unsigned row_bits = 0;
+  while (row_bits < 32 && (1ull << row_bits) < (unsigned long long)batch) ++row_bits;
   if (device_sort) {
-    B.o_keys = take(N * sizeof(K));
-    B.o_keys2 = take(N * sizeof(K));
-    B.o_idx = take(N * sizeof(uint32_t));
-    B.o_rk = take(N * sizeof(uint32_t));
-    B.o_rk2 = take(N * sizeof(uint32_t));
+    const size_t ksz = row_keys ? sizeof(uint64_t) : sizeof(K);
+    B.o_keys = take(N * ksz);
+    B.o_keys2 = take(N * ksz);
+    if (!row_keys) {
+      B.o_idx = take(N * sizeof(uint32_t));
+      B.o_rk = take(N * sizeof(uint32_t));
+      B.o_rk2 = take(N * sizeof(uint32_t));
+    }
   }
   B.o_z = take(N * sizeof(double));
   B.o_v = take(N * sizeof(double));
@@ -466,9 +474,14 @@ int run_soft_rank(const T* x, int64_t batch, int64_t n, double eps, T* r, uint32
   B.fit = make_layout(batch, n);
   B.o_ws = take(B.fit.total);
   if (device_sort) {
-    if (sr_sort<K>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, batch, n, nullptr, B.tmp_bytes, s) !=
-        hipSuccess)
-      return ISO_EHIP;
+    hipError_t e;
+    if (row_keys)
+      e = rocprim::radix_sort_pairs(nullptr, B.tmp_bytes, (uint64_t*)nullptr, (uint64_t*)nullptr,
+                                    rocprim::counting_iterator<uint32_t>(0), (uint32_t*)nullptr, (size_t)N, 0,
+                                    32 + row_bits, s);
+    else
+      e = sr_sort<K>(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, batch, n, nullptr, B.tmp_bytes, s);
+    if (e != hipSuccess) return ISO_EHIP;
     B.o_tmp = take(B.tmp_bytes);
   }
   B.total = off;
@@ -483,6 +496,20 @@ int run_soft_rank(const T* x, int64_t batch, int64_t n, double eps, T* r, uint32
     // one workgroup sorts each row in LDS and writes perm and z
     hipLaunchKernelGGL((k_sr_row_sort<T, K>), dim3((unsigned)batch), dim3(kSrThreads), 0, s, x, n, eps, perm, z);
     if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+  } else if (row_keys) {
+    uint64_t* k64 = (uint64_t*)(buf + B.o_keys);
+    hipLaunchKernelGGL(k_sr_row_keys, dim3(grid), dim3(kSrThreads), 0, s, (const float*)x, N, n, k64);
+    if (hipGetLastError() != hipSuccess ||
+        rocprim::radix_sort_pairs(buf + B.o_tmp, B.tmp_bytes, k64, (uint64_t*)(buf + B.o_keys2),
+                                  rocprim::counting_iterator<uint32_t>(0), perm, (size_t)N, 0, 32 + row_bits,
+                                  s) != hipSuccess) {
+      rc = ISO_EHIP;
+    }
+    if (rc == ISO_OK) {
+      hipLaunchKernelGGL((k_sr_problem<T>), dim3(grid), dim3(kSrThreads), 0, s, x, (const uint32_t*)perm, N, n,
+                         eps, z);
+      if (hipGetLastError() != hipSuccess) rc = ISO_EHIP;
+    }
   } else {
     hipLaunchKernelGGL((k_sr_keys<T, K>), dim3(grid), dim3(kSrThreads), 0, s, x, N, keys);
     if (hipGetLastError() != hipSuccess ||

@@ -36,6 +36,14 @@ __global__ __launch_bounds__(kSrThreads) void k_sr_keys(const T* __restrict__ x,
   if (i < N) keys[i] = sr_key(x[i]);
 }
 
+// fp32 values of several rows: 64-bit keys holding the row above the value's key, so that one
+// stable sort orders by row, then by decreasing value, equal values keeping their column order.
+__global__ __launch_bounds__(kSrThreads) void k_sr_row_keys(const float* __restrict__ x, int64_t N, int64_t n,
+                                                            uint64_t* __restrict__ keys) {
+  const int64_t i = (int64_t)blockIdx.x * kSrThreads + threadIdx.x;
+  if (i < N) keys[i] = ((uint64_t)(i / n) << 32) | (uint64_t)sr_key(x[i]);
+}
+
 // Rows of at most kSrRowMax elements: one workgroup sorts a row in LDS (rocPRIM's block radix
 // sort, stable, items in blocked order: thread t holds columns 8t .. 8t + 7, so equal keys keep
 // their column order) and writes perm and z directly.
