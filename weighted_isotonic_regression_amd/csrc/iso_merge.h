@@ -70,6 +70,7 @@ __device__ __forceinline__ GPt shfl_pt(const GPt& p, int src) {
 // where the walk stands.
 constexpr int kWalkK = 4;
 constexpr int kWideCap = 32;  // wide windows of one side pass before switching to the search
+constexpr int kShortWalk = 8;  // single steps tried before memory windows at dense joints
 
 struct WideLds {
   int cum[kWalkK * kWave];
@@ -77,7 +78,7 @@ struct WideLds {
 };
 
 template <class VS, class Stop>
-__device__ bool walk_window_wide(const VS& S, const NodeList& L, int dir, VRef& v, GPt& Pv,
+__device__ __forceinline__ bool walk_window_wide(const VS& S, const NodeList& L, int dir, VRef& v, GPt& Pv,
                                  int lane, WideLds& W, Stop stop) {
   constexpr int NW = kWalkK * kWave;
   // segments j = lane * kWalkK + t: v.u + dir * j, and the number of their vertices beyond v
@@ -189,10 +190,13 @@ __device__ bool walk_window_wide(const VS& S, const NodeList& L, int dir, VRef& 
   return stop_at_f || (f < NW && list_end);
 }
 
-// Walk to the bridge one vertex at a time (no cap), from alpha in A and beta in B.
+// Walk to the bridge one vertex at a time, from alpha in A and beta in B, for at most `steps`
+// moves (steps < 0: no cap).  Returns true when the walk ends (a round in which neither side
+// moves), false with the positions reached when the moves run out.  Every lane walks the same
+// vertices.
 template <class VS>
-__device__ void merge_finish_walk(const VS& S, const NodeList& LA, const NodeList& LB,
-                                  VRef firstA, VRef lastB, VRef& al, VRef& be) {
+__device__ __forceinline__ bool merge_finish_walk(const VS& S, const NodeList& LA, const NodeList& LB, VRef firstA,
+                                  VRef lastB, VRef& al, VRef& be, int steps) {
   GPt Pa = load_v(S, LA, al), Pb = load_v(S, LB, be);
   for (;;) {
     bool moved = false;
@@ -200,6 +204,8 @@ __device__ void merge_finish_walk(const VS& S, const NodeList& LA, const NodeLis
       const VRef p = list_pred(LA, al);
       const GPt Pp = load_v(S, LA, p);
       if (gturn(Pp, Pa, Pb) > 0.0) break;
+      if (steps == 0) return false;
+      --steps;
       al = p;
       Pa = Pp;
       moved = true;
@@ -208,11 +214,13 @@ __device__ void merge_finish_walk(const VS& S, const NodeList& LA, const NodeLis
       const VRef q = list_succ(LB, be);
       const GPt Pq = load_v(S, LB, q);
       if (gturn(Pa, Pb, Pq) > 0.0) break;
+      if (steps == 0) return false;
+      --steps;
       be = q;
       Pb = Pq;
       moved = true;
     }
-    if (!moved) break;
+    if (!moved) return true;
   }
 }
 
@@ -221,7 +229,7 @@ __device__ void merge_finish_walk(const VS& S, const NodeList& LA, const NodeLis
 // the (i+1)-th vertex from s (mine, P) when i < nw.  exhausted: the window reaches the end of the
 // list.  One read of descriptors and one read of points.
 template <class VS>
-__device__ void side_window(const VS& S, const NodeList& L, int dir, VRef s, int lane,
+__device__ __forceinline__ void side_window(const VS& S, const NodeList& L, int dir, VRef s, int lane,
                             MergeLds& W, int& nw, bool& exhausted, VRef& mine, GPt& P) {
   const int u = s.u + dir * lane;
   const bool inr = dir < 0 ? u >= 0 : u < L.n;
@@ -273,7 +281,7 @@ __device__ void side_window(const VS& S, const NodeList& L, int dir, VRef s, int
 // false with the furthest positions reached (al, be, Pa, Pb), from which the walk continues in
 // memory.
 template <class VS>
-__device__ bool window_bridge(const VS& S, const NodeList& LA, const NodeList& LB, int lane,
+__device__ __forceinline__ bool window_bridge(const VS& S, const NodeList& LA, const NodeList& LB, int lane,
                               MergeLds& WA, MergeLds& WB, const GPt& Sp, VRef& al, VRef& be,
                               GPt& Pa, GPt& Pb) {
   int na, nb;
@@ -397,8 +405,23 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
       }
     }
   }
-  if (!settled) {
-    // the walk continues in memory, kWalkK * 64 vertices at a time, from where the windows ended
+  // What is left is walked in phases: 0, a few single steps (taken first when s lies in a
+  // dense-form chunk on one side, where the bridge is usually a vertex or two from s and a single
+  // step reads one vertex where a memory window recomputes 256 of them); 1, memory windows, then
+  // the Overmars-van Leeuwen bisection for long walks; 2, single steps to the end (when rounding
+  // defeats the bisection).  The single-step walk has one call site, so it stays inline.
+  int phase = (desc_form(LA.d[LA.n - 1]) != 0 || desc_form(LB.d[0]) != 0) ? 0 : 1;
+  while (!settled) {
+    if (phase != 1) {
+      settled = merge_finish_walk(S, LA, LB, firstA, lastB, al, be, phase == 0 ? kShortWalk : -1);
+      if (!settled) {  // (after phase 0 only: phase 2 always ends)
+        Pa = load_v(S, LA, al);
+        Pb = load_v(S, LB, be);
+        phase = 1;
+      }
+      continue;
+    }
+    // the walk continues in memory, kWalkK * 64 vertices at a time, from where it stands
     WideLds& Ww = sww[wid];
     bool searched = false;
     for (int pass = 0; pass < 4 * kChunk; ++pass) {
@@ -435,6 +458,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
       }
       if (searched || !moved) break;
     }
+    settled = true;
     if (searched) {
       // long walk: Overmars-van Leeuwen bisection over the ranges still open (every lane runs the
       // same serial search, reading the same addresses)
@@ -443,8 +467,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
         al = a2;
         be = b2;
       } else {
-        // rounding defeated the search: finish by plain walking
-        merge_finish_walk(S, LA, LB, firstA, lastB, al, be);
+        settled = false;  // rounding defeated the search: finish by single steps
+        phase = 2;
       }
     }
   }
