@@ -1152,7 +1152,7 @@ __global__ __launch_bounds__(kVjpScanThreads) void k_vjp_scan_apply(const VjpTil
 
 // Pass 3: each element's block sums from the two scans, seeded with its tile's carries.
 template <typename T>
-__global__ __launch_bounds__(kVjpThreads) void k_vjp_apply(const T* __restrict__ g, const T* __restrict__ y,
+__global__ __launch_bounds__(kVjpThreads, 4) void k_vjp_apply(const T* __restrict__ g, const T* __restrict__ y,
                                                            const T* __restrict__ w, const T* __restrict__ z,
                                                            const uint8_t* __restrict__ bs,
                                                            const double4* __restrict__ cc, T* __restrict__ gy,
