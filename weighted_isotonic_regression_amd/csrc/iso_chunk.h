@@ -15,8 +15,8 @@
 //                chunk-relative coordinates are its start (a wave scan of the lane totals) plus
 //                those.  All sums are fp64.
 //
-// Per lane state: the top two stack entries in registers, the last kRing entries in an LDS ring
-// indexed by depth, the stack as a bit mask in LDS, and the running sums every 32 points (the
+// Per lane state: the top three stack entries in registers, the last kRingS entries in an LDS
+// ring indexed by depth, the stack as a bit mask in LDS, and the running sums every 32 points (the
 // checkpoints).  An entry that has left the ring is found again from the mask and recomputed
 // from its checkpoint and the inputs; on the measured workloads this is rare (the stacks of noisy
 // rows stay shallow and dense rows never pop).

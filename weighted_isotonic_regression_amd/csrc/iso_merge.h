@@ -16,7 +16,9 @@
 // of the lower levels.  A longer walk continues in memory 256 vertices at a time: the lanes
 // gather the next vertices of the walk (the segments' lengths come from one coalesced read of
 // descriptors and a scan), test the walk's predicate on all of them at once and take the first
-// stop with a ballot.  The tail of the right child's list is moved by all lanes.
+// stop with a ballot.  Where s lies in a dense-form chunk, a few single steps come first, since a
+// dense hull's bridge is usually a vertex or two from s.  The tail of the right child's list is
+// moved by all lanes.
 #pragma once
 
 #include <hip/hip_runtime.h>
