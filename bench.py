@@ -79,7 +79,7 @@ def stage_alg_bytes(stage, n_elems, esz, weighted, whole_diagram):
 
 
 STAGE_KERNEL = {"increasing": "k_increasing", "chunk": "k_chunk", "scan": "k_scan",
-                "merge": "k_merge_wave", "ends": "k_ends", "fit": "k_fit"}
+                "merge": "k_merge_levels", "ends": "k_ends", "fit": "k_fit"}
 
 
 def time_fit(torch, B, sets, steps, warmup, flags=0, stages=True):
@@ -365,8 +365,8 @@ def summarize_pmc(fetch_dir, write_dir):
     calls = max(sum(len(vs) for k, vs in fetch.items() if mine(k, "k_chunk") or mine(k, "k_wave") or
                     mine(k, "k_tiny")), 1)
     lines = []
-    for key in ("k_tiny", "k_wave", "k_increasing", "k_chunk", "k_scan_reduce", "k_scan_apply", "k_merge_wave", "k_ends",
-                "k_fit"):
+    for key in ("k_tiny", "k_wave", "k_increasing", "k_chunk", "k_scan_reduce", "k_scan_apply", "k_merge_levels",
+                "k_ends", "k_fit"):
         fs = [v for k, vs in fetch.items() if mine(k, key) for v in vs]
         wsz = [v for k, vs in write.items() if mine(k, key) for v in vs]
         if fs and wsz:

@@ -31,10 +31,10 @@ def _counter_csv(d, counter, rows):
 def test_counters_are_scaled_by_the_calibration_copy(tmp_path):
     # the copy of 1 GiB reads 2^19 KiB of FETCH_SIZE (so fetch bytes scale by 2) and writes
     # 2^20 KiB of WRITE_SIZE (scale 1); k_chunk reads 1000 KiB and writes 300 KiB per launch over two
-    # fit calls, and k_merge_wave runs 3 times per call
+    # fit calls, and k_merge_levels runs 3 times per call
     copy = "void at::native::elementwise_kernel<copy>(int)"
     chunk = "void iso::k_chunk<float, true, false>(float const*)"
-    merge = "void iso::k_merge_wave<float, true, false>(iso::VertexStore<float, true, false>)"
+    merge = "void iso::k_merge_levels<float, true, false>(iso::VertexStore<float, true, false>, int, int, long)"
     _counter_csv(str(tmp_path / "f"), "FETCH_SIZE", [(copy, 524288), (chunk, 1000), (chunk, 1000)] +
                  [(merge, 10)] * 6)
     _counter_csv(str(tmp_path / "w"), "WRITE_SIZE", [(copy, 1048576), (chunk, 300), (chunk, 300)] +
@@ -43,7 +43,7 @@ def test_counters_are_scaled_by_the_calibration_copy(tmp_path):
     assert sf == pytest.approx(2.0) and sw == pytest.approx(1.0)
     got = {k: (fb, wb, lpc) for k, fb, wb, lpc in lines}
     assert got["k_chunk"] == (pytest.approx(1000 * 1024 * 2.0), pytest.approx(300 * 1024 * 1.0), 1.0)
-    assert got["k_merge_wave"] == (pytest.approx(10 * 1024 * 2.0), pytest.approx(4 * 1024 * 1.0), 3.0)
+    assert got["k_merge_levels"] == (pytest.approx(10 * 1024 * 2.0), pytest.approx(4 * 1024 * 1.0), 3.0)
 
 
 def test_stored_traffic_of_other_sources_is_ignored(tmp_path, monkeypatch):

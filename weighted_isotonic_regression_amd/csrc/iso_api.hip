@@ -8,7 +8,8 @@
 //   n >  8192   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
 //               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls),
 //               k_scan_reduce + k_scan_apply (chunk starts),
-//               ceil(log2 m) launches of k_merge_wave, k_ends, k_fit (Section 3.3 and 3.4).
+//               ceil(ceil(log2 m) / 3) launches of k_merge_levels, k_ends, k_fit
+//               (Section 3.3 and 3.4).
 // Rows of unequal lengths (iso_fit_ragged) are bucketed by length, padded into a rectangular
 // buffer per bucket (iso_ragged.h) and fitted by the paths above.  The soft rank (iso_soft_rank,
 // iso_softrank.h) sorts each row with rocPRIM's radix sort and fits the decreasing direction.
@@ -257,17 +258,20 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   S.w = w;
   S.n = n;
   S.m = m;
+  // the merge levels, kMergeGroup per launch (a workgroup per subtree)
   int levels = 0;
-  for (int r = 0; (1 << r) < m; ++r) {
-    ++levels;
-    const int span = 1 << (r + 1);
-    const int per_row = (m - (1 << r) + span - 1) / span;
-    const int64_t merges = batch * (int64_t)per_row;
-    const int64_t blocks = (merges + kMergeWaves - 1) / kMergeWaves;
-    hipLaunchKernelGGL((k_merge_wave<T, W, D>), dim3((unsigned)blocks), dim3(kMergeWaves * kWave), 0, s, S,
-                       batch, r, per_row);
+  while ((1 << levels) < m) ++levels;
+  int launches = 0;
+  for (int r0 = 0; r0 < levels; r0 += kMergeGroup) {
+    const int nlev = std::min(kMergeGroup, levels - r0);
+    const int64_t span = (int64_t)1 << (r0 + nlev);
+    const int64_t per_row = (m + span - 1) / span;
+    hipLaunchKernelGGL((k_merge_levels<T, W, D>), dim3((unsigned)(batch * per_row)), dim3(kMergeWaves * kWave),
+                       0, s, S, r0, nlev, per_row);
+    ++launches;
   }
-  prof.mark(levels);
+  if (launches > 0) prof.mark(launches);
+  else prof.skip();
   hipLaunchKernelGGL((k_ends<T, W, D>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,
                      batch);
   prof.mark(1);

@@ -9,7 +9,7 @@
 //   k_chunk         (iso_chunk.h) the chunk pass of longer rows.
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
-//   k_merge_wave    (iso_merge.h) one launch per level of the merge tree, one wavefront per merge.
+//   k_merge_levels  (iso_merge.h) three levels of the merge tree per launch, one wavefront per merge.
 //   k_ends          per chunk: its range of surviving vertices and the slopes into and out of it,
 //                   by bisection over the root list (Section 3.4).
 //   k_fit           per chunk: every element not already final gets the slope of the hull edge

@@ -1,4 +1,4 @@
-// iso_merge.h -- one level of the segment-list merge tree with one wavefront per merge (gfx950).
+// iso_merge.h -- the levels of the segment-list merge tree, one wavefront per merge (gfx950).
 //
 // "Merge Hulls Without Copying Vertices: GPU Isotonic Regression":
 //   Section 3.3 / Definition 4.3 / Theorem 4.4  a node's hull is a list of segments (chunk,
@@ -10,8 +10,10 @@
 //   Section 5.2  a walk that runs long is replaced by a search (here the Overmars-van Leeuwen
 //                bisection of iso_geom.h).
 //
-// On the page a level runs one thread per merge when it has many merges.  Here every merge has
-// a wavefront.  It first reads up to 64 list-form vertices on each side of s into registers and
+// On the page a level runs one thread per merge when it has many merges, one launch per level.
+// Here every merge has a wavefront, and one launch takes three levels: a workgroup of four
+// wavefronts merges a subtree of eight nodes (four merges, then two, then one, with a barrier
+// between levels), so a row of m chunks needs ceil(log2 m / 3) launches.  It first reads up to 64 list-form vertices on each side of s into registers and
 // runs both walks there, one ballot per walk (window_bridge); that settles nearly every merge
 // of the lower levels.  A longer walk continues in memory 256 vertices at a time: the lanes
 // gather the next vertices of the walk (the segments' lengths come from one coalesced read of
@@ -362,19 +364,10 @@ __device__ __forceinline__ bool window_bridge(const VS& S, const NodeList& LA, c
   return false;
 }
 
+// Merges node A (chunks from jA) with node B (chunks from jB) of one row: one wavefront.
 template <typename T, bool W, bool D>
-__global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<T, W, D> S,
-                                                                    int64_t batch, int r,
-                                                                    int per_row) {
-  __shared__ MergeLds sw[kMergeWaves][2];
-  __shared__ WideLds sww[kMergeWaves];
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * kMergeWaves + wid;
-  if (t >= batch * per_row) return;  // the whole wavefront
-  const int64_t row = t / per_row;
-  const int qm = (int)(t - row * per_row);
-  const int jA = qm << (r + 1);
-  const int jB = jA + (1 << r);
+__device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_t row, int jA, int jB,
+                                           int lane, MergeLds& WA, MergeLds& WB, WideLds& Ww) {
   const int64_t rb = row * S.m;
   Desc* dA = S.desc + rb + jA;
   Desc* dB = S.desc + rb + jB;
@@ -385,7 +378,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
   VRef al, be;
   GPt Pa, Pb;
   const GPt Sp = load_v(S, LA, list_last(LA));
-  bool settled = window_bridge(S, LA, LB, lane, sw[wid][0], sw[wid][1], Sp, al, be, Pa, Pb);
+  bool settled = window_bridge(S, LA, LB, lane, WA, WB, Sp, al, be, Pa, Pb);
   if (!settled) {
     // both walks may already stop where the windows ended (always the case at a strictly convex
     // s, which dense-form chunks, outside the windows, reach this way): one step of each side
@@ -424,7 +417,6 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
       continue;
     }
     // the walk continues in memory, kWalkK * 64 vertices at a time, from where it stands
-    WideLds& Ww = sww[wid];
     bool searched = false;
     for (int pass = 0; pass < 4 * kChunk; ++pass) {
       bool moved = false;
@@ -503,6 +495,33 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_wave(VertexStore<
     }
   }
   if (lane == 0) S.nseg[rb + jA] = nA + nB;
+}
+
+// Levels r0 .. r0 + nlev - 1 of the merge tree in one launch (nlev <= kMergeGroup): a workgroup
+// takes the subtree over 2^(r0 + nlev) chunks of one row and merges it level by level, its
+// wavefronts separated by a barrier between levels.  A merge reads only its two children's lists
+// (and the chunk hulls, which no merge writes), so subtrees are independent; per_row = subtrees
+// per row.
+constexpr int kMergeGroup = 3;  // 2^(kMergeGroup - 1) = kMergeWaves merges at the group's first level
+static_assert((1 << (kMergeGroup - 1)) <= kMergeWaves, "a group's first level needs a wavefront per merge");
+template <typename T, bool W, bool D>
+__global__ __launch_bounds__(kMergeWaves * kWave) void k_merge_levels(VertexStore<T, W, D> S, int r0,
+                                                                      int nlev, int64_t per_row) {
+  __shared__ MergeLds sw[kMergeWaves][2];
+  __shared__ WideLds sww[kMergeWaves];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x / per_row;
+  const int64_t sub = (int64_t)blockIdx.x - row * per_row;
+  for (int k = 0; k < nlev; ++k) {
+    const int r = r0 + k;
+    const int nm = 1 << (nlev - 1 - k);  // merges of the subtree at level r
+    if (wid < nm) {
+      const int64_t jA = (sub * nm + wid) << (r + 1);
+      const int64_t jB = jA + ((int64_t)1 << r);
+      if (jB < S.m) merge_pair(S, row, (int)jA, (int)jB, lane, sw[wid][0], sw[wid][1], sww[wid]);
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace iso
