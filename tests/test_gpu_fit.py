@@ -185,6 +185,22 @@ def test_row_of_8194_chunks():
     check(y, w, kkt=False)
 
 
+@pytest.mark.parametrize("chunks", [9, 17, 65])
+def test_batched_rows_of_several_merge_subtrees(chunks):
+    """Batches of rows of 9, 17 and 65 chunks, the last one ragged.  The merge tree of such a row
+    has 4, 5 and 7 levels, so its levels do not split evenly into groups of three, and its first
+    group holds 2, 3 and 9 subtrees of eight chunks.  Every row must be merged from its own
+    chunks.  Three families are run: the mixed trend (long walks at the upper levels), noise, and
+    integers (whose partition must match exactly)."""
+    n = (chunks - 1) * 16384 + 1001
+    y, w = W.mixed_1e8(seed=chunks, n=n, batch=3)
+    check(y, w, kkt=False)
+    y, w = W.family("noise", 3, n, seed=chunks, dtype="f64", wkind="uniform")
+    check(y, w, kkt=False)
+    y, w = W.family("integer", 3, n, seed=chunks, dtype="f32", wkind="integer")
+    check(y, w, exact_partition=True, kkt=False)
+
+
 def test_65537_long_rows():
     """A batch of 65537 rows of 2049 (long rows, one chunk each): more rows than a grid's second
     dimension holds."""
