@@ -45,34 +45,50 @@ def _case(rng):
     return n, batch, fam, wkind, dtype, dec, null_w
 
 
+def _run_case(rng, n, batch, fam, wkind, dtype, dec, null_w):
+    y, w = W.family(fam, batch, n, seed=int(rng.integers(1 << 30)), dtype=dtype, wkind=wkind)
+    ww = None if null_w else w
+    z, bs, rf = gpu_fit(y, ww, decreasing=dec)
+    zo, bo, fo = oracle.pav(y.astype(np.float64), None if ww is None else ww.astype(np.float64),
+                            return_blocks=True, decreasing=dec)
+    zo = zo.reshape(y.shape)
+    bo = bo.reshape(y.shape)
+    tag = (n, batch, fam, wkind, dtype, dec, null_w)
+    np.testing.assert_array_equal(rf.astype(np.uint32), fo, err_msg=str(tag))
+    zz = z.astype(np.float64)
+    degenerate = wkind == "extreme" and fam in ("constant", "cancel") and dtype == "f64"
+    if fam == "cancel":  # measured against max |y| (the page's Section 7.6 measure)
+        dev = float(np.max(np.abs(zz - zo)) / np.max(np.abs(y.astype(np.float64))))
+        assert dev <= (1e-7 if degenerate else 1e-14 if dtype == "f64" else 1e-7), (tag, dev)
+    else:
+        dev = float(np.max(np.abs(zz - zo) / (1 + np.abs(zo))))
+        assert dev <= (1e-7 if degenerate else TOL[y.dtype.type]), (tag, dev)
+    if degenerate:
+        steps = np.diff(zz, axis=1)
+        wrong = float(np.max(steps if dec else -steps, initial=0.0)) / max(1.0, float(np.max(np.abs(zz))))
+        assert wrong <= 1e-7, (tag, wrong)
+    if fam in EXACT and wkind in ("unit", "integer"):
+        np.testing.assert_array_equal(bs, bo, err_msg=str(tag))
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_sweep(seed):
     rng = np.random.default_rng(1000 + seed)
     for _ in range(6):
-        n, batch, fam, wkind, dtype, dec, null_w = _case(rng)
-        y, w = W.family(fam, batch, n, seed=int(rng.integers(1 << 30)), dtype=dtype, wkind=wkind)
-        ww = None if null_w else w
-        z, bs, rf = gpu_fit(y, ww, decreasing=dec)
-        zo, bo, fo = oracle.pav(y.astype(np.float64), None if ww is None else ww.astype(np.float64),
-                                return_blocks=True, decreasing=dec)
-        zo = zo.reshape(y.shape)
-        bo = bo.reshape(y.shape)
-        tag = (n, batch, fam, wkind, dtype, dec, null_w)
-        np.testing.assert_array_equal(rf.astype(np.uint32), fo, err_msg=str(tag))
-        zz = z.astype(np.float64)
-        degenerate = wkind == "extreme" and fam in ("constant", "cancel") and dtype == "f64"
-        if fam == "cancel":  # measured against max |y| (the page's Section 7.6 measure)
-            dev = float(np.max(np.abs(zz - zo)) / np.max(np.abs(y.astype(np.float64))))
-            assert dev <= (1e-7 if degenerate else 1e-14 if dtype == "f64" else 1e-7), (tag, dev)
-        else:
-            dev = float(np.max(np.abs(zz - zo) / (1 + np.abs(zo))))
-            assert dev <= (1e-7 if degenerate else TOL[y.dtype.type]), (tag, dev)
-        if degenerate:
-            steps = np.diff(zz, axis=1)
-            wrong = float(np.max(steps if dec else -steps, initial=0.0)) / max(1.0, float(np.max(np.abs(zz))))
-            assert wrong <= 1e-7, (tag, wrong)
-        if fam in EXACT and wkind in ("unit", "integer"):
-            np.testing.assert_array_equal(bs, bo, err_msg=str(tag))
+        _run_case(rng, *_case(rng))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_long_row_batches(seed):
+    """Batches of 1 to 4 rows of 2 to 75 chunks of 16384 with a ragged last chunk: merge trees of
+    1 to 7 levels, cut into launches of three levels with one workgroup per subtree of eight
+    chunks, so that a batch holds many subtrees and rows end inside a subtree."""
+    rng = np.random.default_rng(3000 + seed)
+    for _ in range(3):
+        n = int(rng.integers(16385, 75 * 16384 + 1))
+        batch = int(rng.integers(1, 5))
+        _, _, fam, wkind, dtype, dec, null_w = _case(rng)
+        _run_case(rng, n, batch, fam, wkind, dtype, dec, null_w)
 
 
 @pytest.mark.parametrize("seed", range(4))
