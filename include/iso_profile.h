@@ -7,8 +7,9 @@
  * dominant kernel inside its own timed region.
  *
  * Stages: 0 whole-diagram chunks (k_increasing), 1 chunk pass (k_chunk; k_wave for rows of at
- * most 2048 elements), 2 chunk-start scan (2 launches), 3 merge levels (ceil(log2 m) launches),
- * 4 ends, 5 fit.  Rows of at most 2048 elements run stage 1 only.
+ * most 8192 elements, k_tiny for rows of at most 16), 2 chunk-start scan (2 launches), 3 merge
+ * levels (three levels of the tree per launch: ceil(ceil(log2 m) / 3) launches for m chunks),
+ * 4 ends, 5 fit.  Rows of at most 8192 elements run stage 1 only.
  *
  * While enabled, every iso_fit_ex call records one event before its first kernel and one after
  * each stage, on its stream.  The state is process-global and not thread-safe: enable, run the
