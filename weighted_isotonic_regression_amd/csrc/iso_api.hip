@@ -275,8 +275,12 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   hipLaunchKernelGGL((k_ends<T, W, D>), dim3((unsigned)((G + 255) / 256)), dim3(256), 0, s, S, ends,
                      batch);
   prof.mark(1);
-  hipLaunchKernelGGL((k_fit<T, W, D>), dim3((unsigned)G), dim3(kFitThreads), 0, s, S,
-                     (const EndInfo*)ends, (const uint32_t*)rflags, (const uint8_t*)co.ztile, z, bstart);
+  // a chunk's fit is split over up to kFitMaxSub workgroups when there are fewer than about 2048
+  // chunks, so that rows of a few chunks still occupy the chip
+  const int nsub = (int)std::max<int64_t>(1, std::min<int64_t>(kFitMaxSub, 2048 / std::max<int64_t>(G, 1)));
+  hipLaunchKernelGGL((k_fit<T, W, D>), dim3((unsigned)(G * nsub)), dim3(kFitThreads), 0, s, S,
+                     (const EndInfo*)ends, (const uint32_t*)rflags, (const uint8_t*)co.ztile, z, bstart,
+                     nsub);
   prof.mark(1);
   return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
 }

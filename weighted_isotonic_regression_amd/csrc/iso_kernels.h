@@ -628,8 +628,9 @@ __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W, D> S, EndInfo* _
 }
 
 // ------------------------------------------------------------------ fit
-// One workgroup of 256 threads per chunk, element-parallel (consecutive threads, consecutive
-// elements).  Elements outside the chunk's surviving vertex range [klo, khi) lie under the edges
+// nsub workgroups of 256 threads per chunk (nsub > 1 when there are too few chunks to fill the
+// chip), element-parallel: the chunk's threads t = sub * 256 + tid take consecutive elements, or
+// words, in turn.  Elements outside the chunk's surviving vertex range [klo, khi) lie under the edges
 // into and out of it; inside it they lie under the chunk hull's own edges (Corollary 4.5).
 //   list chunks:  the surviving vertices' point indices and the slopes between them are staged in
 //                 LDS and each element finds its edge by binary search.
@@ -640,24 +641,29 @@ __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W, D> S, EndInfo* _
 //                 one recomputation of that end point.  A one-element edge is its element's y,
 //                 which the chunk pass already wrote in tiles where nothing was popped.
 constexpr int kFitThreads = 256;
+constexpr int kFitMaxSub = 4;  // workgroups per chunk at most
 
 template <typename T, bool W, bool D>
 __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
                                                      const EndInfo* __restrict__ ends,
                                                      const uint32_t* __restrict__ rflags,
                                                      const uint8_t* __restrict__ ztile,
-                                                     T* __restrict__ z, uint8_t* __restrict__ bstart) {
+                                                     T* __restrict__ z, uint8_t* __restrict__ bstart,
+                                                     int nsub) {
   __shared__ double sSlope[kListCap];
   __shared__ int sK[kListCap];
   __shared__ uint32_t sMask[kMaskW];
   constexpr int TN = Tile<T, W>::N;
-  const int64_t g = blockIdx.x;
+  const int64_t g = blockIdx.x / nsub;
+  const int sub = (int)(blockIdx.x - g * nsub);
   const int64_t row = g / S.m;
   const int j = (int)(g - row * S.m);
   const int64_t off = row * S.n + (int64_t)j * kChunk;
   const int64_t rem = S.n - (int64_t)j * kChunk;
   const int len = rem < kChunk ? (int)rem : kChunk;
   const int tid = threadIdx.x;
+  const int t0 = sub * kFitThreads + tid;  // this thread's rank among the chunk's threads
+  const int tstride = nsub * kFitThreads;
   const EndInfo e = ends[g];
   // 16-byte groups of consecutive elements per thread (scalar stores where z is not aligned)
   constexpr int VN = Vec16<T>::N;
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     T zo[VN];
 #pragma unroll
     for (int u = 0; u < VN; ++u) zo[u] = zv;
-    for (int i0 = tid * VN; i0 < len; i0 += kFitThreads * VN) {
+    for (int i0 = t0 * VN; i0 < len; i0 += tstride * VN) {
       if (zvec && i0 + VN <= len) {
         store16(z + off + i0, zo);
       } else {
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     // row's hull (point 0 possibly as the previous chunk's last vertex): every element is its own
     // block, and z = y was written for the whole chunk
     if (bstart) {
-      for (int i = tid; i < len; i += kFitThreads) bstart[off + i] = 1;
+      for (int i = t0; i < len; i += tstride) bstart[off + i] = 1;
     }
     return;
   }
@@ -710,7 +716,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     // next one are all vertices, in tiles whose z the chunk pass wrote, needs nothing
     auto bit = [&](int i) { return ((sMask[i >> 5] >> (i & 31)) & 1u) != 0u; };
     const int nw = (len + 31) >> 5;
-    for (int wd = tid; wd < nw; wd += kFitThreads) {
+    for (int wd = t0; wd < nw; wd += tstride) {
       const int i0 = wd << 5;
       const int i1 = min(i0 + 32, len);
       if (i0 >= e.klo && i1 <= e.khi && sMask[wd] == 0xffffffffu && (sMask[wd + 1] & 1u)) {
@@ -808,7 +814,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
   // a thread takes VN consecutive elements: the first one inside [klo, khi) finds its edge by
   // binary search (edge q covers [sK[q], sK[q + 1])), the next ones step to the following edge
   // when they reach its first point
-  for (int i0 = tid * VN; i0 < len; i0 += kFitThreads * VN) {
+  for (int i0 = t0 * VN; i0 < len; i0 += tstride * VN) {
     T zo[VN];
     uint8_t so[VN];
     int q = -1;
