@@ -2,10 +2,10 @@
 //
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
 //   n <= 16     one lane per row, pool adjacent violators in registers and LDS (k_tiny)
-//   n <= 8192   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront (rows
-//               over 2048: one row per workgroup of 2 or 4 wavefronts); one launch of k_wave
+//   n <= 4096   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront (rows
+//               over 2048: one row per workgroup of 2 wavefronts); one launch of k_wave
 //               writes z, block starts and row flags (Section 3.5).
-//   n >  8192   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
+//   n >  4096   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
 //               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls),
 //               k_scan_reduce + k_scan_apply (chunk starts),
 //               ceil(ceil(log2 m) / 3) launches of k_merge_levels, k_ends, k_fit
@@ -46,9 +46,10 @@ struct Layout {
   size_t total = 0;
   size_t o_rflags = 0, o_any = 0;
   // long rows only
-  size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0, o_lx = 0,
-         o_ly = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0, o_ckx = 0, o_cky = 0, o_zt = 0,
-         o_df = 0, o_bnd = 0, o_bndk = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
+  size_t o_tot = 0, o_totl = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0,
+         o_lx = 0, o_ly = 0, o_lxl = 0, o_lyl = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0,
+         o_lsxl = 0, o_lsyl = 0, o_ckx = 0, o_cky = 0, o_ckxl = 0, o_ckyl = 0, o_zt = 0, o_df = 0,
+         o_bnd = 0, o_bndl = 0, o_bndk = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
   int64_t m = 0, nblk = 0;
 };
 
@@ -69,6 +70,7 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.nblk = (L.m + kScanBlock - 1) / kScanBlock;
     const size_t G = (size_t)batch * (size_t)L.m;
     L.o_tot = take(G * sizeof(double2));
+    L.o_totl = take(G * sizeof(double2));
     L.o_start = take(G * sizeof(double4));
     L.o_nv = take(G * sizeof(int));
     L.o_cf = take(G * sizeof(uint32_t));
@@ -77,15 +79,22 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.o_lk = take(G * (size_t)kListCap * sizeof(uint16_t));
     L.o_lx = take(G * (size_t)kListCap * sizeof(double));
     L.o_ly = take(G * (size_t)kListCap * sizeof(double));
+    L.o_lxl = take(G * (size_t)kListCap * sizeof(double));
+    L.o_lyl = take(G * (size_t)kListCap * sizeof(double));
     L.o_mask = take(G * (size_t)kMaskW * sizeof(uint32_t));
     L.o_mcnt = take(G * (size_t)kMaskW * sizeof(uint16_t));
     L.o_lsx = take(G * (size_t)kWave * sizeof(double));
     L.o_lsy = take(G * (size_t)kWave * sizeof(double));
+    L.o_lsxl = take(G * (size_t)kWave * sizeof(double));
+    L.o_lsyl = take(G * (size_t)kWave * sizeof(double));
     L.o_ckx = take(G * (size_t)kWave * kLaneW * sizeof(double));
     L.o_cky = take(G * (size_t)kWave * kLaneW * sizeof(double));
+    L.o_ckxl = take(G * (size_t)kWave * kLaneW * sizeof(double));
+    L.o_ckyl = take(G * (size_t)kWave * kLaneW * sizeof(double));
     L.o_zt = take(G * (size_t)kZTiles);
     L.o_df = take(G);
     L.o_bnd = take(G * sizeof(double4));
+    L.o_bndl = take(G * sizeof(double4));
     L.o_bndk = take(G * sizeof(int2));
     L.o_ends = take(G * sizeof(EndInfo));
     L.o_bsum = take((size_t)batch * (size_t)L.nblk * sizeof(double4));
@@ -189,11 +198,8 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
       const int64_t tiles = (batch + R - 1) / R;
       hipLaunchKernelGGL((k_wave<T, W, D, 1>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
                          rflags, batch, n, L);
-    } else if (L == 2 * kWave) {  // one row per workgroup of two wavefronts
+    } else {  // one row per workgroup of two wavefronts
       hipLaunchKernelGGL((k_wave<T, W, D, 2>), dim3((unsigned)batch), dim3(2 * kWave), 0, s, y, w, z, bstart,
-                         rflags, batch, n, L);
-    } else {  // one row per workgroup of four wavefronts
-      hipLaunchKernelGGL((k_wave<T, W, D, 4>), dim3((unsigned)batch), dim3(4 * kWave), 0, s, y, w, z, bstart,
                          rflags, batch, n, L);
     }
     prof.mark(1);
@@ -204,6 +210,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   const int64_t G = batch * (int64_t)m;
   ChunkOut co;
   co.tot = (double2*)(ws + Lay.o_tot);
+  co.totl = (double2*)(ws + Lay.o_totl);
   co.nverts = (int*)(ws + Lay.o_nv);
   co.cflags = (uint32_t*)(ws + Lay.o_cf);
   co.desc = (Desc*)(ws + Lay.o_desc);
@@ -211,15 +218,22 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   co.lk = (uint16_t*)(ws + Lay.o_lk);
   co.lx = (double*)(ws + Lay.o_lx);
   co.ly = (double*)(ws + Lay.o_ly);
+  co.lxl = (double*)(ws + Lay.o_lxl);
+  co.lyl = (double*)(ws + Lay.o_lyl);
   co.mask = (uint32_t*)(ws + Lay.o_mask);
   co.mcnt = (uint16_t*)(ws + Lay.o_mcnt);
   co.lsx = (double*)(ws + Lay.o_lsx);
   co.lsy = (double*)(ws + Lay.o_lsy);
+  co.lsxl = (double*)(ws + Lay.o_lsxl);
+  co.lsyl = (double*)(ws + Lay.o_lsyl);
   co.ckx = (double*)(ws + Lay.o_ckx);
   co.cky = (double*)(ws + Lay.o_cky);
+  co.ckxl = (double*)(ws + Lay.o_ckxl);
+  co.ckyl = (double*)(ws + Lay.o_ckyl);
   co.ztile = (uint8_t*)(ws + Lay.o_zt);
   co.dform = (uint8_t*)(ws + Lay.o_df);
   co.bnd = (double4*)(ws + Lay.o_bnd);
+  co.bndl = (double4*)(ws + Lay.o_bndl);
   co.bndk = (int2*)(ws + Lay.o_bndk);
   double4* start = (double4*)(ws + Lay.o_start);
   double4* bsum = (double4*)(ws + Lay.o_bsum);
@@ -232,9 +246,9 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   hipLaunchKernelGGL((k_chunk<T, W, D>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
-                     s, co.tot, co.cflags, bsum, bflag, m, nblk);
+                     s, co.tot, co.totl, co.cflags, bsum, bflag, m, nblk);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
-                     co.tot, bsum, bflag, start, rflags, m, nblk);
+                     co.tot, co.totl, bsum, bflag, start, rflags, m, nblk);
   prof.mark(2);
   VertexStore<T, W, D> S;
   S.desc = co.desc;
@@ -243,16 +257,24 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   S.dense = co.dform;
   S.lx = co.lx;
   S.ly = co.ly;
+  S.lxl = co.lxl;
+  S.lyl = co.lyl;
   S.lk = co.lk;
   S.mask = co.mask;
   S.mcnt = co.mcnt;
   S.lsx = co.lsx;
   S.lsy = co.lsy;
+  S.lsxl = co.lsxl;
+  S.lsyl = co.lsyl;
   S.ckx = co.ckx;
   S.cky = co.cky;
+  S.ckxl = co.ckxl;
+  S.ckyl = co.ckyl;
   S.bnd = co.bnd;
+  S.bndl = co.bndl;
   S.bndk = co.bndk;
   S.tot = co.tot;
+  S.totl = co.totl;
   S.start = start;
   S.y = y;
   S.w = w;

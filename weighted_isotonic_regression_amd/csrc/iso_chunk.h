@@ -12,8 +12,13 @@
 //   Section 3.3  the chunk's hull is emitted for the merge levels, as a vertex list when it is
 //                small and as a bit mask with coordinate checkpoints when it is dense.
 //   Section 6    "Coordinates": a lane works in coordinates relative to its first point; the
-//                chunk-relative coordinates are its start (a wave scan of the lane totals) plus
-//                those.  All sums are fp64.
+//                chunk-relative coordinates are its start (a double-double wave scan of the lane
+//                totals) plus those.  Running sums are pairs (hi, lo): hi is the fp64 running sum
+//                the chain works with, lo the exact sum of its rounding errors.
+//   Section 6    "Predicates": a turn of the chain is evaluated on the hi parts and used when it
+//                exceeds an a-priori bound in terms of the lane's magnitudes; otherwise the three
+//                points' pairs are recomputed from their checkpoints and the turn is decided in
+//                double-double arithmetic.
 //
 // Per lane state: the top three stack entries in registers, the last kRingS entries in an LDS
 // ring indexed by depth, the stack as a bit mask in LDS, and the running sums every 32 points (the
@@ -37,24 +42,32 @@ namespace iso {
 
 // Per-chunk outputs of the chunk pass.
 struct ChunkOut {
-  double2* tot;       // [G] chunk end point (W, S), chunk-relative
+  double2* tot;       // [G] chunk end point (W, S), chunk-relative: hi parts
+  double2* totl;      // [G] and lo parts
   int* nverts;        // [G] vertex count of the chunk hull
   uint32_t* cflags;   // [G] input flags of the chunk
   Desc* desc;         // [G] leaf segment list
   int* nseg;          // [G]
   uint16_t* lk;       // [G * kListCap] list form: chunk point index
-  double* lx;         // [G * kListCap]
+  double* lx;         // [G * kListCap] chunk-relative pairs
   double* ly;
+  double* lxl;
+  double* lyl;
   uint32_t* mask;     // [G * kMaskW] dense form: vertex bits of chunk points 0..16384
   uint16_t* mcnt;     // [G * kMaskW] set bits before each word
-  double* lsx;        // [G * kWave] lane starts (chunk-relative)
+  double* lsx;        // [G * kWave] lane starts (chunk-relative pairs)
   double* lsy;
-  double* ckx;        // [G * kWave * kLaneW] lane-relative running sums at points 32 j
+  double* lsxl;
+  double* lsyl;
+  double* ckx;        // [G * kWave * kLaneW] lane-relative running sums at points 32 j (pairs)
   double* cky;
+  double* ckxl;
+  double* ckyl;
   uint8_t* ztile;     // [G * kZTiles] 1 where the lane chains wrote z = y for the load tile
   uint8_t* dform;     // [G] 0 list form, 1 dense form, 2 dense form with every point a vertex
                       //     and z = y written for the whole chunk
-  double4* bnd;       // [G] dense form: coordinates of hull vertices 1 and V - 2
+  double4* bnd;       // [G] dense form: coordinates of hull vertices 1 and V - 2 (hi parts)
+  double4* bndl;      // [G] (lo parts)
   int2* bndk;         // [G] their point indices
 };
 
@@ -105,7 +118,8 @@ struct ChunkLds {
   uint32_t smask[kSubW][kWave];  // stack bit mask over the lane's points 0..256
   int depth[kWave];              // final stack depth
   int lo[kWave], hi[kWave];      // surviving depth range of the lane's stack
-  double2 start[kWave + 1];      // lane starts, chunk-relative; [l + 1] is lane l's end point
+  double2 start[kWave + 1];      // lane starts, chunk-relative (hi); [l + 1] is lane l's end point
+  double2 startl[kWave + 1];     // (lo)
 };
 
 // Ring slot of stack depth i.
@@ -160,6 +174,39 @@ __device__ double2 lane_point(const double* ckx, const double* cky, int l, int q
   }
   if (!W) P.x = (double)q;
   return P;
+}
+
+// Lane-relative pairs of lane l's point q, from the checkpoint pairs below q and the inputs (the
+// chain's operations in its order, so its hi parts are lane_point's).
+template <typename T, bool W, bool D>
+__device__ PD lane_point_dd(const double* ckx, const double* cky, const double* ckxl, const double* ckyl, int l,
+                            int q, int c, const T* yl, const T* wl) {
+  constexpr bool EX = ExactProd<T, W>::value;
+  q = min(max(q, 0), c);
+  const int j = min(q / kCk, kLaneW - 1);
+  DD ax{0.0, 0.0}, ay{cky[l * kLaneW + j], ckyl[l * kLaneW + j]};
+  if (W) ax = DD{ckx[l * kLaneW + j], ckxl[l * kLaneW + j]};
+  uint32_t f = 0u;
+  for (int e = kCk * j; e < q; ++e) {
+    double yd = yval<D>(yl[e]), wd = W ? (double)wl[e] : 1.0;
+    classify<W>(yd, wd, f);
+    if (W) acc(ax.hi, ax.lo, wd);
+    acc_prod<EX>(ay.hi, ay.lo, wd, yd);
+  }
+  if (!W) ax = DD{(double)q, 0.0};
+  return PD{ax, ay};
+}
+
+// Turn (U, T, K) of lane l's stack entries U = point ui and T = point ti (recomputed from their
+// checkpoints) and K, the lane's running sums (kx + kxl, ky + kyl), in double-double arithmetic.
+// Out of line: the chain reaches it only when its fast turn is inside the error bound.
+template <typename T, bool W, bool D>
+__device__ __noinline__ double chain_turn_dd(const double* ckx, const double* cky, const double* ckxl,
+                                             const double* ckyl, int l, int ui, int ti, int c, const T* yl,
+                                             const T* wl, double kx, double kxl, double ky, double kyl) {
+  const PD Up = lane_point_dd<T, W, D>(ckx, cky, ckxl, ckyl, l, ui, c, yl, wl);
+  const PD Tp = lane_point_dd<T, W, D>(ckx, cky, ckxl, ckyl, l, ti, c, yl, wl);
+  return turn_dd(Up, Tp, PD{DD{kx, kxl}, DD{ky, kyl}}).hi;
 }
 
 // Stack mask word ww of lane l; the word the chain is filling (cw) is still in a register.
@@ -239,25 +286,60 @@ __device__ __forceinline__ double2 chunk_entry(const ChunkLds<W>& L, const doubl
   return chunk_entry<T, W, D>(L, ckx, cky, l, i, len, yc, wc, q);
 }
 
+// Chunk-relative pairs of the stack entry at depth i of lane l: the lane's start, its end point
+// (the next lane's start) or the start plus the entry's lane-relative pairs.
+template <typename T, bool W, bool D>
+__device__ PD chunk_entry_dd(const ChunkLds<W>& L, const double* ckx, const double* cky, const double* ckxl,
+                             const double* ckyl, int l, int i, int len, const T* yc, const T* wc, int& q) {
+  const int c = min(max(len - kSub * l, 0), kSub);
+  if (i == 0 || i == L.depth[l] - 1) {
+    const int ls = i == 0 ? l : l + 1;
+    q = i == 0 ? 0 : c;
+    return PD{DD{L.start[ls].x, L.startl[ls].x}, DD{L.start[ls].y, L.startl[ls].y}};
+  }
+  bool in_ring;
+  q = lane_index<W>(L, l, i, c, in_ring);
+  const PD a = lane_point_dd<T, W, D>(ckx, cky, ckxl, ckyl, l, q, c, yc + kSub * l, W ? wc + kSub * l : nullptr);
+  return VertexStore<T, W, D>::join(DD{L.start[l].x, L.startl[l].x}, DD{L.start[l].y, L.startl[l].y}, a.x, a.y,
+                                    kSub * l + q);
+}
+
+// Turn of three stack entries (lane, depth) of the chunk's lanes from their chunk-relative pairs.
+template <typename T, bool W, bool D>
+__device__ __noinline__ double entries_turn_dd(const ChunkLds<W>* L, const double* ckx, const double* cky,
+                                               const double* ckxl, const double* ckyl, int l1, int i1, int l2,
+                                               int i2, int l3, int i3, int len, const T* yc, const T* wc) {
+  int q;
+  const PD Q1 = chunk_entry_dd<T, W, D>(*L, ckx, cky, ckxl, ckyl, l1, i1, len, yc, wc, q);
+  const PD Q2 = chunk_entry_dd<T, W, D>(*L, ckx, cky, ckxl, ckyl, l2, i2, len, yc, wc, q);
+  const PD Q3 = chunk_entry_dd<T, W, D>(*L, ckx, cky, ckxl, ckyl, l3, i3, len, yc, wc, q);
+  return turn_dd(Q1, Q2, Q3).hi;
+}
+
 // Chunks whose elements are all clean and strictly increasing.  Every turn of such a chunk's
 // diagram compares two consecutive y values, so every point P_0 .. P_len is a strict vertex of the
 // chunk hull: the hull is the whole diagram and every element is its own block.  A workgroup of
 // kIncWaves wavefronts streams the chunk's len elements with coalesced nontemporal 16-byte loads
 // and stores (wavefront q takes the q-th of kIncWaves equal parts), checks the pattern, writes
 // z = y and stores the dense form directly: vertex bits of points 0..len set, lane starts,
-// checkpoints (here block sums accumulated in a fixed order; every later coordinate of the chunk
-// is computed from these stored values), and the cache of vertices 1 and V - 2 computed exactly
-// as the stored-form readers recompute points.  It keeps no z tile marks: form 2 itself tells the
+// checkpoints (here double-double block sums accumulated in a fixed order; every later coordinate
+// of the chunk is computed from these stored pairs), and the cache of vertices 1 and V - 2
+// computed exactly as the stored-form readers recompute points.  It keeps no z tile marks: form 2 itself tells the
 // fit that z = y holds for every element.  It returns false, having written only z, when an
 // element breaks the pattern; the lane chains then process the chunk and rewrite everything.
-// Requires len >= 2 * kCk and 16-byte aligned y, w, z.  bsx, bsy: 512 doubles each of LDS
-// (block sums); bad: an int of LDS.
+// Requires len >= 2 * kCk and 16-byte aligned y, w, z.  bs: LDS for the 512 block sums (pairs of x
+// and y); bad: an int of LDS.
 constexpr int kIncWaves = 4;
+
+struct BlockSums {
+  double x[kChunk / kCk], xl[kChunk / kCk], y[kChunk / kCk], yl[kChunk / kCk];
+};
 
 template <typename T, bool W, bool D>
 __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__ wc,
                                  T* __restrict__ zc, int len, int64_t g, int j,
-                                 const ChunkOut& out, double* bsx, double* bsy, int* bad) {
+                                 const ChunkOut& out, BlockSums& bs, int* bad) {
+  constexpr bool EX = ExactProd<T, W>::value;
   constexpr int VN = Vec16<T>::N;
   constexpr int U = 4;                   // vectors per lane per step
   constexpr int SE = kWave * VN * U;     // elements per step of one wavefront
@@ -310,7 +392,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
       const double last = yval<D>(yv[u * VN + VN - 1]);
       double prev = __shfl_up(last, 1, kWave);
       if (lane == 0) prev = carry;
-      double sw = 0.0, sy = 0.0;
+      DD sw{0.0, 0.0}, sy{0.0, 0.0};
 #pragma unroll
       for (int k = 0; k < VN; ++k) {
         if (e + k < q1) {
@@ -318,19 +400,25 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
           const double wd = W ? (double)wv_[u * VN + k] : 1.0;
           ok = ok && isfinite(yd) && isfinite(wd) && wd > 0.0 && prev < yd;
           prev = yd;
-          if (W) sw += wd;
-          sy += wd * yd;
+          if (W) acc(sw.hi, sw.lo, wd);
+          acc_prod<EX>(sy.hi, sy.lo, wd, yd);
         }
       }
       carry = __shfl(last, kWave - 1, kWave);
+      // block sums: a butterfly of double-double additions (commutative bit for bit, so every
+      // lane of a block holds the same pair)
 #pragma unroll
       for (int o = 1; o < BL; o <<= 1) {
-        if (W) sw += __shfl_xor(sw, o, kWave);
-        sy += __shfl_xor(sy, o, kWave);
+        if (W) sw = dd_add(sw, DD{__shfl_xor(sw.hi, o, kWave), __shfl_xor(sw.lo, o, kWave)});
+        sy = dd_add(sy, DD{__shfl_xor(sy.hi, o, kWave), __shfl_xor(sy.lo, o, kWave)});
       }
       if ((lane & (BL - 1)) == 0 && e < q1) {
-        if (W) bsx[e / kCk] = sw;
-        bsy[e / kCk] = sy;
+        if (W) {
+          bs.x[e / kCk] = sw.hi;
+          bs.xl[e / kCk] = sw.lo;
+        }
+        bs.y[e / kCk] = sy.hi;
+        bs.yl[e / kCk] = sy.lo;
       }
       if (e + VN <= q1) {
         store16_nt(zc + e, &yv[u * VN]);
@@ -352,41 +440,50 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   // blocks; a block past len sums to zero) and its total; jv = the block of point len - 1 in the
   // lane that holds it
   const int kv = len - 1, lv = kv / kSub, jv = (kv % kSub) / kCk;
-  double cx = 0.0, cy = 0.0, cvx = 0.0, cvy = 0.0;
+  DD cx{0.0, 0.0}, cy{0.0, 0.0}, cvx{0.0, 0.0}, cvy{0.0, 0.0};
   const int64_t cb = (g * kWave + lane) * (int64_t)kLaneW;
 #pragma unroll
   for (int jj = 0; jj < kLaneW; ++jj) {
-    if (W) out.ckx[cb + jj] = cx;
-    out.cky[cb + jj] = cy;
+    if (W) {
+      out.ckx[cb + jj] = cx.hi;
+      out.ckxl[cb + jj] = cx.lo;
+    }
+    out.cky[cb + jj] = cy.hi;
+    out.ckyl[cb + jj] = cy.lo;
     if (jj == jv) {
       cvx = cx;
       cvy = cy;
     }
     const int bi = kLaneW * lane + jj;
     if (kCk * bi < len) {
-      if (W) cx += bsx[bi];
-      cy += bsy[bi];
+      if (W) cx = dd_add(cx, DD{bs.x[bi], bs.xl[bi]});
+      cy = dd_add(cy, DD{bs.y[bi], bs.yl[bi]});
     }
   }
-  // lane starts: wave scan of the lane totals
-  double ix = cx, iy = cy;
+  // lane starts: double-double wave scan of the lane totals
+  DD ix = cx, iy = cy;
 #pragma unroll
   for (int dd = 1; dd < kWave; dd <<= 1) {
-    const double vx = __shfl_up(ix, dd, kWave);
-    const double vy = __shfl_up(iy, dd, kWave);
+    const DD vx{__shfl_up(ix.hi, dd, kWave), __shfl_up(ix.lo, dd, kWave)};
+    const DD vy{__shfl_up(iy.hi, dd, kWave), __shfl_up(iy.lo, dd, kWave)};
     if (lane >= dd) {
-      ix += vx;
-      iy += vy;
+      ix = dd_add(vx, ix);
+      iy = dd_add(vy, iy);
     }
   }
-  double sx = __shfl_up(ix, 1, kWave), sy = __shfl_up(iy, 1, kWave);
+  DD sx{__shfl_up(ix.hi, 1, kWave), __shfl_up(ix.lo, 1, kWave)};
+  DD sy{__shfl_up(iy.hi, 1, kWave), __shfl_up(iy.lo, 1, kWave)};
   if (lane == 0) {
-    sx = 0.0;
-    sy = 0.0;
+    sx = DD{0.0, 0.0};
+    sy = DD{0.0, 0.0};
   }
-  if (!W) sx = (double)(kSub * lane);
-  if (W) out.lsx[g * kWave + lane] = sx;
-  out.lsy[g * kWave + lane] = sy;
+  if (!W) sx = DD{(double)(kSub * lane), 0.0};
+  if (W) {
+    out.lsx[g * kWave + lane] = sx.hi;
+    out.lsxl[g * kWave + lane] = sx.lo;
+  }
+  out.lsy[g * kWave + lane] = sy.hi;
+  out.lsyl[g * kWave + lane] = sy.lo;
   // vertex bits of points 0..len, set bits before each word
   const int64_t mb = g * (int64_t)kMaskW;
 #pragma unroll
@@ -399,13 +496,16 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     out.mcnt[mb + kLaneW * lane + wd] = (uint16_t)min(w0, len + 1);
   }
   if (lane == 0) {
-    // vertex 1 = point 1: lane 0's checkpoint 0 (zero) plus element 0
+    // vertex 1 = point 1: lane 0's start and checkpoint 0 (zero) plus element 0
     const double w0 = W ? (double)wc[0] : 1.0;
-    double ax = 0.0, ay = 0.0;
-    if (W) ax += w0;
-    ay += w0 * yval<D>(yc[0]);
-    out.bnd[g].x = W ? 0.0 + ax : 1.0;
-    out.bnd[g].y = 0.0 + ay;
+    DD ax{0.0, 0.0}, ay{0.0, 0.0};
+    if (W) acc(ax.hi, ax.lo, w0);
+    acc_prod<EX>(ay.hi, ay.lo, w0, yval<D>(yc[0]));
+    const PD P = VertexStore<T, W, D>::join(sx, sy, ax, ay, 1);
+    out.bnd[g].x = P.x.hi;
+    out.bnd[g].y = P.y.hi;
+    out.bndl[g].x = P.x.lo;
+    out.bndl[g].y = P.y.lo;
     out.bndk[g].x = 1;
     out.nverts[g] = len + 1;
     out.desc[g] = make_int4(j, 0, len, desc_w(2, len + 1));
@@ -416,12 +516,13 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   if (lane == kWave - 1) {
     out.mask[mb + kMaskW - 1] = len == kChunk ? 1u : 0u;  // point 16384
     out.mcnt[mb + kMaskW - 1] = (uint16_t)min(kChunk, len + 1);
-    out.tot[g] = make_double2(W ? ix : (double)len, iy);
+    out.tot[g] = make_double2(W ? ix.hi : (double)len, iy.hi);
+    out.totl[g] = make_double2(W ? ix.lo : 0.0, iy.lo);
   }
   if (lane == lv) {
     // vertex V - 2 = point len - 1: this lane's checkpoint below it plus its elements from the
     // checkpoint on, in order (all loads issued before the first add)
-    double ax = cvx, ay = cvy;
+    DD ax = cvx, ay = cvy;
     const int e0v = kSub * lv + kCk * jv;
     T ye[kCk - 1], we[kCk - 1];
 #pragma unroll
@@ -433,12 +534,15 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     for (int k = 0; k < kCk - 1; ++k) {
       if (e0v + k < kv) {
         const double wd = W ? (double)we[k] : 1.0;
-        if (W) ax += wd;
-        ay += wd * yval<D>(ye[k]);
+        if (W) acc(ax.hi, ax.lo, wd);
+        acc_prod<EX>(ay.hi, ay.lo, wd, yval<D>(ye[k]));
       }
     }
-    out.bnd[g].z = W ? sx + ax : (double)kv;
-    out.bnd[g].w = sy + ay;
+    const PD P = (kv % kSub == 0) ? PD{sx, sy} : VertexStore<T, W, D>::join(sx, sy, ax, ay, kv);
+    out.bnd[g].z = P.x.hi;
+    out.bnd[g].w = P.y.hi;
+    out.bndl[g].z = P.x.lo;
+    out.bndl[g].w = P.y.lo;
     out.bndk[g].y = kv;
   }
   return true;
@@ -452,8 +556,7 @@ __global__ __launch_bounds__(kIncWaves * kWave) void k_increasing(const T* __res
                                                                   const T* __restrict__ w,
                                                                   T* __restrict__ z, int64_t n,
                                                                   int m, ChunkOut out) {
-  __shared__ double bsx[kChunk / kCk];
-  __shared__ double bsy[kChunk / kCk];
+  __shared__ BlockSums bs;
   __shared__ int bad;
   const int64_t g = blockIdx.x;
   const int64_t row = g / m;
@@ -465,8 +568,7 @@ __global__ __launch_bounds__(kIncWaves * kWave) void k_increasing(const T* __res
                    (((uintptr_t)(z + off)) % 16 == 0);
   bool done = false;
   if (len >= 2 * kCk && vec)
-    done = increasing_chunk<T, W, D>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bsx, bsy,
-                                  &bad);
+    done = increasing_chunk<T, W, D>(y + off, W ? w + off : nullptr, z + off, len, g, j, out, bs, &bad);
   if (!done && threadIdx.x == 0) out.dform[g] = 3;
 }
 
@@ -476,6 +578,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
                                                         T* __restrict__ z, int64_t n, int m,
                                                         ChunkOut out) {
   __shared__ ChunkLds<W> L;
+  constexpr bool EX = ExactProd<T, W>::value;
   constexpr int TN = Tile<T, W>::N;  // elements per load tile
   constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
@@ -497,6 +600,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   T* zl = z + off + e0;
   double* ckx = out.ckx + g * (int64_t)(kWave * kLaneW);  // the chunk's checkpoints
   double* cky = out.cky + g * (int64_t)(kWave * kLaneW);
+  double* ckxl = out.ckxl + g * (int64_t)(kWave * kLaneW);
+  double* ckyl = out.ckyl + g * (int64_t)(kWave * kLaneW);
   if (out.dform[g] == 2) return;  // done by k_increasing
 
   // ---- a1-a3: stream the lane's elements through the chain.  Point P_q (0 < q < c) lies between
@@ -509,7 +614,9 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   // with their point indices ti, ui, vi and ring slots ts, us, vs.
   int d = 0, ti = 0, ui = 0, vi = 0, ts = 0, us = 0, vs = 0;
   double tx = 0.0, ty = 0.0, ux = 0.0, uy = 0.0, vx = 0.0, vy = 0.0;
-  double lx = 0.0, ly = 0.0;
+  double lx = 0.0, ly = 0.0;     // running sums (hi)
+  double lxl = 0.0, lyl = 0.0;   // their lo parts
+  double aabs = 0.0;             // sum of |w y| so far: bounds every |y| of the lane's points
   double yprev = 0.0;
   int wi = 0;
   uint32_t curw = 0u;
@@ -545,11 +652,23 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     }
     vchk = false;
   };
+  // The turn (U, T, K) of the hi parts.  Every point so far has 0 <= x <= Ax (the current x) and
+  // |y| <= Ay = sum |w y|, and each lo part is at most 257 u times those (256 rounded additions
+  // and the products' errors), so the fast turn is within 3100 u Ax Ay of the turn of the pairs
+  // (2^-41 = 4096 u).  Inside that bound U and T are recomputed from their checkpoints and the
+  // turn is decided in double-double arithmetic, K being the running sums themselves.
+  auto turn_utk = [&](const double kx, const double ky, const int q) {
+    double t = cross2(tx - ux, ty - uy, kx - ux, ky - uy);
+    const double E = ((W ? lx : (double)q) * 0x1p-41) * aabs;
+    if (d >= 2 && !(fabs(t) > E))
+      t = chain_turn_dd<T, W, D>(ckx, cky, ckxl, ckyl, lane, ui, ti, c, yl, wl, kx, W ? lxl : 0.0, ky, lyl);
+    return t;
+  };
   // pushes point q with lane-relative coordinates (kx, ky), first popping what it makes
   // non-convex (pop while the turn (U, T, K) is not strictly left).  A popped entry's stack bit
   // is cleared in LDS (the word being filled is rewritten from curw later) and in curw.
   auto push = [&](const double kx, const double ky, const int q) {
-    bool more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
+    bool more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
     if (more) {
       while (more) {
         check_v();
@@ -579,7 +698,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         }
         vtag = tg;  // (the point index and the check wait until V is used)
         vchk = true;
-        more = (d >= 2) & !(cross2(tx - ux, ty - uy, kx - ux, ky - uy) > 0.0);
+        more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
       }
     }
     const int ks = ring_next(ts);
@@ -622,8 +741,12 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   for (int t = 0; t < ntiles; ++t) {
     const int eb = t * TN;  // lane-relative index of the tile's first element
     if ((eb & (kCk - 1)) == 0) {
-      if (W) ckx[lane * kLaneW + eb / kCk] = lx;
+      if (W) {
+        ckx[lane * kLaneW + eb / kCk] = lx;
+        ckxl[lane * kLaneW + eb / kCk] = lxl;
+      }
       cky[lane * kLaneW + eb / kCk] = ly;
+      ckyl[lane * kLaneW + eb / kCk] = lyl;
     }
     if ((eb >> 5) != wi) {  // the tile's points 32 w .. are in mask word w (same for every lane)
       L.smask[wi][lane] = curw;
@@ -680,8 +803,10 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         if (yprev < yd) push(W ? lx : (double)q, ly, q);
         else skipped = true;
       }
-      if (W) lx += wd;
-      ly += wd * yd;
+      if (W) acc(lx, lxl, wd);
+      const double p = wd * yd;
+      acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+      aabs += fabs(p);
       yprev = yd;
     };
     // pushes the tile's points eb + k, k >= kp, without tests, and consumes its elements k >= kc
@@ -710,8 +835,11 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         }
         if (k >= kc) {
           const double wd = W ? (double)wv[k] : 1.0;
-          if (W) lx += wd;
-          ly += wd * yval<D>(yv[k]);
+          const double yd = yval<D>(yv[k]);
+          if (W) acc(lx, lxl, wd);
+          const double p = wd * yd;
+          acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+          aabs += fabs(p);
         }
       }
       yprev = yval<D>(yv[TN - 1]);
@@ -749,8 +877,12 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
     // point of the lane has one)
     if ((c & (kCk - 1)) == 0 && c < kSub) {
-      if (W) ckx[lane * kLaneW + c / kCk] = lx;
+      if (W) {
+        ckx[lane * kLaneW + c / kCk] = lx;
+        ckxl[lane * kLaneW + c / kCk] = lxl;
+      }
       cky[lane * kLaneW + c / kCk] = ly;
+      ckyl[lane * kLaneW + c / kCk] = lyl;
     }
     if ((c >> 5) != wi) {
       L.smask[wi][lane] = curw;
@@ -762,28 +894,37 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   }
   for (int t = ntiles; t < kSub / TN; ++t) out.ztile[g * (int64_t)kZTiles + (e0 + t * TN) / TN] = 0;
 
-  // ---- lane starts: wave scan of the lane totals (chunk-relative coordinates).
-  double ix = lx, iy = ly;
+  // ---- lane starts: double-double wave scan of the lane totals (chunk-relative coordinates).
+  DD ix = two_sum(lx, lxl), iy = two_sum(ly, lyl);
 #pragma unroll
   for (int dd = 1; dd < kWave; dd <<= 1) {
-    const double vx = __shfl_up(ix, dd, kWave);
-    const double vy = __shfl_up(iy, dd, kWave);
+    const DD vx{__shfl_up(ix.hi, dd, kWave), __shfl_up(ix.lo, dd, kWave)};
+    const DD vy{__shfl_up(iy.hi, dd, kWave), __shfl_up(iy.lo, dd, kWave)};
     if (lane >= dd) {
-      ix += vx;
-      iy += vy;
+      ix = dd_add(vx, ix);
+      iy = dd_add(vy, iy);
     }
   }
-  double sx = __shfl_up(ix, 1, kWave), sy = __shfl_up(iy, 1, kWave);
+  DD sx{__shfl_up(ix.hi, 1, kWave), __shfl_up(ix.lo, 1, kWave)};
+  DD sy{__shfl_up(iy.hi, 1, kWave), __shfl_up(iy.lo, 1, kWave)};
   if (lane == 0) {
-    sx = 0.0;
-    sy = 0.0;
+    sx = DD{0.0, 0.0};
+    sy = DD{0.0, 0.0};
   }
   if (!W) {
-    sx = (double)e0;
-    ix = (double)(e0 + c);
+    sx = DD{(double)e0, 0.0};
+    ix = DD{(double)(e0 + c), 0.0};
   }
-  L.start[lane] = double2{sx, sy};
-  if (lane == nl - 1) L.start[lane + 1] = double2{ix, iy};
+  L.start[lane] = double2{sx.hi, sy.hi};
+  L.startl[lane] = double2{sx.lo, sy.lo};
+  if (lane == nl - 1) {
+    L.start[lane + 1] = double2{ix.hi, iy.hi};
+    L.startl[lane + 1] = double2{ix.lo, iy.lo};
+  }
+  // bound of the in-chunk walks' fast turns: chunk-relative x in [0, Xc], |y| <= Yc
+  double yc_abs = aabs;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) yc_abs += __shfl_xor(yc_abs, o, kWave);
   L.depth[lane] = d;
   int lo = 1, hi = d - 1;  // depth 0 is the previous lane's end point (lane 0: the chunk start)
   L.lo[lane] = lo;
@@ -809,6 +950,15 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       bi = L.lo[bl];
       double2 Pa = chunk_entry<T, W, D>(L, ckx, cky, al, ai, len, yc, wc);
       double2 Pb = chunk_entry<T, W, D>(L, ckx, cky, bl, bi, len, yc, wc);
+      // a strict left turn of three stack entries: the fast turn of the chunk-relative hi parts
+      // (each within 259 u of Xc or Yc of its pair: start, lane lo, rounding) when it exceeds
+      // 2^-41 Xc Yc, else the turn of the pairs
+      const double Ec = ((W ? L.start[nl].x : (double)len) * 0x1p-41) * yc_abs;
+      auto wleft = [&](int l1, int i1, double2 P1, int l2, int i2, double2 P2, int l3, int i3, double2 P3) {
+        const double t = turn_pts(P1, P2, P3);
+        if (fabs(t) > Ec) return t > 0.0;
+        return entries_turn_dd<T, W, D>(&L, ckx, cky, ckxl, ckyl, l1, i1, l2, i2, l3, i3, len, yc, wc) > 0.0;
+      };
       for (int pass = 0; pass <= kChunk; ++pass) {
         bool moved = false;
         // alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
@@ -828,7 +978,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
             }
           }
           const double2 Pp = chunk_entry<T, W, D>(L, ckx, cky, pl, pi, len, yc, wc);
-          if (turn_pts(Pp, Pa, Pb) > 0.0) break;
+          if (wleft(pl, pi, Pp, al, ai, Pa, bl, bi, Pb)) break;
           al = pl;
           ai = pi;
           Pa = Pp;
@@ -845,7 +995,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
             qi = max(L.lo[ql], 1);
           }
           const double2 Pq = chunk_entry<T, W, D>(L, ckx, cky, ql, qi, len, yc, wc);
-          if (turn_pts(Pa, Pb, Pq) > 0.0) break;
+          if (wleft(al, ai, Pa, bl, bi, Pb, ql, qi, Pq)) break;
           bl = ql;
           bi = qi;
           Pb = Pq;
@@ -892,8 +1042,9 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     out.nseg[g] = 1;
     out.cflags[g] = fl;
     out.dform[g] = listable ? 0 : 1;
-    const double2 E = L.start[nl];
+    const double2 E = L.start[nl], El = L.startl[nl];
     out.tot[g] = make_double2(E.x, E.y);
+    out.totl[g] = make_double2(El.x, El.y);
   }
   if (listable) {
     const int64_t lb0 = g * (int64_t)kListCap;
@@ -902,14 +1053,18 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       out.lk[lb0] = 0;
       out.lx[lb0] = 0.0;
       out.ly[lb0] = 0.0;
+      out.lxl[lb0] = 0.0;
+      out.lyl[lb0] = 0.0;
       pos = 1;
     }
     for (int i = lo; i <= hi; ++i) {
       int q;
-      const double2 P = chunk_entry<T, W, D>(L, ckx, cky, lane, i, len, yc, wc, q);
+      const PD P = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, lane, i, len, yc, wc, q);
       out.lk[lb0 + pos] = (uint16_t)(e0 + q);
-      out.lx[lb0 + pos] = P.x;
-      out.ly[lb0 + pos] = P.y;
+      out.lx[lb0 + pos] = P.x.hi;
+      out.ly[lb0 + pos] = P.y.hi;
+      out.lxl[lb0 + pos] = P.x.lo;
+      out.lyl[lb0 + pos] = P.y.lo;
       ++pos;
     }
     return;
@@ -923,9 +1078,11 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     const int lz = 63 - __builtin_clzll(nz);  // vertex V - 1 ends the last range
     if (lane == l1) {
       int q;
-      const double2 P = chunk_entry<T, W, D>(L, ckx, cky, lane, lo, len, yc, wc, q);
-      out.bnd[g].x = P.x;
-      out.bnd[g].y = P.y;
+      const PD P = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, lane, lo, len, yc, wc, q);
+      out.bnd[g].x = P.x.hi;
+      out.bnd[g].y = P.y.hi;
+      out.bndl[g].x = P.x.lo;
+      out.bndl[g].y = P.y.lo;
       out.bndk[g].x = e0 + q;
     }
     // vertex V - 2: the entry before lz's last, or the last of the range before it, or point 0
@@ -936,15 +1093,17 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     if (lane == src) {
       const bool in_lz = lzc >= 1;
       int i = in_lz ? hi - 1 : hi;
-      double2 P{0.0, 0.0};
+      PD P{DD{0.0, 0.0}, DD{0.0, 0.0}};
       int kq = 0;
       if (in_lz || before) {
         int q;
-        P = chunk_entry<T, W, D>(L, ckx, cky, lane, i, len, yc, wc, q);
+        P = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, lane, i, len, yc, wc, q);
         kq = e0 + q;
       }
-      out.bnd[g].z = P.x;
-      out.bnd[g].w = P.y;
+      out.bnd[g].z = P.x.hi;
+      out.bnd[g].w = P.y.hi;
+      out.bndl[g].z = P.x.lo;
+      out.bndl[g].w = P.y.lo;
       out.bndk[g].y = kq;
     }
   }
@@ -992,8 +1151,12 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     out.mcnt[mb + kMaskW - 1] = (uint16_t)run;
   }
   const int64_t sb = g * (int64_t)kWave;
-  if (W) out.lsx[sb + lane] = L.start[lane].x;
+  if (W) {
+    out.lsx[sb + lane] = L.start[lane].x;
+    out.lsxl[sb + lane] = L.startl[lane].x;
+  }
   out.lsy[sb + lane] = L.start[lane].y;
+  out.lsyl[sb + lane] = L.startl[lane].y;
 }
 
 }  // namespace iso

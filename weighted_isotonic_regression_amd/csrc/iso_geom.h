@@ -16,8 +16,12 @@
 //   Section 2.2 / 5.2  Overmars-van Leeuwen simultaneous bisection for the bridge of two
 //                x-separated hulls.  The page's case analysis (its Appendix A) did not survive,
 //                so the cases below are derived here from the slopes; see bridge_search().
-//   Section 6 "Coordinates"  chunk-relative coordinates plus double-double chunk starts, so
-//                that differences of nearby points keep their precision.
+//   Section 6 "Coordinates" / "Predicates"  every coordinate is a pair (hi, lo) whose sum is
+//                the coordinate: running sums carry the exact rounding error of each addition
+//                (and of each product w*y) in lo, lane and chunk starts are double-double.  A turn
+//                is first evaluated on the hi parts; when it falls inside an a-priori bound on
+//                the error of that evaluation, it is recomputed from the pairs in double-double
+//                arithmetic.  Slopes are formed from double-double differences.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,7 +33,7 @@ namespace iso {
 
 constexpr int kWave = 64;                    // lanes of a wavefront
 constexpr int kLanePts = 32;                 // elements per lane of a packed short-row tile
-constexpr int kShortMax = 4 * kWave * kLanePts;  // rows of at most this many go to the short-row kernel
+constexpr int kShortMax = 2 * kWave * kLanePts;  // rows of at most this many go to the short-row kernel
 constexpr int kSub = 256;                    // points per lane of a long-row chunk
 constexpr int kChunk = kWave * kSub;         // elements per chunk of a long row (one wavefront)
 constexpr int kCk = 32;                      // spacing of a lane's running-sum checkpoints
@@ -89,24 +93,87 @@ ISO_HD DD dd_add(DD a, DD b) {
   return quick_two_sum(s.hi, e);
 }
 
-// Sign-exact comparison helper: sign of (a*b - c*d) for exactly representable factors whose
-// products may exceed 2^53 (used by the separator test of the bridge search).
-ISO_HD double diff_of_products(double a, double b, double c, double d) {
-  double p1 = a * b;
-  double e1 = fma(a, b, -p1);
-  double p2 = c * d;
-  double e2 = fma(c, d, -p2);
-  return (p1 - p2) + (e1 - e2);
+ISO_HD DD two_prod(double a, double b) {
+  const double p = a * b;
+  return {p, fma(a, b, -p)};
+}
+
+ISO_HD DD dd_neg(DD a) { return {-a.hi, -a.lo}; }
+ISO_HD DD dd_sub(DD a, DD b) { return dd_add(a, dd_neg(b)); }
+
+ISO_HD DD dd_mul(DD a, DD b) {
+  DD p = two_prod(a.hi, b.hi);
+  const double c = a.hi * b.lo + a.lo * b.hi;
+  return quick_two_sum(p.hi, p.lo + c);
+}
+
+// Running sums.  acc adds v to the pair (hi, lo): hi becomes the rounded sum, as a plain fp64
+// running sum would, and the exact error of that addition goes to lo.  acc_pe adds a product p
+// whose own rounding error pe is known (zero when the product is exact).  After k additions
+// |lo| <= k u max|partial sum| (+ u sum|p| for inexact products), u = 2^-53.
+ISO_HD void acc_pe(double& hi, double& lo, double v, double pe) {
+  const double s = hi + v;
+  const double bb = s - hi;
+  const double e = (hi - (s - bb)) + (v - bb);
+  lo += e + pe;
+  hi = s;
+}
+ISO_HD void acc(double& hi, double& lo, double v) { acc_pe(hi, lo, v, 0.0); }
+
+// The increment w*y of one element.  For fp32 inputs and for unit weights the fp64 product is
+// exact; otherwise its rounding error is added to lo.
+template <bool EXACT>
+ISO_HD void acc_prod(double& hi, double& lo, double w, double y) {
+  const double p = w * y;
+  acc_pe(hi, lo, p, EXACT ? 0.0 : fma(w, y, -p));
+}
+template <typename T, bool W>
+struct ExactProd {
+  static constexpr bool value = !W || sizeof(T) == 4;
+};
+
+// A point of the diagram as a pair of double-double coordinates.
+struct PD {
+  DD x, y;
+};
+
+// turn(a, b, c) = (b - a) x (c - a) in double-double arithmetic (relative error a few u^2 of
+// the two products); its sign decides the predicate when the fast evaluation cannot.
+ISO_HD DD turn_dd(const PD& a, const PD& b, const PD& c) {
+  const DD dx1 = dd_sub(b.x, a.x), dy1 = dd_sub(b.y, a.y);
+  const DD dx2 = dd_sub(c.x, a.x), dy2 = dd_sub(c.y, a.y);
+  return dd_sub(dd_mul(dx1, dy2), dd_mul(dy1, dx2));
+}
+
+// dy / dx for double-double differences, rounded once (within about one ulp of the quotient of
+// the pairs): the quotient of the hi parts corrected by its remainder.
+ISO_HD double dd_quot(DD dy, DD dx) {
+  const double q = dy.hi / dx.hi;
+  const DD p = two_prod(q, dx.hi);
+  const double r = (((dy.hi - p.hi) - p.lo) + dy.lo) - q * dx.lo;
+  return q + r / dx.hi;
+}
+
+ISO_HD double slope_dd(const PD& a, const PD& b) { return dd_quot(dd_sub(b.y, a.y), dd_sub(b.x, a.x)); }
+
+// A little above u = 2^-53: the error of a rounded operation relative to its rounded result.
+constexpr double kU = 0x1.0001p-53;
+
+// Fast turn of three points given by their hi parts, for a predicate filter: t = turn(a, b, c)
+// with one rounded product.
+ISO_HD double turn_hi(double ax, double ay, double bx, double by, double cx, double cy) {
+  return cross2(bx - ax, by - ay, cx - ax, cy - ay);
 }
 
 // ------------------------------------------------------------------ lane hull
 
-// Monotone chain over the points 0..c of one lane (c <= 32), read through P(k, &x, &y).
-// Returns the hull as a bit mask (bit k set iff point k is a vertex).  A point is popped when
-// the turn (under, top, next) is <= 0, so collinear middle points are dropped.  Every iteration
+// Monotone chain over the points 0..c of one lane (c <= 32), read through P(k, &x, &y) (hi
+// parts) and Q(k) (the point as a PD).  Returns the hull as a bit mask (bit k set iff point k is
+// a vertex).  A point is popped when the turn (under, top, next) is <= 0, so collinear middle
+// points are dropped; a fast turn within E of zero is decided by turn_dd.  Every iteration
 // either pops or pushes, and exactly one point load is issued per iteration.
-template <class PtFn>
-ISO_HD uint64_t lane_chain(int c, PtFn P) {
+template <class PtFn, class PdFn>
+ISO_HD uint64_t lane_chain(int c, PtFn P, PdFn Q, double E) {
   if (c <= 0) return 0;
   if (c == 1) return 3ull;
   uint64_t mask = 3ull;
@@ -117,7 +184,8 @@ ISO_HD uint64_t lane_chain(int c, PtFn P) {
   P(2, kx, ky);
   // <= 2c iterations: each point is pushed once and popped at most once.
   for (int it = 0; it < 2 * kLanePts + 2 && k <= c; ++it) {
-    double t = cross2(tx - ux, ty - uy, kx - ux, ky - uy);
+    double t = turn_hi(ux, uy, tx, ty, kx, ky);
+    if (!(fabs(t) > E)) t = turn_dd(Q(und), Q(top), Q(k)).hi;
     bool pop = (top != 0) && (t <= 0.0);
     int load_idx;
     if (pop) {
@@ -187,16 +255,22 @@ ISO_HD void mask_clear_between(uint32_t* M, int a, int b) {
 }
 
 // Merge of two neighbouring nodes of one tile by walking (Lemma 4.2): node A spans points
-// [a0, s], node B spans [s, b1]; vertices are set bits of M, coordinates come from P.
+// [a0, s], node B spans [s, b1]; vertices are set bits of M, coordinates come from P (hi parts)
+// and Q (pairs), with fast turns within E of zero decided by turn_dd.
 // The bridge (alpha, beta) is found with alpha the leftmost contact in A (s included) and beta
 // the rightmost contact in B \ {s}; the bits strictly between them are cleared.
-template <class PtFn>
-ISO_HD void tile_walk_merge(uint32_t* M, int a0, int s, int b1, PtFn P) {
+template <class PtFn, class PdFn>
+ISO_HD void tile_walk_merge(uint32_t* M, int a0, int s, int b1, PtFn P, PdFn Q, double E) {
   int al = s;
   int be = mask_succ(M, s);
   double ax, ay, bx, by;
   P(al, ax, ay);
   P(be, bx, by);
+  auto left = [&](int i, double ix, double iy, int j, double jx, double jy, int k, double kx, double ky) {
+    const double t = turn_hi(ix, iy, jx, jy, kx, ky);
+    if (fabs(t) > E) return t > 0.0;
+    return turn_dd(Q(i), Q(j), Q(k)).hi > 0.0;
+  };
   // Each move removes a vertex of A or B, so the total number of moves is below b1 - a0.
   for (int pass = 0; pass <= b1 - a0; ++pass) {
     bool moved = false;
@@ -204,7 +278,7 @@ ISO_HD void tile_walk_merge(uint32_t* M, int a0, int s, int b1, PtFn P) {
       int p = mask_pred(M, al);
       double px, py;
       P(p, px, py);
-      if (cross2(ax - px, ay - py, bx - px, by - py) <= 0.0) {
+      if (!left(p, px, py, al, ax, ay, be, bx, by)) {
         al = p;
         ax = px;
         ay = py;
@@ -217,7 +291,7 @@ ISO_HD void tile_walk_merge(uint32_t* M, int a0, int s, int b1, PtFn P) {
       int q = mask_succ(M, be);
       double qx, qy;
       P(q, qx, qy);
-      if (cross2(bx - ax, by - ay, qx - ax, qy - ay) <= 0.0) {
+      if (!left(al, ax, ay, be, bx, by, q, qx, qy)) {
         be = q;
         bx = qx;
         by = qy;
@@ -233,32 +307,65 @@ ISO_HD void tile_walk_merge(uint32_t* M, int a0, int s, int b1, PtFn P) {
 
 // ------------------------------------------------------------------ segment lists
 
-// A point in row coordinates: chunk-relative (x, y) plus the chunk's double-double start.
+// A point in row coordinates: the chunk's double-double start (sxh, syh: hi parts) plus the
+// point's chunk-relative coordinates (x, y: hi parts), with the start's lo part and the local
+// lo part added into sxl, syl.  The represented coordinate is sxh + sxl + x (and likewise y):
+// folding the two lo parts costs a rounding of u |sxl|, far below the pairs' own accuracy.
 struct GPt {
   double x, y;
   double sxh, sxl, syh, syl;
 };
 
-// q - p with the coordinate hierarchy: the start difference first (exact for nearby chunks by
-// Sterbenz's lemma), then the local difference.  For two points of one chunk the starts cancel
-// to exactly zero and the result is the local difference.
-ISO_HD void gdiff(const GPt& p, const GPt& q, double& dx, double& dy) {
-  dx = ((q.sxh - p.sxh) + (q.sxl - p.sxl)) + (q.x - p.x);
-  dy = ((q.syh - p.syh) + (q.syl - p.syl)) + (q.y - p.y);
+// q - p with the coordinate hierarchy, on doubles: the start difference first (exact for nearby
+// chunks by Sterbenz's lemma; zero within one chunk), then the local difference.  ex, ey bound
+// the error against the represented difference: every rounded operation contributes at most kU
+// times its result.
+ISO_HD void gdiff(const GPt& p, const GPt& q, double& dx, double& dy, double& ex, double& ey) {
+  const double ax = q.sxh - p.sxh, bx = q.sxl - p.sxl, cx = ax + bx, lx = q.x - p.x;
+  dx = cx + lx;
+  ex = kU * (fabs(ax) + fabs(bx) + fabs(cx) + fabs(lx) + fabs(dx));
+  const double ay = q.syh - p.syh, by = q.syl - p.syl, cy = ay + by, ly = q.y - p.y;
+  dy = cy + ly;
+  ey = kU * (fabs(ay) + fabs(by) + fabs(cy) + fabs(ly) + fabs(dy));
 }
 
-ISO_HD double gturn(const GPt& a, const GPt& b, const GPt& c) {
-  double dx1, dy1, dx2, dy2;
-  gdiff(a, b, dx1, dy1);
-  gdiff(a, c, dx2, dy2);
-  return cross2(dx1, dy1, dx2, dy2);
+// q - p of the represented coordinates in double-double arithmetic.
+ISO_HD DD gdx_dd(const GPt& p, const GPt& q) {
+  return dd_add(dd_sub(DD{q.sxh, q.sxl}, DD{p.sxh, p.sxl}), two_sum(q.x, -p.x));
+}
+ISO_HD DD gdy_dd(const GPt& p, const GPt& q) {
+  return dd_add(dd_sub(DD{q.syh, q.syl}, DD{p.syh, p.syl}), two_sum(q.y, -p.y));
 }
 
-ISO_HD double gslope(const GPt& a, const GPt& b) {
-  double dx, dy;
-  gdiff(a, b, dx, dy);
-  return dy / dx;
+ISO_HD DD gturn_dd(const GPt& a, const GPt& b, const GPt& c) {
+  const DD dx1 = gdx_dd(a, b), dy1 = gdy_dd(a, b), dx2 = gdx_dd(a, c), dy2 = gdy_dd(a, c);
+  return dd_sub(dd_mul(dx1, dy2), dd_mul(dy1, dx2));
 }
+
+// turn(a, b, c) > 0 (a strict left turn): the fast turn when it exceeds its error bound, else the
+// sign of the double-double turn.  With |DX - dx| <= ex and so on, the fast turn
+// fma(dx1, dy2, -fl(dy1 dx2)) is within
+//   ex1 (|dy2| + ey2) + ey2 |dx1| + ex2 (|dy1| + ey1) + ey1 |dx2| + u (|dy1 dx2| + |t|)
+// of the turn of the represented points; the bound itself is evaluated with a margin for its
+// own rounding.
+// The rare second evaluation (inline: a call would pin the live registers of every call site).
+__device__ __forceinline__ bool gleft_slow(const GPt& a, const GPt& b, const GPt& c) { return gturn_dd(a, b, c).hi > 0.0; }
+
+__device__ __forceinline__ bool gleft(const GPt& a, const GPt& b, const GPt& c) {
+  double dx1, dy1, dx2, dy2, ex1, ey1, ex2, ey2;
+  gdiff(a, b, dx1, dy1, ex1, ey1);
+  gdiff(a, c, dx2, dy2, ex2, ey2);
+  const double p2 = dy1 * dx2;
+  const double t = fma(dx1, dy2, -p2);
+  double E = ex1 * (fabs(dy2) + ey2) + ey2 * fabs(dx1) + ex2 * (fabs(dy1) + ey1) + ey1 * fabs(dx2) +
+             kU * (fabs(p2) + fabs(t));
+  E = E * 1.001 + 0x1p-1000;
+  if (fabs(t) > E) return t > 0.0;
+  return gleft_slow(a, b, c);
+}
+
+// Slope of the edge from a to b, from double-double differences.
+ISO_HD double gslope(const GPt& a, const GPt& b) { return dd_quot(gdy_dd(a, b), gdx_dd(a, b)); }
 
 // Segment descriptor: x = chunk index within the row, y = first vertex position, z = last
 // vertex position (positions count the chunk hull's vertices from 0), w = the chunk hull's
@@ -272,32 +379,45 @@ ISO_HD int desc_nverts(const Desc& d) { return d.w >> 2; }
 
 // ------------------------------------------------------------------ chunk hull storage
 // A chunk's hull is stored in one of two forms:
-//   list   the vertices' chunk-relative coordinates and chunk point indices, in order (hulls of
-//          at most kListCap vertices whose coordinates the chunk pass had at hand);
+//   list   the vertices' chunk-relative coordinate pairs and chunk point indices, in order (hulls
+//          of at most kListCap vertices);
 //   dense  the vertex bit mask of the chunk's points 0..16384, the number of set bits before
-//          each word, the lane starts and every lane's running sums at each 32nd point.  A
-//          vertex's coordinates are recomputed from these and the inputs with the same fp64
+//          each word, the lane starts and every lane's running sums at each 32nd point, all as
+//          pairs.  A vertex's pairs are recomputed from these and the inputs with the same fp64
 //          operations in the same order as the chunk pass, so they are bitwise its values.
 // Dense chunks are the ones whose points nearly all survive; storing them as lists would move
-// about 18 bytes per element, while the dense form takes under one.
+// about 34 bytes per element, while the dense form takes under two.
+//
+// Chunk-relative point k of lane l (k = 256 l + q) is the double-double sum of the lane's start
+// S_l and the lane-relative running sum a(q) (accumulated with acc from the checkpoint below q);
+// a lane's end point is the next lane's start, the chunk's end point its total.
 template <typename T, bool W, bool D>
 struct VertexStore {
+  static constexpr bool EX = ExactProd<T, W>::value;
   Desc* desc;             // [G] descriptor slots
   int* nseg;              // [G] length of the list of the node starting at this slot
   const int* nverts;      // [G] vertex count of each chunk hull
   const uint8_t* dense;   // [G] 0 list form, 1 dense form, 2 dense form of an all-vertex chunk
-  const double* lx;       // [G * kListCap] list form
+  const double* lx;       // [G * kListCap] list form (pairs)
   const double* ly;
+  const double* lxl;
+  const double* lyl;
   const uint16_t* lk;
   const uint32_t* mask;   // [G * kMaskW] dense form
   const uint16_t* mcnt;   // [G * kMaskW]
-  const double* lsx;      // [G * kWave]  lane starts (weighted only)
-  const double* lsy;      // [G * kWave]
-  const double* ckx;      // [G * kWave * kLaneW] lane-relative running sums (weighted only)
+  const double* lsx;      // [G * kWave]  lane starts (weighted only: x), pairs
+  const double* lsy;
+  const double* lsxl;
+  const double* lsyl;
+  const double* ckx;      // [G * kWave * kLaneW] lane-relative running sums (weighted only: x)
   const double* cky;
-  const double2* tot;     // [G] chunk end point (W, S)
+  const double* ckxl;
+  const double* ckyl;
+  const double2* tot;     // [G] chunk end point (W, S), hi and lo parts
+  const double2* totl;
   const double4* start;   // [G] chunk start {x hi, x lo, y hi, y lo}
-  const double4* bnd;     // [G] dense form: coordinates of vertices 1 and V - 2
+  const double4* bnd;     // [G] dense form: vertices 1 and V - 2 {x1, y1, x2, y2}, hi and lo parts
+  const double4* bndl;
   const int2* bndk;       // [G] their point indices
   const T* y;
   const T* w;
@@ -306,111 +426,83 @@ struct VertexStore {
 
   ISO_HD bool is_list(int64_t g) const { return dense[g] == 0; }
 
-  // Chunk-relative coordinates of point k (0..len) of dense chunk j of `row`.
-  ISO_HD void dense_point(int64_t row, int j, int k, double& x, double& yy) const {
+  // Lane start S_l and lane-relative running sum a at point k (0 <= k < len) of dense chunk j:
+  // point k is S_l + a (for unit weights x is k itself), and adding elements k, k + 1, ... to a
+  // with acc gives the points after k up to the next multiple of 32.
+  ISO_HD void dense_state(int64_t row, int j, int k, DD& sx, DD& sy, DD& ax, DD& ay) const {
+    const int64_t g = row * m + j;
+    const int l = k / kSub, q = k % kSub;
+    sx = W ? DD{lsx[g * kWave + l], lsxl[g * kWave + l]} : DD{(double)(kSub * l), 0.0};
+    sy = DD{lsy[g * kWave + l], lsyl[g * kWave + l]};
+    ax = DD{0.0, 0.0};
+    ay = DD{0.0, 0.0};
+    if (q == 0) return;
+    const int jj = q / kCk;
+    const int64_t cb = (g * kWave + l) * kLaneW + jj;
+    if (W) ax = DD{ckx[cb], ckxl[cb]};
+    ay = DD{cky[cb], ckyl[cb]};
+    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
+    for (int e = kCk * jj; e < q; ++e) {
+      double wd = W ? (double)w[e0 + e] : 1.0;
+      double yd = yval<D>(y[e0 + e]);
+      if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
+        yd = 0.0;
+        wd = 1.0;
+      }
+      if (W) acc(ax.hi, ax.lo, wd);
+      acc_prod<EX>(ay.hi, ay.lo, wd, yd);
+    }
+  }
+
+  // The point whose lane start is (sx, sy) and lane-relative running sum (ax, ay), chunk point k.
+  ISO_HD static PD join(const DD& sx, const DD& sy, const DD& ax, const DD& ay, int k) {
+    return PD{W ? dd_add(sx, ax) : DD{(double)k, 0.0}, dd_add(sy, ay)};
+  }
+
+  // Chunk-relative pairs of point k (0..len) of dense chunk j of `row`.
+  ISO_HD PD dense_point(int64_t row, int j, int k) const {
     const int64_t g = row * m + j;
     const int64_t rem = n - (int64_t)j * kChunk;
     const int len = rem < kChunk ? (int)rem : kChunk;
     if (k == len) {
-      const double2 t = tot[g];
-      x = t.x;
-      yy = t.y;
-      return;
+      const double2 t = tot[g], tl = totl[g];
+      return PD{DD{t.x, tl.x}, DD{t.y, tl.y}};
     }
-    const int l = k / kSub, q = k % kSub;
-    const double sx = W ? lsx[g * kWave + l] : (double)(kSub * l);
-    const double sy = lsy[g * kWave + l];
-    if (q == 0) {
-      x = sx;
-      yy = sy;
-      return;
-    }
-    const int jj = q / kCk;
-    const int64_t cb = (g * kWave + l) * kLaneW + jj;
-    double ax = W ? ckx[cb] : 0.0, ay = cky[cb];
-    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
-    for (int e = kCk * jj; e < q; ++e) {
-      double wd = W ? (double)w[e0 + e] : 1.0;
-      double yd = yval<D>(y[e0 + e]);
-      if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
-        yd = 0.0;
-        wd = 1.0;
-      }
-      if (W) ax += wd;
-      ay += wd * yd;
-    }
-    x = W ? sx + ax : (double)k;
-    yy = sy + ay;
+    DD sx, sy, ax, ay;
+    dense_state(row, j, k, sx, sy, ax, ay);
+    if (k % kSub == 0) return PD{sx, sy};
+    return join(sx, sy, ax, ay, k);
   }
 
-  // Lane start (sx, sy) and lane-relative running sums (ax, ay) at point k (0 <= k < len) of
-  // dense chunk j: point k is (W ? sx + ax : k, sy + ay), with the operations of dense_point, so
-  // adding elements k, k + 1, ... to (ax, ay) in order gives dense_point's values of the points
-  // after k up to the next multiple of 32.
-  ISO_HD void dense_state(int64_t row, int j, int k, double& sx, double& sy, double& ax, double& ay) const {
-    const int64_t g = row * m + j;
-    const int l = k / kSub, q = k % kSub;
-    sx = W ? lsx[g * kWave + l] : (double)(kSub * l);
-    sy = lsy[g * kWave + l];
-    ax = 0.0;
-    ay = 0.0;
-    if (q == 0) return;
-    const int jj = q / kCk;
-    const int64_t cb = (g * kWave + l) * kLaneW + jj;
-    if (W) ax = ckx[cb];
-    ay = cky[cb];
-    const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
-    for (int e = kCk * jj; e < q; ++e) {
-      double wd = W ? (double)w[e0 + e] : 1.0;
-      double yd = yval<D>(y[e0 + e]);
-      if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
-        yd = 0.0;
-        wd = 1.0;
-      }
-      if (W) ax += wd;
-      ay += wd * yd;
-    }
-  }
-
-  // Chunk-relative coordinates and point index of vertex p of chunk j of `row`.
-  ISO_HD void local(int64_t row, int j, int p, double& x, double& yy, int& k) const {
+  // Chunk-relative pairs and point index of vertex p of chunk j of `row`.
+  ISO_HD PD local(int64_t row, int j, int p, int& k) const {
     const int64_t g = row * m + j;
     if (dense[g] == 0) {
       const int64_t idx = g * kListCap + p;
-      x = lx[idx];
-      yy = ly[idx];
       k = lk[idx];
-      return;
+      return PD{DD{lx[idx], lxl[idx]}, DD{ly[idx], lyl[idx]}};
     }
     // the vertices the merges and ends touch most: the chunk's two ends and their neighbours
     const int V = nverts[g];
     if (p == 0) {
-      x = 0.0;
-      yy = 0.0;
       k = 0;
-      return;
+      return PD{DD{0.0, 0.0}, DD{0.0, 0.0}};
     }
     if (p == V - 1) {
       const int64_t rem = n - (int64_t)j * kChunk;
       k = rem < kChunk ? (int)rem : kChunk;
-      const double2 t = tot[g];
-      x = t.x;
-      yy = t.y;
-      return;
+      const double2 t = tot[g], tl = totl[g];
+      return PD{DD{t.x, tl.x}, DD{t.y, tl.y}};
     }
     if (p == 1 || p == V - 2) {
-      const double4 b = bnd[g];
+      const double4 b = bnd[g], bl = bndl[g];
       const int2 bk = bndk[g];
       if (p == 1) {
-        x = b.x;
-        yy = b.y;
         k = bk.x;
-      } else {
-        x = b.z;
-        yy = b.w;
-        k = bk.y;
+        return PD{DD{b.x, bl.x}, DD{b.y, bl.y}};
       }
-      return;
+      k = bk.y;
+      return PD{DD{b.z, bl.z}, DD{b.w, bl.w}};
     }
     // select: the word holding the p-th set bit (the last word whose count of earlier set bits
     // is <= p), starting from where it would be if the bits were spread evenly, then the bit
@@ -422,22 +514,25 @@ struct VertexStore {
     uint32_t word = mask[g * kMaskW + lo];
     for (int r = p - (int)mc[lo]; r > 0; --r) word &= word - 1u;
     k = lo * 32 + __builtin_ctz(word);
-    dense_point(row, j, k, x, yy);
+    return dense_point(row, j, k);
+  }
+
+  ISO_HD static GPt make_gpt(const PD& P, const double4& s) {
+    GPt r;
+    r.x = P.x.hi;
+    r.y = P.y.hi;
+    r.sxh = s.x;
+    r.sxl = s.y + P.x.lo;
+    r.syh = s.z;
+    r.syl = s.w + P.y.lo;
+    return r;
   }
 
   // pt() for a chunk known to be in list form (one round of independent loads).
   ISO_HD GPt pt_list(int64_t row, int j, int p) const {
     const int64_t g = row * m + j;
     const int64_t idx = g * kListCap + p;
-    GPt r;
-    r.x = lx[idx];
-    r.y = ly[idx];
-    const double4 s = start[g];
-    r.sxh = s.x;
-    r.sxl = s.y;
-    r.syh = s.z;
-    r.syl = s.w;
-    return r;
+    return make_gpt(PD{DD{lx[idx], lxl[idx]}, DD{ly[idx], lyl[idx]}}, start[g]);
   }
 
   // pt() of vertex p of the chunk of descriptor d, whose form and vertex count the descriptor
@@ -447,39 +542,25 @@ struct VertexStore {
     if (form == 0) return pt_list(row, d.x, p);
     const int64_t g = row * m + d.x;
     if (p == 0 || p == V - 1 || p == 1 || p == V - 2) {
-      GPt r;
-      const double4 s = start[g];
-      r.sxh = s.x;
-      r.sxl = s.y;
-      r.syh = s.z;
-      r.syl = s.w;
+      PD P;
       if (p == 0) {
-        r.x = 0.0;
-        r.y = 0.0;
+        P = PD{DD{0.0, 0.0}, DD{0.0, 0.0}};
       } else if (p == V - 1) {
-        const double2 t = tot[g];
-        r.x = t.x;
-        r.y = t.y;
+        const double2 t = tot[g], tl = totl[g];
+        P = PD{DD{t.x, tl.x}, DD{t.y, tl.y}};
       } else {
-        const double4 b = bnd[g];
-        r.x = p == 1 ? b.x : b.z;
-        r.y = p == 1 ? b.y : b.w;
+        const double4 b = bnd[g], bl = bndl[g];
+        P = p == 1 ? PD{DD{b.x, bl.x}, DD{b.y, bl.y}} : PD{DD{b.z, bl.z}, DD{b.w, bl.w}};
       }
-      return r;
+      return make_gpt(P, start[g]);
     }
     return pt(row, d.x, p);
   }
 
   ISO_HD GPt pt(int64_t row, int j, int p) const {
-    GPt r;
     int k;
-    local(row, j, p, r.x, r.y, k);
-    const double4 s = start[row * m + j];
-    r.sxh = s.x;
-    r.sxl = s.y;
-    r.syh = s.z;
-    r.syl = s.w;
-    return r;
+    const PD P = local(row, j, p, k);
+    return make_gpt(P, start[row * m + j]);
   }
 };
 
@@ -566,22 +647,22 @@ ISO_HD bool bridge_search(const VS& S, const NodeList& LA, const NodeList& LB, V
     if (hasPA) {
       pi = list_pred(LA, i);
       pa = load_v(S, LA, pi);
-      Ab = gturn(pa, a, b) <= 0.0;
+      Ab = !gleft(pa, a, b);
     }
     if (!Ab && hasSA) {
       si = list_succ(LA, i);
       sa = load_v(S, LA, si);
-      Aa = gturn(a, sa, b) > 0.0;
+      Aa = gleft(a, sa, b);
     }
     if (hasSB) {
       sk = list_succ(LB, k);
       sb = load_v(S, LB, sk);
-      Bb = gturn(a, b, sb) <= 0.0;
+      Bb = !gleft(a, b, sb);
     }
     if (!Bb && hasPB) {
       pk = list_pred(LB, k);
       pb = load_v(S, LB, pk);
-      Ba = gturn(a, pb, b) > 0.0;
+      Ba = gleft(a, pb, b);
     }
     bool Ac = !Ab && !Aa, Bc = !Bb && !Ba;
     if (Ac && Bc) {
@@ -602,13 +683,10 @@ ISO_HD bool bridge_search(const VS& S, const NodeList& LA, const NodeList& LB, V
     if (Aa && Ba) {
       // Heights of s above l_A and above l_B, scaled by the edges' widths:
       //   h_A = turn(a_i, a_{i+1}, s) / dxA,  h_B = turn(b_{k-1}, b_k, s) / dxB.
-      // l_B(x_s) >= l_A(x_s)  <=>  h_B <= h_A  <=>  turnB * dxA <= turnA * dxB.
-      double dxA, dyA, dxB, dyB;
-      gdiff(a, sa, dxA, dyA);
-      gdiff(pb, b, dxB, dyB);
-      double tA = gturn(a, sa, Sp);
-      double tB = gturn(pb, b, Sp);
-      if (diff_of_products(tA, dxB, tB, dxA) >= 0.0) {
+      // l_B(x_s) >= l_A(x_s)  <=>  h_B <= h_A  <=>  turnB * dxA <= turnA * dxB (double-double).
+      const DD dxA = gdx_dd(a, sa), dxB = gdx_dd(pb, b);
+      const DD tA = gturn_dd(a, sa, Sp), tB = gturn_dd(pb, b, Sp);
+      if (dd_sub(dd_mul(tA, dxB), dd_mul(tB, dxA)).hi >= 0.0) {
         loA = si;
       } else {
         hiB = pk;
@@ -675,11 +753,9 @@ ISO_HD EndInfo chunk_ends(const VS& S, int64_t row, int j) {
   if (du.x == j) {
     e.lo = du.y;
     e.hi = du.z;
-    GPt plo = S.pt(row, j, du.y);
-    GPt phi = S.pt(row, j, du.z);
-    double tx, ty;
-    S.local(row, j, du.y, tx, ty, e.klo);
-    S.local(row, j, du.z, tx, ty, e.khi);
+    const double4 sj = S.start[g];
+    const GPt plo = S.make_gpt(S.local(row, j, du.y, e.klo), sj);
+    const GPt phi = S.make_gpt(S.local(row, j, du.z, e.khi), sj);
     e.sin = 0.0;
     e.sout = 0.0;
     if (u > 0) {

@@ -106,11 +106,11 @@ __device__ __forceinline__ void store16_nt(T* p, const T* in) {
   __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
 }
 
-// Elements per load tile of the chunk pass: 64 bytes of each input per lane when weights are
-// passed, 128 bytes otherwise (the tile and its prefetched successor stay in registers).
+// Elements per load tile of the chunk pass: 16 elements of each input per lane, 8 for weighted
+// fp64 (the tile and its prefetched successor stay in registers).
 template <typename T, bool W>
 struct Tile {
-  static constexpr int N = (W ? 64 : 128) / (int)sizeof(T);
+  static constexpr int N = (W && sizeof(T) == 8) ? 8 : 16;
 };
 
 // q = e / d for 0 <= e < 8192, 1 <= d <= 8192 (float reciprocal, corrected to exact).
@@ -133,19 +133,43 @@ struct TilePts {
   }
 };
 
+// The same points as pairs (x of an unweighted point is its index k0 + k, exact).
+template <bool W>
+struct TilePairs {
+  const double* sX;
+  const double* sY;
+  const double* sXl;
+  const double* sYl;
+  int base;
+  int k0;
+  __device__ __forceinline__ PD operator()(int k) const {
+    int idx = lds_pad(base + k);
+    return PD{W ? DD{sX[idx], sXl[idx]} : DD{(double)(k0 + k), 0.0}, DD{sY[idx], sYl[idx]}};
+  }
+};
+
+// Rows of 17 to 4096 elements.  Points are pairs (hi in sX/sY, lo in sXl/sYl): the lane's start,
+// from a double-double scan of the lane totals, plus the lane's running sums.  A fast turn is
+// used when it exceeds 2^-47 X Y, X the row's total weight (or length) and Y its sum of |w y|:
+// every hi part is within u of its pair's magnitude (at most X or Y), so the fast turn of three
+// points is within 26 u X Y of the turn of the pairs.  Slopes come from the pairs.
 template <typename T, bool W, bool D, int NW>
 __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
                                                      T* __restrict__ z, uint8_t* __restrict__ bstart,
                                                      uint32_t* __restrict__ rflags, int64_t batch,
                                                      int64_t n, int Lpack) {
+  static_assert(NW == 1 || NW == 2, "rows of at most 4096 elements");
+  constexpr bool EX = ExactProd<T, W>::value;
   constexpr int kThreads = NW * kWave;
   constexpr int kPts = lds_pts(NW);
   constexpr int kMW = mask_words(NW);
   __shared__ double sX[W ? kPts : 1];
   __shared__ double sY[kPts];
+  __shared__ double sXl[W ? kPts : 1];
+  __shared__ double sYl[kPts];
   __shared__ uint32_t sM[kMW];
   __shared__ uint32_t sF[kWave];
-  __shared__ double sWave[2 * NW];  // per wavefront: lane-total sums, then their prefixes
+  __shared__ double sWave[6 * NW];  // per wavefront: lane-total sums, then their prefixes
 
   constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
@@ -196,7 +220,8 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
     }
   }
   __syncthreads();
-  // classify and stage (w, w*y) in fp64 at each element's left point
+  // classify and stage (w, w*y) in fp64 at each element's left point, with the product's
+  // rounding error in the lo slot
 #pragma unroll
   for (int k = 0; k < kLanePts; ++k) {
     const int e = vec ? (lane + kThreads * (k / VN)) * VN + (k % VN) : lane + kThreads * k;
@@ -215,13 +240,16 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
       }
       const int slot = lds_pad(r * rowStride + i);
       if (W) sX[slot] = wd;
-      sY[slot] = wd * yd;
+      const double p = wd * yd;
+      sY[slot] = p;
+      sYl[slot] = EX ? 0.0 : fma(wd, yd, -p);
     }
   }
   __syncthreads();
 
-  // ---- a2: cumulative sums.  Lane-serial fp64 sums of its 32 increments, a segmented wave
-  // scan of the lane totals, then each lane rewrites its slots with chunk-relative points.
+  // ---- a2: cumulative sums.  Lane-serial sums (pairs) of its 32 increments, a segmented
+  // double-double scan of the lane totals, then each lane rewrites its slots with row-relative
+  // pairs.
   const int lgL = __builtin_ctz(L);
   const int r2 = lane >> lgL;
   const int ql = lane & (L - 1);
@@ -234,89 +262,116 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
   const int rbase = r2 * rowStride;
   const int pbase = rbase + kLanePts * ql;
   const int nl = (seglen + kLanePts - 1) / kLanePts;  // active lanes of a row segment
+  double Erow;  // the row's turn bound
   {
-    double tx = 0.0, ty = 0.0;
+    DD tx{0.0, 0.0}, ty{0.0, 0.0};
+    double ta = 0.0;
     for (int k = 0; k < kLanePts; ++k) {
       if (k < c) {
         const int idx = lds_pad(pbase + k);
-        if (W) tx += sX[idx];
-        ty += sY[idx];
+        if (W) acc(tx.hi, tx.lo, sX[idx]);
+        acc_pe(ty.hi, ty.lo, sY[idx], sYl[idx]);
+        ta += fabs(sY[idx]);
       }
     }
-    double ix = tx, iy = ty, sx0, sy0;
+    tx = two_sum(tx.hi, tx.lo);
+    ty = two_sum(ty.hi, ty.lo);
+    DD ix = tx, iy = ty, sx0, sy0;
+    double xr = tx.hi, ar = ta;  // row sums of the lane totals (for the bound)
     if constexpr (NW == 1) {
       for (int d = 1; d < L; d <<= 1) {
-        double vx = __shfl_up(ix, d, L);
-        double vy = __shfl_up(iy, d, L);
+        const DD vx{__shfl_up(ix.hi, d, L), __shfl_up(ix.lo, d, L)};
+        const DD vy{__shfl_up(iy.hi, d, L), __shfl_up(iy.lo, d, L)};
         if (ql >= d) {
-          ix += vx;
-          iy += vy;
+          ix = dd_add(vx, ix);
+          iy = dd_add(vy, iy);
         }
+        xr += __shfl_xor(xr, d, L);
+        ar += __shfl_xor(ar, d, L);
       }
-      sx0 = __shfl_up(ix, 1, L);
-      sy0 = __shfl_up(iy, 1, L);
+      sx0 = DD{__shfl_up(ix.hi, 1, L), __shfl_up(ix.lo, 1, L)};
+      sy0 = DD{__shfl_up(iy.hi, 1, L), __shfl_up(iy.lo, 1, L)};
       if (ql == 0) {
-        sx0 = 0.0;
-        sy0 = 0.0;
+        sx0 = DD{0.0, 0.0};
+        sy0 = DD{0.0, 0.0};
       }
     } else {
-      // one row over NW wavefronts: a scan in each, then the wavefronts' prefixes in turn, so
-      // that a lane's start is bitwise its left neighbour's end
+      // one row over NW wavefronts: a scan in each, then the wavefronts' prefixes in turn
       const int wl = lane & (kWave - 1), wv = lane / kWave;
       for (int d = 1; d < kWave; d <<= 1) {
-        double vx = __shfl_up(ix, d, kWave);
-        double vy = __shfl_up(iy, d, kWave);
+        const DD vx{__shfl_up(ix.hi, d, kWave), __shfl_up(ix.lo, d, kWave)};
+        const DD vy{__shfl_up(iy.hi, d, kWave), __shfl_up(iy.lo, d, kWave)};
         if (wl >= d) {
-          ix += vx;
-          iy += vy;
+          ix = dd_add(vx, ix);
+          iy = dd_add(vy, iy);
         }
+        xr += __shfl_xor(xr, d, kWave);
+        ar += __shfl_xor(ar, d, kWave);
       }
-      double ex = __shfl_up(ix, 1, kWave), ey = __shfl_up(iy, 1, kWave);
+      DD ex{__shfl_up(ix.hi, 1, kWave), __shfl_up(ix.lo, 1, kWave)};
+      DD ey{__shfl_up(iy.hi, 1, kWave), __shfl_up(iy.lo, 1, kWave)};
       if (wl == kWave - 1) {
-        sWave[2 * wv] = ix;
-        sWave[2 * wv + 1] = iy;
+        sWave[6 * wv + 0] = ix.hi;
+        sWave[6 * wv + 1] = ix.lo;
+        sWave[6 * wv + 2] = iy.hi;
+        sWave[6 * wv + 3] = iy.lo;
+      }
+      if (wl == 0) {
+        sWave[6 * wv + 4] = xr;
+        sWave[6 * wv + 5] = ar;
       }
       __syncthreads();
       if (lane == 0) {
-        double px = 0.0, py = 0.0;
+        DD px{0.0, 0.0}, py{0.0, 0.0};
         for (int v = 0; v < NW; ++v) {
-          const double tvx = sWave[2 * v], tvy = sWave[2 * v + 1];
-          sWave[2 * v] = px;
-          sWave[2 * v + 1] = py;
-          px = tvx + px;
-          py = tvy + py;
+          const DD tvx{sWave[6 * v + 0], sWave[6 * v + 1]}, tvy{sWave[6 * v + 2], sWave[6 * v + 3]};
+          sWave[6 * v + 0] = px.hi;
+          sWave[6 * v + 1] = px.lo;
+          sWave[6 * v + 2] = py.hi;
+          sWave[6 * v + 3] = py.lo;
+          px = dd_add(px, tvx);
+          py = dd_add(py, tvy);
         }
       }
       __syncthreads();
-      const double px = sWave[2 * wv], py = sWave[2 * wv + 1];
+      const DD px{sWave[6 * wv + 0], sWave[6 * wv + 1]}, py{sWave[6 * wv + 2], sWave[6 * wv + 3]};
+      xr = 0.0;
+      ar = 0.0;
+      for (int v = 0; v < NW; ++v) {
+        xr += sWave[6 * v + 4];
+        ar += sWave[6 * v + 5];
+      }
       if (wl == 0) {
         sx0 = px;
         sy0 = py;
       } else {
-        sx0 = ex + px;
-        sy0 = ey + py;
+        sx0 = dd_add(px, ex);
+        sy0 = dd_add(py, ey);
       }
-      ix = ix + px;
-      iy = iy + py;
     }
-    double lx = 0.0, ly = 0.0;
-    for (int k = 0; k < kLanePts; ++k) {
-      if (k < c) {
+    Erow = ((W ? xr : (double)seglen) * 0x1p-47) * ar;
+    DD lx{0.0, 0.0}, ly{0.0, 0.0};
+    for (int k = 0; k <= kLanePts; ++k) {
+      // point k of the lane (the row segment's end point is written by its last active lane:
+      // its slot belongs to no other lane's elements)
+      if (k < c || (k == c && c > 0 && kLanePts * ql + c == seglen)) {
         const int idx = lds_pad(pbase + k);
-        double rx = W ? sX[idx] : 0.0;
-        double ry = sY[idx];
-        if (W) sX[idx] = sx0 + lx;
-        sY[idx] = sy0 + ly;
-        if (W) lx += rx;
-        ly += ry;
+        double rx = 0.0, ry = 0.0, rye = 0.0;
+        if (k < c) {
+          rx = W ? sX[idx] : 0.0;
+          ry = sY[idx];
+          rye = sYl[idx];
+        }
+        const PD P{W ? dd_add(sx0, lx) : DD{0.0, 0.0}, dd_add(sy0, ly)};
+        if (W) {
+          sX[idx] = P.x.hi;
+          sXl[idx] = P.x.lo;
+        }
+        sY[idx] = P.y.hi;
+        sYl[idx] = P.y.lo;
+        if (W) acc(lx.hi, lx.lo, rx);
+        acc_pe(ly.hi, ly.lo, ry, rye);
       }
-    }
-    // The row segment's end point is written by its last active lane (its slot belongs to no
-    // other lane's elements).
-    if (c > 0 && kLanePts * ql + c == seglen) {
-      const int idx = lds_pad(pbase + c);
-      if (W) sX[idx] = sx0 + lx;
-      sY[idx] = sy0 + ly;
     }
   }
   __syncthreads();
@@ -324,12 +379,13 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
   // ---- a3: lane hulls.
   {
     TilePts<W> P{sX, sY, pbase};
+    TilePairs<W> Q{sX, sY, sXl, sYl, pbase, kLanePts * ql};
     // x of an unweighted point is its row-local index.
     auto Pl = [&](int k, double& xx, double& yy) {
       P(k, xx, yy);
       if (!W) xx = (double)(kLanePts * ql + k);
     };
-    uint64_t mk = lane_chain(c, Pl);
+    uint64_t mk = lane_chain(c, Pl, Q, Erow);
     if (c > 0) {
       sM[r2 * maskStride + ql] = (uint32_t)mk;
       if (c == kLanePts && kLanePts * ql + c == seglen) sM[r2 * maskStride + ql + 1] = 1u;
@@ -340,6 +396,7 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
   // ---- a4: pairwise merges of lane hulls within each row segment, by walking.
   {
     TilePts<W> Prow{sX, sY, rbase};
+    TilePairs<W> Qrow{sX, sY, sXl, sYl, rbase, 0};
     uint32_t* Mr = &sM[r2 * maskStride];
     for (int d = 1; d < L; d <<= 1) {
       if (rowOK && (ql & (2 * d - 1)) == 0 && ql + d < nl) {
@@ -347,7 +404,7 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
         const int s = kLanePts * (ql + d);
         int b1 = kLanePts * (ql + 2 * d);
         if (b1 > seglen) b1 = seglen;
-        tile_walk_merge(Mr, a0, s, b1, Prow);
+        tile_walk_merge(Mr, a0, s, b1, Prow, Qrow, Erow);
       }
       __syncthreads();
     }
@@ -364,15 +421,12 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
       const int r = small_div(e, seglen, inv_seg);
       const int i = e - r * seglen;
       const uint32_t* Mr = &sM[r * maskStride];
-      TilePts<W> Pr{sX, sY, r * rowStride};
+      TilePairs<W> Qr{sX, sY, sXl, sYl, r * rowStride, 0};
       const bool isv = (Mr[i >> 5] >> (i & 31)) & 1u;
       const int a = isv ? i : mask_pred(Mr, i);
       const int b = mask_succ(Mr, i);
-      double ax, ay, bx, by;
-      Pr(a, ax, ay);
-      Pr(b, bx, by);
       const bool bad = sF[r] != 0u;
-      const double slope = (by - ay) / (bx - ax);
+      const double slope = slope_dd(Qr(a), Qr(b));
       z[off + e] = bad ? (T)NAN : (isv && b == i + 1) ? ye : (T)zval<D>(slope);
       if (bstart) bstart[off + e] = (!bad && isv) ? 1 : 0;
     }
@@ -530,6 +584,7 @@ __device__ __forceinline__ DD2 block_scan_incl(DD2 v, double* sh) {
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const double2* __restrict__ tot,
+                                                              const double2* __restrict__ totl,
                                                               const uint32_t* __restrict__ cflags,
                                                               double4* __restrict__ bsum,
                                                               uint32_t* __restrict__ bflag, int m,
@@ -546,8 +601,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const double2* __r
   for (int k = 0; k < kScanPer; ++k) {
     const int jj = b * kScanBlock + kScanPer * t + k;
     if (jj < m) {
-      const double2 v = tot[row * m + jj];
-      acc = dd2_add(acc, DD2{{v.x, 0.0}, {v.y, 0.0}});
+      const double2 v = tot[row * m + jj], vl = totl[row * m + jj];
+      acc = dd2_add(acc, DD2{{v.x, vl.x}, {v.y, vl.y}});
       f |= cflags[row * m + jj];
     }
   }
@@ -561,6 +616,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const double2* __r
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __restrict__ tot,
+                                                             const double2* __restrict__ totl,
                                                              const double4* __restrict__ bsum,
                                                              const uint32_t* __restrict__ bflag,
                                                              double4* __restrict__ start,
@@ -591,8 +647,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __re
     const int jj = b * kScanBlock + kScanPer * t + k;
     DD2 v{{0.0, 0.0}, {0.0, 0.0}};
     if (jj < m) {
-      const double2 tv = tot[row * m + jj];
-      v = DD2{{tv.x, 0.0}, {tv.y, 0.0}};
+      const double2 tv = tot[row * m + jj], tl = totl[row * m + jj];
+      v = DD2{{tv.x, tl.x}, {tv.y, tl.y}};
     }
     loc[k + 1] = dd2_add(loc[k], v);
   }
@@ -742,26 +798,28 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
       const int a0 = max(i0, e.klo), a1 = min(i1, e.khi);
       if (a0 >= a1) continue;
       // the edge (pa, b) covers the elements pa .. b - 1; its slope goes to those of them from
-      // pend on (a one-element edge is its element's y, already written where its tile is marked)
-      auto close_edge = [&](int pend, int pa, double pax, double pay, int b, double bx, double by) {
+      // pend on inside this word (a later word holding more of the edge finds the same two
+      // vertices and writes its own part; a one-element edge is its element's y, already written
+      // where its tile is marked)
+      auto close_edge = [&](int pend, int pa, const PD& Pa, int b, const PD& Pb) {
         if (b == pa + 1) {
           if (!zall && !ztile[g * kZTiles + pa / TN]) z[off + pa] = S.y[off + pa];
           return;
         }
-        const T zv = (T)zval<D>((by - pay) / (bx - pax));
-        for (int i = pend; i < b; ++i) z[off + i] = zv;
+        const T zv = (T)zval<D>(slope_dd(Pa, Pb));
+        const int stop = min(b, a1);
+        for (int i = pend; i < stop; ++i) z[off + i] = zv;
       };
-      double sx, sy, ax, ay;
+      DD sx, sy, ax, ay;
       S.dense_state(row, j, a0, sx, sy, ax, ay);
       int pa, pend = a0;
-      double pax, pay;
+      PD Pa;
       if (bit(a0)) {
         pa = a0;
-        pax = W ? sx + ax : (double)a0;
-        pay = sy + ay;
+        Pa = S.join(sx, sy, ax, ay, a0);
       } else {
         pa = mask_pred(sMask, a0);
-        S.dense_point(row, j, pa, pax, pay);
+        Pa = S.dense_point(row, j, pa);
       }
       for (int i = a0; i < a1; ++i) {
         double wd = W ? (double)S.w[off + i] : 1.0;
@@ -771,29 +829,27 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
           wd = 1.0;
         }
         if (bstart) bstart[off + i] = bit(i) ? 1 : 0;
-        if (W) ax += wd;
-        ay += wd * yd;
+        if (W) acc(ax.hi, ax.lo, wd);
+        acc_prod<VertexStore<T, W, D>::EX>(ay.hi, ay.lo, wd, yd);
         const int ni = i + 1;
         if (ni < a1 && bit(ni)) {
-          const double bx = W ? sx + ax : (double)ni, by = sy + ay;
-          close_edge(pend, pa, pax, pay, ni, bx, by);
+          const PD Pb = S.join(sx, sy, ax, ay, ni);
+          close_edge(pend, pa, Pa, ni, Pb);
           pa = ni;
-          pax = bx;
-          pay = by;
+          Pa = Pb;
           pend = ni;
         }
       }
       // the elements left lie under the edge from pa to the first vertex at or after a1: point a1
       // continues the walk unless it starts a word (a checkpoint) or ends the chunk
       const int b = bit(a1) ? a1 : mask_succ(sMask, a1);
-      double bx, by;
+      PD Pb;
       if (b == a1 && (a1 & (kCk - 1)) != 0 && a1 != len) {
-        bx = W ? sx + ax : (double)a1;
-        by = sy + ay;
+        Pb = S.join(sx, sy, ax, ay, a1);
       } else {
-        S.dense_point(row, j, b, bx, by);
+        Pb = S.dense_point(row, j, b);
       }
-      close_edge(pend, pa, pax, pay, b, bx, by);
+      close_edge(pend, pa, Pa, b, Pb);
     }
     return;
   }
@@ -807,7 +863,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     if (q + 1 < nv) {
       const int k1 = S.lk[lb + q + 1];
       sSlope[q] = k1 == k0 + 1 ? yval<D>(S.y[off + k0])
-                               : (S.ly[lb + q + 1] - S.ly[lb + q]) / (S.lx[lb + q + 1] - S.lx[lb + q]);
+                               : slope_dd(PD{DD{S.lx[lb + q], S.lxl[lb + q]}, DD{S.ly[lb + q], S.lyl[lb + q]}},
+                                          PD{DD{S.lx[lb + q + 1], S.lxl[lb + q + 1]},
+                                             DD{S.ly[lb + q + 1], S.lyl[lb + q + 1]}});
     }
   }
   __syncthreads();

@@ -207,7 +207,7 @@ __device__ __forceinline__ bool merge_finish_walk(const VS& S, const NodeList& L
     while (!vref_eq(al, firstA)) {
       const VRef p = list_pred(LA, al);
       const GPt Pp = load_v(S, LA, p);
-      if (gturn(Pp, Pa, Pb) > 0.0) break;
+      if (gleft(Pp, Pa, Pb)) break;
       if (steps == 0) return false;
       --steps;
       al = p;
@@ -217,7 +217,7 @@ __device__ __forceinline__ bool merge_finish_walk(const VS& S, const NodeList& L
     while (!vref_eq(be, lastB)) {
       const VRef q = list_succ(LB, be);
       const GPt Pq = load_v(S, LB, q);
-      if (gturn(Pa, Pb, Pq) > 0.0) break;
+      if (gleft(Pa, Pb, Pq)) break;
       if (steps == 0) return false;
       --steps;
       be = q;
@@ -323,7 +323,7 @@ __device__ __forceinline__ bool window_bridge(const VS& S, const NodeList& LA, c
     bool moved = false;
     // alpha: lane i decides k = i (a_{i+1} = its own PA); k = na has no a_{na+1} in the window
     {
-      const bool st = lane >= ka && ((lane < na && gturn(PA, Aprev, Pb) > 0.0) || (lane == na && exA));
+      const bool st = lane >= ka && ((lane < na && gleft(PA, Aprev, Pb)) || (lane == na && exA));
       const uint64_t hit = __ballot(st);
       if (!hit) {  // alpha walks past the window
         ka = na;
@@ -343,7 +343,7 @@ __device__ __forceinline__ bool window_bridge(const VS& S, const NodeList& LA, c
     // has no b_{nb+1} in the window
     {
       const int k1 = lane + 1;
-      const bool st = k1 >= kb && ((k1 < nb && gturn(Pa, PB, Bnext) > 0.0) || (k1 == nb && exB));
+      const bool st = k1 >= kb && ((k1 < nb && gleft(Pa, PB, Bnext)) || (k1 == nb && exB));
       const uint64_t hit = __ballot(st);
       if (!hit) {  // beta walks past the window
         kb = nb;
@@ -385,7 +385,7 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
     settled = true;
     if (!vref_eq(al, firstA)) {
       const GPt Pp = load_v(S, LA, list_pred(LA, al));
-      if (!(gturn(Pp, Pa, Pb) > 0.0)) settled = false;
+      if (!(gleft(Pp, Pa, Pb))) settled = false;
     }
     if (settled && !vref_eq(be, lastB)) {
       // (alpha, beta, succ beta) three consecutive points of a chunk whose y is strictly
@@ -396,7 +396,7 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
                                be.p == d0.y + 1 && be.p < d0.z;
       if (!consecutive) {
         const GPt Pq = load_v(S, LB, list_succ(LB, be));
-        if (!(gturn(Pa, Pb, Pq) > 0.0)) settled = false;
+        if (!(gleft(Pa, Pb, Pq))) settled = false;
       }
     }
   }
@@ -422,7 +422,7 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
       bool moved = false;
       // (from the second pass on, a side whose first step already stops gathers no window)
       bool walk_a = !vref_eq(al, firstA);
-      if (pass > 0 && walk_a) walk_a = !(gturn(load_v(S, LA, list_pred(LA, al)), Pa, Pb) > 0.0);
+      if (pass > 0 && walk_a) walk_a = !(gleft(load_v(S, LA, list_pred(LA, al)), Pa, Pb));
       // A side: alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
       for (int win = 0; walk_a && !vref_eq(al, firstA); ++win) {
         if (win == kWideCap) {
@@ -431,13 +431,13 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
         }
         const VRef before = al;
         const bool done = walk_window_wide(S, LA, -1, al, Pa, lane, Ww,
-                                           [&](const GPt& vi, const GPt& vn) { return gturn(vn, vi, Pb) > 0.0; });
+                                           [&](const GPt& vi, const GPt& vn) { return gleft(vn, vi, Pb); });
         if (!vref_eq(before, al)) moved = true;
         if (done) break;
       }
       if (searched) break;
       bool walk_b = !vref_eq(be, lastB);
-      if (pass > 0 && walk_b) walk_b = !(gturn(Pa, Pb, load_v(S, LB, list_succ(LB, be))) > 0.0);
+      if (pass > 0 && walk_b) walk_b = !(gleft(Pa, Pb, load_v(S, LB, list_succ(LB, be))));
       // B side: beta moves right while (alpha, beta, succ beta) is not a strict left turn
       for (int win = 0; walk_b && !vref_eq(be, lastB); ++win) {
         if (win == kWideCap) {
@@ -446,7 +446,7 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
         }
         const VRef before = be;
         const bool done = walk_window_wide(S, LB, +1, be, Pb, lane, Ww,
-                                           [&](const GPt& vi, const GPt& vn) { return gturn(Pa, vi, vn) > 0.0; });
+                                           [&](const GPt& vi, const GPt& vn) { return gleft(Pa, vi, vn); });
         if (!vref_eq(before, be)) moved = true;
         if (done) break;
       }
