@@ -157,13 +157,16 @@ def blocks_from_exact(z):
 
 
 def kkt_residual(y, w, z, decreasing=False):
-    """Largest KKT violation of an output z, relative to 2 * sum w |y| (0 for an empty row).
+    """Largest violation of the optimality certificate of an output z (0 for an empty row).
 
-    lambda_i = -2 sum_{j<=i} w_j (z_j - y_j) must be >= 0, zero at the last element and zero
-    wherever z steps up (z_{i+1} > z_i).  Feasibility (z non-decreasing) plus these
-    conditions prove optimality of the convex problem.  For the decreasing fit the sign of
-    lambda flips and the steps that free it are steps down.  Sums use 80-bit extended
-    precision.
+    Two parts, the larger of which is returned:
+      stationarity  lambda_i = -2 sum_{j<=i} w_j (z_j - y_j) must be >= 0, zero at the last
+                    element and zero wherever z steps up (z_{i+1} > z_i); violations are
+                    relative to 2 * sum w |y|;
+      feasibility   z must be non-decreasing; the largest step down is relative to max |y|.
+    Feasibility plus stationarity prove optimality of the convex problem.  For the decreasing
+    fit the sign of lambda flips, the steps that free it are steps down, and feasibility asks
+    for a non-increasing z.  Sums use 80-bit extended precision.
     """
     y = np.asarray(y, dtype=np.float64).ravel()
     z = np.asarray(z, dtype=np.float64).ravel()
@@ -184,7 +187,11 @@ def kkt_residual(y, w, z, decreasing=False):
     up = (z[1:] < z[:-1]) if decreasing else (z[1:] > z[:-1])
     if np.any(up):
         res = max(res, float(np.abs(lam[:-1][up]).max()))
-    return float(res / scale)
+    steps = np.diff(z)
+    against = float(np.max(steps if decreasing else -steps, initial=0.0))
+    ymax = float(np.max(np.abs(y)))
+    feas = max(against, 0.0) / (ymax if ymax > 0 else 1.0)
+    return max(float(res / scale), feas)
 
 
 def measures(y, w, z, z_ref=None, block_start=None, eps=None):

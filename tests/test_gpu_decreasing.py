@@ -33,7 +33,7 @@ def test_decreasing_families(fam, dtype):
         for wk in ("unit", "integer"):
             y, w = W.family(fam, 2, n, seed=n + 3, dtype=dtype, wkind=wk)
             cancel = fam == "cancel"
-            tol = (1e-14 if dtype == "f64" else 1e-7) if cancel else None
+            tol = (1.4e-15 if dtype == "f64" else 1e-7) if cancel else None
             check(y, None if wk == "unit" else w, exact_partition=fam in ("integer", "constant"), tol=tol,
                   kkt=not cancel, scale_abs=cancel, decreasing=True)
 

@@ -85,11 +85,11 @@ def test_families(fam, dtype):
         for wk in ("unit", "uniform", "integer"):
             y, w = W.family(fam, 2, n, seed=n + 1, dtype=dtype, wkind=wk)
             w_ = None if wk == "unit" else w
-            # The cancellation family is measured against max|y| (the page's Section 7.6 does so).
-            # Chunk-relative coordinates there reach 32 B, so a slope carries a few ulp(32 B) of
-            # error: 1e-14 max|y| in fp64 (45 ulp of max|y|), 1e-7 max|y| in fp32.
+            # The cancellation family is measured against max|y| (the page's Section 7.6 does so),
+            # to the page's fp64 figure, 1.4e-15 max|y|; fp32 outputs carry their own rounding,
+            # up to 6e-8 of |z| <= max|y|.
             cancel = fam == "cancel"
-            tol = (1e-14 if dtype == "f64" else 1e-7) if cancel else None
+            tol = (1.4e-15 if dtype == "f64" else 1e-7) if cancel else None
             check(y, w_, exact_partition=(fam in ("integer", "constant") and wk != "uniform"), tol=tol,
                   kkt=not cancel, scale_abs=cancel)
 
@@ -134,8 +134,54 @@ def test_config_mixed_1e8():
 
 def test_nearly_monotone_1e8_fp64():
     y, w = W.nearly_monotone_1e8()
-    z, bs = check(y, None, kkt=False)
+    for ww in (None, w):
+        z, bs = check(y, ww, kkt=False)
+        assert bs.all()
+        np.testing.assert_array_equal(z, y)  # one-element blocks output their y
+
+
+def wrong_steps(z, decreasing=False):
+    """Largest step of z against the fit direction, relative to max(1, max |z|)."""
+    z = np.asarray(z, dtype=np.float64)
+    steps = np.diff(z, axis=-1)
+    worst = float(np.max(steps if decreasing else -steps, initial=0.0))
+    return max(worst, 0.0) / max(1.0, float(np.max(np.abs(z))))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("decreasing", [False, True])
+@pytest.mark.parametrize("fam", W.FAMILIES)
+def test_extreme_weights(fam, decreasing, dtype):
+    """Weights spanning eight orders of magnitude (LogUniform[1e-4, 1e4], the page's "extreme
+    weights" of Section 7.6) on every family and size class: the fp64 bar 1e-10 and fp32 1e-6 (the
+    cancellation family against max |y| at the page's fp64 figure 1.4e-15), the KKT certificate,
+    and no step against the fit direction beyond a few units in the last place.  Slopes of short
+    edges over tiny weights are differences of prefix sums many orders larger, so these rows need
+    the coordinate pairs and the filtered predicates."""
+    cancel = fam == "cancel"
+    for n in (700, 5000, 70001, 1_000_000):
+        y, w = W.family(fam, 2 if n < 100000 else 1, n, seed=n + 17, dtype=dtype, wkind="extreme")
+        tol = (1.4e-15 if dtype == "f64" else 1e-7) if cancel else None
+        z, bs = check(y, w, tol=tol, kkt=not cancel, scale_abs=cancel, decreasing=decreasing)
+        assert wrong_steps(z, decreasing) <= 1e-15, (n, wrong_steps(z, decreasing))
+
+
+def test_page_stress_row_increasing_extreme_weights_1e7():
+    """The page's Section 7.6 stress case: 10^7 strictly increasing fp64 values with extreme
+    weights, whose cumulative sums reach about 10^10.  Every point is a vertex of the exact hull,
+    so every element is its own block and the fit is y itself; the page reports that a version
+    without the coordinate hierarchy pools 681 of these points."""
+    y, w = W.family("increasing", 1, 10_000_000, seed=11, dtype="f64", wkind="extreme")
+    assert np.all(np.diff(y[0]) > 0)
+    z, bs, rf = gpu_fit(y, w)
+    assert rf[0] == 0
     assert bs.all()
+    np.testing.assert_array_equal(z, y)
+    # the same row with reversals every few hundred elements: most points stay vertices
+    yr = y.copy()
+    yr[0, 300::977] -= 3e-6
+    z, bs = check(yr, w, kkt=False)
+    assert wrong_steps(z) <= 1e-15
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64"])

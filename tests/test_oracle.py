@@ -194,6 +194,50 @@ def test_invariants_and_kkt(fam, wkind):
         assert m["kkt"] < 1e-12, m
 
 
+def test_certificate_and_measures_reject_outputs_that_are_not_the_fit():
+    """Negative pins of exact.kkt_residual and exact.measures: each must flag an output that is
+    not the fit, so that a checker returning 0 (or ignoring feasibility) fails here."""
+    y, w = workloads.family("noise", 1, 3000, seed=5, wkind="uniform")
+    y, w = y[0], w[0]
+    z, s, _ = oracle.pav(y, w, return_blocks=True)
+    s = s.astype(bool)
+    assert exact.kkt_residual(y, w, z) < 1e-12
+    # the unfitted row: lambda is zero everywhere, but y is not non-decreasing
+    assert np.any(np.diff(y) < 0)
+    assert exact.kkt_residual(y, w, y) > 1e-2
+    # the fit in a shuffled order: infeasible
+    zs = np.random.default_rng(1).permutation(z)
+    assert exact.kkt_residual(y, w, zs) > 1e-2
+    # a uniform shift breaks lambda_{n-1} = 0; a shift of one block breaks lambda = 0 at its end
+    assert exact.kkt_residual(y, w, z + 1e-6) > 1e-7
+    ids = np.cumsum(s) - 1
+    big = np.argmax(np.bincount(ids, weights=w))
+    zb = z.copy()
+    zb[ids == big] += 1e-6
+    assert exact.kkt_residual(y, w, zb) > 1e-9
+    # the fit of the other direction, certified in this one: infeasible (unless constant)
+    zd = oracle.pav(y, w, decreasing=True)
+    assert exact.kkt_residual(y, w, zd, decreasing=True) < 1e-12
+    assert exact.kkt_residual(y, w, z, decreasing=True) > 1e-2
+    assert exact.kkt_residual(y, w, zd) > 1e-2
+
+    m = exact.measures(y, w, z, z_ref=z, block_start=s)
+    assert m["step_down"] == 0.0 and m["deviation"] == 0.0 and m["objective"] <= 0.0
+    assert m["block_mean"] < 1e-14 and m["sum_wz"] < 1e-12
+    mb = exact.measures(y, w, zb, z_ref=z, block_start=s)
+    assert mb["deviation"] > 1e-7
+    assert mb["objective"] > 0.0  # any other feasible z has a larger objective
+    assert mb["block_mean"] > 1e-7
+    assert mb["sum_wz"] > 1e-9
+    assert mb["kkt"] > 1e-9
+    ms = exact.measures(y, w, zs, z_ref=z, block_start=s)
+    assert ms["step_down"] > 1e-2 and ms["kkt"] > 1e-2 and ms["deviation"] > 1e-2
+    # block starts that are not the fit's: the block means no longer match z
+    s2 = s.copy()
+    s2[np.flatnonzero(~s)[::7]] = True
+    assert exact.measures(y, w, z, block_start=s2)["block_mean"] > 1e-3
+
+
 def test_scipy_cross_check():
     from scipy.optimize import isotonic_regression
 
