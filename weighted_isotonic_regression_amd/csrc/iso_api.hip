@@ -6,7 +6,8 @@
 //               over 2048: one row per workgroup of 2 wavefronts); one launch of k_wave
 //               writes z, block starts and row flags (Section 3.5).
 //   n >  4096   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
-//               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls),
+//               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls; a
+//               second, exact instantiation takes the chunks whose fast turns left one undecided),
 //               k_scan_reduce + k_scan_apply (chunk starts),
 //               ceil(ceil(log2 m) / 3) launches of k_merge_levels, k_ends, k_fit
 //               (Section 3.3 and 3.4).
@@ -46,10 +47,10 @@ struct Layout {
   size_t total = 0;
   size_t o_rflags = 0, o_any = 0;
   // long rows only
-  size_t o_tot = 0, o_totl = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0,
-         o_lx = 0, o_ly = 0, o_lxl = 0, o_lyl = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0,
-         o_lsxl = 0, o_lsyl = 0, o_ckx = 0, o_cky = 0, o_ckxl = 0, o_ckyl = 0, o_zt = 0, o_df = 0,
-         o_bnd = 0, o_bndl = 0, o_bndk = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
+  // arrays of coordinate pairs hold the hi parts of all G chunks, then the lo parts
+  size_t o_tot = 0, o_start = 0, o_nv = 0, o_cf = 0, o_desc = 0, o_nseg = 0, o_lk = 0, o_lx = 0,
+         o_ly = 0, o_mask = 0, o_mcnt = 0, o_lsx = 0, o_lsy = 0, o_ckx = 0, o_cky = 0, o_zt = 0,
+         o_df = 0, o_bnd = 0, o_bndk = 0, o_ends = 0, o_bsum = 0, o_bflag = 0;
   int64_t m = 0, nblk = 0;
 };
 
@@ -69,32 +70,24 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.m = (n + kChunk - 1) / kChunk;
     L.nblk = (L.m + kScanBlock - 1) / kScanBlock;
     const size_t G = (size_t)batch * (size_t)L.m;
-    L.o_tot = take(G * sizeof(double2));
-    L.o_totl = take(G * sizeof(double2));
+    L.o_tot = take(2 * G * sizeof(double2));
     L.o_start = take(G * sizeof(double4));
     L.o_nv = take(G * sizeof(int));
     L.o_cf = take(G * sizeof(uint32_t));
     L.o_desc = take(G * sizeof(Desc));
     L.o_nseg = take(G * sizeof(int));
     L.o_lk = take(G * (size_t)kListCap * sizeof(uint16_t));
-    L.o_lx = take(G * (size_t)kListCap * sizeof(double));
-    L.o_ly = take(G * (size_t)kListCap * sizeof(double));
-    L.o_lxl = take(G * (size_t)kListCap * sizeof(double));
-    L.o_lyl = take(G * (size_t)kListCap * sizeof(double));
+    L.o_lx = take(2 * G * (size_t)kListCap * sizeof(double));
+    L.o_ly = take(2 * G * (size_t)kListCap * sizeof(double));
     L.o_mask = take(G * (size_t)kMaskW * sizeof(uint32_t));
     L.o_mcnt = take(G * (size_t)kMaskW * sizeof(uint16_t));
-    L.o_lsx = take(G * (size_t)kWave * sizeof(double));
-    L.o_lsy = take(G * (size_t)kWave * sizeof(double));
-    L.o_lsxl = take(G * (size_t)kWave * sizeof(double));
-    L.o_lsyl = take(G * (size_t)kWave * sizeof(double));
-    L.o_ckx = take(G * (size_t)kWave * kLaneW * sizeof(double));
-    L.o_cky = take(G * (size_t)kWave * kLaneW * sizeof(double));
-    L.o_ckxl = take(G * (size_t)kWave * kLaneW * sizeof(double));
-    L.o_ckyl = take(G * (size_t)kWave * kLaneW * sizeof(double));
+    L.o_lsx = take(2 * G * (size_t)kWave * sizeof(double));
+    L.o_lsy = take(2 * G * (size_t)kWave * sizeof(double));
+    L.o_ckx = take(2 * G * (size_t)kWave * kLaneW * sizeof(double));
+    L.o_cky = take(2 * G * (size_t)kWave * kLaneW * sizeof(double));
     L.o_zt = take(G * (size_t)kZTiles);
     L.o_df = take(G);
-    L.o_bnd = take(G * sizeof(double4));
-    L.o_bndl = take(G * sizeof(double4));
+    L.o_bnd = take(2 * G * sizeof(double4));
     L.o_bndk = take(G * sizeof(int2));
     L.o_ends = take(G * sizeof(EndInfo));
     L.o_bsum = take((size_t)batch * (size_t)L.nblk * sizeof(double4));
@@ -210,7 +203,6 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   const int64_t G = batch * (int64_t)m;
   ChunkOut co;
   co.tot = (double2*)(ws + Lay.o_tot);
-  co.totl = (double2*)(ws + Lay.o_totl);
   co.nverts = (int*)(ws + Lay.o_nv);
   co.cflags = (uint32_t*)(ws + Lay.o_cf);
   co.desc = (Desc*)(ws + Lay.o_desc);
@@ -218,23 +210,17 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   co.lk = (uint16_t*)(ws + Lay.o_lk);
   co.lx = (double*)(ws + Lay.o_lx);
   co.ly = (double*)(ws + Lay.o_ly);
-  co.lxl = (double*)(ws + Lay.o_lxl);
-  co.lyl = (double*)(ws + Lay.o_lyl);
   co.mask = (uint32_t*)(ws + Lay.o_mask);
   co.mcnt = (uint16_t*)(ws + Lay.o_mcnt);
   co.lsx = (double*)(ws + Lay.o_lsx);
   co.lsy = (double*)(ws + Lay.o_lsy);
-  co.lsxl = (double*)(ws + Lay.o_lsxl);
-  co.lsyl = (double*)(ws + Lay.o_lsyl);
   co.ckx = (double*)(ws + Lay.o_ckx);
   co.cky = (double*)(ws + Lay.o_cky);
-  co.ckxl = (double*)(ws + Lay.o_ckxl);
-  co.ckyl = (double*)(ws + Lay.o_ckyl);
   co.ztile = (uint8_t*)(ws + Lay.o_zt);
   co.dform = (uint8_t*)(ws + Lay.o_df);
   co.bnd = (double4*)(ws + Lay.o_bnd);
-  co.bndl = (double4*)(ws + Lay.o_bndl);
   co.bndk = (int2*)(ws + Lay.o_bndk);
+  co.G = G;
   double4* start = (double4*)(ws + Lay.o_start);
   double4* bsum = (double4*)(ws + Lay.o_bsum);
   uint32_t* bflag = (uint32_t*)(ws + Lay.o_bflag);
@@ -243,12 +229,13 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   hipLaunchKernelGGL((k_increasing<T, W, D>), dim3((unsigned)G), dim3(kIncWaves * kWave), 0, s, y, w, z, n,
                      m, co);
   prof.mark(1);
-  hipLaunchKernelGGL((k_chunk<T, W, D>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
-  prof.mark(1);
+  hipLaunchKernelGGL((k_chunk<T, W, D, false>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
+  hipLaunchKernelGGL((k_chunk<T, W, D, true>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
+  prof.mark(2);
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
-                     s, co.tot, co.totl, co.cflags, bsum, bflag, m, nblk);
+                     s, co.tot, co.tot + G, co.cflags, bsum, bflag, m, nblk);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
-                     co.tot, co.totl, bsum, bflag, start, rflags, m, nblk);
+                     co.tot, co.tot + G, bsum, bflag, start, rflags, m, nblk);
   prof.mark(2);
   VertexStore<T, W, D> S;
   S.desc = co.desc;
@@ -257,29 +244,22 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   S.dense = co.dform;
   S.lx = co.lx;
   S.ly = co.ly;
-  S.lxl = co.lxl;
-  S.lyl = co.lyl;
   S.lk = co.lk;
   S.mask = co.mask;
   S.mcnt = co.mcnt;
   S.lsx = co.lsx;
   S.lsy = co.lsy;
-  S.lsxl = co.lsxl;
-  S.lsyl = co.lsyl;
   S.ckx = co.ckx;
   S.cky = co.cky;
-  S.ckxl = co.ckxl;
-  S.ckyl = co.ckyl;
   S.bnd = co.bnd;
-  S.bndl = co.bndl;
   S.bndk = co.bndk;
   S.tot = co.tot;
-  S.totl = co.totl;
   S.start = start;
   S.y = y;
   S.w = w;
   S.n = n;
   S.m = m;
+  S.G = G;
   // the merge levels, kMergeGroup per launch (a workgroup per subtree)
   int levels = 0;
   while ((1 << levels) < m) ++levels;

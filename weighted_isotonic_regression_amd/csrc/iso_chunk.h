@@ -42,33 +42,37 @@ namespace iso {
 
 // Per-chunk outputs of the chunk pass.
 struct ChunkOut {
-  double2* tot;       // [G] chunk end point (W, S), chunk-relative: hi parts
-  double2* totl;      // [G] and lo parts
+  // Each array of lo parts follows its array of hi parts in the same allocation (G chunks apart),
+  // so that only the hi pointers are passed.
+  double2* tot;       // [2G] chunk end point (W, S), chunk-relative: hi parts, then lo parts
   int* nverts;        // [G] vertex count of the chunk hull
   uint32_t* cflags;   // [G] input flags of the chunk
   Desc* desc;         // [G] leaf segment list
   int* nseg;          // [G]
   uint16_t* lk;       // [G * kListCap] list form: chunk point index
-  double* lx;         // [G * kListCap] chunk-relative pairs
+  double* lx;         // [2G * kListCap] chunk-relative pairs: hi parts, then lo parts
   double* ly;
-  double* lxl;
-  double* lyl;
   uint32_t* mask;     // [G * kMaskW] dense form: vertex bits of chunk points 0..16384
   uint16_t* mcnt;     // [G * kMaskW] set bits before each word
-  double* lsx;        // [G * kWave] lane starts (chunk-relative pairs)
+  double* lsx;        // [2G * kWave] lane starts (chunk-relative pairs)
   double* lsy;
-  double* lsxl;
-  double* lsyl;
-  double* ckx;        // [G * kWave * kLaneW] lane-relative running sums at points 32 j (pairs)
+  double* ckx;        // [2G * kWave * kLaneW] lane-relative running sums at points 32 j (pairs)
   double* cky;
-  double* ckxl;
-  double* ckyl;
   uint8_t* ztile;     // [G * kZTiles] 1 where the lane chains wrote z = y for the load tile
   uint8_t* dform;     // [G] 0 list form, 1 dense form, 2 dense form with every point a vertex
-                      //     and z = y written for the whole chunk
-  double4* bnd;       // [G] dense form: coordinates of hull vertices 1 and V - 2 (hi parts)
-  double4* bndl;      // [G] (lo parts)
+                      //     and z = y written for the whole chunk, 3 not yet processed
+  double4* bnd;       // [2G] dense form: coordinates of hull vertices 1 and V - 2 (hi, then lo)
   int2* bndk;         // [G] their point indices
+  int64_t G;          // chunks of the call
+
+  __device__ double2* totl() const { return tot + G; }
+  __device__ double* lxl() const { return lx + G * kListCap; }
+  __device__ double* lyl() const { return ly + G * kListCap; }
+  __device__ double* lsxl() const { return lsx + G * kWave; }
+  __device__ double* lsyl() const { return lsy + G * kWave; }
+  __device__ double* ckxl() const { return ckx + G * (kWave * kLaneW); }
+  __device__ double* ckyl() const { return cky + G * (kWave * kLaneW); }
+  __device__ double4* bndl() const { return bnd + G; }
 };
 
 __device__ __forceinline__ double turn_pts(double2 p, double2 q, double2 r) {
@@ -179,8 +183,8 @@ __device__ double2 lane_point(const double* ckx, const double* cky, int l, int q
 // Lane-relative pairs of lane l's point q, from the checkpoint pairs below q and the inputs (the
 // chain's operations in its order, so its hi parts are lane_point's).
 template <typename T, bool W, bool D>
-__device__ PD lane_point_dd(const double* ckx, const double* cky, const double* ckxl, const double* ckyl, int l,
-                            int q, int c, const T* yl, const T* wl) {
+__device__ __forceinline__ PD lane_point_dd(const double* ckx, const double* cky, const double* ckxl,
+                                            const double* ckyl, int l, int q, int c, const T* yl, const T* wl) {
   constexpr bool EX = ExactProd<T, W>::value;
   q = min(max(q, 0), c);
   const int j = min(q / kCk, kLaneW - 1);
@@ -306,14 +310,16 @@ __device__ PD chunk_entry_dd(const ChunkLds<W>& L, const double* ckx, const doub
 
 // Turn of three stack entries (lane, depth) of the chunk's lanes from their chunk-relative pairs.
 template <typename T, bool W, bool D>
-__device__ __noinline__ double entries_turn_dd(const ChunkLds<W>* L, const double* ckx, const double* cky,
-                                               const double* ckxl, const double* ckyl, int l1, int i1, int l2,
-                                               int i2, int l3, int i3, int len, const T* yc, const T* wc) {
-  int q;
-  const PD Q1 = chunk_entry_dd<T, W, D>(*L, ckx, cky, ckxl, ckyl, l1, i1, len, yc, wc, q);
-  const PD Q2 = chunk_entry_dd<T, W, D>(*L, ckx, cky, ckxl, ckyl, l2, i2, len, yc, wc, q);
-  const PD Q3 = chunk_entry_dd<T, W, D>(*L, ckx, cky, ckxl, ckyl, l3, i3, len, yc, wc, q);
-  return turn_dd(Q1, Q2, Q3).hi;
+__device__ __forceinline__ double entries_turn_dd(const ChunkLds<W>& L, const double* ckx, const double* cky,
+                                                  const double* ckxl, const double* ckyl, const int (&ls)[3],
+                                                  const int (&is)[3], int len, const T* yc, const T* wc) {
+  PD Q[3];
+#pragma unroll 1
+  for (int k = 0; k < 3; ++k) {
+    int q;
+    Q[k] = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, ls[k], is[k], len, yc, wc, q);
+  }
+  return turn_dd(Q[0], Q[1], Q[2]).hi;
 }
 
 // Chunks whose elements are all clean and strictly increasing.  Every turn of such a chunk's
@@ -405,13 +411,10 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
         }
       }
       carry = __shfl(last, kWave - 1, kWave);
-      // block sums: a butterfly of double-double additions (commutative bit for bit, so every
-      // lane of a block holds the same pair)
-#pragma unroll
-      for (int o = 1; o < BL; o <<= 1) {
-        if (W) sw = dd_add(sw, DD{__shfl_xor(sw.hi, o, kWave), __shfl_xor(sw.lo, o, kWave)});
-        sy = dd_add(sy, DD{__shfl_xor(sy.hi, o, kWave), __shfl_xor(sy.lo, o, kWave)});
-      }
+      // block sums: a DPP butterfly over the block's BL lanes (every lane of a block ends with
+      // the same pair)
+      if (W) sw = group_pair_sum<BL>(sw);
+      sy = group_pair_sum<BL>(sy);
       if ((lane & (BL - 1)) == 0 && e < q1) {
         if (W) {
           bs.x[e / kCk] = sw.hi;
@@ -446,10 +449,10 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   for (int jj = 0; jj < kLaneW; ++jj) {
     if (W) {
       out.ckx[cb + jj] = cx.hi;
-      out.ckxl[cb + jj] = cx.lo;
+      out.ckxl()[cb + jj] = cx.lo;
     }
     out.cky[cb + jj] = cy.hi;
-    out.ckyl[cb + jj] = cy.lo;
+    out.ckyl()[cb + jj] = cy.lo;
     if (jj == jv) {
       cvx = cx;
       cvy = cy;
@@ -480,10 +483,10 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   if (!W) sx = DD{(double)(kSub * lane), 0.0};
   if (W) {
     out.lsx[g * kWave + lane] = sx.hi;
-    out.lsxl[g * kWave + lane] = sx.lo;
+    out.lsxl()[g * kWave + lane] = sx.lo;
   }
   out.lsy[g * kWave + lane] = sy.hi;
-  out.lsyl[g * kWave + lane] = sy.lo;
+  out.lsyl()[g * kWave + lane] = sy.lo;
   // vertex bits of points 0..len, set bits before each word
   const int64_t mb = g * (int64_t)kMaskW;
 #pragma unroll
@@ -504,8 +507,8 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     const PD P = VertexStore<T, W, D>::join(sx, sy, ax, ay, 1);
     out.bnd[g].x = P.x.hi;
     out.bnd[g].y = P.y.hi;
-    out.bndl[g].x = P.x.lo;
-    out.bndl[g].y = P.y.lo;
+    out.bndl()[g].x = P.x.lo;
+    out.bndl()[g].y = P.y.lo;
     out.bndk[g].x = 1;
     out.nverts[g] = len + 1;
     out.desc[g] = make_int4(j, 0, len, desc_w(2, len + 1));
@@ -517,7 +520,7 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     out.mask[mb + kMaskW - 1] = len == kChunk ? 1u : 0u;  // point 16384
     out.mcnt[mb + kMaskW - 1] = (uint16_t)min(kChunk, len + 1);
     out.tot[g] = make_double2(W ? ix.hi : (double)len, iy.hi);
-    out.totl[g] = make_double2(W ? ix.lo : 0.0, iy.lo);
+    out.totl()[g] = make_double2(W ? ix.lo : 0.0, iy.lo);
   }
   if (lane == lv) {
     // vertex V - 2 = point len - 1: this lane's checkpoint below it plus its elements from the
@@ -541,8 +544,8 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
     const PD P = (kv % kSub == 0) ? PD{sx, sy} : VertexStore<T, W, D>::join(sx, sy, ax, ay, kv);
     out.bnd[g].z = P.x.hi;
     out.bnd[g].w = P.y.hi;
-    out.bndl[g].z = P.x.lo;
-    out.bndl[g].w = P.y.lo;
+    out.bndl()[g].z = P.x.lo;
+    out.bndl()[g].w = P.y.lo;
     out.bndk[g].y = kv;
   }
   return true;
@@ -572,7 +575,7 @@ __global__ __launch_bounds__(kIncWaves * kWave) void k_increasing(const T* __res
   if (!done && threadIdx.x == 0) out.dform[g] = 3;
 }
 
-template <typename T, bool W, bool D>
+template <typename T, bool W, bool D, bool EXACT>
 __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y,
                                                         const T* __restrict__ w,
                                                         T* __restrict__ z, int64_t n, int m,
@@ -600,9 +603,10 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   T* zl = z + off + e0;
   double* ckx = out.ckx + g * (int64_t)(kWave * kLaneW);  // the chunk's checkpoints
   double* cky = out.cky + g * (int64_t)(kWave * kLaneW);
-  double* ckxl = out.ckxl + g * (int64_t)(kWave * kLaneW);
-  double* ckyl = out.ckyl + g * (int64_t)(kWave * kLaneW);
-  if (out.dform[g] == 2) return;  // done by k_increasing
+  double* ckxl = out.ckxl() + g * (int64_t)(kWave * kLaneW);
+  double* ckyl = out.ckyl() + g * (int64_t)(kWave * kLaneW);
+  // done by k_increasing (form 2), or by the first pass (forms 0 and 1)
+  if (EXACT ? out.dform[g] != 3 : out.dform[g] == 2) return;
 
   // ---- a1-a3: stream the lane's elements through the chain.  Point P_q (0 < q < c) lies between
   // the elements q - 1 and q, whose slopes are y_{q-1} and y_q; unless y_{q-1} < y_q it is not a
@@ -617,6 +621,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   double lx = 0.0, ly = 0.0;     // running sums (hi)
   double lxl = 0.0, lyl = 0.0;   // their lo parts
   double aabs = 0.0;             // sum of |w y| so far: bounds every |y| of the lane's points
+  double lomx = 0.0, lomy = 0.0; // largest |lo| of the running sums so far
   double yprev = 0.0;
   int wi = 0;
   uint32_t curw = 0u;
@@ -652,22 +657,40 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     }
     vchk = false;
   };
-  // The turn (U, T, K) of the hi parts.  Every point so far has 0 <= x <= Ax (the current x) and
-  // |y| <= Ay = sum |w y|, and each lo part is at most 257 u times those (256 rounded additions
-  // and the products' errors), so the fast turn is within 3100 u Ax Ay of the turn of the pairs
-  // (2^-41 = 4096 u).  Inside that bound U and T are recomputed from their checkpoints and the
-  // turn is decided in double-double arithmetic, K being the running sums themselves.
+  // The turn (U, T, K) of the hi parts.  Every point so far has 0 <= x <= Ax (the current x),
+  // |y| <= Ay = sum |w y|, and lo parts of at most LX and LY in magnitude (the largest seen), so
+  // each difference of hi parts is within u |d| + 2 LX (or 2 LY) of the difference of the pairs
+  // and the fast turn is within 14 u Ax Ay + 4 Ax LY + 8 Ay LX (to first order) of the turn of
+  // the pairs; Ecur = 16 u Ax Ay + 8 (Ax LY + Ay LX), set before each push.  While every point
+  // pushed so far has integer coordinates below 2^25 (frac = 0, Ax and Ay below 2^25), the fast
+  // turn is exact.  Otherwise a turn inside the bound is decided only by the EXACT instantiation,
+  // in double-double arithmetic from U and T recomputed from their checkpoints and K's running
+  // pairs; the first pass merely records the smallest margin |t| - Ecur (marg) and leaves the
+  // chunk to the exact pass, which runs on the chunks it left.  On noisy rows that is rare, and
+  // the first pass carries no slow path.
+  double Ecur = 0.0;
+  double marg = INFINITY;  // smallest |t| - Ecur of the turns taken
+  double frac = 0.0;       // largest fractional part of a pushed point's coordinates
   auto turn_utk = [&](const double kx, const double ky, const int q) {
     double t = cross2(tx - ux, ty - uy, kx - ux, ky - uy);
-    const double E = ((W ? lx : (double)q) * 0x1p-41) * aabs;
-    if (d >= 2 && !(fabs(t) > E))
-      t = chain_turn_dd<T, W, D>(ckx, cky, ckxl, ckyl, lane, ui, ti, c, yl, wl, kx, W ? lxl : 0.0, ky, lyl);
+    if constexpr (EXACT) {
+      const bool ilane = frac == 0.0 && (W ? lx : (double)q) < 0x1p25 && aabs < 0x1p25;
+      if (d >= 2 && !ilane && !(fabs(t) > Ecur))
+        t = chain_turn_dd<T, W, D>(ckx, cky, ckxl, ckyl, lane, ui, ti, c, yl, wl, kx, W ? lxl : 0.0, ky, lyl);
+    } else {
+      marg = fmin(marg, (d >= 2 ? fabs(t) : INFINITY) - Ecur);
+    }
     return t;
   };
   // pushes point q with lane-relative coordinates (kx, ky), first popping what it makes
   // non-convex (pop while the turn (U, T, K) is not strictly left).  A popped entry's stack bit
   // is cleared in LDS (the word being filled is rewritten from curw later) and in curw.
   auto push = [&](const double kx, const double ky, const int q) {
+    {
+      const double ax = W ? lx : (double)q;
+      Ecur = fma(ax * 0x1p-49, aabs, 8.0 * fma(ax, lomy, aabs * lomx));
+    }
+    frac = fmax(frac, fabs(ky - floor(ky)) + (W ? fabs(kx - floor(kx)) : 0.0));
     bool more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
     if (more) {
       while (more) {
@@ -807,6 +830,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       const double p = wd * yd;
       acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
       aabs += fabs(p);
+      if (W) lomx = fmax(lomx, fabs(lxl));
+      lomy = fmax(lomy, fabs(lyl));
       yprev = yd;
     };
     // pushes the tile's points eb + k, k >= kp, without tests, and consumes its elements k >= kc
@@ -817,6 +842,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       for (int k = 0; k < TN; ++k) {
         if (k >= kp) {
           const double kx = W ? lx : (double)(eb + k), ky = ly;
+          frac = fmax(frac, fabs(ky - floor(ky)) + (W ? fabs(kx - floor(kx)) : 0.0));
           s = ring_next(s);
           if (k >= TN - (kRingS - 2) || d < 2) ring_put<W>(L, s, lane, kx, ky, ring_tag(eb + k, d));
           vx = ux;
@@ -840,6 +866,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           const double p = wd * yd;
           acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
           aabs += fabs(p);
+          if (W) lomx = fmax(lomx, fabs(lxl));
+          lomy = fmax(lomy, fabs(lyl));
         }
       }
       yprev = yval<D>(yv[TN - 1]);
@@ -957,7 +985,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       auto wleft = [&](int l1, int i1, double2 P1, int l2, int i2, double2 P2, int l3, int i3, double2 P3) {
         const double t = turn_pts(P1, P2, P3);
         if (fabs(t) > Ec) return t > 0.0;
-        return entries_turn_dd<T, W, D>(&L, ckx, cky, ckxl, ckyl, l1, i1, l2, i2, l3, i3, len, yc, wc) > 0.0;
+        const int ls[3] = {l1, l2, l3}, is[3] = {i1, i2, i3};
+        return entries_turn_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, ls, is, len, yc, wc) > 0.0;
       };
       for (int pass = 0; pass <= kChunk; ++pass) {
         bool moved = false;
@@ -1036,15 +1065,18 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   const uint32_t fl = (__ballot((f & ISO_ROW_NONFINITE_BIT) != 0) ? ISO_ROW_NONFINITE_BIT : 0u) |
                       (__ballot((f & ISO_ROW_BAD_WEIGHT_BIT) != 0) ? ISO_ROW_BAD_WEIGHT_BIT : 0u);
   const bool listable = total <= kListCap;
+  // a chunk with an undecided turn keeps form byte 3 and is processed again by the exact pass
+  const bool ilane = frac == 0.0 && (W ? lx : (double)c) < 0x1p25 && aabs < 0x1p25;
+  const bool leave = !EXACT && __any(!(marg > 0.0) && !ilane);
   if (lane == 0) {
     out.nverts[g] = total;
     out.desc[g] = make_int4(j, 0, total - 1, desc_w(listable ? 0 : 1, total));
     out.nseg[g] = 1;
     out.cflags[g] = fl;
-    out.dform[g] = listable ? 0 : 1;
+    out.dform[g] = leave ? 3 : listable ? 0 : 1;
     const double2 E = L.start[nl], El = L.startl[nl];
     out.tot[g] = make_double2(E.x, E.y);
-    out.totl[g] = make_double2(El.x, El.y);
+    out.totl()[g] = make_double2(El.x, El.y);
   }
   if (listable) {
     const int64_t lb0 = g * (int64_t)kListCap;
@@ -1053,18 +1085,26 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       out.lk[lb0] = 0;
       out.lx[lb0] = 0.0;
       out.ly[lb0] = 0.0;
-      out.lxl[lb0] = 0.0;
-      out.lyl[lb0] = 0.0;
+      out.lxl()[lb0] = 0.0;
+      out.lyl()[lb0] = 0.0;
       pos = 1;
     }
+    // every lane integral: the chunk's coordinates are integers below 2^31, exact in the hi parts
+    const bool exact_chunk = __all(ilane);
     for (int i = lo; i <= hi; ++i) {
       int q;
-      const PD P = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, lane, i, len, yc, wc, q);
+      PD P;
+      if (exact_chunk) {
+        const double2 Ph = chunk_entry<T, W, D>(L, ckx, cky, lane, i, len, yc, wc, q);
+        P = PD{DD{Ph.x, 0.0}, DD{Ph.y, 0.0}};
+      } else {
+        P = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, lane, i, len, yc, wc, q);
+      }
       out.lk[lb0 + pos] = (uint16_t)(e0 + q);
       out.lx[lb0 + pos] = P.x.hi;
       out.ly[lb0 + pos] = P.y.hi;
-      out.lxl[lb0 + pos] = P.x.lo;
-      out.lyl[lb0 + pos] = P.y.lo;
+      out.lxl()[lb0 + pos] = P.x.lo;
+      out.lyl()[lb0 + pos] = P.y.lo;
       ++pos;
     }
     return;
@@ -1081,8 +1121,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       const PD P = chunk_entry_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, lane, lo, len, yc, wc, q);
       out.bnd[g].x = P.x.hi;
       out.bnd[g].y = P.y.hi;
-      out.bndl[g].x = P.x.lo;
-      out.bndl[g].y = P.y.lo;
+      out.bndl()[g].x = P.x.lo;
+      out.bndl()[g].y = P.y.lo;
       out.bndk[g].x = e0 + q;
     }
     // vertex V - 2: the entry before lz's last, or the last of the range before it, or point 0
@@ -1102,8 +1142,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       }
       out.bnd[g].z = P.x.hi;
       out.bnd[g].w = P.y.hi;
-      out.bndl[g].z = P.x.lo;
-      out.bndl[g].w = P.y.lo;
+      out.bndl()[g].z = P.x.lo;
+      out.bndl()[g].w = P.y.lo;
       out.bndk[g].y = kq;
     }
   }
@@ -1153,10 +1193,10 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   const int64_t sb = g * (int64_t)kWave;
   if (W) {
     out.lsx[sb + lane] = L.start[lane].x;
-    out.lsxl[sb + lane] = L.startl[lane].x;
+    out.lsxl()[sb + lane] = L.startl[lane].x;
   }
   out.lsy[sb + lane] = L.start[lane].y;
-  out.lsyl[sb + lane] = L.startl[lane].y;
+  out.lsyl()[sb + lane] = L.startl[lane].y;
 }
 
 }  // namespace iso

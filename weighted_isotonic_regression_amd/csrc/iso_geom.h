@@ -400,29 +400,31 @@ struct VertexStore {
   const uint8_t* dense;   // [G] 0 list form, 1 dense form, 2 dense form of an all-vertex chunk
   const double* lx;       // [G * kListCap] list form (pairs)
   const double* ly;
-  const double* lxl;
-  const double* lyl;
   const uint16_t* lk;
   const uint32_t* mask;   // [G * kMaskW] dense form
   const uint16_t* mcnt;   // [G * kMaskW]
   const double* lsx;      // [G * kWave]  lane starts (weighted only: x), pairs
   const double* lsy;
-  const double* lsxl;
-  const double* lsyl;
   const double* ckx;      // [G * kWave * kLaneW] lane-relative running sums (weighted only: x)
   const double* cky;
-  const double* ckxl;
-  const double* ckyl;
   const double2* tot;     // [G] chunk end point (W, S), hi and lo parts
-  const double2* totl;
   const double4* start;   // [G] chunk start {x hi, x lo, y hi, y lo}
   const double4* bnd;     // [G] dense form: vertices 1 and V - 2 {x1, y1, x2, y2}, hi and lo parts
-  const double4* bndl;
   const int2* bndk;       // [G] their point indices
   const T* y;
   const T* w;
   int64_t n;              // row length
   int m;                  // chunks per row
+  int64_t G;              // chunks of the call: each lo array follows its hi array, G chunks on
+
+  ISO_HD const double* lxl() const { return lx + G * kListCap; }
+  ISO_HD const double* lyl() const { return ly + G * kListCap; }
+  ISO_HD const double* lsxl() const { return lsx + G * kWave; }
+  ISO_HD const double* lsyl() const { return lsy + G * kWave; }
+  ISO_HD const double* ckxl() const { return ckx + G * (kWave * kLaneW); }
+  ISO_HD const double* ckyl() const { return cky + G * (kWave * kLaneW); }
+  ISO_HD const double2* totl() const { return tot + G; }
+  ISO_HD const double4* bndl() const { return bnd + G; }
 
   ISO_HD bool is_list(int64_t g) const { return dense[g] == 0; }
 
@@ -432,15 +434,15 @@ struct VertexStore {
   ISO_HD void dense_state(int64_t row, int j, int k, DD& sx, DD& sy, DD& ax, DD& ay) const {
     const int64_t g = row * m + j;
     const int l = k / kSub, q = k % kSub;
-    sx = W ? DD{lsx[g * kWave + l], lsxl[g * kWave + l]} : DD{(double)(kSub * l), 0.0};
-    sy = DD{lsy[g * kWave + l], lsyl[g * kWave + l]};
+    sx = W ? DD{lsx[g * kWave + l], lsxl()[g * kWave + l]} : DD{(double)(kSub * l), 0.0};
+    sy = DD{lsy[g * kWave + l], lsyl()[g * kWave + l]};
     ax = DD{0.0, 0.0};
     ay = DD{0.0, 0.0};
     if (q == 0) return;
     const int jj = q / kCk;
     const int64_t cb = (g * kWave + l) * kLaneW + jj;
-    if (W) ax = DD{ckx[cb], ckxl[cb]};
-    ay = DD{cky[cb], ckyl[cb]};
+    if (W) ax = DD{ckx[cb], ckxl()[cb]};
+    ay = DD{cky[cb], ckyl()[cb]};
     const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
     for (int e = kCk * jj; e < q; ++e) {
       double wd = W ? (double)w[e0 + e] : 1.0;
@@ -465,7 +467,7 @@ struct VertexStore {
     const int64_t rem = n - (int64_t)j * kChunk;
     const int len = rem < kChunk ? (int)rem : kChunk;
     if (k == len) {
-      const double2 t = tot[g], tl = totl[g];
+      const double2 t = tot[g], tl = totl()[g];
       return PD{DD{t.x, tl.x}, DD{t.y, tl.y}};
     }
     DD sx, sy, ax, ay;
@@ -480,7 +482,7 @@ struct VertexStore {
     if (dense[g] == 0) {
       const int64_t idx = g * kListCap + p;
       k = lk[idx];
-      return PD{DD{lx[idx], lxl[idx]}, DD{ly[idx], lyl[idx]}};
+      return PD{DD{lx[idx], lxl()[idx]}, DD{ly[idx], lyl()[idx]}};
     }
     // the vertices the merges and ends touch most: the chunk's two ends and their neighbours
     const int V = nverts[g];
@@ -491,11 +493,11 @@ struct VertexStore {
     if (p == V - 1) {
       const int64_t rem = n - (int64_t)j * kChunk;
       k = rem < kChunk ? (int)rem : kChunk;
-      const double2 t = tot[g], tl = totl[g];
+      const double2 t = tot[g], tl = totl()[g];
       return PD{DD{t.x, tl.x}, DD{t.y, tl.y}};
     }
     if (p == 1 || p == V - 2) {
-      const double4 b = bnd[g], bl = bndl[g];
+      const double4 b = bnd[g], bl = bndl()[g];
       const int2 bk = bndk[g];
       if (p == 1) {
         k = bk.x;
@@ -532,7 +534,7 @@ struct VertexStore {
   ISO_HD GPt pt_list(int64_t row, int j, int p) const {
     const int64_t g = row * m + j;
     const int64_t idx = g * kListCap + p;
-    return make_gpt(PD{DD{lx[idx], lxl[idx]}, DD{ly[idx], lyl[idx]}}, start[g]);
+    return make_gpt(PD{DD{lx[idx], lxl()[idx]}, DD{ly[idx], lyl()[idx]}}, start[g]);
   }
 
   // pt() of vertex p of the chunk of descriptor d, whose form and vertex count the descriptor
@@ -546,10 +548,10 @@ struct VertexStore {
       if (p == 0) {
         P = PD{DD{0.0, 0.0}, DD{0.0, 0.0}};
       } else if (p == V - 1) {
-        const double2 t = tot[g], tl = totl[g];
+        const double2 t = tot[g], tl = totl()[g];
         P = PD{DD{t.x, tl.x}, DD{t.y, tl.y}};
       } else {
-        const double4 b = bnd[g], bl = bndl[g];
+        const double4 b = bnd[g], bl = bndl()[g];
         P = p == 1 ? PD{DD{b.x, bl.x}, DD{b.y, bl.y}} : PD{DD{b.z, bl.z}, DD{b.w, bl.w}};
       }
       return make_gpt(P, start[g]);

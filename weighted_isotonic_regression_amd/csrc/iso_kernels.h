@@ -106,6 +106,39 @@ __device__ __forceinline__ void store16_nt(T* p, const T* in) {
   __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
 }
 
+// A double moved across lanes by a DPP permutation within each row of 16 lanes (a VALU move, no
+// LDS traffic).  Controls used: quad_perm [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E) pair lanes at
+// distance 1 and 2; row_half_mirror (0x141) pairs lane i with 7 - i of its eight; row_mirror
+// (0x140) pairs lane i with 15 - i of its sixteen.  Applied in this order they combine, after k
+// steps, every aligned group of 2^k lanes.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(b & 0xffffffffll), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// One step of a butterfly sum of pairs (hi, lo): the partner's pair is added with the exact
+// error of the hi addition kept in lo.  The sum is symmetric bit for bit, so both lanes of every
+// step, and so every lane of the group at the end, hold the same pair.
+template <int CTRL>
+__device__ __forceinline__ DD dpp_pair_sum(DD a) {
+  const DD b{dpp_move<CTRL>(a.hi), dpp_move<CTRL>(a.lo)};
+  const DD s = two_sum(a.hi, b.hi);
+  return DD{s.hi, (a.lo + b.lo) + s.lo};
+}
+
+// Sum of the pairs of each aligned group of G lanes (G = 2, 4, 8 or 16), in every lane of it.
+template <int G>
+__device__ __forceinline__ DD group_pair_sum(DD a) {
+  if (G >= 2) a = dpp_pair_sum<0xB1>(a);
+  if (G >= 4) a = dpp_pair_sum<0x4E>(a);
+  if (G >= 8) a = dpp_pair_sum<0x141>(a);
+  if (G >= 16) a = dpp_pair_sum<0x140>(a);
+  return a;
+}
+
 // Elements per load tile of the chunk pass: 16 elements of each input per lane, 8 for weighted
 // fp64 (the tile and its prefetched successor stay in registers).
 template <typename T, bool W>
@@ -863,9 +896,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     if (q + 1 < nv) {
       const int k1 = S.lk[lb + q + 1];
       sSlope[q] = k1 == k0 + 1 ? yval<D>(S.y[off + k0])
-                               : slope_dd(PD{DD{S.lx[lb + q], S.lxl[lb + q]}, DD{S.ly[lb + q], S.lyl[lb + q]}},
-                                          PD{DD{S.lx[lb + q + 1], S.lxl[lb + q + 1]},
-                                             DD{S.ly[lb + q + 1], S.lyl[lb + q + 1]}});
+                               : slope_dd(PD{DD{S.lx[lb + q], S.lxl()[lb + q]}, DD{S.ly[lb + q], S.lyl()[lb + q]}},
+                                          PD{DD{S.lx[lb + q + 1], S.lxl()[lb + q + 1]},
+                                             DD{S.ly[lb + q + 1], S.lyl()[lb + q + 1]}});
     }
   }
   __syncthreads();
