@@ -49,8 +49,12 @@ enum {
                       workspace too small */
   ISO_EWEIGHT = 2, /* synchronous weight check found a row with a weight <= 0 (or non-finite) */
   ISO_ENOMEM = 3,  /* device allocation of the workspace failed (iso_fit only) */
-  ISO_EHIP = 4     /* a HIP runtime call or kernel launch failed */
+  ISO_EHIP = 4,    /* a HIP runtime call or kernel launch failed */
+  ISO_ESCRATCH = 5 /* iso_fit_noalloc: the call needs more than ISO_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Bytes of the fixed device scratch of iso_fit_noalloc (256 MiB per GPU). */
+enum { ISO_NOALLOC_SCRATCH_BYTES = 268435456 };
 
 /* Flags of iso_fit_ex. */
 enum {
@@ -105,6 +109,25 @@ size_t iso_workspace_bytes(int64_t batch, int64_t n, int dtype, int weighted);
 int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,
                int64_t batch, int64_t n, int dtype, void* ws, size_t ws_bytes, unsigned flags,
                void* stream);
+
+/*
+ * iso_fit_noalloc -- iso_fit_ex for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with
+ * the workspace taken from a fixed scratch array of ISO_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The call itself allocates nothing.
+ *   Arguments as in iso_fit_ex, without ws and ws_bytes.  The stream's device must be the
+ *   current device (its scratch is looked up once per device, on the first call there).
+ *   A shape whose iso_workspace_bytes exceeds ISO_NOALLOC_SCRATCH_BYTES returns ISO_ESCRATCH
+ *   before anything is launched (one row of up to about 1.35e8 elements fits, and so do 1024
+ *   rows of 131072).
+ *   Every call on a GPU shares that GPU's scratch: calls that may overlap in time (different
+ *   streams, or different host threads) race and must not be issued; calls ordered on one
+ *   stream are safe.  No result depends on the scratch's previous contents.
+ * Returns ISO_OK, ISO_EINVAL, ISO_ESCRATCH, ISO_EWEIGHT (only with ISO_FLAG_CHECK_WEIGHTS, which
+ * waits for the stream) or ISO_EHIP.
+ */
+int iso_fit_noalloc(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,
+                    int64_t batch, int64_t n, int dtype, unsigned flags, void* stream);
 
 /*
  * iso_vjp -- backward of the fit: the vector-Jacobian product with a cotangent g.  The fit is

@@ -40,7 +40,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     assert set(_declared()) == {"iso_fit", "iso_workspace_bytes", "iso_fit_ex", "iso_vjp", "iso_strerror",
                                 "iso_fit_ragged", "iso_ragged_workspace_bytes", "iso_soft_rank",
-                                "iso_soft_rank_vjp"}
+                                "iso_soft_rank_vjp", "iso_fit_noalloc"}
     names = _declared(HEADERS)
     out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True,
                          check=True).stdout
@@ -55,7 +55,8 @@ def test_header_constants_match_binding():
     assert e["ISO_F32"] == binding.ISO_F32 and e["ISO_F64"] == binding.ISO_F64
     assert e["ISO_OK"] == binding.ISO_OK and e["ISO_EINVAL"] == binding.ISO_EINVAL
     assert e["ISO_EWEIGHT"] == binding.ISO_EWEIGHT and e["ISO_ENOMEM"] == binding.ISO_ENOMEM
-    assert e["ISO_EHIP"] == binding.ISO_EHIP
+    assert e["ISO_EHIP"] == binding.ISO_EHIP and e["ISO_ESCRATCH"] == binding.ISO_ESCRATCH
+    assert e["ISO_NOALLOC_SCRATCH_BYTES"] == binding.ISO_NOALLOC_SCRATCH_BYTES
     assert e["ISO_FLAG_CHECK_WEIGHTS"] == binding.ISO_FLAG_CHECK_WEIGHTS
     assert e["ISO_FLAG_DECREASING"] == binding.ISO_FLAG_DECREASING
     assert e["ISO_ROW_NONFINITE"] == binding.ISO_ROW_NONFINITE
@@ -63,7 +64,7 @@ def test_header_constants_match_binding():
 
 
 def test_strerror(lib):
-    for code in range(5):
+    for code in range(6):
         assert binding.iso_strerror(code)
     assert "unknown" in binding.iso_strerror(99)
 
@@ -104,6 +105,26 @@ def test_argument_errors_before_any_launch(lib):
     assert binding.iso_fit(None, None, Z, 1, 5, 0, None) == EINVAL
 
 
+def test_noalloc_argument_errors_before_any_launch(lib):
+    na = binding.iso_fit_noalloc
+    EINVAL, OK = binding.ISO_EINVAL, binding.ISO_OK
+    assert na(None, None, Z, None, None, 1, 10, 0, 0, None) == EINVAL         # y NULL
+    assert na(Y, None, None, None, None, 1, 10, 0, 0, None) == EINVAL         # z NULL
+    assert na(Y, None, Z, None, None, -1, 10, 0, 0, None) == EINVAL           # negative batch
+    assert na(Y, None, Z, None, None, 1, 10, 3, 0, None) == EINVAL            # bad dtype
+    assert na(Y, None, Z, None, None, 1, 10, 0, 8, None) == EINVAL            # unknown flag
+    assert na(Y, None, Z, None, None, 0, 10, 0, 0, None) == OK                # empty
+    assert na(Y, None, Z, None, None, 3, 0, 1, 2, None) == OK
+    # more workspace than the fixed scratch holds: refused before the scratch is looked up
+    cap = binding.ISO_NOALLOC_SCRATCH_BYTES
+    assert binding.iso_workspace_bytes(1, 135_000_000, 1, 0) <= cap
+    assert binding.iso_workspace_bytes(1, 140_000_000, 1, 0) > cap
+    assert binding.iso_workspace_bytes(1024, 131072, 0, 1) <= cap
+    assert na(Y, None, Z, None, None, 1, 140_000_000, 1, 0, None) == binding.ISO_ESCRATCH
+    assert na(Y, W, Z, None, None, 4096, 131072, 0, 1, None) == binding.ISO_ESCRATCH
+    assert "scratch" in binding.iso_strerror(binding.ISO_ESCRATCH)
+
+
 def test_vjp_argument_errors(lib):
     vj = binding.iso_vjp
     EINVAL = binding.ISO_EINVAL
@@ -123,10 +144,11 @@ def test_workspace_sizes(lib):
     assert ws(-1, 10, 0, 0) == 0 and ws(1, 10, 9, 0) == 0
     short = ws(65536, 16, 0, 1)
     assert 65536 * 4 <= short < 65536 * 4 + 4096
-    # long rows: per chunk of 16384 a list of up to 256 vertices (18 B each), the dense form's mask,
-    # lane starts and checkpoints, tile marks and descriptors: about 1 byte per element
+    # long rows: per chunk of 16384 a list of up to 256 vertices, the dense form's mask, lane starts
+    # and checkpoints (coordinates as pairs of doubles), tile marks and descriptors: about 2 bytes
+    # per element
     big = ws(1, 10 ** 8, 0, 1)
-    assert 0.5 * 10 ** 8 < big < 2 * 10 ** 8
+    assert 10 ** 8 < big < 2.5 * 10 ** 8
 
 
 def _offs(vals):

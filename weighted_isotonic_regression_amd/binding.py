@@ -15,7 +15,8 @@ import threading
 from . import build as _build
 
 ISO_F32, ISO_F64 = 0, 1
-ISO_OK, ISO_EINVAL, ISO_EWEIGHT, ISO_ENOMEM, ISO_EHIP = 0, 1, 2, 3, 4
+ISO_OK, ISO_EINVAL, ISO_EWEIGHT, ISO_ENOMEM, ISO_EHIP, ISO_ESCRATCH = 0, 1, 2, 3, 4, 5
+ISO_NOALLOC_SCRATCH_BYTES = 256 << 20
 ISO_FLAG_CHECK_WEIGHTS = 1
 ISO_FLAG_DECREASING = 2
 ISO_ROW_NONFINITE, ISO_ROW_BAD_WEIGHT = 1, 2
@@ -30,6 +31,7 @@ _SIGS = {
     "iso_workspace_bytes": ([_I64, _I64, ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
     "iso_fit_ex": ([_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, ctypes.c_size_t, ctypes.c_uint, _P],
                    ctypes.c_int),
+    "iso_fit_noalloc": ([_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, ctypes.c_uint, _P], ctypes.c_int),
     "iso_vjp": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P], ctypes.c_int),
     "iso_fit_ragged": ([_P, _P, _P, _I64, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_uint, _P],
                        ctypes.c_int),
@@ -83,6 +85,10 @@ def iso_workspace_bytes(batch, n, dtype, weighted):
 
 def iso_fit_ex(y, w, z, block_start, row_flags, batch, n, dtype, ws, ws_bytes, flags, stream):
     return load().iso_fit_ex(y, w, z, block_start, row_flags, batch, n, dtype, ws, ws_bytes, flags, stream)
+
+
+def iso_fit_noalloc(y, w, z, block_start, row_flags, batch, n, dtype, flags, stream):
+    return load().iso_fit_noalloc(y, w, z, block_start, row_flags, batch, n, dtype, flags, stream)
 
 
 def iso_vjp(g, y, w, z, block_start, gy, gw, batch, n, dtype, stream):

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include <rocprim/device/device_radix_sort.hpp>
@@ -31,6 +32,11 @@
 #include "iso_merge.h"
 #include "iso_ragged.h"
 #include "iso_softrank.h"
+
+// The fixed scratch of iso_fit_noalloc: one copy on every GPU the library runs on, kept until the
+// process ends.  Host code never uses this name as an address; scratch_address() looks up the
+// copy of the current device once and keeps it.
+static __device__ __align__(256) char scratch[ISO_NOALLOC_SCRATCH_BYTES];
 
 static_assert(iso::ISO_ROW_NONFINITE_BIT == ISO_ROW_NONFINITE, "flag bits");
 static_assert(iso::ISO_ROW_BAD_WEIGHT_BIT == ISO_ROW_BAD_WEIGHT, "flag bits");
@@ -164,6 +170,29 @@ struct Prof {
     if (on && c.marks > 1) g_prof_calls.push_back(c);
   }
 };
+
+// ---- scratch of iso_fit_noalloc: its device address, per device, looked up on first use
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ISO_EHIP;
+  if (s) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return ISO_EHIP;
+    if (sdev != dev) return ISO_EINVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ISO_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ISO_OK;
+}
 
 int lanes_per_row(int64_t n) {
   int need = (int)((n + kLanePts - 1) / kLanePts);
@@ -591,6 +620,7 @@ const char* iso_strerror(int code) {
     case ISO_EWEIGHT: return "a row holds a weight <= 0";
     case ISO_ENOMEM: return "device allocation failed";
     case ISO_EHIP: return "HIP runtime error";
+    case ISO_ESCRATCH: return "the call needs more workspace than iso_fit_noalloc's fixed scratch (256 MiB)";
     default: return "unknown error code";
   }
 }
@@ -640,6 +670,21 @@ int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint
     if (host & ISO_ROW_BAD_WEIGHT) return ISO_EWEIGHT;
   }
   return ISO_OK;
+}
+
+int iso_fit_noalloc(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,
+                    int64_t batch, int64_t n, int dtype, unsigned flags, void* stream) {
+  if (!shape_ok(batch, n, dtype)) return ISO_EINVAL;
+  if (flags & ~(unsigned)(ISO_FLAG_CHECK_WEIGHTS | ISO_FLAG_DECREASING)) return ISO_EINVAL;
+  if (batch == 0 || n == 0) return ISO_OK;
+  if (!y || !z) return ISO_EINVAL;
+  const size_t need = make_layout(batch, n).total;
+  if (need > (size_t)ISO_NOALLOC_SCRATCH_BYTES) return ISO_ESCRATCH;
+  void* ws = nullptr;
+  const int rc = scratch_address((hipStream_t)stream, &ws);
+  if (rc != ISO_OK) return rc;
+  return iso_fit_ex(y, w, z, block_start, row_flags, batch, n, dtype, ws, (size_t)ISO_NOALLOC_SCRATCH_BYTES, flags,
+                    stream);
 }
 
 int iso_fit(const void* y, const void* w, void* z, int64_t batch, int64_t n, int dtype,
