@@ -78,7 +78,7 @@ def stage_alg_bytes(stage, n_elems, esz, weighted, whole_diagram):
     return 0
 
 
-STAGE_KERNEL = {"increasing": "k_increasing", "chunk": "k_chunk", "scan": "k_scan",
+STAGE_KERNEL = {"increasing": "k_increasing", "chunk": "k_chunk", "exact": "k_chunk_exact", "scan": "k_scan",
                 "merge": "k_merge_levels", "ends": "k_ends", "fit": "k_fit"}
 
 
@@ -173,23 +173,29 @@ def read_traffic():
 
 
 def roofline_of(workload, stages_ms, stages_launch, calls, n_elems, esz, weighted, whole_diagram, traffic):
+    """The dominant stage's kernel against HBM: the fit's algorithmic bytes per element (read y,
+    read w, write z) times the elements one launch processes, over its average launch time.
+    `kernel_alg_bytes_per_launch` is what that kernel itself must move (its own reads and writes)."""
     dom = max(stages_ms, key=lambda k: stages_ms[k])
     launches = max(stages_launch[dom], 1)
     avg_ms = stages_ms[dom] / launches
-    per_launch_bytes = stage_alg_bytes(dom, n_elems, esz, weighted, whole_diagram) * calls / launches
+    per_launch_bytes = alg_bytes_per_elem(esz, weighted) * n_elems * calls / launches
+    own_bytes = stage_alg_bytes(dom, n_elems, esz, weighted, whole_diagram) * calls / launches
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
     kern = STAGE_KERNEL[dom]
     t = traffic.get(workload, {}).get(kern)
     return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if t is None else int(t[0] + t[1]),
-            "kernel": kern, "alg_bytes_per_launch": int(per_launch_bytes), "avg_launch_ms": round(avg_ms, 4)}
+            "kernel": kern, "alg_bytes_per_launch": int(per_launch_bytes),
+            "kernel_alg_bytes_per_launch": int(own_bytes), "avg_launch_ms": round(avg_ms, 4)}
 
 
 def stage_line(st_ms, calls):
     return {k: round(v / max(calls, 1), 4) for k, v in st_ms.items()}
 
 
-ONLY = {"mixed": "mixed_1e8", "dense": "nearly_monotone_1e8", "short": "short_rows_16", "calib": "calibration",
+ONLY = {"mixed": "mixed_1e8", "dense": "nearly_monotone_1e8", "hull": "nearly_monotone_reversals_1e8",
+        "short": "short_rows_16", "calib": "calibration",
         "mono7": "nearly_monotone_1e7", "ramp": "ramp_noise_4096", "table1": "noise_1e7_decreasing"}
 
 
@@ -359,14 +365,21 @@ def summarize_pmc(fetch_dir, write_dir):
     sf = COPY_BYTES / (sorted(copy_f)[len(copy_f) // 2])
     sw = COPY_BYTES / (sorted(copy_w)[len(copy_w) // 2])
     def mine(k, key):
+        if key in ("k_chunk", "k_chunk_exact"):
+            # k_chunk<T, W, D, EXACT>: the first pass, or the exact pass over the chunks it left
+            i = k.find("iso::k_chunk<")
+            if i < 0:
+                return False
+            args = k[i + len("iso::k_chunk<"):].split(">")[0].split(",")
+            return (args[-1].strip() == "true") == (key == "k_chunk_exact")
         return ("iso::%s<" % key) in k or ("iso::%s(" % key) in k
 
     # fit calls in the run: one k_chunk (long rows), k_wave (short rows) or k_tiny dispatch each
     calls = max(sum(len(vs) for k, vs in fetch.items() if mine(k, "k_chunk") or mine(k, "k_wave") or
                     mine(k, "k_tiny")), 1)
     lines = []
-    for key in ("k_tiny", "k_wave", "k_increasing", "k_chunk", "k_scan_reduce", "k_scan_apply", "k_merge_levels",
-                "k_ends", "k_fit"):
+    for key in ("k_tiny", "k_wave", "k_increasing", "k_chunk", "k_chunk_exact", "k_scan_reduce", "k_scan_apply",
+                "k_merge_levels", "k_ends", "k_fit"):
         fs = [v for k, vs in fetch.items() if mine(k, key) for v in vs]
         wsz = [v for k, vs in write.items() if mine(k, key) for v in vs]
         if fs and wsz:
@@ -528,6 +541,22 @@ def main():
                                 "stage_ms": stage_line(dms, dc),
                                 "roofline": roofline_of("dense_1e8_f64", dms, dla, dc, nd, 8, True, True, traffic),
                                 "max_deviation_vs_y": dev_y}
+        del yd, wd, zd
+        torch.cuda.empty_cache()
+        # dense hull through the general chunk pass: the same row with a few reversals per chunk
+        print("bench: timing nearly_monotone_reversals_1e8 (fp64)", file=sys.stderr, flush=True)
+        _, _, yr, wr = load_workload(torch, W, "hull", dev)
+        _, msr, _, _, _ = time_fit(torch, B, [(yr, wr)], max(3, args.steps // 2), 2, stages=False)
+        _, _, rms, rla, rc = time_fit(torch, B, [(yr, wr)], max(3, args.steps // 2), 2)
+        nr = yr.shape[1]
+        gbs = nr * alg_bytes_per_elem(8, True) / (msr * 1e-3) / 1e9
+        out["dense_hull_1e8_f64"] = {"elements_per_s": round(nr / (msr * 1e-3), 1), "ms_per_call": round(msr, 4),
+                                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "achieved_gbs": round(gbs, 2),
+                                     "stage_ms": stage_line(rms, rc),
+                                     "roofline": roofline_of("hull_1e8_f64", rms, rla, rc, nr, 8, True, False,
+                                                             traffic)}
+        del yr, wr
+        torch.cuda.empty_cache()
         out["soft_rank_f32"] = time_soft_rank(torch, B, dev)
     print(json.dumps(out), flush=True)
 

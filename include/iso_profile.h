@@ -7,9 +7,10 @@
  * dominant kernel inside its own timed region.
  *
  * Stages: 0 whole-diagram chunks (k_increasing), 1 chunk pass (k_chunk; k_wave for rows of at
- * most 8192 elements, k_tiny for rows of at most 16), 2 chunk-start scan (2 launches), 3 merge
- * levels (three levels of the tree per launch: ceil(ceil(log2 m) / 3) launches for m chunks),
- * 4 ends, 5 fit.  Rows of at most 8192 elements run stage 1 only.
+ * most 4096 elements, k_tiny for rows of at most 16), 2 exact chunk pass (k_chunk on the chunks
+ * whose turns the first pass could not decide), 3 chunk-start scan (2 launches), 4 merge levels
+ * (three levels of the tree per launch: ceil(ceil(log2 m) / 3) launches for m chunks), 5 ends,
+ * 6 fit.  Rows of at most 4096 elements run stage 1 only.
  *
  * While enabled, every iso_fit_ex call records one event before its first kernel and one after
  * each stage, on its stream.  The state is process-global and not thread-safe: enable, run the
@@ -24,18 +25,18 @@
 extern "C" {
 #endif
 
-enum { ISO_PROF_STAGES = 6 };
+enum { ISO_PROF_STAGES = 7 };
 
 /* Turn event recording on (1) or off (0).  Returns ISO_OK. */
 int iso_prof_enable(int on);
 
 /* Wait for the recorded events, add each stage's elapsed milliseconds and kernel launch count
- * since the last reset into ms[0..5] and launches[0..5] (arrays of ISO_PROF_STAGES entries
+ * since the last reset into ms[0..6] and launches[0..6] (arrays of ISO_PROF_STAGES entries
  * owned by the caller), store the number of timed calls in *calls, then forget the events.
  * Returns ISO_OK or ISO_EHIP. */
 int iso_prof_read(double* ms, int64_t* launches, int64_t* calls);
 
-/* Static name of a stage ("increasing", "chunk", "scan", "merge", "ends", "fit"), or "?". */
+/* Static name of a stage ("increasing", "chunk", "exact", "scan", "merge", "ends", "fit"), or "?". */
 const char* iso_prof_stage_name(int stage);
 
 #ifdef __cplusplus

@@ -33,16 +33,18 @@ def test_counters_are_scaled_by_the_calibration_copy(tmp_path):
     # 2^20 KiB of WRITE_SIZE (scale 1); k_chunk reads 1000 KiB and writes 300 KiB per launch over two
     # fit calls, and k_merge_levels runs 3 times per call
     copy = "void at::native::elementwise_kernel<copy>(int)"
-    chunk = "void iso::k_chunk<float, true, false>(float const*)"
+    chunk = "void iso::k_chunk<float, true, false, false>(float const*)"
+    exact = "void iso::k_chunk<float, true, false, true>(float const*)"
     merge = "void iso::k_merge_levels<float, true, false>(iso::VertexStore<float, true, false>, int, int, long)"
-    _counter_csv(str(tmp_path / "f"), "FETCH_SIZE", [(copy, 524288), (chunk, 1000), (chunk, 1000)] +
+    _counter_csv(str(tmp_path / "f"), "FETCH_SIZE", [(copy, 524288), (chunk, 1000), (exact, 7), (chunk, 1000), (exact, 7)] +
                  [(merge, 10)] * 6)
-    _counter_csv(str(tmp_path / "w"), "WRITE_SIZE", [(copy, 1048576), (chunk, 300), (chunk, 300)] +
+    _counter_csv(str(tmp_path / "w"), "WRITE_SIZE", [(copy, 1048576), (chunk, 300), (exact, 5), (chunk, 300), (exact, 5)] +
                  [(merge, 4)] * 6)
     sf, sw, lines = bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"))
     assert sf == pytest.approx(2.0) and sw == pytest.approx(1.0)
     got = {k: (fb, wb, lpc) for k, fb, wb, lpc in lines}
     assert got["k_chunk"] == (pytest.approx(1000 * 1024 * 2.0), pytest.approx(300 * 1024 * 1.0), 1.0)
+    assert got["k_chunk_exact"] == (pytest.approx(7 * 1024 * 2.0), pytest.approx(5 * 1024 * 1.0), 1.0)
     assert got["k_merge_levels"] == (pytest.approx(10 * 1024 * 2.0), pytest.approx(4 * 1024 * 1.0), 3.0)
 
 
@@ -56,15 +58,17 @@ def test_stored_traffic_of_other_sources_is_ignored(tmp_path, monkeypatch):
 
 
 def test_roofline_arithmetic():
-    # one fit call of a 10^8 fp32 weighted row: the chunk pass (dominant stage) reads y and w of the
-    # 10^8 elements (8 bytes each) in 1 ms
-    st_ms = {"increasing": 0.02, "chunk": 1.0, "scan": 0.01, "merge": 0.2, "ends": 0.01, "fit": 0.07}
+    # one fit call of a 10^8 fp32 weighted row: the chunk pass (dominant stage) takes 1 ms for the
+    # 10^8 elements, whose fit must move 12 bytes each (read y and w, write z); the pass itself reads 8
+    st_ms = {"increasing": 0.02, "chunk": 1.0, "exact": 0.01, "scan": 0.01, "merge": 0.2, "ends": 0.01,
+             "fit": 0.07}
     st_la = {k: 1 for k in st_ms}
     st_la["merge"] = 13
     traffic = {"w": {"k_chunk": (1.3e9, 0.3e9)}}
     r = bench.roofline_of("w", st_ms, st_la, 1, 10**8, 4, True, False, traffic)
     assert r["kernel"] == "k_chunk" and r["bound"] == "hbm" and r["unit"] == "GB/s"
-    assert r["alg_bytes_per_launch"] == 8 * 10**8
-    assert r["achieved"] == pytest.approx(800.0)
-    assert r["frac"] == pytest.approx(800.0 / 8000.0, abs=1e-4)
+    assert r["alg_bytes_per_launch"] == 12 * 10**8
+    assert r["kernel_alg_bytes_per_launch"] == 8 * 10**8
+    assert r["achieved"] == pytest.approx(1200.0)
+    assert r["frac"] == pytest.approx(1200.0 / 8000.0, abs=1e-4)
     assert r["traffic"] == int(1.6e9)

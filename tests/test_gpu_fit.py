@@ -140,6 +140,19 @@ def test_nearly_monotone_1e8_fp64():
         np.testing.assert_array_equal(z, y)  # one-element blocks output their y
 
 
+def test_nearly_monotone_reversals_1e8_fp64():
+    """The dense hull through the general chunk pass: a few reversals in nearly every chunk of
+    16384, so the strictly increasing shortcut rarely applies and almost every point is a
+    vertex.  Against the oracle at 1e-10, block starts identical (every block boundary here is
+    decided by steps of about 1e-8 against noise of 2e-9, far from any tie)."""
+    y, w = W.nearly_monotone_reversals_1e8()
+    chunks = y[0, : (y.shape[1] // 16384) * 16384].reshape(-1, 16384)
+    assert np.mean(np.any(np.diff(chunks, axis=1) <= 0, axis=1)) > 0.9
+    for ww in (w, None):
+        z, bs = check(y, ww, kkt=False, exact_partition=True)
+        assert bs.mean() > 0.99
+
+
 def wrong_steps(z, decreasing=False):
     """Largest step of z against the fit direction, relative to max(1, max |z|)."""
     z = np.asarray(z, dtype=np.float64)

@@ -43,7 +43,7 @@ _SIGS = {
     "iso_prof_read": ([_P, _P, _P], ctypes.c_int),
     "iso_prof_stage_name": ([ctypes.c_int], ctypes.c_char_p),
 }
-ISO_PROF_STAGES = 6
+ISO_PROF_STAGES = 7
 
 
 class IsoError(RuntimeError):

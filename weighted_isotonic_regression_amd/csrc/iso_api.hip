@@ -259,8 +259,9 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
                      m, co);
   prof.mark(1);
   hipLaunchKernelGGL((k_chunk<T, W, D, false>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
+  prof.mark(1);
   hipLaunchKernelGGL((k_chunk<T, W, D, true>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
-  prof.mark(2);
+  prof.mark(1);
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
                      s, co.tot, co.tot + G, co.cflags, bsum, bflag, m, nblk);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
@@ -609,7 +610,7 @@ int iso_prof_read(double* ms, int64_t* launches, int64_t* calls) {
 }
 
 const char* iso_prof_stage_name(int stage) {
-  static const char* names[ISO_PROF_STAGES] = {"increasing", "chunk", "scan", "merge", "ends", "fit"};
+  static const char* names[ISO_PROF_STAGES] = {"increasing", "chunk", "exact", "scan", "merge", "ends", "fit"};
   return (stage >= 0 && stage < ISO_PROF_STAGES) ? names[stage] : "?";
 }
 

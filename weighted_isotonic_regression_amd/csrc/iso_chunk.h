@@ -16,9 +16,10 @@
 //                totals) plus those.  Running sums are pairs (hi, lo): hi is the fp64 running sum
 //                the chain works with, lo the exact sum of its rounding errors.
 //   Section 6    "Predicates": a turn of the chain is evaluated on the hi parts and used when it
-//                exceeds an a-priori bound in terms of the lane's magnitudes; otherwise the three
-//                points' pairs are recomputed from their checkpoints and the turn is decided in
-//                double-double arithmetic.
+//                exceeds an a-priori bound built from the magnitudes of its own differences and
+//                products and of the lo parts; a chunk with a turn inside its bound is processed
+//                again by an exact pass, which decides such turns in double-double arithmetic
+//                from the three points' pairs, recomputed from their checkpoints.
 //
 // Per lane state: the top three stack entries in registers, the last kRingS entries in an LDS
 // ring indexed by depth, the stack as a bit mask in LDS, and the running sums every 32 points (the
@@ -26,10 +27,15 @@
 // from its checkpoint and the inputs; on the measured workloads this is rare (the stacks of noisy
 // rows stay shallow and dense rows never pop).
 //
-// Dense rows: a tile of elements during which a lane popped nothing has had every element pushed
-// as its own block, so the lane writes z = y for it and marks the tile.  The fit pass keeps
-// those values where the final hull confirms single-element blocks (Corollary 4.5) and writes
-// the rest.
+// In the first pass a lane does not pop at the element that causes the pops: its candidate points
+// wait in a short LDS queue, and the wave runs chain steps (one push or pop per lane) only when
+// some queue is full, so that lanes with few pops are not held at every element by the lane with
+// the most.  The exact pass keeps the plain element-by-element chain.
+//
+// Dense rows: a clean strictly increasing tile pushed on top of its two predecessors has every
+// element as its own block so far, so the lane writes z = y for it and marks the tile.  The fit
+// pass keeps those values where the final hull confirms single-element blocks (Corollary 4.5)
+// and writes the rest.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -84,6 +90,10 @@ __device__ __forceinline__ uint64_t lanes_below(int x) {
   return x >= 64 ? ~0ull : ((1ull << x) - 1ull);
 }
 
+// c ? a : b on values (never on references, so both sides stay in registers).
+__device__ __forceinline__ double sel(bool c, double a, double b) { return c ? a : b; }
+__device__ __forceinline__ int sel(bool c, int a, int b) { return c ? a : b; }
+
 // One input element as the chain uses it: a non-finite value or a weight <= 0 is replaced by
 // (y, w) = (0, 1), and its kind is or-ed into f.
 template <bool W>
@@ -99,7 +109,7 @@ __device__ __forceinline__ void classify(double& yd, double& wd, uint32_t& f) {
 }
 
 // Stack entries a lane keeps in LDS: depths 0 and 1 have slots of their own, deeper entries cycle
-// through kRingS - 2 slots.  Every slot carries a tag (point index | depth << 16), so a read knows
+// through kRingS - 2 slots.  Every slot carries a tag (point index and depth), so a read knows
 // whether the slot still holds the entry of the depth it asks for; an entry that has been
 // overwritten is found again from the stack mask and recomputed from its checkpoint and the
 // inputs.
@@ -114,17 +124,35 @@ struct RingCoord<false> {
   using type = double;  // y only: x is the point index
 };
 
-// LDS of one wavefront.
+// The first pass's candidate queue: a lane's points waiting for the chain, kQ slots per lane.  The
+// elements stream through kQStep at a time; before the next kQStep points can arrive, every lane
+// must hold at most kQ - kQStep, so the wave runs chain steps (one push or one pop per lane) only
+// while some lane is above that.  A lane with few pops thus runs ahead of the others instead of
+// waiting at every element for the lane with the most.
+constexpr int kQ = 4;
+constexpr int kQStep = 2;
+
+// LDS of one wavefront.  The queue is used only during the chains and the lane results only
+// after them, so they share their space.
 template <bool W>
 struct ChunkLds {
   typename RingCoord<W>::type ring[kRingS][kWave];
-  uint32_t rtag[kRingS][kWave];
+  uint16_t rtag[kRingS][kWave];
   uint32_t smask[kSubW][kWave];  // stack bit mask over the lane's points 0..256
-  int depth[kWave];              // final stack depth
-  int lo[kWave], hi[kWave];      // surviving depth range of the lane's stack
-  double2 start[kWave + 1];      // lane starts, chunk-relative (hi); [l + 1] is lane l's end point
-  double2 startl[kWave + 1];     // (lo)
+  union {
+    struct {
+      int depth[kWave];              // final stack depth
+      int lo[kWave], hi[kWave];      // surviving depth range of the lane's stack
+      double2 start[kWave + 1];      // lane starts, chunk-relative (hi); [l + 1] is lane l's end point
+      double2 startl[kWave + 1];     // (lo)
+    };
+    struct {
+      typename RingCoord<W>::type qp[kQ][kWave];  // queued points, lane-relative (y only without w)
+      uint8_t qi[kQ][kWave];                      // their point indices less one
+    };
+  };
 };
+
 
 // Ring slot of stack depth i.
 __device__ __forceinline__ int ring_slot(int i) { return i < 2 ? i : 2 + (i - 2) % (kRingS - 2); }
@@ -133,14 +161,19 @@ __device__ __forceinline__ int ring_slot(int i) { return i < 2 ? i : 2 + (i - 2)
 __device__ __forceinline__ int ring_next(int s) { return s == kRingS - 1 ? 2 : s + 1; }
 __device__ __forceinline__ int ring_prev(int s, int i) { return (s == 2 && i > 2) ? kRingS - 1 : s - 1; }
 
-__device__ __forceinline__ uint32_t ring_tag(int q, int i) { return (uint32_t)q | ((uint32_t)i << 16); }
+// A slot's tag: point index q (9 bits) and depth i mod 128.  Slots are reused only by depths that
+// differ by multiples of the ring's cycle (kRingS - 2 = 10), so two depths of one slot below 640
+// never share a residue mod 128: the tag tells the depth exactly.
+__device__ __forceinline__ uint32_t ring_tag(int q, int i) { return (uint32_t)q | ((uint32_t)(i & 127) << 9); }
+__device__ __forceinline__ int tag_q(uint32_t tg) { return (int)(tg & 0x1ffu); }
+__device__ __forceinline__ bool tag_is(uint32_t tg, int i) { return (tg >> 9) == (uint32_t)(i & 127); }
 
 template <bool W>
 __device__ __forceinline__ void ring_put(ChunkLds<W>& L, int s, int lane, double x, double y,
                                          uint32_t tag) {
   if constexpr (W) L.ring[s][lane] = double2{x, y};
   else L.ring[s][lane] = y;
-  L.rtag[s][lane] = tag;
+  L.rtag[s][lane] = (uint16_t)tag;
 }
 
 // Reads slot s of lane l: point index q, lane-relative coordinates, and whether the slot holds
@@ -150,7 +183,7 @@ __device__ __forceinline__ bool ring_get(const ChunkLds<W>& L, int s, int l, int
                                          double& x, double& y) {
   const uint32_t tg = L.rtag[s][l];
   const typename RingCoord<W>::type P = L.ring[s][l];
-  q = (int)(tg & 0xffffu);
+  q = tag_q(tg);
   if constexpr (W) {
     x = P.x;
     y = P.y;
@@ -158,7 +191,7 @@ __device__ __forceinline__ bool ring_get(const ChunkLds<W>& L, int s, int l, int
     x = (double)q;
     y = P;
   }
-  return (tg >> 16) == (uint32_t)i;
+  return tag_is(tg, i);
 }
 
 // Lane-relative coordinates of lane l's point q, from the checkpoint below q and the inputs (the
@@ -229,9 +262,9 @@ __device__ int lane_index(const ChunkLds<W>& L, int l, int i, int c, bool& in_ri
   if (i == 0) return 0;
   const int s = ring_slot(i);
   const uint32_t tg = L.rtag[s][l];
-  if ((tg >> 16) == (uint32_t)i) {
+  if (tag_is(tg, i)) {
     in_ring = true;
-    return (int)(tg & 0xffffu);
+    return tag_q(tg);
   }
   int rem = i;
   int wd = 0;
@@ -612,219 +645,468 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   // the elements q - 1 and q, whose slopes are y_{q-1} and y_q; unless y_{q-1} < y_q it is not a
   // strict vertex of any hull containing its neighbours, so it is never pushed.
   for (int wd = 0; wd < kSubW; ++wd) L.smask[wd][lane] = 0u;
-  for (int sl = 0; sl < kRingS; ++sl) L.rtag[sl][lane] = 0xffffffffu;
+  for (int sl = 0; sl < kRingS; ++sl) L.rtag[sl][lane] = 0xffffu;
   uint32_t f = 0u;
   // The top three stack entries T (depth d - 1), U (d - 2) and V (d - 3) are held in registers
   // with their point indices ti, ui, vi and ring slots ts, us, vs.
-  int d = 0, ti = 0, ui = 0, vi = 0, ts = 0, us = 0, vs = 0;
+  int d = 0;
   double tx = 0.0, ty = 0.0, ux = 0.0, uy = 0.0, vx = 0.0, vy = 0.0;
   double lx = 0.0, ly = 0.0;     // running sums (hi)
   double lxl = 0.0, lyl = 0.0;   // their lo parts
   double aabs = 0.0;             // sum of |w y| so far: bounds every |y| of the lane's points
   double lomx = 0.0, lomy = 0.0; // largest |lo| of the running sums so far
   double yprev = 0.0;
-  int wi = 0;
-  uint32_t curw = 0u;
-  if (c > 0) {  // point 0 at depth 0
-    ring_put<W>(L, 0, lane, 0.0, 0.0, ring_tag(0, 0));
-    d = 1;
-    curw = 1u;
-  }
-  int pops = 0;
-  // V is refilled from the ring after each pop (depth d - 3); its tag is checked only when the
-  // next pop is about to make it U, so the LDS read overlaps the next turn.  An overwritten entry
-  // is recomputed: the highest stack bit below ui, from its checkpoint and the inputs; that
-  // recomputation waits for its own loads before it leaves, so no load of it is still pending
-  // where the loop continues.
-  uint32_t vtag = 0u;
-  bool vchk = false;
-  auto check_v = [&]() {
-    if (!vchk) return;
-    vi = (int)(vtag & 0xffffu);
-    if (!W) vx = (double)vi;
-    if (d >= 3 && (vtag >> 16) != (uint32_t)(d - 3)) {
-      int ww = ui >> 5;
-      uint32_t mw = mask_word<W>(L, lane, ww, wi, curw) & ((1u << (ui & 31)) - 1u);
-      while (mw == 0u) {
-        --ww;
-        mw = mask_word<W>(L, lane, ww, wi, curw);
-      }
-      vi = kCk * ww + 31 - __builtin_clz(mw);
-      const double2 P = lane_point<T, W, D>(ckx, cky, lane, vi, c, yl, wl);
-      vx = P.x;
-      vy = P.y;
-      __builtin_amdgcn_s_waitcnt(0);
+  double marg = INFINITY;  // smallest |t| - (error bound of t) of the turns taken
+  double frac = 0.0;       // 0 while every coordinate so far is an integer
+  const int ntiles = (c + TN - 1) / TN;
+  if constexpr (EXACT) {
+    int ti = 0, ui = 0, vi = 0, ts = 0, us = 0, vs = 0;
+    int wi = 0;
+    uint32_t curw = 0u;
+    if (c > 0) {  // point 0 at depth 0
+      ring_put<W>(L, 0, lane, 0.0, 0.0, ring_tag(0, 0));
+      d = 1;
+      curw = 1u;
     }
-    vchk = false;
-  };
-  // The turn (U, T, K) of the hi parts.  Every point so far has 0 <= x <= Ax (the current x),
-  // |y| <= Ay = sum |w y|, and lo parts of at most LX and LY in magnitude (the largest seen), so
-  // each difference of hi parts is within u |d| + 2 LX (or 2 LY) of the difference of the pairs
-  // and the fast turn is within 14 u Ax Ay + 4 Ax LY + 8 Ay LX (to first order) of the turn of
-  // the pairs; Ecur = 16 u Ax Ay + 8 (Ax LY + Ay LX), set before each push.  While every point
-  // pushed so far has integer coordinates below 2^25 (frac = 0, Ax and Ay below 2^25), the fast
-  // turn is exact.  Otherwise a turn inside the bound is decided only by the EXACT instantiation,
-  // in double-double arithmetic from U and T recomputed from their checkpoints and K's running
-  // pairs; the first pass merely records the smallest margin |t| - Ecur (marg) and leaves the
-  // chunk to the exact pass, which runs on the chunks it left.  On noisy rows that is rare, and
-  // the first pass carries no slow path.
-  double Ecur = 0.0;
-  double marg = INFINITY;  // smallest |t| - Ecur of the turns taken
-  double frac = 0.0;       // largest fractional part of a pushed point's coordinates
-  auto turn_utk = [&](const double kx, const double ky, const int q) {
-    double t = cross2(tx - ux, ty - uy, kx - ux, ky - uy);
-    if constexpr (EXACT) {
+    int pops = 0;
+    // V is refilled from the ring after each pop (depth d - 3); its tag is checked only when the
+    // next pop is about to make it U, so the LDS read overlaps the next turn.  An overwritten entry
+    // is recomputed: the highest stack bit below ui, from its checkpoint and the inputs; that
+    // recomputation waits for its own loads before it leaves, so no load of it is still pending
+    // where the loop continues.
+    uint32_t vtag = 0u;
+    bool vchk = false;
+    auto check_v = [&]() {
+      if (!vchk) return;
+      vi = tag_q(vtag);
+      if (!W) vx = (double)vi;
+      if (d >= 3 && !tag_is(vtag, d - 3)) {
+        int ww = ui >> 5;
+        uint32_t mw = mask_word<W>(L, lane, ww, wi, curw) & ((1u << (ui & 31)) - 1u);
+        while (mw == 0u) {
+          --ww;
+          mw = mask_word<W>(L, lane, ww, wi, curw);
+        }
+        vi = kCk * ww + 31 - __builtin_clz(mw);
+        const double2 P = lane_point<T, W, D>(ckx, cky, lane, vi, c, yl, wl);
+        vx = P.x;
+        vy = P.y;
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      vchk = false;
+    };
+    // The exact pass (the chunks the first pass left).  The turn (U, T, K) is first taken on the
+    // hi parts.  Every point so far has 0 <= x <= Ax (the current x), |y| <= Ay = sum |w y|, and
+    // lo parts of at most LX and LY in magnitude (the largest seen), so each difference of hi parts
+    // is within u |d| + 2 LX (or 2 LY) of the difference of the pairs and the fast turn is within
+    // 14 u Ax Ay + 4 Ax LY + 8 Ay LX (to first order) of the turn of the pairs; Ecur = 16 u Ax Ay +
+    // 8 (Ax LY + Ay LX), set before each push.  While every point pushed so far has integer
+    // coordinates below 2^25 (frac = 0, Ax and Ay below 2^25), the fast turn is exact.  Otherwise
+    // a turn inside the bound is decided in double-double arithmetic from U and T recomputed from
+    // their checkpoints and K's running pairs.
+    double Ecur = 0.0;
+    auto turn_utk = [&](const double kx, const double ky, const int q) {
+      double t = cross2(tx - ux, ty - uy, kx - ux, ky - uy);
       const bool ilane = frac == 0.0 && (W ? lx : (double)q) < 0x1p25 && aabs < 0x1p25;
       if (d >= 2 && !ilane && !(fabs(t) > Ecur))
         t = chain_turn_dd<T, W, D>(ckx, cky, ckxl, ckyl, lane, ui, ti, c, yl, wl, kx, W ? lxl : 0.0, ky, lyl);
-    } else {
-      marg = fmin(marg, (d >= 2 ? fabs(t) : INFINITY) - Ecur);
-    }
-    return t;
-  };
-  // pushes point q with lane-relative coordinates (kx, ky), first popping what it makes
-  // non-convex (pop while the turn (U, T, K) is not strictly left).  A popped entry's stack bit
-  // is cleared in LDS (the word being filled is rewritten from curw later) and in curw.
-  auto push = [&](const double kx, const double ky, const int q) {
-    {
-      const double ax = W ? lx : (double)q;
-      Ecur = fma(ax * 0x1p-49, aabs, 8.0 * fma(ax, lomy, aabs * lomx));
-    }
-    frac = fmax(frac, fabs(ky - floor(ky)) + (W ? fabs(kx - floor(kx)) : 0.0));
-    bool more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
-    if (more) {
-      while (more) {
-        check_v();
-        {
-          const uint32_t nbit = ~(1u << (ti & 31));
-          atomicAnd(&L.smask[ti >> 5][lane], nbit);
-          if ((ti >> 5) == wi) curw &= nbit;
+      return t;
+    };
+    // pushes point q with lane-relative coordinates (kx, ky), first popping what it makes
+    // non-convex (pop while the turn (U, T, K) is not strictly left).  A popped entry's stack bit
+    // is cleared in LDS (the word being filled is rewritten from curw later) and in curw.
+    auto push = [&](const double kx, const double ky, const int q) {
+      {
+        const double ax = W ? lx : (double)q;
+        Ecur = fma(ax * 0x1p-49, aabs, 8.0 * fma(ax, lomy, aabs * lomx));
+      }
+      frac = fmax(frac, fabs(ky - floor(ky)) + (W ? fabs(kx - floor(kx)) : 0.0));
+      bool more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
+      if (more) {
+        while (more) {
+          check_v();
+          {
+            const uint32_t nbit = ~(1u << (ti & 31));
+            atomicAnd(&L.smask[ti >> 5][lane], nbit);
+            if ((ti >> 5) == wi) curw &= nbit;
+          }
+          ++pops;
+          tx = ux;
+          ty = uy;
+          ti = ui;
+          ts = us;
+          ux = vx;
+          uy = vy;
+          ui = vi;
+          us = vs;
+          --d;
+          vs = max(ring_prev(us, d - 2), 0);
+          const uint32_t tg = L.rtag[vs][lane];
+          if constexpr (W) {
+            const double2 P = L.ring[vs][lane];
+            vx = P.x;
+            vy = P.y;
+          } else {
+            vy = L.ring[vs][lane];
+          }
+          vtag = tg;  // (the point index and the check wait until V is used)
+          vchk = true;
+          more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
         }
-        ++pops;
-        tx = ux;
-        ty = uy;
-        ti = ui;
-        ts = us;
-        ux = vx;
-        uy = vy;
-        ui = vi;
-        us = vs;
-        --d;
-        vs = max(ring_prev(us, d - 2), 0);
-        const uint32_t tg = L.rtag[vs][lane];
-        if constexpr (W) {
-          const double2 P = L.ring[vs][lane];
-          vx = P.x;
-          vy = P.y;
-        } else {
-          vy = L.ring[vs][lane];
+      }
+      const int ks = ring_next(ts);
+      ring_put<W>(L, ks, lane, kx, ky, ring_tag(q, d));
+      curw |= 1u << (q & 31);
+      vx = ux;
+      vy = uy;
+      vi = ui;
+      vs = us;
+      ux = tx;
+      uy = ty;
+      ui = ti;
+      us = ts;
+      tx = kx;
+      ty = ky;
+      ti = q;
+      ts = ks;
+      vchk = false;
+      ++d;
+    };
+    // the next tile's inputs are loaded while the current one is processed
+    T ny[TN], nw[TN];
+    auto load_tile = [&](int eb) {
+      if (vec && eb + TN <= c) {
+  #pragma unroll
+        for (int k = 0; k < TN / VN; ++k) {
+          load16(yl + eb + k * VN, &ny[k * VN]);
+          if (W) load16(wl + eb + k * VN, &nw[k * VN]);
         }
-        vtag = tg;  // (the point index and the check wait until V is used)
-        vchk = true;
-        more = (d >= 2) & !(turn_utk(kx, ky, q) > 0.0);
+      } else {
+  #pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          ny[k] = (eb + k < c) ? yl[eb + k] : (T)0;
+          if (W) nw[k] = (eb + k < c) ? wl[eb + k] : (T)1;
+        }
       }
-    }
-    const int ks = ring_next(ts);
-    ring_put<W>(L, ks, lane, kx, ky, ring_tag(q, d));
-    curw |= 1u << (q & 31);
-    vx = ux;
-    vy = uy;
-    vi = ui;
-    vs = us;
-    ux = tx;
-    uy = ty;
-    ui = ti;
-    us = ts;
-    tx = kx;
-    ty = ky;
-    ti = q;
-    ts = ks;
-    vchk = false;
-    ++d;
-  };
-  const int ntiles = (c + TN - 1) / TN;
-  // the next tile's inputs are loaded while the current one is processed
-  T ny[TN], nw[TN];
-  auto load_tile = [&](int eb) {
-    if (vec && eb + TN <= c) {
-#pragma unroll
-      for (int k = 0; k < TN / VN; ++k) {
-        load16(yl + eb + k * VN, &ny[k * VN]);
-        if (W) load16(wl + eb + k * VN, &nw[k * VN]);
+    };
+    if (ntiles > 0) load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+      const int eb = t * TN;  // lane-relative index of the tile's first element
+      if ((eb & (kCk - 1)) == 0) {
+        if (W) {
+          ckx[lane * kLaneW + eb / kCk] = lx;
+          ckxl[lane * kLaneW + eb / kCk] = lxl;
+        }
+        cky[lane * kLaneW + eb / kCk] = ly;
+        ckyl[lane * kLaneW + eb / kCk] = lyl;
       }
-    } else {
-#pragma unroll
+      if ((eb >> 5) != wi) {  // the tile's points 32 w .. are in mask word w (same for every lane)
+        L.smask[wi][lane] = curw;
+        wi = eb >> 5;
+        curw = 0u;
+      }
+      T yv[TN], wv[TN];
+  #pragma unroll
       for (int k = 0; k < TN; ++k) {
-        ny[k] = (eb + k < c) ? yl[eb + k] : (T)0;
-        if (W) nw[k] = (eb + k < c) ? wl[eb + k] : (T)1;
+        yv[k] = ny[k];
+        wv[k] = W ? nw[k] : (T)1;
       }
-    }
-  };
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int eb = t * TN;  // lane-relative index of the tile's first element
-    if ((eb & (kCk - 1)) == 0) {
-      if (W) {
-        ckx[lane * kLaneW + eb / kCk] = lx;
-        ckxl[lane * kLaneW + eb / kCk] = lxl;
+      if (t + 1 < ntiles) load_tile(eb + TN);
+      const int kn = min(TN, c - eb);
+      // Tile checks.  A non-finite value or a weight <= 0 is replaced by (y, w) = (0, 1) and its
+      // kind recorded.  When the tile's elements are clean and strictly increasing in y after the
+      // previous element, every turn among its points and the two before them is strictly convex
+      // in exact arithmetic (the slopes of the one-element edges are the y values), so once the
+      // stack's top two entries are the points just before the tile's (the first of them was
+      // pushed on top of its own predecessor, so its turn is convex too), all of the tile's points
+      // are pushed without tests.
+      bool clean = kn == TN, incr = true;
+      {
+        double yp = yprev;
+  #pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          const double yd = yval<D>(yv[k]);
+          const double wd = W ? (double)wv[k] : 1.0;
+          clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0;
+          incr = incr && (yp < yd || (eb == 0 && k == 0));
+          yp = yd;
+        }
       }
-      cky[lane * kLaneW + eb / kCk] = ly;
-      ckyl[lane * kLaneW + eb / kCk] = lyl;
-    }
-    if ((eb >> 5) != wi) {  // the tile's points 32 w .. are in mask word w (same for every lane)
-      L.smask[wi][lane] = curw;
-      wi = eb >> 5;
-      curw = 0u;
-    }
-    T yv[TN], wv[TN];
-#pragma unroll
-    for (int k = 0; k < TN; ++k) {
-      yv[k] = ny[k];
-      wv[k] = W ? nw[k] : (T)1;
-    }
-    if (t + 1 < ntiles) load_tile(eb + TN);
-    const int kn = min(TN, c - eb);
-    // Tile checks.  A non-finite value or a weight <= 0 is replaced by (y, w) = (0, 1) and its
-    // kind recorded.  When the tile's elements are clean and strictly increasing in y after the
-    // previous element, every turn among its points and the two before them is strictly convex
-    // in exact arithmetic (the slopes of the one-element edges are the y values), so once the
-    // stack's top two entries are the points just before the tile's (the first of them was
-    // pushed on top of its own predecessor, so its turn is convex too), all of the tile's points
-    // are pushed without tests.
-    bool clean = kn == TN, incr = true;
-    {
-      double yp = yprev;
-#pragma unroll
-      for (int k = 0; k < TN; ++k) {
+      if (!__all(clean)) {
+  #pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          if (k < kn) {
+            double yd = (double)yv[k], wd = W ? (double)wv[k] : 1.0;
+            classify<W>(yd, wd, f);
+            yv[k] = (T)yd;
+            if (W) wv[k] = (T)wd;
+          }
+        }
+      }
+      const int pops0 = pops;
+      bool skipped = false;
+      // one element through the chain: its left point q (a candidate when y_{q-1} < y_q), then
+      // the running sums
+      auto element = [&](int k) {
         const double yd = yval<D>(yv[k]);
         const double wd = W ? (double)wv[k] : 1.0;
-        clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0;
-        incr = incr && (yp < yd || (eb == 0 && k == 0));
-        yp = yd;
+        const int q = eb + k;
+        if (q > 0) {
+          if (yprev < yd) push(W ? lx : (double)q, ly, q);
+          else skipped = true;
+        }
+        if (W) acc(lx, lxl, wd);
+        const double p = wd * yd;
+        acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+        aabs += fabs(p);
+        if (W) lomx = fmax(lomx, fabs(lxl));
+        lomy = fmax(lomy, fabs(lyl));
+        yprev = yd;
+      };
+      // pushes the tile's points eb + k, k >= kp, without tests, and consumes its elements k >= kc
+      // (point eb + k is pushed before element k is added to the running sums)
+      auto bulk_push = [&](const int kp, const int kc) {
+        int s = ts;
+  #pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          if (k >= kp) {
+            const double kx = W ? lx : (double)(eb + k), ky = ly;
+            frac = fmax(frac, fabs(ky - floor(ky)) + (W ? fabs(kx - floor(kx)) : 0.0));
+            s = ring_next(s);
+            if (k >= TN - (kRingS - 2) || d < 2) ring_put<W>(L, s, lane, kx, ky, ring_tag(eb + k, d));
+            vx = ux;
+            vy = uy;
+            vi = ui;
+            vs = us;
+            ux = tx;
+            uy = ty;
+            ui = ti;
+            us = ts;
+            tx = kx;
+            ty = ky;
+            ti = eb + k;
+            ts = s;
+            ++d;
+          }
+          if (k >= kc) {
+            const double wd = W ? (double)wv[k] : 1.0;
+            const double yd = yval<D>(yv[k]);
+            if (W) acc(lx, lxl, wd);
+            const double p = wd * yd;
+            acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+            aabs += fabs(p);
+            if (W) lomx = fmax(lomx, fabs(lxl));
+            lomy = fmax(lomy, fabs(lyl));
+          }
+        }
+        yprev = yval<D>(yv[TN - 1]);
+        const int b0 = (eb & 31) + kp, b1 = (eb & 31) + TN - 1;  // bits of points eb+kp .. eb+TN-1
+        curw |= (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u);
+      };
+      // bulk from the tile's first point, or else after element 0 went through the chain (at
+      // eb == 0, d == 1 means point 0 alone on the stack)
+      bool bulk = __all(clean && incr && (eb == 0 ? d == 1 : (ti == eb - 1 && ui == eb - 2)));
+      int kp = eb == 0 ? 1 : 0, kc = 0;
+      if (!bulk) {
+        if (kn > 0) element(0);
+        bulk = __all(clean && incr && ti == eb && (eb == 0 ? d == 1 : ui == eb - 1));
+        kp = 1;
+        kc = 1;
       }
+      if (bulk) {
+        bulk_push(kp, kc);
+      } else {
+  #pragma unroll
+        for (int k = 1; k < TN; ++k)
+          if (k < kn) element(k);
+      }
+      // speculative fit of a tile that pushed every point and popped none: every element is its
+      // own block so far
+      uint8_t zt = 0;
+      if (pops == pops0 && !skipped && kn == TN && vec) {
+  #pragma unroll
+        for (int k = 0; k < TN / VN; ++k) store16(zl + eb + k * VN, &yv[k * VN]);
+        zt = 1;
+      }
+      out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
     }
-    if (!__all(clean)) {
-#pragma unroll
-      for (int k = 0; k < TN; ++k) {
-        if (k < kn) {
-          double yd = (double)yv[k], wd = W ? (double)wv[k] : 1.0;
-          classify<W>(yd, wd, f);
-          yv[k] = (T)yd;
-          if (W) wv[k] = (T)wd;
+    if (c > 0) {
+      // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
+      // point of the lane has one)
+      if ((c & (kCk - 1)) == 0 && c < kSub) {
+        if (W) {
+          ckx[lane * kLaneW + c / kCk] = lx;
+          ckxl[lane * kLaneW + c / kCk] = lxl;
+        }
+        cky[lane * kLaneW + c / kCk] = ly;
+        ckyl[lane * kLaneW + c / kCk] = lyl;
+      }
+      if ((c >> 5) != wi) {
+        L.smask[wi][lane] = curw;
+        wi = c >> 5;
+        curw = 0u;
+      }
+      push(W ? lx : (double)c, ly, c);
+      L.smask[wi][lane] = curw;
+    }
+  } else {
+    // The first pass.  Each lane queues its candidate points in LDS as the elements stream
+    // through, and the wave runs chain steps on the queues whenever a lane's queue is about to
+    // overflow.  A turn is decided by the sign of its fp64 value on the hi parts when that value
+    // exceeds its error bound, built from the magnitudes of the differences and products it is
+    // made of (below); a chunk with a turn inside its bound is left to the exact pass, unless
+    // every input so far is an integer and the sums stay below 2^25, which makes every turn exact.
+    int ti = 0, ui = 0, vi = 0, ts = 0, us = 0, vs = 0;
+    if (c > 0) {  // point 0 at depth 0
+      ring_put<W>(L, 0, lane, 0.0, 0.0, ring_tag(0, 0));
+      L.smask[0][lane] = 1u;
+      d = 1;
+    }
+    int qh = 0, qt = 0;  // queue head and tail counters (slot = counter mod kQ)
+    // K = the queue's head and N = the entry after it, read one step ahead
+    double kx = 0.0, ky = 0.0, nx = 0.0, ny_ = 0.0;
+    int kq = 0, nq = 0;
+    bool intin = true;   // every input so far an integer
+    // Error bound of the turn (U, T, K) computed as p1 - p2, p1 = dx1 dy2, p2 = dy1 dx2, with
+    // (dx1, dy1) = T - U and (dx2, dy2) = K - T on the hi parts.  A hi part is within LX (LY) of its
+    // pair (the largest |lo| so far), so each difference is within u|d| + 2 LX (or LY) of the
+    // difference of the pairs; with the rounding of the two products and the subtraction, the
+    // turn of the pairs is within 4u' (|p1| + |p2|) + 2 LX (|dy1| + |dy2|) + 2 LY (|dx1| + |dx2|)
+    // + 8 LX LY of t, to first order; each term is taken 1 % larger for the neglected ones.
+    double cLX = 0.0, cLY = 0.0, E0 = 0x1p-1000;
+    // After a pop, V's ring entry is read into (rvx, rvy, rtg) and taken into V only when the next
+    // pop needs it (vpend), so the read overlaps a whole step.  An entry whose tag shows it was
+    // overwritten is recomputed: the highest stack bit below ui, from its checkpoint and the
+    // inputs (waiting for its own loads before it leaves).
+    double rvx = 0.0, rvy = 0.0;
+    uint32_t rtg = 0u;
+    bool vpend = false;
+    struct QE {
+      double x, y;
+      int q;
+    };
+    auto read_q = [&](const int h) __attribute__((always_inline)) {
+      const int s = h & (kQ - 1);
+      QE e;
+      if constexpr (W) {
+        const double2 P = L.qp[s][lane];
+        e.x = P.x;
+        e.y = P.y;
+      } else {
+        e.y = L.qp[s][lane];
+      }
+      e.q = (int)L.qi[s][lane] + 1;
+      if (!W) e.x = (double)e.q;
+      return e;
+    };
+    // one push or pop of the queue's head K, for every lane that has one
+    auto step = [&]() __attribute__((always_inline)) {
+      const bool act = qt != qh;
+      const double dx1 = tx - ux, dy1 = ty - uy, dx2 = kx - tx, dy2 = ky - ty;
+      const double p1 = dx1 * dy2, p2 = dy1 * dx2;
+      const double t = p1 - p2;
+      const double E = fma(4.04 * kU, fabs(p1) + fabs(p2),
+                           fma(cLY, fabs(dx1) + fabs(dx2), fma(cLX, fabs(dy1) + fabs(dy2), E0)));
+      const bool tst = act && d >= 2;
+      marg = sel(tst, fmin(marg, fabs(t) - E), marg);
+      const bool push = act && (d < 2 || t > 0.0);
+      const bool pop = act && !push;
+      // V becomes U on a pop: take the entry read after the previous pop
+      const bool take = pop && vpend;
+      vx = sel(take, W ? rvx : (double)tag_q(rtg), vx);
+      vy = sel(take, rvy, vy);
+      vi = sel(take, tag_q(rtg), vi);
+      if (__any(take && d >= 3 && !tag_is(rtg, d - 3))) {
+        if (take && d >= 3 && !tag_is(rtg, d - 3)) {
+          int ww = ui >> 5;
+          uint32_t mw = L.smask[ww][lane] & ((1u << (ui & 31)) - 1u);
+          while (mw == 0u) {
+            --ww;
+            mw = L.smask[ww][lane];
+          }
+          vi = kCk * ww + 31 - __builtin_clz(mw);
+          const double2 P = lane_point<T, W, D>(ckx, cky, lane, vi, c, yl, wl);
+          vx = P.x;
+          vy = P.y;
+          __builtin_amdgcn_s_waitcnt(0);
         }
       }
-    }
-    const int pops0 = pops;
-    bool skipped = false;
-    // one element through the chain: its left point q (a candidate when y_{q-1} < y_q), then
-    // the running sums
-    auto element = [&](int k) {
+      const int ks = ring_next(ts);
+      if (push) {
+        ring_put<W>(L, ks, lane, kx, ky, ring_tag(kq, d));
+        atomicOr(&L.smask[kq >> 5][lane], 1u << (kq & 31));
+      }
+      if (pop) atomicAnd(&L.smask[ti >> 5][lane], ~(1u << (ti & 31)));
+      // push: (V, U, T) <- (U, T, K); pop: (U, T) <- (V, U), V read below
+      const double ntx = sel(push, kx, sel(pop, ux, tx)), nty = sel(push, ky, sel(pop, uy, ty));
+      const int nti = sel(push, kq, sel(pop, ui, ti)), nts = sel(push, ks, sel(pop, us, ts));
+      const double nux = sel(push, tx, sel(pop, vx, ux)), nuy = sel(push, ty, sel(pop, vy, uy));
+      const int nui = sel(push, ti, sel(pop, vi, ui)), nus = sel(push, ts, sel(pop, vs, us));
+      vx = sel(push, ux, vx);
+      vy = sel(push, uy, vy);
+      vi = sel(push, ui, vi);
+      vs = sel(push, us, vs);
+      tx = ntx;
+      ty = nty;
+      ti = nti;
+      ts = nts;
+      ux = nux;
+      uy = nuy;
+      ui = nui;
+      us = nus;
+      d += push ? 1 : pop ? -1 : 0;
+      vs = sel(pop, max(ring_prev(us, d - 2), 0), vs);
+      vpend = pop || (!push && vpend);
+      qh += push ? 1 : 0;
+      kx = sel(push, nx, kx);
+      ky = sel(push, ny_, ky);
+      kq = sel(push, nq, kq);
+      // the reads for the next steps: the entry after the head, and V's ring slot
+      {
+        const QE e = read_q(qh + 1);
+        nx = e.x;
+        ny_ = e.y;
+        nq = e.q;
+      }
+      rtg = L.rtag[vs][lane];
+      if constexpr (W) {
+        const double2 P = L.ring[vs][lane];
+        rvx = P.x;
+        rvy = P.y;
+      } else {
+        rvy = L.ring[vs][lane];
+      }
+    };
+    // chain steps until no lane holds more than `keep` queued points
+    auto drain = [&](const int keep) __attribute__((always_inline)) {
+      cLX = 2.02 * lomx;
+      cLY = 2.02 * lomy;
+      E0 = 8.08 * lomx * lomy + 0x1p-1000;
+      {
+        const QE e = read_q(qh), e2 = read_q(qh + 1);
+        kx = e.x;
+        ky = e.y;
+        kq = e.q;
+        nx = e2.x;
+        ny_ = e2.y;
+        nq = e2.q;
+      }
+      while (__any(qt - qh > keep)) step();
+    };
+    // element k of the tile: its left point joins the queue when it is a candidate, then the
+    // element joins the running sums
+    T yv[TN], wv[TN];
+    int eb = 0;
+    auto produce = [&](const int k) __attribute__((always_inline)) {
       const double yd = yval<D>(yv[k]);
       const double wd = W ? (double)wv[k] : 1.0;
       const int q = eb + k;
-      if (q > 0) {
-        if (yprev < yd) push(W ? lx : (double)q, ly, q);
-        else skipped = true;
+      if (q > 0 && yprev < yd) {
+        const int s = qt & (kQ - 1);
+        if constexpr (W) L.qp[s][lane] = double2{lx, ly};
+        else L.qp[s][lane] = ly;
+        L.qi[s][lane] = (uint8_t)(q - 1);
+        ++qt;
       }
       if (W) acc(lx, lxl, wd);
       const double p = wd * yd;
@@ -832,19 +1114,19 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       aabs += fabs(p);
       if (W) lomx = fmax(lomx, fabs(lxl));
       lomy = fmax(lomy, fabs(lyl));
+      intin = intin && yd == rint(yd) && (!W || wd == rint(wd));
       yprev = yd;
     };
-    // pushes the tile's points eb + k, k >= kp, without tests, and consumes its elements k >= kc
-    // (point eb + k is pushed before element k is added to the running sums)
-    auto bulk_push = [&](const int kp, const int kc) {
+    // pushes the tile's points eb + k, k >= kp, without tests (a clean strictly increasing tile
+    // on top of its two predecessors, every queue empty), and consumes its elements k >= kc
+    auto bulk_push = [&](const int kp, const int kc) __attribute__((always_inline)) {
       int s = ts;
 #pragma unroll
       for (int k = 0; k < TN; ++k) {
         if (k >= kp) {
-          const double kx = W ? lx : (double)(eb + k), ky = ly;
-          frac = fmax(frac, fabs(ky - floor(ky)) + (W ? fabs(kx - floor(kx)) : 0.0));
+          const double px = W ? lx : (double)(eb + k), py = ly;
           s = ring_next(s);
-          if (k >= TN - (kRingS - 2) || d < 2) ring_put<W>(L, s, lane, kx, ky, ring_tag(eb + k, d));
+          if (k >= TN - (kRingS - 2) || d < 2) ring_put<W>(L, s, lane, px, py, ring_tag(eb + k, d));
           vx = ux;
           vy = uy;
           vi = ui;
@@ -853,8 +1135,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           uy = ty;
           ui = ti;
           us = ts;
-          tx = kx;
-          ty = ky;
+          tx = px;
+          ty = py;
           ti = eb + k;
           ts = s;
           ++d;
@@ -868,57 +1150,126 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           aabs += fabs(p);
           if (W) lomx = fmax(lomx, fabs(lxl));
           lomy = fmax(lomy, fabs(lyl));
+          intin = intin && yd == rint(yd) && (!W || wd == rint(wd));
         }
       }
+      vpend = false;
       yprev = yval<D>(yv[TN - 1]);
       const int b0 = (eb & 31) + kp, b1 = (eb & 31) + TN - 1;  // bits of points eb+kp .. eb+TN-1
-      curw |= (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u);
+      atomicOr(&L.smask[eb >> 5][lane],
+               (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u));
     };
-    // bulk from the tile's first point, or else after element 0 went through the chain (at
-    // eb == 0, d == 1 means point 0 alone on the stack)
-    bool bulk = __all(clean && incr && (eb == 0 ? d == 1 : (ti == eb - 1 && ui == eb - 2)));
-    int kp = eb == 0 ? 1 : 0, kc = 0;
-    if (!bulk) {
-      if (kn > 0) element(0);
-      bulk = __all(clean && incr && ti == eb && (eb == 0 ? d == 1 : ui == eb - 1));
-      kp = 1;
-      kc = 1;
-    }
-    if (bulk) {
-      bulk_push(kp, kc);
-    } else {
+    // the next tile's inputs are loaded while the current one is processed
+    T ny[TN], nw[TN];
+    auto load_tile = [&](int e) __attribute__((always_inline)) {
+      if (vec && e + TN <= c) {
 #pragma unroll
-      for (int k = 1; k < TN; ++k)
-        if (k < kn) element(k);
-    }
-    // speculative fit of a tile that pushed every point and popped none: every element is its
-    // own block so far
-    uint8_t zt = 0;
-    if (pops == pops0 && !skipped && kn == TN && vec) {
+        for (int k = 0; k < TN / VN; ++k) {
+          load16(yl + e + k * VN, &ny[k * VN]);
+          if (W) load16(wl + e + k * VN, &nw[k * VN]);
+        }
+      } else {
 #pragma unroll
-      for (int k = 0; k < TN / VN; ++k) store16(zl + eb + k * VN, &yv[k * VN]);
-      zt = 1;
-    }
-    out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
-  }
-  if (c > 0) {
-    // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
-    // point of the lane has one)
-    if ((c & (kCk - 1)) == 0 && c < kSub) {
-      if (W) {
-        ckx[lane * kLaneW + c / kCk] = lx;
-        ckxl[lane * kLaneW + c / kCk] = lxl;
+        for (int k = 0; k < TN; ++k) {
+          ny[k] = (e + k < c) ? yl[e + k] : (T)0;
+          if (W) nw[k] = (e + k < c) ? wl[e + k] : (T)1;
+        }
       }
-      cky[lane * kLaneW + c / kCk] = ly;
-      ckyl[lane * kLaneW + c / kCk] = lyl;
+    };
+    if (ntiles > 0) load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+      eb = t * TN;
+      if ((eb & (kCk - 1)) == 0) {
+        if (W) {
+          ckx[lane * kLaneW + eb / kCk] = lx;
+          ckxl[lane * kLaneW + eb / kCk] = lxl;
+        }
+        cky[lane * kLaneW + eb / kCk] = ly;
+        ckyl[lane * kLaneW + eb / kCk] = lyl;
+      }
+#pragma unroll
+      for (int k = 0; k < TN; ++k) {
+        yv[k] = ny[k];
+        wv[k] = W ? nw[k] : (T)1;
+      }
+      if (t + 1 < ntiles) load_tile(eb + TN);
+      const int kn = min(TN, c - eb);
+      // tile checks, as in the exact pass
+      bool clean = kn == TN, incr = true;
+      {
+        double yp = yprev;
+#pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          const double yd = yval<D>(yv[k]);
+          const double wd = W ? (double)wv[k] : 1.0;
+          clean = clean && isfinite(yd) && isfinite(wd) && wd > 0.0;
+          incr = incr && (yp < yd || (eb == 0 && k == 0));
+          yp = yd;
+        }
+      }
+      if (!__all(clean)) {
+#pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          if (k < kn) {
+            double yd = (double)yv[k], wd = W ? (double)wv[k] : 1.0;
+            classify<W>(yd, wd, f);
+            yv[k] = (T)yd;
+            if (W) wv[k] = (T)wd;
+          }
+        }
+      }
+      // a clean strictly increasing tile goes on the stack without tests once the queues are
+      // empty and the top two entries are the points just before the tile (at eb == 0, point 0
+      // alone); failing that, after its first point went through the chain
+      bool bulk = false;
+      int kc = 0;
+      if (__all(clean && incr)) {
+        drain(0);
+        bulk = __all(eb == 0 ? d == 1 : (ti == eb - 1 && ui == eb - 2));
+        if (!bulk) {
+          produce(0);
+          drain(0);
+          kc = 1;
+          bulk = __all(ti == eb && (eb == 0 ? d == 1 : ui == eb - 1));
+        }
+      }
+      uint8_t zt = 0;
+      if (bulk) {
+        bulk_push(eb == 0 ? 1 : kc, kc);
+        // every element of the tile is its own block so far
+        if (kn == TN && vec) {
+#pragma unroll
+          for (int k = 0; k < TN / VN; ++k) store16(zl + eb + k * VN, &yv[k * VN]);
+          zt = 1;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < TN; ++k) {
+          if (k >= kc && k < kn) produce(k);
+          if ((k & (kQStep - 1)) == kQStep - 1) drain(kQ - kQStep);
+        }
+      }
+      out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
     }
-    if ((c >> 5) != wi) {
-      L.smask[wi][lane] = curw;
-      wi = c >> 5;
-      curw = 0u;
+    if (c > 0) {
+      // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
+      // point of the lane has one) joins the queue, and the queues are emptied
+      if ((c & (kCk - 1)) == 0 && c < kSub) {
+        if (W) {
+          ckx[lane * kLaneW + c / kCk] = lx;
+          ckxl[lane * kLaneW + c / kCk] = lxl;
+        }
+        cky[lane * kLaneW + c / kCk] = ly;
+        ckyl[lane * kLaneW + c / kCk] = lyl;
+      }
+      const int s = qt & (kQ - 1);
+      if constexpr (W) L.qp[s][lane] = double2{lx, ly};
+      else L.qp[s][lane] = ly;
+      L.qi[s][lane] = (uint8_t)(c - 1);
+      ++qt;
     }
-    push(W ? lx : (double)c, ly, c);
-    L.smask[wi][lane] = curw;
+    drain(0);
+    frac = intin ? 0.0 : 1.0;
   }
   for (int t = ntiles; t < kSub / TN; ++t) out.ztile[g * (int64_t)kZTiles + (e0 + t * TN) / TN] = 0;
 
