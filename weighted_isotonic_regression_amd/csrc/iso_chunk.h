@@ -928,7 +928,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         for (int k = 0; k < TN / VN; ++k) store16(zl + eb + k * VN, &yv[k * VN]);
         zt = 1;
       }
-      out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
+#pragma unroll
+      for (int h = 0; h < TN / kZT; ++h) out.ztile[g * (int64_t)kZTiles + (e0 + eb) / kZT + h] = zt;
     }
     if (c > 0) {
       // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
@@ -1249,7 +1250,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           if ((k & (kQStep - 1)) == kQStep - 1) drain(kQ - kQStep);
         }
       }
-      out.ztile[g * (int64_t)kZTiles + (e0 + eb) / TN] = zt;
+#pragma unroll
+      for (int h = 0; h < TN / kZT; ++h) out.ztile[g * (int64_t)kZTiles + (e0 + eb) / kZT + h] = zt;
     }
     if (c > 0) {
       // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
@@ -1271,7 +1273,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     drain(0);
     frac = intin ? 0.0 : 1.0;
   }
-  for (int t = ntiles; t < kSub / TN; ++t) out.ztile[g * (int64_t)kZTiles + (e0 + t * TN) / TN] = 0;
+  for (int e = ntiles * TN; e < kSub; e += kZT) out.ztile[g * (int64_t)kZTiles + (e0 + e) / kZT] = 0;
 
   // ---- lane starts: double-double wave scan of the lane totals (chunk-relative coordinates).
   DD ix = two_sum(lx, lxl), iy = two_sum(ly, lyl);
@@ -1330,12 +1332,21 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       double2 Pa = chunk_entry<T, W, D>(L, ckx, cky, al, ai, len, yc, wc);
       double2 Pb = chunk_entry<T, W, D>(L, ckx, cky, bl, bi, len, yc, wc);
       // a strict left turn of three stack entries: the fast turn of the chunk-relative hi parts
-      // (each within 259 u of Xc or Yc of its pair: start, lane lo, rounding) when it exceeds
-      // 2^-41 Xc Yc, else the turn of the pairs
-      const double Ec = ((W ? L.start[nl].x : (double)len) * 0x1p-41) * yc_abs;
+      // when it exceeds its error bound, else the turn of the pairs.  Each hi coordinate is within
+      // ex = 259 u Xc (ey = 259 u Yc) of its pair (the start's lo, the lane sum's lo, the
+      // rounding of the sum), so with (dx1, dy1) = P2 - P1, (dx2, dy2) = P3 - P2 the turn
+      // dx1 dy2 - dy1 dx2 of the pairs is within 4u'(|p1| + |p2|) + 2 ex (|dy1| + |dy2|)
+      // + 2 ey (|dx1| + |dx2|) + 8 ex ey of the computed one, each term taken 1 % larger.
+      const double ex2 = (W ? L.start[nl].x : (double)len) * (2.02 * 259.0 * kU);
+      const double ey2 = yc_abs * (2.02 * 259.0 * kU);
+      const double E00 = 2.0 * ex2 * ey2 + 0x1p-1000;
       auto wleft = [&](int l1, int i1, double2 P1, int l2, int i2, double2 P2, int l3, int i3, double2 P3) {
-        const double t = turn_pts(P1, P2, P3);
-        if (fabs(t) > Ec) return t > 0.0;
+        const double dx1 = P2.x - P1.x, dy1 = P2.y - P1.y, dx2 = P3.x - P2.x, dy2 = P3.y - P2.y;
+        const double p1 = dx1 * dy2, p2 = dy1 * dx2;
+        const double t = p1 - p2;
+        const double Ew = fma(4.04 * kU, fabs(p1) + fabs(p2),
+                              fma(ex2, fabs(dy1) + fabs(dy2), fma(ey2, fabs(dx1) + fabs(dx2), E00)));
+        if (fabs(t) > Ew) return t > 0.0;
         const int ls[3] = {l1, l2, l3}, is[3] = {i1, i2, i3};
         return entries_turn_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, ls, is, len, yc, wc) > 0.0;
       };

@@ -809,15 +809,13 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
       const int i0 = wd << 5;
       const int i1 = min(i0 + 32, len);
       if (i0 >= e.klo && i1 <= e.khi && sMask[wd] == 0xffffffffu && (sMask[wd + 1] & 1u)) {
-        bool written = true;
-        if (!zall)
-          for (int tt = i0 / TN; tt < (i1 + TN - 1) / TN; ++tt) written = written && ztile[g * kZTiles + tt];
-        if (written) {
-          if (bstart) {
-            for (int i = i0; i < i1; ++i) bstart[off + i] = 1;
-          }
-          continue;
+        // every element of the word is a block of its own, whose mean is its y (Corollary 4.5):
+        // z = y where the chunk pass has not written it yet
+        for (int i = i0; i < i1; ++i) {
+          if (!zall && !ztile[g * kZTiles + i / kZT]) z[off + i] = S.y[off + i];
+          if (bstart) bstart[off + i] = 1;
         }
+        continue;
       }
       // elements before klo and from khi on lie under the edges into and out of the chunk
       for (int i = i0; i < min(i1, e.klo); ++i) {
@@ -836,7 +834,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
       // where its tile is marked)
       auto close_edge = [&](int pend, int pa, const PD& Pa, int b, const PD& Pb) {
         if (b == pa + 1) {
-          if (!zall && !ztile[g * kZTiles + pa / TN]) z[off + pa] = S.y[off + pa];
+          if (!zall && !ztile[g * kZTiles + pa / kZT]) z[off + pa] = S.y[off + pa];
           return;
         }
         const T zv = (T)zval<D>(slope_dd(Pa, Pb));
