@@ -141,7 +141,9 @@ int iso_fit_noalloc(const void* y, const void* w, void* z, uint8_t* block_start,
  *                are not re-derived from z, since distinct means can round to equal values)
  *   gy           [batch, n] output (required)
  *   gw           [batch, n] output or NULL
- * Sums are taken in fp64 without atomics.  Returns ISO_OK, ISO_EINVAL or ISO_EHIP.
+ * Sums are taken in fp64 without atomics.  Rows of at most 2048 elements take one kernel launch
+ * and no workspace; longer rows take four launches and a stream-ordered workspace allocation.
+ * Returns ISO_OK, ISO_EINVAL, ISO_ENOMEM or ISO_EHIP.
  */
 int iso_vjp(const void* g, const void* y, const void* w, const void* z,
             const uint8_t* block_start, void* gy, void* gw, int64_t batch, int64_t n, int dtype,

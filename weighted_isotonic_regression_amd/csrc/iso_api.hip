@@ -722,6 +722,18 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
   if (batch * ntile > (int64_t)INT32_MAX) return ISO_EINVAL;
   const int64_t T = batch * ntile;
   hipStream_t s = (hipStream_t)stream;
+  if (ntile == 1) {
+    // rows of one tile: every block lies inside its tile, one launch and no workspace
+    if (dtype == ISO_F64)
+      hipLaunchKernelGGL((k_vjp_apply<double>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const double*)g,
+                         (const double*)y, (const double*)w, (const double*)z, block_start,
+                         (const double4*)nullptr, (double*)gy, (double*)gw, n, 1);
+    else
+      hipLaunchKernelGGL((k_vjp_apply<float>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const float*)g,
+                         (const float*)y, (const float*)w, (const float*)z, block_start,
+                         (const double4*)nullptr, (float*)gy, (float*)gw, n, 1);
+    return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
+  }
   const int64_t nblk = (ntile + kVjpBlock - 1) / kVjpBlock;
   const size_t tb = align_up((size_t)T * sizeof(VjpTile));
   const size_t cb = align_up((size_t)T * sizeof(double4));

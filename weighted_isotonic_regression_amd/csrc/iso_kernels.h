@@ -1031,13 +1031,16 @@ __device__ void vjp_wg_scans(Seg f, Seg r, const Seg& fseed, const Seg& bseed, S
   __syncthreads();
 }
 
-template <typename T>
+template <typename T, bool NT = false>
 __device__ __forceinline__ void vjp_load(const T* __restrict__ p, int64_t e0, int c, T (&v)[kVjpPer2],
                                          T fill) {
   constexpr int VN = Vec16<T>::N;
   if (c == kVjpPer2 && ((uintptr_t)(p + e0)) % 16 == 0) {
 #pragma unroll
-    for (int k = 0; k < kVjpPer2 / VN; ++k) load16(p + e0 + k * VN, &v[k * VN]);
+    for (int k = 0; k < kVjpPer2 / VN; ++k) {
+      if constexpr (NT) load16_nt(p + e0 + k * VN, &v[k * VN]);
+      else load16(p + e0 + k * VN, &v[k * VN]);
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < kVjpPer2; ++k) v[k] = k < c ? p[e0 + k] : fill;
@@ -1262,13 +1265,15 @@ __global__ __launch_bounds__(kVjpThreads, 4) void k_vjp_apply(const T* __restric
   const int i0 = kVjpPer2 * threadIdx.x;
   const int c = min(max(len - i0, 0), kVjpPer2);
   // every load is issued here, the tile's carries included, before any of them is waited for
-  const double4 me = cc[tid];
-  const double4 nx = tt == ntile - 1 ? make_double4(0.0, 0.0, 0.0, 0.0) : cc[tid + 1];
+  // (cc == nullptr: every row is one tile, so no block crosses a tile)
+  const double4 zero4 = make_double4(0.0, 0.0, 0.0, 0.0);
+  const double4 me = cc ? cc[tid] : zero4;
+  const double4 nx = (!cc || tt == ntile - 1) ? zero4 : cc[tid + 1];
   T gv[kVjpPer2], wv[kVjpPer2], yv[kVjpPer2], zv[kVjpPer2];
-  vjp_load(g, off + i0, c, gv, (T)0);
-  if (w) vjp_load(w, off + i0, c, wv, (T)0);
-  vjp_load(y, off + i0, c, yv, (T)0);
-  vjp_load(z, off + i0, c, zv, (T)0);
+  vjp_load<T, true>(g, off + i0, c, gv, (T)0);
+  if (w) vjp_load<T, true>(w, off + i0, c, wv, (T)0);
+  vjp_load<T, true>(y, off + i0, c, yv, (T)0);
+  vjp_load<T, true>(z, off + i0, c, zv, (T)0);
   int st[kVjpPer2 + 1];  // starts of this thread's elements and of the one after them
   if (kVjpPer2 == 8 && c == kVjpPer2 && ((uintptr_t)(bs + off + i0)) % 8 == 0) {
     const uint64_t b8 = *reinterpret_cast<const uint64_t*>(bs + off + i0);
@@ -1325,8 +1330,8 @@ __global__ __launch_bounds__(kVjpThreads, 4) void k_vjp_apply(const T* __restric
   if (vec) {
 #pragma unroll
     for (int k = 0; k < kVjpPer2 / VN; ++k) {
-      store16(gy + off + i0 + k * VN, &oy[k * VN]);
-      if (gw) store16(gw + off + i0 + k * VN, &ow[k * VN]);
+      store16_nt(gy + off + i0 + k * VN, &oy[k * VN]);
+      if (gw) store16_nt(gw + off + i0 + k * VN, &ow[k * VN]);
     }
   } else {
 #pragma unroll
