@@ -857,7 +857,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         }
         if (W) acc(lx, lxl, wd);
         const double p = wd * yd;
-        acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+        if constexpr (EX) acc(ly, lyl, p);
+        else acc_pe(ly, lyl, p, fma(wd, yd, -p));
         aabs += fabs(p);
         if (W) lomx = fmax(lomx, fabs(lxl));
         lomy = fmax(lomy, fabs(lyl));
@@ -893,7 +894,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
             const double yd = yval<D>(yv[k]);
             if (W) acc(lx, lxl, wd);
             const double p = wd * yd;
-            acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+            if constexpr (EX) acc(ly, lyl, p);
+            else acc_pe(ly, lyl, p, fma(wd, yd, -p));
             aabs += fabs(p);
             if (W) lomx = fmax(lomx, fabs(lxl));
             lomy = fmax(lomy, fabs(lyl));
@@ -1111,7 +1113,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       }
       if (W) acc(lx, lxl, wd);
       const double p = wd * yd;
-      acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+      if constexpr (EX) acc(ly, lyl, p);
+      else acc_pe(ly, lyl, p, fma(wd, yd, -p));
       aabs += fabs(p);
       if (W) lomx = fmax(lomx, fabs(lxl));
       lomy = fmax(lomy, fabs(lyl));
@@ -1147,7 +1150,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           const double yd = yval<D>(yv[k]);
           if (W) acc(lx, lxl, wd);
           const double p = wd * yd;
-          acc_pe(ly, lyl, p, EX ? 0.0 : fma(wd, yd, -p));
+          if constexpr (EX) acc(ly, lyl, p);
+          else acc_pe(ly, lyl, p, fma(wd, yd, -p));
           aabs += fabs(p);
           if (W) lomx = fmax(lomx, fabs(lxl));
           lomy = fmax(lomy, fabs(lyl));

@@ -119,14 +119,21 @@ ISO_HD void acc_pe(double& hi, double& lo, double v, double pe) {
   lo += e + pe;
   hi = s;
 }
-ISO_HD void acc(double& hi, double& lo, double v) { acc_pe(hi, lo, v, 0.0); }
+ISO_HD void acc(double& hi, double& lo, double v) {
+  const double s = hi + v;
+  const double bb = s - hi;
+  const double e = (hi - (s - bb)) + (v - bb);
+  lo += e;
+  hi = s;
+}
 
 // The increment w*y of one element.  For fp32 inputs and for unit weights the fp64 product is
 // exact; otherwise its rounding error is added to lo.
 template <bool EXACT>
 ISO_HD void acc_prod(double& hi, double& lo, double w, double y) {
   const double p = w * y;
-  acc_pe(hi, lo, p, EXACT ? 0.0 : fma(w, y, -p));
+  if constexpr (EXACT) acc(hi, lo, p);
+  else acc_pe(hi, lo, p, fma(w, y, -p));
 }
 template <typename T, bool W>
 struct ExactProd {
