@@ -3,14 +3,16 @@
 One step = one iso_fit_ex call (every stage of the fit) over the 1 x 10^8 fp32 mixed row
 (y_i = sin(8 pi i/n) + 2 i/n + N(0, 0.05^2), w ~ LogUniform[0.1, 10], seed 5), inputs resident
 in HBM.  Prints one JSON line: elements/s of the whole fit; the roofline of the dominant kernel
-(its algorithmic bytes per launch over its average launch time, timed with HIP events recorded
-on the launch stream inside the timed region) with the HBM traffic measured by rocprofv3
-counters when they were taken on the current kernel sources; the fit's whole-call fraction of
-the HBM roofline; rows/s on 65536 rows of 16 elements; the dense 1 x 10^8 fp64 nearly monotone
-row; and the CPU oracle timed on this host.
+(the fit's algorithmic bytes per element times the elements of one launch, over its average
+launch time, timed with HIP events recorded on the launch stream inside the timed region) with
+the HBM traffic measured by rocprofv3 counters when they were taken on the current kernel
+sources; the fit's whole-call fraction of the HBM roofline; the backward; rows/s on 65536 rows of
+16 elements; the 1 x 10^8 fp64 nearly monotone row (every chunk strictly increasing) and the same
+row with a few reversals per chunk (the dense hull through the general chunk pass); the soft
+rank; and the CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
-    python bench.py --only mixed|dense|short|vjp [--copy-calib] (one workload, for profilers)
+    python bench.py --only mixed|dense|hull|calib|short|mono7|ramp|table1|vjp|vjpshort|softrank [--copy-calib]
     python bench.py --configs   (every measured configuration: per-call median and IQR, oracle)
     python bench.py --summarize-pmc WORKLOAD FETCH_DIR WRITE_DIR  (updates profiles/traffic.txt)
 
@@ -329,9 +331,10 @@ def run_only(args, torch, B, W, dev):
     if args.only == "softrank":
         print(json.dumps({"workload": "softrank", **time_soft_rank(torch, B, dev)}), flush=True)
         return
-    if args.only == "vjp":
-        _, _, y, w = load_workload(torch, W, "mixed", dev)
-        print(json.dumps({"workload": "vjp", **time_vjp(torch, B, y, w, dev, args.steps)}), flush=True)
+    if args.only in ("vjp", "vjpshort"):
+        # the backward of the mixed 10^8 row, or of 65536 rows of 16 (rows of one tile)
+        _, _, y, w = load_workload(torch, W, "mixed" if args.only == "vjp" else "short", dev)
+        print(json.dumps({"workload": args.only, **time_vjp(torch, B, y, w, dev, args.steps)}), flush=True)
         return
     _, _, y, w = load_workload(torch, W, args.only, dev)
     print("bench: timing %s" % args.only, file=sys.stderr, flush=True)
@@ -395,7 +398,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the short-row and dense-row lines")
     ap.add_argument("--configs", action="store_true", help="measure every configuration, one JSON line each")
-    ap.add_argument("--only", choices=sorted(ONLY) + ["vjp", "softrank"], default=None,
+    ap.add_argument("--only", choices=sorted(ONLY) + ["vjp", "vjpshort", "softrank"], default=None,
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="with --only: first run a 1 GiB device copy (memory-counter calibration)")
