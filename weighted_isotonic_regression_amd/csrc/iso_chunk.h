@@ -62,7 +62,8 @@ struct ChunkOut {
   uint16_t* mcnt;     // [G * kMaskW] set bits before each word
   double* lsx;        // [2G * kWave] lane starts (chunk-relative pairs)
   double* lsy;
-  double* ckx;        // [2G * kWave * kLaneW] lane-relative running sums at points 32 j (pairs)
+  double* ckx;        // [2G * kLaneW * kWave] lane-relative running sums at points 32 j (pairs),
+                      //     [j * kWave + lane] within a chunk, so a wave's stores are contiguous
   double* cky;
   uint8_t* ztile;     // [G * kZTiles] 1 where the lane chains wrote z = y for the load tile
   uint8_t* dform;     // [G] 0 list form, 1 dense form, 2 dense form with every point a vertex
@@ -201,7 +202,7 @@ __device__ double2 lane_point(const double* ckx, const double* cky, int l, int q
                               const T* yl, const T* wl) {
   q = min(max(q, 0), c);
   const int j = min(q / kCk, kLaneW - 1);
-  double2 P{W ? ckx[l * kLaneW + j] : 0.0, cky[l * kLaneW + j]};
+  double2 P{W ? ckx[j * kWave + l] : 0.0, cky[j * kWave + l]};
   uint32_t f = 0u;
   for (int e = kCk * j; e < q; ++e) {
     double yd = yval<D>(yl[e]), wd = W ? (double)wl[e] : 1.0;
@@ -221,8 +222,8 @@ __device__ __forceinline__ PD lane_point_dd(const double* ckx, const double* cky
   constexpr bool EX = ExactProd<T, W>::value;
   q = min(max(q, 0), c);
   const int j = min(q / kCk, kLaneW - 1);
-  DD ax{0.0, 0.0}, ay{cky[l * kLaneW + j], ckyl[l * kLaneW + j]};
-  if (W) ax = DD{ckx[l * kLaneW + j], ckxl[l * kLaneW + j]};
+  DD ax{0.0, 0.0}, ay{cky[j * kWave + l], ckyl[j * kWave + l]};
+  if (W) ax = DD{ckx[j * kWave + l], ckxl[j * kWave + l]};
   uint32_t f = 0u;
   for (int e = kCk * j; e < q; ++e) {
     double yd = yval<D>(yl[e]), wd = W ? (double)wl[e] : 1.0;
@@ -477,15 +478,15 @@ __device__ bool increasing_chunk(const T* __restrict__ yc, const T* __restrict__
   // lane that holds it
   const int kv = len - 1, lv = kv / kSub, jv = (kv % kSub) / kCk;
   DD cx{0.0, 0.0}, cy{0.0, 0.0}, cvx{0.0, 0.0}, cvy{0.0, 0.0};
-  const int64_t cb = (g * kWave + lane) * (int64_t)kLaneW;
+  const int64_t cb = g * (int64_t)(kWave * kLaneW) + lane;
 #pragma unroll
   for (int jj = 0; jj < kLaneW; ++jj) {
     if (W) {
-      out.ckx[cb + jj] = cx.hi;
-      out.ckxl()[cb + jj] = cx.lo;
+      out.ckx[cb + jj * kWave] = cx.hi;
+      out.ckxl()[cb + jj * kWave] = cx.lo;
     }
-    out.cky[cb + jj] = cy.hi;
-    out.ckyl()[cb + jj] = cy.lo;
+    out.cky[cb + jj * kWave] = cy.hi;
+    out.ckyl()[cb + jj * kWave] = cy.lo;
     if (jj == jv) {
       cvx = cx;
       cvy = cy;
@@ -794,11 +795,11 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       const int eb = t * TN;  // lane-relative index of the tile's first element
       if ((eb & (kCk - 1)) == 0) {
         if (W) {
-          ckx[lane * kLaneW + eb / kCk] = lx;
-          ckxl[lane * kLaneW + eb / kCk] = lxl;
+          ckx[(eb / kCk) * kWave + lane] = lx;
+          ckxl[(eb / kCk) * kWave + lane] = lxl;
         }
-        cky[lane * kLaneW + eb / kCk] = ly;
-        ckyl[lane * kLaneW + eb / kCk] = lyl;
+        cky[(eb / kCk) * kWave + lane] = ly;
+        ckyl[(eb / kCk) * kWave + lane] = lyl;
       }
       if ((eb >> 5) != wi) {  // the tile's points 32 w .. are in mask word w (same for every lane)
         L.smask[wi][lane] = curw;
@@ -938,11 +939,11 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       // point of the lane has one)
       if ((c & (kCk - 1)) == 0 && c < kSub) {
         if (W) {
-          ckx[lane * kLaneW + c / kCk] = lx;
-          ckxl[lane * kLaneW + c / kCk] = lxl;
+          ckx[(c / kCk) * kWave + lane] = lx;
+          ckxl[(c / kCk) * kWave + lane] = lxl;
         }
-        cky[lane * kLaneW + c / kCk] = ly;
-        ckyl[lane * kLaneW + c / kCk] = lyl;
+        cky[(c / kCk) * kWave + lane] = ly;
+        ckyl[(c / kCk) * kWave + lane] = lyl;
       }
       if ((c >> 5) != wi) {
         L.smask[wi][lane] = curw;
@@ -1186,11 +1187,11 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       eb = t * TN;
       if ((eb & (kCk - 1)) == 0) {
         if (W) {
-          ckx[lane * kLaneW + eb / kCk] = lx;
-          ckxl[lane * kLaneW + eb / kCk] = lxl;
+          ckx[(eb / kCk) * kWave + lane] = lx;
+          ckxl[(eb / kCk) * kWave + lane] = lxl;
         }
-        cky[lane * kLaneW + eb / kCk] = ly;
-        ckyl[lane * kLaneW + eb / kCk] = lyl;
+        cky[(eb / kCk) * kWave + lane] = ly;
+        ckyl[(eb / kCk) * kWave + lane] = lyl;
       }
 #pragma unroll
       for (int k = 0; k < TN; ++k) {
@@ -1262,11 +1263,11 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       // point of the lane has one) joins the queue, and the queues are emptied
       if ((c & (kCk - 1)) == 0 && c < kSub) {
         if (W) {
-          ckx[lane * kLaneW + c / kCk] = lx;
-          ckxl[lane * kLaneW + c / kCk] = lxl;
+          ckx[(c / kCk) * kWave + lane] = lx;
+          ckxl[(c / kCk) * kWave + lane] = lxl;
         }
-        cky[lane * kLaneW + c / kCk] = ly;
-        ckyl[lane * kLaneW + c / kCk] = lyl;
+        cky[(c / kCk) * kWave + lane] = ly;
+        ckyl[(c / kCk) * kWave + lane] = lyl;
       }
       const int s = qt & (kQ - 1);
       if constexpr (W) L.qp[s][lane] = double2{lx, ly};

@@ -448,7 +448,7 @@ struct VertexStore {
     ay = DD{0.0, 0.0};
     if (q == 0) return;
     const int jj = q / kCk;
-    const int64_t cb = (g * kWave + l) * kLaneW + jj;
+    const int64_t cb = g * (int64_t)(kWave * kLaneW) + jj * kWave + l;
     if (W) ax = DD{ckx[cb], ckxl()[cb]};
     ay = DD{cky[cb], ckyl()[cb]};
     const int64_t e0 = row * n + (int64_t)j * kChunk + (int64_t)l * kSub;
