@@ -118,7 +118,7 @@ int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint
  *   Arguments as in iso_fit_ex, without ws and ws_bytes.  The stream's device must be the
  *   current device (its scratch is looked up once per device, on the first call there).
  *   A shape whose iso_workspace_bytes exceeds ISO_NOALLOC_SCRATCH_BYTES returns ISO_ESCRATCH
- *   before anything is launched (one row of up to about 1.35e8 elements fits, and so do 1024
+ *   before anything is launched (one row of up to about 1.43e8 elements fits, and so do 1024
  *   rows of 131072).
  *   Every call on a GPU shares that GPU's scratch: calls that may overlap in time (different
  *   streams, or different host threads) race and must not be issued; calls ordered on one

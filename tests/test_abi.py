@@ -117,10 +117,10 @@ def test_noalloc_argument_errors_before_any_launch(lib):
     assert na(Y, None, Z, None, None, 3, 0, 1, 2, None) == OK
     # more workspace than the fixed scratch holds: refused before the scratch is looked up
     cap = binding.ISO_NOALLOC_SCRATCH_BYTES
-    assert binding.iso_workspace_bytes(1, 135_000_000, 1, 0) <= cap
-    assert binding.iso_workspace_bytes(1, 140_000_000, 1, 0) > cap
+    assert binding.iso_workspace_bytes(1, 140_000_000, 1, 0) <= cap
+    assert binding.iso_workspace_bytes(1, 150_000_000, 1, 0) > cap
     assert binding.iso_workspace_bytes(1024, 131072, 0, 1) <= cap
-    assert na(Y, None, Z, None, None, 1, 140_000_000, 1, 0, None) == binding.ISO_ESCRATCH
+    assert na(Y, None, Z, None, None, 1, 150_000_000, 1, 0, None) == binding.ISO_ESCRATCH
     assert na(Y, W, Z, None, None, 4096, 131072, 0, 1, None) == binding.ISO_ESCRATCH
     assert "scratch" in binding.iso_strerror(binding.ISO_ESCRATCH)
 

@@ -99,10 +99,10 @@ def test_noalloc_without_optional_outputs_and_weight_check():
 
 @pytest.mark.gpu
 def test_noalloc_rejects_oversize_before_launching():
-    # one row of 1.4e8 elements needs more than the 256 MiB scratch; nothing is launched
+    # one row of 1.5e8 elements needs more than the 256 MiB scratch; nothing is launched
     y = torch.zeros(16, dtype=torch.float64, device="cuda")
     z = torch.empty_like(y)
-    n = 140_000_000
+    n = 150_000_000
     assert B.iso_workspace_bytes(1, n, B.ISO_F64, 0) > B.ISO_NOALLOC_SCRATCH_BYTES
     rc = B.iso_fit_noalloc(B._ptr(y), None, B._ptr(z), None, None, 1, n, B.ISO_F64, 0,
                            B._stream(torch, y.device))

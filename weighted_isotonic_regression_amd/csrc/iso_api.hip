@@ -91,7 +91,7 @@ Layout make_layout(int64_t batch, int64_t n) {
     L.o_lsy = take(2 * G * (size_t)kWave * sizeof(double));
     L.o_ckx = take(2 * G * (size_t)kWave * kLaneW * sizeof(double));
     L.o_cky = take(2 * G * (size_t)kWave * kLaneW * sizeof(double));
-    L.o_zt = take(G * (size_t)kZTiles);
+    L.o_zt = take(G * (size_t)kWave * sizeof(uint32_t));
     L.o_df = take(G);
     L.o_bnd = take(2 * G * sizeof(double4));
     L.o_bndk = take(G * sizeof(int2));
@@ -245,7 +245,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   co.lsy = (double*)(ws + Lay.o_lsy);
   co.ckx = (double*)(ws + Lay.o_ckx);
   co.cky = (double*)(ws + Lay.o_cky);
-  co.ztile = (uint8_t*)(ws + Lay.o_zt);
+  co.ztile = (uint32_t*)(ws + Lay.o_zt);
   co.dform = (uint8_t*)(ws + Lay.o_df);
   co.bnd = (double4*)(ws + Lay.o_bnd);
   co.bndk = (int2*)(ws + Lay.o_bndk);
@@ -311,7 +311,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   // chunks, so that rows of a few chunks still occupy the chip
   const int nsub = (int)std::max<int64_t>(1, std::min<int64_t>(kFitMaxSub, 2048 / std::max<int64_t>(G, 1)));
   hipLaunchKernelGGL((k_fit<T, W, D>), dim3((unsigned)(G * nsub)), dim3(kFitThreads), 0, s, S,
-                     (const EndInfo*)ends, (const uint32_t*)rflags, (const uint8_t*)co.ztile, z, bstart,
+                     (const EndInfo*)ends, (const uint32_t*)rflags, (const uint32_t*)co.ztile, z, bstart,
                      nsub);
   prof.mark(1);
   return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;

@@ -65,7 +65,8 @@ struct ChunkOut {
   double* ckx;        // [2G * kLaneW * kWave] lane-relative running sums at points 32 j (pairs),
                       //     [j * kWave + lane] within a chunk, so a wave's stores are contiguous
   double* cky;
-  uint8_t* ztile;     // [G * kZTiles] 1 where the lane chains wrote z = y for the load tile
+  uint32_t* ztile;    // [G * kWave] per lane: bit t set where the lane chain wrote z = y for its
+                      //     elements 8 t .. 8 t + 7
   uint8_t* dform;     // [G] 0 list form, 1 dense form, 2 dense form with every point a vertex
                       //     and z = y written for the whole chunk, 3 not yet processed
   double4* bnd;       // [2G] dense form: coordinates of hull vertices 1 and V - 2 (hi, then lo)
@@ -659,6 +660,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   double yprev = 0.0;
   double marg = INFINITY;  // smallest |t| - (error bound of t) of the turns taken
   double frac = 0.0;       // 0 while every coordinate so far is an integer
+  uint32_t ztb = 0u;       // z-tile marks of the lane's elements
   const int ntiles = (c + TN - 1) / TN;
   if constexpr (EXACT) {
     int ti = 0, ui = 0, vi = 0, ts = 0, us = 0, vs = 0;
@@ -932,7 +934,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         zt = 1;
       }
 #pragma unroll
-      for (int h = 0; h < TN / kZT; ++h) out.ztile[g * (int64_t)kZTiles + (e0 + eb) / kZT + h] = zt;
+      for (int h = 0; h < TN / kZT; ++h) ztb |= (uint32_t)zt << (eb / kZT + h);
     }
     if (c > 0) {
       // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
@@ -1256,7 +1258,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         }
       }
 #pragma unroll
-      for (int h = 0; h < TN / kZT; ++h) out.ztile[g * (int64_t)kZTiles + (e0 + eb) / kZT + h] = zt;
+      for (int h = 0; h < TN / kZT; ++h) ztb |= (uint32_t)zt << (eb / kZT + h);
     }
     if (c > 0) {
       // the lane's end point (and its checkpoint when it starts a checkpoint block, so that every
@@ -1278,7 +1280,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     drain(0);
     frac = intin ? 0.0 : 1.0;
   }
-  for (int e = ntiles * TN; e < kSub; e += kZT) out.ztile[g * (int64_t)kZTiles + (e0 + e) / kZT] = 0;
+  out.ztile[g * (int64_t)kWave + lane] = ztb;
 
   // ---- lane starts: double-double wave scan of the lane totals (chunk-relative coordinates).
   DD ix = two_sum(lx, lxl), iy = two_sum(ly, lyl);

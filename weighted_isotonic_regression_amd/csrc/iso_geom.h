@@ -41,8 +41,7 @@ constexpr int kLaneW = kSub / kCk;           // mask words (and checkpoints) per
 constexpr int kSubW = kLaneW + 1;            // mask words of a lane's points 0..256
 constexpr int kListCap = 256;                // chunks with at most this many hull vertices keep a list
 constexpr int kMaskW = kChunk / 32 + 1;      // mask words of a chunk (points 0..16384)
-constexpr int kZT = 8;                       // elements per z-tile mark of the chunk pass
-constexpr int kZTiles = kChunk / kZT;        // z-tile marks of a chunk
+constexpr int kZT = 8;                       // elements per z-tile mark of the chunk pass (32 per lane)
 constexpr int kVjpTile = kWave * 32;         // elements per backward tile (256 threads, 8 each)
 
 // Per-row input flags (same values as ISO_ROW_NONFINITE / ISO_ROW_BAD_WEIGHT of iso.h).

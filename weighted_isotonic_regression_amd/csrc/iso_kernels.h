@@ -732,11 +732,16 @@ __global__ __launch_bounds__(256) void k_ends(VertexStore<T, W, D> S, EndInfo* _
 constexpr int kFitThreads = 256;
 constexpr int kFitMaxSub = 4;  // workgroups per chunk at most
 
+// Whether the chunk pass wrote z = y for element i (chunk-relative) of chunk g.
+__device__ __forceinline__ bool ztile_set(const uint32_t* __restrict__ zt, int64_t g, int i) {
+  return ((zt[g * kWave + i / kSub] >> ((i % kSub) / kZT)) & 1u) != 0u;
+}
+
 template <typename T, bool W, bool D>
 __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
                                                      const EndInfo* __restrict__ ends,
                                                      const uint32_t* __restrict__ rflags,
-                                                     const uint8_t* __restrict__ ztile,
+                                                     const uint32_t* __restrict__ ztile,
                                                      T* __restrict__ z, uint8_t* __restrict__ bstart,
                                                      int nsub) {
   __shared__ double sSlope[kListCap];
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
         // every element of the word is a block of its own, whose mean is its y (Corollary 4.5):
         // z = y where the chunk pass has not written it yet
         for (int i = i0; i < i1; ++i) {
-          if (!zall && !ztile[g * kZTiles + i / kZT]) z[off + i] = S.y[off + i];
+          if (!zall && !ztile_set(ztile, g, i)) z[off + i] = S.y[off + i];
           if (bstart) bstart[off + i] = 1;
         }
         continue;
@@ -834,7 +839,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
       // where its tile is marked)
       auto close_edge = [&](int pend, int pa, const PD& Pa, int b, const PD& Pb) {
         if (b == pa + 1) {
-          if (!zall && !ztile[g * kZTiles + pa / kZT]) z[off + pa] = S.y[off + pa];
+          if (!zall && !ztile_set(ztile, g, pa)) z[off + pa] = S.y[off + pa];
           return;
         }
         const T zv = (T)zval<D>(slope_dd(Pa, Pb));
