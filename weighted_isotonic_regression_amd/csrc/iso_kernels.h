@@ -810,18 +810,34 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     // next one are all vertices, in tiles whose z the chunk pass wrote, needs nothing
     auto bit = [&](int i) { return ((sMask[i >> 5] >> (i & 31)) & 1u) != 0u; };
     const int nw = (len + 31) >> 5;
+    // a word inside [klo, khi) whose points and the next one are all vertices holds blocks of
+    // one element each, whose means are their y (Corollary 4.5): z = y where the chunk pass has
+    // not written it yet, copied by all threads together in 16-byte groups (a group lies inside
+    // one word and one z-tile mark)
+    auto one_blocks = [&](int wd) {
+      const int i0 = wd << 5, i1 = min(i0 + 32, len);
+      return i0 >= e.klo && i1 <= e.khi && sMask[wd] == 0xffffffffu && (sMask[wd + 1] & 1u);
+    };
+    const bool yvec = zvec && ((uintptr_t)(S.y + off)) % 16 == 0;
+    for (int i0 = t0 * VN; i0 < len; i0 += tstride * VN) {
+      if (!one_blocks(i0 >> 5)) continue;
+      const int n1 = min(VN, len - i0);
+      if (bstart) {
+        for (int u = 0; u < n1; ++u) bstart[off + i0 + u] = 1;
+      }
+      if (zall || ztile_set(ztile, g, i0)) continue;
+      if (yvec && n1 == VN) {
+        T v[VN];
+        load16(S.y + off + i0, v);
+        store16(z + off + i0, v);
+      } else {
+        for (int u = 0; u < n1; ++u) z[off + i0 + u] = S.y[off + i0 + u];
+      }
+    }
     for (int wd = t0; wd < nw; wd += tstride) {
       const int i0 = wd << 5;
       const int i1 = min(i0 + 32, len);
-      if (i0 >= e.klo && i1 <= e.khi && sMask[wd] == 0xffffffffu && (sMask[wd + 1] & 1u)) {
-        // every element of the word is a block of its own, whose mean is its y (Corollary 4.5):
-        // z = y where the chunk pass has not written it yet
-        for (int i = i0; i < i1; ++i) {
-          if (!zall && !ztile_set(ztile, g, i)) z[off + i] = S.y[off + i];
-          if (bstart) bstart[off + i] = 1;
-        }
-        continue;
-      }
+      if (one_blocks(wd)) continue;
       // elements before klo and from khi on lie under the edges into and out of the chunk
       for (int i = i0; i < min(i1, e.klo); ++i) {
         z[off + i] = zin;
