@@ -723,15 +723,19 @@ int iso_vjp(const void* g, const void* y, const void* w, const void* z,
   const int64_t T = batch * ntile;
   hipStream_t s = (hipStream_t)stream;
   if (ntile == 1) {
-    // rows of one tile: every block lies inside its tile, one launch and no workspace
+    // rows of at most one tile: whole rows packed kVjpTile / n to a tile, so no block crosses a
+    // tile; one launch and no workspace
+    const int rpt = (int)(kVjpTile / n);
+    const int64_t nt = (batch + rpt - 1) / rpt;
+    if (nt > (int64_t)INT32_MAX) return ISO_EINVAL;
     if (dtype == ISO_F64)
-      hipLaunchKernelGGL((k_vjp_apply<double>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const double*)g,
+      hipLaunchKernelGGL((k_vjp_apply<double, true>), dim3((unsigned)nt), dim3(kVjpThreads), 0, s, (const double*)g,
                          (const double*)y, (const double*)w, (const double*)z, block_start,
-                         (const double4*)nullptr, (double*)gy, (double*)gw, n, 1);
+                         (const double4*)nullptr, (double*)gy, (double*)gw, n, 1, batch, rpt);
     else
-      hipLaunchKernelGGL((k_vjp_apply<float>), dim3((unsigned)T), dim3(kVjpThreads), 0, s, (const float*)g,
+      hipLaunchKernelGGL((k_vjp_apply<float, true>), dim3((unsigned)nt), dim3(kVjpThreads), 0, s, (const float*)g,
                          (const float*)y, (const float*)w, (const float*)z, block_start,
-                         (const double4*)nullptr, (float*)gy, (float*)gw, n, 1);
+                         (const double4*)nullptr, (float*)gy, (float*)gw, n, 1, batch, rpt);
     return hipGetLastError() == hipSuccess ? ISO_OK : ISO_EHIP;
   }
   const int64_t nblk = (ntile + kVjpBlock - 1) / kVjpBlock;

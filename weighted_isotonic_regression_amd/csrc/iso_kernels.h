@@ -1270,26 +1270,38 @@ __global__ __launch_bounds__(kVjpScanThreads) void k_vjp_scan_apply(const VjpTil
 }
 
 // Pass 3: each element's block sums from the two scans, seeded with its tile's carries.
-template <typename T>
+// PACKED (rows of at most kVjpTile elements): a tile holds `rpt` whole rows, so no block crosses a
+// tile and there are no carries; every row's first element starts a block whatever its flag says.
+template <typename T, bool PACKED = false>
 __global__ __launch_bounds__(kVjpThreads, 4) void k_vjp_apply(const T* __restrict__ g, const T* __restrict__ y,
                                                            const T* __restrict__ w, const T* __restrict__ z,
                                                            const uint8_t* __restrict__ bs,
                                                            const double4* __restrict__ cc, T* __restrict__ gy,
-                                                           T* __restrict__ gw, int64_t n, int ntile) {
+                                                           T* __restrict__ gw, int64_t n, int ntile,
+                                                           int64_t batch = 1, int rpt = 1) {
   __shared__ Seg sh[2 * kVjpThreads / kWave];
   const int64_t tid = blockIdx.x;
-  const int64_t row = tid / ntile;
-  const int tt = (int)(tid - row * ntile);
-  const int64_t off = row * n + (int64_t)tt * kVjpTile;
-  const int64_t rem = n - (int64_t)tt * kVjpTile;
-  const int len = rem < kVjpTile ? (int)rem : kVjpTile;
+  int64_t off;
+  int len;
+  int tt = 0;
+  if constexpr (PACKED) {
+    const int64_t r0 = tid * rpt;
+    const int64_t nr = min((int64_t)rpt, batch - r0);
+    off = r0 * n;
+    len = (int)(nr * n);
+  } else {
+    const int64_t row = tid / ntile;
+    tt = (int)(tid - row * ntile);
+    off = row * n + (int64_t)tt * kVjpTile;
+    const int64_t rem = n - (int64_t)tt * kVjpTile;
+    len = rem < kVjpTile ? (int)rem : kVjpTile;
+  }
   const int i0 = kVjpPer2 * threadIdx.x;
   const int c = min(max(len - i0, 0), kVjpPer2);
   // every load is issued here, the tile's carries included, before any of them is waited for
-  // (cc == nullptr: every row is one tile, so no block crosses a tile)
   const double4 zero4 = make_double4(0.0, 0.0, 0.0, 0.0);
-  const double4 me = cc ? cc[tid] : zero4;
-  const double4 nx = (!cc || tt == ntile - 1) ? zero4 : cc[tid + 1];
+  const double4 me = PACKED ? zero4 : cc[tid];
+  const double4 nx = (PACKED || tt == ntile - 1) ? zero4 : cc[tid + 1];
   T gv[kVjpPer2], wv[kVjpPer2], yv[kVjpPer2], zv[kVjpPer2];
   vjp_load<T, true>(g, off + i0, c, gv, (T)0);
   if (w) vjp_load<T, true>(w, off + i0, c, wv, (T)0);
@@ -1304,6 +1316,15 @@ __global__ __launch_bounds__(kVjpThreads, 4) void k_vjp_apply(const T* __restric
   } else {
 #pragma unroll
     for (int k = 0; k <= kVjpPer2; ++k) st[k] = (k < c || (k == c && i0 + k < len)) ? (bs[off + i0 + k] ? 1 : 0) : 0;
+  }
+  if constexpr (PACKED) {
+    // row starts (the tile starts at a row start)
+    int rk = (i0 < len) ? (int)((int64_t)i0 % n) : 0;
+#pragma unroll
+    for (int k = 0; k <= kVjpPer2; ++k) {
+      if (rk == 0 && (k < c || (k == c && i0 + k < len))) st[k] = 1;
+      if (++rk == n) rk = 0;
+    }
   }
   // forward fold (restart at starts) and backward fold (restart after block ends: the flag of
   // element k is the start of element k + 1)
