@@ -980,6 +980,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     // turn of the pairs is within 4u' (|p1| + |p2|) + 2 LX (|dy1| + |dy2|) + 2 LY (|dx1| + |dx2|)
     // + 8 LX LY of t, to first order; each term is taken 1 % larger for the neglected ones.
     double cLX = 0.0, cLY = 0.0, E0 = 0x1p-1000;
+    bool dexact = false;  // every sum exact so far, but not the integer case below 2^25
     // After a pop, V's ring entry is read into (rvx, rvy, rtg) and taken into V only when the next
     // pop needs it (vpend), so the read overlaps a whole step.  An entry whose tag shows it was
     // overwritten is recomputed: the highest stack bit below ui, from its checkpoint and the
@@ -1014,8 +1015,25 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       const double E = fma(4.04 * kU, fabs(p1) + fabs(p2),
                            fma(cLY, fabs(dx1) + fabs(dx2), fma(cLX, fabs(dy1) + fabs(dy2), E0)));
       const bool tst = act && d >= 2;
-      marg = sel(tst, fmin(marg, fabs(t) - E), marg);
-      const bool push = act && (d < 2 || t > 0.0);
+      // While no running sum of the lane has rounded (every lo part so far is zero: LX = LY = 0)
+      // the hi parts are the coordinates, and a turn inside its bound is decided here, in
+      // double-double arithmetic on them, as the exact pass would (ties and collinear runs of
+      // values that sum exactly, e.g. fp32 values of one binade in an fp64 row without weights,
+      // which the soft rank's problems are).  Integer inputs below 2^25 need none of it: there
+      // the fast turn is exact.  Only unweighted fp64 rows carry this code.
+      bool und = false;
+      double td = t;
+      if constexpr (!W && sizeof(T) == 8) {  // (the soft rank's problems are of this kind)
+        und = dexact && tst && !(fabs(t) > E);
+        if (__any(und)) {
+          if (und) {
+            td = turn_dd(PD{DD{ux, 0.0}, DD{uy, 0.0}}, PD{DD{tx, 0.0}, DD{ty, 0.0}},
+                         PD{DD{kx, 0.0}, DD{ky, 0.0}}).hi;
+          }
+        }
+      }
+      marg = sel(tst && !und, fmin(marg, fabs(t) - E), marg);
+      const bool push = act && (d < 2 || td > 0.0);
       const bool pop = act && !push;
       // V becomes U on a pop: take the entry read after the previous pop
       const bool take = pop && vpend;
@@ -1088,6 +1106,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       cLX = 2.02 * lomx;
       cLY = 2.02 * lomy;
       E0 = 8.08 * lomx * lomy + 0x1p-1000;
+      dexact = lomx == 0.0 && lomy == 0.0 && !(intin && (W ? lx : 0.0) < 0x1p25 && aabs < 0x1p25);
       {
         const QE e = read_q(qh), e2 = read_q(qh + 1);
         kx = e.x;
