@@ -132,7 +132,7 @@ struct RingCoord<false> {
 // while some lane is above that.  A lane with few pops thus runs ahead of the others instead of
 // waiting at every element for the lane with the most.
 constexpr int kQ = 4;
-constexpr int kQStep = 2;
+constexpr int kQStep = 1;
 
 // LDS of one wavefront.  The queue is used only during the chains and the lane results only
 // after them, so they share their space.
@@ -1103,6 +1103,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     };
     // chain steps until no lane holds more than `keep` queued points
     auto drain = [&](const int keep) __attribute__((always_inline)) {
+      if (!__any(qt - qh > keep)) return;
       cLX = 2.02 * lomx;
       cLY = 2.02 * lomy;
       E0 = 8.08 * lomx * lomy + 0x1p-1000;
@@ -1116,17 +1117,47 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         ny_ = e2.y;
         nq = e2.q;
       }
-      while (__any(qt - qh > keep)) step();
+      do {
+        step();
+      } while (__any(qt - qh > keep));
     };
     // element k of the tile: its left point joins the queue when it is a candidate, then the
     // element joins the running sums
     T yv[TN], wv[TN];
-    int eb = 0;
+    T ny[TN], nw[TN];  // the next tile's inputs (loaded while the current one is processed)
+    int eb = 0, kn = 0;  // the tile's first element and its element count
+    double ypp = 0.0, wpp = 1.0, wprev = 1.0;  // elements q - 2 and q - 1 (y_{q-1} is yprev)
     auto produce = [&](const int k) __attribute__((always_inline)) {
       const double yd = yval<D>(yv[k]);
       const double wd = W ? (double)wv[k] : 1.0;
       const int q = eb + k;
-      if (q > 0 && yprev < yd) {
+      // Point P_q with y_{q-1} < y_q is also not a vertex when it is not a strict vertex of
+      // (P_{q-2}, P_q, P_{q+1}) or of (P_{q-1}, P_q, P_{q+2}), i.e. when the weighted mean of
+      // elements q - 2 and q - 1 is at least y_q, or that of elements q and q + 1 at most y_{q-1}.
+      // In terms of the inputs, with dq = y_q - y_{q-1} > 0: w_{q-2} (y_{q-2} - y_q) >= w_{q-1} dq,
+      // or w_{q+1} (y_{q-1} - y_{q+1}) >= w_q dq.  Each side is a difference and a product, so
+      // its computed value is within a factor (1 +- u)^2 of the exact one, and a side that exceeds
+      // the other one taken 2^-50 larger (plus 2^-960 against underflow) exceeds it exactly; such
+      // a point is left out of the queue (any hull that holds it and those neighbours has it
+      // above a chord), which does not change the lane's hull.
+      bool cand = q > 0 && yprev < yd;
+      {
+        const bool hasn = k + 1 < TN ? (k + 1 < kn) : (eb + TN < c);
+        const double yn = yval<D>(k + 1 < TN ? yv[k + 1 < TN ? k + 1 : 0] : ny[0]);
+        const double wn = W ? (double)(k + 1 < TN ? wv[k + 1 < TN ? k + 1 : 0] : nw[0]) : 1.0;
+        const double dq = yd - yprev;
+        const double tl = fma(W ? wprev * dq : dq, 0x1.0000000000004p0, 0x1p-960);
+        const double tr = fma(W ? wd * dq : dq, 0x1.0000000000004p0, 0x1p-960);
+        const double al = W ? wpp * (ypp - yd) : ypp - yd;
+        const double ar = W ? wn * (yprev - yn) : yprev - yn;
+        const bool xl = q >= 2 && al >= tl && tl < INFINITY;
+        const bool xr = hasn && ar >= tr && tr < INFINITY;
+        cand = cand && !xl && !xr;
+      }
+      ypp = yprev;
+      wpp = wprev;
+      wprev = wd;
+      if (cand) {
         const int s = qt & (kQ - 1);
         if constexpr (W) L.qp[s][lane] = double2{lx, ly};
         else L.qp[s][lane] = ly;
@@ -1182,12 +1213,13 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       }
       vpend = false;
       yprev = yval<D>(yv[TN - 1]);
+      ypp = yval<D>(yv[TN - 2]);
+      wprev = W ? (double)wv[TN - 1] : 1.0;
+      wpp = W ? (double)wv[TN - 2] : 1.0;
       const int b0 = (eb & 31) + kp, b1 = (eb & 31) + TN - 1;  // bits of points eb+kp .. eb+TN-1
       atomicOr(&L.smask[eb >> 5][lane],
                (b1 >= 31 ? 0xffffffffu : ((2u << b1) - 1u)) & ~((1u << b0) - 1u));
     };
-    // the next tile's inputs are loaded while the current one is processed
-    T ny[TN], nw[TN];
     auto load_tile = [&](int e) __attribute__((always_inline)) {
       if (vec && e + TN <= c) {
 #pragma unroll
@@ -1220,7 +1252,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         wv[k] = W ? nw[k] : (T)1;
       }
       if (t + 1 < ntiles) load_tile(eb + TN);
-      const int kn = min(TN, c - eb);
+      kn = min(TN, c - eb);
       // tile checks, as in the exact pass
       bool clean = kn == TN, incr = true;
       {
