@@ -658,7 +658,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   double aabs = 0.0;             // sum of |w y| so far: bounds every |y| of the lane's points
   double lomx = 0.0, lomy = 0.0; // largest |lo| of the running sums so far
   double yprev = 0.0;
-  double marg = INFINITY;  // smallest |t| - (error bound of t) of the turns taken
+  bool undec = false;      // a turn of the first pass fell inside its error bound
   double frac = 0.0;       // 0 while every coordinate so far is an integer
   uint32_t ztb = 0u;       // z-tile marks of the lane's elements
   const int ntiles = (c + TN - 1) / TN;
@@ -1032,59 +1032,72 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           }
         }
       }
-      marg = sel(tst && !und, fmin(marg, fabs(t) - E), marg);
+      undec = undec || (tst && !und && !(fabs(t) > E));
       const bool push = act && (d < 2 || td > 0.0);
       const bool pop = act && !push;
-      // V becomes U on a pop: take the entry read after the previous pop
-      const bool take = pop && vpend;
-      vx = sel(take, W ? rvx : (double)tag_q(rtg), vx);
-      vy = sel(take, rvy, vy);
-      vi = sel(take, tag_q(rtg), vi);
-      if (__any(take && d >= 3 && !tag_is(rtg, d - 3))) {
-        if (take && d >= 3 && !tag_is(rtg, d - 3)) {
+      // the stack mask: a push sets K's bit, a pop clears T's
+      if (act) {
+        const int mi = push ? kq : ti;
+        atomicXor(&L.smask[mi >> 5][lane], 1u << (mi & 31));
+      }
+      // A pop makes V the new U: V is the entry read after the previous pop when that read is
+      // pending (vpend), and an entry whose tag shows it was overwritten is recomputed first.
+      const bool stale = pop && vpend && d >= 3 && !tag_is(rtg, d - 3);
+      if (__any(stale)) {
+        if (stale) {
           int ww = ui >> 5;
           uint32_t mw = L.smask[ww][lane] & ((1u << (ui & 31)) - 1u);
           while (mw == 0u) {
             --ww;
             mw = L.smask[ww][lane];
           }
-          vi = kCk * ww + 31 - __builtin_clz(mw);
-          const double2 P = lane_point<T, W, D>(ckx, cky, lane, vi, c, yl, wl);
-          vx = P.x;
-          vy = P.y;
+          const int q = kCk * ww + 31 - __builtin_clz(mw);
+          const double2 P = lane_point<T, W, D>(ckx, cky, lane, q, c, yl, wl);
+          rvx = P.x;
+          rvy = P.y;
+          rtg = ring_tag(q, d - 3);
           __builtin_amdgcn_s_waitcnt(0);
         }
       }
-      const int ks = ring_next(ts);
       if (push) {
+        const int ks = ring_next(ts);
         ring_put<W>(L, ks, lane, kx, ky, ring_tag(kq, d));
-        atomicOr(&L.smask[kq >> 5][lane], 1u << (kq & 31));
+        vx = ux;
+        vy = uy;
+        vi = ui;
+        vs = us;
+        ux = tx;
+        uy = ty;
+        ui = ti;
+        us = ts;
+        tx = kx;
+        ty = ky;
+        ti = kq;
+        ts = ks;
+        ++d;
+        ++qh;
+        vpend = false;
+        kx = nx;
+        ky = ny_;
+        kq = nq;
+      } else if (pop) {
+        if (vpend) {
+          vi = tag_q(rtg);
+          vx = W ? rvx : (double)vi;
+          vy = rvy;
+        }
+        tx = ux;
+        ty = uy;
+        ti = ui;
+        ts = us;
+        ux = vx;
+        uy = vy;
+        ui = vi;
+        us = vs;
+        --d;
+        vs = max(ring_prev(us, d - 2), 0);
+        vpend = true;
       }
-      if (pop) atomicAnd(&L.smask[ti >> 5][lane], ~(1u << (ti & 31)));
-      // push: (V, U, T) <- (U, T, K); pop: (U, T) <- (V, U), V read below
-      const double ntx = sel(push, kx, sel(pop, ux, tx)), nty = sel(push, ky, sel(pop, uy, ty));
-      const int nti = sel(push, kq, sel(pop, ui, ti)), nts = sel(push, ks, sel(pop, us, ts));
-      const double nux = sel(push, tx, sel(pop, vx, ux)), nuy = sel(push, ty, sel(pop, vy, uy));
-      const int nui = sel(push, ti, sel(pop, vi, ui)), nus = sel(push, ts, sel(pop, vs, us));
-      vx = sel(push, ux, vx);
-      vy = sel(push, uy, vy);
-      vi = sel(push, ui, vi);
-      vs = sel(push, us, vs);
-      tx = ntx;
-      ty = nty;
-      ti = nti;
-      ts = nts;
-      ux = nux;
-      uy = nuy;
-      ui = nui;
-      us = nus;
-      d += push ? 1 : pop ? -1 : 0;
-      vs = sel(pop, max(ring_prev(us, d - 2), 0), vs);
-      vpend = pop || (!push && vpend);
-      qh += push ? 1 : 0;
-      kx = sel(push, nx, kx);
-      ky = sel(push, ny_, ky);
-      kq = sel(push, nq, kq);
       // the reads for the next steps: the entry after the head, and V's ring slot
       {
         const QE e = read_q(qh + 1);
@@ -1487,7 +1500,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   const bool listable = total <= kListCap;
   // a chunk with an undecided turn keeps form byte 3 and is processed again by the exact pass
   const bool ilane = frac == 0.0 && (W ? lx : (double)c) < 0x1p25 && aabs < 0x1p25;
-  const bool leave = !EXACT && __any(!(marg > 0.0) && !ilane);
+  const bool leave = !EXACT && __any(undec && !ilane);
   if (lane == 0) {
     out.nverts[g] = total;
     out.desc[g] = make_int4(j, 0, total - 1, desc_w(listable ? 0 : 1, total));
