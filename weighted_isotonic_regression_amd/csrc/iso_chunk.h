@@ -134,6 +134,10 @@ struct RingCoord<false> {
 constexpr int kQ = 4;
 constexpr int kQStep = 1;
 
+// Merge rounds from this one on (groups of 2^r lanes) first walk in a register window.
+constexpr int kWinRound = 3;
+constexpr int kWinDepth = 32;
+
 // LDS of one wavefront.  The queue is used only during the chains and the lane results only
 // after them, so they share their space.
 template <bool W>
@@ -147,6 +151,7 @@ struct ChunkLds {
       int lo[kWave], hi[kWave];      // surviving depth range of the lane's stack
       double2 start[kWave + 1];      // lane starts, chunk-relative (hi); [l + 1] is lane l's end point
       double2 startl[kWave + 1];     // (lo)
+      uint32_t wa[kWave], wb[kWave]; // merge-round windows: (lane << 16 | depth) of the vertices next to s
     };
     struct {
       typename RingCoord<W>::type qp[kQ][kWave];  // queued points, lane-relative (y only without w)
@@ -1386,6 +1391,26 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   // ---- a4: merge rounds.  Node A = lanes [g0, sB), node B = lanes [sB, g0 + size); their
   // shared point s is lane sB - 1's end point.  A's vertices: (g0, 0), then each lane's range;
   // B's: each lane's range, ending at lane lb's end point.
+  //
+  // A strict left turn of three stack entries: the fast turn of the chunk-relative hi parts when
+  // it exceeds its error bound, else the turn of the pairs.  Each hi coordinate is within
+  // ex = 259 u Xc (ey = 259 u Yc) of its pair (the start's lo, the lane sum's lo, the rounding of
+  // the sum), so with (dx1, dy1) = P2 - P1, (dx2, dy2) = P3 - P2 the turn dx1 dy2 - dy1 dx2 of
+  // the pairs is within 4u'(|p1| + |p2|) + 2 ex (|dy1| + |dy2|) + 2 ey (|dx1| + |dx2|) + 8 ex ey
+  // of the computed one, each term taken 1 % larger.
+  const double ex2 = (W ? L.start[nl].x : (double)len) * (2.02 * 259.0 * kU);
+  const double ey2 = yc_abs * (2.02 * 259.0 * kU);
+  const double E00 = 2.0 * ex2 * ey2 + 0x1p-1000;
+  auto wleft = [&](int l1, int i1, double2 P1, int l2, int i2, double2 P2, int l3, int i3, double2 P3) {
+    const double dx1 = P2.x - P1.x, dy1 = P2.y - P1.y, dx2 = P3.x - P2.x, dy2 = P3.y - P2.y;
+    const double p1 = dx1 * dy2, p2 = dy1 * dx2;
+    const double t = p1 - p2;
+    const double Ew = fma(4.04 * kU, fabs(p1) + fabs(p2),
+                          fma(ex2, fabs(dy1) + fabs(dy2), fma(ey2, fabs(dx1) + fabs(dx2), E00)));
+    if (fabs(t) > Ew) return t > 0.0;
+    const int ls[3] = {l1, l2, l3}, is[3] = {i1, i2, i3};
+    return entries_turn_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, ls, is, len, yc, wc) > 0.0;
+  };
 #pragma unroll 1
   for (int r = 1; r <= 6; ++r) {
     const int gsz = 1 << r, half = gsz >> 1;
@@ -1393,34 +1418,158 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
     const int sB = g0 + half;
     const bool merge = sB < nl;
     const uint64_t nzr = __ballot(lo <= hi);  // lanes with a non-empty range
+    const int lb = min(g0 + gsz, nl) - 1;       // B's last lane
     int al = 0, ai = 0, bl = 0, bi = 0;
-    if (merge && lane == sB) {
-      const int lb = min(g0 + gsz, nl) - 1;
-      al = sB - 1;
-      ai = L.depth[al] - 1;                        // alpha = s
-      bl = min(__builtin_ctzll(nzr & ~lanes_below(sB)), lb);  // beta = B's first vertex
-      bi = L.lo[bl];
+    bool settled = false, from_win = false;
+    if (r >= kWinRound) {
+      // Only groups whose lanes' stacks are shallow (depth <= kWinDepth, as on noisy rows) walk
+      // in a window: their entries are mostly still in the ring, where the deep stacks of dense
+      // hulls (whose joints are usually convex at once) would have many window entries
+      // recomputed from their checkpoints.
+      const uint64_t gmk = gsz == kWave ? ~0ull : (((1ull << gsz) - 1ull) << g0);
+      settled = !merge || (__ballot(d > kWinDepth) & gmk) != 0;
+    }
+    const bool serial = merge && (r < kWinRound || settled);
+    if (r >= kWinRound && __any(merge && !settled)) {
+      // The group's lanes gather the vertices next to s into registers: lane k of the group
+      // takes a_{k+1}, the (k+1)-th vertex of A left of s, and b_{k+1}, the (k+1)-th of B right
+      // of it (gsz - 1 of each at most), and both walks run there, a ballot for each move.  The
+      // positions are those of the serial walk below, which continues from them when a walk
+      // leaves its window.
+      const int k = lane - g0;
+      const uint64_t gm = gsz == kWave ? ~0ull : ((1ull << gsz) - 1ull);
+      const bool inA = merge && lane < sB, inB = merge && lane >= sB && lane <= lb;
+      const bool ne = lo <= hi;
+      const int topA = lane == sB - 1 ? min(hi, d - 2) : hi;  // (s itself is a_0)
+      const int cA = (inA && ne) ? max(topA - lo + 1, 0) : 0;
+      const int cB = (inB && ne) ? hi - lo + 1 : 0;
+      int incl = cA + cB;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+      }
+      const int atS = __shfl(incl, sB - 1 < kWave ? sB - 1 : kWave - 1, kWave);
+      const int atG0 = __shfl(incl, g0 > 0 ? g0 - 1 : 0, kWave);
+      const int atL = __shfl(incl, lb >= 0 ? lb : 0, kWave);
+      const int totA = atS - (g0 > 0 ? atG0 : 0), totB = atL - atS;
+      const int nA = min(totA + 1, gsz - 1), nB = min(totB, gsz - 1);
+      const bool exA = totA + 1 <= gsz - 1, exB = totB <= gsz - 1;
+      if (inA) {
+        const int sx = atS - incl;  // A's vertices in the lanes right of this one
+        for (int m = 0; m < cA && sx + m < nA; ++m) L.wa[g0 + sx + m] = (uint32_t)(lane << 16 | (topA - m));
+      }
+      if (merge && lane == g0 && totA < nA) L.wa[g0 + totA] = (uint32_t)(g0 << 16);  // (g0, 0): A's first
+      if (inB) {
+        const int px = incl - cB - atS;  // B's vertices in the lanes left of this one
+        for (int m = 0; m < cB && px + m < nB; ++m) L.wb[g0 + px + m] = (uint32_t)(lane << 16 | (lo + m));
+      }
+      __syncthreads();
+      int oal = 0, oad = 0, obl = 0, obd = 0;
+      double2 PA{0.0, 0.0}, PB{0.0, 0.0};
+      if (merge && !settled && k < nA) {
+        const uint32_t e = L.wa[lane];
+        oal = (int)(e >> 16);
+        oad = (int)(e & 0xffffu);
+        PA = chunk_entry<T, W, D>(L, ckx, cky, oal, oad, len, yc, wc);
+      }
+      if (merge && !settled && k < nB) {
+        const uint32_t e = L.wb[lane];
+        obl = (int)(e >> 16);
+        obd = (int)(e & 0xffffu);
+        PB = chunk_entry<T, W, D>(L, ckx, cky, obl, obd, len, yc, wc);
+      }
+      const int sl = merge ? sB - 1 : 0;
+      const int sd = merge ? L.depth[sl] - 1 : 0;
+      const double2 Sp = merge ? L.start[sB] : double2{0.0, 0.0};  // s, lane sB - 1's end point
+      // lane k: a_k (its left neighbour's a_{k+1}; s for k = 0) and b_{k+2}
+      double2 Aprev{__shfl_up(PA.x, 1, kWave), __shfl_up(PA.y, 1, kWave)};
+      int apl = __shfl_up(oal, 1, kWave), apd = __shfl_up(oad, 1, kWave);
+      if (k == 0) {
+        Aprev = Sp;
+        apl = sl;
+        apd = sd;
+      }
+      const double2 Bnext{__shfl_down(PB.x, 1, kWave), __shfl_down(PB.y, 1, kWave)};
+      const int bnl = __shfl_down(obl, 1, kWave), bnd = __shfl_down(obd, 1, kWave);
+      int ka = 0, kb = 1;
+      double2 Pa = Sp;
+      double2 Pb{__shfl(PB.x, g0, kWave), __shfl(PB.y, g0, kWave)};
+      {
+        const int b1l = __shfl(obl, g0, kWave), b1d = __shfl(obd, g0, kWave);
+        if (!settled) {
+          al = sl;
+          ai = sd;
+          bl = b1l;
+          bi = b1d;
+        }
+      }
+      bool act = merge && !settled && nB >= 1;
+      for (int it = 0; it < 4 * kWave; ++it) {
+        if (!__any(act)) break;
+        bool moved = false;
+        // alpha: lane k decides the stop at a_k (k = nA: a_nA is A's first vertex when exA)
+        {
+          const bool st = act && k >= ka &&
+                          ((k < nA && wleft(oal, oad, PA, apl, apd, Aprev, bl, bi, Pb)) || (k == nA && exA));
+          const uint64_t hit = (__ballot(st) >> g0) & gm;
+          const int kk = hit ? __builtin_ctzll(hit) : nA;  // no stop: alpha walks past the window
+          const int src = g0 + max(kk - 1, 0);
+          const double2 Pn{__shfl(PA.x, src, kWave), __shfl(PA.y, src, kWave)};
+          const int nl_ = __shfl(oal, src, kWave), nd_ = __shfl(oad, src, kWave);
+          if (act && kk != ka) {
+            moved = true;
+            ka = kk;
+            Pa = kk == 0 ? Sp : Pn;
+            al = kk == 0 ? sl : nl_;
+            ai = kk == 0 ? sd : nd_;
+          }
+          if (act && !hit) {
+            act = false;
+            from_win = true;
+          }
+        }
+        // beta: lane k decides the stop at b_{k+1} (k + 1 = nB: B's last vertex when exB)
+        {
+          const int k1 = k + 1;
+          const bool st = act && k1 >= kb &&
+                          ((k1 < nB && wleft(al, ai, Pa, obl, obd, PB, bnl, bnd, Bnext)) || (k1 == nB && exB));
+          const uint64_t hit = (__ballot(st) >> g0) & gm;
+          const int kk = hit ? __builtin_ctzll(hit) + 1 : nB;
+          const int src = g0 + kk - 1;
+          const double2 Pn{__shfl(PB.x, src, kWave), __shfl(PB.y, src, kWave)};
+          const int nl_ = __shfl(obl, src, kWave), nd_ = __shfl(obd, src, kWave);
+          if (act && kk != kb) {
+            moved = true;
+            kb = kk;
+            Pb = Pn;
+            bl = nl_;
+            bi = nd_;
+          }
+          if (act && !hit) {
+            act = false;
+            from_win = true;
+          }
+        }
+        if (act && !moved) {
+          act = false;
+          settled = true;
+        }
+      }
+      if (merge && !settled) from_win = true;  // (the iteration cap: continue serially)
+      __syncthreads();  // (the window slots are rewritten by the next round)
+    }
+    // a strict left turn of three stack entries: the fast turn of the chunk-relative hi parts
+    // when it exceeds its error bound, else the turn of the pairs (wleft above)
+    if (merge && lane == sB && (serial || (!settled && from_win))) {
+      if (!from_win) {
+        al = sB - 1;
+        ai = L.depth[al] - 1;                        // alpha = s
+        bl = min(__builtin_ctzll(nzr & ~lanes_below(sB)), lb);  // beta = B's first vertex
+        bi = L.lo[bl];
+      }
       double2 Pa = chunk_entry<T, W, D>(L, ckx, cky, al, ai, len, yc, wc);
       double2 Pb = chunk_entry<T, W, D>(L, ckx, cky, bl, bi, len, yc, wc);
-      // a strict left turn of three stack entries: the fast turn of the chunk-relative hi parts
-      // when it exceeds its error bound, else the turn of the pairs.  Each hi coordinate is within
-      // ex = 259 u Xc (ey = 259 u Yc) of its pair (the start's lo, the lane sum's lo, the
-      // rounding of the sum), so with (dx1, dy1) = P2 - P1, (dx2, dy2) = P3 - P2 the turn
-      // dx1 dy2 - dy1 dx2 of the pairs is within 4u'(|p1| + |p2|) + 2 ex (|dy1| + |dy2|)
-      // + 2 ey (|dx1| + |dx2|) + 8 ex ey of the computed one, each term taken 1 % larger.
-      const double ex2 = (W ? L.start[nl].x : (double)len) * (2.02 * 259.0 * kU);
-      const double ey2 = yc_abs * (2.02 * 259.0 * kU);
-      const double E00 = 2.0 * ex2 * ey2 + 0x1p-1000;
-      auto wleft = [&](int l1, int i1, double2 P1, int l2, int i2, double2 P2, int l3, int i3, double2 P3) {
-        const double dx1 = P2.x - P1.x, dy1 = P2.y - P1.y, dx2 = P3.x - P2.x, dy2 = P3.y - P2.y;
-        const double p1 = dx1 * dy2, p2 = dy1 * dx2;
-        const double t = p1 - p2;
-        const double Ew = fma(4.04 * kU, fabs(p1) + fabs(p2),
-                              fma(ex2, fabs(dy1) + fabs(dy2), fma(ey2, fabs(dx1) + fabs(dx2), E00)));
-        if (fabs(t) > Ew) return t > 0.0;
-        const int ls[3] = {l1, l2, l3}, is[3] = {i1, i2, i3};
-        return entries_turn_dd<T, W, D>(L, ckx, cky, ckxl, ckyl, ls, is, len, yc, wc) > 0.0;
-      };
       for (int pass = 0; pass <= kChunk; ++pass) {
         bool moved = false;
         // alpha moves left while (pred alpha, alpha, beta) is not a strict left turn
