@@ -92,6 +92,10 @@ __device__ __forceinline__ uint64_t lanes_below(int x) {
   return x >= 64 ? ~0ull : ((1ull << x) - 1ull);
 }
 
+// Nearest integer in the input's own precision (an integer test needs no conversion).
+__device__ __forceinline__ float rint_t(float v) { return rintf(v); }
+__device__ __forceinline__ double rint_t(double v) { return rint(v); }
+
 // c ? a : b on values (never on references, so both sides stay in registers).
 __device__ __forceinline__ double sel(bool c, double a, double b) { return c ? a : b; }
 __device__ __forceinline__ int sel(bool c, int a, int b) { return c ? a : b; }
@@ -1168,8 +1172,9 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         const double tr = fma(W ? wd * dq : dq, 0x1.0000000000004p0, 0x1p-960);
         const double al = W ? wpp * (ypp - yd) : ypp - yd;
         const double ar = W ? wn * (yprev - yn) : yprev - yn;
-        const bool xl = q >= 2 && al >= tl && tl < INFINITY;
-        const bool xr = hasn && ar >= tr && tr < INFINITY;
+        // (for fp32 inputs the sides are finite: w dq stays below 2^256)
+        const bool xl = q >= 2 && al >= tl && (sizeof(T) == 4 || tl < INFINITY);
+        const bool xr = hasn && ar >= tr && (sizeof(T) == 4 || tr < INFINITY);
         cand = cand && !xl && !xr;
       }
       ypp = yprev;
@@ -1189,7 +1194,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       aabs += fabs(p);
       if (W) lomx = fmax(lomx, fabs(lxl));
       lomy = fmax(lomy, fabs(lyl));
-      intin = intin && yd == rint(yd) && (!W || wd == rint(wd));
+      intin = intin && yv[k] == rint_t(yv[k]) && (!W || wv[k] == rint_t(wv[k]));
       yprev = yd;
     };
     // pushes the tile's points eb + k, k >= kp, without tests (a clean strictly increasing tile
@@ -1226,7 +1231,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           aabs += fabs(p);
           if (W) lomx = fmax(lomx, fabs(lxl));
           lomy = fmax(lomy, fabs(lyl));
-          intin = intin && yd == rint(yd) && (!W || wd == rint(wd));
+          intin = intin && yv[k] == rint_t(yv[k]) && (!W || wv[k] == rint_t(wv[k]));
         }
       }
       vpend = false;
