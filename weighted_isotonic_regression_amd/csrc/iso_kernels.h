@@ -201,6 +201,7 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
   __shared__ double sXl[W ? kPts : 1];
   __shared__ double sYl[kPts];
   __shared__ uint32_t sM[kMW];
+  __shared__ int sLst[kMW], sFst[kMW];  // per mask word: last vertex at or before it, first at or after
   __shared__ uint32_t sF[kWave];
   __shared__ double sWave[6 * NW];  // per wavefront: lane-total sums, then their prefixes
 
@@ -445,6 +446,40 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
 
   // ---- a5: emit.
   {
+    // Per mask word of a row, the last vertex in the words up to it and the first in the words
+    // from it on (a segmented max and min scan over the row's words), so that an element finds
+    // the vertices around it with two lookups however far apart they are.
+    constexpr int KW = (kMW + kThreads - 1) / kThreads;
+    const int nwords = rows * maskStride;
+    for (int p = lane; p < nwords; p += kThreads) {
+      const uint32_t m = sM[p];
+      const int u = p % maskStride;
+      sLst[p] = m ? (u << 5) + 31 - __builtin_clz(m) : -1;
+      sFst[p] = m ? (u << 5) + __builtin_ctz(m) : INT_MAX;
+    }
+    __syncthreads();
+    for (int dd = 1; dd < maskStride; dd <<= 1) {
+      int lv[KW], fv[KW];
+#pragma unroll
+      for (int t = 0; t < KW; ++t) {
+        const int p = lane + t * kThreads;
+        if (p < nwords) {
+          const int u = p % maskStride;
+          lv[t] = u >= dd ? max(sLst[p], sLst[p - dd]) : sLst[p];
+          fv[t] = u + dd < maskStride ? min(sFst[p], sFst[p + dd]) : sFst[p];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < KW; ++t) {
+        const int p = lane + t * kThreads;
+        if (p < nwords) {
+          sLst[p] = lv[t];
+          sFst[p] = fv[t];
+        }
+      }
+      __syncthreads();
+    }
     // Element-parallel: element e (row r, index i) gets the slope of the tile hull's edge over
     // it, from the vertex at or before point i to the vertex after it; an element whose two
     // points are both vertices is a block of its own and gets its y, the block's exact mean.
@@ -455,9 +490,15 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
       const int i = e - r * seglen;
       const uint32_t* Mr = &sM[r * maskStride];
       TilePairs<W> Qr{sX, sY, sXl, sYl, r * rowStride, 0};
-      const bool isv = (Mr[i >> 5] >> (i & 31)) & 1u;
-      const int a = isv ? i : mask_pred(Mr, i);
-      const int b = mask_succ(Mr, i);
+      const int u = i >> 5, bt = i & 31;
+      const uint32_t mw = Mr[u];
+      const bool isv = (mw >> bt) & 1u;
+      // point 0 is a vertex, so a word without a vertex at or before i is not the first one;
+      // the row's end point is a vertex, so one without a vertex after i is not the last one
+      const uint32_t ml = mw & (bt == 31 ? ~0u : ((2u << bt) - 1u));
+      const uint32_t mh = bt == 31 ? 0u : (mw & ~((2u << bt) - 1u));
+      const int a = ml ? (u << 5) + 31 - __builtin_clz(ml) : sLst[r * maskStride + u - 1];
+      const int b = mh ? (u << 5) + __builtin_ctz(mh) : sFst[r * maskStride + u + 1];
       const bool bad = sF[r] != 0u;
       const double slope = slope_dd(Qr(a), Qr(b));
       z[off + e] = bad ? (T)NAN : (isv && b == i + 1) ? ye : (T)zval<D>(slope);
