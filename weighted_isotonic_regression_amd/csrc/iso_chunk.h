@@ -1023,7 +1023,8 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       const double t = p1 - p2;
       const double E = fma(4.04 * kU, fabs(p1) + fabs(p2),
                            fma(cLY, fabs(dx1) + fabs(dx2), fma(cLX, fabs(dy1) + fabs(dy2), E0)));
-      const bool tst = act && d >= 2;
+      // (bitwise operators throughout, so that the compiler keeps the step free of branches)
+      const bool tst = act & (d >= 2);
       // While no running sum of the lane has rounded (every lo part so far is zero: LX = LY = 0)
       // the hi parts are the coordinates, and a turn inside its bound is decided here, in
       // double-double arithmetic on them, as the exact pass would (ties and collinear runs of
@@ -1033,7 +1034,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       bool und = false;
       double td = t;
       if constexpr (!W && sizeof(T) == 8) {  // (the soft rank's problems are of this kind)
-        und = dexact && tst && !(fabs(t) > E);
+        und = dexact & tst & !(fabs(t) > E);
         if (__any(und)) {
           if (und) {
             td = turn_dd(PD{DD{ux, 0.0}, DD{uy, 0.0}}, PD{DD{tx, 0.0}, DD{ty, 0.0}},
@@ -1041,17 +1042,17 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
           }
         }
       }
-      undec = undec || (tst && !und && !(fabs(t) > E));
-      const bool push = act && (d < 2 || td > 0.0);
-      const bool pop = act && !push;
-      // the stack mask: a push sets K's bit, a pop clears T's
-      if (act) {
+      undec = undec | (tst & !und & !(fabs(t) > E));
+      const bool push = act & ((d < 2) | (td > 0.0));
+      const bool pop = act & !push;
+      // the stack mask: a push sets K's bit, a pop clears T's (an idle lane xors zero)
+      {
         const int mi = push ? kq : ti;
-        atomicXor(&L.smask[mi >> 5][lane], 1u << (mi & 31));
+        atomicXor(&L.smask[mi >> 5][lane], act ? 1u << (mi & 31) : 0u);
       }
       // A pop makes V the new U: V is the entry read after the previous pop when that read is
       // pending (vpend), and an entry whose tag shows it was overwritten is recomputed first.
-      const bool stale = pop && vpend && d >= 3 && !tag_is(rtg, d - 3);
+      const bool stale = pop & vpend & (d >= 3) & !tag_is(rtg, d - 3);
       if (__any(stale)) {
         if (stale) {
           int ww = ui >> 5;
