@@ -1163,7 +1163,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       // the other one taken 2^-50 larger (plus 2^-960 against underflow) exceeds it exactly; such
       // a point is left out of the queue (any hull that holds it and those neighbours has it
       // above a chord), which does not change the lane's hull.
-      bool cand = q > 0 && yprev < yd;
+      bool cand = (q > 0) & (yprev < yd);
       {
         const bool hasn = k + 1 < TN ? (k + 1 < kn) : (eb + TN < c);
         const double yn = yval<D>(k + 1 < TN ? yv[k + 1 < TN ? k + 1 : 0] : ny[0]);
@@ -1174,19 +1174,21 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
         const double al = W ? wpp * (ypp - yd) : ypp - yd;
         const double ar = W ? wn * (yprev - yn) : yprev - yn;
         // (for fp32 inputs the sides are finite: w dq stays below 2^256)
-        const bool xl = q >= 2 && al >= tl && (sizeof(T) == 4 || tl < INFINITY);
-        const bool xr = hasn && ar >= tr && (sizeof(T) == 4 || tr < INFINITY);
-        cand = cand && !xl && !xr;
+        const bool xl = (q >= 2) & (al >= tl) & (sizeof(T) == 4 || tl < INFINITY);
+        const bool xr = hasn & (ar >= tr) & (sizeof(T) == 4 || tr < INFINITY);
+        cand = cand & !xl & !xr;
       }
       ypp = yprev;
       wpp = wprev;
       wprev = wd;
-      if (cand) {
+      // every lane writes the slot after its queue's tail, which is free (at most kQ - 1 points
+      // wait when an element arrives); only a candidate moves the tail over it
+      {
         const int s = qt & (kQ - 1);
         if constexpr (W) L.qp[s][lane] = double2{lx, ly};
         else L.qp[s][lane] = ly;
         L.qi[s][lane] = (uint8_t)(q - 1);
-        ++qt;
+        qt += cand ? 1 : 0;
       }
       if (W) acc(lx, lxl, wd);
       const double p = wd * yd;
@@ -1195,7 +1197,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
       aabs += fabs(p);
       if (W) lomx = fmax(lomx, fabs(lxl));
       lomy = fmax(lomy, fabs(lyl));
-      intin = intin && yv[k] == rint_t(yv[k]) && (!W || wv[k] == rint_t(wv[k]));
+      intin = intin & (yv[k] == rint_t(yv[k])) & (!W || wv[k] == rint_t(wv[k]));
       yprev = yd;
     };
     // pushes the tile's points eb + k, k >= kp, without tests (a clean strictly increasing tile
