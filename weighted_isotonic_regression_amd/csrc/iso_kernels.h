@@ -509,60 +509,81 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
 }
 
 // ------------------------------------------------------------------ tiny rows
-// Rows of at most kTinyMax elements: one lane fits one row by pool adjacent violators, the
-// classical sequential method the page names (Section 1), which for so few elements beats
-// building the diagram's hull: the row's inputs sit in registers, each block's fp64 sums (w, w*y)
-// in LDS at its first element, and the block starts in a register bit mask.  The top block is
-// pooled with the one below while the lower mean is at least the top one, compared by
-// cross-multiplication, with the sums added in stack order: exactly the oracle's arithmetic.  The
-// fit is each block's sum quotient rounded once, or y for a block of one element (its exact mean).
+// Rows of at most kTinyMax elements, two lanes per row: pool adjacent violators, the classical
+// sequential method the page names (Section 1), which for so few elements beats building the
+// diagram's hull.  The row is split at h = ceil(n / 2); each lane of the pair pools its half into a
+// stack of blocks (the top block's fp64 sums (w, w*y) in registers, the blocks below it in LDS at
+// their first element, the block starts in a bit mask).  The left lane then pushes the right
+// lane's blocks onto its stack in order, pooling while the block below has a mean >= the top one
+// (means compared by cross-multiplication); the right half's own blocks have increasing means, so
+// once one of them is pushed without pooling the rest stay as they are.  This is the pool adjacent
+// violators fit of the whole row (pooling is order independent); its sums are added in a different
+// order than by one sequential scan.  The fit is each block's sum quotient rounded once, or y for a
+// block of one element (its exact mean).
 constexpr int kTinyMax = 16;
+constexpr int kTinyHalf = kTinyMax / 2;
+constexpr int kTinyRows = kWave / 2;  // rows per wavefront
 
 template <typename T, bool W, bool D>
 __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T* __restrict__ w,
                                                 T* __restrict__ z, uint8_t* __restrict__ bstart,
                                                 uint32_t* __restrict__ rflags, int64_t batch, int n) {
-  __shared__ double sS[kTinyMax][kWave];
-  __shared__ double sW[W ? kTinyMax : 1][kWave];
-  constexpr int VN = Vec16<T>::N;
+  __shared__ double sS[kTinyMax][kTinyRows];
+  __shared__ double sW[W ? kTinyMax : 1][kTinyRows];
+  __shared__ uint32_t sMask[kTinyRows];
   const int lane = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * kWave + lane;
-  if (row >= batch) return;
-  const int64_t off = row * n;
-  T yv[kTinyMax], wv[kTinyMax];
-  const bool vec = (n % VN) == 0 && ((uintptr_t)(y + off)) % 16 == 0 && (!W || ((uintptr_t)(w + off)) % 16 == 0);
+  const int rr = lane >> 1;        // the row within the wavefront
+  const int half = lane & 1;
+  const int64_t row = (int64_t)blockIdx.x * kTinyRows + rr;
+  const bool live = row < batch;
+  const int hl = (n + 1) >> 1;     // the left lane's elements
+  const int h0 = half ? hl : 0;
+  const int nh = half ? n - hl : hl;
+  const int64_t off = (live ? row : 0) * n + h0;
+  constexpr int VN = Vec16<T>::N;
+  // 16-byte vectors when both halves are whole vectors at 16-byte aligned addresses
+  const bool vec = (hl % VN) == 0 && (n % VN) == 0 && ((uintptr_t)y) % 16 == 0 && ((uintptr_t)z) % 16 == 0 &&
+                   (!W || ((uintptr_t)w) % 16 == 0);
+  T yv[kTinyHalf], wv[kTinyHalf];
   if (vec) {
 #pragma unroll
-    for (int k = 0; k < kTinyMax / VN; ++k) {
-      if (k * VN < n) {
-        load16(y + off + k * VN, &yv[k * VN]);
-        if (W) load16(w + off + k * VN, &wv[k * VN]);
+    for (int k = 0; k < kTinyHalf; k += VN) {
+      if (live && k < nh) {
+        load16(y + off + k, &yv[k]);
+        if (W) load16(w + off + k, &wv[k]);
       }
+    }
+#pragma unroll
+    for (int k = 0; k < kTinyHalf; ++k) {
+      if (!(live && k < nh)) {
+        yv[k] = (T)0;
+        wv[k] = (T)1;
+      }
+      if (!W) wv[k] = (T)1;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kTinyMax; ++i) {
-      if (i < n) {
-        yv[i] = y[off + i];
-        if (W) wv[i] = w[off + i];
-      }
+    for (int k = 0; k < kTinyHalf; ++k) {
+      yv[k] = (live && k < nh) ? y[off + k] : (T)0;
+      wv[k] = (W && live && k < nh) ? w[off + k] : (T)1;
     }
   }
   uint32_t flag = 0u, mask = 0u;
   double tS = 0.0, tW = 1.0;
-  int tt = 0;
+  int tt = h0;
+  // the lane's half: push element i as a block, then pool while the block below has a mean >= the
+  // top one's
 #pragma unroll
-  for (int i = 0; i < kTinyMax; ++i) {
-    if (i < n) {
-      const double yd = yval<D>(yv[i]);
-      const double wd = W ? (double)wv[i] : 1.0;
+  for (int k = 0; k < kTinyHalf; ++k) {
+    if (live && k < nh) {
+      const int i = h0 + k;
+      const double yd = yval<D>(yv[k]);
+      const double wd = W ? (double)wv[k] : 1.0;
       if (!isfinite(yd) || !isfinite(wd)) flag |= ISO_ROW_NONFINITE_BIT;
       else if (!(wd > 0.0)) flag |= ISO_ROW_BAD_WEIGHT_BIT;
-      // push element i as a block, then pool while the block below has a mean >= the top one's;
-      // the top block lives in registers (tS, tW, tt), the blocks below it in LDS
       double Sn = wd * yd, Wn = wd;
       int tn = i;
-      if (i > 0) {
+      if (k > 0) {
         if (tS * Wn >= Sn * tW) {
           Sn = tS + Sn;
           Wn = tW + Wn;
@@ -570,7 +591,7 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
           uint32_t below = mask & ~(1u << tt);
           while (below) {
             const int p = 31 - __builtin_clz(below);
-            const double Sp = sS[p][lane], Wp = W ? sW[p][lane] : (double)(tn - p);
+            const double Sp = sS[p][rr], Wp = W ? sW[p][rr] : (double)(tn - p);
             if (!(Sp * Wn >= Sn * Wp)) break;
             Sn = Sp + Sn;
             Wn = Wp + Wn;
@@ -579,8 +600,8 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
           }
           mask = below;
         } else {
-          sS[tt][lane] = tS;
-          if (W) sW[tt][lane] = tW;
+          sS[tt][rr] = tS;
+          if (W) sW[tt][rr] = tW;
         }
       }
       mask |= 1u << tn;
@@ -589,41 +610,87 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
       tt = tn;
     }
   }
-  sS[tt][lane] = tS;
-  if (W) sW[tt][lane] = tW;
+  if (live && nh > 0) {
+    sS[tt][rr] = tS;
+    if (W) sW[tt][rr] = tW;
+  }
+  flag |= __shfl_xor(flag, 1, kWave);
+  const uint32_t mR = __shfl_xor(mask, 1, kWave);  // (the left lane's view: the right half's starts)
+  __syncthreads();
+  // the left lane pushes the right half's blocks in order
+  if (live && half == 0 && mR != 0u) {
+    uint32_t rest = mR;
+    while (rest) {
+      const int p = __builtin_ctz(rest);
+      rest &= rest - 1u;
+      const int pe = rest ? __builtin_ctz(rest) : n;  // the block's end
+      double Sn = sS[p][rr], Wn = W ? sW[p][rr] : (double)(pe - p);
+      if (!(tS * Wn >= Sn * tW)) {  // no pooling: this block and the rest stay as they are
+        mask |= (1u << p) | rest;
+        rest = 0u;
+        break;
+      }
+      Sn = tS + Sn;
+      Wn = tW + Wn;
+      int tn = tt;
+      uint32_t below = mask & ~(1u << tt);
+      while (below) {
+        const int q = 31 - __builtin_clz(below);
+        const double Sp = sS[q][rr], Wp = W ? sW[q][rr] : (double)(tn - q);
+        if (!(Sp * Wn >= Sn * Wp)) break;
+        Sn = Sp + Sn;
+        Wn = Wp + Wn;
+        tn = q;
+        below &= ~(1u << q);
+      }
+      mask = below | (1u << tn);
+      tS = Sn;
+      tW = Wn;
+      tt = tn;
+    }
+    sS[tt][rr] = tS;
+    if (W) sW[tt][rr] = tW;
+    sMask[rr] = mask;
+  } else if (live && half == 0) {
+    sMask[rr] = mask;
+  }
+  __syncthreads();
+  if (!live) return;
+  const uint32_t fm = sMask[rr];
   // the fit: element i takes the mean of the block starting at the highest set bit <= i
-  T zv[kTinyMax];
-  uint8_t bs[kTinyMax];
+  T zv[kTinyHalf];
+  uint8_t bs[kTinyHalf];
 #pragma unroll
-  for (int i = 0; i < kTinyMax; ++i) {
-    if (i < n) {
-      const int b = 31 - __builtin_clz(mask & ((2u << i) - 1u));
-      const uint32_t after = mask & ~((2u << i) - 1u);  // block starts after i
-      const int e = after ? __builtin_ctz(after) : n;     // end of i's block
-      bs[i] = (b == i && !flag) ? 1 : 0;
-      if (flag) zv[i] = (T)NAN;
-      else if (e - b == 1) zv[i] = yv[i];
+  for (int k = 0; k < kTinyHalf; ++k) {
+    if (k < nh) {
+      const int i = h0 + k;
+      const int b = 31 - __builtin_clz(fm & ((2u << i) - 1u));
+      const uint32_t after = fm & ~((2u << i) - 1u);  // block starts after i
+      const int e = after ? __builtin_ctz(after) : n;  // end of i's block
+      bs[k] = (b == i && !flag) ? 1 : 0;
+      if (flag) zv[k] = (T)NAN;
+      else if (e - b == 1) zv[k] = yv[k];
       else {
-        const double Wb = W ? sW[b][lane] : (double)(e - b);
-        zv[i] = (T)zval<D>(sS[b][lane] / Wb);
+        const double Wb = W ? sW[b][rr] : (double)(e - b);
+        zv[k] = (T)zval<D>(sS[b][rr] / Wb);
       }
     }
   }
   if (vec) {
 #pragma unroll
-    for (int k = 0; k < kTinyMax / VN; ++k)
-      if (k * VN < n) store16(z + off + k * VN, &zv[k * VN]);
+    for (int k = 0; k < kTinyHalf; k += VN)
+      if (k < nh) store16(z + off + k, &zv[k]);
   } else {
 #pragma unroll
-    for (int i = 0; i < kTinyMax; ++i)
-      if (i < n) z[off + i] = zv[i];
+    for (int k = 0; k < kTinyHalf; ++k)
+      if (k < nh) z[off + k] = zv[k];
   }
   if (bstart) {
 #pragma unroll
-    for (int i = 0; i < kTinyMax; ++i)
-      if (i < n) bstart[off + i] = bs[i];
+    for (int k = 0; k < kTinyHalf; ++k)
+      if (k < nh) bstart[off + k] = bs[k];
   }
-  if (rflags) rflags[row] = flag;
+  if (rflags && half == 0) rflags[row] = flag;
 }
 
 // ------------------------------------------------------------------ chunk-start scan
