@@ -509,20 +509,22 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
 }
 
 // ------------------------------------------------------------------ tiny rows
-// Rows of at most kTinyMax elements, two lanes per row: pool adjacent violators, the classical
-// sequential method the page names (Section 1), which for so few elements beats building the
-// diagram's hull.  The row is split at h = ceil(n / 2); each lane of the pair pools its half into a
-// stack of blocks (the top block's fp64 sums (w, w*y) in registers, the blocks below it in LDS at
-// their first element, the block starts in a bit mask).  The left lane then pushes the right
-// lane's blocks onto its stack in order, pooling while the block below has a mean >= the top one
-// (means compared by cross-multiplication); the right half's own blocks have increasing means, so
-// once one of them is pushed without pooling the rest stay as they are.  This is the pool adjacent
-// violators fit of the whole row (pooling is order independent); its sums are added in a different
-// order than by one sequential scan.  The fit is each block's sum quotient rounded once, or y for a
-// block of one element (its exact mean).
+// Rows of at most kTinyMax elements, kTinyLanes lanes per row: pool adjacent violators, the
+// classical sequential method the page names (Section 1), which for so few elements beats building
+// the diagram's hull.  The row is cut into kTinyLanes parts of h = ceil(n / kTinyLanes) elements;
+// each lane pools its part into a stack of blocks (the top block's fp64 sums (w, w*y) in
+// registers, the blocks below it in LDS at their first element, the block starts in a bit mask).
+// Then, in rounds, the first lane of each pair of neighbouring groups pushes the right group's
+// blocks onto its stack in order, pooling while the block below has a mean >= the top one (means
+// compared by cross-multiplication); a group's own blocks have increasing means, so once one of
+// them is pushed without pooling the rest stay as they are.  The result is the pool adjacent
+// violators fit of the whole row (pooling is order independent), its sums added in a different
+// order than by one sequential scan.  The fit is each block's sum quotient rounded once, or y for
+// a block of one element (its exact mean).
 constexpr int kTinyMax = 16;
-constexpr int kTinyHalf = kTinyMax / 2;
-constexpr int kTinyRows = kWave / 2;  // rows per wavefront
+constexpr int kTinyLanes = 4;                        // lanes per row
+constexpr int kTinyPart = kTinyMax / kTinyLanes;     // elements per lane at most
+constexpr int kTinyRows = kWave / kTinyLanes;        // rows per wavefront
 
 template <typename T, bool W, bool D>
 __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T* __restrict__ w,
@@ -532,29 +534,29 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
   __shared__ double sW[W ? kTinyMax : 1][kTinyRows];
   __shared__ uint32_t sMask[kTinyRows];
   const int lane = threadIdx.x;
-  const int rr = lane >> 1;        // the row within the wavefront
-  const int half = lane & 1;
+  const int rr = lane / kTinyLanes;  // the row within the wavefront
+  const int q = lane % kTinyLanes;   // the part of the row
   const int64_t row = (int64_t)blockIdx.x * kTinyRows + rr;
   const bool live = row < batch;
-  const int hl = (n + 1) >> 1;     // the left lane's elements
-  const int h0 = half ? hl : 0;
-  const int nh = half ? n - hl : hl;
+  const int hp = (n + kTinyLanes - 1) / kTinyLanes;
+  const int h0 = min(q * hp, n);
+  const int nh = min(hp, n - h0);
   const int64_t off = (live ? row : 0) * n + h0;
   constexpr int VN = Vec16<T>::N;
-  // 16-byte vectors when both halves are whole vectors at 16-byte aligned addresses
-  const bool vec = (hl % VN) == 0 && (n % VN) == 0 && ((uintptr_t)y) % 16 == 0 && ((uintptr_t)z) % 16 == 0 &&
+  // 16-byte vectors when every part is whole vectors at 16-byte aligned addresses
+  const bool vec = (hp % VN) == 0 && (n % VN) == 0 && ((uintptr_t)y) % 16 == 0 && ((uintptr_t)z) % 16 == 0 &&
                    (!W || ((uintptr_t)w) % 16 == 0);
-  T yv[kTinyHalf], wv[kTinyHalf];
+  T yv[kTinyPart], wv[kTinyPart];
   if (vec) {
 #pragma unroll
-    for (int k = 0; k < kTinyHalf; k += VN) {
+    for (int k = 0; k < kTinyPart; k += VN) {
       if (live && k < nh) {
         load16(y + off + k, &yv[k]);
         if (W) load16(w + off + k, &wv[k]);
       }
     }
 #pragma unroll
-    for (int k = 0; k < kTinyHalf; ++k) {
+    for (int k = 0; k < kTinyPart; ++k) {
       if (!(live && k < nh)) {
         yv[k] = (T)0;
         wv[k] = (T)1;
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kTinyHalf; ++k) {
+    for (int k = 0; k < kTinyPart; ++k) {
       yv[k] = (live && k < nh) ? y[off + k] : (T)0;
       wv[k] = (W && live && k < nh) ? w[off + k] : (T)1;
     }
@@ -571,97 +573,95 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
   uint32_t flag = 0u, mask = 0u;
   double tS = 0.0, tW = 1.0;
   int tt = h0;
-  // the lane's half: push element i as a block, then pool while the block below has a mean >= the
-  // top one's
+  // pools the top block (tS, tW, tt) with the blocks below it while the one below has a mean >=
+  // the top one's
+  auto pool_down = [&]() {
+    uint32_t below = mask & ~(1u << tt);
+    while (below) {
+      const int p = 31 - __builtin_clz(below);
+      const double Sp = sS[p][rr], Wp = W ? sW[p][rr] : (double)(tt - p);
+      if (!(Sp * tW >= tS * Wp)) break;
+      tS = Sp + tS;
+      tW = Wp + tW;
+      tt = p;
+      below &= ~(1u << p);
+    }
+    mask = below | (1u << tt);
+  };
+  // the lane's part: push element i as a block, then pool
 #pragma unroll
-  for (int k = 0; k < kTinyHalf; ++k) {
+  for (int k = 0; k < kTinyPart; ++k) {
     if (live && k < nh) {
       const int i = h0 + k;
       const double yd = yval<D>(yv[k]);
       const double wd = W ? (double)wv[k] : 1.0;
       if (!isfinite(yd) || !isfinite(wd)) flag |= ISO_ROW_NONFINITE_BIT;
       else if (!(wd > 0.0)) flag |= ISO_ROW_BAD_WEIGHT_BIT;
-      double Sn = wd * yd, Wn = wd;
-      int tn = i;
-      if (k > 0) {
-        if (tS * Wn >= Sn * tW) {
-          Sn = tS + Sn;
-          Wn = tW + Wn;
-          tn = tt;
-          uint32_t below = mask & ~(1u << tt);
-          while (below) {
-            const int p = 31 - __builtin_clz(below);
-            const double Sp = sS[p][rr], Wp = W ? sW[p][rr] : (double)(tn - p);
-            if (!(Sp * Wn >= Sn * Wp)) break;
-            Sn = Sp + Sn;
-            Wn = Wp + Wn;
-            tn = p;
-            below &= ~(1u << p);
-          }
-          mask = below;
-        } else {
+      const double Sn = wd * yd, Wn = wd;
+      if (k > 0 && tS * Wn >= Sn * tW) {
+        tS = tS + Sn;
+        tW = tW + Wn;
+        pool_down();
+      } else {
+        if (k > 0) {
           sS[tt][rr] = tS;
           if (W) sW[tt][rr] = tW;
         }
+        mask |= 1u << i;
+        tS = Sn;
+        tW = Wn;
+        tt = i;
       }
-      mask |= 1u << tn;
-      tS = Sn;
-      tW = Wn;
-      tt = tn;
     }
   }
   if (live && nh > 0) {
     sS[tt][rr] = tS;
     if (W) sW[tt][rr] = tW;
   }
-  flag |= __shfl_xor(flag, 1, kWave);
-  const uint32_t mR = __shfl_xor(mask, 1, kWave);  // (the left lane's view: the right half's starts)
-  __syncthreads();
-  // the left lane pushes the right half's blocks in order
-  if (live && half == 0 && mR != 0u) {
-    uint32_t rest = mR;
-    while (rest) {
-      const int p = __builtin_ctz(rest);
-      rest &= rest - 1u;
-      const int pe = rest ? __builtin_ctz(rest) : n;  // the block's end
-      double Sn = sS[p][rr], Wn = W ? sW[p][rr] : (double)(pe - p);
-      if (!(tS * Wn >= Sn * tW)) {  // no pooling: this block and the rest stay as they are
-        mask |= (1u << p) | rest;
-        rest = 0u;
-        break;
+#pragma unroll
+  for (int o = 1; o < kTinyLanes; o <<= 1) flag |= __shfl_xor(flag, o, kWave);
+  // rounds: the group of lanes [q, q + 2 st) joins its right half [q + st, q + 2 st)
+#pragma unroll
+  for (int st = 1; st < kTinyLanes; st <<= 1) {
+    const uint32_t mR = __shfl_down(mask, st, kWave);  // (used by the lanes with q % 2 st = 0)
+    __syncthreads();
+    if (live && q % (2 * st) == 0 && mR != 0u) {
+      const int gend = min(h0 + 2 * st * hp, n);  // the right group's end
+      uint32_t rest = mR;
+      bool kept = false;
+      while (rest) {
+        const int p = __builtin_ctz(rest);
+        rest &= rest - 1u;
+        const int pe = rest ? __builtin_ctz(rest) : gend;  // the pushed block's end
+        const double Sn = sS[p][rr], Wn = W ? sW[p][rr] : (double)(pe - p);
+        if (!(tS * Wn >= Sn * tW)) {  // no pooling: this block and the rest stay as they are
+          mask |= (1u << p) | rest;
+          kept = true;
+          break;
+        }
+        tS = tS + Sn;
+        tW = tW + Wn;
+        pool_down();
       }
-      Sn = tS + Sn;
-      Wn = tW + Wn;
-      int tn = tt;
-      uint32_t below = mask & ~(1u << tt);
-      while (below) {
-        const int q = 31 - __builtin_clz(below);
-        const double Sp = sS[q][rr], Wp = W ? sW[q][rr] : (double)(tn - q);
-        if (!(Sp * Wn >= Sn * Wp)) break;
-        Sn = Sp + Sn;
-        Wn = Wp + Wn;
-        tn = q;
-        below &= ~(1u << q);
+      sS[tt][rr] = tS;
+      if (W) sW[tt][rr] = tW;
+      if (kept) {  // the joined group's top is the right group's last block
+        tt = 31 - __builtin_clz(mask);
+        tS = sS[tt][rr];
+        tW = W ? sW[tt][rr] : (double)(gend - tt);
       }
-      mask = below | (1u << tn);
-      tS = Sn;
-      tW = Wn;
-      tt = tn;
     }
-    sS[tt][rr] = tS;
-    if (W) sW[tt][rr] = tW;
-    sMask[rr] = mask;
-  } else if (live && half == 0) {
-    sMask[rr] = mask;
+    __syncthreads();
   }
+  if (live && q == 0) sMask[rr] = mask;
   __syncthreads();
   if (!live) return;
   const uint32_t fm = sMask[rr];
   // the fit: element i takes the mean of the block starting at the highest set bit <= i
-  T zv[kTinyHalf];
-  uint8_t bs[kTinyHalf];
+  T zv[kTinyPart];
+  uint8_t bs[kTinyPart];
 #pragma unroll
-  for (int k = 0; k < kTinyHalf; ++k) {
+  for (int k = 0; k < kTinyPart; ++k) {
     if (k < nh) {
       const int i = h0 + k;
       const int b = 31 - __builtin_clz(fm & ((2u << i) - 1u));
@@ -678,19 +678,19 @@ __global__ __launch_bounds__(kWave) void k_tiny(const T* __restrict__ y, const T
   }
   if (vec) {
 #pragma unroll
-    for (int k = 0; k < kTinyHalf; k += VN)
+    for (int k = 0; k < kTinyPart; k += VN)
       if (k < nh) store16(z + off + k, &zv[k]);
   } else {
 #pragma unroll
-    for (int k = 0; k < kTinyHalf; ++k)
+    for (int k = 0; k < kTinyPart; ++k)
       if (k < nh) z[off + k] = zv[k];
   }
   if (bstart) {
 #pragma unroll
-    for (int k = 0; k < kTinyHalf; ++k)
+    for (int k = 0; k < kTinyPart; ++k)
       if (k < nh) bstart[off + k] = bs[k];
   }
-  if (rflags && half == 0) rflags[row] = flag;
+  if (rflags && q == 0) rflags[row] = flag;
 }
 
 // ------------------------------------------------------------------ chunk-start scan
