@@ -1,7 +1,7 @@
 // iso_api.hip -- the C ABI of include/iso.h: argument checks, workspace layout and launches.
 //
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
-//   n <= 16     two lanes per row, pool adjacent violators in registers and LDS (k_tiny)
+//   n <= 16     four lanes per row, pool adjacent violators in registers and LDS (k_tiny)
 //   n <= 4096   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront (rows
 //               over 2048: one row per workgroup of 2 wavefronts); one launch of k_wave
 //               writes z, block starts and row flags (Section 3.5).

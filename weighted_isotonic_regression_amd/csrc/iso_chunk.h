@@ -8,7 +8,10 @@
 //                run 64 independent chains and the chunk needs only six merge rounds.
 //   Section 3.2  the lane hulls of the chunk merge pairwise in rounds; the first lane of each
 //                right half walks to the bridge (Lemma 4.2).  A lane's surviving vertices are
-//                always one contiguous range of its stack, so a round only cuts ranges.
+//                always one contiguous range of its stack, so a round only cuts ranges.  From
+//                groups of eight lanes on, a group whose stacks are shallow first runs both walks
+//                on a register window of the vertices next to the shared point, a ballot per
+//                move, and walks on serially only if a walk leaves the window.
 //   Section 3.3  the chunk's hull is emitted for the merge levels, as a vertex list when it is
 //                small and as a bit mask with coordinate checkpoints when it is dense.
 //   Section 6    "Coordinates": a lane works in coordinates relative to its first point; the
@@ -28,9 +31,11 @@
 // rows stay shallow and dense rows never pop).
 //
 // In the first pass a lane does not pop at the element that causes the pops: its candidate points
-// wait in a short LDS queue, and the wave runs chain steps (one push or pop per lane) only when
-// some queue is full, so that lanes with few pops are not held at every element by the lane with
-// the most.  The exact pass keeps the plain element-by-element chain.
+// wait in a short LDS queue, and after each element the wave runs chain steps (one push or pop
+// per lane) only while some queue is full, so that lanes with few pops are not held at every
+// element by the lane with the most.  A point joins the queue only if it can be a vertex at all:
+// y_{q-1} < y_q, and it passes two exact tests against its second neighbours (Lemma 4.1 lets any
+// stage drop its own non-vertices).  The exact pass keeps the plain element-by-element chain.
 //
 // Dense rows: a clean strictly increasing tile pushed on top of its two predecessors has every
 // element as its own block so far, so the lane writes z = y for it and marks the tile.  The fit

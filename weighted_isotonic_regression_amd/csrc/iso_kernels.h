@@ -1,11 +1,13 @@
 // iso_kernels.h -- HIP kernels of the isotonic fit for gfx950 (wave64).
 //
 // Pipeline ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 3):
-//   k_wave          rows of at most 2048 elements, packed L = 1, 2, .., 64 lanes per row and
-//                   64 / L rows per wavefront (Section 3.5): coalesced 16-byte loads, fp64
-//                   cumulative sums in LDS (lane-serial, then a wave scan of lane totals), lane
-//                   hulls by the bit-mask monotone chain (Section 3.1), pairwise walks merging
-//                   lane hulls (Section 3.2); writes z and block starts.
+//   k_tiny          rows of at most 16 elements, four lanes per row: pool adjacent violators.
+//   k_wave          rows of 17 to 4096 elements, packed L = 1, 2, .., 64 lanes per row and
+//                   64 / L rows per wavefront (Section 3.5), a row of more than 2048 over two
+//                   wavefronts: coalesced 16-byte loads, double-double cumulative sums in LDS
+//                   (lane-serial, then a wave scan of lane totals), lane hulls by the bit-mask
+//                   monotone chain (Section 3.1), pairwise walks merging lane hulls (Section 3.2);
+//                   writes z and block starts.
 //   k_chunk         (iso_chunk.h) the chunk pass of longer rows.
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
