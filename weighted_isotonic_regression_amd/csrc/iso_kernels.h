@@ -846,6 +846,10 @@ constexpr int kFitMaxSub = 4;  // workgroups per chunk at most
 __device__ __forceinline__ bool ztile_set(const uint32_t* __restrict__ zt, int64_t g, int i) {
   return ((zt[g * kWave + i / kSub] >> ((i % kSub) / kZT)) & 1u) != 0u;
 }
+// The same from the chunk's marks staged in LDS (zl = its kWave words).
+__device__ __forceinline__ bool ztile_set_l(const uint32_t* zl, int i) {
+  return ((zl[i / kSub] >> ((i % kSub) / kZT)) & 1u) != 0u;
+}
 
 template <typename T, bool W, bool D>
 __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
@@ -857,6 +861,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
   __shared__ double sSlope[kListCap];
   __shared__ int sK[kListCap];
   __shared__ uint32_t sMask[kMaskW];
+  __shared__ uint32_t sZt[kWave];  // the chunk's z-tile marks (dense form)
   constexpr int TN = Tile<T, W>::N;
   const int64_t g = blockIdx.x / nsub;
   const int sub = (int)(blockIdx.x - g * nsub);
@@ -915,6 +920,8 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
     // a whole-diagram chunk (form 2) wrote z = y for every element and keeps no tile marks
     const bool zall = S.dense[g] == 2;
     for (int q = tid; q < kMaskW; q += kFitThreads) sMask[q] = S.mask[g * kMaskW + q];
+    if (!zall)
+      for (int q = tid; q < kWave; q += kFitThreads) sZt[q] = ztile[g * kWave + q];
     __syncthreads();
     // one word (32 elements) per thread at a time: a word inside [klo, khi) whose points and the
     // next one are all vertices, in tiles whose z the chunk pass wrote, needs nothing
@@ -935,7 +942,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
       if (bstart) {
         for (int u = 0; u < n1; ++u) bstart[off + i0 + u] = 1;
       }
-      if (zall || ztile_set(ztile, g, i0)) continue;
+      if (zall || ztile_set_l(sZt, i0)) continue;
       if (yvec && n1 == VN) {
         T v[VN];
         load16(S.y + off + i0, v);
@@ -965,7 +972,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
       // where its tile is marked)
       auto close_edge = [&](int pend, int pa, const PD& Pa, int b, const PD& Pb) {
         if (b == pa + 1) {
-          if (!zall && !ztile_set(ztile, g, pa)) z[off + pa] = S.y[off + pa];
+          if (!zall && !ztile_set_l(sZt, pa)) z[off + pa] = S.y[off + pa];
           return;
         }
         const T zv = (T)zval<D>(slope_dd(Pa, Pb));
@@ -983,23 +990,37 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(VertexStore<T, W, D> S,
         pa = mask_pred(sMask, a0);
         Pa = S.dense_point(row, j, pa);
       }
-      for (int i = a0; i < a1; ++i) {
-        double wd = W ? (double)S.w[off + i] : 1.0;
-        double yd = yval<D>(S.y[off + i]);
-        if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
-          yd = 0.0;
-          wd = 1.0;
+      // the word's inputs are read four at a time, every read of a group issued before the
+      // first one is used; the sums are taken in order, as before
+      for (int i8 = a0; i8 < a1; i8 += 4) {
+        T yg[4], wg[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          yg[k] = i8 + k < a1 ? S.y[off + i8 + k] : (T)0;
+          wg[k] = (W && i8 + k < a1) ? S.w[off + i8 + k] : (T)1;
         }
-        if (bstart) bstart[off + i] = bit(i) ? 1 : 0;
-        if (W) acc(ax.hi, ax.lo, wd);
-        acc_prod<VertexStore<T, W, D>::EX>(ay.hi, ay.lo, wd, yd);
-        const int ni = i + 1;
-        if (ni < a1 && bit(ni)) {
-          const PD Pb = S.join(sx, sy, ax, ay, ni);
-          close_edge(pend, pa, Pa, ni, Pb);
-          pa = ni;
-          Pa = Pb;
-          pend = ni;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i8 + k;
+          if (i < a1) {
+            double wd = W ? (double)wg[k] : 1.0;
+            double yd = yval<D>(yg[k]);
+            if (!isfinite(yd) || !isfinite(wd) || !(wd > 0.0)) {
+              yd = 0.0;
+              wd = 1.0;
+            }
+            if (bstart) bstart[off + i] = bit(i) ? 1 : 0;
+            if (W) acc(ax.hi, ax.lo, wd);
+            acc_prod<VertexStore<T, W, D>::EX>(ay.hi, ay.lo, wd, yd);
+            const int ni = i + 1;
+            if (ni < a1 && bit(ni)) {
+              const PD Pb = S.join(sx, sy, ax, ay, ni);
+              close_edge(pend, pa, Pa, ni, Pb);
+              pa = ni;
+              Pa = Pb;
+              pend = ni;
+            }
+          }
         }
       }
       // the elements left lie under the edge from pa to the first vertex at or after a1: point a1
