@@ -39,6 +39,21 @@ int iso_prof_read(double* ms, int64_t* launches, int64_t* calls);
 /* Static name of a stage ("increasing", "chunk", "exact", "scan", "merge", "ends", "fit"), or "?". */
 const char* iso_prof_stage_name(int stage);
 
+/* Device-wide counts of rarely taken branches of the long-row path, kept whether or not timing is
+ * enabled (one atomic add per event, on that branch only), for tests that must know a branch ran:
+ *   [0] merges of the merge levels that fell back on the Overmars-van Leeuwen bisection after
+ *       32 memory windows of one side ("Merge Hulls Without Copying Vertices", Section 5.2);
+ *   [1] of those, bisections that rounding defeated, finished by single steps;
+ *   [2] chunks processed by the exact chunk pass (Section 6 "Predicates": a turn of the first
+ *       pass fell inside its error bound);
+ *   [3] merges that walked in 256-vertex memory windows.
+ * Copies the counts of the current device into out[0..3] (caller-owned, ISO_PROF_COUNTERS
+ * entries) and zeroes them if reset != 0.  Waits for the device's work to finish (a synchronous
+ * copy), so call it after the fits to be counted.  Counts from fits running concurrently on
+ * several streams add up.  Returns ISO_OK, ISO_EINVAL (out NULL) or ISO_EHIP. */
+enum { ISO_PROF_COUNTERS = 4 };
+int iso_prof_counters(uint64_t* out, int reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,17 @@ def test_header_constants_match_binding():
     assert e["ISO_ROW_BAD_WEIGHT"] == binding.ISO_ROW_BAD_WEIGHT
 
 
+def test_profile_header_constants_match_binding():
+    text = open(os.path.join(ROOT, "include", "iso_profile.h")).read()
+    e = {k: int(v) for k, v in re.findall(r"\b(ISO_PROF_[A-Z]+)\s*=\s*([0-9]+)", text)}
+    assert e["ISO_PROF_STAGES"] == binding.ISO_PROF_STAGES
+    assert e["ISO_PROF_COUNTERS"] == binding.ISO_PROF_COUNTERS == len(binding.PROF_COUNTER_NAMES)
+
+
+def test_prof_counters_rejects_null(lib):
+    assert lib.iso_prof_counters(None, 0) == binding.ISO_EINVAL
+
+
 def test_strerror(lib):
     for code in range(6):
         assert binding.iso_strerror(code)

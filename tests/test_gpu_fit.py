@@ -381,3 +381,33 @@ def test_tiny_rows_flags_and_ties():
     np.testing.assert_array_equal(bs[0], [1, 0, 0, 0])
     np.testing.assert_array_equal(z[3], [0.0, 11.0 / 3, 11.0 / 3, 11.0 / 3])
     np.testing.assert_array_equal(bs[3], [1, 1, 0, 0])
+
+
+def test_rare_branches_run_and_stay_exact():
+    """The branches that only degenerate or far-reaching diagrams take, each shown to run (through
+    iso_prof_counters) on a row whose fit is then checked against the oracle:
+    - a cliff (a ramp whose last element is -1e6) pulls the top merge's bridge back over the whole
+      first half, past 32 memory windows, onto the Overmars-van Leeuwen bisection;
+    - sawtooth ramps make merges walk in memory windows;
+    - y alternating 0.5, 1.5 with weights 0.25, 0.75: the candidate points (each 1.5 after a 0.5)
+      are exactly collinear and every sum is exact, so the chain's turns are exactly zero, inside
+      their error bounds, and the exact chunk pass decides them.  The fit is 0.5 for the first
+      element and 1.25 (one pooled block) for the rest."""
+    b = _gpu()
+    b.iso_prof_counters(reset=True)
+    y, w = W.family("cliff", 1, 1 << 20, seed=3, dtype="f64", wkind="uniform")
+    check(y, w, kkt=False)
+    c = b.iso_prof_counters(reset=True)
+    assert c["bisections"] >= 1, c
+    assert c["memory_window_merges"] >= 1, c
+    y, w = W.family("sawtooth", 1, 1 << 20, seed=4, dtype="f32", wkind="unit")
+    check(y, w, kkt=False)
+    c = b.iso_prof_counters(reset=True)
+    assert c["memory_window_merges"] >= 1, c
+    n = 70001
+    y = np.where(np.arange(n) % 2 == 0, 0.5, 1.5).reshape(1, n)
+    w = np.where(np.arange(n) % 2 == 0, 0.25, 0.75).reshape(1, n)
+    z, _ = check(y, w, exact_partition=True)
+    c = b.iso_prof_counters(reset=True)
+    assert c["exact_pass_chunks"] >= 1, c
+    assert z[0, 0] == 0.5 and np.all(z[0, 1:] == 1.25)

@@ -42,8 +42,11 @@ _SIGS = {
     "iso_prof_enable": ([ctypes.c_int], ctypes.c_int),
     "iso_prof_read": ([_P, _P, _P], ctypes.c_int),
     "iso_prof_stage_name": ([ctypes.c_int], ctypes.c_char_p),
+    "iso_prof_counters": ([_P, ctypes.c_int], ctypes.c_int),
 }
 ISO_PROF_STAGES = 7
+ISO_PROF_COUNTERS = 4
+PROF_COUNTER_NAMES = ("bisections", "bisections_finished_by_steps", "exact_pass_chunks", "memory_window_merges")
 
 
 class IsoError(RuntimeError):
@@ -130,6 +133,15 @@ def iso_prof_read():
         raise IsoError(rc, "iso_prof_read")
     names = [load().iso_prof_stage_name(k).decode() for k in range(ISO_PROF_STAGES)]
     return dict(zip(names, list(ms))), dict(zip(names, list(la))), calls.value
+
+
+def iso_prof_counters(reset=True):
+    """Counts of rarely taken branches since the last reset, as {name: count} (waits for the device)."""
+    out = (ctypes.c_uint64 * ISO_PROF_COUNTERS)()
+    rc = load().iso_prof_counters(out, int(bool(reset)))
+    if rc != ISO_OK:
+        raise IsoError(rc, "iso_prof_counters")
+    return dict(zip(PROF_COUNTER_NAMES, list(out)))
 
 
 # ------------------------------------------------------------------ torch marshalling

@@ -609,6 +609,20 @@ int iso_prof_read(double* ms, int64_t* launches, int64_t* calls) {
   return rc;
 }
 
+int iso_prof_counters(uint64_t* out, int reset) {
+  if (!out) return ISO_EINVAL;
+  unsigned long long h[ISO_PROF_COUNTERS];
+  if (hipDeviceSynchronize() != hipSuccess) return ISO_EHIP;
+  if (hipMemcpyFromSymbol(h, HIP_SYMBOL(iso::g_branch_counts), sizeof(h)) != hipSuccess) return ISO_EHIP;
+  for (int i = 0; i < ISO_PROF_COUNTERS; ++i) out[i] = (uint64_t)h[i];
+  if (reset) {
+    const unsigned long long zero[ISO_PROF_COUNTERS] = {};
+    if (hipMemcpyToSymbol(HIP_SYMBOL(iso::g_branch_counts), zero, sizeof(zero)) != hipSuccess) return ISO_EHIP;
+    if (hipDeviceSynchronize() != hipSuccess) return ISO_EHIP;
+  }
+  return ISO_OK;
+}
+
 const char* iso_prof_stage_name(int stage) {
   static const char* names[ISO_PROF_STAGES] = {"increasing", "chunk", "exact", "scan", "merge", "ends", "fit"};
   return (stage >= 0 && stage < ISO_PROF_STAGES) ? names[stage] : "?";

@@ -656,6 +656,7 @@ __global__ __launch_bounds__(64, W ? 2 : 3) void k_chunk(const T* __restrict__ y
   double* ckyl = out.ckyl() + g * (int64_t)(kWave * kLaneW);
   // done by k_increasing (form 2), or by the first pass (forms 0 and 1)
   if (EXACT ? out.dform[g] != 3 : out.dform[g] == 2) return;
+  if (EXACT && lane == 0) atomicAdd(&g_branch_counts[2], 1ull);
 
   // ---- a1-a3: stream the lane's elements through the chain.  Point P_q (0 < q < c) lies between
   // the elements q - 1 and q, whose slopes are y_{q-1} and y_q; unless y_{q-1} < y_q it is not a

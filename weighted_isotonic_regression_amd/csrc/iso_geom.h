@@ -163,6 +163,12 @@ ISO_HD double dd_quot(DD dy, DD dx) {
 
 ISO_HD double slope_dd(const PD& a, const PD& b) { return dd_quot(dd_sub(b.y, a.y), dd_sub(b.x, a.x)); }
 
+// Device-wide counts of rarely taken branches, read and reset by iso_prof_counters: [0] merges of
+// the merge levels that fell back on the Overmars-van Leeuwen bisection, [1] bisections that
+// rounding defeated (finished by single steps), [2] chunks processed by the exact chunk pass,
+// [3] merges that walked in memory windows.  Each is one atomic add by one lane, on its path only.
+__device__ unsigned long long g_branch_counts[4];
+
 // A little above u = 2^-53: the error of a rounded operation relative to its rounded result.
 constexpr double kU = 0x1.0001p-53;
 

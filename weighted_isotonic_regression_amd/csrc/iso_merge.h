@@ -417,6 +417,7 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
       continue;
     }
     // the walk continues in memory, kWalkK * 64 vertices at a time, from where it stands
+    if (lane == 0) atomicAdd(&g_branch_counts[3], 1ull);
     bool searched = false;
     for (int pass = 0; pass < 4 * kChunk; ++pass) {
       bool moved = false;
@@ -457,12 +458,14 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
       // long walk: Overmars-van Leeuwen bisection over the ranges still open (every lane runs the
       // same serial search, reading the same addresses)
       VRef a2, b2;
+      if (lane == 0) atomicAdd(&g_branch_counts[0], 1ull);
       if (bridge_search(S, LA, LB, firstA, al, be, lastB, Sp, a2, b2)) {
         al = a2;
         be = b2;
       } else {
         settled = false;  // rounding defeated the search: finish by single steps
         phase = 2;
+        if (lane == 0) atomicAdd(&g_branch_counts[1], 1ull);
       }
     }
   }
