@@ -228,52 +228,81 @@ __device__ __forceinline__ bool merge_finish_walk(const VS& S, const NodeList& L
   }
 }
 
-// The vertices beyond s on one side (dir -1: towards the list's first vertex, +1: towards its
-// last), up to kWave of them, stopping before the first dense-form segment: lane i gets v_{i+1},
-// the (i+1)-th vertex from s (mine, P) when i < nw.  exhausted: the window reaches the end of the
-// list.  One read of descriptors and one read of points.
+// The vertices beyond s on each side of a merge, up to kWave - 1 of them, stopping before the
+// first dense-form segment: lane i gets v_{i+1}, the (i+1)-th vertex from s (mine, P), towards
+// A's first vertex from sA and towards B's last from sB; n: how many, ex: the window reaches the
+// end of the list.  Both sides are read together, so that their memory and LDS round trips
+// overlap: one read of descriptors, a scan, one wavefront sync, side-by-side searches, one read of
+// points.
 template <class VS>
-__device__ __forceinline__ void side_window(const VS& S, const NodeList& L, int dir, VRef s, int lane,
-                            MergeLds& W, int& nw, bool& exhausted, VRef& mine, GPt& P) {
-  const int u = s.u + dir * lane;
-  const bool inr = dir < 0 ? u >= 0 : u < L.n;
-  Desc dj = make_int4(0, 0, -1, 0);
-  if (inr) dj = L.d[u];
-  const uint64_t dm = __ballot(inr && desc_form(dj) != 0);
-  const int fd = dm ? __builtin_ctzll(dm) : kWave;  // first dense segment
-  int cnt = 0;
-  if (inr && lane < fd) cnt = lane == 0 ? (dir < 0 ? s.p - dj.y : dj.z - s.p) : dj.z - dj.y + 1;
-  int cum = cnt;
+__device__ __forceinline__ void side_windows2(const VS& S, const NodeList& LA, VRef sA, const NodeList& LB,
+                                              VRef sB, int lane, MergeLds& WA, MergeLds& WB, int& na,
+                                              bool& exA, VRef& mineA, GPt& PA, int& nb, bool& exB,
+                                              VRef& mineB, GPt& PB) {
+  const int uA = sA.u - lane, uB = sB.u + lane;
+  const bool inA = uA >= 0, inB = uB < LB.n;
+  Desc dA = make_int4(0, 0, -1, 0), dB = make_int4(0, 0, -1, 0);
+  if (inA) dA = LA.d[uA];
+  if (inB) dB = LB.d[uB];
+  const uint64_t dmA = __ballot(inA && desc_form(dA) != 0), dmB = __ballot(inB && desc_form(dB) != 0);
+  const int fdA = dmA ? __builtin_ctzll(dmA) : kWave, fdB = dmB ? __builtin_ctzll(dmB) : kWave;
+  int cA = 0, cB = 0;
+  if (inA && lane < fdA) cA = lane == 0 ? sA.p - dA.y : dA.z - dA.y + 1;
+  if (inB && lane < fdB) cB = lane == 0 ? dB.z - sB.p : dB.z - dB.y + 1;
+  int cumA = cA, cumB = cB;
 #pragma unroll
   for (int dd = 1; dd < kWave; dd <<= 1) {
-    const int o = __shfl_up(cum, dd, kWave);
-    if (lane >= dd) cum += o;
-  }
-  W.cum[lane] = cum;
-  W.d[lane] = dj;
-  wave_sync();
-  const int total = __shfl(cum, kWave - 1, kWave);
-  nw = min(total, kWave - 1);
-  const bool all_segs = dir < 0 ? (s.u - (kWave - 1) <= 0) : (s.u + (kWave - 1) >= L.n - 1);
-  exhausted = fd == kWave && all_segs && total <= kWave - 1;
-  mine = s;
-  P = GPt{0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  const int want = lane + 1;
-  if (want <= nw) {
-    int lo = 0, hi = kWave - 1;  // smallest j with cum[j] >= want
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (W.cum[mid] >= want) hi = mid;
-      else lo = mid + 1;
+    const int oA = __shfl_up(cumA, dd, kWave), oB = __shfl_up(cumB, dd, kWave);
+    if (lane >= dd) {
+      cumA += oA;
+      cumB += oB;
     }
-    const int before = lo > 0 ? W.cum[lo - 1] : 0;
-    const int k = want - before - 1;  // 0-based from the segment's near end
-    const Desc d = W.d[lo];
-    int rank;
-    if (dir < 0) rank = (lo == 0) ? s.p - 1 - k : d.z - k;
-    else rank = (lo == 0) ? s.p + 1 + k : d.y + k;
-    mine = VRef{s.u + dir * lo, rank};
-    P = S.pt_list(L.row, d.x, rank);
+  }
+  WA.cum[lane] = cumA;
+  WA.d[lane] = dA;
+  WB.cum[lane] = cumB;
+  WB.d[lane] = dB;
+  wave_sync();
+  const int totA = __shfl(cumA, kWave - 1, kWave), totB = __shfl(cumB, kWave - 1, kWave);
+  na = min(totA, kWave - 1);
+  nb = min(totB, kWave - 1);
+  exA = fdA == kWave && (sA.u - (kWave - 1) <= 0) && totA <= kWave - 1;
+  exB = fdB == kWave && (sB.u + (kWave - 1) >= LB.n - 1) && totB <= kWave - 1;
+  mineA = sA;
+  mineB = sB;
+  PA = GPt{0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  PB = PA;
+  const int want = lane + 1;
+  // smallest j with cum[j] >= want, on both tables side by side
+  int loA = 0, hiA = kWave - 1, loB = 0, hiB = kWave - 1;
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int midA = (loA + hiA) >> 1, midB = (loB + hiB) >> 1;
+    const int vA = WA.cum[midA], vB = WB.cum[midB];
+    if (loA < hiA) {
+      if (vA >= want) hiA = midA;
+      else loA = midA + 1;
+    }
+    if (loB < hiB) {
+      if (vB >= want) hiB = midB;
+      else loB = midB + 1;
+    }
+  }
+  if (want <= na) {
+    const int before = loA > 0 ? WA.cum[loA - 1] : 0;
+    const int k = want - before - 1;
+    const Desc d = WA.d[loA];
+    const int rank = (loA == 0) ? sA.p - 1 - k : d.z - k;
+    mineA = VRef{sA.u - loA, rank};
+    PA = S.pt_list(LA.row, d.x, rank);
+  }
+  if (want <= nb) {
+    const int before = loB > 0 ? WB.cum[loB - 1] : 0;
+    const int k = want - before - 1;
+    const Desc d = WB.d[loB];
+    const int rank = (loB == 0) ? sB.p + 1 + k : d.y + k;
+    mineB = VRef{sB.u + loB, rank};
+    PB = S.pt_list(LB.row, d.x, rank);
   }
 }
 
@@ -292,8 +321,7 @@ __device__ __forceinline__ bool window_bridge(const VS& S, const NodeList& LA, c
   bool exA, exB;
   VRef ra, rb;
   GPt PA, PB;
-  side_window(S, LA, -1, list_last(LA), lane, WA, na, exA, ra, PA);
-  side_window(S, LB, +1, list_first(LB), lane, WB, nb, exB, rb, PB);
+  side_windows2(S, LA, list_last(LA), LB, list_first(LB), lane, WA, WB, na, exA, ra, PA, nb, exB, rb, PB);
   al = list_last(LA);
   Pa = Sp;
   if (nb < 1) {  // (no list-form vertex after s in B's window)
