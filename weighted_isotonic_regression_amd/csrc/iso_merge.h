@@ -238,12 +238,14 @@ template <class VS>
 __device__ __forceinline__ void side_windows2(const VS& S, const NodeList& LA, VRef sA, const NodeList& LB,
                                               VRef sB, int lane, MergeLds& WA, MergeLds& WB, int& na,
                                               bool& exA, VRef& mineA, GPt& PA, int& nb, bool& exB,
-                                              VRef& mineB, GPt& PB) {
+                                              VRef& mineB, GPt& PB, GPt& Ps) {
   const int uA = sA.u - lane, uB = sB.u + lane;
   const bool inA = uA >= 0, inB = uB < LB.n;
   Desc dA = make_int4(0, 0, -1, 0), dB = make_int4(0, 0, -1, 0);
   if (inA) dA = LA.d[uA];
   if (inB) dB = LB.d[uB];
+  // s itself (vertex sA.p of A's last segment), read while the windows are located
+  Ps = S.pt_desc(LA.row, LA.d[sA.u], sA.p);
   const uint64_t dmA = __ballot(inA && desc_form(dA) != 0), dmB = __ballot(inB && desc_form(dB) != 0);
   const int fdA = dmA ? __builtin_ctzll(dmA) : kWave, fdB = dmB ? __builtin_ctzll(dmB) : kWave;
   int cA = 0, cB = 0;
@@ -315,13 +317,13 @@ __device__ __forceinline__ void side_windows2(const VS& S, const NodeList& LA, V
 // memory.
 template <class VS>
 __device__ __forceinline__ bool window_bridge(const VS& S, const NodeList& LA, const NodeList& LB, int lane,
-                              MergeLds& WA, MergeLds& WB, const GPt& Sp, VRef& al, VRef& be,
+                              MergeLds& WA, MergeLds& WB, GPt& Sp, VRef& al, VRef& be,
                               GPt& Pa, GPt& Pb) {
   int na, nb;
   bool exA, exB;
   VRef ra, rb;
   GPt PA, PB;
-  side_windows2(S, LA, list_last(LA), LB, list_first(LB), lane, WA, WB, na, exA, ra, PA, nb, exB, rb, PB);
+  side_windows2(S, LA, list_last(LA), LB, list_first(LB), lane, WA, WB, na, exA, ra, PA, nb, exB, rb, PB, Sp);
   al = list_last(LA);
   Pa = Sp;
   if (nb < 1) {  // (no list-form vertex after s in B's window)
@@ -405,7 +407,7 @@ __device__ __forceinline__ void merge_pair(const VertexStore<T, W, D>& S, int64_
   const VRef lastB = list_last(LB);
   VRef al, be;
   GPt Pa, Pb;
-  const GPt Sp = load_v(S, LA, list_last(LA));
+  GPt Sp;  // the shared point s, A's last vertex (read by window_bridge)
   bool settled = window_bridge(S, LA, LB, lane, WA, WB, Sp, al, be, Pa, Pb);
   if (!settled) {
     // both walks may already stop where the windows ended (always the case at a strictly convex
