@@ -377,11 +377,11 @@ def summarize_pmc(fetch_dir, write_dir):
             return (args[-1].strip() == "true") == (key == "k_chunk_exact")
         return ("iso::%s<" % key) in k or ("iso::%s(" % key) in k
 
-    # fit calls in the run: one k_chunk (long rows), k_wave (short rows) or k_tiny dispatch each
+    # fit calls in the run: one k_chunk (long rows), k_row, k_wave (short rows) or k_tiny dispatch each
     calls = max(sum(len(vs) for k, vs in fetch.items() if mine(k, "k_chunk") or mine(k, "k_wave") or
-                    mine(k, "k_tiny")), 1)
+                    mine(k, "k_row") or mine(k, "k_tiny")), 1)
     lines = []
-    for key in ("k_tiny", "k_wave", "k_increasing", "k_chunk", "k_chunk_exact", "k_scan_reduce", "k_scan_apply",
+    for key in ("k_tiny", "k_wave", "k_row", "k_increasing", "k_chunk", "k_chunk_exact", "k_scan_reduce", "k_scan_apply",
                 "k_merge_levels", "k_ends", "k_fit"):
         fs = [v for k, vs in fetch.items() if mine(k, key) for v in vs]
         wsz = [v for k, vs in write.items() if mine(k, key) for v in vs]

@@ -2,9 +2,10 @@
 //
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
 //   n <= 16     four lanes per row, pool adjacent violators in registers and LDS (k_tiny)
-//   n <= 4096   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront (rows
-//               over 2048: one row per workgroup of 2 wavefronts); one launch of k_wave
-//               writes z, block starts and row flags (Section 3.5).
+//   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
+//               launch of k_wave writes z, block starts and row flags (Section 3.5).
+//   n <= 4096   one row per workgroup of 1024 threads, its diagram in LDS, merged level by level
+//               with candidate-parallel bridge searches (k_row, iso_row.h).
 //   n >  4096   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
 //               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls; a
 //               second, exact instantiation takes the chunks whose fast turns left one undecided),
@@ -31,6 +32,7 @@
 #include "iso_chunk.h"
 #include "iso_merge.h"
 #include "iso_ragged.h"
+#include "iso_row.h"
 #include "iso_softrank.h"
 
 // The fixed scratch of iso_fit_noalloc: one copy on every GPU the library runs on, kept until the
@@ -194,6 +196,13 @@ int scratch_address(hipStream_t s, void** out) {
   return ISO_OK;
 }
 
+// Rows of 2049 to 4096 elements go one to a workgroup of 1024 threads (k_row), where a thread's
+// chain is four points long and the merges search their bridges with many threads at once.
+bool row_kernel(int64_t batch, int64_t n) {
+  (void)batch;
+  return n > kShortMax / 2;
+}
+
 int lanes_per_row(int64_t n) {
   int need = (int)((n + kLanePts - 1) / kLanePts);
   int L = 1;
@@ -215,13 +224,13 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   if (!long_rows(n)) {
     const int L = lanes_per_row(n);
     prof.skip();
-    if (L <= kWave) {
+    if (row_kernel(batch, n)) {
+      hipLaunchKernelGGL((k_row<T, W, D>), dim3((unsigned)batch), dim3(kRowThreads), 0, s, y, w, z, bstart,
+                         rflags, (int)n);
+    } else {
       const int R = kWave / L;
       const int64_t tiles = (batch + R - 1) / R;
-      hipLaunchKernelGGL((k_wave<T, W, D, 1>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
-                         rflags, batch, n, L);
-    } else {  // one row per workgroup of two wavefronts
-      hipLaunchKernelGGL((k_wave<T, W, D, 2>), dim3((unsigned)batch), dim3(2 * kWave), 0, s, y, w, z, bstart,
+      hipLaunchKernelGGL((k_wave<T, W, D>), dim3((unsigned)tiles), dim3(kWave), 0, s, y, w, z, bstart,
                          rflags, batch, n, L);
     }
     prof.mark(1);

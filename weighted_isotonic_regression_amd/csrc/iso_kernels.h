@@ -2,12 +2,14 @@
 //
 // Pipeline ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 3):
 //   k_tiny          rows of at most 16 elements, four lanes per row: pool adjacent violators.
-//   k_wave          rows of 17 to 4096 elements, packed L = 1, 2, .., 64 lanes per row and
-//                   64 / L rows per wavefront (Section 3.5), a row of more than 2048 over two
-//                   wavefronts: coalesced 16-byte loads, double-double cumulative sums in LDS
+//   k_wave          rows of 17 to 2048 elements, packed L = 1, 2, .., 64 lanes per row and
+//                   64 / L rows per wavefront (Section 3.5): coalesced 16-byte loads,
+//                   double-double cumulative sums in LDS
 //                   (lane-serial, then a wave scan of lane totals), lane hulls by the bit-mask
 //                   monotone chain (Section 3.1), pairwise walks merging lane hulls (Section 3.2);
 //                   writes z and block starts.
+//   k_row           (iso_row.h) rows of 2049 to 4096 elements, one per workgroup of 1024
+//                   threads, with candidate-parallel bridge searches.
 //   k_chunk         (iso_chunk.h) the chunk pass of longer rows.
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
@@ -31,14 +33,9 @@ namespace iso {
 // 0..len occupy raw LDS indices r * (32 L + 1) + k; raw index i is stored at lds_pad(i) to
 // spread a lane's 32 consecutive points over the banks.  Element i's increment (w_i, w_i y_i)
 // is staged at the slot of its left point i and replaced by that point's coordinates.
-// A workgroup of NW > 1 wavefronts holds one row of up to 2048 NW elements (L = 64 NW lanes).
 constexpr int kRawPts = kWave * (kLanePts + 1);           // 2112 = max R (32 L + 1)
 constexpr int kLdsPts = kRawPts + (kRawPts >> 5) + 8;     // padded
 constexpr int kMaskWords = 2 * kWave + 8;                 // R (L + 1) <= 128
-constexpr int lds_pts(int nw) {
-  return nw == 1 ? kLdsPts : (kLanePts * kWave * nw + 1) + ((kLanePts * kWave * nw + 1) >> 5) + 8;
-}
-constexpr int mask_words(int nw) { return nw == 1 ? kMaskWords : kWave * nw + 1 + 8; }
 
 __device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
 
@@ -183,21 +180,20 @@ struct TilePairs {
   }
 };
 
-// Rows of 17 to 4096 elements.  Points are pairs (hi in sX/sY, lo in sXl/sYl): the lane's start,
+// Rows of 17 to 2048 elements.  Points are pairs (hi in sX/sY, lo in sXl/sYl): the lane's start,
 // from a double-double scan of the lane totals, plus the lane's running sums.  A fast turn is
 // used when it exceeds 2^-47 X Y, X the row's total weight (or length) and Y its sum of |w y|:
 // every hi part is within u of its pair's magnitude (at most X or Y), so the fast turn of three
 // points is within 26 u X Y of the turn of the pairs.  Slopes come from the pairs.
-template <typename T, bool W, bool D, int NW>
-__global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
+template <typename T, bool W, bool D>
+__global__ __launch_bounds__(kWave) void k_wave(const T* __restrict__ y, const T* __restrict__ w,
                                                      T* __restrict__ z, uint8_t* __restrict__ bstart,
                                                      uint32_t* __restrict__ rflags, int64_t batch,
                                                      int64_t n, int Lpack) {
-  static_assert(NW == 1 || NW == 2, "rows of at most 4096 elements");
   constexpr bool EX = ExactProd<T, W>::value;
-  constexpr int kThreads = NW * kWave;
-  constexpr int kPts = lds_pts(NW);
-  constexpr int kMW = mask_words(NW);
+  constexpr int kThreads = kWave;
+  constexpr int kPts = kLdsPts;
+  constexpr int kMW = kMaskWords;
   __shared__ double sX[W ? kPts : 1];
   __shared__ double sY[kPts];
   __shared__ double sXl[W ? kPts : 1];
@@ -205,7 +201,6 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
   __shared__ uint32_t sM[kMW];
   __shared__ int sLst[kMW], sFst[kMW];  // per mask word: last vertex at or before it, first at or after
   __shared__ uint32_t sF[kWave];
-  __shared__ double sWave[6 * NW];  // per wavefront: lane-total sums, then their prefixes
 
   constexpr int VN = Vec16<T>::N;
   const int lane = threadIdx.x;
@@ -314,76 +309,21 @@ __global__ __launch_bounds__(NW * kWave) void k_wave(const T* __restrict__ y, co
     ty = two_sum(ty.hi, ty.lo);
     DD ix = tx, iy = ty, sx0, sy0;
     double xr = tx.hi, ar = ta;  // row sums of the lane totals (for the bound)
-    if constexpr (NW == 1) {
-      for (int d = 1; d < L; d <<= 1) {
-        const DD vx{__shfl_up(ix.hi, d, L), __shfl_up(ix.lo, d, L)};
-        const DD vy{__shfl_up(iy.hi, d, L), __shfl_up(iy.lo, d, L)};
-        if (ql >= d) {
-          ix = dd_add(vx, ix);
-          iy = dd_add(vy, iy);
-        }
-        xr += __shfl_xor(xr, d, L);
-        ar += __shfl_xor(ar, d, L);
+    for (int d = 1; d < L; d <<= 1) {
+      const DD vx{__shfl_up(ix.hi, d, L), __shfl_up(ix.lo, d, L)};
+      const DD vy{__shfl_up(iy.hi, d, L), __shfl_up(iy.lo, d, L)};
+      if (ql >= d) {
+        ix = dd_add(vx, ix);
+        iy = dd_add(vy, iy);
       }
-      sx0 = DD{__shfl_up(ix.hi, 1, L), __shfl_up(ix.lo, 1, L)};
-      sy0 = DD{__shfl_up(iy.hi, 1, L), __shfl_up(iy.lo, 1, L)};
-      if (ql == 0) {
-        sx0 = DD{0.0, 0.0};
-        sy0 = DD{0.0, 0.0};
-      }
-    } else {
-      // one row over NW wavefronts: a scan in each, then the wavefronts' prefixes in turn
-      const int wl = lane & (kWave - 1), wv = lane / kWave;
-      for (int d = 1; d < kWave; d <<= 1) {
-        const DD vx{__shfl_up(ix.hi, d, kWave), __shfl_up(ix.lo, d, kWave)};
-        const DD vy{__shfl_up(iy.hi, d, kWave), __shfl_up(iy.lo, d, kWave)};
-        if (wl >= d) {
-          ix = dd_add(vx, ix);
-          iy = dd_add(vy, iy);
-        }
-        xr += __shfl_xor(xr, d, kWave);
-        ar += __shfl_xor(ar, d, kWave);
-      }
-      DD ex{__shfl_up(ix.hi, 1, kWave), __shfl_up(ix.lo, 1, kWave)};
-      DD ey{__shfl_up(iy.hi, 1, kWave), __shfl_up(iy.lo, 1, kWave)};
-      if (wl == kWave - 1) {
-        sWave[6 * wv + 0] = ix.hi;
-        sWave[6 * wv + 1] = ix.lo;
-        sWave[6 * wv + 2] = iy.hi;
-        sWave[6 * wv + 3] = iy.lo;
-      }
-      if (wl == 0) {
-        sWave[6 * wv + 4] = xr;
-        sWave[6 * wv + 5] = ar;
-      }
-      __syncthreads();
-      if (lane == 0) {
-        DD px{0.0, 0.0}, py{0.0, 0.0};
-        for (int v = 0; v < NW; ++v) {
-          const DD tvx{sWave[6 * v + 0], sWave[6 * v + 1]}, tvy{sWave[6 * v + 2], sWave[6 * v + 3]};
-          sWave[6 * v + 0] = px.hi;
-          sWave[6 * v + 1] = px.lo;
-          sWave[6 * v + 2] = py.hi;
-          sWave[6 * v + 3] = py.lo;
-          px = dd_add(px, tvx);
-          py = dd_add(py, tvy);
-        }
-      }
-      __syncthreads();
-      const DD px{sWave[6 * wv + 0], sWave[6 * wv + 1]}, py{sWave[6 * wv + 2], sWave[6 * wv + 3]};
-      xr = 0.0;
-      ar = 0.0;
-      for (int v = 0; v < NW; ++v) {
-        xr += sWave[6 * v + 4];
-        ar += sWave[6 * v + 5];
-      }
-      if (wl == 0) {
-        sx0 = px;
-        sy0 = py;
-      } else {
-        sx0 = dd_add(px, ex);
-        sy0 = dd_add(py, ey);
-      }
+      xr += __shfl_xor(xr, d, L);
+      ar += __shfl_xor(ar, d, L);
+    }
+    sx0 = DD{__shfl_up(ix.hi, 1, L), __shfl_up(ix.lo, 1, L)};
+    sy0 = DD{__shfl_up(iy.hi, 1, L), __shfl_up(iy.lo, 1, L)};
+    if (ql == 0) {
+      sx0 = DD{0.0, 0.0};
+      sy0 = DD{0.0, 0.0};
     }
     Erow = ((W ? xr : (double)seglen) * 0x1p-47) * ar;
     DD lx{0.0, 0.0}, ly{0.0, 0.0};
