@@ -6,11 +6,12 @@
  * the same breakdown on the caller's stream with HIP events, so a benchmark can time the
  * dominant kernel inside its own timed region.
  *
- * Stages: 0 whole-diagram chunks (k_increasing), 1 chunk pass (k_chunk; k_wave for rows of at
- * most 4096 elements, k_tiny for rows of at most 16), 2 exact chunk pass (k_chunk on the chunks
- * whose turns the first pass could not decide), 3 chunk-start scan (2 launches), 4 merge levels
- * (three levels of the tree per launch: ceil(ceil(log2 m) / 3) launches for m chunks), 5 ends,
- * 6 fit.  Rows of at most 4096 elements run stage 1 only.
+ * Stages: 0 whole-diagram chunks (k_increasing), 1 chunk pass (k_chunk; for rows of at most 4096
+ * elements the one kernel that fits them: k_row, k_wave or k_tiny), 2 exact chunk
+ * pass (k_chunk on the chunks whose turns the first pass could not decide), 3 chunk-start scan
+ * (2 launches; 1 for rows of at most 1024 chunks), 4 merge levels (three levels of the tree per
+ * launch: ceil(ceil(log2 m) / 3) launches for m chunks), 5 ends, 6 fit.  Rows of at most 4096
+ * elements run stage 1 only.
  *
  * While enabled, every iso_fit_ex call records one event before its first kernel and one after
  * each stage, on its stream.  The state is process-global and not thread-safe: enable, run the

@@ -1,8 +1,9 @@
-"""GPU parity of rows of 2049 to 4096 elements, each fitted by one workgroup of 1024 threads with
-the diagram in LDS and candidate-parallel bridge searches: every test family, weight kind,
-direction and element type against the oracle (fp64 1e-10, fp32 1e-6, identical block starts
-where the partition is exact), rows that start off 16-byte alignment, all-vertex rows, and
-batches."""
+"""GPU parity of the one-row-per-workgroup kernel (1024 threads, the diagram in LDS,
+candidate-parallel bridge searches), which fits rows of 2049 to 4096 elements and shorter rows in
+batches of at most 256: every test family, weight kind, direction and element type against the
+oracle (fp64 1e-10, fp32 1e-6, identical block starts where the partition is exact), rows that
+start off 16-byte alignment, all-vertex rows, and batches.  Larger batches of rows of at most 2048
+go to the packed short-row kernel, checked here too."""
 import numpy as np
 import pytest
 
@@ -80,3 +81,30 @@ def test_row_integer_partitions_exact():
         check(y, w, exact_partition=True)
         y, w = W.calibration(seed=n, batch=2, n=n)
         check(y, w, exact_partition=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("fam", W.FAMILIES)
+def test_row_short_rows_small_batches(fam, dtype):
+    """Rows of 17 to 2048 elements in batches of at most 256 (one workgroup per row, most threads
+    without elements), both directions."""
+    cancel = fam == "cancel"
+    for n, batch in ((17, 1), (33, 256), (64, 5), (100, 3), (257, 2), (1000, 2), (2047, 1), (2048, 3)):
+        for wk in ("unit", "uniform", "extreme"):
+            y, w = W.family(fam, batch, n, seed=n + batch, dtype=dtype, wkind=wk)
+            tol = (1.4e-15 if dtype == "f64" else 1e-7) if cancel else None
+            exact = fam in ("integer", "constant") and wk == "unit"
+            for dec in (False, True):
+                check(y, None if wk == "unit" else w, exact_partition=exact, tol=tol, kkt=not cancel,
+                      scale_abs=cancel, decreasing=dec)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_packed_short_rows_large_batches(dtype):
+    """Batches of more than 256 rows of 17 to 2048 elements: 64 / L rows packed per wavefront of the
+    short-row kernel, a last wavefront partly filled."""
+    for n, batch in ((17, 1000), (31, 257), (100, 300), (513, 301), (1000, 300), (2048, 257)):
+        for fam, wk in (("noise", "uniform"), ("sawtooth", "unit"), ("integer", "integer")):
+            y, w = W.family(fam, batch, n, seed=n, dtype=dtype, wkind=wk)
+            check(y, None if wk == "unit" else w, exact_partition=fam == "integer")
+            check(y, w, decreasing=True)

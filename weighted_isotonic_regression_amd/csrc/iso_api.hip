@@ -2,14 +2,16 @@
 //
 // Paths (by row length n; "Merge Hulls Without Copying Vertices", Section 3 and 6):
 //   n <= 16     four lanes per row, pool adjacent violators in registers and LDS (k_tiny)
-//   n <= 2048   rows packed L = 1, 2, ..., 64 lanes per row, 64 / L rows per wavefront; one
-//               launch of k_wave writes z, block starts and row flags (Section 3.5).
 //   n <= 4096   one row per workgroup of 1024 threads, its diagram in LDS, merged level by level
-//               with candidate-parallel bridge searches (k_row, iso_row.h).
+//               with candidate-parallel bridge searches (k_row, iso_row.h); rows of at most 2048
+//               in batches of more than 256 instead packed L = 1, 2, ..., 64 lanes per row,
+//               64 / L rows per wavefront (k_wave).  Either launch writes z, block starts and
+//               row flags (Section 3.5).
 //   n >  4096   rows split into chunks of 16384 (one wavefront each, 256 points per lane):
 //               k_increasing (chunks whose diagram is its own hull), k_chunk (chunk hulls; a
 //               second, exact instantiation takes the chunks whose fast turns left one undecided),
-//               k_scan_reduce + k_scan_apply (chunk starts),
+//               k_scan_reduce + k_scan_apply (chunk starts; k_scan_apply alone for rows of at
+//               most 1024 chunks),
 //               ceil(ceil(log2 m) / 3) launches of k_merge_levels, k_ends, k_fit
 //               (Section 3.3 and 3.4).
 // Rows of unequal lengths (iso_fit_ragged) are bucketed by length, padded into a rectangular
@@ -197,11 +199,12 @@ int scratch_address(hipStream_t s, void** out) {
 }
 
 // Rows of 2049 to 4096 elements go one to a workgroup of 1024 threads (k_row), where a thread's
-// chain is four points long and the merges search their bridges with many threads at once.
-bool row_kernel(int64_t batch, int64_t n) {
-  (void)batch;
-  return n > kShortMax / 2;
-}
+// chain is four points long and the merges search their bridges with many threads at once; so do
+// shorter rows in batches of at most kRowBatch, which k_row finishes in one round of workgroups
+// (256 CUs) in less time than one k_wave wavefront takes.  Larger batches of shorter rows pack
+// 64 / L rows per k_wave wavefront.
+constexpr int64_t kRowBatch = 256;
+bool row_kernel(int64_t batch, int64_t n) { return n > kShortMax / 2 || batch <= kRowBatch; }
 
 int lanes_per_row(int64_t n) {
   int need = (int)((n + kLanePts - 1) / kLanePts);
@@ -271,11 +274,16 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
   prof.mark(1);
   hipLaunchKernelGGL((k_chunk<T, W, D, true>), dim3((unsigned)G), dim3(kWave), 0, s, y, w, z, n, m, co);
   prof.mark(1);
-  hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
-                     s, co.tot, co.tot + G, co.cflags, bsum, bflag, m, nblk);
-  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
-                     co.tot, co.tot + G, bsum, bflag, start, rflags, m, nblk);
-  prof.mark(2);
+  if (nblk == 1) {  // rows of at most kScanBlock chunks: one launch
+    hipLaunchKernelGGL(k_scan_apply<true>, dim3((unsigned)batch), dim3(kScanThreads), 0, s, co.tot, co.tot + G,
+                       bsum, bflag, co.cflags, start, rflags, m, nblk);
+  } else {
+    hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0,
+                       s, co.tot, co.tot + G, co.cflags, bsum, bflag, m, nblk);
+    hipLaunchKernelGGL(k_scan_apply<false>, dim3((unsigned)(nblk * batch)), dim3(kScanThreads), 0, s,
+                       co.tot, co.tot + G, bsum, bflag, co.cflags, start, rflags, m, nblk);
+  }
+  prof.mark(nblk == 1 ? 1 : 2);
   VertexStore<T, W, D> S;
   S.desc = co.desc;
   S.nseg = co.nseg;

@@ -2,14 +2,14 @@
 //
 // Pipeline ("Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Section 3):
 //   k_tiny          rows of at most 16 elements, four lanes per row: pool adjacent violators.
-//   k_wave          rows of 17 to 2048 elements, packed L = 1, 2, .., 64 lanes per row and
-//                   64 / L rows per wavefront (Section 3.5): coalesced 16-byte loads,
+//   k_wave          batches of more than 256 rows of 17 to 2048 elements, packed L = 1, 2, .., 64
+//                   lanes per row and 64 / L rows per wavefront (Section 3.5): coalesced 16-byte loads,
 //                   double-double cumulative sums in LDS
 //                   (lane-serial, then a wave scan of lane totals), lane hulls by the bit-mask
 //                   monotone chain (Section 3.1), pairwise walks merging lane hulls (Section 3.2);
 //                   writes z and block starts.
-//   k_row           (iso_row.h) rows of 2049 to 4096 elements, one per workgroup of 1024
-//                   threads, with candidate-parallel bridge searches.
+//   k_row           (iso_row.h) rows of 2049 to 4096 elements, and shorter rows in batches of at
+//                   most 256: one row per workgroup of 1024 threads, candidate-parallel bridges.
 //   k_chunk         (iso_chunk.h) the chunk pass of longer rows.
 //   k_scan_reduce / k_scan_apply   double-double exclusive scan of the chunk totals: the chunk
 //                   starts of the coordinate hierarchy (Section 3.3 and Section 6 "Coordinates").
@@ -698,19 +698,36 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const double2* __r
   if (t == 0) bflag[row * nblk + b] = sf;
 }
 
+// ONE: a row of at most kScanBlock chunks, scanned by this kernel alone (no block sums; the
+// chunk flags are gathered here).
+template <bool ONE>
 __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __restrict__ tot,
                                                              const double2* __restrict__ totl,
                                                              const double4* __restrict__ bsum,
                                                              const uint32_t* __restrict__ bflag,
+                                                             const uint32_t* __restrict__ cflags,
                                                              double4* __restrict__ start,
                                                              uint32_t* __restrict__ rflags, int m,
                                                              int nblk) {
   __shared__ double sh[4 * kScanThreads];
   __shared__ double soff[4];
+  __shared__ uint32_t sf;
   const int64_t row = blockIdx.x / nblk;  // one-dimensional grid: batch * nblk blocks
   const int b = (int)(blockIdx.x - row * nblk);
   const int t = threadIdx.x;
-  if (t == 0) {
+  if (ONE) {
+    if (t == 0) {
+      soff[0] = soff[1] = soff[2] = soff[3] = 0.0;
+      sf = 0u;
+    }
+    __syncthreads();
+    uint32_t f = 0u;
+    for (int k = 0; k < kScanPer; ++k) {
+      const int jj = kScanPer * t + k;
+      if (jj < m) f |= cflags[row * m + jj];
+    }
+    if (f) atomicOr(&sf, f);
+  } else if (t == 0) {
     DD2 o{{0.0, 0.0}, {0.0, 0.0}};
     uint32_t f = 0u;
     for (int k = 0; k < nblk; ++k) {
@@ -735,7 +752,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const double2* __re
     }
     loc[k + 1] = dd2_add(loc[k], v);
   }
-  DD2 incl = block_scan_incl(loc[kScanPer], sh);
+  DD2 incl = block_scan_incl(loc[kScanPer], sh);  // (its barriers also publish soff and sf)
+  if (ONE && t == 0 && rflags) rflags[row] = sf;
   // exclusive prefix of this thread = inclusive of the previous thread
   __syncthreads();
   sh[4 * t + 0] = incl.x.hi;

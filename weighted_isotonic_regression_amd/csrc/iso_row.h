@@ -1,10 +1,11 @@
-// iso_row.h -- one row of up to 4096 elements per workgroup of 1024 threads (gfx950).
+// iso_row.h -- one row of up to 4096 elements per workgroup of 1024 threads (gfx950): rows of
+// 2049 to 4096 elements, and shorter rows in batches too small to fill the chip otherwise.
 //
 // "Merge Hulls Without Copying Vertices: GPU Isotonic Regression":
 //   Section 2      the fit is the slope sequence of the lower convex hull of the cumulative sum
 //                  diagram (CSD) of (w, w y).
-//   Section 3.1    each thread builds the hull of its own four elements' points by the monotone
-//                  chain.
+//   Section 3.1    each thread builds the hull of its own four elements' points (an inner point
+//                  is a vertex iff it lies strictly below the segment of every pair around it).
 //   Section 3.2 / Lemma 4.2   neighbouring hulls are merged pairwise, level by level, by their
 //                  bridge: alpha the leftmost contact in the left hull, beta the rightmost in the
 //                  right one, the vertices between them dropped.
