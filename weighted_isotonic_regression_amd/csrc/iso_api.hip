@@ -228,7 +228,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     const int L = lanes_per_row(n);
     prof.skip();
     if (row_kernel(batch, n)) {
-      hipLaunchKernelGGL((k_row<T, W, D>), dim3((unsigned)batch), dim3(kRowThreads), 0, s, y, w, z, bstart,
+      hipLaunchKernelGGL((k_row<T, W, D, kRowP>), dim3((unsigned)batch), dim3(kRowMax / kRowP), 0, s, y, w, z, bstart,
                          rflags, (int)n);
     } else {
       const int R = kWave / L;

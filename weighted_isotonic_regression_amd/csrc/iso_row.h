@@ -33,16 +33,16 @@
 
 namespace iso {
 
-constexpr int kRowThreads = 1024;
-constexpr int kRowPer = 4;                            // elements per thread
-constexpr int kRowMax = kRowThreads * kRowPer;        // 4096
-constexpr int kRowCol = kRowThreads + 1;              // slots of one point residue mod 4
-constexpr int kRowSlots = kRowPer * kRowCol;          // point slots (points 0..n)
-constexpr int kRowWaves = kRowThreads / kWave;
+constexpr int kRowMax = 4096;  // elements of a row at most
+// Elements per thread of the launched kernel (kRowMax / kRowP threads).  Measured per call on a
+// 1 x 4096 fp64 weighted row: 4 elements 41.9 us, 8 elements 42.6 us, 16 elements 57.0 us (longer
+// chains in fewer threads lose to more levels of parallel bridge searches).
+constexpr int kRowP = 4;
 
-// LDS slot of point i: residue-major, so four consecutive points of a thread are a column apart
-// and a wavefront's threads touch consecutive slots.
-__device__ __forceinline__ int row_slot(int i) { return (i & (kRowPer - 1)) * kRowCol + (i >> 2); }
+// LDS slot of point i with P points per thread: residue-major, so a thread's consecutive points
+// are a column (kRowMax / P + 1 slots) apart and a wavefront's threads touch consecutive slots.
+template <int P>
+__device__ __forceinline__ int row_slot(int i) { return (i & (P - 1)) * (kRowMax / P + 1) + i / P; }
 
 // A double moved by a DPP control; a lane whose source the control does not reach reads 0.
 template <int CTRL>
@@ -90,11 +90,16 @@ __device__ __forceinline__ DD wave_scan(DD a, int row) {
   return a;
 }
 
-template <typename T, bool W, bool D>
-__global__ __launch_bounds__(kRowThreads) void k_row(const T* __restrict__ y, const T* __restrict__ w,
+template <typename T, bool W, bool D, int P>
+__global__ __launch_bounds__(kRowMax / P) void k_row(const T* __restrict__ y, const T* __restrict__ w,
                                                       T* __restrict__ z, uint8_t* __restrict__ bstart,
                                                       uint32_t* __restrict__ rflags, int n) {
   constexpr bool EX = ExactProd<T, W>::value;
+  constexpr int kRowPer = P;
+  constexpr int kRowThreads = kRowMax / P;
+  constexpr int kRowWaves = kRowThreads / kWave;
+  constexpr int kRowSlots = P * (kRowThreads + 1);
+  static_assert(P == 4 || P == 8 || P == 16, "4, 8 or 16 elements per thread");
   // points: weighted rows keep (x, y) hi parts together (one 16-byte read) and the lo parts
   // apart; unweighted rows keep y only (x is the index)
   __shared__ double2 sH[W ? kRowSlots : 1], sLo[W ? kRowSlots : 1];
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(kRowThreads) void k_row(const T* __restrict__ y, co
   __shared__ uint16_t sC[2][kRowThreads];      // vertex counts: node k of level r at k 2^r
   __shared__ uint32_t sMin[kRowThreads];       // per merge group: level-tagged smallest (alpha, beta)
   __shared__ uint32_t sMax[kRowThreads];       // per merge group: level-tagged largest (alpha, beta)
-  __shared__ double sW[kRowWaves][5];          // per wavefront: sums of the thread totals
+  __shared__ double sW[16][5];                 // per wavefront: sums of the thread totals
   __shared__ uint32_t sFlag;
 
   const int t = threadIdx.x;
@@ -192,10 +197,11 @@ __global__ __launch_bounds__(kRowThreads) void k_row(const T* __restrict__ y, co
   DD px{0.0, 0.0}, py{0.0, 0.0};
   double xr, ar;
   {
-    const int v = wl & (kRowWaves - 1);
-    const DD qx = W ? row_scan(DD{sW[v][0], sW[v][1]}) : DD{0.0, 0.0};
-    const DD qy = row_scan(DD{sW[v][2], sW[v][3]});
-    ar = row_scan(sW[v][4]);
+    const int v = wl & 15;
+    const bool on = v < kRowWaves;
+    const DD qx = W ? row_scan(on ? DD{sW[v][0], sW[v][1]} : DD{0.0, 0.0}) : DD{0.0, 0.0};
+    const DD qy = row_scan(on ? DD{sW[v][2], sW[v][3]} : DD{0.0, 0.0});
+    ar = row_scan(on ? sW[v][4] : 0.0);
     xr = lane_value(qx.hi, 15);
     ar = lane_value(ar, 15);
     const int src = __builtin_amdgcn_readfirstlane(wv > 0 ? wv - 1 : 0);
@@ -212,14 +218,13 @@ __global__ __launch_bounds__(kRowThreads) void k_row(const T* __restrict__ y, co
   const double E = ((W ? xr : (double)n) * 0x1p-47) * ar;  // the row's turn bound
 
   // ---- points e0 .. e0 + c as pairs (the row's end point n written by the thread of its last
-  // element).  Point i sits at slot (i mod 4) * kRowCol + i / 4, so that the threads of a
-  // wavefront touch consecutive slots.
+  // element), at their residue-major slots.
   {
     DD lx{0.0, 0.0}, ly{0.0, 0.0};
 #pragma unroll
     for (int k = 0; k <= kRowPer; ++k) {
       if (k < c || (k == c && c > 0 && e0 + c == n)) {
-        const int i = row_slot(e0 + k);
+        const int i = row_slot<P>(e0 + k);
         const DD Y = dd_add(sy0, ly);
         if constexpr (W) {
           const DD X = dd_add(sx0, lx);
@@ -243,12 +248,12 @@ __global__ __launch_bounds__(kRowThreads) void k_row(const T* __restrict__ y, co
 
   // point i of the diagram (hi parts, and as a pair); x of an unweighted point is its index
   auto hp = [&](int i) -> double2 {
-    const int u = row_slot(i);
+    const int u = row_slot<P>(i);
     if constexpr (W) return sH[u];
     else return make_double2((double)i, sYh[u]);
   };
   auto Q = [&](int i) -> PD {
-    const int u = row_slot(i);
+    const int u = row_slot<P>(i);
     if constexpr (W) {
       const double2 h = sH[u], l = sLo[u];
       return PD{DD{h.x, l.x}, DD{h.y, l.y}};
@@ -268,35 +273,48 @@ __global__ __launch_bounds__(kRowThreads) void k_row(const T* __restrict__ y, co
     return left3(i, pi.x, pi.y, j, pj.x, pj.y, k, pk.x, pk.y);
   };
 
-  // ---- leaves: the hull of points e0 .. e0 + c.  Point e0 + k (0 < k < c) is a vertex iff it
-  // lies strictly below the segment of every pair of points on either side of it; the ten tests
-  // are independent.  Kept as the list of vertices before e0 + c.
+  // ---- leaves: the hull of points e0 .. e0 + c, kept as the list of its vertices before e0 + c.
+  // With four points, point e0 + k (0 < k < c) is a vertex iff it lies strictly below the segment
+  // of every pair of points on either side of it (ten independent tests); with more, the
+  // monotone chain.
   if (c > 0) {
-    double lxv[kRowPer + 1], lyv[kRowPer + 1];
-#pragma unroll
-    for (int k = 0; k <= kRowPer; ++k) {
-      lxv[k] = 0.0;
-      lyv[k] = 0.0;
-      if (k <= c) {
-        const double2 h = hp(e0 + k);
-        lxv[k] = h.x;
-        lyv[k] = h.y;
-      }
-    }
     bool vtx[kRowPer];
+    if constexpr (P == 4) {
+      double lxv[kRowPer + 1], lyv[kRowPer + 1];
 #pragma unroll
-    for (int k = 0; k < kRowPer; ++k) vtx[k] = k < c;
-#pragma unroll
-    for (int k = 1; k < kRowPer; ++k) {
-#pragma unroll
-      for (int a = 0; a < k; ++a) {
-#pragma unroll
-        for (int b = k + 1; b <= kRowPer; ++b) {
-          if (b <= c && vtx[k] &&
-              !left3(e0 + a, lxv[a], lyv[a], e0 + k, lxv[k], lyv[k], e0 + b, lxv[b], lyv[b]))
-            vtx[k] = false;
+      for (int k = 0; k <= kRowPer; ++k) {
+        lxv[k] = 0.0;
+        lyv[k] = 0.0;
+        if (k <= c) {
+          const double2 h = hp(e0 + k);
+          lxv[k] = h.x;
+          lyv[k] = h.y;
         }
       }
+#pragma unroll
+      for (int k = 0; k < kRowPer; ++k) vtx[k] = k < c;
+#pragma unroll
+      for (int k = 1; k < kRowPer; ++k) {
+#pragma unroll
+        for (int a = 0; a < k; ++a) {
+#pragma unroll
+          for (int b = k + 1; b <= kRowPer; ++b) {
+            if (b <= c && vtx[k] &&
+                !left3(e0 + a, lxv[a], lyv[a], e0 + k, lxv[k], lyv[k], e0 + b, lxv[b], lyv[b]))
+              vtx[k] = false;
+          }
+        }
+      }
+    } else {
+      auto Pt = [&](int k, double& xx, double& yy) {
+        const double2 h = hp(e0 + k);
+        xx = h.x;
+        yy = h.y;
+      };
+      auto Pq = [&](int k) -> PD { return Q(e0 + k); };
+      const uint64_t mk = lane_chain(c, Pt, Pq, E);
+#pragma unroll
+      for (int k = 0; k < kRowPer; ++k) vtx[k] = k < c && ((mk >> k) & 1ull);
     }
     int q = 0;
 #pragma unroll
