@@ -2,8 +2,9 @@
 the C ABI.
 
 Each case draws a row length from one of the size classes the library treats differently (1..16
-one lane per row; 17..2048 packed rows; 2049..4096 one row per workgroup of 2 wavefronts;
-longer rows split into chunks of 16384, with ragged tails), a batch, a family, a weight kind, a
+four lanes per row; 17..2048 one row per workgroup of 1024 threads in batches of at most 256,
+packed rows in larger ones; 2049..4096 one row per workgroup; longer rows split into chunks of
+16384, with ragged tails), a batch, a family, a weight kind, a
 direction and a dtype, and checks z, block starts (on integer-valued families) and row flags
 against the oracle with the bars of the other parity tests.  A ragged batch mixing the classes is
 checked the same way, row by row.
