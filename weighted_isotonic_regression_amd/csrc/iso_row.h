@@ -14,15 +14,22 @@
 //                  the hi parts when it clears an a-priori error bound, else from the pairs.
 //
 // A row that fits one workgroup's LDS is latency-bound whatever the kernel does, so this kernel
-// spends threads on shortening the dependent chains: the whole diagram (up to 4097 points as
-// pairs, 131 KB) sits in LDS; a thread's chain is four points long; a merge of two hulls with
-// tpm threads gives each thread a few vertices a of the left hull, finds by bisection the tangent
-// point b(a) of the right hull seen from a, and keeps the a whose neighbours both lie on or above
-// the line a b(a) (the predecessor strictly above, which makes a the leftmost contact).  With
-// exact turns exactly one a passes; if rounding of a near-degenerate turn lets none or several
-// pass, one thread walks to the bridge instead.  Hull vertex lists are kept compact, node k of
-// level r at offset k m (m = 4 * 2^r points per node), without the node's last point (its end,
-// always a vertex, implied), in one of two buffers that alternate by level.
+// spends threads on shortening the dependent chains:
+//   - the whole diagram (up to 4097 points as pairs, 131 KB) sits in LDS, its sums scanned with
+//     DPP row shifts;
+//   - a thread's leaf hull has four points;
+//   - a merge of two hulls by tpm threads gives each thread a few vertices a of the left hull,
+//     finds by bisection the tangent point b(a) of the right hull seen from a, and keeps the a
+//     whose neighbours both lie on or above the line a b(a) (the predecessor strictly above,
+//     which makes a the leftmost contact); in a merge over several wavefronts whose pairs (a, b)
+//     number at most tpm, each thread tests one pair instead, by the neighbours of both ends.  With exact turns exactly one
+//     candidate passes; if rounding of a near-degenerate turn lets none or several pass, the
+//     merge's threads all walk to the bridge instead, with the same result;
+//   - a merge's threads are the ones that built its two nodes, so the levels whose merges fit in
+//     one wavefront only wait for that wavefront.
+// Hull vertex lists are kept compact, node k of level r at offset k m (m = 4 * 2^r points per
+// node), without the node's last point (its end, always a vertex, implied), in one of two buffers
+// that alternate by level.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,7 +43,9 @@ namespace iso {
 constexpr int kRowMax = 4096;  // elements of a row at most
 // Elements per thread of the launched kernel (kRowMax / kRowP threads).  Measured per call on a
 // 1 x 4096 fp64 weighted row: 4 elements 41.9 us, 8 elements 42.6 us, 16 elements 57.0 us (longer
-// chains in fewer threads lose to more levels of parallel bridge searches).
+// chains in fewer threads lose to more levels of parallel bridge searches); leaves of 8 or 16
+// points chained by one thread of each group, with four elements per thread otherwise, took 48.2
+// and 58.9 us against 39.9 us.
 constexpr int kRowP = 4;
 
 // LDS slot of point i with P points per thread: residue-major, so a thread's consecutive points
@@ -355,7 +364,31 @@ __global__ __launch_bounds__(kRowMax / P) void k_row(const T* __restrict__ y, co
     auto Ai = [&](int i) -> int { return i < cA ? (int)LA[i] : s; };
     auto Bk = [&](int k) -> int { return k < cB ? (int)LB[k] : e; };
     int al = cA, be = 1;
-    if (!convex) {
+    const int npair = (cA + 1) * cB;  // candidate bridges (alpha, beta): alpha in A', beta in B' \ {s}
+    if (!convex && tpm > kWave && npair <= tpm) {
+      // few enough pairs for one each: the pair (i, k) is the bridge iff A'[i]'s predecessor lies
+      // strictly above the line A'[i] B'[k] and its successor on or above it, and B'[k]'s
+      // successor strictly above and predecessor on or above (four independent turns).  Only for
+      // merges over several wavefronts: below that the hulls are small, a bisection takes a step
+      // or two, and four turns per pair cost more (measured on the 4096 ramp: levels 0-5 +3.6 us,
+      // levels 6-9 -1.7 us).
+      if (q < npair) {
+        const int i = q / cB, k = 1 + (q - (q / cB) * cB);
+        const int a = Ai(i), b = Bk(k);
+        const int ap = i > 0 ? Ai(i - 1) : a, an = i < cA ? Ai(i + 1) : a;
+        const int bp = Bk(k - 1), bn = k < cB ? Bk(k + 1) : b;
+        const double2 pa = hp(a), pb = hp(b), pap = hp(ap), pan = hp(an), pbp = hp(bp), pbn = hp(bn);
+        const bool c1 = i == 0 || left3(ap, pap.x, pap.y, a, pa.x, pa.y, b, pb.x, pb.y);
+        const bool c2 = i == cA || !left3(a, pa.x, pa.y, an, pan.x, pan.y, b, pb.x, pb.y);
+        const bool c3 = k == cB || left3(a, pa.x, pa.y, b, pb.x, pb.y, bn, pbn.x, pbn.y);
+        const bool c4 = k == 1 || !left3(a, pa.x, pa.y, bp, pbp.x, pbp.y, b, pb.x, pb.y);
+        if (c1 && c2 && c3 && c4) {
+          const uint32_t pay = (uint32_t)i << 13 | (uint32_t)k;
+          atomicMin(&sMin[slot], (uint32_t)(14 - r) << 28 | pay);
+          atomicMax(&sMax[slot], (uint32_t)(r + 1) << 28 | pay);
+        }
+      }
+    } else if (!convex) {
       for (int i = q; i <= cA; i += tpm) {
         const int a = Ai(i);
         const double2 pa = hp(a);
