@@ -3,9 +3,11 @@ oracle/softrank.py, through the C ABI.  The page's setting (Section 7.9, Table 6
 values, eps = 1 (each row pools into one block) and eps = 1/n (most elements start a block),
 rows of 10^2 to 10^6, and the training-step shapes 256 x 10^3 and 4 x 10^5.
 
-Bars: max |r - r*| / (1 + n + max |theta|) per row <= 1e-10 (fp64) and 1e-6 (fp32), the scale of
-the row's problem z = s - w; the same sort permutation; the same block starts; gradients to 1e-10
-(fp64) and 1e-6 (fp32) of their largest entry.
+Bars: max |r - r*| / (1 + n + max |theta|) per row, the scale of the row's problem z = s - w,
+<= 1e-13 for fp64 (measured at most 7.2e-15 over these cases) and <= 2.4e-7 for fp32 (four fp32
+units in the last place of that scale; the fp32 outputs measured identical to the oracle's,
+which rounds its fp64 result to fp32 once); the same sort permutation; the same block starts;
+gradients to 1e-10 (fp64) and 1e-6 (fp32) of their largest entry.
 """
 import numpy as np
 import pytest
@@ -15,7 +17,8 @@ from oracle import softrank
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {np.float32: 1e-6, np.float64: 1e-10}
+TOL = {np.float32: 1e-6, np.float64: 1e-10}  # gradients, relative to their largest entry
+TOL_R = {np.float32: 2.4e-7, np.float64: 1e-13}  # soft ranks, relative to the row's scale
 
 
 def _gpu():
@@ -39,7 +42,7 @@ def _check(x, eps, grad=True):
     n = x.shape[-1]
     scale = 1.0 + n + np.max(np.abs(x.astype(np.float64) / eps), axis=-1, keepdims=True)
     dev = float(np.max(np.abs(r - ro) / scale))
-    assert dev <= TOL[t], dev
+    assert dev <= TOL_R[t], dev
     np.testing.assert_array_equal(perm.cpu().numpy().astype(np.int64) % x.shape[-1], permo)
     np.testing.assert_array_equal(bs.cpu().numpy(), bso)
     assert np.all(rf.cpu().numpy() == 0)
