@@ -424,11 +424,11 @@ def main():
             f.write("# write_bytes launches_per_call.  Valid only for the kernel sources of this hash (bench.py\n")
             f.write("# checks it).\n")
             f.write("# Made by, for each workload W in mixed, dense, hull, short, calib, mono7\n")
-            f.write("# (R = the repository root, run from /tmp):\n")
-            f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/meas/pf_W -o run -- \\\n")
+            f.write("# (R = the repository root, OUT = an output directory, run from /tmp):\n")
+            f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pf_W -o run -- \\\n")
             f.write("#     python3 $R/bench.py --only W --steps 2 --warmup 1 --copy-calib\n")
             f.write("#   (the same with WRITE_SIZE into pw_W), then\n")
-            f.write("#   python bench.py --summarize-pmc NAME gpurun_out/meas/pf_W gpurun_out/meas/pw_W\n")
+            f.write("#   python bench.py --summarize-pmc NAME $OUT/pf_W $OUT/pw_W\n")
             f.write("# with NAME mixed_1e8_f32, dense_1e8_f64, hull_1e8_f64, short_65536x16_f32,\n")
             f.write("# calib_512x131072_f32, mono_1e7_f64 for those W.\n")
             f.write("source_sha256 = %s\n" % sha)
@@ -439,7 +439,7 @@ def main():
         print(open(TRAFFIC_FILE).read())
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows are independent and a "
+        print("bench.py measures one GPU: the library has no multi-GPU path (rows are independent and a "
               "long row is fitted on one device); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
