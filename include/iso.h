@@ -68,7 +68,14 @@ enum {
      nearest is symmetric, so the result is exactly that mirror.  Block starts mark where a block
      of the decreasing fit starts; neighbouring blocks then have strictly decreasing means.
      iso_vjp needs no flag: given the block starts, its formula holds in either direction. */
-  ISO_FLAG_DECREASING = 2u
+  ISO_FLAG_DECREASING = 2u,
+  /* For testing.  Rows of at most 4096 elements fitted one per workgroup (rows of 2049 to 4096,
+     and shorter rows in batches of at most 256) find every bridge that is not a plain
+     concatenation by the walk from the shared point (the page's Lemma 4.2) instead of the
+     parallel search.  Where the turns are exact both give the same hull; the walk otherwise runs
+     only when rounding of a near-degenerate turn leaves the parallel search inconclusive, and
+     this flag lets a test check it.  No effect on other rows. */
+  ISO_FLAG_ROW_WALK = 4u
 };
 
 /* Per-row flag bits written to row_flags. */
@@ -103,7 +110,7 @@ size_t iso_workspace_bytes(int64_t batch, int64_t n, int dtype, int weighted);
  *                bytes, 256-byte aligned; may be NULL when that size is 0.  Its contents on entry
  *                do not matter and on return are unspecified.  Calls that share a workspace must
  *                be ordered on one stream.
- *   flags        0, or ISO_FLAG_CHECK_WEIGHTS and/or ISO_FLAG_DECREASING.
+ *   flags        0, or ISO_FLAG_CHECK_WEIGHTS, ISO_FLAG_DECREASING and/or ISO_FLAG_ROW_WALK.
  * Returns ISO_OK, ISO_EINVAL, ISO_EWEIGHT (only with ISO_FLAG_CHECK_WEIGHTS) or ISO_EHIP.
  */
 int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint32_t* row_flags,

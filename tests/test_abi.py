@@ -59,6 +59,7 @@ def test_header_constants_match_binding():
     assert e["ISO_NOALLOC_SCRATCH_BYTES"] == binding.ISO_NOALLOC_SCRATCH_BYTES
     assert e["ISO_FLAG_CHECK_WEIGHTS"] == binding.ISO_FLAG_CHECK_WEIGHTS
     assert e["ISO_FLAG_DECREASING"] == binding.ISO_FLAG_DECREASING
+    assert e["ISO_FLAG_ROW_WALK"] == binding.ISO_FLAG_ROW_WALK
     assert e["ISO_ROW_NONFINITE"] == binding.ISO_ROW_NONFINITE
     assert e["ISO_ROW_BAD_WEIGHT"] == binding.ISO_ROW_BAD_WEIGHT
 
@@ -93,7 +94,7 @@ def test_argument_errors_before_any_launch(lib):
     assert fx(Y, None, Z, None, None, 1, -5, 0, None, 0, 0, None) == EINVAL         # negative n
     assert fx(Y, None, Z, None, None, 1, 10, 7, None, 0, 0, None) == EINVAL         # bad dtype
     assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 8, None) == EINVAL         # unknown flag
-    assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 4 | 2, None) == EINVAL     # unknown with known
+    assert fx(Y, None, Z, None, None, 1, 10, 0, None, 0, 8 | 2, None) == EINVAL     # unknown with known
     assert fx(Y, None, Y, None, None, 1, 10, 0, None, 0, 2, None) == EINVAL         # decreasing, z aliases y
     assert fx(Y, None, Z, None, None, 1, 20000, 0, None, 0, 2, None) == EINVAL      # decreasing, no workspace
     assert fx(Y, None, Z, None, None, 0, 10, 0, None, 0, 2, None) == OK             # decreasing, empty

@@ -108,3 +108,40 @@ def test_packed_short_rows_large_batches(dtype):
             y, w = W.family(fam, batch, n, seed=n, dtype=dtype, wkind=wk)
             check(y, None if wk == "unit" else w, exact_partition=fam == "integer")
             check(y, w, decreasing=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_row_walk_fallback_matches_search(dtype):
+    """The walk from the shared point, which the one-row kernel uses when rounding leaves its
+    parallel bridge search inconclusive, forced for every bridge (ISO_FLAG_ROW_WALK): z and block
+    starts bit for bit those of the parallel search on every family, and against the oracle."""
+    from tests.test_gpu_fit import _gpu
+
+    b = _gpu()
+    tol = 1e-6 if dtype == "f32" else 1e-10
+    for fam in W.FAMILIES:
+        # bit for bit where no turn is near zero (integer and constant rows with integer weights,
+        # whose sums and turns are exact; generic rows, where ties have probability zero); every
+        # family against the oracle.  Equal neighbouring means with fractional weights make a turn
+        # that is zero in exact arithmetic, which the two paths may round either way: z is the
+        # same, the block start between the two blocks may not be.
+        same = fam in ("noise", "sawtooth", "cliff", "integer", "constant", "increasing", "decreasing")
+        wk = "integer" if fam in ("integer", "constant") else "uniform"
+        for n, batch in ((17, 3), (1000, 2), (4096, 2)):
+            y, w = W.family(fam, batch, n, seed=n + 11, dtype=dtype, wkind=wk)
+            yt, wt = torch.from_numpy(y).cuda(), torch.from_numpy(w).cuda()
+            for dec in (False, True):
+                z1, b1 = b.fit(yt, wt, block_starts=True, decreasing=dec)
+                z2, b2 = b.fit(yt, wt, block_starts=True, decreasing=dec, row_walk=True)
+                torch.cuda.synchronize()
+                z2 = z2.cpu().numpy()
+                if same:
+                    np.testing.assert_array_equal(z2, z1.cpu().numpy(), err_msg=f"{fam} {n} {dec}")
+                    np.testing.assert_array_equal(b2.cpu().numpy(), b1.cpu().numpy())
+                zo = oracle.pav(y.astype(np.float64), w.astype(np.float64), decreasing=dec).reshape(y.shape)
+                if fam == "cancel":
+                    dev = np.max(np.abs(z2.astype(np.float64) - zo)) / np.max(np.abs(y.astype(np.float64)))
+                    assert dev <= (1.4e-15 if dtype == "f64" else 1e-7), (fam, n, dec, dev)
+                else:
+                    dev = np.max(np.abs(z2.astype(np.float64) - zo) / (1 + np.abs(zo)))
+                    assert dev <= tol, (fam, n, dec, dev)

@@ -19,6 +19,7 @@ ISO_OK, ISO_EINVAL, ISO_EWEIGHT, ISO_ENOMEM, ISO_EHIP, ISO_ESCRATCH = 0, 1, 2, 3
 ISO_NOALLOC_SCRATCH_BYTES = 256 << 20
 ISO_FLAG_CHECK_WEIGHTS = 1
 ISO_FLAG_DECREASING = 2
+ISO_FLAG_ROW_WALK = 4
 ISO_ROW_NONFINITE, ISO_ROW_BAD_WEIGHT = 1, 2
 
 _lock = threading.Lock()
@@ -190,11 +191,12 @@ def workspace(batch, n, dtype_code, weighted, device):
 
 
 def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, decreasing=False, out=None,
-        ws=None):
+        ws=None, row_walk=False):
     """Isotonic weighted L2 fit of every row of ``y`` on its device: non-decreasing, or
     non-increasing with ``decreasing=True``.
 
     y: float32/float64 CUDA tensor [n] or [batch, n]; w: same shape and dtype, or None.
+    row_walk (testing): ISO_FLAG_ROW_WALK, bridges of the one-row kernel found by the walk.
     Returns z, or (z, block_start[uint8], row_flags[int32]) as requested.
     """
     torch = _torch()
@@ -216,6 +218,8 @@ def fit(y, w=None, *, block_starts=False, row_flags=False, check_weights=False, 
     else:
         nbytes = ws.numel()
     flags = (ISO_FLAG_CHECK_WEIGHTS if check_weights else 0) | (ISO_FLAG_DECREASING if decreasing else 0)
+    if row_walk:  # testing: ISO_FLAG_ROW_WALK
+        flags |= ISO_FLAG_ROW_WALK
     rc = iso_fit_ex(_ptr(y2), _ptr(w2), _ptr(z), _ptr(bs), _ptr(rf), batch, n, code, _ptr(ws), nbytes, flags,
                     _stream(torch, y2.device))
     if rc != ISO_OK:

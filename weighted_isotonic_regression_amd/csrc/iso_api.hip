@@ -215,7 +215,7 @@ int lanes_per_row(int64_t n) {
 
 template <typename T, bool W, bool D>
 int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int64_t batch,
-            int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
+            int64_t n, char* ws, const Layout& Lay, hipStream_t s, bool row_walk = false) {
   Prof prof(s);
   if (n <= kTinyMax) {
     prof.skip();
@@ -229,7 +229,7 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
     prof.skip();
     if (row_kernel(batch, n)) {
       hipLaunchKernelGGL((k_row<T, W, D, kRowP>), dim3((unsigned)batch), dim3(kRowMax / kRowP), 0, s, y, w, z, bstart,
-                         rflags, (int)n);
+                         rflags, (int)n, row_walk ? 1 : 0);
     } else {
       const int R = kWave / L;
       const int64_t tiles = (batch + R - 1) / R;
@@ -336,10 +336,10 @@ int run_fit(const T* y, const T* w, T* z, uint8_t* bstart, uint32_t* rflags, int
 
 template <typename T, bool D>
 int dispatch_fit(const void* y, const void* w, void* z, uint8_t* bstart, uint32_t* rflags,
-                 int64_t batch, int64_t n, char* ws, const Layout& Lay, hipStream_t s) {
+                 int64_t batch, int64_t n, char* ws, const Layout& Lay, hipStream_t s, bool row_walk = false) {
   if (w)
-    return run_fit<T, true, D>((const T*)y, (const T*)w, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
-  return run_fit<T, false, D>((const T*)y, nullptr, (T*)z, bstart, rflags, batch, n, ws, Lay, s);
+    return run_fit<T, true, D>((const T*)y, (const T*)w, (T*)z, bstart, rflags, batch, n, ws, Lay, s, row_walk);
+  return run_fit<T, false, D>((const T*)y, nullptr, (T*)z, bstart, rflags, batch, n, ws, Lay, s, row_walk);
 }
 
 // ---- rows of unequal lengths (iso_ragged.h)
@@ -667,7 +667,7 @@ int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint
                int64_t batch, int64_t n, int dtype, void* ws, size_t ws_bytes, unsigned flags,
                void* stream) {
   if (!shape_ok(batch, n, dtype)) return ISO_EINVAL;
-  if (flags & ~(unsigned)(ISO_FLAG_CHECK_WEIGHTS | ISO_FLAG_DECREASING)) return ISO_EINVAL;
+  if (flags & ~(unsigned)(ISO_FLAG_CHECK_WEIGHTS | ISO_FLAG_DECREASING | ISO_FLAG_ROW_WALK)) return ISO_EINVAL;
   if (batch == 0 || n == 0) return ISO_OK;
   if (!y || !z) return ISO_EINVAL;
   const size_t esz = dtype == ISO_F64 ? 8 : 4;
@@ -684,12 +684,13 @@ int iso_fit_ex(const void* y, const void* w, void* z, uint8_t* block_start, uint
   if (!rflags && need_ws) rflags = (uint32_t*)(wsb + Lay.o_rflags);
   hipStream_t s = (hipStream_t)stream;
   int rc;
+  const bool rw = (flags & ISO_FLAG_ROW_WALK) != 0;
   if (flags & ISO_FLAG_DECREASING)
-    rc = dtype == ISO_F64 ? dispatch_fit<double, true>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s)
-                          : dispatch_fit<float, true>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s);
+    rc = dtype == ISO_F64 ? dispatch_fit<double, true>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s, rw)
+                          : dispatch_fit<float, true>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s, rw);
   else
-    rc = dtype == ISO_F64 ? dispatch_fit<double, false>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s)
-                          : dispatch_fit<float, false>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s);
+    rc = dtype == ISO_F64 ? dispatch_fit<double, false>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s, rw)
+                          : dispatch_fit<float, false>(y, w, z, block_start, rflags, batch, n, wsb, Lay, s, rw);
   if (rc != ISO_OK) return rc;
   if (flags & ISO_FLAG_CHECK_WEIGHTS) {
     uint32_t* any = (uint32_t*)(wsb + Lay.o_any);

@@ -102,7 +102,7 @@ __device__ __forceinline__ DD wave_scan(DD a, int row) {
 template <typename T, bool W, bool D, int P>
 __global__ __launch_bounds__(kRowMax / P) void k_row(const T* __restrict__ y, const T* __restrict__ w,
                                                       T* __restrict__ z, uint8_t* __restrict__ bstart,
-                                                      uint32_t* __restrict__ rflags, int n) {
+                                                      uint32_t* __restrict__ rflags, int n, int walk) {
   constexpr bool EX = ExactProd<T, W>::value;
   constexpr int kRowPer = P;
   constexpr int kRowThreads = kRowMax / P;
@@ -365,7 +365,8 @@ __global__ __launch_bounds__(kRowMax / P) void k_row(const T* __restrict__ y, co
     auto Bk = [&](int k) -> int { return k < cB ? (int)LB[k] : e; };
     int al = cA, be = 1;
     const int npair = (cA + 1) * cB;  // candidate bridges (alpha, beta): alpha in A', beta in B' \ {s}
-    if (!convex && tpm > kWave && npair <= tpm) {
+    const bool search = !convex && !walk;  // walk != 0: every bridge by the walk (testing)
+    if (search && tpm > kWave && npair <= tpm) {
       // few enough pairs for one each: the pair (i, k) is the bridge iff A'[i]'s predecessor lies
       // strictly above the line A'[i] B'[k] and its successor on or above it, and B'[k]'s
       // successor strictly above and predecessor on or above (four independent turns).  Only for
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(kRowMax / P) void k_row(const T* __restrict__ y, co
           atomicMax(&sMax[slot], (uint32_t)(r + 1) << 28 | pay);
         }
       }
-    } else if (!convex) {
+    } else if (search) {
       for (int i = q; i <= cA; i += tpm) {
         const int a = Ai(i);
         const double2 pa = hp(a);
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kRowMax / P) void k_row(const T* __restrict__ y, co
         be = 1;
         const uint32_t kmin = sMin[slot], kmax = sMax[slot];
         const uint32_t pmask = (1u << 28) - 1u;
-        if ((kmin >> 28) == (uint32_t)(14 - r) && (kmax >> 28) == (uint32_t)(r + 1) &&
+        if (search && (kmin >> 28) == (uint32_t)(14 - r) && (kmax >> 28) == (uint32_t)(r + 1) &&
             (kmin & pmask) == (kmax & pmask)) {
           al = (int)((kmin & pmask) >> 13);
           be = (int)(kmin & 8191u);
